@@ -1,0 +1,28 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    import oracle
+    if not os.path.exists(oracle.LIB):
+        oracle.build()
+    return oracle
+
+
+@pytest.fixture(scope="session")
+def gen_host():
+    import dsa_inputs
+    if not os.path.exists(dsa_inputs.HOST_LIB):
+        dsa_inputs.build()
+    return dsa_inputs
