@@ -1,0 +1,278 @@
+"""Python binding of the gfx950 DSA sparse-attention C ABI (``include/dsa.h``).
+
+Argument marshalling only: every step runs in the HIP library
+``lib/libdsa_mi355x.so``; nothing here computes.  Functions take torch tensors
+on the GPU (PyTorch provides device memory and streams), check dtypes, devices,
+contiguity and sizes, and call the entry point of the same name on the current
+torch stream (or ``stream=`` a torch.cuda.Stream).  A missing library raises.
+
+Layouts are those of the header: caches are group-major, V is
+region-transposed ([B][G][tcap/8][D][8]); bf16 tensors are torch.bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libdsa_mi355x.so")
+
+REGION, PROXY, GROUPS, IDX_HEADS, Q_HEADS, HEAD_DIM, MAX_TOPK, WINDOW = 8, 256, 4, 16, 64, 192, 512, 512
+
+ENTRY_POINTS = [
+    "dsa_geometry_default", "dsa_status_string", "dsa_last_error", "dsa_cache_write",
+    "dsa_compress_regions", "dsa_score_topk_workspace_size", "dsa_score_topk",
+    "dsa_sparse_gqa_workspace_size", "dsa_sparse_gqa_decode", "dsa_sparse_gqa_prefill",
+    "swa_attention_workspace_size", "swa_attention", "swa_ring_append",
+]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [("region_size", ctypes.c_int32), ("proxy_dim", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the HIP library; raises if it is not built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library {LIB_PATH} is missing; build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    G = ctypes.POINTER(Geometry)
+    L.dsa_geometry_default.argtypes = [G]
+    L.dsa_status_string.argtypes = [ctypes.c_int]
+    L.dsa_status_string.restype = ctypes.c_char_p
+    L.dsa_last_error.restype = ctypes.c_char_p
+    L.dsa_cache_write.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, vp]
+    L.dsa_compress_regions.argtypes = [G, i32, vp, i64, vp, vp, i32, vp, vp, vp]
+    L.dsa_score_topk_workspace_size.argtypes = [G, i32, i32]
+    L.dsa_score_topk_workspace_size.restype = sz
+    L.dsa_score_topk.argtypes = [G, i32, vp, vp, vp, vp, i32, vp, vp, i64, i32, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_gqa_workspace_size.argtypes = [G, i32]
+    L.dsa_sparse_gqa_workspace_size.restype = sz
+    L.dsa_sparse_gqa_decode.argtypes = [G, i32, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_gqa_prefill.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp]
+    L.swa_attention_workspace_size.argtypes = [G, i32, i32, i32]
+    L.swa_attention_workspace_size.restype = sz
+    L.swa_attention.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.swa_ring_append.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    for name in ENTRY_POINTS:
+        f = getattr(L, name)
+        if f.restype is ctypes.c_int:  # default
+            f.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def geometry(topk: int = MAX_TOPK, softmax_scale: float | None = None) -> Geometry:
+    g = Geometry()
+    load().dsa_geometry_default(ctypes.byref(g))
+    g.topk = topk
+    if softmax_scale is not None:
+        g.softmax_scale = softmax_scale
+    return g
+
+
+def _check(status: int):
+    if status != 0:
+        L = load()
+        raise DsaError(status, f"{L.dsa_status_string(status).decode()}: {L.dsa_last_error().decode()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _numel_at_least(t, n, name):
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {n}")
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A 256-byte aligned device buffer (uint8) of at least nbytes."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+# ---------------------------------------------------------------------------------------------
+def dsa_cache_write(geom, tok_seq, tok_pos, k_new, v_new, ik_new, k_cache, v_cache, ik_cache, n_seqs, tcap,
+                    stream=None):
+    n = tok_seq.numel()
+    for t, nm in ((tok_seq, "tok_seq"), (tok_pos, "tok_pos")):
+        _dt(t, torch.int32, nm)
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (ik_new, "ik_new"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache"), (ik_cache, "ik_cache")):
+        _dt(t, torch.bfloat16, nm)
+    _numel_at_least(k_new, n * GROUPS * HEAD_DIM, "k_new")
+    _numel_at_least(v_new, n * GROUPS * HEAD_DIM, "v_new")
+    _numel_at_least(k_cache, n_seqs * GROUPS * tcap * HEAD_DIM, "k_cache")
+    _numel_at_least(v_cache, n_seqs * GROUPS * tcap * HEAD_DIM, "v_cache")
+    if ik_new is not None:
+        _numel_at_least(ik_new, n * GROUPS * PROXY, "ik_new")
+        _numel_at_least(ik_cache, n_seqs * GROUPS * tcap * PROXY, "ik_cache")
+    _check(load().dsa_cache_write(ctypes.byref(geom), n, _ptr(tok_seq), _ptr(tok_pos), _ptr(k_new), _ptr(v_new),
+                                  _ptr(ik_new), _ptr(k_cache), _ptr(v_cache), _ptr(ik_cache), n_seqs, tcap,
+                                  _stream(stream)))
+
+
+def dsa_compress_regions(geom, index_k, tcap, region_begin, region_end, max_span, summ, scale, stream=None):
+    batch = region_begin.numel()
+    _dt(index_k, torch.bfloat16, "index_k")
+    _dt(region_begin, torch.int32, "region_begin")
+    _dt(region_end, torch.int32, "region_end")
+    _dt(summ, torch.uint8, "summ")
+    _dt(scale, torch.float32, "scale")
+    _numel_at_least(index_k, batch * GROUPS * tcap * PROXY, "index_k")
+    _numel_at_least(summ, batch * GROUPS * (tcap // REGION) * PROXY, "summ")
+    _numel_at_least(scale, batch * GROUPS * (tcap // REGION), "scale")
+    _check(load().dsa_compress_regions(ctypes.byref(geom), batch, _ptr(index_k), tcap, _ptr(region_begin),
+                                       _ptr(region_end), max_span, _ptr(summ), _ptr(scale), _stream(stream)))
+
+
+def dsa_score_topk_workspace_size(geom, n_queries, max_regions) -> int:
+    return int(load().dsa_score_topk_workspace_size(ctypes.byref(geom), n_queries, max_regions))
+
+
+def dsa_score_topk(geom, index_q, z, q_seq, q_pos, n_seqs, summ, scale, tcap, max_regions, sel, n_sel,
+                   scores_out=None, workspace=None, stream=None):
+    nq = q_seq.numel()
+    _dt(index_q, torch.bfloat16, "index_q")
+    _dt(z, torch.float32, "z")
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _dt(summ, torch.uint8, "summ")
+    _dt(scale, torch.float32, "scale")
+    _dt(scores_out, torch.float32, "scores_out")
+    _numel_at_least(index_q, nq * IDX_HEADS * PROXY, "index_q")
+    _numel_at_least(z, nq * IDX_HEADS, "z")
+    _numel_at_least(summ, n_seqs * GROUPS * (tcap // REGION) * PROXY, "summ")
+    _numel_at_least(scale, n_seqs * GROUPS * (tcap // REGION), "scale")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _numel_at_least(scores_out, nq * GROUPS * max_regions, "scores_out")
+    need = dsa_score_topk_workspace_size(geom, nq, max_regions)
+    if workspace is None:
+        workspace = globals()["workspace"](need, q_seq.device)
+    _check(load().dsa_score_topk(ctypes.byref(geom), nq, _ptr(index_q), _ptr(z), _ptr(q_seq), _ptr(q_pos), n_seqs,
+                                 _ptr(summ), _ptr(scale), tcap, max_regions, _ptr(sel), _ptr(n_sel),
+                                 _ptr(scores_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dsa_sparse_gqa_workspace_size(geom, batch) -> int:
+    return int(load().dsa_sparse_gqa_workspace_size(ctypes.byref(geom), batch))
+
+
+def dsa_sparse_gqa_decode(geom, q, k_cache, v_cache, tcap, seq_len, sel, n_sel, out, workspace=None, stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(k_cache, batch * GROUPS * tcap * HEAD_DIM, "k_cache")
+    _numel_at_least(v_cache, batch * GROUPS * tcap * HEAD_DIM, "v_cache")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_workspace_size(geom, batch), q.device)
+    _check(load().dsa_sparse_gqa_decode(ctypes.byref(geom), batch, _ptr(q), _ptr(k_cache), _ptr(v_cache), tcap,
+                                        _ptr(seq_len), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
+
+
+def dsa_sparse_gqa_prefill(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap, sel, n_sel, out, stream=None):
+    nq = q_seq.numel()
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, nq * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, nq * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(k_cache, n_seqs * GROUPS * tcap * HEAD_DIM, "k_cache")
+    _numel_at_least(v_cache, n_seqs * GROUPS * tcap * HEAD_DIM, "v_cache")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _check(load().dsa_sparse_gqa_prefill(ctypes.byref(geom), nq, _ptr(q), _ptr(q_seq), _ptr(q_pos), n_seqs,
+                                         _ptr(k_cache), _ptr(v_cache), tcap, _ptr(sel), _ptr(n_sel), _ptr(out),
+                                         _stream(stream)))
+
+
+def swa_attention_workspace_size(geom, window, n_seqs, max_new_per_seq) -> int:
+    return int(load().swa_attention_workspace_size(ctypes.byref(geom), window, n_seqs, max_new_per_seq))
+
+
+def _swa_common(n_seqs, max_new, seq_pos0, seq_row0, k_new, v_new, k_ring, v_ring, window):
+    _dt(seq_pos0, torch.int32, "seq_pos0")
+    _dt(seq_row0, torch.int32, "seq_row0")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_ring, "k_ring"), (v_ring, "v_ring")):
+        _dt(t, torch.bfloat16, nm)
+    _numel_at_least(seq_pos0, n_seqs, "seq_pos0")
+    _numel_at_least(seq_row0, n_seqs + 1, "seq_row0")
+    _numel_at_least(k_ring, n_seqs * GROUPS * window * HEAD_DIM, "k_ring")
+    _numel_at_least(v_ring, n_seqs * GROUPS * window * HEAD_DIM, "v_ring")
+    rows = n_seqs * max_new
+    _numel_at_least(k_new, rows * GROUPS * HEAD_DIM, "k_new")
+    _numel_at_least(v_new, rows * GROUPS * HEAD_DIM, "v_new")
+
+
+def swa_attention(geom, window, max_new_per_seq, seq_pos0, seq_row0, q, k_new, v_new, k_ring, v_ring, out,
+                  workspace=None, stream=None):
+    n_seqs = seq_pos0.numel()
+    _swa_common(n_seqs, max_new_per_seq, seq_pos0, seq_row0, k_new, v_new, k_ring, v_ring, window)
+    _dt(q, torch.bfloat16, "q")
+    _dt(out, torch.bfloat16, "out")
+    _numel_at_least(q, n_seqs * max_new_per_seq * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, n_seqs * max_new_per_seq * Q_HEADS * HEAD_DIM, "out")
+    if workspace is None:
+        workspace = globals()["workspace"](swa_attention_workspace_size(geom, window, n_seqs, max_new_per_seq),
+                                           q.device)
+    _check(load().swa_attention(ctypes.byref(geom), window, n_seqs, max_new_per_seq, _ptr(seq_pos0),
+                                _ptr(seq_row0), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
+                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def swa_ring_append(geom, window, max_new_per_seq, seq_pos0, seq_row0, k_new, v_new, k_ring, v_ring, stream=None):
+    n_seqs = seq_pos0.numel()
+    _swa_common(n_seqs, max_new_per_seq, seq_pos0, seq_row0, k_new, v_new, k_ring, v_ring, window)
+    _check(load().swa_ring_append(ctypes.byref(geom), window, n_seqs, max_new_per_seq, _ptr(seq_pos0),
+                                  _ptr(seq_row0), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
+                                  _stream(stream)))
+
+
+def default_softmax_scale() -> float:
+    return 1.0 / math.sqrt(HEAD_DIM)

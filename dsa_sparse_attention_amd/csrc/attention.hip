@@ -1,0 +1,597 @@
+// Sparse GQA (decode and chunked prefill) and sliding-window attention.
+//
+// [P1] kwkr.cn/news/601179, section DSA 稀疏注意力, step ④: attention runs over
+// the real K/V of the selected regions only; [P3] kwkr.cn/news/593658, section
+// 一: 64 query heads in 4 KV groups (GQA), kernels sparse_attention_prefill /
+// _decode; [P2] yfxerp.com/news/376439, sections 512 Token 的环形缓冲区 and
+// 给预填充做的小优化 for the sliding-window layers (512-slot ring written at
+// position mod 512; banded prefill).
+//
+// One MFMA core serves every form.  A wave owns one (query, KV group): the 16
+// query heads of the group are the N = 16 side of v_mfma_f32_16x16x32_bf16,
+// so GQA maps onto the matrix cores without padding.  Regions are consumed
+// four at a time (32 tokens):
+//   S^T[token][head] = K(32x192) . Q^T  -> 2 tiles x 6 k-steps, A = K rows
+//     straight from HBM (lane: one token, 48 contiguous channels), B = Q^T in
+//     registers.  Tile t row m holds token 8*(m/4) + 4t + m%4, which leaves
+//     every lane with the 8 tokens of one region in order;
+//   O^T[dv][head] += V^T(192x32) . P^T  -> 12 tiles, A = V^T read straight
+//     from the region-transposed V layout (one 16-byte load = the 8 tokens of
+//     a region for one channel), B = the lane's own 8 softmax weights.
+// Online softmax in fp32 (exp2 domain), weights rounded to bf16 for the PV
+// product.  Masked positions get weight 0 and their V is zeroed, so stale or
+// uninitialised cache rows can never leak in.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace dsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One region as the core sees it: 8 K rows of D channels (contiguous), one V
+// pack [D][8], and the range [lo, hi] of valid positions inside the region
+// (lo > hi: nothing valid).
+struct Region {
+  const uint16_t* k;
+  const uint16_t* v;
+  int lo, hi;
+};
+
+struct CoreState {
+  f32x4 o[12];
+  float m, l;
+};
+
+__device__ __forceinline__ void core_init(CoreState& st) {
+#pragma unroll
+  for (int i = 0; i < 12; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.0f;
+}
+
+// Q^T operand of head (16g + n) of query row `qrow`: channels 48kb + 8s + e.
+__device__ __forceinline__ void load_q(const uint16_t* q, int64_t qrow, int g, bf16x8 qb[6]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const uint16_t* p = q + (qrow * kQHeads + kHeadsPerGroup * g + n) * kHeadDim + 48 * kb;
+#pragma unroll
+  for (int s = 0; s < 6; ++s) qb[s] = as_bf16x8(ld16(p + 8 * s));
+}
+
+// Processes 4 regions. ra = region of this lane's K rows (entry n/4), rb =
+// region of this lane's softmax weights and V pack (entry kb).
+__device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], const Region& ra,
+                                           const Region& rb, float scale_log2) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  u32x4 kv0[6], kv1[6], vv[12];
+  const uint16_t* k0 = ra.k + (int64_t)(n & 3) * kHeadDim + 48 * kb;
+  const uint16_t* k1 = k0 + 4 * kHeadDim;
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    kv0[s] = ld16(k0 + 8 * s);
+    kv1[s] = ld16(k1 + 8 * s);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) vv[nt] = ld16(rb.v + (16 * nt + n) * 8);
+
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    s0 = mfma16x16x32(as_bf16x8(kv0[s]), qb[s], s0);
+    s1 = mfma16x16x32(as_bf16x8(kv1[s]), qb[s], s1);
+  }
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (i >= rb.lo && i <= rb.hi) ? s0[i] * scale_log2 : -INFINITY;
+    sv[4 + i] = (4 + i >= rb.lo && 4 + i <= rb.hi) ? s1[i] * scale_log2 : -INFINITY;
+  }
+  float cmax = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[i]);
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+  const float m_new = fmaxf(st.m, cmax);
+  float alpha = 1.0f;
+  float p[8];
+  if (m_new == -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = 0.0f;
+  } else {
+    alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+  }
+  float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) st.o[nt] *= alpha;
+
+  // zero V of masked positions (only regions at the causal/window edge)
+  const bool full = (rb.lo <= 0 && rb.hi >= 7);
+  if (__any(!full)) {
+    uint32_t mk[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bool a0 = (2 * w >= rb.lo && 2 * w <= rb.hi);
+      const bool a1 = (2 * w + 1 >= rb.lo && 2 * w + 1 <= rb.hi);
+      mk[w] = (a0 ? 0x0000FFFFu : 0u) | (a1 ? 0xFFFF0000u : 0u);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) {
+      vv[nt].x &= mk[0];
+      vv[nt].y &= mk[1];
+      vv[nt].z &= mk[2];
+      vv[nt].w &= mk[3];
+    }
+  }
+  u32x4 pp;
+  pp.x = pack_bf16x2(p[0], p[1]);
+  pp.y = pack_bf16x2(p[2], p[3]);
+  pp.z = pack_bf16x2(p[4], p[5]);
+  pp.w = pack_bf16x2(p[6], p[7]);
+  const bf16x8 pb = as_bf16x8(pp);
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) st.o[nt] = mfma16x16x32(as_bf16x8(vv[nt]), pb, st.o[nt]);
+}
+
+// Total softmax denominator of the lane's head (sum over the 4 kb lanes).
+__device__ __forceinline__ float core_total_l(const CoreState& st) {
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  return l;
+}
+
+// Writes the normalised output of head (16g + n) of query row qrow.
+__device__ __forceinline__ void core_store(const CoreState& st, uint16_t* out, int64_t qrow, int g) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const float l = core_total_l(st);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  uint16_t* p = out + (qrow * kQHeads + kHeadsPerGroup * g + n) * kHeadDim + 4 * kb;
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) {
+    uint2 w;
+    w.x = pack_bf16x2(st.o[nt][0] * inv, st.o[nt][1] * inv);
+    w.y = pack_bf16x2(st.o[nt][2] * inv, st.o[nt][3] * inv);
+    *(uint2*)(p + 16 * nt) = w;
+  }
+}
+
+// Region r of a DSA cache (sequence/group bases given), valid up to position p.
+__device__ __forceinline__ Region dsa_region(const uint16_t* kbase, const uint16_t* vbase,
+                                             int32_t rid, int64_t p) {
+  Region rg;
+  const int64_t c = p / kRegion;
+  if (rid < 0 || rid > c) {
+    rg.k = kbase;
+    rg.v = vbase;
+    rg.lo = 1;
+    rg.hi = 0;
+    return rg;
+  }
+  rg.k = kbase + (int64_t)rid * kRegion * kHeadDim;
+  rg.v = vbase + (int64_t)rid * kHeadDim * kRegion;
+  rg.lo = 0;
+  const int64_t last = p - (int64_t)rid * kRegion;
+  rg.hi = last >= 7 ? 7 : (int)last;
+  return rg;
+}
+
+// ---------------------------------------------------------------------------
+// Decode: block = (sequence b, group g, split s of 16 selected regions); its
+// 4 waves take one chunk of 4 regions each and are merged through LDS into
+// one partial (max, sum, unnormalised O) per split; k_merge combines splits.
+// ---------------------------------------------------------------------------
+constexpr int kSplitRegions = 16;
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seq_len;
+  const int32_t* sel;
+  const int32_t* nsel;
+  float* part;  // [B][G][nsplit][16][2 + 192]
+  int64_t tcap;
+  int32_t topk, nsplit;
+  float scale_log2;
+};
+
+constexpr int kPartStride = 2 + kHeadDim;  // per head: m, l, o[192]
+
+__global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_o[4][16][kHeadDim];
+
+  int64_t L = a.seq_len[b];
+  L = L < 1 ? 1 : (L > a.tcap ? a.tcap : L);
+  const int64_t p = L - 1;
+  const int64_t sg = (int64_t)b * kGroups + g;
+  const uint16_t* kbase = a.k + sg * a.tcap * kHeadDim;
+  const uint16_t* vbase = a.v + sg * (a.tcap / kRegion) * kHeadDim * kRegion;
+  const int32_t* lst = a.sel + sg * a.topk;
+  int32_t cnt = a.nsel[sg];
+  cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
+
+  CoreState st;
+  core_init(st);
+  const int e0 = split * kSplitRegions + wave * 4;
+  if (e0 < cnt) {
+    bf16x8 qb[6];
+    load_q(a.q, b, g, qb);
+    const int ea = e0 + (n >> 2), eb = e0 + kb;
+    const Region ra = dsa_region(kbase, vbase, ea < cnt ? lst[ea] : -1, p);
+    const Region rb = dsa_region(kbase, vbase, eb < cnt ? lst[eb] : -1, p);
+    core_chunk(st, qb, ra, rb, a.scale_log2);
+  }
+  // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i)
+  const float lt = core_total_l(st);
+  if (kb == 0) {
+    sm_m[wave][n] = st.m;
+    sm_l[wave][n] = lt;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[wave][n][16 * nt + 4 * kb + i] = st.o[nt][i];
+  __syncthreads();
+  float* part = a.part + ((sg * a.nsplit) + split) * 16 * kPartStride;
+  for (int e = threadIdx.x; e < 16 * kHeadDim; e += 256) {
+    const int h = e / kHeadDim, d = e - h * kHeadDim;
+    float M = fmaxf(fmaxf(sm_m[0][h], sm_m[1][h]), fmaxf(sm_m[2][h], sm_m[3][h]));
+    float acc = 0.0f, lsum = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
+        acc += f * sm_o[w][h][d];
+        lsum += f * sm_l[w][h];
+      }
+    }
+    part[h * kPartStride + 2 + d] = acc;
+    if (d == 0) {
+      part[h * kPartStride] = M;
+      part[h * kPartStride + 1] = lsum;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sgqa_merge(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                    int32_t nsplit) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int64_t sg = (int64_t)b * kGroups + g;
+  const float* pp = part + sg * nsplit * 16 * kPartStride;
+  for (int e = threadIdx.x; e < 16 * kHeadDim; e += blockDim.x) {
+    const int h = e / kHeadDim, d = e - h * kHeadDim;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[(s * 16 + h) * kPartStride]);
+    float acc = 0.0f, lsum = 0.0f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < nsplit; ++s) {
+        const float* ps = pp + (s * 16 + h) * kPartStride;
+        const float f = __builtin_amdgcn_exp2f(ps[0] - M);
+        acc += f * ps[2 + d];
+        lsum += f * ps[1];
+      }
+    }
+    const float o = lsum > 0.0f ? acc / lsum : 0.0f;
+    out[((int64_t)b * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + d] = f32_to_bf16(o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one wave per (query, group) over its whole selection.
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+  const uint16_t* q;
+  const int32_t* qseq;
+  const int32_t* qpos;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* sel;
+  const int32_t* nsel;
+  uint16_t* out;
+  int64_t tcap;
+  int32_t nq, n_seqs, topk;
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(256) void k_sgqa_prefill(PrefillArgs a) {
+  const int64_t qi = blockIdx.x;
+  const int g = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  int32_t s = a.qseq[qi];
+  s = s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
+  int64_t p = a.qpos[qi];
+  p = p < 0 ? 0 : (p >= a.tcap ? a.tcap - 1 : p);
+  const int64_t sg = (int64_t)s * kGroups + g;
+  const uint16_t* kbase = a.k + sg * a.tcap * kHeadDim;
+  const uint16_t* vbase = a.v + sg * (a.tcap / kRegion) * kHeadDim * kRegion;
+  const int64_t pg = qi * kGroups + g;
+  const int32_t* lst = a.sel + pg * a.topk;
+  int32_t cnt = a.nsel[pg];
+  cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
+
+  bf16x8 qb[6];
+  load_q(a.q, qi, g, qb);
+  CoreState st;
+  core_init(st);
+  for (int e0 = 0; e0 < cnt; e0 += 4) {
+    const int ea = e0 + (n >> 2), eb = e0 + kb;
+    const Region ra = dsa_region(kbase, vbase, ea < cnt ? lst[ea] : -1, p);
+    const Region rb = dsa_region(kbase, vbase, eb < cnt ? lst[eb] : -1, p);
+    core_chunk(st, qb, ra, rb, a.scale_log2);
+  }
+  core_store(st, a.out, qi, g);
+}
+
+// ---------------------------------------------------------------------------
+// Sliding window.  The ring holds positions < P0 (first new position of the
+// sequence); the new tokens and the old positions sharing P0's region are
+// staged into a region-aligned buffer so that every region the core reads
+// comes from exactly one source.
+// ---------------------------------------------------------------------------
+struct SwaArgs {
+  const int32_t* pos0;  // [S]
+  const int32_t* row0;  // [S+1]
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const uint16_t* k_ring;
+  const uint16_t* v_ring;
+  uint16_t* out;
+  uint16_t* st_k;  // [S][G][nst][8][D]
+  uint16_t* st_v;  // [S][G][nst][D][8]
+  int32_t n_seqs, max_new, nst, window;
+  int64_t rows;
+  float scale_log2;
+};
+
+__device__ __forceinline__ void seq_rows(const SwaArgs& a, int s, int64_t& p0, int64_t& r0, int64_t& nnew) {
+  p0 = a.pos0[s];
+  p0 = p0 < 0 ? 0 : p0;
+  r0 = a.row0[s];
+  int64_t r1 = a.row0[s + 1];
+  r0 = r0 < 0 ? 0 : (r0 > a.rows ? a.rows : r0);
+  r1 = r1 < r0 ? r0 : (r1 > a.rows ? a.rows : r1);
+  nnew = r1 - r0;
+  if (nnew > a.max_new) nnew = a.max_new;
+}
+
+// block = (staged region j, sequence s); threads cover (group, channel).
+__global__ __launch_bounds__(256) void k_swa_stage(SwaArgs a) {
+  const int j = blockIdx.x, s = blockIdx.y;
+  int64_t p0, r0, nnew;
+  seq_rows(a, s, p0, r0, nnew);
+  const int64_t base_pos = (p0 / kRegion) * kRegion + (int64_t)j * kRegion;
+  if (base_pos >= p0 + nnew) return;
+  const int W = a.window;
+  for (int e = threadIdx.x; e < kGroups * kHeadDim; e += 256) {
+    const int g = e / kHeadDim, d = e - g * kHeadDim;
+    const int64_t sg = (int64_t)s * kGroups + g;
+    uint16_t* sk = a.st_k + ((sg * a.nst + j) * kRegion) * kHeadDim + d;
+    uint16_t* sv = a.st_v + ((sg * a.nst + j) * kHeadDim + d) * kRegion;
+    for (int t = 0; t < kRegion; ++t) {
+      const int64_t pos = base_pos + t;
+      uint16_t kv = 0, vv = 0;
+      if (pos < p0) {
+        const int64_t slot = pos % W;
+        kv = a.k_ring[(sg * W + slot) * kHeadDim + d];
+        vv = a.v_ring[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion];
+      } else if (pos < p0 + nnew) {
+        const int64_t row = r0 + (pos - p0);
+        kv = a.k_new[(row * kGroups + g) * kHeadDim + d];
+        vv = a.v_new[(row * kGroups + g) * kHeadDim + d];
+      }
+      sk[(int64_t)t * kHeadDim] = kv;
+      sv[t] = vv;
+    }
+  }
+}
+
+// block = (new token i of sequence s); 4 waves = 4 groups.
+__global__ __launch_bounds__(256) void k_swa_attend(SwaArgs a) {
+  const int64_t i = blockIdx.x;
+  const int s = blockIdx.y;
+  const int g = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  int64_t p0, r0, nnew;
+  seq_rows(a, s, p0, r0, nnew);
+  if (i >= nnew) return;
+  const int64_t p = p0 + i, row = r0 + i;
+  const int W = a.window;
+  const int64_t lo = p - W + 1 < 0 ? 0 : p - W + 1;
+  const int64_t rlo = lo / kRegion, rhi = p / kRegion, rst = p0 / kRegion;
+  const int64_t sg = (int64_t)s * kGroups + g;
+  const uint16_t* rk = a.k_ring + sg * W * kHeadDim;
+  const uint16_t* rv = a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion;
+  const uint16_t* sk = a.st_k + sg * a.nst * kRegion * kHeadDim;
+  const uint16_t* sv = a.st_v + sg * a.nst * kHeadDim * kRegion;
+
+  bf16x8 qb[6];
+  load_q(a.q, row, g, qb);
+  CoreState st;
+  core_init(st);
+  const int64_t nreg = rhi - rlo + 1;
+  for (int64_t e0 = 0; e0 < nreg; e0 += 4) {
+    Region rr[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int64_t e = e0 + (w == 0 ? (n >> 2) : kb);
+      Region rg;
+      if (e >= nreg) {
+        rg.k = rk; rg.v = rv; rg.lo = 1; rg.hi = 0;
+      } else {
+        const int64_t r = rlo + e;
+        if (r < rst) {
+          const int64_t pk = r % (W / kRegion);
+          rg.k = rk + pk * kRegion * kHeadDim;
+          rg.v = rv + pk * kHeadDim * kRegion;
+        } else {
+          rg.k = sk + (r - rst) * kRegion * kHeadDim;
+          rg.v = sv + (r - rst) * kHeadDim * kRegion;
+        }
+        const int64_t first = r * kRegion;
+        rg.lo = (int)((lo > first ? lo : first) - first);
+        rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
+      }
+      rr[w] = rg;
+    }
+    core_chunk(st, qb, rr[0], rr[1], a.scale_log2);
+  }
+  core_store(st, a.out, row, g);
+}
+
+// block = (new token i of sequence s): writes it to the ring if it is among
+// the last `window` new tokens of its sequence.
+__global__ __launch_bounds__(256) void k_ring_append(SwaArgs a, uint16_t* k_ring, uint16_t* v_ring) {
+  const int64_t i = blockIdx.x;
+  const int s = blockIdx.y;
+  int64_t p0, r0, nnew;
+  seq_rows(a, s, p0, r0, nnew);
+  if (i >= nnew || i < nnew - a.window) return;
+  const int W = a.window;
+  const int64_t pos = p0 + i, row = r0 + i, slot = pos % W;
+  for (int e = threadIdx.x; e < kGroups * kHeadDim; e += 256) {
+    const int g = e / kHeadDim, d = e - g * kHeadDim;
+    const int64_t sg = (int64_t)s * kGroups + g;
+    k_ring[(sg * W + slot) * kHeadDim + d] = a.k_new[(row * kGroups + g) * kHeadDim + d];
+    v_ring[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion] =
+        a.v_new[(row * kGroups + g) * kHeadDim + d];
+  }
+}
+
+static int32_t nsplit_of(int32_t topk) { return (topk + kSplitRegions - 1) / kSplitRegions; }
+static int32_t nstage_of(int32_t max_new) { return (max_new + kRegion - 1) / kRegion + 1; }
+
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" size_t dsa_sparse_gqa_workspace_size(const dsa_geometry* geom, int32_t batch) {
+  const int32_t topk = (geom && geom->topk > 0 && geom->topk <= kMaxTopk) ? geom->topk : kMaxTopk;
+  if (batch <= 0) return 256;
+  return (size_t)batch * kGroups * nsplit_of(topk) * 16 * kPartStride * sizeof(float) + 256;
+}
+
+extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                            const uint16_t* k_cache, const uint16_t* v_cache,
+                                            int64_t tcap, const int32_t* seq_len,
+                                            const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (batch < 0 || tcap <= 0 || tcap % kRegion)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: bad sizes (tcap must be a positive multiple of 8)");
+  if (batch == 0) return DSA_OK;
+  if (!q || !k_cache || !v_cache || !seq_len || !sel || !n_sel || !out || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: NULL pointer");
+  if ((size_t)workspace & 255)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: workspace must be 256-byte aligned");
+  if (workspace_bytes < dsa_sparse_gqa_workspace_size(geom, batch))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_sparse_gqa_decode: workspace too small");
+  if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_gqa_decode: batch > 65535");
+  DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.seq_len = seq_len; a.sel = sel; a.nsel = n_sel;
+  a.part = (float*)workspace; a.tcap = tcap; a.topk = geom->topk; a.nsplit = nsplit_of(geom->topk);
+  a.scale_log2 = geom->softmax_scale * kLog2e;
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(k_sgqa_decode, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
+  st = check_launch("dsa_sparse_gqa_decode");
+  if (st != DSA_OK) return st;
+  hipLaunchKernelGGL(k_sgqa_merge, dim3(kGroups, batch), dim3(256), 0, s, (const float*)workspace, out, a.nsplit);
+  return check_launch("dsa_sparse_gqa_decode: merge");
+}
+
+extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                             const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                             const uint16_t* k_cache, const uint16_t* v_cache,
+                                             int64_t tcap, const int32_t* sel, const int32_t* n_sel,
+                                             uint16_t* out, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (n_queries < 0 || n_seqs < 0 || tcap <= 0 || tcap % kRegion)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: bad sizes (tcap must be a positive multiple of 8)");
+  if (n_queries == 0) return DSA_OK;
+  if (n_seqs == 0) return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: n_seqs must be positive");
+  if (!q || !q_seq || !q_pos || !k_cache || !v_cache || !sel || !n_sel || !out)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: NULL pointer");
+  PrefillArgs a;
+  a.q = q; a.qseq = q_seq; a.qpos = q_pos; a.k = k_cache; a.v = v_cache; a.sel = sel; a.nsel = n_sel;
+  a.out = out; a.tcap = tcap; a.nq = n_queries; a.n_seqs = n_seqs; a.topk = geom->topk;
+  a.scale_log2 = geom->softmax_scale * kLog2e;
+  hipLaunchKernelGGL(k_sgqa_prefill, dim3(n_queries), dim3(256), 0, as_stream(stream), a);
+  return check_launch("dsa_sparse_gqa_prefill");
+}
+
+extern "C" size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
+                                               int32_t max_new_per_seq) {
+  (void)geom;
+  (void)window;
+  if (n_seqs <= 0 || max_new_per_seq <= 0) return 256;
+  const size_t one = (size_t)n_seqs * kGroups * nstage_of(max_new_per_seq) * kRegion * kHeadDim * sizeof(uint16_t);
+  return 2 * ((one + 255) / 256 * 256) + 256;
+}
+
+static dsa_status swa_check(const dsa_geometry* geom, int32_t window, int32_t n_seqs, int32_t max_new,
+                            const char* who) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (window != kWindow) return fail(DSA_ERR_UNSUPPORTED, std::string(who) + ": window must be 512");
+  if (n_seqs < 0 || max_new < 0) return fail(DSA_ERR_INVALID_ARGUMENT, std::string(who) + ": negative size");
+  if (n_seqs > 65535) return fail(DSA_ERR_UNSUPPORTED, std::string(who) + ": n_seqs > 65535");
+  return DSA_OK;
+}
+
+extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
+                                    int32_t max_new_per_seq, const int32_t* seq_pos0, const int32_t* seq_row0,
+                                    const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                    const uint16_t* k_ring, const uint16_t* v_ring, uint16_t* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = swa_check(geom, window, n_seqs, max_new_per_seq, "swa_attention");
+  if (st != DSA_OK) return st;
+  if (n_seqs == 0 || max_new_per_seq == 0) return DSA_OK;
+  if (!seq_pos0 || !seq_row0 || !q || !k_new || !v_new || !k_ring || !v_ring || !out || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "swa_attention: NULL pointer");
+  if ((size_t)workspace & 255)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "swa_attention: workspace must be 256-byte aligned");
+  if (workspace_bytes < swa_attention_workspace_size(geom, window, n_seqs, max_new_per_seq))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "swa_attention: workspace too small");
+  SwaArgs a;
+  a.pos0 = seq_pos0; a.row0 = seq_row0; a.q = q; a.k_new = k_new; a.v_new = v_new;
+  a.k_ring = k_ring; a.v_ring = v_ring; a.out = out;
+  a.n_seqs = n_seqs; a.max_new = max_new_per_seq; a.nst = nstage_of(max_new_per_seq); a.window = window;
+  a.rows = (int64_t)n_seqs * max_new_per_seq;
+  a.scale_log2 = geom->softmax_scale * kLog2e;
+  const size_t one = (size_t)n_seqs * kGroups * a.nst * kRegion * kHeadDim * sizeof(uint16_t);
+  a.st_k = (uint16_t*)workspace;
+  a.st_v = (uint16_t*)((char*)workspace + (one + 255) / 256 * 256);
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(k_swa_stage, dim3(a.nst, n_seqs), dim3(256), 0, s, a);
+  st = check_launch("swa_attention: stage");
+  if (st != DSA_OK) return st;
+  hipLaunchKernelGGL(k_swa_attend, dim3(max_new_per_seq, n_seqs), dim3(256), 0, s, a);
+  return check_launch("swa_attention");
+}
+
+extern "C" dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
+                                      int32_t max_new_per_seq, const int32_t* seq_pos0, const int32_t* seq_row0,
+                                      const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_ring,
+                                      uint16_t* v_ring, void* stream) {
+  dsa_status st = swa_check(geom, window, n_seqs, max_new_per_seq, "swa_ring_append");
+  if (st != DSA_OK) return st;
+  if (n_seqs == 0 || max_new_per_seq == 0) return DSA_OK;
+  if (!seq_pos0 || !seq_row0 || !k_new || !v_new || !k_ring || !v_ring)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "swa_ring_append: NULL pointer");
+  SwaArgs a = {};
+  a.pos0 = seq_pos0; a.row0 = seq_row0; a.k_new = k_new; a.v_new = v_new;
+  a.n_seqs = n_seqs; a.max_new = max_new_per_seq; a.window = window;
+  a.rows = (int64_t)n_seqs * max_new_per_seq;
+  hipLaunchKernelGGL(k_ring_append, dim3(max_new_per_seq, n_seqs), dim3(256), 0, as_stream(stream), a,
+                     k_ring, v_ring);
+  return check_launch("swa_ring_append");
+}

@@ -1,0 +1,66 @@
+// Shared device/host helpers of the gfx950 DSA library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+// Compiled geometry ([P2] sparse_config table; [P3] section 一 config table).
+constexpr int kRegion = 8;
+constexpr int kProxy = 256;
+constexpr int kGroups = 4;
+constexpr int kIdxHeads = 16;
+constexpr int kIdxHeadsPerGroup = kIdxHeads / kGroups;  // 4
+constexpr int kQHeads = 64;
+constexpr int kHeadsPerGroup = kQHeads / kGroups;  // 16 = one MFMA tile edge
+constexpr int kHeadDim = 192;
+constexpr int kMaxTopk = 512;
+constexpr int kWindow = 512;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A(16x32) * B(32x16) + C on the matrix cores; lane l holds A row l%16,
+// B column l%16 (8 contraction elements each, slot l/16) and D rows
+// 4*(l/16)..+3 of column l%16.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+
+}  // namespace dsa
+
+// ---- host-side helpers (api.hip) ----
+namespace dsa {
+dsa_status fail(dsa_status s, const std::string& msg);
+dsa_status check_geometry(const dsa_geometry* g);
+dsa_status check_launch(const char* what);
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+}  // namespace dsa

@@ -1,0 +1,146 @@
+// Region compression (CSA summaries) and cache writes.
+//
+// Summary rule ([P1] kwkr.cn/news/601179, section DSA 稀疏注意力, steps ①②;
+// [P2] yfxerp.com/news/376439, section 区域压缩（CSA）: every complete region of
+// 8 tokens becomes one 256-d summary stored in FP8; a partial tail region is
+// held back).  The pages give no maths for the summary; the stand-in rule is
+// the mean of the 8 index_k rows of the group, quantised to OCP E4M3 with one
+// fp32 scale amax/448 per (region, group).
+#include "common.hpp"
+
+namespace dsa {
+
+// fp32 -> OCP E4M3 (e4m3fn): round to nearest even, saturate to +-448,
+// keep the sign of zero.  Written from the format definition: normal values
+// keep 3 mantissa bits (rounding on the fp32 bit pattern, the carry moves into
+// the exponent), values below 2^-6 are multiples of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;
+  float af = __uint_as_float(a);
+  if (af >= 448.0f) return sign | 0x7Eu;
+  if (af < 0.015625f) return sign | (uint32_t)__builtin_rintf(af * 512.0f);
+  uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
+}
+
+// One wave per (region, group): lane l owns channels 4l..4l+3.  The block's
+// four waves are the four groups of one region.
+__global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ ik, int64_t tcap,
+                                                  const int32_t* __restrict__ rbeg,
+                                                  const int32_t* __restrict__ rend,
+                                                  int32_t max_span, uint8_t* __restrict__ summ,
+                                                  float* __restrict__ scale) {
+  const int b = blockIdx.y;
+  const int g = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t R = tcap / kRegion;
+  int64_t r0 = rbeg[b], r1 = rend[b];
+  r0 = r0 < 0 ? 0 : (r0 > R ? R : r0);
+  r1 = r1 < r0 ? r0 : (r1 > R ? R : r1);
+  if (r1 - r0 > max_span) r1 = r0 + max_span;
+  const int64_t r = r0 + blockIdx.x;
+  if (r >= r1) return;
+
+  const uint16_t* src = ik + (((int64_t)b * kGroups + g) * tcap + (int64_t)kRegion * r) * kProxy + 4 * lane;
+  uint2 row[kRegion];
+#pragma unroll
+  for (int t = 0; t < kRegion; ++t) row[t] = *(const uint2*)(src + (int64_t)t * kProxy);
+  float m[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t w0 = (e < 2) ? row[0].x : row[0].y;
+    float s = __uint_as_float((e & 1) ? (w0 & 0xFFFF0000u) : (w0 << 16));
+#pragma unroll
+    for (int t = 1; t < kRegion; ++t) {
+      const uint32_t w = (e < 2) ? row[t].x : row[t].y;
+      s = s + __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    m[e] = s * 0.125f;
+  }
+  float amax = fmaxf(fmaxf(fabsf(m[0]), fabsf(m[1])), fmaxf(fabsf(m[2]), fabsf(m[3])));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float sc = __fdiv_rn(amax, 448.0f);
+  uint32_t packed = 0;
+  if (sc != 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) packed |= e4m3_rne_sat(__fdiv_rn(m[e], sc)) << (8 * e);
+  }
+  const int64_t rg = ((int64_t)b * kGroups + g) * R + r;
+  *(uint32_t*)(summ + rg * kProxy + 4 * lane) = packed;
+  if (lane == 0) scale[rg] = sc;
+}
+
+// One block per new token row: copies K/V (and index_k) into the cache
+// layouts (V region-transposed).
+__global__ __launch_bounds__(256) void k_cache_write(
+    const int32_t* __restrict__ tok_seq, const int32_t* __restrict__ tok_pos,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint16_t* __restrict__ ik_new, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, uint16_t* __restrict__ ik_cache, int32_t n_seqs,
+    int64_t tcap) {
+  const int64_t i = blockIdx.x;
+  const int s = tok_seq[i];
+  const int64_t t = tok_pos[i];
+  if (s < 0 || s >= n_seqs || t < 0 || t >= tcap) return;
+  const int64_t R = tcap / kRegion;
+  for (int e = threadIdx.x; e < kGroups * kHeadDim; e += blockDim.x) {
+    const int g = e / kHeadDim, d = e - g * kHeadDim;
+    const int64_t sg = (int64_t)s * kGroups + g;
+    k_cache[(sg * tcap + t) * kHeadDim + d] = k_new[i * kGroups * kHeadDim + e];
+    v_cache[((sg * R + t / kRegion) * kHeadDim + d) * kRegion + (t % kRegion)] =
+        v_new[i * kGroups * kHeadDim + e];
+  }
+  if (ik_new) {
+    for (int e = threadIdx.x; e < kGroups * kProxy; e += blockDim.x) {
+      const int g = e / kProxy, d = e - g * kProxy;
+      ik_cache[(((int64_t)s * kGroups + g) * tcap + t) * kProxy + d] = ik_new[i * kGroups * kProxy + e];
+    }
+  }
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" dsa_status dsa_compress_regions(const dsa_geometry* geom, int32_t batch,
+                                           const uint16_t* index_k, int64_t tcap,
+                                           const int32_t* region_begin, const int32_t* region_end,
+                                           int32_t max_span, uint8_t* summ, float* scale,
+                                           void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (batch < 0 || max_span < 0 || tcap <= 0 || tcap % kRegion)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_compress_regions: batch/max_span must be >= 0 and tcap a positive multiple of 8");
+  if (batch == 0 || max_span == 0) return DSA_OK;
+  if (!index_k || !region_begin || !region_end || !summ || !scale)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_compress_regions: NULL pointer");
+  if (max_span > tcap / kRegion) max_span = (int32_t)(tcap / kRegion);
+  if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, "dsa_compress_regions: batch > 65535");
+  hipLaunchKernelGGL(k_compress, dim3(max_span, batch), dim3(256), 0, as_stream(stream), index_k,
+                     tcap, region_begin, region_end, max_span, summ, scale);
+  return check_launch("dsa_compress_regions");
+}
+
+extern "C" dsa_status dsa_cache_write(const dsa_geometry* geom, int32_t n_tokens,
+                                      const int32_t* tok_seq, const int32_t* tok_pos,
+                                      const uint16_t* k_new, const uint16_t* v_new,
+                                      const uint16_t* ik_new, uint16_t* k_cache,
+                                      uint16_t* v_cache, uint16_t* ik_cache, int32_t n_seqs,
+                                      int64_t tcap, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (n_tokens < 0 || n_seqs < 0 || tcap <= 0 || tcap % kRegion)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: bad sizes (tcap must be a positive multiple of 8)");
+  if (n_tokens == 0 || n_seqs == 0) return DSA_OK;
+  if (!tok_seq || !tok_pos || !k_new || !v_new || !k_cache || !v_cache)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: NULL pointer");
+  if ((ik_new == nullptr) != (ik_cache == nullptr))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: ik_new and ik_cache must both be set or both NULL");
+  hipLaunchKernelGGL(k_cache_write, dim3(n_tokens), dim3(256), 0, as_stream(stream), tok_seq, tok_pos,
+                     k_new, v_new, ik_new, k_cache, v_cache, ik_cache, n_seqs, tcap);
+  return check_launch("dsa_cache_write");
+}

@@ -1,0 +1,243 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DSA sparse-attention library.
+ *
+ * The layer is the one Step-5-Preview uses in its full-attention layers, as
+ * described on these pages (cited by title and section):
+ *  [P1] Step-5-Preview long-context explainer (no title in the extract),
+ *       kwkr.cn/news/601179, section DSA 稀疏注意力 (four-step list ①-④) and
+ *       section 滑窗注意力只读最近 512 个 token.
+ *  [P2] "Step-5-Preview 如何实现1M长上下文？滑窗+DSA稀疏注意力混合机制完整揭秘",
+ *       yfxerp.com/news/376439: sparse_config table, sections 区域压缩（CSA）,
+ *       索引器打分 + Top-K 选择, 512 Token 的环形缓冲区, 给预填充做的小优化.
+ *  [P3] "100 万 token 上下文实测：Step 5 Preview 一次能吞下多大的工程",
+ *       kwkr.cn/news/593658, section 一 (config table, kernel list).
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *    row-major and contiguous in the layout documented below.  bf16 values are
+ *    passed as uint16_t bit patterns, E4M3 (OCP e4m3fn) codes as uint8_t.
+ *  - `geom` is HOST memory.  The library is compiled for one geometry:
+ *    region 8, proxy 256, 4 KV groups, 16 indexer heads, 64 query heads,
+ *    head_dim 192, 1 <= topk <= 512; anything else returns DSA_ERR_UNSUPPORTED.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work and returns; it never synchronises.
+ *  - Ownership: the caller allocates and owns every buffer, caches and
+ *    workspaces included.  The library allocates no device memory, keeps no
+ *    pointer after a call returns, and holds no global device state.
+ *  - Errors: argument checks run on the host before any launch and return a
+ *    status without touching memory; a failed launch returns DSA_ERR_HIP.
+ *    dsa_last_error() gives a message for the calling thread's last failure.
+ *    Index arrays that live on the device (positions, region lists, ranges)
+ *    are the caller's contract; kernels clamp them so that every access stays
+ *    inside the buffers described by the host-side sizes, but results for
+ *    out-of-contract indices are unspecified.
+ *  - Outputs are bitwise reproducible from run to run (no floating-point
+ *    atomics on any result path).
+ *
+ * Cache layouts (per sequence b of a batch, capacity tcap tokens, tcap a
+ * multiple of 8; region r = tokens 8r..8r+7; R = tcap/8):
+ *   index_k  [B][G][tcap][P]    bf16   indexer keys
+ *   K        [B][G][tcap][D]    bf16   keys (post-RoPE)
+ *   V        [B][G][R][D][8]    bf16   values, "region-transposed": the 8
+ *                                      tokens of one region are contiguous
+ *                                      for each channel
+ *   summ     [B][G][R][P]       uint8  E4M3 region summaries
+ *   scale    [B][G][R]          fp32   per-(region, group) summary scale
+ * Sliding-window ring (window W = 512, slot of position t = t mod W):
+ *   k_ring   [S][G][W][D]       bf16
+ *   v_ring   [S][G][W/8][D][8]  bf16   region-transposed like V
+ */
+#ifndef DSA_MI355X_H
+#define DSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_HIP = 4
+} dsa_status;
+
+/* Geometry of the layer ([P2] sparse_config table: topk 512, region_block_size
+ * 8, proxy_dim 256; [P1] step ③: 16-head indexer; [P3] section 一: 64 query
+ * heads in 4 groups; head_dim 192 per [P3]'s KV arithmetic).  softmax_scale
+ * is 1/sqrt(head_dim) by default; any finite positive value is accepted. */
+typedef struct {
+  int32_t region_size; /* 8   */
+  int32_t proxy_dim;   /* 256 */
+  int32_t n_groups;    /* 4   */
+  int32_t n_idx_heads; /* 16  */
+  int32_t n_q_heads;   /* 64  */
+  int32_t head_dim;    /* 192 */
+  int32_t topk;        /* 512 */
+  float softmax_scale; /* 1/sqrt(192) */
+} dsa_geometry;
+
+/* Fills the default geometry.  Never fails for a non-NULL pointer. */
+dsa_status dsa_geometry_default(dsa_geometry* geom);
+/* Static English text for a status code. */
+const char* dsa_status_string(int status);
+/* Message of the calling thread's last failing call ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Writes the K/V (and optionally index_k) rows of new tokens into the caches,
+ * converting to the cache layouts above (the DSA layer cache keeps the full
+ * K/V for exact attention: [P2] section 区域压缩（CSA）, DSALayerCache).
+ *   n_tokens        number of new token rows
+ *   tok_seq/tok_pos [n_tokens] int32 device: sequence index in [0, n_seqs)
+ *                   and absolute position in [0, tcap); rows with either out
+ *                   of range are skipped
+ *   k_new, v_new    [n_tokens][G][D] bf16; ik_new [n_tokens][G][P] or NULL
+ *   k_cache, v_cache, ik_cache (NULL iff ik_new is NULL): caches of n_seqs
+ *                   sequences with capacity tcap
+ */
+dsa_status dsa_cache_write(const dsa_geometry* geom, int32_t n_tokens, const int32_t* tok_seq,
+                           const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
+                           const uint16_t* ik_new, uint16_t* k_cache, uint16_t* v_cache,
+                           uint16_t* ik_cache, int32_t n_seqs, int64_t tcap, void* stream);
+
+/*
+ * Region compression ([P1] steps ①②; [P2] section 区域压缩（CSA）; [P3] kernel
+ * list: csa_compress_regions).  For every sequence b and region r in
+ * [region_begin[b], region_end[b]) (clamped to [0, tcap/8) and to at most
+ * max_span regions), and every group g: the mean of index_k rows 8r..8r+7 of
+ * group g (fp32, summed in token order, times 0.125) is quantised to E4M3
+ * with scale = amax/448 (fp32 IEEE division m/scale, round to nearest even,
+ * saturating at +-448; scale 0 gives all-zero codes).  The pages do not give
+ * the summary maths; this is the stand-in rule.  Only complete regions are
+ * summarised: the caller passes region_end <= (tokens written)/8, keeping the
+ * partial tail region back until it fills.
+ *   batch           number of sequences
+ *   index_k         [batch][G][tcap][P] bf16
+ *   region_begin/end [batch] int32 device
+ *   max_span        host bound on region_end - region_begin (grid size), >= 0
+ *   summ, scale     [batch][G][tcap/8][P] uint8, [batch][G][tcap/8] fp32
+ * Output is bit-exact with the stated rule.
+ */
+dsa_status dsa_compress_regions(const dsa_geometry* geom, int32_t batch, const uint16_t* index_k,
+                                int64_t tcap, const int32_t* region_begin,
+                                const int32_t* region_end, int32_t max_span, uint8_t* summ,
+                                float* scale, void* stream);
+
+/* Workspace bytes dsa_score_topk needs for n_queries and max_regions. */
+size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_t n_queries,
+                                     int32_t max_regions);
+
+/*
+ * Indexer scoring + top-k region selection ([P2] section 索引器打分 + Top-K
+ * 选择: score_regions, radix-style top-k, prefill/decode_metadata, current
+ * region always kept; [P3] kernel list: indexer_logits_radix_topk_threshold).
+ * For query i at position p = q_pos[i] of sequence q_seq[i], current region
+ * c = p/8, and each group g:
+ *   score(r) = sum_{h=4g..4g+3} z[i][h] * ReLU(index_q[i][h] . S_g[r]),
+ *   S_g[r] = E4M3 value of summ[...][g][r][:] * scale[...][g][r],
+ * for the complete regions r < c (stand-in maths; the pages give none).  The
+ * selection is region c plus the min(topk-1, c) best of 0..c-1 ranked by
+ * score descending, lower index first on ties; it is written ascending.
+ *   index_q   [n_queries][16][P] bf16;  z [n_queries][16] fp32
+ *   q_seq, q_pos [n_queries] int32 device; q_seq in [0, n_seqs)
+ *   summ, scale  summaries of n_seqs sequences with capacity tcap (layout above)
+ *   max_regions  host bound: p/8 < max_regions for every query (grid, workspace)
+ *   sel       [n_queries][G][topk] int32, ascending region ids, -1 padded
+ *   n_sel     [n_queries][G] int32 = min(topk, c+1)
+ *   scores_out NULL or [n_queries][G][max_regions] fp32: score(r) for r < c
+ *             (entries r >= c are left untouched)
+ *   workspace device buffer of at least dsa_score_topk_workspace_size() bytes
+ * Scores are fp32 (bf16 x E4M3 products, fp32 accumulation); on equal fp32
+ * scores the lower index wins.
+ */
+dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries, const uint16_t* index_q,
+                          const float* z, const int32_t* q_seq, const int32_t* q_pos,
+                          int32_t n_seqs, const uint8_t* summ, const float* scale, int64_t tcap,
+                          int32_t max_regions, int32_t* sel, int32_t* n_sel, float* scores_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dsa_sparse_gqa_decode needs for `batch` queries. */
+size_t dsa_sparse_gqa_workspace_size(const dsa_geometry* geom, int32_t batch);
+
+/*
+ * Sparse GQA decode ([P1] step ④; [P3] kernel list: sparse_attention_decode;
+ * attention_impl sparse_gqa in [P2]'s sparse_config table).  Query b sits at
+ * position p = seq_len[b]-1 of sequence b.  Head h (group g = h/16) attends
+ * to the tokens 8r..min(8r+7, p) of every region r in sel[b][g][0..n_sel):
+ *   out[b][h] = sum_j softmax_j(softmax_scale * q[b][h] . K_j) V_j
+ * (fp32 softmax and accumulation, bf16 MFMA products, bf16 output).  Region
+ * ids outside [0, p/8] are ignored.
+ *   q   [batch][64][D] bf16 (post-RoPE);  out [batch][64][D] bf16
+ *   k_cache, v_cache: caches of `batch` sequences with capacity tcap
+ *   seq_len [batch] int32 device (1 <= seq_len <= tcap)
+ *   sel, n_sel as produced by dsa_score_topk
+ */
+dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                 const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                                 const int32_t* seq_len, const int32_t* sel, const int32_t* n_sel,
+                                 uint16_t* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * Sparse GQA for a chunk of prefill queries ([P3] kernel list:
+ * sparse_attention_prefill).  Same maths as decode, per query i of sequence
+ * q_seq[i] at position q_pos[i] (the current region may be partial; tokens
+ * after p are masked).  The chunk's own K/V must already be in the caches.
+ *   q, out [n_queries][64][D] bf16;  caches of n_seqs sequences, capacity tcap
+ */
+dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                  const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                  const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                                  const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                  void* stream);
+
+/* Workspace bytes swa_attention needs. */
+size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
+                                    int32_t max_new_per_seq);
+
+/*
+ * Sliding-window attention of the other layers ([P1] section 滑窗注意力只读最近
+ * 512 个 token; [P2] sections 512 Token 的环形缓冲区 and 给预填充做的小优化):
+ * the query at position p attends to positions max(0, p-W+1)..p.  Decode is
+ * the case of one new token per sequence; chunked prefill passes a chunk of
+ * new tokens (any length: the band mask is applied per query, so the result
+ * does not depend on how a prompt is cut into chunks).
+ *   window           512 (the only supported value)
+ *   n_seqs           sequences in this call; sequence s has new tokens at
+ *                    positions seq_pos0[s] .. seq_pos0[s]+n_s-1 stored in rows
+ *                    seq_row0[s] .. seq_row0[s+1]-1 (n_s = the difference)
+ *   max_new_per_seq  host bound on n_s (grid, workspace)
+ *   seq_pos0 [n_seqs], seq_row0 [n_seqs+1] int32 device
+ *   q [rows][64][D], k_new/v_new [rows][G][D] bf16, out [rows][64][D] bf16
+ *   k_ring, v_ring   the ring of each sequence BEFORE this call's tokens are
+ *                    appended: it holds positions seq_pos0[s]-W .. seq_pos0[s]-1
+ *                    (those >= 0) in slots t mod W
+ *   workspace        >= swa_attention_workspace_size() bytes
+ * Call swa_ring_append afterwards to advance the rings.
+ */
+dsa_status swa_attention(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
+                         int32_t max_new_per_seq, const int32_t* seq_pos0,
+                         const int32_t* seq_row0, const uint16_t* q, const uint16_t* k_new,
+                         const uint16_t* v_new, const uint16_t* k_ring, const uint16_t* v_ring,
+                         uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Ring-buffer append ([P2] section 512 Token 的环形缓冲区: DenseLayerCache.write
+ * puts each token in slot position mod window): writes the last min(n_s, W)
+ * new rows of every sequence into slots t mod W of k_ring/v_ring.  Arguments
+ * as for swa_attention.
+ */
+dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
+                           int32_t max_new_per_seq, const int32_t* seq_pos0,
+                           const int32_t* seq_row0, const uint16_t* k_new, const uint16_t* v_new,
+                           uint16_t* k_ring, uint16_t* v_ring, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_MI355X_H */

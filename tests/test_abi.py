@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every function include/dsa.h declares, and rejects bad arguments
+on the host before any launch (these calls return before touching the GPU, so they run on CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dsa_sparse_attention_amd as dsa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dsa.h")
+
+
+def _declared():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:dsa_status|size_t|const char\*)\s+(\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.LIB_PATH):
+        from dsa_sparse_attention_amd import build
+        build.build()
+    return dsa.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["dsa_compress_regions", "dsa_score_topk", "dsa_sparse_gqa_decode", "dsa_sparse_gqa_prefill",
+              "swa_attention", "swa_ring_append"]:
+        assert n in names
+    assert set(names) == set(dsa.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_geometry_default_and_status_strings(lib):
+    g = dsa.geometry()
+    assert (g.region_size, g.proxy_dim, g.n_groups, g.n_idx_heads, g.n_q_heads, g.head_dim, g.topk) == \
+        (8, 256, 4, 16, 64, 192, 512)
+    assert abs(g.softmax_scale - 192 ** -0.5) < 1e-7
+    assert lib.dsa_status_string(0) == b"ok"
+    assert lib.dsa_status_string(3) == b"workspace too small"
+
+
+def _bad(geom_changes):
+    g = dsa.geometry()
+    for k, v in geom_changes.items():
+        setattr(g, k, v)
+    return g
+
+
+@pytest.mark.parametrize("change,status", [({"head_dim": 128}, 2), ({"n_groups": 8}, 2), ({"topk": 0}, 2),
+                                           ({"topk": 513}, 2), ({"softmax_scale": -1.0}, 1)])
+def test_unsupported_geometry_is_refused(lib, change, status):
+    g = _bad(change)
+    vp = ctypes.c_void_p(16)  # never dereferenced: the check fails first
+    rc = lib.dsa_compress_regions(ctypes.byref(g), 1, vp, 64, vp, vp, 1, vp, vp, None)
+    assert rc == status
+    assert lib.dsa_last_error()
+
+
+def test_null_geometry_and_pointers(lib):
+    vp = ctypes.c_void_p(16)
+    assert lib.dsa_compress_regions(None, 1, vp, 64, vp, vp, 1, vp, vp, None) == 1
+    g = dsa.geometry()
+    assert lib.dsa_compress_regions(ctypes.byref(g), 1, None, 64, vp, vp, 1, vp, vp, None) == 1
+    assert lib.dsa_compress_regions(ctypes.byref(g), 1, vp, 60, vp, vp, 1, vp, vp, None) == 1  # tcap % 8
+    assert lib.dsa_sparse_gqa_decode(ctypes.byref(g), 1, None, vp, vp, 64, vp, vp, vp, vp, vp, 1 << 20, None) == 1
+
+
+def test_empty_work_is_a_no_op(lib):
+    g = dsa.geometry()
+    assert lib.dsa_compress_regions(ctypes.byref(g), 0, None, 64, None, None, 1, None, None, None) == 0
+    assert lib.dsa_score_topk(ctypes.byref(g), 0, None, None, None, None, 1, None, None, 64, 8, None, None, None,
+                              None, 0, None) == 0
+    assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 0, None, None, None, 1, None, None, 64, None, None, None,
+                                      None) == 0
+
+
+def test_workspace_checks(lib):
+    g = dsa.geometry()
+    vp = ctypes.c_void_p(256)
+    need = lib.dsa_score_topk_workspace_size(ctypes.byref(g), 4, 1000)
+    assert need >= 4 * 4 * 1000 * 4
+    rc = lib.dsa_score_topk(ctypes.byref(g), 4, vp, vp, vp, vp, 1, vp, vp, 8000, 1000, vp, vp, None, vp, need - 1,
+                            None)
+    assert rc == 3
+    rc = lib.dsa_score_topk(ctypes.byref(g), 4, vp, vp, vp, vp, 1, vp, vp, 8000, 1000, vp, vp, None,
+                            ctypes.c_void_p(260), need, None)
+    assert rc == 1  # misaligned workspace
+    need = lib.dsa_sparse_gqa_workspace_size(ctypes.byref(g), 3)
+    rc = lib.dsa_sparse_gqa_decode(ctypes.byref(g), 3, vp, vp, vp, 64, vp, vp, vp, vp, vp, need - 1, None)
+    assert rc == 3
+
+
+def test_swa_window_must_be_512(lib):
+    g = dsa.geometry()
+    vp = ctypes.c_void_p(256)
+    assert lib.swa_attention(ctypes.byref(g), 256, 1, 1, vp, vp, vp, vp, vp, vp, vp, vp, vp, 1 << 20, None) == 2
+    assert lib.swa_ring_append(ctypes.byref(g), 1024, 1, 1, vp, vp, vp, vp, vp, vp, None) == 2

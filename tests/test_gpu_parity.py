@@ -1,0 +1,224 @@
+"""GPU vs oracle parity through the C ABI, at sizes the oracle finishes in seconds (several tiles,
+ragged tails, partial regions, short contexts, small top-k), plus determinism."""
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as gi
+import dsa_sparse_attention_amd as dsa
+import oracle as O
+
+import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+G, P, HQ, D = H.G, H.P, H.HQ, H.D
+
+
+def test_compress_bit_exact_in_two_calls():
+    seed = 0xC0
+    lens = [8192, 1003, 64, 7]
+    B, tcap = len(lens), 8192
+    R = tcap // 8
+    geom = dsa.geometry()
+    ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
+    summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
+    ends = np.array([L // 8 for L in lens], dtype=np.int32)
+    mids = ends // 2
+    dsa.dsa_compress_regions(geom, ik, tcap, H.i32(np.zeros(B)), H.i32(mids), R, summ, scale)
+    dsa.dsa_compress_regions(geom, ik, tcap, H.i32(mids), H.i32(ends), R, summ, scale)
+    torch.cuda.synchronize()
+    s = summ.cpu().numpy().reshape(B, G, R, P)
+    sc = scale.cpu().numpy().reshape(B, G, R)
+    for b, L in enumerate(lens):
+        nr = L // 8
+        ikh = gi.host_index_k(seed, tcap, G, P, b, 0, L)
+        codes, scales = O.compress_regions(ikh, 0, nr)
+        assert np.array_equal(s[b, :, :nr], codes[:nr].transpose(1, 0, 2))
+        assert np.array_equal(sc[b, :, :nr].view(np.uint32), scales[:nr].T.copy().view(np.uint32))
+        assert not s[b, :, nr:].any() and not sc[b, :, nr:].any()  # partial tail held back
+
+
+def test_compress_planted_bit_exact():
+    r = H.run_dsa_decode(0xC1, [4096, 4096], topk=64, planted=True)
+    H.assert_decode_parity(r)
+
+
+@pytest.mark.parametrize("lens,topk", [
+    ([8192], 512),                     # the 8K single-query decode workload
+    ([5003, 1000, 17, 1], 512),        # ragged: partial current regions, short contexts, p = 0
+    ([3000, 2047, 4096], 37),          # odd top-k (splits partially filled)
+    ([600, 4104], 1),                  # top-1: only the current region
+])
+def test_decode_end_to_end(lens, topk):
+    r = H.run_dsa_decode(0xD0 + len(lens) + topk, lens, topk=topk)
+    H.assert_decode_parity(r)
+
+
+def test_decode_attention_on_oracle_selection():
+    """Sparse GQA alone: the oracle's selection is fed to the GPU kernel, every head compared."""
+    seed = 0xD7
+    lens = [4096, 1001, 9]
+    r = H.run_dsa_decode(seed, lens, topk=512)
+    B, tcap, topk = len(lens), r["tcap"], 512
+    sel = np.full((B, G, topk), -1, dtype=np.int32)
+    nsel = np.zeros((B, G), dtype=np.int32)
+    for b in range(B):
+        sel[b] = r["oracle"][b]["sel"]
+        nsel[b] = r["oracle"][b]["nsel"]
+    out = torch.empty(B * HQ * D, dtype=H.BF16, device="cuda")
+    dsa.dsa_sparse_gqa_decode(r["dev"]["geom"], r["dev"]["q"], r["dev"]["K"], r["dev"]["V"], tcap,
+                              H.i32(lens), H.i32(sel.ravel()), H.i32(nsel.ravel()), out)
+    go = H.bf16_np(out).reshape(B, HQ, D)
+    for b in range(B):
+        H.assert_attn(go[b], r["oracle"][b]["out"], f"seq {b}")
+
+
+def _prefill(seed, seqs, topk=512, check_every=1):
+    """seqs: list of (P0, n) -- each sequence has a prefix of P0 tokens and a chunk of n new queries.
+    Queries of all sequences are interleaved to exercise mixed-sequence query blocks when len(seqs)>1."""
+    B = len(seqs)
+    tcap = H.round8(max(p0 + n for p0, n in seqs))
+    R = tcap // 8
+    geom = dsa.geometry(topk=topk)
+    ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
+    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_GROUP_MAJOR)
+    V = H.dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
+    summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
+    p0 = np.array([s[0] for s in seqs], dtype=np.int32)
+    end = np.array([s[0] + s[1] for s in seqs], dtype=np.int32)
+    dsa.dsa_compress_regions(geom, ik, tcap, H.i32(np.zeros(B)), H.i32(p0 // 8), R, summ, scale)  # prefix
+    dsa.dsa_compress_regions(geom, ik, tcap, H.i32(p0 // 8), H.i32(end // 8), R, summ, scale)  # in-chunk
+    qs, qp = [], []
+    for i in range(max(n for _, n in seqs)):
+        for b, (s0, n) in enumerate(seqs):
+            if i < n:
+                qs.append(b)
+                qp.append(s0 + i)
+    nq = len(qs)
+    q, iq, z = H.dev_queries(seed, nq)
+    sel = torch.empty(nq * G * topk, dtype=torch.int32, device="cuda")
+    nsel = torch.empty(nq * G, dtype=torch.int32, device="cuda")
+    scores = torch.full((nq * G * R,), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_score_topk(geom, iq, z, H.i32(qs), H.i32(qp), B, summ, scale, tcap, R, sel, nsel, scores_out=scores)
+    out = torch.empty(nq * HQ * D, dtype=H.BF16, device="cuda")
+    dsa.dsa_sparse_gqa_prefill(geom, q, H.i32(qs), H.i32(qp), B, K, V, tcap, sel, nsel, out)
+    torch.cuda.synchronize()
+    gsel = sel.cpu().numpy().reshape(nq, G, topk)
+    gnsel = nsel.cpu().numpy().reshape(nq, G)
+    gsc = scores.cpu().numpy().reshape(nq, G, R)
+    gout = H.bf16_np(out).reshape(nq, HQ, D)
+    hq, hiq, hz = H.host_queries(seed, nq)
+    host = {}
+    for b, (s0, n) in enumerate(seqs):
+        L = s0 + n
+        ikh = gi.host_index_k(seed, tcap, G, P, b, 0, L)
+        host[b] = (O.compress_regions(ikh, 0, L // 8), gi.host_tokens_bf16(seed, gi.TID_K, tcap, G, D, b, 0, L),
+                   gi.host_tokens_bf16(seed, gi.TID_V, tcap, G, D, b, 0, L))
+    n_same = n_tot = 0
+    osels = np.full((nq, G, topk), -1, dtype=np.int32)
+    onsel = np.zeros((nq, G), dtype=np.int32)
+    for i in range(0, nq, check_every):
+        b, p = qs[i], qp[i]
+        (codes, scales), Kh, Vh = host[b]
+        osel, on, oout, osc = O.dsa_query(hiq[i], hz[i], codes, scales, hq[i], Kh, Vh, p, k=topk, want_scores=True)
+        osels[i], onsel[i] = osel, on
+        c = p // 8
+        for g in range(G):
+            if c:
+                tol = 2e-5 * max(np.abs(osc[g]).max(), 1e-30)
+                assert np.all(np.abs(gsc[i, g, :c] - osc[g]) <= tol), f"query {i} group {g}: scores"
+            assert gnsel[i, g] == on[g]
+            same = H.check_selection(gsel[i, g, :gnsel[i, g]], osel[g, :on[g]], osc[g], c)
+            n_tot += 1
+            if same:
+                n_same += 1
+                H.assert_attn(gout[i, 16 * g:16 * g + 16], oout[16 * g:16 * g + 16], f"query {i} group {g}")
+    assert n_same >= 0.9 * n_tot, (n_same, n_tot)
+    # attention alone on the oracle's selection, every head
+    out2 = torch.empty(nq * HQ * D, dtype=H.BF16, device="cuda")
+    checked = list(range(0, nq, check_every))
+    dsa.dsa_sparse_gqa_prefill(geom, q, H.i32(qs), H.i32(qp), B, K, V, tcap, H.i32(osels.ravel()),
+                               H.i32(onsel.ravel()), out2)
+    g2 = H.bf16_np(out2).reshape(nq, HQ, D)
+    for i in checked:
+        b, p = qs[i], qp[i]
+        (codes, scales), Kh, Vh = host[b]
+        ref = O.attend(hq[i], Kh, Vh, p, [osels[i, g, :onsel[i, g]] for g in range(G)], k=topk)
+        H.assert_attn(g2[i], ref, f"query {i} on oracle selection")
+
+
+def test_prefill_chunk_one_sequence():
+    # prefix of 4003 tokens (partial region), 300 new queries: several 16-query blocks + a ragged one
+    _prefill(0xE0, [(4003, 300)], check_every=7)
+
+
+def test_prefill_mixed_sequences_and_small_topk():
+    _prefill(0xE1, [(2000, 40), (511, 37), (8, 20)], topk=100, check_every=3)
+
+
+def test_prefill_short_chunk_uses_decode_tiling():
+    _prefill(0xE2, [(1200, 20)], topk=512)
+
+
+@pytest.mark.parametrize("chunks", [[530, 40, 1], [1, 1, 1, 600], [700, 513, 3]])
+def test_swa_chunks_and_decode(chunks):
+    H.check_swa_sequence(0xF0 + sum(chunks), chunks, check_from=0, sample=48)
+
+
+def test_swa_batched_decode_with_prefilled_rings():
+    """Several sequences, one new token each, rings written directly by the generator."""
+    seed = 0xF5
+    pos = [0, 7, 300, 511, 512, 519, 5000]
+    S = len(pos)
+    T = max(pos) + 1
+    tq, tk, tv = H.swa_tids(0)
+    geom = dsa.geometry()
+    k_ring = torch.full((S * G * H.W * D,), float("nan"), dtype=H.BF16, device="cuda")
+    v_ring = torch.full((S * G * H.W * D,), float("nan"), dtype=H.BF16, device="cuda")
+    per = G * H.W * D
+    for s, p in enumerate(pos):
+        t0 = max(0, p - H.W)
+        if p > t0:
+            # write positions t0..p-1 of sequence s (logical batch index s) into its ring
+            for layout, ring, tid in ((gi.LAYOUT_GROUP_MAJOR, k_ring, tk), (gi.LAYOUT_REGION_T, v_ring, tv)):
+                tmp = torch.empty((s + 1) * per, dtype=H.BF16, device="cuda")
+                gi.dev_tokens(tmp.data_ptr(), H.stream_ptr(), seed, tid, s + 1, T, G, D, t0, p - t0, H.W, H.W,
+                              layout, 1.0)
+                ring[s * per:(s + 1) * per] = tmp[s * per:(s + 1) * per]
+    rows = []
+    q = torch.empty(S * HQ * D, dtype=H.BF16, device="cuda")
+    kn = torch.empty(S * G * D, dtype=H.BF16, device="cuda")
+    vn = torch.empty(S * G * D, dtype=H.BF16, device="cuda")
+    for s, p in enumerate(pos):
+        gi.dev_flat(q[s * HQ * D:].data_ptr(), H.stream_ptr(), seed, tq, HQ * D, 0, 1.0, start=(s * T + p) * HQ * D)
+        tmpk = H.dev_cache(seed, tk, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=1)
+        tmpv = H.dev_cache(seed, tv, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=1)
+        kn[s * G * D:(s + 1) * G * D] = tmpk[s * G * D:(s + 1) * G * D]
+        vn[s * G * D:(s + 1) * G * D] = tmpv[s * G * D:(s + 1) * G * D]
+    out = torch.empty(S * HQ * D, dtype=H.BF16, device="cuda")
+    dsa.swa_attention(geom, H.W, 1, H.i32(pos), H.i32(np.arange(S + 1)), q, kn, vn, k_ring, v_ring, out)
+    torch.cuda.synchronize()
+    go = H.bf16_np(out).reshape(S, HQ, D)
+    for s, p in enumerate(pos):
+        Kh = gi.host_tokens_bf16(seed, tk, T, G, D, s, 0, p + 1)
+        Vh = gi.host_tokens_bf16(seed, tv, T, G, D, s, 0, p + 1)
+        hq = gi.host_normal_bf16(seed, tq, HQ * D, 1.0, start=(s * T + p) * HQ * D).reshape(HQ, D)
+        H.assert_attn(go[s], O.swa(hq, Kh, Vh, p, H.W), f"seq {s} at {p}")
+    # the append then leaves each ring holding positions p-511..p
+    dsa.swa_ring_append(geom, H.W, 1, H.i32(pos), H.i32(np.arange(S + 1)), kn, vn, k_ring, v_ring)
+    torch.cuda.synchronize()
+    kr = k_ring.view(torch.int16).cpu().numpy().reshape(S, G, H.W, D).view(np.uint16)
+    for s, p in enumerate(pos):
+        Kh = gi.host_tokens_bf16(seed, tk, T, G, D, s, 0, p + 1)
+        for t in range(max(0, p - H.W + 1), p + 1):
+            assert np.array_equal(kr[s, :, t % H.W, :], Kh[t])
+
+
+def test_decode_is_deterministic():
+    a = H.run_dsa_decode(0xAA, [6000, 3001], topk=512, check_seqs=[])
+    b = H.run_dsa_decode(0xAA, [6000, 3001], topk=512, check_seqs=[])
+    for k in ("summ", "scale", "sel", "nsel", "out"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
