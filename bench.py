@@ -1,0 +1,417 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA sparse-attention layer on one MI355X.
+
+Headline: DSA decode queries/s at a 1,048,576-token context (batch 4, top-512, planted low-rank
+bias on 2% of regions), one step = compress the region the query token completes -> indexer
+score + top-512 selection -> sparse GQA over the selected regions, inputs resident in HBM.
+Also measured in the same run: prefill tokens/s of a 2048-token chunk appended to a 63,488-token
+prefix (64K total).  Each figure carries the roofline of its dominant kernel (bytes or flops the
+method needs / the kernel's average hipEvent-timed duration, against the MI355X peak) and the
+CPU oracle's rate on a bounded sample of the same work.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu] [--profile-run]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+G, P, HI, HQ, D, REG, TOPK = 4, 256, 16, 64, 192, 8, 512
+
+DECODE = dict(name="DSA decode, batch 4, 1,048,576-token context, top-512, planted bias on 2% of regions",
+              batch=4, context=1048576, topk=TOPK, planted=True, seed_index=3)
+PREFILL = dict(name="DSA chunked prefill, 2048 new tokens after a 63,488-token prefix (64K), top-512",
+               prefix=63488, chunk=2048, topk=TOPK, seed_index=2)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# algorithmic work (bytes / flops the method needs; implementation scratch traffic is not counted)
+# ------------------------------------------------------------------------------------------------
+def decode_bytes(B, L, topk):
+    """Per decode step.  compress: 8 index_k rows x 4 groups in, codes+scales out; score: every
+    candidate region's 4 group summaries (256 B codes + 4 B scale each) + the query's index_q/z;
+    select: the selection out; attention: K and V of the selected tokens + q in + out."""
+    R = L // REG
+    compress = B * (REG * G * P * 2 + G * (P + 4))
+    score = B * ((R - 1) * G * (P + 4) + HI * P * 2 + HI * 4)
+    select = B * G * (topk + 1) * 4
+    tokens = min(topk, R) * REG  # L % 8 == 0: every selected region is complete
+    attend = B * (G * tokens * D * 2 * 2 + HQ * D * 2 * 2)
+    return dict(compress=compress, score=score, select=select, attend=attend,
+                total=compress + score + select + attend)
+
+
+def prefill_flops(prefix, chunk, topk):
+    """Per chunk: indexer dot products (4 heads x 256 channels per candidate region and group) and
+    sparse attention (QK^T and PV over the attended tokens, 16 heads per group)."""
+    score = attend = 0
+    for p in range(prefix, prefix + chunk):
+        c = p // REG
+        score += c * G * 4 * P * 2
+        tokens = min(topk - 1, c) * REG + (p % REG + 1)
+        attend += G * tokens * 16 * D * 2 * 2
+    return dict(score=score, attend=attend, total=score + attend)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "dsa_sparse_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload_key, src_hash):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/<kernel>__<workload>.md holds
+    a line 'traffic_json: {...}'); None if absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload_key}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path, encoding="utf-8"):
+        if line.startswith("traffic_json:"):
+            d = json.loads(line.split(":", 1)[1])
+            if d.get("source_hash") != src_hash:
+                return None
+            return d.get("bytes_per_launch")
+    return None
+
+
+# ------------------------------------------------------------------------------------------------
+class Calls:
+    """Pre-marshalled C-ABI calls (argument checks done once by the binding's conventions)."""
+
+    def __init__(self, dsa):
+        self.L = dsa.load()
+
+    @staticmethod
+    def p(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+
+def setup_decode(cfg, steps_hint=1):
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+
+    B, Lc, topk = cfg["batch"], cfg["context"], cfg["topk"]
+    tcap, R = Lc, Lc // REG
+    seed = gi.SEED_BASE + cfg["seed_index"]
+    s = torch.cuda.current_stream().cuda_stream
+    geom = dsa.geometry(topk=topk)
+    t0 = time.time()
+    ik = torch.empty(B * G * tcap * P, dtype=torch.bfloat16, device="cuda")
+    K = torch.empty(B * G * tcap * D, dtype=torch.bfloat16, device="cuda")
+    V = torch.empty(B * G * tcap * D, dtype=torch.bfloat16, device="cuda")
+    gi.dev_tokens(ik.data_ptr(), s, seed, gi.TID_IK, B, tcap, G, P, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR,
+                  gi.IK_SCALE, cfg["planted"])
+    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR)
+    gi.dev_tokens(V.data_ptr(), s, seed, gi.TID_V, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_REGION_T)
+    q = torch.empty(B * HQ * D, dtype=torch.bfloat16, device="cuda")
+    iq = torch.empty(B * HI * P, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(B * HI, dtype=torch.float32, device="cuda")
+    gi.dev_flat(q.data_ptr(), s, seed, gi.TID_Q, q.numel(), 0, 1.0)
+    gi.dev_flat(iq.data_ptr(), s, seed, gi.TID_IQ, iq.numel(), 0, gi.IK_SCALE)
+    gi.dev_flat(z.data_ptr(), s, seed, gi.TID_Z, z.numel(), 1)
+    summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device="cuda")
+    # untimed: summaries of every region before the one the query token completes
+    dsa.dsa_compress_regions(geom, ik, tcap, i32([0] * B), i32([R - 1] * B), R - 1, summ, scale)
+    torch.cuda.synchronize()
+    log(f"decode setup: {time.time() - t0:.1f}s")
+    rb, re_ = i32([R - 1] * B), i32([R] * B)
+    qseq, qpos, slen = i32(list(range(B))), i32([Lc - 1] * B), i32([Lc] * B)
+    sel = torch.empty(B * G * topk, dtype=torch.int32, device="cuda")
+    nsel = torch.empty(B * G, dtype=torch.int32, device="cuda")
+    out = torch.empty(B * HQ * D, dtype=torch.bfloat16, device="cuda")
+    ws1 = dsa.workspace(dsa.dsa_score_topk_workspace_size(geom, B, R))
+    ws2 = dsa.workspace(dsa.dsa_sparse_gqa_workspace_size(geom, B))
+    L = dsa.load()
+    p = Calls.p
+    gp = ctypes.byref(geom)
+    st = ctypes.c_void_p(s)
+    a_comp = (gp, B, p(ik), tcap, p(rb), p(re_), 1, p(summ), p(scale), st)
+    a_score = (gp, B, p(iq), p(z), p(qseq), p(qpos), B, p(summ), p(scale), tcap, R, p(sel), p(nsel), None,
+               p(ws1), ws1.numel(), st)
+    a_attn = (gp, B, p(q), p(K), p(V), tcap, p(slen), p(sel), p(nsel), p(out), p(ws2), ws2.numel(), st)
+
+    def step():
+        rc = L.dsa_compress_regions(*a_comp) or L.dsa_score_topk(*a_score) or L.dsa_sparse_gqa_decode(*a_attn)
+        if rc:
+            raise RuntimeError(f"decode step failed: {rc} {L.dsa_last_error().decode()}")
+
+    keep = (ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, slen, sel, nsel, out, ws1, ws2, geom)
+    return step, keep
+
+
+def setup_prefill(cfg):
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+
+    P0, n, topk = cfg["prefix"], cfg["chunk"], cfg["topk"]
+    Lc = P0 + n
+    tcap, R = Lc, Lc // REG
+    seed = gi.SEED_BASE + cfg["seed_index"]
+    s = torch.cuda.current_stream().cuda_stream
+    geom = dsa.geometry(topk=topk)
+    ik = torch.empty(G * tcap * P, dtype=torch.bfloat16, device="cuda")
+    K = torch.empty(G * tcap * D, dtype=torch.bfloat16, device="cuda")
+    V = torch.empty(G * tcap * D, dtype=torch.bfloat16, device="cuda")
+    gi.dev_tokens(ik.data_ptr(), s, seed, gi.TID_IK, 1, tcap, G, P, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR,
+                  gi.IK_SCALE)
+    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, 1, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR)
+    gi.dev_tokens(V.data_ptr(), s, seed, gi.TID_V, 1, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_REGION_T)
+    q = torch.empty(n * HQ * D, dtype=torch.bfloat16, device="cuda")
+    iq = torch.empty(n * HI * P, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(n * HI, dtype=torch.float32, device="cuda")
+    gi.dev_flat(q.data_ptr(), s, seed, gi.TID_Q, q.numel(), 0, 1.0)
+    gi.dev_flat(iq.data_ptr(), s, seed, gi.TID_IQ, iq.numel(), 0, gi.IK_SCALE)
+    gi.dev_flat(z.data_ptr(), s, seed, gi.TID_Z, z.numel(), 1)
+    summ = torch.zeros(G * R * P, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(G * R, dtype=torch.float32, device="cuda")
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device="cuda")
+    dsa.dsa_compress_regions(geom, ik, tcap, i32([0]), i32([P0 // REG]), P0 // REG, summ, scale)  # prefix
+    torch.cuda.synchronize()
+    rb, re_ = i32([P0 // REG]), i32([Lc // REG])
+    span = Lc // REG - P0 // REG
+    qseq, qpos = i32([0] * n), i32(list(range(P0, Lc)))
+    sel = torch.empty(n * G * topk, dtype=torch.int32, device="cuda")
+    nsel = torch.empty(n * G, dtype=torch.int32, device="cuda")
+    out = torch.empty(n * HQ * D, dtype=torch.bfloat16, device="cuda")
+    ws1 = dsa.workspace(dsa.dsa_score_topk_workspace_size(geom, n, R))
+    L = dsa.load()
+    p = Calls.p
+    gp = ctypes.byref(geom)
+    st = ctypes.c_void_p(s)
+    a_comp = (gp, 1, p(ik), tcap, p(rb), p(re_), span, p(summ), p(scale), st)
+    a_score = (gp, n, p(iq), p(z), p(qseq), p(qpos), 1, p(summ), p(scale), tcap, R, p(sel), p(nsel), None,
+               p(ws1), ws1.numel(), st)
+    a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, p(K), p(V), tcap, p(sel), p(nsel), p(out), st)
+
+    def step():
+        rc = L.dsa_compress_regions(*a_comp) or L.dsa_score_topk(*a_score) or L.dsa_sparse_gqa_prefill(*a_attn)
+        if rc:
+            raise RuntimeError(f"prefill step failed: {rc} {L.dsa_last_error().decode()}")
+
+    keep = (ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, sel, nsel, out, ws1, geom)
+    return step, keep
+
+
+def timed(step, steps, warmup, kernels):
+    """Runs warmup steps, then exactly `steps` steps between two synchronisations with the
+    library's per-kernel hipEvents on.  Returns (seconds, {kernel: (avg_ms, launches)})."""
+    import torch
+    import dsa_sparse_attention_amd as dsa
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    dsa.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stats = {}
+    for k in kernels:
+        ms, n = dsa.profile_kernel_stats(k)
+        stats[k] = (ms / max(n, 1), n)
+    dsa.profile_enable(False)
+    return t1 - t0, stats
+
+
+def cpu_baseline_decode(cfg, budget_s=15.0):
+    """The oracle on the host cores: one decode query of sequence 0 of the 1M workload (compress the
+    completed region, score all 131,071 candidate regions x 4 groups, top-512, sparse GQA), repeated
+    until about budget_s of CPU time.  The prefix summaries are built untimed, as on the GPU."""
+    import numpy as np
+    import dsa_inputs as gi
+    import oracle as O
+
+    B, Lc, topk = cfg["batch"], cfg["context"], cfg["topk"]
+    R = Lc // REG
+    seed = gi.SEED_BASE + cfg["seed_index"]
+    t0 = time.time()
+    ik = gi.host_index_k(seed, Lc, G, P, 0, 0, Lc, cfg["planted"])
+    K = gi.host_tokens_bf16(seed, gi.TID_K, Lc, G, D, 0, 0, Lc)
+    V = gi.host_tokens_bf16(seed, gi.TID_V, Lc, G, D, 0, 0, Lc)
+    q = gi.host_normal_bf16(seed, gi.TID_Q, HQ * D).reshape(HQ, D)
+    iq = gi.host_normal_bf16(seed, gi.TID_IQ, HI * P, gi.IK_SCALE).reshape(HI, P)
+    z = gi.host_uniform_f32(seed, gi.TID_Z, HI)
+    codes, scales = O.compress_regions(ik, 0, R - 1, np.zeros((R, G, P), np.uint8), np.zeros((R, G), np.float32))
+    log(f"cpu baseline setup: {time.time() - t0:.1f}s")
+    n = 0
+    t1 = time.perf_counter()
+    while True:
+        O.compress_regions(ik, R - 1, R, codes, scales)
+        O.dsa_query(iq, z, codes, scales, q, K, V, Lc - 1, k=topk)
+        n += 1
+        el = time.perf_counter() - t1
+        if el >= budget_s or n >= 200:
+            break
+    return dict(value=n / el, unit="queries/s", cores=O.num_threads(), kind="oracle",
+                sample=f"{n} decode queries of one sequence at {Lc} tokens (compress 1 region, score {R - 1} "
+                       f"regions x 4 groups, top-{topk}, sparse GQA), fp64 C with OpenMP; prefix summaries untimed")
+
+
+def cpu_baseline_prefill(cfg, n_queries=24):
+    """The oracle on a bounded sample of the 64K prefill chunk: compress the chunk's complete regions,
+    then n_queries evenly spaced chunk queries end to end."""
+    import numpy as np
+    import dsa_inputs as gi
+    import oracle as O
+
+    P0, n, topk = cfg["prefix"], cfg["chunk"], cfg["topk"]
+    Lc = P0 + n
+    R = Lc // REG
+    seed = gi.SEED_BASE + cfg["seed_index"]
+    ik = gi.host_index_k(seed, Lc, G, P, 0, 0, Lc)
+    K = gi.host_tokens_bf16(seed, gi.TID_K, Lc, G, D, 0, 0, Lc)
+    V = gi.host_tokens_bf16(seed, gi.TID_V, Lc, G, D, 0, 0, Lc)
+    q = gi.host_normal_bf16(seed, gi.TID_Q, n * HQ * D).reshape(n, HQ, D)
+    iq = gi.host_normal_bf16(seed, gi.TID_IQ, n * HI * P, gi.IK_SCALE).reshape(n, HI, P)
+    z = gi.host_uniform_f32(seed, gi.TID_Z, n * HI).reshape(n, HI)
+    codes, scales = O.compress_regions(ik, 0, P0 // REG, np.zeros((R, G, P), np.uint8), np.zeros((R, G), np.float32))
+    qs = np.linspace(0, n - 1, n_queries).astype(int)
+    t1 = time.perf_counter()
+    O.compress_regions(ik, P0 // REG, R, codes, scales)
+    for i in qs:
+        O.dsa_query(iq[i], z[i], codes, scales, q[i], K, V, P0 + int(i), k=topk)
+    el = time.perf_counter() - t1
+    return dict(value=len(qs) / el, unit="tokens/s", cores=O.num_threads(), kind="oracle",
+                sample=f"{len(qs)} of the {n} chunk queries (evenly spaced) end to end, after compressing the "
+                       f"chunk's {R - P0 // REG} complete regions; fp64 C with OpenMP")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="setup + a few steps of each workload + a 1 GiB copy kernel, for rocprofv3")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only: the DSA layer here runs on a single MI355X "
+              f"(requested --gpus {args.gpus}); multi-GPU sharding is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dsa_sparse_attention_amd as dsa
+
+    torch.cuda.set_device(0)
+    dsa.load()
+
+    if args.profile_run:
+        step, keep = setup_decode(DECODE)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        del keep
+        if not args.no_prefill:
+            step, keep = setup_prefill(PREFILL)
+            for _ in range(2):
+                step()
+            torch.cuda.synchronize()
+            del keep
+        # calibration: a plain copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("profile run done")
+        return
+
+    # ---- decode at 1M
+    step, keep = setup_decode(DECODE)
+    kn = ["k_compress", "k_fill_u32", "k_score_decode", "k_select", "k_sgqa_decode", "k_sgqa_merge"]
+    secs, st = timed(step, args.steps, args.warmup, kn)
+    del keep
+    torch.cuda.empty_cache()
+    B, Lc = DECODE["batch"], DECODE["context"]
+    ms_step = secs * 1e3 / args.steps
+    qps = B * args.steps / secs
+    byt = decode_bytes(B, Lc, DECODE["topk"])
+    score_ms = st["k_score_decode"][0]
+    achieved = byt["score"] / (score_ms * 1e-3) / 1e9
+    src = source_hash("score_topk.hip")
+    traffic = load_traffic("k_score_decode", "decode_b4_1m", src)
+    result = {
+        "metric": "DSA layer decode queries/s @1M ctx + prefill tok/s @64K, % HBM/MFMA roofline",
+        "value": round(qps, 2), "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": DECODE["name"], "batch": B, "context_tokens": Lc, "topk": DECODE["topk"],
+                   "regions_per_sequence": Lc // REG},
+        "roofline": {"bound": "hbm", "kernel": "k_score_decode", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": byt["score"],
+                     "avg_launch_us": round(score_ms * 1e3, 2)},
+        "step_hbm": {"algorithmic_bytes": byt["total"],
+                     "achieved_GBs": round(byt["total"] / (ms_step * 1e-3) / 1e9, 1),
+                     "frac": round(byt["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in st.items()},
+    }
+    log(f"decode: {qps:.1f} q/s, {ms_step:.3f} ms/step, score kernel {achieved:.0f} GB/s")
+
+    # ---- prefill at 64K
+    if not args.no_prefill:
+        step, keep = setup_prefill(PREFILL)
+        kp = ["k_compress", "k_score_prefill", "k_select", "k_sgqa_prefill"]
+        psteps = max(3, args.steps // 3)
+        psecs, pst = timed(step, psteps, max(1, args.warmup // 2), kp)
+        del keep
+        torch.cuda.empty_cache()
+        n = PREFILL["chunk"]
+        fl = prefill_flops(PREFILL["prefix"], n, PREFILL["topk"])
+        pms = psecs * 1e3 / psteps
+        att_ms, sc_ms = pst["k_sgqa_prefill"][0], pst["k_score_prefill"][0]
+        att_tf = fl["attend"] / (att_ms * 1e-3) / 1e12
+        sc_tf = fl["score"] / (sc_ms * 1e-3) / 1e12
+        step_tf = fl["total"] / (pms * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": PREFILL["name"], "value": round(n * psteps / psecs, 1), "unit": "tokens/s",
+            "steps": psteps, "ms_per_step": round(pms, 3),
+            "roofline": {"bound": "mfma", "kernel": "k_sgqa_prefill", "achieved": round(att_tf, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": load_traffic("k_sgqa_prefill", "prefill_64k", source_hash("attention.hip")),
+                         "algorithmic_flops_per_launch": fl["attend"], "avg_launch_us": round(att_ms * 1e3, 1)},
+            "score_kernel": {"kernel": "k_score_prefill", "achieved_TFLOPs": round(sc_tf, 2),
+                             "frac": round(sc_tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl["score"],
+                             "avg_launch_us": round(sc_ms * 1e3, 1)},
+            "step_mfma": {"algorithmic_flops": fl["total"], "achieved_TFLOPs": round(step_tf, 2),
+                          "frac": round(step_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in pst.items()},
+        }
+        log(f"prefill: {n * psteps / psecs:.0f} tok/s, {pms:.3f} ms/step")
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_decode(DECODE)
+        if "prefill" in result:
+            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(PREFILL)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

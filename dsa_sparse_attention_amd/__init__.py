@@ -27,6 +27,7 @@ ENTRY_POINTS = [
     "dsa_compress_regions", "dsa_score_topk_workspace_size", "dsa_score_topk",
     "dsa_sparse_gqa_workspace_size", "dsa_sparse_gqa_decode", "dsa_sparse_gqa_prefill",
     "swa_attention_workspace_size", "swa_attention", "swa_ring_append",
+    "dsa_profile_enable", "dsa_profile_kernel_stats",
 ]
 
 
@@ -73,6 +74,9 @@ def load() -> ctypes.CDLL:
     L.swa_attention_workspace_size.restype = sz
     L.swa_attention.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.swa_ring_append.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.dsa_profile_enable.argtypes = [ctypes.c_int]
+    L.dsa_profile_kernel_stats.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int32)]
     for name in ENTRY_POINTS:
         f = getattr(L, name)
         if f.restype is ctypes.c_int:  # default
@@ -272,6 +276,18 @@ def swa_ring_append(geom, window, max_new_per_seq, seq_pos0, seq_row0, k_new, v_
     _check(load().swa_ring_append(ctypes.byref(geom), window, n_seqs, max_new_per_seq, _ptr(seq_pos0),
                                   _ptr(seq_row0), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
                                   _stream(stream)))
+
+
+def profile_enable(on: bool = True):
+    """Starts (clearing earlier records) or stops per-kernel hipEvent timing inside the library."""
+    _check(load().dsa_profile_enable(1 if on else 0))
+
+
+def profile_kernel_stats(kernel: str):
+    """(total milliseconds, launches) of one kernel since profile_enable(True); waits for its events."""
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    _check(load().dsa_profile_kernel_stats(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def default_softmax_scale() -> float:

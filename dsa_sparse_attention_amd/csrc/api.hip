@@ -1,7 +1,11 @@
 // Host-side plumbing of the C ABI: geometry, status strings, error reporting.
 #include <math.h>
+#include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "common.hpp"
 
@@ -35,9 +39,82 @@ dsa_status check_launch(const char* what) {
   return DSA_OK;
 }
 
+// ---- instrumentation ----
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+  bool done;
+};
+static std::atomic<bool> g_prof_on{false};
+static std::mutex g_prof_mu;
+static std::vector<ProfRec> g_prof_recs;
+static std::vector<hipEvent_t> g_prof_pool;
+constexpr size_t kProfMaxRecs = 8192;
+
+static hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : rec(-1), stream(s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_recs.size() >= kProfMaxRecs) return;
+  ProfRec r{name, prof_event(), prof_event(), false};
+  if (!r.a || !r.b || hipEventRecord(r.a, s) != hipSuccess) return;
+  g_prof_recs.push_back(r);
+  rec = (int)g_prof_recs.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+  if (rec < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if ((size_t)rec < g_prof_recs.size() && hipEventRecord(g_prof_recs[rec].b, stream) == hipSuccess)
+    g_prof_recs[rec].done = true;
+}
+
 }  // namespace dsa
 
 extern "C" {
+
+dsa_status dsa_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(dsa::g_prof_mu);
+  for (auto& r : dsa::g_prof_recs) {
+    (void)hipEventSynchronize(r.b);
+    dsa::g_prof_pool.push_back(r.a);
+    dsa::g_prof_pool.push_back(r.b);
+  }
+  dsa::g_prof_recs.clear();
+  dsa::g_prof_on.store(on != 0);
+  return DSA_OK;
+}
+
+dsa_status dsa_profile_kernel_stats(const char* kernel, double* total_ms, int32_t* launches) {
+  if (!kernel || !total_ms || !launches)
+    return dsa::fail(DSA_ERR_INVALID_ARGUMENT, "dsa_profile_kernel_stats: NULL pointer");
+  std::lock_guard<std::mutex> lk(dsa::g_prof_mu);
+  double tot = 0.0;
+  int32_t n = 0;
+  for (auto& r : dsa::g_prof_recs) {
+    if (!r.done || strcmp(r.name, kernel) != 0) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return dsa::fail(DSA_ERR_HIP, "event synchronize failed");
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return dsa::fail(DSA_ERR_HIP, "event elapsed failed");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return DSA_OK;
+}
 
 dsa_status dsa_geometry_default(dsa_geometry* g) {
   if (!g) return dsa::fail(DSA_ERR_INVALID_ARGUMENT, "geometry pointer is NULL");

@@ -500,10 +500,16 @@ extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t ba
   a.part = (float*)workspace; a.tcap = tcap; a.topk = geom->topk; a.nsplit = nsplit_of(geom->topk);
   a.scale_log2 = geom->softmax_scale * kLog2e;
   hipStream_t s = as_stream(stream);
-  hipLaunchKernelGGL(k_sgqa_decode, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
+  {
+    ProfScope prof_("k_sgqa_decode", s);
+    hipLaunchKernelGGL(k_sgqa_decode, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
+  }
   st = check_launch("dsa_sparse_gqa_decode");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(k_sgqa_merge, dim3(kGroups, batch), dim3(256), 0, s, (const float*)workspace, out, a.nsplit);
+  {
+    ProfScope prof_("k_sgqa_merge", s);
+    hipLaunchKernelGGL(k_sgqa_merge, dim3(kGroups, batch), dim3(256), 0, s, (const float*)workspace, out, a.nsplit);
+  }
   return check_launch("dsa_sparse_gqa_decode: merge");
 }
 
@@ -524,7 +530,10 @@ extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n
   a.q = q; a.qseq = q_seq; a.qpos = q_pos; a.k = k_cache; a.v = v_cache; a.sel = sel; a.nsel = n_sel;
   a.out = out; a.tcap = tcap; a.nq = n_queries; a.n_seqs = n_seqs; a.topk = geom->topk;
   a.scale_log2 = geom->softmax_scale * kLog2e;
-  hipLaunchKernelGGL(k_sgqa_prefill, dim3(n_queries), dim3(256), 0, as_stream(stream), a);
+  {
+    ProfScope prof_("k_sgqa_prefill", as_stream(stream));
+    hipLaunchKernelGGL(k_sgqa_prefill, dim3(n_queries), dim3(256), 0, as_stream(stream), a);
+  }
   return check_launch("dsa_sparse_gqa_prefill");
 }
 
@@ -571,10 +580,16 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   a.st_k = (uint16_t*)workspace;
   a.st_v = (uint16_t*)((char*)workspace + (one + 255) / 256 * 256);
   hipStream_t s = as_stream(stream);
-  hipLaunchKernelGGL(k_swa_stage, dim3(a.nst, n_seqs), dim3(256), 0, s, a);
+  {
+    ProfScope prof_("k_swa_stage", s);
+    hipLaunchKernelGGL(k_swa_stage, dim3(a.nst, n_seqs), dim3(256), 0, s, a);
+  }
   st = check_launch("swa_attention: stage");
   if (st != DSA_OK) return st;
-  hipLaunchKernelGGL(k_swa_attend, dim3(max_new_per_seq, n_seqs), dim3(256), 0, s, a);
+  {
+    ProfScope prof_("k_swa_attend", s);
+    hipLaunchKernelGGL(k_swa_attend, dim3(max_new_per_seq, n_seqs), dim3(256), 0, s, a);
+  }
   return check_launch("swa_attention");
 }
 
@@ -591,7 +606,10 @@ extern "C" dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, 
   a.pos0 = seq_pos0; a.row0 = seq_row0; a.k_new = k_new; a.v_new = v_new;
   a.n_seqs = n_seqs; a.max_new = max_new_per_seq; a.window = window;
   a.rows = (int64_t)n_seqs * max_new_per_seq;
-  hipLaunchKernelGGL(k_ring_append, dim3(max_new_per_seq, n_seqs), dim3(256), 0, as_stream(stream), a,
-                     k_ring, v_ring);
+  {
+    ProfScope prof_("k_ring_append", as_stream(stream));
+    hipLaunchKernelGGL(k_ring_append, dim3(max_new_per_seq, n_seqs), dim3(256), 0, as_stream(stream), a,
+                       k_ring, v_ring);
+  }
   return check_launch("swa_ring_append");
 }

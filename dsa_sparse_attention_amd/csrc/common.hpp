@@ -63,4 +63,14 @@ dsa_status fail(dsa_status s, const std::string& msg);
 dsa_status check_geometry(const dsa_geometry* g);
 dsa_status check_launch(const char* what);
 inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Instrumentation: while enabled (dsa_profile_enable), a ProfScope brackets
+// the kernel launched inside its lifetime with two hipEvents on the launch
+// stream; dsa_profile_kernel_stats sums the intervals per kernel name.
+struct ProfScope {
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  int rec;
+  hipStream_t stream;
+};
 }  // namespace dsa

@@ -120,8 +120,11 @@ extern "C" dsa_status dsa_compress_regions(const dsa_geometry* geom, int32_t bat
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_compress_regions: NULL pointer");
   if (max_span > tcap / kRegion) max_span = (int32_t)(tcap / kRegion);
   if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, "dsa_compress_regions: batch > 65535");
-  hipLaunchKernelGGL(k_compress, dim3(max_span, batch), dim3(256), 0, as_stream(stream), index_k,
-                     tcap, region_begin, region_end, max_span, summ, scale);
+  {
+    ProfScope prof_("k_compress", as_stream(stream));
+    hipLaunchKernelGGL(k_compress, dim3(max_span, batch), dim3(256), 0, as_stream(stream), index_k,
+                       tcap, region_begin, region_end, max_span, summ, scale);
+  }
   return check_launch("dsa_compress_regions");
 }
 
@@ -140,7 +143,10 @@ extern "C" dsa_status dsa_cache_write(const dsa_geometry* geom, int32_t n_tokens
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: NULL pointer");
   if ((ik_new == nullptr) != (ik_cache == nullptr))
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: ik_new and ik_cache must both be set or both NULL");
-  hipLaunchKernelGGL(k_cache_write, dim3(n_tokens), dim3(256), 0, as_stream(stream), tok_seq, tok_pos,
-                     k_new, v_new, ik_new, k_cache, v_cache, ik_cache, n_seqs, tcap);
+  {
+    ProfScope prof_("k_cache_write", as_stream(stream));
+    hipLaunchKernelGGL(k_cache_write, dim3(n_tokens), dim3(256), 0, as_stream(stream), tok_seq, tok_pos,
+                       k_new, v_new, ik_new, k_cache, v_cache, ik_cache, n_seqs, tcap);
+  }
   return check_launch("dsa_cache_write");
 }

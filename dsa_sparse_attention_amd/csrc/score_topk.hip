@@ -471,10 +471,19 @@ extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries
   if (decode_shape) {
     int64_t fill_blocks = (hist_n + 255) / 256;
     if (fill_blocks > 4096) fill_blocks = 4096;
-    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)fill_blocks), dim3(256), 0, s, hist, hist_n, 0u);
-    hipLaunchKernelGGL(k_score<1>, dim3(ranges, kGroups, n_queries), dim3(256), 0, s, sa);
+    {
+      ProfScope prof_("k_fill_u32", s);
+      hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)fill_blocks), dim3(256), 0, s, hist, hist_n, 0u);
+    }
+    {
+      ProfScope prof_("k_score_decode", s);
+      hipLaunchKernelGGL(k_score<1>, dim3(ranges, kGroups, n_queries), dim3(256), 0, s, sa);
+    }
   } else {
-    hipLaunchKernelGGL(k_score<16>, dim3(ranges, kGroups, (n_queries + 15) / 16), dim3(256), 0, s, sa);
+    {
+      ProfScope prof_("k_score_prefill", s);
+      hipLaunchKernelGGL(k_score<16>, dim3(ranges, kGroups, (n_queries + 15) / 16), dim3(256), 0, s, sa);
+    }
   }
   st = check_launch("dsa_score_topk: score");
   if (st != DSA_OK) return st;
@@ -483,6 +492,9 @@ extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries
   se.scores = scores; se.hist = decode_shape ? hist : nullptr; se.qpos = q_pos; se.sel = sel;
   se.nsel = n_sel; se.R = tcap / kRegion; se.nq = n_queries; se.max_regions = max_regions;
   se.ws_stride = stride; se.topk = geom->topk;
-  hipLaunchKernelGGL(k_select, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(kSelThreads), 0, s, se);
+  {
+    ProfScope prof_("k_select", s);
+    hipLaunchKernelGGL(k_select, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(kSelThreads), 0, s, se);
+  }
   return check_launch("dsa_score_topk: select");
 }

@@ -23,7 +23,8 @@
  *    enqueues work and returns; it never synchronises.
  *  - Ownership: the caller allocates and owns every buffer, caches and
  *    workspaces included.  The library allocates no device memory, keeps no
- *    pointer after a call returns, and holds no global device state.
+ *    pointer after a call returns, and holds no global device state (the
+ *    optional instrumentation below keeps host-side event records only).
  *  - Errors: argument checks run on the host before any launch and return a
  *    status without touching memory; a failed launch returns DSA_ERR_HIP.
  *    dsa_last_error() gives a message for the calling thread's last failure.
@@ -212,7 +213,9 @@ size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, in
  *                    seq_row0[s] .. seq_row0[s+1]-1 (n_s = the difference)
  *   max_new_per_seq  host bound on n_s (grid, workspace)
  *   seq_pos0 [n_seqs], seq_row0 [n_seqs+1] int32 device
- *   q [rows][64][D], k_new/v_new [rows][G][D] bf16, out [rows][64][D] bf16
+ *   q [rows][64][D], k_new/v_new [rows][G][D] bf16, out [rows][64][D] bf16,
+ *                    rows <= n_seqs*max_new_per_seq (kernels clamp row indices
+ *                    to that bound, so the arrays must hold that many rows)
  *   k_ring, v_ring   the ring of each sequence BEFORE this call's tokens are
  *                    appended: it holds positions seq_pos0[s]-W .. seq_pos0[s]-1
  *                    (those >= 0) in slots t mod W
@@ -235,6 +238,21 @@ dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_s
                            int32_t max_new_per_seq, const int32_t* seq_pos0,
                            const int32_t* seq_row0, const uint16_t* k_new, const uint16_t* v_new,
                            uint16_t* k_ring, uint16_t* v_ring, void* stream);
+
+/*
+ * Instrumentation (not part of the layer's maths).  While enabled, every
+ * kernel the library launches outside stream capture is bracketed by two
+ * hipEvents recorded on its launch stream.  dsa_profile_enable(on) drops
+ * earlier records (waiting for them) and switches recording on or off;
+ * dsa_profile_kernel_stats waits for the recorded events of one kernel and
+ * returns the summed interval (ms) and the number of launches.  Kernel
+ * names: k_compress, k_cache_write, k_fill_u32, k_score_decode,
+ * k_score_prefill, k_select, k_sgqa_decode, k_sgqa_merge, k_sgqa_prefill,
+ * k_swa_stage, k_swa_attend, k_ring_append.  Host-side state only, guarded
+ * by a mutex; at most 8192 launches are recorded between resets.
+ */
+dsa_status dsa_profile_enable(int on);
+dsa_status dsa_profile_kernel_stats(const char* kernel, double* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,7 @@ def lib():
             raise RuntimeError(f"{LIB} is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(LIB)
         vp, i64, i32, f64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float
+        L.or_num_threads.restype = ctypes.c_int
         L.or_e4m3_value.argtypes = [ctypes.c_uint8]
         L.or_e4m3_value.restype = f64
         L.or_e4m3_encode.argtypes = [f32]
@@ -62,6 +63,10 @@ def lib():
                                    vp, vp, vp, vp]
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    return int(lib().or_num_threads())
 
 
 def _p(a: np.ndarray):

@@ -32,9 +32,13 @@
  * region is selected (dense causal GQA) and against a banded mask (window).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the OpenMP loops below use (reported with CPU timings). */
+int or_num_threads(void) { return omp_get_max_threads(); }
 
 static double bf16_value(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
