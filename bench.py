@@ -144,14 +144,14 @@ def setup_decode(cfg, steps_hint=1):
     L = dsa.load()
     p = Calls.p
     gp = ctypes.byref(geom)
-    st = ctypes.c_void_p(s)
-    a_comp = (gp, B, p(ik), tcap, p(rb), p(re_), 1, p(summ), p(scale), st)
+    a_comp = (gp, B, p(ik), tcap, p(rb), p(re_), 1, p(summ), p(scale))
     a_score = (gp, B, p(iq), p(z), p(qseq), p(qpos), B, p(summ), p(scale), tcap, R, p(sel), p(nsel), None,
-               p(ws1), ws1.numel(), st)
-    a_attn = (gp, B, p(q), p(K), p(V), tcap, p(slen), p(sel), p(nsel), p(out), p(ws2), ws2.numel(), st)
+               p(ws1), ws1.numel())
+    a_attn = (gp, B, p(q), p(K), p(V), tcap, p(slen), p(sel), p(nsel), p(out), p(ws2), ws2.numel())
 
-    def step():
-        rc = L.dsa_compress_regions(*a_comp) or L.dsa_score_topk(*a_score) or L.dsa_sparse_gqa_decode(*a_attn)
+    def step(st):
+        rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
+              or L.dsa_sparse_gqa_decode(*a_attn, st))
         if rc:
             raise RuntimeError(f"decode step failed: {rc} {L.dsa_last_error().decode()}")
 
@@ -198,14 +198,14 @@ def setup_prefill(cfg):
     L = dsa.load()
     p = Calls.p
     gp = ctypes.byref(geom)
-    st = ctypes.c_void_p(s)
-    a_comp = (gp, 1, p(ik), tcap, p(rb), p(re_), span, p(summ), p(scale), st)
+    a_comp = (gp, 1, p(ik), tcap, p(rb), p(re_), span, p(summ), p(scale))
     a_score = (gp, n, p(iq), p(z), p(qseq), p(qpos), 1, p(summ), p(scale), tcap, R, p(sel), p(nsel), None,
-               p(ws1), ws1.numel(), st)
-    a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, p(K), p(V), tcap, p(sel), p(nsel), p(out), st)
+               p(ws1), ws1.numel())
+    a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, p(K), p(V), tcap, p(sel), p(nsel), p(out))
 
-    def step():
-        rc = L.dsa_compress_regions(*a_comp) or L.dsa_score_topk(*a_score) or L.dsa_sparse_gqa_prefill(*a_attn)
+    def step(st):
+        rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
+              or L.dsa_sparse_gqa_prefill(*a_attn, st))
         if rc:
             raise RuntimeError(f"prefill step failed: {rc} {L.dsa_last_error().decode()}")
 
@@ -213,28 +213,57 @@ def setup_prefill(cfg):
     return step, keep
 
 
-def timed(step, steps, warmup, kernels):
-    """Runs warmup steps, then exactly `steps` steps between two synchronisations with the
-    library's per-kernel hipEvents on.  Returns (seconds, {kernel: (avg_ms, launches)})."""
+def cur_stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def timed(step, steps, warmup, kernels, graph=True):
+    """Warmup, then three passes of exactly `steps` steps, each between two synchronisations:
+    (1) eager launches; (2) replays of a HIP graph holding one step (the timed headline when
+    graph=True); (3) eager launches with the library's per-kernel hipEvents on (roofline).
+    Returns (seconds_headline, seconds_eager, {kernel: (avg_ms, launches)})."""
     import torch
     import dsa_sparse_attention_amd as dsa
 
     for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    dsa.profile_enable(True)
+        step(cur_stream())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        step(cur_stream())
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    eager = time.perf_counter() - t0
+    head = eager
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(cur_stream())
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(cur_stream())
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        head = time.perf_counter() - t0
+        del g
+    dsa.profile_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step(cur_stream())
+    torch.cuda.synchronize()
     stats = {}
     for k in kernels:
         ms, n = dsa.profile_kernel_stats(k)
         stats[k] = (ms / max(n, 1), n)
     dsa.profile_enable(False)
-    return t1 - t0, stats
+    return head, eager, stats
 
 
 def cpu_baseline_decode(cfg, budget_s=15.0):
@@ -307,6 +336,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--profile-run", action="store_true",
                     help="setup + a few steps of each workload + a 1 GiB copy kernel, for rocprofv3")
     args = ap.parse_args()
@@ -324,13 +354,13 @@ def main():
     if args.profile_run:
         step, keep = setup_decode(DECODE)
         for _ in range(3):
-            step()
+            step(cur_stream())
         torch.cuda.synchronize()
         del keep
         if not args.no_prefill:
             step, keep = setup_prefill(PREFILL)
             for _ in range(2):
-                step()
+                step(cur_stream())
             torch.cuda.synchronize()
             del keep
         # calibration: a plain copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)
@@ -345,8 +375,9 @@ def main():
 
     # ---- decode at 1M
     step, keep = setup_decode(DECODE)
-    kn = ["k_compress", "k_fill_u32", "k_score_decode", "k_select", "k_sgqa_decode", "k_sgqa_merge"]
-    secs, st = timed(step, args.steps, args.warmup, kn)
+    kn = ["k_compress", "k_fill_u32", "k_score_decode", "k_select_thresh", "k_select_collect", "k_select",
+          "k_sgqa_decode", "k_sgqa_merge"]
+    secs, eager, st = timed(step, args.steps, args.warmup, kn, graph=not args.no_graph)
     del keep
     torch.cuda.empty_cache()
     B, Lc = DECODE["batch"], DECODE["context"]
@@ -360,7 +391,8 @@ def main():
     result = {
         "metric": "DSA layer decode queries/s @1M ctx + prefill tok/s @64K, % HBM/MFMA roofline",
         "value": round(qps, 2), "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms_step, 4), "timing": "graph replay" if not args.no_graph else "eager",
+        "eager_ms_per_step": round(eager * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": DECODE["name"], "batch": B, "context_tokens": Lc, "topk": DECODE["topk"],
                    "regions_per_sequence": Lc // REG},
@@ -380,7 +412,7 @@ def main():
         step, keep = setup_prefill(PREFILL)
         kp = ["k_compress", "k_score_prefill", "k_select", "k_sgqa_prefill"]
         psteps = max(3, args.steps // 3)
-        psecs, pst = timed(step, psteps, max(1, args.warmup // 2), kp)
+        psecs, peager, pst = timed(step, psteps, max(1, args.warmup // 2), kp, graph=not args.no_graph)
         del keep
         torch.cuda.empty_cache()
         n = PREFILL["chunk"]
@@ -392,7 +424,7 @@ def main():
         step_tf = fl["total"] / (pms * 1e-3) / 1e12
         result["prefill"] = {
             "workload": PREFILL["name"], "value": round(n * psteps / psecs, 1), "unit": "tokens/s",
-            "steps": psteps, "ms_per_step": round(pms, 3),
+            "steps": psteps, "ms_per_step": round(pms, 3), "eager_ms_per_step": round(peager * 1e3 / psteps, 3),
             "roofline": {"bound": "mfma", "kernel": "k_sgqa_prefill", "achieved": round(att_tf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": load_traffic("k_sgqa_prefill", "prefill_64k", source_hash("attention.hip")),

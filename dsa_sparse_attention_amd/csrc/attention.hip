@@ -260,27 +260,32 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_sgqa_merge(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                    int32_t nsplit) {
-  const int g = blockIdx.x, b = blockIdx.y;
+// One block per (head, group, sequence); thread d owns output channel d.
+// Split weights exp2(m_s - M) are formed once in LDS by the first wave
+// (nsplit <= 64).
+__global__ __launch_bounds__(kHeadDim) void k_sgqa_merge(const float* __restrict__ part,
+                                                         uint16_t* __restrict__ out, int32_t nsplit) {
+  const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int64_t sg = (int64_t)b * kGroups + g;
-  const float* pp = part + sg * nsplit * 16 * kPartStride;
-  for (int e = threadIdx.x; e < 16 * kHeadDim; e += blockDim.x) {
-    const int h = e / kHeadDim, d = e - h * kHeadDim;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[(s * 16 + h) * kPartStride]);
-    float acc = 0.0f, lsum = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* ps = pp + (s * 16 + h) * kPartStride;
-        const float f = __builtin_amdgcn_exp2f(ps[0] - M);
-        acc += f * ps[2 + d];
-        lsum += f * ps[1];
-      }
-    }
-    const float o = lsum > 0.0f ? acc / lsum : 0.0f;
-    out[((int64_t)b * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + d] = f32_to_bf16(o);
+  const float* pp = part + sg * nsplit * 16 * kPartStride + h * kPartStride;
+  __shared__ float w[64];
+  __shared__ float inv_l;
+  if (d < 64) {
+    const float m = d < nsplit ? pp[(int64_t)d * 16 * kPartStride] : -INFINITY;
+    float M = m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float f = (M == -INFINITY || d >= nsplit) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    w[d] = f;
+    float l = d < nsplit ? f * pp[(int64_t)d * 16 * kPartStride + 1] : 0.0f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    if (d == 0) inv_l = l > 0.0f ? 1.0f / l : 0.0f;
   }
+  __syncthreads();
+  float acc = 0.0f;
+  for (int s = 0; s < nsplit; ++s) acc += w[s] * pp[(int64_t)s * 16 * kPartStride + 2 + d];
+  out[((int64_t)b * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + d] = f32_to_bf16(acc * inv_l);
 }
 
 // ---------------------------------------------------------------------------
@@ -508,7 +513,7 @@ extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t ba
   if (st != DSA_OK) return st;
   {
     ProfScope prof_("k_sgqa_merge", s);
-    hipLaunchKernelGGL(k_sgqa_merge, dim3(kGroups, batch), dim3(256), 0, s, (const float*)workspace, out, a.nsplit);
+    hipLaunchKernelGGL(k_sgqa_merge, dim3(16, kGroups, batch), dim3(kHeadDim), 0, s, (const float*)workspace, out, a.nsplit);
   }
   return check_launch("dsa_sparse_gqa_decode: merge");
 }

@@ -30,7 +30,6 @@ namespace dsa {
 constexpr int kScoreRange = 1024;  // regions per k_score block
 constexpr int kTile = 16;          // regions per MFMA tile
 constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
-constexpr int kSelThreads = 512;
 constexpr int kSelCap = 4096;      // LDS candidate capacity of k_select
 
 struct ScoreArgs {
@@ -44,7 +43,7 @@ struct ScoreArgs {
   float* scores_out;    // nullable [Nq][G][max_regions]
   uint32_t* hist;       // [Nq][G][4096] (decode only)
   int64_t R;            // tcap / 8
-  int32_t nq, n_seqs, max_regions, ws_stride;
+  int32_t nq, n_seqs, max_regions, ws_stride, topk;
 };
 
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -73,6 +72,71 @@ __device__ __forceinline__ void codes_to_bf16(u32x4 c, bf16x8& lo, bf16x8& hi) {
   bf16x2 p7 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.w, 1.0f, true);
   lo = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
   hi = bf16x8{p4[0], p4[1], p5[0], p5[1], p6[0], p6[1], p7[0], p7[1]};
+}
+
+// Exclusive prefix sum over a block of NT threads.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i)
+    if (i < w) base += wsum[i];
+  __syncthreads();
+  return base + x - v;
+}
+
+// Given hist[0..nb) of the elements still in play, finds digit d (scanning
+// from the top) with above(d) < need <= above(d) + hist[d]; returns d and
+// sets *above_out.  Every thread of the block gets the result.
+template <int NT>
+__device__ __forceinline__ int find_digit(const uint32_t* hist, int nb, uint32_t need, uint32_t* above_out,
+                                          uint32_t* wsum, int* sh_d, uint32_t* sh_above) {
+  const int per = (nb + NT - 1) / NT;
+  const int hi_bin = nb - 1 - per * (int)threadIdx.x;  // this thread's bins, counted from the top
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int bin = hi_bin - i;
+    if (bin >= 0) local += hist[bin];
+  }
+  uint32_t run = block_excl_scan<NT>(local, wsum);
+  for (int i = 0; i < per; ++i) {
+    const int bin = hi_bin - i;
+    if (bin < 0) break;
+    const uint32_t h = hist[bin];
+    if (run < need && run + h >= need) {
+      *sh_d = bin;
+      *sh_above = run;
+    }
+    run += h;
+  }
+  __syncthreads();
+  *above_out = *sh_above;
+  const int d = *sh_d;
+  __syncthreads();
+  return d;
+}
+
+// Wave-aggregated append: one atomic per wave; returns this lane's slot when
+// pred holds.  Must be reached by every active lane of the wave.
+__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
+  const uint64_t mask = __ballot(pred);
+  const int lane = threadIdx.x & 63;
+  uint32_t base = 0;
+  if (mask) {
+    const int leader = __ffsll((long long)mask) - 1;
+    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+    base = __shfl(base, leader);
+  }
+  return base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
 }
 
 // QW queries per wave (1: decode, rows 0..3 of the tile used; 16: prefill,
@@ -186,12 +250,10 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
 
   if (QW == 1) {
     __syncthreads();
-    if (q0 < a.nq) {
-      uint32_t* gh = a.hist + ((int64_t)q0 * kGroups + g) * kHistBins;
-      for (int i = threadIdx.x; i < kHistBins; i += 256) {
-        uint32_t v = hist_lds[i];
-        if (v) atomicAdd(gh + i, v);
-      }
+    uint32_t* gh = a.hist + ((int64_t)q0 * kGroups + g) * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) {
+      const uint32_t v = hist_lds[i];
+      if (v) atomicAdd(gh + i, v);
     }
   }
 }
@@ -202,69 +264,19 @@ __global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// k_select
+// selection
 // ---------------------------------------------------------------------------
 
-// Exclusive prefix sum over the block (kSelThreads threads).
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-  for (int i = 0; i < kSelThreads / 64; ++i) {
-    if (i < w) base += wsum[i];
-    tot += wsum[i];
-  }
-  if (total) *total = tot;
-  __syncthreads();
-  return base + x - v;
-}
-
-// Given hist[0..nb) of the elements still in play, find digit d (scanning
-// from the top) with above(d) < need <= above(d) + hist[d].  Returns d and
-// writes above(d) to *above_out.  All threads get the result.
-__device__ __forceinline__ int find_digit(const uint32_t* hist, int nb, uint32_t need,
-                                          uint32_t* above_out, uint32_t* wsum, int* sh_d,
-                                          uint32_t* sh_above) {
-  // thread t owns bins [per*t', per*t'+per) with t' counted from the top.
-  const int per = (nb + kSelThreads - 1) / kSelThreads;
-  const int tr = threadIdx.x;  // rank from the top
-  const int hi_bin = nb - 1 - per * tr;  // highest bin of this thread
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) {
-    int bin = hi_bin - i;
-    if (bin >= 0) local += hist[bin];
-  }
-  uint32_t run = block_excl_scan(local, wsum, nullptr);
-  for (int i = 0; i < per; ++i) {
-    int bin = hi_bin - i;
-    if (bin < 0) break;
-    uint32_t h = hist[bin];
-    if (run < need && run + h >= need) {
-      *sh_d = bin;
-      *sh_above = run;
-    }
-    run += h;
-  }
-  __syncthreads();
-  *above_out = *sh_above;
-  int d = *sh_d;
-  __syncthreads();
-  return d;
-}
-
 struct SelectArgs {
-  const float* scores;   // [Nq][G][ws_stride]
-  uint32_t* hist;        // [Nq][G][4096] or nullptr (computed here)
+  const float* scores;  // [Nq][G][ws_stride]
+  const uint32_t* hist; // [Nq][G][4096] level-0 histograms, or nullptr (computed in k_select)
+  uint32_t* bcnt;       // [Nq][G][nblk] candidates found by each collect block (decode)
+  uint64_t* cand;       // [Nq][G][nblk][kCollectChunk] candidate keys (decode), or nullptr
+  uint32_t* thr;        // [Nq][G][4] level-0 threshold: digit, count above, count in digit (decode)
+  int32_t nblk;         // collect blocks per (query, group)
   const int32_t* qpos;
-  int32_t* sel;          // [Nq][G][topk]
-  int32_t* nsel;         // [Nq][G]
+  int32_t* sel;         // [Nq][G][topk]
+  int32_t* nsel;        // [Nq][G]
   int64_t R;
   int32_t nq, max_regions, ws_stride, topk;
 };
@@ -273,20 +285,104 @@ __device__ __forceinline__ uint64_t cand_key(const float* sc, int64_t r) {
   return ((uint64_t)score_key(sc[r]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)r);
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
-  const int64_t pq = blockIdx.x;  // (query, group)
+constexpr int kCollectThreads = 256;
+constexpr int kCollectPer = 8;  // consecutive scores per thread
+constexpr int kCollectChunk = kCollectThreads * kCollectPer;
+
+// Decode, step 1: one block per (query, group) turns the level-0 histogram
+// built by k_score into the threshold digit (the digit holding the k-th key).
+__global__ __launch_bounds__(256) void k_select_thresh(SelectArgs a) {
+  const int64_t pq = blockIdx.x;
+  const int qi = (int)(pq / kGroups);
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t wsum[4];
+  __shared__ int sh_d;
+  __shared__ uint32_t sh_above;
+  if (threadIdx.x == 0) {
+    sh_d = 0;
+    sh_above = 0;
+  }
+  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  const int64_t need = (c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1);
+  if (need == c || need == 0) return;
+  const uint32_t* gh = a.hist + pq * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) hist[i] = gh[i];
+  __syncthreads();
+  uint32_t above;
+  const int d = find_digit<256>(hist, kHistBins, (uint32_t)need, &above, wsum, &sh_d, &sh_above);
+  if (threadIdx.x == 0) {
+    a.thr[pq * 4 + 0] = (uint32_t)d;
+    a.thr[pq * 4 + 1] = above;
+    a.thr[pq * 4 + 2] = hist[d];
+  }
+}
+
+// Decode, step 2: block j of (query, group) scans scores [2048j, 2048j+2048)
+// and keeps every key whose level-0 digit is at or above the threshold digit,
+// compacted in LDS and written to its own slice of the candidate buffer with
+// its count (no global atomics).  Blocks write count 0 when the problem needs
+// no list or the list would not fit (k_select then narrows on its own).
+__global__ __launch_bounds__(kCollectThreads) void k_select_collect(SelectArgs a) {
+  const int64_t pq = (int64_t)blockIdx.z * kGroups + blockIdx.y;
+  const int qi = blockIdx.z;
+  const int blk = blockIdx.x;
+  __shared__ uint64_t buf[kCollectChunk];
+  __shared__ uint32_t n;
+  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  const int64_t need = (c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1);
+  uint32_t* bc = a.bcnt + pq * a.nblk + blk;
+  const int64_t rb = (int64_t)blk * kCollectChunk;
+  if (need == c || need == 0 || rb >= c || a.thr[pq * 4 + 1] + a.thr[pq * 4 + 2] > (uint32_t)kSelCap) {
+    if (threadIdx.x == 0) *bc = 0;
+    return;
+  }
+  if (threadIdx.x == 0) n = 0;
+  __syncthreads();
+  const int d = (int)a.thr[pq * 4 + 0];
+  const float* sc = a.scores + pq * a.ws_stride;
+  const int64_t r0 = rb + (int64_t)threadIdx.x * kCollectPer;
+  float v[kCollectPer];
+  if (r0 + kCollectPer <= c) {
+    const f32x4 x0 = *(const f32x4*)(sc + r0), x1 = *(const f32x4*)(sc + r0 + 4);
+    v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
+    v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < kCollectPer; ++e) v[e] = (r0 + e < c) ? sc[r0 + e] : 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < kCollectPer; ++e) {
+    const int64_t r = r0 + e;
+    const uint32_t key = score_key(v[e]);
+    const bool take = r < c && (int)(key >> 20) >= d;
+    const uint32_t pos = wave_append(take, &n);
+    if (take) buf[pos] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)r);
+  }
+  __syncthreads();
+  const uint32_t m = n;
+  uint64_t* out = a.cand + (pq * a.nblk + blk) * kCollectChunk;
+  for (uint32_t i = threadIdx.x; i < m; i += kCollectThreads) out[i] = buf[i];
+  if (threadIdx.x == 0) *bc = m;
+}
+
+// One block per (query, group): exact selection of the need = min(topk-1, c)
+// best candidates among regions 0..c-1 by 64-bit key, plus region c.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
+  const int64_t pq = blockIdx.x;
   const int qi = (int)(pq / kGroups);
   const int tid = threadIdx.x;
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint64_t list[kSelCap];
   __shared__ int32_t outl[kMaxTopk];
-  __shared__ uint32_t wsum[kSelThreads / 64];
+  __shared__ uint32_t wsum[NT / 64];
   __shared__ int sh_d;
   __shared__ uint32_t sh_above, sh_count;
 
   if (tid == 0) {
     sh_d = 0;
     sh_above = 0;
+    sh_count = 0;
   }
   __syncthreads();
   const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
@@ -296,12 +392,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   const float* sc = a.scores + pq * a.ws_stride;
 
   if (need64 == c) {  // every candidate fits: regions 0..c
-    for (int i = tid; i < a.topk; i += kSelThreads) sel[i] = (i <= c) ? i : -1;
+    for (int i = tid; i < a.topk; i += NT) sel[i] = (i <= c) ? i : -1;
     if (tid == 0) a.nsel[pq] = (int32_t)(c + 1);
     return;
   }
   if (need == 0) {  // topk == 1: only the current region
-    for (int i = tid; i < a.topk; i += kSelThreads) sel[i] = (i == 0) ? (int32_t)c : -1;
+    for (int i = tid; i < a.topk; i += NT) sel[i] = (i == 0) ? (int32_t)c : -1;
     if (tid == 0) a.nsel[pq] = 1;
     return;
   }
@@ -309,50 +405,83 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   // ---- level 0: 12-bit digit of the score key (bits 63..52 of the 64-bit key)
   if (a.hist) {
     const uint32_t* gh = a.hist + pq * kHistBins;
-    for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = gh[i];
+    for (int i = tid; i < kHistBins; i += NT) hist[i] = gh[i];
   } else {
-    for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int64_t r = tid; r < c; r += kSelThreads) atomicAdd(&hist[score_key(sc[r]) >> 20], 1u);
+    for (int64_t r = tid; r < c; r += NT) atomicAdd(&hist[score_key(sc[r]) >> 20], 1u);
   }
   __syncthreads();
   uint32_t above;
-  int d = find_digit(hist, kHistBins, need, &above, wsum, &sh_d, &sh_above);
+  int d = find_digit<NT>(hist, kHistBins, need, &above, wsum, &sh_d, &sh_above);
   uint64_t prefix = (uint64_t)d;
   int shift = 52;
   uint32_t inbin = hist[d];
   __syncthreads();
+  const bool from_cand = a.cand != nullptr && a.nblk < kMaxTopk && above + inbin <= (uint32_t)kSelCap;
 
-  // ---- narrow over global memory until the candidates fit in LDS
-  while (above + inbin > (uint32_t)kSelCap && shift > 0) {
-    const int width = shift >= 12 ? 12 : shift;
-    const int nshift = shift - width;
-    const int nb = 1 << width;
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+  if (!from_cand) {
+    // ---- narrow over global memory until the candidates fit in LDS
+    while (above + inbin > (uint32_t)kSelCap && shift > 0) {
+      const int width = shift >= 12 ? 12 : shift;
+      const int nshift = shift - width;
+      const int nb = 1 << width;
+      for (int i = tid; i < nb; i += NT) hist[i] = 0;
+      __syncthreads();
+      for (int64_t r = tid; r < c; r += NT) {
+        const uint64_t k = cand_key(sc, r);
+        if ((k >> shift) == prefix) atomicAdd(&hist[(uint32_t)(k >> nshift) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t ab;
+      d = find_digit<NT>(hist, nb, need - above, &ab, wsum, &sh_d, &sh_above);
+      above += ab;
+      inbin = hist[d];
+      prefix = (prefix << width) | (uint64_t)d;
+      shift = nshift;
+      __syncthreads();
+    }
+    // ---- collect everything at or above the current bin into LDS
+    for (int64_t base = 0; base < c; base += NT) {
+      const int64_t r = base + tid;
+      uint64_t k = 0;
+      bool take = false;
+      if (r < c) {
+        k = cand_key(sc, r);
+        take = (k >> shift) >= prefix;
+      }
+      const uint32_t pos = wave_append(take, &sh_count);
+      if (take && pos < (uint32_t)kSelCap) list[pos] = k;
+    }
+  } else {
+    // concatenate the collect blocks' lists: offsets by a block-wide scan
+    // over their counts (in rounds of NT blocks), then a flat copy where
+    // each element finds its block by binary search over the offsets.
+    uint32_t* offs = (uint32_t*)outl;  // nblk + 1 <= kMaxTopk entries
+    uint32_t base = 0;
+    for (int j0 = 0; j0 < a.nblk; j0 += NT) {
+      const int j = j0 + tid;
+      const uint32_t cj = j < a.nblk ? a.bcnt[pq * a.nblk + j] : 0u;
+      const uint32_t ex = block_excl_scan<NT>(cj, wsum);
+      if (j < a.nblk) offs[j] = base + ex;
+      if (tid == NT - 1) sh_count = base + ex + cj;
+      __syncthreads();
+      base = sh_count;
+      __syncthreads();
+    }
+    if (tid == 0) offs[a.nblk] = base;
     __syncthreads();
-    for (int64_t r = tid; r < c; r += kSelThreads) {
-      uint64_t k = cand_key(sc, r);
-      if ((k >> shift) == prefix) atomicAdd(&hist[(uint32_t)(k >> nshift) & (nb - 1)], 1u);
+    const uint32_t m = base < (uint32_t)kSelCap ? base : (uint32_t)kSelCap;
+    for (uint32_t i = tid; i < m; i += NT) {
+      int lo = 0, hi = a.nblk - 1;  // last j with offs[j] <= i
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offs[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      list[i] = a.cand[(pq * a.nblk + lo) * kCollectChunk + (i - offs[lo])];
     }
     __syncthreads();
-    uint32_t ab;
-    d = find_digit(hist, nb, need - above, &ab, wsum, &sh_d, &sh_above);
-    above += ab;
-    inbin = hist[d];
-    prefix = (prefix << width) | (uint64_t)d;
-    shift = nshift;
-    __syncthreads();
-  }
-
-  // ---- collect everything at or above the current bin into LDS
-  if (tid == 0) sh_count = 0;
-  __syncthreads();
-  for (int64_t r = tid; r < c; r += kSelThreads) {
-    uint64_t k = cand_key(sc, r);
-    if ((k >> shift) >= prefix) {
-      uint32_t pos = atomicAdd(&sh_count, 1u);
-      if (pos < (uint32_t)kSelCap) list[pos] = k;
-    }
   }
   __syncthreads();
   const uint32_t M = sh_count < (uint32_t)kSelCap ? sh_count : (uint32_t)kSelCap;
@@ -363,15 +492,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     const int width = shift >= 8 ? 8 : shift;
     const int nshift = shift - width;
     const int nb = 1 << width;
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < nb; i += NT) hist[i] = 0;
     __syncthreads();
-    for (uint32_t i = tid; i < M; i += kSelThreads) {
-      uint64_t k = list[i];
+    for (uint32_t i = tid; i < M; i += NT) {
+      const uint64_t k = list[i];
       if ((k >> shift) == prefix) atomicAdd(&hist[(uint32_t)(k >> nshift) & (nb - 1)], 1u);
     }
     __syncthreads();
     uint32_t ab;
-    d = find_digit(hist, nb, need_in, &ab, wsum, &sh_d, &sh_above);
+    d = find_digit<NT>(hist, nb, need_in, &ab, wsum, &sh_d, &sh_above);
     need_in -= ab;
     inbin = hist[d];
     prefix = (prefix << width) | (uint64_t)d;
@@ -382,42 +511,80 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
   // ---- selected = list entries with (key >> shift) >= prefix (exactly need)
   if (tid == 0) sh_count = 0;
   __syncthreads();
-  for (uint32_t i = tid; i < M; i += kSelThreads) {
-    uint64_t k = list[i];
-    if ((k >> shift) >= prefix) {
-      uint32_t pos = atomicAdd(&sh_count, 1u);
-      if (pos < (uint32_t)kMaxTopk - 1) outl[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+  for (uint32_t base = 0; base < M; base += NT) {
+    const uint32_t i = base + tid;
+    uint64_t k = 0;
+    bool take = false;
+    if (i < M) {
+      k = list[i];
+      take = (k >> shift) >= prefix;
     }
+    const uint32_t pos = wave_append(take, &sh_count);
+    if (take && pos < (uint32_t)kMaxTopk - 1) outl[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
   }
   __syncthreads();
   const uint32_t nsel = need + 1;
-  for (int i = tid; i < kMaxTopk; i += kSelThreads) {
+  for (int i = tid; i < kMaxTopk; i += NT) {
     if ((uint32_t)i == need) outl[i] = (int32_t)c;
     else if ((uint32_t)i > need) outl[i] = 0x7FFFFFFF;
   }
   __syncthreads();
-  // bitonic sort of 512 ascending
+  // bitonic sort of 512 ascending; sorted prefix [0, nsel) is the selection
   for (int size = 2; size <= kMaxTopk; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < kMaxTopk; i += kSelThreads) {
-        int j = i ^ stride;
-        if (j > i) {
-          bool up = ((i & size) == 0);
-          int32_t x = outl[i], y = outl[j];
-          if ((x > y) == up) {
-            outl[i] = y;
-            outl[j] = x;
-          }
+      for (int i = tid; i < kMaxTopk / 2; i += NT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0);
+        const int32_t x = outl[lo], y = outl[hi];
+        if ((x > y) == up) {
+          outl[lo] = y;
+          outl[hi] = x;
         }
       }
       __syncthreads();
     }
   }
-  for (int i = tid; i < a.topk; i += kSelThreads) sel[i] = ((uint32_t)i < nsel) ? outl[i] : -1;
+  for (int i = tid; i < a.topk; i += NT) sel[i] = ((uint32_t)i < nsel) ? outl[i] : -1;
   if (tid == 0) a.nsel[pq] = (int32_t)nsel;
 }
 
 static int64_t ws_stride_of(int32_t max_regions) { return ((int64_t)max_regions + 63) / 64 * 64; }
+static bool decode_shaped(int32_t n_queries) { return n_queries < 64; }
+
+struct ScoreWs {
+  uint32_t* hist;
+  uint32_t* thr;
+  uint32_t* bcnt;
+  uint64_t* cand;
+  float* scores;
+  size_t bytes;
+};
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static int32_t collect_blocks(int32_t max_regions) { return (max_regions + kCollectChunk - 1) / kCollectChunk; }
+
+static ScoreWs score_ws_layout(void* base, int32_t nq, int32_t max_regions) {
+  ScoreWs w;
+  char* p = (char*)base;
+  const size_t np = (size_t)nq * kGroups;
+  const bool dec = decode_shaped(nq);
+  const size_t nblk = (size_t)collect_blocks(max_regions);
+  size_t off = 0;
+  w.hist = (uint32_t*)(p + off);
+  off += align256(np * kHistBins * 4);
+  w.thr = (uint32_t*)(p + off);
+  off += align256(np * 4 * 4);
+  w.bcnt = (uint32_t*)(p + off);
+  off += align256(np * nblk * 4);
+  w.cand = dec ? (uint64_t*)(p + off) : nullptr;
+  if (dec) off += align256(np * nblk * kCollectChunk * 8);
+  w.scores = (float*)(p + off);
+  off += align256(np * (size_t)ws_stride_of(max_regions) * 4);
+  w.bytes = off;
+  return w;
+}
 
 }  // namespace dsa
 
@@ -427,9 +594,7 @@ extern "C" size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_
                                                 int32_t max_regions) {
   (void)geom;
   if (n_queries <= 0 || max_regions <= 0) return 256;
-  size_t hist = (size_t)n_queries * kGroups * kHistBins * sizeof(uint32_t);
-  size_t sc = (size_t)n_queries * kGroups * (size_t)ws_stride_of(max_regions) * sizeof(float);
-  return hist + sc + 256;
+  return score_ws_layout(nullptr, n_queries, max_regions).bytes;
 }
 
 extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries,
@@ -452,49 +617,66 @@ extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_score_topk: workspace must be 256-byte aligned");
   if (workspace_bytes < dsa_score_topk_workspace_size(geom, n_queries, max_regions))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_score_topk: workspace too small");
+  if (n_queries > 65535 * 16) return fail(DSA_ERR_UNSUPPORTED, "dsa_score_topk: too many queries");
   hipStream_t s = as_stream(stream);
-
-  uint32_t* hist = (uint32_t*)workspace;
-  const int64_t hist_n = (int64_t)n_queries * kGroups * kHistBins;
-  float* scores = (float*)(hist + hist_n);
+  const ScoreWs w = score_ws_layout(workspace, n_queries, max_regions);
   const int32_t stride = (int32_t)ws_stride_of(max_regions);
 
   ScoreArgs sa;
   sa.iq = index_q; sa.z = z; sa.qseq = q_seq; sa.qpos = q_pos; sa.summ = summ; sa.scale = scale;
-  sa.scores = scores; sa.scores_out = scores_out; sa.hist = hist; sa.R = tcap / kRegion;
-  sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions; sa.ws_stride = stride;
+  sa.scores = w.scores; sa.scores_out = scores_out; sa.hist = w.hist;
+  sa.R = tcap / kRegion; sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions;
+  sa.ws_stride = stride; sa.topk = geom->topk;
   const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
-  // Decode-shaped calls (few queries, many regions) score one query per wave
-  // and build the level-0 histogram on the fly; prefill-shaped calls score
-  // 16 queries per wave so each summary tile feeds 4 MFMA row-sets.
-  const bool decode_shape = n_queries < 64;
-  if (decode_shape) {
-    int64_t fill_blocks = (hist_n + 255) / 256;
+  // Decode-shaped calls (few queries, many regions) score one query per wave,
+  // build the level-0 histogram on the fly and collect candidates with many
+  // blocks; prefill-shaped calls score 16 queries per wave so each summary
+  // tile feeds 4 MFMA row-sets, and select with one block per problem.
+  const bool dec = decode_shaped(n_queries);
+  SelectArgs se;
+  se.scores = w.scores; se.hist = dec ? w.hist : nullptr; se.bcnt = w.bcnt; se.cand = w.cand; se.thr = w.thr;
+  se.nblk = collect_blocks(max_regions); se.qpos = q_pos;
+  se.sel = sel; se.nsel = n_sel; se.R = tcap / kRegion; se.nq = n_queries; se.max_regions = max_regions;
+  se.ws_stride = stride; se.topk = geom->topk;
+  if (dec) {
+    const int64_t fill_n = (int64_t)n_queries * kGroups * kHistBins;
+    int64_t fill_blocks = (fill_n + 255) / 256;
     if (fill_blocks > 4096) fill_blocks = 4096;
     {
       ProfScope prof_("k_fill_u32", s);
-      hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)fill_blocks), dim3(256), 0, s, hist, hist_n, 0u);
+      hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)fill_blocks), dim3(256), 0, s, w.hist, fill_n, 0u);
     }
     {
       ProfScope prof_("k_score_decode", s);
       hipLaunchKernelGGL(k_score<1>, dim3(ranges, kGroups, n_queries), dim3(256), 0, s, sa);
+    }
+    st = check_launch("dsa_score_topk: score");
+    if (st != DSA_OK) return st;
+    {
+      ProfScope prof_("k_select_thresh", s);
+      hipLaunchKernelGGL(k_select_thresh, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(256), 0, s, se);
+    }
+    {
+      ProfScope prof_("k_select_collect", s);
+      hipLaunchKernelGGL(k_select_collect, dim3(se.nblk, kGroups, n_queries), dim3(kCollectThreads), 0, s, se);
+    }
+    st = check_launch("dsa_score_topk: collect");
+    if (st != DSA_OK) return st;
+    {
+      ProfScope prof_("k_select", s);
+      hipLaunchKernelGGL(k_select<512>, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(512), 0, s, se);
     }
   } else {
     {
       ProfScope prof_("k_score_prefill", s);
       hipLaunchKernelGGL(k_score<16>, dim3(ranges, kGroups, (n_queries + 15) / 16), dim3(256), 0, s, sa);
     }
-  }
-  st = check_launch("dsa_score_topk: score");
-  if (st != DSA_OK) return st;
-
-  SelectArgs se;
-  se.scores = scores; se.hist = decode_shape ? hist : nullptr; se.qpos = q_pos; se.sel = sel;
-  se.nsel = n_sel; se.R = tcap / kRegion; se.nq = n_queries; se.max_regions = max_regions;
-  se.ws_stride = stride; se.topk = geom->topk;
-  {
-    ProfScope prof_("k_select", s);
-    hipLaunchKernelGGL(k_select, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(kSelThreads), 0, s, se);
+    st = check_launch("dsa_score_topk: score");
+    if (st != DSA_OK) return st;
+    {
+      ProfScope prof_("k_select", s);
+      hipLaunchKernelGGL(k_select<256>, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(256), 0, s, se);
+    }
   }
   return check_launch("dsa_score_topk: select");
 }

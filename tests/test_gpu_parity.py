@@ -222,3 +222,60 @@ def test_decode_is_deterministic():
     b = H.run_dsa_decode(0xAA, [6000, 3001], topk=512, check_seqs=[])
     for k in ("summ", "scale", "sel", "nsel", "out"):
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+
+
+def test_decode_step_replays_from_a_hip_graph():
+    """The whole decode step captured once and replayed several times, with eager work and
+    synchronisations in between, gives the eager result bit for bit on every replay."""
+    seed = 0xAB
+    lens = [3000, 1505]
+    B, topk = len(lens), 512
+    tcap = H.round8(max(lens))
+    R = tcap // 8
+    geom = dsa.geometry(topk=topk)
+    ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
+    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_GROUP_MAJOR)
+    V = H.dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
+    q, iq, z = H.dev_queries(seed, B)
+    lens_np = np.asarray(lens, dtype=np.int32)
+    zero, rend = H.i32(np.zeros(B)), H.i32(lens_np // 8)
+    qs, qp, sl = H.i32(np.arange(B)), H.i32(lens_np - 1), H.i32(lens_np)
+    ws1 = dsa.workspace(dsa.dsa_score_topk_workspace_size(geom, B, R))
+    ws2 = dsa.workspace(dsa.dsa_sparse_gqa_workspace_size(geom, B))
+
+    def make_bufs():
+        return dict(summ=torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda"),
+                    scale=torch.zeros(B * G * R, dtype=torch.float32, device="cuda"),
+                    sel=torch.empty(B * G * topk, dtype=torch.int32, device="cuda"),
+                    nsel=torch.empty(B * G, dtype=torch.int32, device="cuda"),
+                    out=torch.empty(B * HQ * D, dtype=H.BF16, device="cuda"))
+
+    def step(b):
+        dsa.dsa_compress_regions(geom, ik, tcap, zero, rend, R, b["summ"], b["scale"])
+        dsa.dsa_score_topk(geom, iq, z, qs, qp, B, b["summ"], b["scale"], tcap, R, b["sel"], b["nsel"],
+                           workspace=ws1)
+        dsa.dsa_sparse_gqa_decode(geom, q, K, V, tcap, sl, b["sel"], b["nsel"], b["out"], workspace=ws2)
+
+    ref = make_bufs()
+    step(ref)
+    torch.cuda.synchronize()
+    gb = make_bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(gb)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(gb)
+    for rep in range(3):
+        for t in gb.values():
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(gb[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+        other = make_bufs()  # eager work between replays, sharing the workspaces
+        step(other)
+        torch.cuda.synchronize()
+        assert torch.equal(other["out"].view(torch.uint8), ref["out"].view(torch.uint8))
