@@ -336,7 +336,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
     ap.add_argument("--profile-run", action="store_true",
                     help="setup + a few steps of each workload + a 1 GiB copy kernel, for rocprofv3")
     args = ap.parse_args()
@@ -377,7 +377,7 @@ def main():
     step, keep = setup_decode(DECODE)
     kn = ["k_compress", "k_fill_u32", "k_score_decode", "k_select_thresh", "k_select_collect", "k_select",
           "k_sgqa_decode", "k_sgqa_merge"]
-    secs, eager, st = timed(step, args.steps, args.warmup, kn, graph=not args.no_graph)
+    secs, eager, st = timed(step, args.steps, args.warmup, kn, graph=args.graph)
     del keep
     torch.cuda.empty_cache()
     B, Lc = DECODE["batch"], DECODE["context"]
@@ -391,7 +391,7 @@ def main():
     result = {
         "metric": "DSA layer decode queries/s @1M ctx + prefill tok/s @64K, % HBM/MFMA roofline",
         "value": round(qps, 2), "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "timing": "graph replay" if not args.no_graph else "eager",
+        "ms_per_step": round(ms_step, 4), "timing": "graph replay" if args.graph else "eager",
         "eager_ms_per_step": round(eager * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": DECODE["name"], "batch": B, "context_tokens": Lc, "topk": DECODE["topk"],
@@ -412,7 +412,7 @@ def main():
         step, keep = setup_prefill(PREFILL)
         kp = ["k_compress", "k_score_prefill", "k_select", "k_sgqa_prefill"]
         psteps = max(3, args.steps // 3)
-        psecs, peager, pst = timed(step, psteps, max(1, args.warmup // 2), kp, graph=not args.no_graph)
+        psecs, peager, pst = timed(step, psteps, max(1, args.warmup // 2), kp, graph=args.graph)
         del keep
         torch.cuda.empty_cache()
         n = PREFILL["chunk"]

@@ -490,8 +490,8 @@ extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t ba
                                             void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (batch < 0 || tcap <= 0 || tcap % kRegion)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: bad sizes (tcap must be a positive multiple of 8)");
+  if (batch < 0 || tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: bad sizes (tcap must be a positive multiple of 128)");
   if (batch == 0) return DSA_OK;
   if (!q || !k_cache || !v_cache || !seq_len || !sel || !n_sel || !out || !workspace)
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: NULL pointer");
@@ -525,8 +525,8 @@ extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n
                                              uint16_t* out, void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (n_queries < 0 || n_seqs < 0 || tcap <= 0 || tcap % kRegion)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: bad sizes (tcap must be a positive multiple of 8)");
+  if (n_queries < 0 || n_seqs < 0 || tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: bad sizes (tcap must be a positive multiple of 128)");
   if (n_queries == 0) return DSA_OK;
   if (n_seqs == 0) return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: n_seqs must be positive");
   if (!q || !q_seq || !q_pos || !k_cache || !v_cache || !sel || !n_sel || !out)

@@ -21,6 +21,15 @@ constexpr int kHeadsPerGroup = kQHeads / kGroups;  // 16 = one MFMA tile edge
 constexpr int kHeadDim = 192;
 constexpr int kMaxTopk = 512;
 constexpr int kWindow = 512;
+constexpr int kTcapAlign = 128;  // cache capacity granule: 16 regions = one summary tile
+
+// Summaries of one (sequence, group) are stored in tiles of 16 regions
+// (4096 bytes).  Byte j of region r lives at
+//   (r/16)*4096 + (j/64)*1024 + ((j%64)/16)*256 + (r%16)*16 + j%16,
+// i.e. each 1 KB quarter of a tile holds, for every region of the tile, the
+// 16-byte pieces that one 64-lane load instruction hands to the MFMA
+// B operand (lane 16*kb + n <- region n, channels 64q + 16kb .. +15).
+__device__ __forceinline__ int64_t summ_tile_base(int64_t r) { return (r >> 4) * 4096; }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -50,8 +59,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+#ifndef DSA_NT_LOADS
+#define DSA_NT_LOADS 1
+#endif
+// 16-byte load of data streamed once (non-temporal hint).
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
+#if DSA_NT_LOADS
   return __builtin_nontemporal_load((const u32x4*)p);
+#else
+  return *(const u32x4*)p;
+#endif
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 

@@ -69,9 +69,12 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ i
 #pragma unroll
     for (int e = 0; e < 4; ++e) packed |= e4m3_rne_sat(__fdiv_rn(m[e], sc)) << (8 * e);
   }
-  const int64_t rg = ((int64_t)b * kGroups + g) * R + r;
-  *(uint32_t*)(summ + rg * kProxy + 4 * lane) = packed;
-  if (lane == 0) scale[rg] = sc;
+  const int64_t sg = (int64_t)b * kGroups + g;
+  // channels 4l..4l+3 of region r in the tiled summary layout
+  const int64_t off = summ_tile_base(r) + (lane >> 4) * 1024 + ((lane & 15) >> 2) * 256 + (r & 15) * 16 +
+                      4 * (lane & 3);
+  *(uint32_t*)(summ + sg * R * kProxy + off) = packed;
+  if (lane == 0) scale[sg * R + r] = sc;
 }
 
 // One block per new token row: copies K/V (and index_k) into the cache
@@ -113,8 +116,8 @@ extern "C" dsa_status dsa_compress_regions(const dsa_geometry* geom, int32_t bat
                                            void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (batch < 0 || max_span < 0 || tcap <= 0 || tcap % kRegion)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_compress_regions: batch/max_span must be >= 0 and tcap a positive multiple of 8");
+  if (batch < 0 || max_span < 0 || tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_compress_regions: batch/max_span must be >= 0 and tcap a positive multiple of 128");
   if (batch == 0 || max_span == 0) return DSA_OK;
   if (!index_k || !region_begin || !region_end || !summ || !scale)
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_compress_regions: NULL pointer");
@@ -136,8 +139,8 @@ extern "C" dsa_status dsa_cache_write(const dsa_geometry* geom, int32_t n_tokens
                                       int64_t tcap, void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (n_tokens < 0 || n_seqs < 0 || tcap <= 0 || tcap % kRegion)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: bad sizes (tcap must be a positive multiple of 8)");
+  if (n_tokens < 0 || n_seqs < 0 || tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: bad sizes (tcap must be a positive multiple of 128)");
   if (n_tokens == 0 || n_seqs == 0) return DSA_OK;
   if (!tok_seq || !tok_pos || !k_new || !v_new || !k_cache || !v_cache)
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write: NULL pointer");

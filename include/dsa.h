@@ -36,13 +36,17 @@
  *    atomics on any result path).
  *
  * Cache layouts (per sequence b of a batch, capacity tcap tokens, tcap a
- * multiple of 8; region r = tokens 8r..8r+7; R = tcap/8):
+ * multiple of 128; region r = tokens 8r..8r+7; R = tcap/8):
  *   index_k  [B][G][tcap][P]    bf16   indexer keys
  *   K        [B][G][tcap][D]    bf16   keys (post-RoPE)
  *   V        [B][G][R][D][8]    bf16   values, "region-transposed": the 8
  *                                      tokens of one region are contiguous
  *                                      for each channel
- *   summ     [B][G][R][P]       uint8  E4M3 region summaries
+ *   summ     [B][G][R/16][4096] uint8  E4M3 region summaries, tiled: byte j
+ *                                      (channel j) of region r of (b, g) is at
+ *                                      (r/16)*4096 + (j/64)*1024
+ *                                      + ((j%64)/16)*256 + (r%16)*16 + j%16
+ *                                      within that (b, g)'s R*256 bytes
  *   scale    [B][G][R]          fp32   per-(region, group) summary scale
  * Sliding-window ring (window W = 512, slot of position t = t mod W):
  *   k_ring   [S][G][W][D]       bf16
@@ -120,7 +124,8 @@ dsa_status dsa_cache_write(const dsa_geometry* geom, int32_t n_tokens, const int
  *   index_k         [batch][G][tcap][P] bf16
  *   region_begin/end [batch] int32 device
  *   max_span        host bound on region_end - region_begin (grid size), >= 0
- *   summ, scale     [batch][G][tcap/8][P] uint8, [batch][G][tcap/8] fp32
+ *   summ, scale     summaries (tiled layout above) and scales of `batch`
+ *                   sequences with capacity tcap
  * Output is bit-exact with the stated rule.
  */
 dsa_status dsa_compress_regions(const dsa_geometry* geom, int32_t batch, const uint16_t* index_k,

@@ -33,6 +33,17 @@ def round8(x):
     return (x + 7) // 8 * 8
 
 
+def round128(x):
+    """Cache capacities are multiples of 128 tokens (16 regions = one summary tile)."""
+    return (x + 127) // 128 * 128
+
+
+def summ_logical(summ_np, B, R):
+    """The library's tiled summary bytes [B][G][R/16][4096] -> [B][G][R][P] (layout of include/dsa.h)."""
+    t = summ_np.reshape(B, G, R // 16, 4, 4, 16, 16)  # tile, j/64, (j%64)/16, r%16, j%16
+    return t.transpose(0, 1, 2, 5, 3, 4, 6).reshape(B, G, R, P)
+
+
 # ------------------------------------------------------------------------------------------------
 # device inputs (dsa_inputs HIP generator) and host inputs (dsa_inputs C generator)
 # ------------------------------------------------------------------------------------------------
@@ -118,17 +129,19 @@ def check_selection(gsel, or_sel, or_scores_g, c):
 # ------------------------------------------------------------------------------------------------
 # DSA decode end to end
 # ------------------------------------------------------------------------------------------------
-def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=None):
+def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=None, zero_z=False):
     """Runs compress -> score_topk -> sparse GQA decode on the GPU for len(lens) sequences (query b at
     position lens[b]-1), and the oracle for the sequences in check_seqs (default all)."""
     B = len(lens)
-    tcap = tcap or round8(max(lens))
+    tcap = tcap or round128(max(lens))
     R = tcap // 8
     geom = dsa.geometry(topk=topk)
     ik = dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE, planted)
     K = dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_GROUP_MAJOR)
     V = dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
     q, iq, z = dev_queries(seed, B)
+    if zero_z:  # every score 0: selection falls to the lowest regions (tie rule)
+        z.zero_()
     summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
     scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
     lens_np = np.asarray(lens, dtype=np.int32)
@@ -142,11 +155,13 @@ def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=No
     dsa.dsa_sparse_gqa_decode(geom, q, K, V, tcap, i32(lens_np), sel, nsel, out)
     torch.cuda.synchronize()
     res = dict(lens=list(lens), topk=topk, tcap=tcap, R=R, B=B,
-               summ=summ.cpu().numpy().reshape(B, G, R, P), scale=scale.cpu().numpy().reshape(B, G, R),
+               summ=summ_logical(summ.cpu().numpy(), B, R), scale=scale.cpu().numpy().reshape(B, G, R),
                sel=sel.cpu().numpy().reshape(B, G, topk), nsel=nsel.cpu().numpy().reshape(B, G),
                scores=scores.cpu().numpy().reshape(B, G, R), out=bf16_np(out).reshape(B, HQ, D),
                oracle={}, dev=dict(K=K, V=V, q=q, geom=geom))
     hq, hiq, hz = host_queries(seed, B)
+    if zero_z:
+        hz = np.zeros_like(hz)
     for b in (range(B) if check_seqs is None else check_seqs):
         L = lens[b]
         ikh = gi.host_index_k(seed, tcap, G, P, b, 0, L, planted)

@@ -69,16 +69,17 @@ def test_null_geometry_and_pointers(lib):
     assert lib.dsa_compress_regions(None, 1, vp, 64, vp, vp, 1, vp, vp, None) == 1
     g = dsa.geometry()
     assert lib.dsa_compress_regions(ctypes.byref(g), 1, None, 64, vp, vp, 1, vp, vp, None) == 1
-    assert lib.dsa_compress_regions(ctypes.byref(g), 1, vp, 60, vp, vp, 1, vp, vp, None) == 1  # tcap % 8
-    assert lib.dsa_sparse_gqa_decode(ctypes.byref(g), 1, None, vp, vp, 64, vp, vp, vp, vp, vp, 1 << 20, None) == 1
+    assert lib.dsa_compress_regions(ctypes.byref(g), 1, vp, 60, vp, vp, 1, vp, vp, None) == 1  # tcap % 128
+    assert lib.dsa_compress_regions(ctypes.byref(g), 1, vp, 192, vp, vp, 1, vp, vp, None) == 1
+    assert lib.dsa_sparse_gqa_decode(ctypes.byref(g), 1, None, vp, vp, 128, vp, vp, vp, vp, vp, 1 << 20, None) == 1
 
 
 def test_empty_work_is_a_no_op(lib):
     g = dsa.geometry()
-    assert lib.dsa_compress_regions(ctypes.byref(g), 0, None, 64, None, None, 1, None, None, None) == 0
-    assert lib.dsa_score_topk(ctypes.byref(g), 0, None, None, None, None, 1, None, None, 64, 8, None, None, None,
+    assert lib.dsa_compress_regions(ctypes.byref(g), 0, None, 128, None, None, 1, None, None, None) == 0
+    assert lib.dsa_score_topk(ctypes.byref(g), 0, None, None, None, None, 1, None, None, 128, 8, None, None, None,
                               None, 0, None) == 0
-    assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 0, None, None, None, 1, None, None, 64, None, None, None,
+    assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 0, None, None, None, 1, None, None, 128, None, None, None,
                                       None) == 0
 
 
@@ -87,14 +88,14 @@ def test_workspace_checks(lib):
     vp = ctypes.c_void_p(256)
     need = lib.dsa_score_topk_workspace_size(ctypes.byref(g), 4, 1000)
     assert need >= 4 * 4 * 1000 * 4
-    rc = lib.dsa_score_topk(ctypes.byref(g), 4, vp, vp, vp, vp, 1, vp, vp, 8000, 1000, vp, vp, None, vp, need - 1,
+    rc = lib.dsa_score_topk(ctypes.byref(g), 4, vp, vp, vp, vp, 1, vp, vp, 8192, 1000, vp, vp, None, vp, need - 1,
                             None)
     assert rc == 3
-    rc = lib.dsa_score_topk(ctypes.byref(g), 4, vp, vp, vp, vp, 1, vp, vp, 8000, 1000, vp, vp, None,
+    rc = lib.dsa_score_topk(ctypes.byref(g), 4, vp, vp, vp, vp, 1, vp, vp, 8192, 1000, vp, vp, None,
                             ctypes.c_void_p(260), need, None)
     assert rc == 1  # misaligned workspace
     need = lib.dsa_sparse_gqa_workspace_size(ctypes.byref(g), 3)
-    rc = lib.dsa_sparse_gqa_decode(ctypes.byref(g), 3, vp, vp, vp, 64, vp, vp, vp, vp, vp, need - 1, None)
+    rc = lib.dsa_sparse_gqa_decode(ctypes.byref(g), 3, vp, vp, vp, 128, vp, vp, vp, vp, vp, need - 1, None)
     assert rc == 3
 
 

@@ -29,7 +29,7 @@ def test_compress_bit_exact_in_two_calls():
     dsa.dsa_compress_regions(geom, ik, tcap, H.i32(np.zeros(B)), H.i32(mids), R, summ, scale)
     dsa.dsa_compress_regions(geom, ik, tcap, H.i32(mids), H.i32(ends), R, summ, scale)
     torch.cuda.synchronize()
-    s = summ.cpu().numpy().reshape(B, G, R, P)
+    s = H.summ_logical(summ.cpu().numpy(), B, R)
     sc = scale.cpu().numpy().reshape(B, G, R)
     for b, L in enumerate(lens):
         nr = L // 8
@@ -56,6 +56,17 @@ def test_decode_end_to_end(lens, topk):
     H.assert_decode_parity(r)
 
 
+def test_decode_all_equal_scores_take_the_lowest_regions():
+    """Every score is 0 (z = 0): the level-0 digit holds all candidates, the short list cannot hold
+    them, and the selection falls back to exact narrowing; ties go to the lowest regions."""
+    r = H.run_dsa_decode(0xDE, [40000, 9000], topk=512, zero_z=True)
+    H.assert_decode_parity(r)
+    for b, L in enumerate([40000, 9000]):
+        c = (L - 1) // 8
+        for g in range(G):
+            assert r["sel"][b, g, :512].tolist() == list(range(511)) + [c]
+
+
 def test_decode_attention_on_oracle_selection():
     """Sparse GQA alone: the oracle's selection is fed to the GPU kernel, every head compared."""
     seed = 0xD7
@@ -79,7 +90,7 @@ def _prefill(seed, seqs, topk=512, check_every=1):
     """seqs: list of (P0, n) -- each sequence has a prefix of P0 tokens and a chunk of n new queries.
     Queries of all sequences are interleaved to exercise mixed-sequence query blocks when len(seqs)>1."""
     B = len(seqs)
-    tcap = H.round8(max(p0 + n for p0, n in seqs))
+    tcap = H.round128(max(p0 + n for p0, n in seqs))
     R = tcap // 8
     geom = dsa.geometry(topk=topk)
     ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
@@ -159,6 +170,16 @@ def test_prefill_mixed_sequences_and_small_topk():
     _prefill(0xE1, [(2000, 40), (511, 37), (8, 20)], topk=100, check_every=3)
 
 
+def test_prefill_beyond_8192_regions():
+    # ~8,750 candidate regions per query: the 1024-thread register selection
+    _prefill(0xE3, [(69997, 70)], topk=512, check_every=7)
+
+
+def test_prefill_beyond_32768_regions():
+    # ~33,800 candidate regions per query: selection by radix narrowing in global memory
+    _prefill(0xE4, [(270001, 64)], topk=512, check_every=16)
+
+
 def test_prefill_short_chunk_uses_decode_tiling():
     _prefill(0xE2, [(1200, 20)], topk=512)
 
@@ -230,7 +251,7 @@ def test_decode_step_replays_from_a_hip_graph():
     seed = 0xAB
     lens = [3000, 1505]
     B, topk = len(lens), 512
-    tcap = H.round8(max(lens))
+    tcap = H.round128(max(lens))
     R = tcap // 8
     geom = dsa.geometry(topk=topk)
     ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
