@@ -119,7 +119,7 @@ def setup_decode(cfg, steps_hint=1):
     V = torch.empty(B * G * tcap * D, dtype=torch.bfloat16, device="cuda")
     gi.dev_tokens(ik.data_ptr(), s, seed, gi.TID_IK, B, tcap, G, P, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR,
                   gi.IK_SCALE, cfg["planted"])
-    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR)
+    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_KTILED)
     gi.dev_tokens(V.data_ptr(), s, seed, gi.TID_V, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_REGION_T)
     q = torch.empty(B * HQ * D, dtype=torch.bfloat16, device="cuda")
     iq = torch.empty(B * HI * P, dtype=torch.bfloat16, device="cuda")
@@ -175,7 +175,7 @@ def setup_prefill(cfg):
     V = torch.empty(G * tcap * D, dtype=torch.bfloat16, device="cuda")
     gi.dev_tokens(ik.data_ptr(), s, seed, gi.TID_IK, 1, tcap, G, P, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR,
                   gi.IK_SCALE)
-    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, 1, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR)
+    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, 1, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_KTILED)
     gi.dev_tokens(V.data_ptr(), s, seed, gi.TID_V, 1, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_REGION_T)
     q = torch.empty(n * HQ * D, dtype=torch.bfloat16, device="cuda")
     iq = torch.empty(n * HI * P, dtype=torch.bfloat16, device="cuda")

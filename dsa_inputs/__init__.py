@@ -28,7 +28,7 @@ SEED_BASE = 0xD5A00000
 TID_Q, TID_K, TID_V, TID_IK, TID_IQ, TID_Z, TID_MASK, TID_COEF = 1, 2, 3, 4, 5, 6, 7, 9
 IK_SCALE = 1.0 / 16.0
 
-LAYOUT_GROUP_MAJOR, LAYOUT_REGION_T, LAYOUT_TOKEN_MAJOR = 0, 1, 2
+LAYOUT_GROUP_MAJOR, LAYOUT_REGION_T, LAYOUT_TOKEN_MAJOR, LAYOUT_KTILED = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBDIR = os.path.join(_HERE, "lib")

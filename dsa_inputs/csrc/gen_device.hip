@@ -8,6 +8,9 @@
  *   GEN_L_REGION_T    : out[(((b*G + g)*(tcap/8) + s/8)*C + c)*8 + s%8], s = t % tmod
  *                       (8 consecutive tokens of one channel are contiguous)
  *   GEN_L_TOKEN_MAJOR : out[((b*nt + (t - t0))*G + g)*C + c]
+ *   GEN_L_KTILED      : out[((b*G + g)*(tcap/8) + s/8)*1536 + koff(s%8, c)], C = 192, with
+ *                       koff(p, c) = ((((p/4)*6 + (c%48)/8)*4 + c/48)*4 + p%4)*8 + c%8
+ *                       (the attention library's key layout: MFMA A-operand order)
  * tmod is the ring size for ring buffers, or >= tcap for plain caches.
  */
 #include <hip/hip_runtime.h>
@@ -17,6 +20,7 @@
 #define GEN_L_GROUP_MAJOR 0
 #define GEN_L_REGION_T 1
 #define GEN_L_TOKEN_MAJOR 2
+#define GEN_L_KTILED 3
 
 struct GenTok {
   uint64_t key, kmask, kcoef;
@@ -31,6 +35,11 @@ __device__ static inline uint64_t gen_phys(const GenTok& a, int64_t b, int64_t t
     return (((uint64_t)b * a.nt + (uint64_t)(t - a.t0)) * a.G + g) * a.C + c;
   int64_t s = t % a.tmod;
   if (a.layout == GEN_L_GROUP_MAJOR) return (((uint64_t)b * a.G + g) * a.tcap + s) * a.C + c;
+  if (a.layout == GEN_L_KTILED) {
+    const int64_t p = s % 8;
+    return (((uint64_t)b * a.G + g) * (a.tcap / 8) + s / 8) * 1536 +
+           (uint64_t)(((((p / 4) * 6 + (c % 48) / 8) * 4 + c / 48) * 4 + p % 4) * 8 + c % 8);
+  }
   return ((((uint64_t)b * a.G + g) * (a.tcap / 8) + s / 8) * a.C + c) * 8 + (s % 8);
 }
 
@@ -82,8 +91,10 @@ int dsagen_dev_tokens(uint64_t seed, uint32_t tid, uint32_t tid_mask, uint32_t t
                       int64_t nt, int64_t tcap, int64_t tmod, int32_t layout, float scale,
                       uint16_t* out, hipStream_t stream) {
   if (B <= 0 || nt <= 0) return 0;
-  if (layout < 0 || layout > 2 || G <= 0 || C <= 0 || t0 < 0 || t0 + nt > T) return 1;
-  if (layout != GEN_L_TOKEN_MAJOR && (tmod <= 0 || tcap <= 0 || (layout == GEN_L_REGION_T && (tcap % 8 || tmod % 8))))
+  if (layout < 0 || layout > 3 || G <= 0 || C <= 0 || t0 < 0 || t0 + nt > T) return 1;
+  if (layout == GEN_L_KTILED && C != 192) return 1;
+  if (layout != GEN_L_TOKEN_MAJOR &&
+      (tmod <= 0 || tcap <= 0 || ((layout == GEN_L_REGION_T || layout == GEN_L_KTILED) && (tcap % 8 || tmod % 8))))
     return 1;
   if (layout != GEN_L_TOKEN_MAJOR && tmod > tcap) return 1;
   GenTok a;

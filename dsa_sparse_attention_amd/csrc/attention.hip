@@ -11,9 +11,10 @@
 // query heads of the group are the N = 16 side of v_mfma_f32_16x16x32_bf16,
 // so GQA maps onto the matrix cores without padding.  Regions are consumed
 // four at a time (32 tokens):
-//   S^T[token][head] = K(32x192) . Q^T  -> 2 tiles x 6 k-steps, A = K rows
-//     straight from HBM (lane: one token, 48 contiguous channels), B = Q^T in
-//     registers.  Tile t row m holds token 8*(m/4) + 4t + m%4, which leaves
+//   S^T[token][head] = K(32x192) . Q^T  -> 2 tiles x 6 k-steps, A = K read
+//     straight from the region-tiled K layout (one 16-byte load = 8 channels
+//     of one token; a wave's load = four contiguous 256-byte pieces), B = Q^T
+//     in registers.  Tile t row m holds token 8*(m/4) + 4t + m%4, which leaves
 //     every lane with the 8 tokens of one region in order;
 //   O^T[dv][head] += V^T(192x32) . P^T  -> 12 tiles, A = V^T read straight
 //     from the region-transposed V layout (one 16-byte load = the 8 tokens of
@@ -29,8 +30,8 @@ namespace dsa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One region as the core sees it: 8 K rows of D channels (contiguous), one V
-// pack [D][8], and the range [lo, hi] of valid positions inside the region
+// One region as the core sees it: its 1536 keys (region-tiled), its V pack
+// [D][8], and the range [lo, hi] of valid positions inside the region
 // (lo > hi: nothing valid).
 struct Region {
   const uint16_t* k;
@@ -58,72 +59,86 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int64_t qrow, int g, b
   for (int s = 0; s < 6; ++s) qb[s] = as_bf16x8(ld16(p + 8 * s));
 }
 
-// Processes 4 regions. ra = region of this lane's K rows (entry n/4), rb =
-// region of this lane's softmax weights and V pack (entry kb).
-__device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], const Region& ra,
-                                           const Region& rb, float scale_log2) {
+// The 4-region chunk as held in registers between its loads and its use:
+// K rows of tile 0 and tile 1 (lane: one token, 48 channels) and the 12
+// V^T operands (lane: one channel, the 8 tokens of region kb), plus the valid
+// position range of the lane's softmax region.
+struct ChunkRegs {
+  u32x4 k0[6], k1[6], v[12];
+  int lo, hi;
+};
+
+// Issues the chunk's loads. ra = region of this lane's K rows (entry n/4),
+// rb = region of this lane's softmax weights and V pack (entry kb).
+__device__ __forceinline__ void core_load(ChunkRegs& c, const Region& ra, const Region& rb) {
   const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
-  u32x4 kv0[6], kv1[6], vv[12];
-  const uint16_t* k0 = ra.k + (int64_t)(n & 3) * kHeadDim + 48 * kb;
-  const uint16_t* k1 = k0 + 4 * kHeadDim;
+  // region-tiled K: unit ((t*6 + s)*4 + kb)*4 + (n&3) holds token 4t + n%4,
+  // channels 48kb + 8s .. +7
+  const uint16_t* kp = ra.k + (kb * 4 + (n & 3)) * 8;
 #pragma unroll
   for (int s = 0; s < 6; ++s) {
-    kv0[s] = ld16(k0 + 8 * s);
-    kv1[s] = ld16(k1 + 8 * s);
+    c.k0[s] = ld16(kp + (s * 16) * 8);
+    c.k1[s] = ld16(kp + ((6 + s) * 16) * 8);
   }
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) vv[nt] = ld16(rb.v + (16 * nt + n) * 8);
+  for (int nt = 0; nt < 12; ++nt) c.v[nt] = ld16(rb.v + (16 * nt + n) * 8);
+  c.lo = rb.lo;
+  c.hi = rb.hi;
+}
 
+// S^T tiles, online softmax update, O^T += V^T P^T for one loaded chunk.
+__device__ __forceinline__ void core_compute(CoreState& st, const bf16x8 qb[6], ChunkRegs& c, float scale_log2) {
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 6; ++s) {
-    s0 = mfma16x16x32(as_bf16x8(kv0[s]), qb[s], s0);
-    s1 = mfma16x16x32(as_bf16x8(kv1[s]), qb[s], s1);
+    s0 = mfma16x16x32(as_bf16x8(c.k0[s]), qb[s], s0);
+    s1 = mfma16x16x32(as_bf16x8(c.k1[s]), qb[s], s1);
   }
   float sv[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sv[i] = (i >= rb.lo && i <= rb.hi) ? s0[i] * scale_log2 : -INFINITY;
-    sv[4 + i] = (4 + i >= rb.lo && 4 + i <= rb.hi) ? s1[i] * scale_log2 : -INFINITY;
+    sv[i] = (i >= c.lo && i <= c.hi) ? s0[i] * scale_log2 : -INFINITY;
+    sv[4 + i] = (4 + i >= c.lo && 4 + i <= c.hi) ? s1[i] * scale_log2 : -INFINITY;
   }
   float cmax = sv[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[i]);
   cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+  // Lazy rescaling: the reference max m only moves (and O, l are rescaled)
+  // when some head's running max exceeds it by more than 8 (log2 units), so
+  // every weight exp2(s - m) stays <= 256 and most chunks skip the rescale.
+  // The first chunk with a valid score always moves m off -inf.
   const float m_new = fmaxf(st.m, cmax);
-  float alpha = 1.0f;
-  float p[8];
-  if (m_new == -INFINITY) {
+  if (__any(m_new > st.m + 8.0f)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 when st.m = -inf
+    st.l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = 0.0f;
-  } else {
-    alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+    for (int nt = 0; nt < 12; ++nt) st.o[nt] *= alpha;
+    st.m = m_new;
   }
-  float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
+  const float m_use = st.m == -INFINITY ? 0.0f : st.m;  // all masked so far: weights stay 0
+  float p[8];
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) st.o[nt] *= alpha;
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 
   // zero V of masked positions (only regions at the causal/window edge)
-  const bool full = (rb.lo <= 0 && rb.hi >= 7);
+  const bool full = (c.lo <= 0 && c.hi >= 7);
   if (__any(!full)) {
     uint32_t mk[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const bool a0 = (2 * w >= rb.lo && 2 * w <= rb.hi);
-      const bool a1 = (2 * w + 1 >= rb.lo && 2 * w + 1 <= rb.hi);
+      const bool a0 = (2 * w >= c.lo && 2 * w <= c.hi);
+      const bool a1 = (2 * w + 1 >= c.lo && 2 * w + 1 <= c.hi);
       mk[w] = (a0 ? 0x0000FFFFu : 0u) | (a1 ? 0xFFFF0000u : 0u);
     }
 #pragma unroll
     for (int nt = 0; nt < 12; ++nt) {
-      vv[nt].x &= mk[0];
-      vv[nt].y &= mk[1];
-      vv[nt].z &= mk[2];
-      vv[nt].w &= mk[3];
+      c.v[nt].x &= mk[0];
+      c.v[nt].y &= mk[1];
+      c.v[nt].z &= mk[2];
+      c.v[nt].w &= mk[3];
     }
   }
   u32x4 pp;
@@ -133,7 +148,48 @@ __device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], co
   pp.w = pack_bf16x2(p[6], p[7]);
   const bf16x8 pb = as_bf16x8(pp);
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) st.o[nt] = mfma16x16x32(as_bf16x8(vv[nt]), pb, st.o[nt]);
+  for (int nt = 0; nt < 12; ++nt) st.o[nt] = mfma16x16x32(as_bf16x8(c.v[nt]), pb, st.o[nt]);
+}
+
+// One chunk, loads then compute (no overlap).
+__device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], const Region& ra,
+                                           const Region& rb, float scale_log2) {
+  ChunkRegs c;
+  core_load(c, ra, rb);
+  core_compute(st, qb, c, scale_log2);
+}
+
+// A run of chunks with the next chunk's loads in flight while the current
+// one computes.  region_of(e, lane) gives the Region for list entry e as seen
+// by this lane; entries >= n are invalid.
+#ifndef DSA_ATTN_PIPELINE
+#define DSA_ATTN_PIPELINE 1
+#endif
+#ifndef DSA_ATTN_WAVES
+#define DSA_ATTN_WAVES 1
+#endif
+template <class RegionOf>
+__device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int64_t n, const RegionOf& region_of,
+                                         float scale_log2) {
+  const int lane = threadIdx.x & 63, nn = lane & 15, kb = lane >> 4;
+  if (n <= 0) return;
+  if (!DSA_ATTN_PIPELINE) {
+    // one chunk in registers per wave; several waves per SIMD overlap the loads
+    for (int64_t e0 = 0; e0 < n; e0 += 4) core_chunk(st, qb, region_of(e0 + (nn >> 2)), region_of(e0 + kb), scale_log2);
+    return;
+  }
+  // The prefetch is issued unconditionally (past the end it reads the dummy
+  // region of an invalid entry), so the wait before each compute only covers
+  // the chunk being used and not the one in flight behind it.
+  ChunkRegs b0, b1;
+  core_load(b0, region_of(nn >> 2), region_of(kb));
+  for (int64_t e0 = 0; e0 < n; e0 += 8) {
+    core_load(b1, region_of(e0 + 4 + (nn >> 2)), region_of(e0 + 4 + kb));
+    core_compute(st, qb, b0, scale_log2);
+    if (e0 + 4 >= n) break;
+    core_load(b0, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
+    core_compute(st, qb, b1, scale_log2);
+  }
 }
 
 // Total softmax denominator of the lane's head (sum over the 4 kb lanes).
@@ -305,32 +361,42 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-__global__ __launch_bounds__(256) void k_sgqa_prefill(PrefillArgs a) {
-  const int64_t qi = blockIdx.x;
-  const int g = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
-  int32_t s = a.qseq[qi];
+// Block = 4 waves = 4 consecutive queries of one KV group; blocks are ordered
+// group-major, so at any time the GPU works through one group's K/V (a
+// quarter of the cache), which keeps the gathered regions cache-resident.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES, DSA_ATTN_WAVES)))
+void k_sgqa_prefill(PrefillArgs a) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nqb = (a.nq + 3) / 4;
+  const int g = blockIdx.x / nqb;
+  const int64_t qi = (int64_t)(blockIdx.x % nqb) * 4 + wave;
+  __shared__ int32_t ids[4][kMaxTopk];
+  const bool live = qi < a.nq;
+  int32_t s = live ? a.qseq[qi] : 0;
   s = s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
-  int64_t p = a.qpos[qi];
+  int64_t p = live ? a.qpos[qi] : 0;
   p = p < 0 ? 0 : (p >= a.tcap ? a.tcap - 1 : p);
   const int64_t sg = (int64_t)s * kGroups + g;
   const uint16_t* kbase = a.k + sg * a.tcap * kHeadDim;
   const uint16_t* vbase = a.v + sg * (a.tcap / kRegion) * kHeadDim * kRegion;
   const int64_t pg = qi * kGroups + g;
-  const int32_t* lst = a.sel + pg * a.topk;
-  int32_t cnt = a.nsel[pg];
+  int32_t cnt = live ? a.nsel[pg] : 0;
   cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
+  const int32_t* lst = a.sel + pg * a.topk;
+  for (int i = lane; i < cnt; i += 64) ids[wave][i] = lst[i];  // wave-private slice
+  __syncthreads();
+  if (!live) return;
 
   bf16x8 qb[6];
   load_q(a.q, qi, g, qb);
   CoreState st;
   core_init(st);
-  for (int e0 = 0; e0 < cnt; e0 += 4) {
-    const int ea = e0 + (n >> 2), eb = e0 + kb;
-    const Region ra = dsa_region(kbase, vbase, ea < cnt ? lst[ea] : -1, p);
-    const Region rb = dsa_region(kbase, vbase, eb < cnt ? lst[eb] : -1, p);
-    core_chunk(st, qb, ra, rb, a.scale_log2);
-  }
+  const int32_t* my = ids[wave];
+  auto region_of = [&](int64_t e) -> Region {
+    return dsa_region(kbase, vbase, e < cnt ? my[e] : -1, p);
+  };
+  core_run(st, qb, cnt, region_of, a.scale_log2);
   core_store(st, a.out, qi, g);
 }
 
@@ -349,7 +415,7 @@ struct SwaArgs {
   const uint16_t* k_ring;
   const uint16_t* v_ring;
   uint16_t* out;
-  uint16_t* st_k;  // [S][G][nst][8][D]
+  uint16_t* st_k;  // [S][G][nst][1536] region-tiled
   uint16_t* st_v;  // [S][G][nst][D][8]
   int32_t n_seqs, max_new, nst, window;
   int64_t rows;
@@ -378,21 +444,21 @@ __global__ __launch_bounds__(256) void k_swa_stage(SwaArgs a) {
   for (int e = threadIdx.x; e < kGroups * kHeadDim; e += 256) {
     const int g = e / kHeadDim, d = e - g * kHeadDim;
     const int64_t sg = (int64_t)s * kGroups + g;
-    uint16_t* sk = a.st_k + ((sg * a.nst + j) * kRegion) * kHeadDim + d;
+    uint16_t* sk = a.st_k + (sg * a.nst + j) * kRegionElems;
     uint16_t* sv = a.st_v + ((sg * a.nst + j) * kHeadDim + d) * kRegion;
     for (int t = 0; t < kRegion; ++t) {
       const int64_t pos = base_pos + t;
       uint16_t kv = 0, vv = 0;
       if (pos < p0) {
         const int64_t slot = pos % W;
-        kv = a.k_ring[(sg * W + slot) * kHeadDim + d];
+        kv = a.k_ring[(sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, d)];
         vv = a.v_ring[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion];
       } else if (pos < p0 + nnew) {
         const int64_t row = r0 + (pos - p0);
         kv = a.k_new[(row * kGroups + g) * kHeadDim + d];
         vv = a.v_new[(row * kGroups + g) * kHeadDim + d];
       }
-      sk[(int64_t)t * kHeadDim] = kv;
+      sk[k_tile_offset(t, d)] = kv;
       sv[t] = vv;
     }
   }
@@ -422,32 +488,27 @@ __global__ __launch_bounds__(256) void k_swa_attend(SwaArgs a) {
   CoreState st;
   core_init(st);
   const int64_t nreg = rhi - rlo + 1;
-  for (int64_t e0 = 0; e0 < nreg; e0 += 4) {
-    Region rr[2];
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int64_t e = e0 + (w == 0 ? (n >> 2) : kb);
-      Region rg;
-      if (e >= nreg) {
-        rg.k = rk; rg.v = rv; rg.lo = 1; rg.hi = 0;
-      } else {
-        const int64_t r = rlo + e;
-        if (r < rst) {
-          const int64_t pk = r % (W / kRegion);
-          rg.k = rk + pk * kRegion * kHeadDim;
-          rg.v = rv + pk * kHeadDim * kRegion;
-        } else {
-          rg.k = sk + (r - rst) * kRegion * kHeadDim;
-          rg.v = sv + (r - rst) * kHeadDim * kRegion;
-        }
-        const int64_t first = r * kRegion;
-        rg.lo = (int)((lo > first ? lo : first) - first);
-        rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
-      }
-      rr[w] = rg;
+  auto region_of = [&](int64_t e) -> Region {
+    Region rg;
+    if (e >= nreg) {
+      rg.k = rk; rg.v = rv; rg.lo = 1; rg.hi = 0;
+      return rg;
     }
-    core_chunk(st, qb, rr[0], rr[1], a.scale_log2);
-  }
+    const int64_t r = rlo + e;
+    if (r < rst) {
+      const int64_t pk = r % (W / kRegion);
+      rg.k = rk + pk * kRegion * kHeadDim;
+      rg.v = rv + pk * kHeadDim * kRegion;
+    } else {
+      rg.k = sk + (r - rst) * kRegion * kHeadDim;
+      rg.v = sv + (r - rst) * kHeadDim * kRegion;
+    }
+    const int64_t first = r * kRegion;
+    rg.lo = (int)((lo > first ? lo : first) - first);
+    rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
+    return rg;
+  };
+  core_run(st, qb, nreg, region_of, a.scale_log2);
   core_store(st, a.out, row, g);
 }
 
@@ -464,7 +525,8 @@ __global__ __launch_bounds__(256) void k_ring_append(SwaArgs a, uint16_t* k_ring
   for (int e = threadIdx.x; e < kGroups * kHeadDim; e += 256) {
     const int g = e / kHeadDim, d = e - g * kHeadDim;
     const int64_t sg = (int64_t)s * kGroups + g;
-    k_ring[(sg * W + slot) * kHeadDim + d] = a.k_new[(row * kGroups + g) * kHeadDim + d];
+    k_ring[(sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, d)] =
+        a.k_new[(row * kGroups + g) * kHeadDim + d];
     v_ring[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion] =
         a.v_new[(row * kGroups + g) * kHeadDim + d];
   }
@@ -537,7 +599,8 @@ extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n
   a.scale_log2 = geom->softmax_scale * kLog2e;
   {
     ProfScope prof_("k_sgqa_prefill", as_stream(stream));
-    hipLaunchKernelGGL(k_sgqa_prefill, dim3(n_queries), dim3(256), 0, as_stream(stream), a);
+    hipLaunchKernelGGL(k_sgqa_prefill, dim3((unsigned)(kGroups * ((n_queries + 3) / 4))), dim3(256), 0,
+                       as_stream(stream), a);
   }
   return check_launch("dsa_sparse_gqa_prefill");
 }

@@ -31,6 +31,17 @@ constexpr int kTcapAlign = 128;  // cache capacity granule: 16 regions = one sum
 // B operand (lane 16*kb + n <- region n, channels 64q + 16kb .. +15).
 __device__ __forceinline__ int64_t summ_tile_base(int64_t r) { return (r >> 4) * 4096; }
 
+// Keys are stored per region of 8 tokens (1536 bf16) in MFMA A-operand
+// order: element (token pos of the region, channel d) lives at
+//   ((((pos/4)*6 + (d%48)/8)*4 + d/48)*4 + pos%4)*8 + d%8,
+// i.e. 16-byte units ordered (tile pos/4, k-step (d%48)/8, lane slot d/48,
+// token pos%4): one 64-lane load of a 4-region chunk reads four contiguous
+// 256-byte pieces.
+constexpr int kRegionElems = kRegion * kHeadDim;  // 1536
+__device__ __forceinline__ int k_tile_offset(int pos, int d) {
+  return ((((pos >> 2) * 6 + (d % 48) / 8) * 4 + d / 48) * 4 + (pos & 3)) * 8 + (d & 7);
+}
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -38,16 +49,15 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

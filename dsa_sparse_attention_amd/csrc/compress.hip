@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ i
 }
 
 // One block per new token row: copies K/V (and index_k) into the cache
-// layouts (V region-transposed).
+// layouts (K region-tiled, V region-transposed).
 __global__ __launch_bounds__(256) void k_cache_write(
     const int32_t* __restrict__ tok_seq, const int32_t* __restrict__ tok_pos,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) void k_cache_write(
   for (int e = threadIdx.x; e < kGroups * kHeadDim; e += blockDim.x) {
     const int g = e / kHeadDim, d = e - g * kHeadDim;
     const int64_t sg = (int64_t)s * kGroups + g;
-    k_cache[(sg * tcap + t) * kHeadDim + d] = k_new[i * kGroups * kHeadDim + e];
+    k_cache[(sg * R + t / kRegion) * kRegionElems + k_tile_offset((int)(t % kRegion), d)] =
+        k_new[i * kGroups * kHeadDim + e];
     v_cache[((sg * R + t / kRegion) * kHeadDim + d) * kRegion + (t % kRegion)] =
         v_new[i * kGroups * kHeadDim + e];
   }

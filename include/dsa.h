@@ -38,7 +38,10 @@
  * Cache layouts (per sequence b of a batch, capacity tcap tokens, tcap a
  * multiple of 128; region r = tokens 8r..8r+7; R = tcap/8):
  *   index_k  [B][G][tcap][P]    bf16   indexer keys
- *   K        [B][G][tcap][D]    bf16   keys (post-RoPE)
+ *   K        [B][G][R][1536]    bf16   keys (post-RoPE), region-tiled: key
+ *                                      channel d of token 8r+p is element
+ *                                      ((((p/4)*6 + (d%48)/8)*4 + d/48)*4
+ *                                      + p%4)*8 + d%8 of region r's 1536
  *   V        [B][G][R][D][8]    bf16   values, "region-transposed": the 8
  *                                      tokens of one region are contiguous
  *                                      for each channel
@@ -49,7 +52,7 @@
  *                                      within that (b, g)'s R*256 bytes
  *   scale    [B][G][R]          fp32   per-(region, group) summary scale
  * Sliding-window ring (window W = 512, slot of position t = t mod W):
- *   k_ring   [S][G][W][D]       bf16
+ *   k_ring   [S][G][W/8][1536]  bf16   region-tiled like K (8-slot regions)
  *   v_ring   [S][G][W/8][D][8]  bf16   region-transposed like V
  */
 #ifndef DSA_MI355X_H

@@ -38,6 +38,12 @@ def round128(x):
     return (x + 127) // 128 * 128
 
 
+def ktiled_logical(k_np, B, T):
+    """Region-tiled keys [B][G][T/8][1536] -> [B][G][T][D] (layout of include/dsa.h)."""
+    t = k_np.reshape(B, G, T // 8, 2, 6, 4, 4, 8)  # region, pos/4, (d%48)/8, d/48, pos%4, d%8
+    return t.transpose(0, 1, 2, 3, 6, 5, 4, 7).reshape(B, G, T, D)
+
+
 def summ_logical(summ_np, B, R):
     """The library's tiled summary bytes [B][G][R/16][4096] -> [B][G][R][P] (layout of include/dsa.h)."""
     t = summ_np.reshape(B, G, R // 16, 4, 4, 16, 16)  # tile, j/64, (j%64)/16, r%16, j%16
@@ -137,7 +143,7 @@ def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=No
     R = tcap // 8
     geom = dsa.geometry(topk=topk)
     ik = dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE, planted)
-    K = dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_GROUP_MAJOR)
+    K = dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_KTILED)
     V = dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
     q, iq, z = dev_queries(seed, B)
     if zero_z:  # every score 0: selection falls to the lowest regions (tie rule)

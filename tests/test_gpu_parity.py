@@ -94,7 +94,7 @@ def _prefill(seed, seqs, topk=512, check_every=1):
     R = tcap // 8
     geom = dsa.geometry(topk=topk)
     ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
-    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_GROUP_MAJOR)
+    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_KTILED)
     V = H.dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
     summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
     scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
@@ -204,7 +204,7 @@ def test_swa_batched_decode_with_prefilled_rings():
         t0 = max(0, p - H.W)
         if p > t0:
             # write positions t0..p-1 of sequence s (logical batch index s) into its ring
-            for layout, ring, tid in ((gi.LAYOUT_GROUP_MAJOR, k_ring, tk), (gi.LAYOUT_REGION_T, v_ring, tv)):
+            for layout, ring, tid in ((gi.LAYOUT_KTILED, k_ring, tk), (gi.LAYOUT_REGION_T, v_ring, tv)):
                 tmp = torch.empty((s + 1) * per, dtype=H.BF16, device="cuda")
                 gi.dev_tokens(tmp.data_ptr(), H.stream_ptr(), seed, tid, s + 1, T, G, D, t0, p - t0, H.W, H.W,
                               layout, 1.0)
@@ -231,7 +231,7 @@ def test_swa_batched_decode_with_prefilled_rings():
     # the append then leaves each ring holding positions p-511..p
     dsa.swa_ring_append(geom, H.W, 1, H.i32(pos), H.i32(np.arange(S + 1)), kn, vn, k_ring, v_ring)
     torch.cuda.synchronize()
-    kr = k_ring.view(torch.int16).cpu().numpy().reshape(S, G, H.W, D).view(np.uint16)
+    kr = H.ktiled_logical(k_ring.view(torch.int16).cpu().numpy().view(np.uint16), S, H.W)
     for s, p in enumerate(pos):
         Kh = gi.host_tokens_bf16(seed, tk, T, G, D, s, 0, p + 1)
         for t in range(max(0, p - H.W + 1), p + 1):
@@ -255,7 +255,7 @@ def test_decode_step_replays_from_a_hip_graph():
     R = tcap // 8
     geom = dsa.geometry(topk=topk)
     ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
-    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_GROUP_MAJOR)
+    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_KTILED)
     V = H.dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
     q, iq, z = H.dev_queries(seed, B)
     lens_np = np.asarray(lens, dtype=np.int32)
@@ -300,3 +300,39 @@ def test_decode_step_replays_from_a_hip_graph():
         step(other)
         torch.cuda.synchronize()
         assert torch.equal(other["out"].view(torch.uint8), ref["out"].view(torch.uint8))
+
+
+def test_cache_write_produces_the_documented_layouts():
+    """dsa_cache_write of token-major rows gives the same bytes as the generator's direct fill of the
+    group-major index_k, region-tiled K and region-transposed V caches."""
+    seed = 0xCA
+    B, T, tcap = 2, 300, 384
+    geom = dsa.geometry()
+    ref_k = H.dev_cache(seed, gi.TID_K, B, T, D, tcap, gi.LAYOUT_KTILED)
+    ref_v = H.dev_cache(seed, gi.TID_V, B, T, D, tcap, gi.LAYOUT_REGION_T)
+    ref_ik = H.dev_cache(seed, gi.TID_IK, B, T, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
+    kn = H.dev_cache(seed, gi.TID_K, B, T, D, 0, gi.LAYOUT_TOKEN_MAJOR)
+    vn = H.dev_cache(seed, gi.TID_V, B, T, D, 0, gi.LAYOUT_TOKEN_MAJOR)
+    ikn = H.dev_cache(seed, gi.TID_IK, B, T, P, 0, gi.LAYOUT_TOKEN_MAJOR, gi.IK_SCALE)
+    k = torch.zeros_like(ref_k)
+    v = torch.zeros_like(ref_v)
+    ik = torch.zeros_like(ref_ik)
+    seqs = np.repeat(np.arange(B), T).astype(np.int32)
+    pos = np.tile(np.arange(T), B).astype(np.int32)
+    perm = np.random.default_rng(0).permutation(B * T)  # rows in any order
+    dsa.dsa_cache_write(geom, H.i32(seqs[perm]), H.i32(pos[perm]), kn.view(B * T, -1)[perm].contiguous().view(-1),
+                        vn.view(B * T, -1)[perm].contiguous().view(-1), ikn.view(B * T, -1)[perm].contiguous().view(-1),
+                        k, v, ik, B, tcap)
+    torch.cuda.synchronize()
+    # compare the written token range only (positions >= T stay zero in the written caches)
+    kt = H.ktiled_logical(k.view(torch.int16).cpu().numpy().view(np.uint16), B, tcap)
+    rt = H.ktiled_logical(ref_k.view(torch.int16).cpu().numpy().view(np.uint16), B, tcap)
+    assert np.array_equal(kt[:, :, :T], rt[:, :, :T]) and not kt[:, :, T:].any()
+    vv = v.view(torch.int16).cpu().numpy().reshape(B, G, tcap // 8, D, 8)
+    rv = ref_v.view(torch.int16).cpu().numpy().reshape(B, G, tcap // 8, D, 8)
+    vl = vv.transpose(0, 1, 2, 4, 3).reshape(B, G, tcap, D)
+    rl = rv.transpose(0, 1, 2, 4, 3).reshape(B, G, tcap, D)
+    assert np.array_equal(vl[:, :, :T], rl[:, :, :T])
+    ikw = ik.view(torch.int16).cpu().numpy().reshape(B, G, tcap, P)
+    ikr = ref_ik.view(torch.int16).cpu().numpy().reshape(B, G, tcap, P)
+    assert np.array_equal(ikw[:, :, :T], ikr[:, :, :T])
