@@ -363,12 +363,13 @@ def main():
                 step(cur_stream())
             torch.cuda.synchronize()
             del keep
-        # calibration: a plain copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)
+        # calibration: a plain elementwise shader kernel that reads exactly 1 GiB and writes
+        # exactly 1 GiB (torch.bitwise_not on uint8), for scaling the FETCH/WRITE counters
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         a.fill_(1)
         for _ in range(3):
-            b.copy_(a)
+            torch.bitwise_not(a, out=b)
         torch.cuda.synchronize()
         log("profile run done")
         return
