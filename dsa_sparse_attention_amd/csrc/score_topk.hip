@@ -15,14 +15,17 @@
 //    per 16-row MFMA tile), B = 16 regions x 32 channels of E4M3 codes turned
 //    into bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1).  The channel
 //    order inside one 256-d dot is permuted so that each lane reads 64
-//    contiguous bytes of one region; A uses the same permutation.  For decode
-//    it also builds a 4096-bin histogram of the top 12 bits of each score's
-//    order-preserving key (LDS atomics, flushed with integer atomics).
-//  * k_select (one block per (query, group)) finds the exact k-th largest
-//    64-bit key (score key << 32 | ~region) by radix narrowing: 12-bit digits
-//    over global memory until the candidates fit in LDS, then 8-bit digits in
-//    LDS.  Keys are unique, so ties go to the lower region exactly.  The
-//    selected regions are bitonic-sorted ascending.
+//    contiguous bytes of one region; A uses the same permutation.  Besides
+//    the scores it stores, per 16-region tile, the largest order-preserving
+//    score key of the tile.
+//  * Selection ranks regions by (score desc, region asc) with 32-bit keys and
+//    index order.  Short problems (c <= 8192) keep every key in registers and
+//    find the k-th key by bisection with block-wide ballot counts.  Long
+//    problems first select the need best tiles by their maxima: every region
+//    of the answer lies in them (a region outside them is beaten by the
+//    maxima of need tiles that all rank above it), so at most 511 tiles of 16
+//    regions are then ranked exactly.  A radix fallback in global memory
+//    covers problems beyond the register capacity.
 #include "common.hpp"
 
 namespace dsa {
@@ -30,8 +33,10 @@ namespace dsa {
 constexpr int kScoreRange = 1024;  // regions per k_score block
 constexpr int kTile = 16;          // regions per MFMA tile
 constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
-constexpr int kHistCopies = 8;     // decode histogram stripes (one per XCD by block index)
-constexpr int kSelCap = 4096;      // LDS candidate capacity of k_select
+constexpr int kHistCopies = 4;     // decode histogram stripes (by score block index)
+constexpr int kSelCap = 4096;      // LDS candidate capacity of the radix fallback
+constexpr int kCandCap = 1024;     // decode candidates at or above the level-0 digit
+constexpr int kDirectMax = 8192;   // longest problem selected straight from its scores
 
 struct ScoreArgs {
   const uint16_t* iq;   // [Nq][16][P]
@@ -42,12 +47,15 @@ struct ScoreArgs {
   const float* scale;   // [S][G][R]
   float* scores;        // workspace [Nq][G][ws_stride]
   float* scores_out;    // nullable [Nq][G][max_regions]
-  uint32_t* hist;       // [Nq][G][8][4096] striped level-0 histogram (decode only)
+  uint32_t* tilemax;    // nullable workspace [Nq][G][tm_stride]: largest key of each 16-region tile
+  uint32_t* hist;       // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts (zeroed beforehand)
   int64_t R;            // tcap / 8
-  int32_t nq, n_seqs, max_regions, ws_stride, topk;
+  int32_t nq, n_seqs, max_regions, ws_stride, tm_stride, topk;
 };
 
+// Order-preserving key of a score; NaN maps to 0 and ranks below every number.
 __device__ __forceinline__ uint32_t score_key(float s) {
+  if (s != s) return 0u;
   uint32_t u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0;  // -0 ranks as +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -152,9 +160,10 @@ constexpr int kDecDepth = DSA_SCORE_DEC_DEPTH;  // tiles in flight per wave
 // Decode scoring: one query per block, one (query, group) region range.
 // Each wave streams a contiguous run of 16-region tiles with kDecDepth tiles
 // of summary loads in flight; A holds the query's 4 heads of group g in rows
-// 0..3.  Lanes 0..15 turn MFMA rows 0..3 into the region's score, store it
-// and count its level-0 key digit in the block's LDS histogram, which is
-// flushed to the (query, group) histogram with integer atomics.
+// 0..3.  Lanes 0..15 turn MFMA rows 0..3 into the region's score and store
+// it; the tile's largest key is reduced over those 16 lanes and stored too.
+// When a.hist is set, the level-0 digits of the scores are counted in LDS
+// and added to one stripe of the (query, group) histogram at the end.
 __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   const int g = blockIdx.y;
   const int qi = blockIdx.z;
@@ -162,7 +171,8 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kb = lane >> 4;
   __shared__ uint32_t hist_lds[kHistBins];
-  for (int i = threadIdx.x; i < kHistBins; i += 256) hist_lds[i] = 0;
+  if (a.hist)
+    for (int i = threadIdx.x; i < kHistBins; i += 256) hist_lds[i] = 0;
 
   int32_t seq = a.qseq[qi];
   seq = seq < 0 ? 0 : (seq >= a.n_seqs ? a.n_seqs - 1 : seq);
@@ -191,6 +201,7 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   const int64_t pq = (int64_t)qi * kGroups + g;
   float* scores = a.scores + pq * a.ws_stride;
   float* scores_out = a.scores_out ? a.scores_out + pq * a.max_regions : nullptr;
+  uint32_t* tmax = a.tilemax ? a.tilemax + pq * a.tm_stride + w0 / kTile : nullptr;
 
   u32x4 buf[kDecDepth][4];
   float bsc[kDecDepth];
@@ -223,6 +234,7 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) acc = mfma16x16x32(A[s], B[s], acc);
       const int64_t r = w0 + (int64_t)t * kTile + n;
+      uint32_t key = 0;
       if (kb == 0 && r < w1) {
         float sv = zz[0] * fmaxf(acc[0], 0.0f);
         sv = fmaf(zz[1], fmaxf(acc[1], 0.0f), sv);
@@ -231,17 +243,27 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
         sv *= bsc[u];
         scores[r] = sv;
         if (scores_out) scores_out[r] = sv;
-        atomicAdd(&hist_lds[score_key(sv) >> 20], 1u);
+        key = score_key(sv);
+        if (a.hist) atomicAdd(&hist_lds[key >> 20], 1u);
+      }
+      if (tmax) {
+        key = max(key, (uint32_t)__shfl_xor((int)key, 8));
+        key = max(key, (uint32_t)__shfl_xor((int)key, 4));
+        key = max(key, (uint32_t)__shfl_xor((int)key, 2));
+        key = max(key, (uint32_t)__shfl_xor((int)key, 1));
+        if (lane == 0) tmax[t] = key;
       }
     }
   }
-  __syncthreads();
-  // blocks are dealt round-robin to the XCDs; striping the flush by block
-  // index keeps same-address atomics from all blocks off one counter
-  uint32_t* gh = a.hist + (pq * kHistCopies + (blockIdx.x % kHistCopies)) * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += 256) {
-    const uint32_t v = hist_lds[i];
-    if (v) atomicAdd(gh + i, v);
+  if (a.hist) {
+    __syncthreads();
+    // striping the flush by block index spreads same-bin atomics of the
+    // problem's blocks over kHistCopies counters
+    uint32_t* gh = a.hist + (pq * kHistCopies + (blockIdx.x % kHistCopies)) * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) {
+      const uint32_t v = hist_lds[i];
+      if (v) atomicAdd(gh + i, v);
+    }
   }
 }
 
@@ -249,7 +271,10 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
 // 4 heads each), so every summary tile loaded feeds 4 MFMAs per k-step.
 // Block = 4 waves sharing (region range of kScoreRange, group, 16-query
 // block); wave w takes tiles w, w+4, ...  Queries of one block that belong
-// to different sequences are handled one sequence at a time.
+// to different sequences are handled one sequence at a time.  TILEMAX also
+// stores each tile's largest key (left out of the short-context variant,
+// where its registers would halve the waves per SIMD).
+template <bool TILEMAX>
 __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
   constexpr int QW = 16, NRS = 4;
   const int g = blockIdx.y;
@@ -332,6 +357,7 @@ __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 8; ++s) acc = mfma16x16x32(A[rs][s], B[s], acc);
+        uint32_t key = 0;
         if (qidx[rs] >= 0 && r < cq[rs]) {
           float sv = zq[rs][0] * fmaxf(acc[0], 0.0f);
           sv = fmaf(zq[rs][1], fmaxf(acc[1], 0.0f), sv);
@@ -341,15 +367,19 @@ __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
           const int64_t pq = (int64_t)qidx[rs] * kGroups + g;
           a.scores[pq * a.ws_stride + r] = sv;
           if (a.scores_out) a.scores_out[pq * a.max_regions + r] = sv;
+          key = score_key(sv);
+        }
+        if (TILEMAX) {  // lanes 16kb..16kb+15 hold one query's tile
+          key = max(key, (uint32_t)__shfl_xor((int)key, 8));
+          key = max(key, (uint32_t)__shfl_xor((int)key, 4));
+          key = max(key, (uint32_t)__shfl_xor((int)key, 2));
+          key = max(key, (uint32_t)__shfl_xor((int)key, 1));
+          if (n == 0 && qidx[rs] >= 0 && t0 < cq[rs])
+            a.tilemax[((int64_t)qidx[rs] * kGroups + g) * a.tm_stride + t0 / kTile] = key;
         }
       }
     }
   }
-}
-
-__global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -357,143 +387,56 @@ __global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
 // ---------------------------------------------------------------------------
 
 struct SelectArgs {
-  const float* scores;  // [Nq][G][ws_stride]
-  const uint32_t* hist; // [Nq][G][8][4096] level-0 histogram stripes, or nullptr (computed in k_select)
-  uint32_t* bcnt;       // [Nq][G][nblk] candidates found by each collect block (decode)
-  uint64_t* cand;       // [Nq][G][nblk][kCollectChunk] candidate keys (decode), or nullptr
-  uint32_t* thr;        // [Nq][G][4] level-0 threshold: digit, count above, count in digit (decode)
-  int32_t nblk;         // collect blocks per (query, group)
+  const float* scores;      // [Nq][G][ws_stride]
+  const uint32_t* tilemax;  // [Nq][G][tm_stride] largest key per 16-region tile, or nullptr
+  const uint32_t* hist;     // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts
   const int32_t* qpos;
-  int32_t* sel;         // [Nq][G][topk]
-  int32_t* nsel;        // [Nq][G]
+  int32_t* sel;             // [Nq][G][topk]
+  int32_t* nsel;            // [Nq][G]
   int64_t R;
-  int32_t nq, max_regions, ws_stride, topk;
+  int32_t nq, max_regions, ws_stride, tm_stride, topk;
 };
 
 __device__ __forceinline__ uint64_t cand_key(const float* sc, int64_t r) {
   return ((uint64_t)score_key(sc[r]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)r);
 }
 
-constexpr int kCollectThreads = 256;
-constexpr int kCollectPer = 8;  // consecutive scores per thread
-constexpr int kCollectChunk = kCollectThreads * kCollectPer;
-
-// Decode, step 1: one block per (query, group) sums the histogram stripes
-// built by k_score_dec and finds the threshold digit (the digit holding the
-// k-th key), publishing (digit, keys above it, keys in it).
-constexpr int kThreshThreads = 1024;
-__global__ __launch_bounds__(kThreshThreads) void k_select_thresh(SelectArgs a) {
-  const int64_t pq = blockIdx.x;
-  const int qi = (int)(pq / kGroups);
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t wsum[kThreshThreads / 64];
-  __shared__ int sh_d;
-  __shared__ uint32_t sh_above;
-  if (threadIdx.x == 0) {
-    sh_d = 0;
-    sh_above = 0;
-  }
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
-  const int64_t need = (c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1);
-  if (need == c || need == 0) return;
-  const uint32_t* gh = a.hist + pq * kHistCopies * kHistBins;
-  constexpr int kPer = kHistBins / kThreshThreads;
-  uint32_t v[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) v[e] = 0;
-#pragma unroll
-  for (int k = 0; k < kHistCopies; ++k)
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) v[e] += gh[k * kHistBins + e * kThreshThreads + threadIdx.x];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) hist[e * kThreshThreads + threadIdx.x] = v[e];
-  __syncthreads();
-  uint32_t above;
-  const int d = find_digit<kThreshThreads>(hist, kHistBins, (uint32_t)need, &above, wsum, &sh_d, &sh_above);
-  if (threadIdx.x == 0) {
-    a.thr[pq * 4 + 0] = (uint32_t)d;
-    a.thr[pq * 4 + 1] = above;
-    a.thr[pq * 4 + 2] = hist[d];
-  }
-}
-
-// Decode, step 2: block j of (query, group) scans scores [2048j, 2048j+2048)
-// and keeps every key whose level-0 digit is at or above the threshold digit.
-// The kept keys are compacted in index order (block-wide scan, no atomics)
-// into the block's slice of the candidate buffer, with their count, so the
-// concatenation over blocks is in ascending region order.  Blocks write
-// count 0 when the problem needs no list or the list would not fit.
-__global__ __launch_bounds__(kCollectThreads) void k_select_collect(SelectArgs a) {
-  const int64_t pq = (int64_t)blockIdx.z * kGroups + blockIdx.y;
-  const int qi = blockIdx.z;
-  const int blk = blockIdx.x;
-  __shared__ uint32_t wsum[kCollectThreads / 64];
-  __shared__ uint32_t total;
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
-  const int64_t need = (c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1);
-  uint32_t* bc = a.bcnt + pq * a.nblk + blk;
-  const int64_t rb = (int64_t)blk * kCollectChunk;
-  if (need == c || need == 0 || rb >= c || a.thr[pq * 4 + 1] + a.thr[pq * 4 + 2] > (uint32_t)kSelCap) {
-    if (threadIdx.x == 0) *bc = 0;
-    return;
-  }
-  const int d = (int)a.thr[pq * 4 + 0];
-  const float* sc = a.scores + pq * a.ws_stride;
-  const int64_t r0 = rb + (int64_t)threadIdx.x * kCollectPer;
-  float v[kCollectPer];
-  if (r0 + kCollectPer <= c) {
-    const f32x4 x0 = *(const f32x4*)(sc + r0), x1 = *(const f32x4*)(sc + r0 + 4);
-    v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-    v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
-  } else {
-#pragma unroll
-    for (int e = 0; e < kCollectPer; ++e) v[e] = (r0 + e < c) ? sc[r0 + e] : 0.0f;
-  }
-  uint32_t key[kCollectPer];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int e = 0; e < kCollectPer; ++e) {
-    key[e] = score_key(v[e]);
-    if (r0 + e < c && (int)(key[e] >> 20) >= d) ++mine;
-  }
-  const uint32_t off = block_excl_scan<kCollectThreads>(mine, wsum);
-  if (threadIdx.x == kCollectThreads - 1) total = off + mine;
-  uint64_t* out = a.cand + (pq * a.nblk + blk) * kCollectChunk + off;
-  uint32_t j = 0;
-#pragma unroll
-  for (int e = 0; e < kCollectPer; ++e) {
-    const int64_t r = r0 + e;
-    if (r < c && (int)(key[e] >> 20) >= d)
-      out[j++] = ((uint64_t)key[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)r);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) *bc = total;
-}
-
 // ---------------------------------------------------------------------------
 // Ordered selection on keys held in registers.  Entry e of thread t is the
 // (e*NT + t)-th entry of an index-ordered candidate sequence (coalesced
-// loads); absent entries carry key 0.  The need-th largest key T is found by
-// bisection on its bits, with block-wide counts of keys >= a trial value
-// (ballot + scalar popcount per wave).  Keys above T are all taken; keys
-// equal to T are taken lowest index first; the selection is written in
-// ascending index order (ranks from a per-(entry slot, wave) table and one
-// block scan), followed by the forced current region c.
+// loads); absent entries carry key 0 and come last.  The need-th largest key
+// T is found by bisection on its bits with block-wide counts; keys above T
+// are all taken, keys equal to T lowest index first, and the selection is
+// written in ascending index order.
 // ---------------------------------------------------------------------------
 
-// Sum over the block of per-wave totals (each wave passes the same value in
-// every lane); `slot` alternates so one barrier per call suffices.
-template <int NT>
-__device__ __forceinline__ uint32_t block_sum_waves(uint32_t wave_total, uint32_t* red, int slot) {
-  if ((threadIdx.x & 63) == 0) red[slot * (NT / 64) + (threadIdx.x >> 6)] = wave_total;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) t += red[slot * (NT / 64) + i];
-  return t;
+// Shared memory of one selection block.
+template <int NT, int KPT>
+struct alignas(16) SelectSmem {
+  static constexpr int NW = NT / 64;
+  uint32_t red[2][NW];     // per-wave partial counts, alternating
+  uint32_t tgt[KPT * NW];  // per-(entry slot, wave) counts of keys above the boundary, then their scan
+  uint32_t teq[KPT * NW];  // same for keys on the boundary
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts inside
+// each row of 16 lanes, then row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
 }
 
-// Number of keys >= trial held by this wave (trial is never 0).
+// Sum over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
+}
+
+// Number of keys >= trial held by this wave (ballot + scalar popcount).
 template <int KPT>
 __device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[KPT], uint32_t trial) {
   uint32_t n = 0;
@@ -502,78 +445,114 @@ __device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[KPT], ui
   return n;
 }
 
-// Exclusive scan, in place, of tab[0..n) laid out slot-major (slot, wave);
-// n <= NT.
-template <int NT>
-__device__ __forceinline__ void scan_table(uint32_t* tab, int n, uint32_t* wsum) {
+// Block-wide number of keys >= trial; `slot` alternates between calls so one
+// barrier per call suffices.
+template <int NT, int KPT>
+__device__ __forceinline__ uint32_t block_count_ge(const uint32_t (&key)[KPT], uint32_t trial,
+                                                   SelectSmem<NT, KPT>& sm, int slot) {
+  const uint32_t n = wave_count_ge<KPT>(key, trial);
+  if ((threadIdx.x & 63) == 0) sm.red[slot][threadIdx.x >> 6] = n;
   __syncthreads();
-  const uint32_t v = threadIdx.x < n ? tab[threadIdx.x] : 0u;
-  const uint32_t ex = block_excl_scan<NT>(v, wsum);
-  if (threadIdx.x < n) tab[threadIdx.x] = ex;
-  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t += sm.red[slot][i];
+  return t;
 }
 
-// The need-th largest key by bisection over all register-held keys.
+// Boundary of the need best keys: every key above T is taken and `need -
+// above` keys equal to T, lowest index first.
+struct Boundary {
+  uint32_t T, above;
+};
+
+// The need-th largest key (1 <= need <= number of present entries) by
+// bisection on its 32 bits.
 template <int NT, int KPT>
-__device__ uint32_t kth_key_bisect(const uint32_t (&key)[KPT], uint32_t need, uint32_t* red) {
+__device__ Boundary block_boundary(const uint32_t (&key)[KPT], uint32_t need, SelectSmem<NT, KPT>& sm) {
   uint32_t T = 0;
+#pragma unroll 1
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t trial = T | (1u << bit);
-    if (block_sum_waves<NT>(wave_count_ge<KPT>(key, trial), red, bit & 1) >= need) T = trial;
+    if (block_count_ge<NT, KPT>(key, trial, sm, bit & 1) >= need) T = trial;
   }
-  return T;
+  const uint32_t above = (T == 0xFFFFFFFFu) ? 0u : block_count_ge<NT, KPT>(key, T + 1, sm, 1);
+  return Boundary{T, above};
 }
 
-// Writes the selection given T = the need-th largest key: keys above T, then
-// keys equal to T lowest index first, in ascending index order, then c.
+// Exclusive scan, in place, of two tables of n <= 512 counts by wave 0,
+// between block barriers.
+template <int NT>
+__device__ __forceinline__ void scan_tables(uint32_t* ta, uint32_t* tb, int n) {
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (n + 63) / 64;
+    const int i0 = lane * per;
+    uint32_t sa = 0, sb = 0;
+    for (int i = 0; i < per; ++i)
+      if (i0 + i < n) {
+        sa += ta[i0 + i];
+        sb += tb[i0 + i];
+      }
+    uint32_t ra = wave_incl_scan(sa) - sa, rb = wave_incl_scan(sb) - sb;
+    for (int i = 0; i < per; ++i)
+      if (i0 + i < n) {
+        const uint32_t va = ta[i0 + i], vb = tb[i0 + i];
+        ta[i0 + i] = ra;
+        tb[i0 + i] = rb;
+        ra += va;
+        rb += vb;
+      }
+  }
+  __syncthreads();
+}
+
+// Writes the idx of the need best entries to out[0..need) in index order.
+// An entry's position is the number of taken entries before it: entries
+// above T before it plus min(entries equal to T before it, need - above).
 template <int NT, int KPT>
-__device__ void emit_selection(const uint32_t (&key)[KPT], const int32_t (&idx)[KPT], uint32_t T, uint32_t need,
-                               int64_t c, int32_t* sel, int32_t* nsel_out, int topk, uint32_t* red, uint32_t* tab,
-                               uint32_t* wsum) {
+__device__ void emit_top(const uint32_t (&key)[KPT], const int32_t (&idx)[KPT], const Boundary& bd, uint32_t need,
+                         int32_t* out, SelectSmem<NT, KPT>& sm) {
   constexpr int NW = NT / 64;
-  static_assert(KPT * NW <= NT, "rank table larger than the block");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
-  __syncthreads();
-  const uint32_t above = (T == 0xFFFFFFFFu) ? 0u : block_sum_waves<NT>(wave_count_ge<KPT>(key, T + 1), red, 1);
-  const uint32_t need_eq = need - above;  // >= 1 by the choice of T
-  // ranks of keys equal to T, in index order
-  uint64_t meq[KPT];
+  const uint32_t need_eq = need - bd.above;
+  uint64_t mgt[KPT], meq[KPT];
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
-    meq[e] = __ballot(key[e] == T);
-    if (lane == 0) tab[e * NW + w] = (uint32_t)__popcll(meq[e]);
+    mgt[e] = __ballot(key[e] > bd.T);
+    meq[e] = __ballot(key[e] == bd.T);
+    if (lane == 0) {
+      sm.tgt[e * NW + w] = (uint32_t)__popcll(mgt[e]);
+      sm.teq[e * NW + w] = (uint32_t)__popcll(meq[e]);
+    }
   }
-  scan_table<NT>(tab, KPT * NW, wsum);
-  uint64_t msel[KPT];
+  scan_tables<NT>(sm.tgt, sm.teq, KPT * NW);
+  // absent entries (key 0) come after every present entry, and at least need
+  // present entries are >= T, so an absent entry is never taken
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
-    // absent entries (key 0) have the highest indices, so they can only rank
-    // after every present key equal to T and are never taken
-    const bool s = key[e] > T || (key[e] == T && tab[e * NW + w] + (uint32_t)__popcll(meq[e] & lt) < need_eq);
-    msel[e] = __ballot(s);
+    const uint32_t gt = sm.tgt[e * NW + w] + (uint32_t)__popcll(mgt[e] & lt);
+    const uint32_t eq = sm.teq[e * NW + w] + (uint32_t)__popcll(meq[e] & lt);
+    uint32_t pos = need;  // need = not taken
+    if ((mgt[e] >> lane) & 1ull) pos = gt + (eq < need_eq ? eq : need_eq);
+    else if (((meq[e] >> lane) & 1ull) && eq < need_eq) pos = gt + eq;
+    if (pos < need) out[pos] = idx[e];
   }
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < KPT; ++e)
-    if (lane == 0) tab[e * NW + w] = (uint32_t)__popcll(msel[e]);
-  scan_table<NT>(tab, KPT * NW, wsum);
-#pragma unroll
-  for (int e = 0; e < KPT; ++e)
-    if ((msel[e] >> lane) & 1ull) sel[tab[e * NW + w] + (uint32_t)__popcll(msel[e] & lt)] = idx[e];
+}
+
+// The selection of one problem: the need best candidates in ascending index
+// order, then the forced current region c, then -1 padding.
+template <int NT, int KPT>
+__device__ void select_strided(const uint32_t (&key)[KPT], const int32_t (&idx)[KPT], uint32_t need, int64_t c,
+                               int32_t* sel, int32_t* nsel_out, int topk, SelectSmem<NT, KPT>& sm) {
+  const Boundary bd = block_boundary<NT, KPT>(key, need, sm);
+  emit_top<NT, KPT>(key, idx, bd, need, sel, sm);
   for (int i = (int)need + 1 + threadIdx.x; i < topk; i += NT) sel[i] = -1;
   if (threadIdx.x == 0) {
     sel[need] = (int32_t)c;
     *nsel_out = (int32_t)need + 1;
   }
-}
-
-template <int NT, int KPT>
-__device__ void select_strided(const uint32_t (&key)[KPT], const int32_t (&idx)[KPT], uint32_t need, int64_t c,
-                               int32_t* sel, int32_t* nsel_out, int topk, uint32_t* red, uint32_t* tab,
-                               uint32_t* wsum) {
-  const uint32_t T = kth_key_bisect<NT, KPT>(key, need, red);
-  emit_selection<NT, KPT>(key, idx, T, need, c, sel, nsel_out, topk, red, tab, wsum);
 }
 
 // Trivial cases shared by the selection kernels.  Returns true when handled.
@@ -603,27 +582,32 @@ template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void k_select_pre(SelectArgs a) {
   const int64_t pq = blockIdx.x;
   const int qi = (int)(pq / kGroups);
-  __shared__ uint32_t red[2 * (NT / 64)];
-  __shared__ uint32_t wsum[NT / 64];
-  __shared__ uint32_t tab[KPT * (NT / 64)];
+  __shared__ SelectSmem<NT, KPT> sm;
   const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
   if (select_trivial(c, need, sel, a.nsel + pq, a.topk, NT)) return;
   const float* sc = a.scores + pq * a.ws_stride;
+  // unconditional loads (clamped index) so that all of them are in flight at once
+  float v[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const int64_t r = (int64_t)e * NT + threadIdx.x;
+    v[e] = sc[r < c ? r : 0];
+  }
   uint32_t key[KPT];
   int32_t idx[KPT];
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
     const int64_t r = (int64_t)e * NT + threadIdx.x;
-    key[e] = r < c ? score_key(sc[r]) : 0u;
+    key[e] = r < c ? score_key(v[e]) : 0u;
     idx[e] = (int32_t)r;
   }
-  select_strided<NT, KPT>(key, idx, need, c, sel, a.nsel + pq, a.topk, red, tab, wsum);
+  select_strided<NT, KPT>(key, idx, need, c, sel, a.nsel + pq, a.topk, sm);
 }
 
-// Decode fallback and very long prefill contexts: exact selection by radix
-// narrowing over the scores in global memory (12-bit digits) until the
+// Problems beyond the register capacity of the tile selection: exact
+// selection by radix narrowing over the scores in global memory (12-bit digits) until the
 // candidates fit in LDS, 8-bit digits in LDS, bitonic sort of the result.
 template <int NT>
 __device__ void select_fallback(const SelectArgs& a, int64_t pq) {
@@ -659,22 +643,15 @@ __device__ void select_fallback(const SelectArgs& a, int64_t pq) {
     return;
   }
 
-  // ---- level 0: 12-bit digit of the score key (bits 63..52 of the 64-bit key),
-  // published by k_select_thresh for decode, found here for prefill
+  // ---- level 0: 12-bit digit of the score key (bits 63..52 of the 64-bit key)
   uint32_t above, inbin;
   int d;
-  if (a.thr) {
-    d = (int)a.thr[pq * 4 + 0];
-    above = a.thr[pq * 4 + 1];
-    inbin = a.thr[pq * 4 + 2];
-  } else {
-    for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
-    __syncthreads();
-    for (int64_t r = tid; r < c; r += NT) atomicAdd(&hist[score_key(sc[r]) >> 20], 1u);
-    __syncthreads();
-    d = find_digit<NT>(hist, kHistBins, need, &above, wsum, &sh_d, &sh_above);
-    inbin = hist[d];
-  }
+  for (int i = tid; i < kHistBins; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int64_t r = tid; r < c; r += NT) atomicAdd(&hist[score_key(sc[r]) >> 20], 1u);
+  __syncthreads();
+  d = find_digit<NT>(hist, kHistBins, need, &above, wsum, &sh_d, &sh_above);
+  inbin = hist[d];
   uint64_t prefix = (uint64_t)d;
   int shift = 52;
   __syncthreads();
@@ -777,106 +754,432 @@ __device__ void select_fallback(const SelectArgs& a, int64_t pq) {
 }
 
 
-// Prefill with more than 32768 candidate regions per query.
-__global__ __launch_bounds__(512) void k_select_long(SelectArgs a) {
+// Long problems: one block per (query, group).  Pass 1 ranks the tiles of 16
+// regions by their largest key and keeps the best need of them (all tiles
+// when there are at most need).  Every selected region lies in a kept tile:
+// a region in a dropped tile ranks below that tile's maximum, which ranks
+// below the maxima of need kept tiles, so need regions rank above it.
+// Pass 2 ranks the <= need*16 regions of the kept tiles exactly.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void k_select_tiles(SelectArgs a) {
+  static_assert(NT * KPT >= kMaxTopk * kTile, "kept tiles must fit in registers");
   const int64_t pq = blockIdx.x;
   const int qi = (int)(pq / kGroups);
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
-  const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
-  if (select_trivial(c, need, a.sel + pq * a.topk, a.nsel + pq, a.topk, 512)) return;
-  select_fallback<512>(a, pq);
-}
-
-// Decode, step 3: one block per (query, group).  The collected list (index
-// order, at most kSelCap keys) is loaded into registers and finished with the
-// ordered selection; problems whose list would not fit use the fallback.
-constexpr int kFinalThreads = 512;
-constexpr int kFinalKpt = kSelCap / kFinalThreads;  // 8
-__global__ __launch_bounds__(kFinalThreads) void k_select_dec(SelectArgs a) {
-  const int64_t pq = blockIdx.x;
-  const int qi = (int)(pq / kGroups);
-  __shared__ uint32_t red[2 * (kFinalThreads / 64)];
-  __shared__ uint32_t wsum[kFinalThreads / 64];
-  __shared__ uint32_t offs[kMaxTopk + 1];
-  __shared__ uint32_t tab[kFinalKpt * (kFinalThreads / 64)];
-  __shared__ uint32_t sh_total;
+  __shared__ SelectSmem<NT, KPT> sm;
+  __shared__ int32_t tiles[kMaxTopk];
   const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
-  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kFinalThreads)) return;
-  const bool fits = a.nblk <= kMaxTopk && a.thr[pq * 4 + 1] + a.thr[pq * 4 + 2] <= (uint32_t)kSelCap;
-  if (!fits) {
-    select_fallback<kFinalThreads>(a, pq);
+  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, NT)) return;
+  const int64_t ntiles = (c + kTile - 1) / kTile;
+  if (ntiles > (int64_t)NT * KPT) {
+    select_fallback<NT>(a, pq);
     return;
   }
-  // offsets of the blocks' lists (rounds of kFinalThreads blocks)
-  uint32_t base = 0;
-  for (int j0 = 0; j0 < a.nblk; j0 += kFinalThreads) {
-    const int j = j0 + threadIdx.x;
-    const uint32_t cj = j < a.nblk ? a.bcnt[pq * a.nblk + j] : 0u;
-    const uint32_t ex = block_excl_scan<kFinalThreads>(cj, wsum);
-    if (j < a.nblk) offs[j] = base + ex;
-    if (threadIdx.x == kFinalThreads - 1) sh_total = base + ex + cj;
-    __syncthreads();
-    base = sh_total;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) offs[a.nblk] = base;
-  __syncthreads();
-  const uint32_t m = base < (uint32_t)kSelCap ? base : (uint32_t)kSelCap;
-  uint32_t key[kFinalKpt];
-  int32_t idx[kFinalKpt];
+  uint32_t kept;
+  if (ntiles <= (int64_t)need) {
+    for (int j = threadIdx.x; j < ntiles; j += NT) tiles[j] = j;
+    kept = (uint32_t)ntiles;
+  } else {
+    const uint32_t* tm = a.tilemax + pq * a.tm_stride;
+    uint32_t tk[KPT];
+    int32_t ti[KPT];
 #pragma unroll
-  for (int e = 0; e < kFinalKpt; ++e) {
-    const uint32_t i = (uint32_t)e * kFinalThreads + threadIdx.x;
-    key[e] = 0;
-    idx[e] = 0;
-    if (i < m) {
-      int lo = 0, hi = a.nblk - 1;  // collect block holding entry i: last j with offs[j] <= i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offs[mid] <= i) lo = mid;
-        else hi = mid - 1;
-      }
-      const uint64_t k = a.cand[(pq * a.nblk + lo) * kCollectChunk + (i - offs[lo])];
-      key[e] = (uint32_t)(k >> 32);
-      idx[e] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+    for (int e = 0; e < KPT; ++e) {
+      const int j = e * NT + threadIdx.x;
+      tk[e] = tm[j < ntiles ? j : 0];
+    }
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const int j = e * NT + threadIdx.x;
+      if (j >= ntiles) tk[e] = 0u;
+      ti[e] = j;
+    }
+    const Boundary bd = block_boundary<NT, KPT>(tk, need, sm);
+    emit_top<NT, KPT>(tk, ti, bd, need, tiles, sm);
+    kept = need;
+  }
+  __syncthreads();
+  const float* sc = a.scores + pq * a.ws_stride;
+  const uint32_t m = kept * kTile;
+  uint32_t key[KPT];
+  int32_t idx[KPT];
+  float v[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const uint32_t i = (uint32_t)e * NT + threadIdx.x;
+    const int64_t r = (int64_t)tiles[i < m ? i / kTile : 0] * kTile + (i % kTile);
+    idx[e] = (int32_t)r;
+    v[e] = sc[r < c ? r : 0];
+  }
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const uint32_t i = (uint32_t)e * NT + threadIdx.x;
+    key[e] = (i < m && idx[e] < c) ? score_key(v[e]) : 0u;
+    if (i >= m) idx[e] = 0;
+  }
+  select_strided<NT, KPT>(key, idx, need, c, sel, a.nsel + pq, a.topk, sm);
+}
+
+// Ordered compaction over a block: the entries (e, thread) with flag set get
+// consecutive positions in sequence order e*NT + thread.  tab needs
+// KPT*NT/64 + 1 entries; returns the number of flagged entries.
+template <int NT, int KPT>
+__device__ uint32_t ordered_positions(const bool (&flag)[KPT], uint32_t (&pos)[KPT], uint32_t* tab) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint64_t m[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    m[e] = __ballot(flag[e]);
+    if (lane == 0) tab[e * NW + w] = (uint32_t)__popcll(m[e]);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {  // exclusive scan of the table by wave 0, total at tab[n]
+    constexpr int n = KPT * NW, per = (n + 63) / 64;
+    const int i0 = lane * per;
+    uint32_t v[per], sum = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      v[i] = (i0 + i < n) ? tab[i0 + i] : 0u;
+      sum += v[i];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    uint32_t run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      if (i0 + i < n) tab[i0 + i] = run;
+      run += v[i];
+    }
+    if (lane == 63) tab[n] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) pos[e] = tab[e * NW + w] + (uint32_t)__popcll(m[e] & lt);
+  return tab[KPT * NW];
+}
+
+// Two flag sets at once (tab needs 2*(KPT*NT/64) + 2 entries); totals in
+// *na, *nb.
+template <int NT, int KPT>
+__device__ void ordered_positions2(const bool (&fa)[KPT], const bool (&fb)[KPT], uint32_t (&pa)[KPT],
+                                   uint32_t (&pb)[KPT], uint32_t* tab, uint32_t* na, uint32_t* nb) {
+  constexpr int NW = NT / 64, n = KPT * NW;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t* ta = tab;
+  uint32_t* tb = tab + n + 1;
+  uint64_t ma[KPT], mb[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    ma[e] = __ballot(fa[e]);
+    mb[e] = __ballot(fb[e]);
+    if (lane == 0) {
+      ta[e * NW + w] = (uint32_t)__popcll(ma[e]);
+      tb[e * NW + w] = (uint32_t)__popcll(mb[e]);
     }
   }
-  select_strided<kFinalThreads, kFinalKpt>(key, idx, need, c, sel, a.nsel + pq, a.topk, red, tab, wsum);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    constexpr int per = (n + 63) / 64;
+    const int i0 = lane * per;
+    uint32_t va[per], vb[per], sa = 0, sb = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      va[i] = (i0 + i < n) ? ta[i0 + i] : 0u;
+      vb[i] = (i0 + i < n) ? tb[i0 + i] : 0u;
+      sa += va[i];
+      sb += vb[i];
+    }
+    const uint32_t ia = wave_incl_scan(sa), ib = wave_incl_scan(sb);
+    uint32_t ra = ia - sa, rb = ib - sb;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      if (i0 + i < n) {
+        ta[i0 + i] = ra;
+        tb[i0 + i] = rb;
+      }
+      ra += va[i];
+      rb += vb[i];
+    }
+    if (lane == 63) {
+      ta[n] = ia;
+      tb[n] = ib;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    pa[e] = ta[e * NW + w] + (uint32_t)__popcll(ma[e] & lt);
+    pb[e] = tb[e * NW + w] + (uint32_t)__popcll(mb[e] & lt);
+  }
+  *na = ta[n];
+  *nb = tb[n];
 }
+
+constexpr int kDecNT = 1024;
+constexpr int kDecTilesPT = 8;                          // tile keys per thread (8192 tiles)
+constexpr int kDecCandPT = kCandCap * kTile / kDecNT;   // candidate slots per thread
+
+struct alignas(16) DecSmem {
+  uint32_t wtot[kDecNT / 64];
+  uint32_t res[4];
+  uint32_t tab[2 * (kDecCandPT * (kDecNT / 64) + 1)];
+  union {
+    int32_t tiles[kCandCap];  // kept tiles (step 2)
+    uint32_t hh[1024];        // 10-bit digit histogram of the finishing wave (step 3)
+  };
+  uint32_t ck[kCandCap];      // candidate keys, index order
+  int32_t ci[kCandCap];       // candidate regions
+  uint32_t kin[kCandCap];     // keys in the level-0 digit, any order
+};
+
+// One wave: the digit (of `bits` bits at `shift`) holding the rem-th largest
+// of the keys kin[0..n) whose bits above shift+bits equal `hi`; counts of the
+// keys in higher digits go to *above.  LDS operations of one wave complete in
+// order, so no barrier is needed.
+__device__ __forceinline__ uint32_t wave_digit(const uint32_t* kin, uint32_t n, uint32_t hi, int shift, uint32_t rem,
+                                               uint32_t* hh, uint32_t* above) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *(u32x4*)&hh[16 * lane + 4 * i] = u32x4{0u, 0u, 0u, 0u};
+  for (uint32_t q = lane; q < n; q += 64) {
+    const uint32_t k = kin[q];
+    if ((k >> (shift + 10)) == hi) atomicAdd(&hh[(k >> shift) & 1023u], 1u);
+  }
+  // lane l owns digits 1023-16l down to 1008-16l
+  uint32_t cnt[16], mine = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = *(const u32x4*)&hh[1008 - 16 * lane + 4 * i];
+    cnt[15 - 4 * i] = v.x;
+    cnt[14 - 4 * i] = v.y;
+    cnt[13 - 4 * i] = v.z;
+    cnt[12 - 4 * i] = v.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mine += cnt[j];
+  const uint32_t incl = wave_incl_scan(mine);
+  uint32_t run = incl - mine, dig = 0, ab = 0;
+  bool hit = false;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (run < rem && run + cnt[j] >= rem) {
+      hit = true;
+      dig = (uint32_t)(1023 - 16 * lane - j);
+      ab = run;
+    }
+    run += cnt[j];
+  }
+  const uint64_t hm = __ballot(hit);
+  const int src = hm ? __ffsll((long long)hm) - 1 : 0;
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+  return (uint32_t)__builtin_amdgcn_readlane((int)dig, src);
+}
+
+// Decode selection, one block per (query, group), on what k_score_dec left:
+// the scores, each tile's largest key and the level-0 digit histogram.
+//  1. The histogram gives the digit d holding the need-th largest key, the
+//     count above it and the count in it.
+//  2. Tiles whose largest key has a digit >= d hold every region at or above
+//     d; they are compacted in index order, and their regions at or above d
+//     (the candidates, exactly above + in-digit of them) too.
+//  3. One wave finds the need-th largest key from the keys inside digit d
+//     (two 10-bit rounds) and writes the selection in index order.
+// Problems with more candidates than kCandCap or more tiles than the block
+// holds use the radix fallback.
+__global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
+  const int64_t pq = blockIdx.x;
+  const int qi = (int)(pq / kGroups);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ DecSmem sm;
+  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
+  int32_t* sel = a.sel + pq * a.topk;
+  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kDecNT)) return;
+  const int64_t ntiles = (c + kTile - 1) / kTile;
+  if (ntiles > (int64_t)kDecNT * kDecTilesPT) {
+    select_fallback<kDecNT>(a, pq);
+    return;
+  }
+  const uint32_t* tm = a.tilemax + pq * a.tm_stride;
+  uint32_t tk[kDecTilesPT];
+#pragma unroll
+  for (int e = 0; e < kDecTilesPT; ++e) {
+    const int64_t j = (int64_t)e * kDecNT + tid;
+    tk[e] = tm[j < ntiles ? j : 0];
+  }
+#pragma unroll
+  for (int e = 0; e < kDecTilesPT; ++e)
+    if ((int64_t)e * kDecNT + tid >= ntiles) tk[e] = 0u;
+  // 1. level-0 digit: thread t holds digits 4095-4t down to 4092-4t
+  const uint32_t* gh = a.hist + pq * kHistCopies * kHistBins + (kHistBins - 4 - 4 * tid);
+  u32x4 h = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < kHistCopies; ++k) h += *(const u32x4*)(gh + k * kHistBins);
+  const uint32_t cnt[4] = {h.w, h.z, h.y, h.x};
+  const uint32_t mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+  const uint32_t wi = wave_incl_scan(mine);
+  if (lane == 63) sm.wtot[w] = wi;
+  if (tid == 0) sm.res[0] = 0xFFFFFFFFu;
+  __syncthreads();
+  uint32_t run = wi - mine;
+#pragma unroll
+  for (int i = 0; i < kDecNT / 256; ++i) {
+    const u32x4 v = *(const u32x4*)&sm.wtot[4 * i];
+    run += (4 * i < w ? v.x : 0u) + (4 * i + 1 < w ? v.y : 0u) + (4 * i + 2 < w ? v.z : 0u) +
+           (4 * i + 3 < w ? v.w : 0u);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (run < need && run + cnt[j] >= need) {
+      sm.res[0] = (uint32_t)(kHistBins - 1 - 4 * tid - j);
+      sm.res[1] = run;
+      sm.res[2] = cnt[j];
+    }
+    run += cnt[j];
+  }
+  __syncthreads();
+  const uint32_t d = sm.res[0], above = sm.res[1], inbin = sm.res[2];
+  if (d == 0xFFFFFFFFu || above + inbin > (uint32_t)kCandCap) {
+    select_fallback<kDecNT>(a, pq);
+    return;
+  }
+  const uint32_t Tlo = d << 20;
+  // 2. kept tiles, then the candidates in them
+  {
+    bool f[kDecTilesPT];
+    uint32_t pos[kDecTilesPT];
+#pragma unroll
+    for (int e = 0; e < kDecTilesPT; ++e) f[e] = tk[e] >= Tlo && (int64_t)e * kDecNT + tid < ntiles;
+    ordered_positions<kDecNT, kDecTilesPT>(f, pos, sm.tab);
+#pragma unroll
+    for (int e = 0; e < kDecTilesPT; ++e)
+      if (f[e] && pos[e] < (uint32_t)kCandCap) sm.tiles[pos[e]] = e * kDecNT + tid;
+  }
+  const uint32_t ntl = min(sm.tab[kDecTilesPT * (kDecNT / 64)], (uint32_t)kCandCap);
+  __syncthreads();
+  uint32_t ncand, nin;
+  {
+    const float* sc = a.scores + pq * a.ws_stride;
+    const uint32_t m = ntl * kTile;
+    uint32_t ck[kDecCandPT], pos[kDecCandPT];
+    int32_t ci[kDecCandPT];
+    bool f[kDecCandPT];
+    float v[kDecCandPT];
+    // unconditional loads (clamped index) so that all of them are in flight at once
+#pragma unroll
+    for (int e = 0; e < kDecCandPT; ++e) {
+      const uint32_t i = (uint32_t)e * kDecNT + tid;
+      const int64_t r = (int64_t)sm.tiles[i < m ? i / kTile : 0] * kTile + (i % kTile);
+      ci[e] = (int32_t)r;
+      v[e] = sc[r < c ? r : 0];
+    }
+    bool fin[kDecCandPT];
+    uint32_t pin[kDecCandPT];
+#pragma unroll
+    for (int e = 0; e < kDecCandPT; ++e) {
+      const uint32_t i = (uint32_t)e * kDecNT + tid;
+      const bool ok = i < m && ci[e] < c;
+      ck[e] = ok ? score_key(v[e]) : 0u;
+      f[e] = ok && ck[e] >= Tlo;
+      fin[e] = f[e] && (ck[e] >> 20) == d;
+    }
+    ordered_positions2<kDecNT, kDecCandPT>(f, fin, pos, pin, sm.tab, &ncand, &nin);
+#pragma unroll
+    for (int e = 0; e < kDecCandPT; ++e) {
+      if (f[e] && pos[e] < (uint32_t)kCandCap) {
+        sm.ck[pos[e]] = ck[e];
+        sm.ci[pos[e]] = ci[e];
+      }
+      if (fin[e] && pin[e] < (uint32_t)kCandCap) sm.kin[pin[e]] = ck[e];
+    }
+  }
+  for (int i = (int)need + 1 + tid; i < a.topk; i += kDecNT) sel[i] = -1;
+  if (tid == 0) {
+    sel[need] = (int32_t)c;
+    a.nsel[pq] = (int32_t)need + 1;
+  }
+  __syncthreads();
+  // 3. wave 0: the need-th largest key T lies in digit d; its next 10 bits,
+  // then its last 10, from histograms of the in-digit keys
+  const uint32_t M = min(ncand, (uint32_t)kCandCap);
+  if (w == 0) {
+    const uint32_t n_in = min(nin, (uint32_t)kCandCap);
+    uint32_t ab1, ab2;
+    const uint32_t d1 = wave_digit(sm.kin, n_in, d, 10, need - above, sm.hh, &ab1);
+    const uint32_t d2 = wave_digit(sm.kin, n_in, (d << 10) | d1, 0, need - above - ab1, sm.hh, &ab2);
+    if (lane == 0) {
+      sm.res[0] = (((d << 10) | d1) << 10) | d2;
+      sm.res[1] = need - above - ab1 - ab2;  // keys equal to T to take
+    }
+  }
+  __syncthreads();
+  const uint32_t T = sm.res[0], need_eq = sm.res[1];
+  // 4. every thread places one candidate: taken entries before it are the
+  // keys above T before it plus min(keys equal to T before it, need_eq)
+  static_assert(kCandCap <= kDecNT, "one candidate per thread");
+  const uint32_t k = tid < M ? sm.ck[tid] : 0u;
+  const bool fg[1] = {tid < M && k > T}, fe[1] = {tid < M && k == T};
+  uint32_t pg[1], pe[1], ng, ne;
+  ordered_positions2<kDecNT, 1>(fg, fe, pg, pe, sm.tab, &ng, &ne);
+  uint32_t pos = need;
+  if (fg[0]) pos = pg[0] + (pe[0] < need_eq ? pe[0] : need_eq);
+  else if (fe[0] && pe[0] < need_eq) pos = pg[0] + pe[0];
+  if (pos < need) sel[pos] = sm.ci[tid];
+}
+
+__global__ void k_zero(u32x4* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+#ifndef DSA_TILE_SELECT_NT
+#define DSA_TILE_SELECT_NT 1024
+#endif
+constexpr int kTileNT = DSA_TILE_SELECT_NT;
 
 static int64_t ws_stride_of(int32_t max_regions) { return ((int64_t)max_regions + 63) / 64 * 64; }
 static bool decode_shaped(int32_t n_queries) { return n_queries < 64; }
 
+// Problems with more candidate regions than kDirectMax go through the tile
+// maxima.
+static bool tiled_select(int32_t max_regions) { return max_regions > kDirectMax; }
+static int64_t tm_stride_of(int32_t max_regions) { return ((int64_t)max_regions / kTile + 1 + 63) / 64 * 64; }
+
+// Decode-shaped problems long enough for the tile path also get the level-0
+// histogram from the score kernel.
+static bool hist_select(int32_t n_queries, int32_t max_regions) {
+  return decode_shaped(n_queries) && tiled_select(max_regions);
+}
+
 struct ScoreWs {
   uint32_t* hist;
-  uint32_t* thr;
-  uint32_t* bcnt;
-  uint64_t* cand;
+  uint32_t* tilemax;
   float* scores;
-  size_t bytes;
+  size_t hist_bytes, bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
-static int32_t collect_blocks(int32_t max_regions) { return (max_regions + kCollectChunk - 1) / kCollectChunk; }
 
 static ScoreWs score_ws_layout(void* base, int32_t nq, int32_t max_regions) {
   ScoreWs w;
   char* p = (char*)base;
   const size_t np = (size_t)nq * kGroups;
-  const bool dec = decode_shaped(nq);
-  const size_t nblk = (size_t)collect_blocks(max_regions);
   size_t off = 0;
-  w.hist = (uint32_t*)(p + off);
-  off += align256(np * (dec ? kHistCopies : 1) * kHistBins * 4);
-  w.thr = (uint32_t*)(p + off);
-  off += align256(np * 4 * 4);
-  w.bcnt = (uint32_t*)(p + off);
-  off += align256(np * nblk * 4);
-  w.cand = dec ? (uint64_t*)(p + off) : nullptr;
-  if (dec) off += align256(np * nblk * kCollectChunk * 8);
+  w.hist = nullptr;
+  w.hist_bytes = 0;
+  if (hist_select(nq, max_regions)) {
+    w.hist = (uint32_t*)(p + off);
+    w.hist_bytes = align256(np * kHistCopies * kHistBins * 4);
+    off += w.hist_bytes;
+  }
+  w.tilemax = nullptr;
+  if (tiled_select(max_regions)) {
+    w.tilemax = (uint32_t*)(p + off);
+    off += align256(np * (size_t)tm_stride_of(max_regions) * 4);
+  }
   w.scores = (float*)(p + off);
   off += align256(np * (size_t)ws_stride_of(max_regions) * 4);
   w.bytes = off;
@@ -921,69 +1224,45 @@ extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries
 
   ScoreArgs sa;
   sa.iq = index_q; sa.z = z; sa.qseq = q_seq; sa.qpos = q_pos; sa.summ = summ; sa.scale = scale;
-  sa.scores = w.scores; sa.scores_out = scores_out; sa.hist = w.hist;
+  sa.scores = w.scores; sa.scores_out = scores_out; sa.tilemax = w.tilemax; sa.hist = w.hist;
   sa.R = tcap / kRegion; sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions;
-  sa.ws_stride = stride; sa.topk = geom->topk;
-  const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
-  // Decode-shaped calls (few queries, many regions) score one query per wave,
-  // build the level-0 histogram on the fly and collect candidates with many
-  // blocks; prefill-shaped calls score 16 queries per wave so each summary
-  // tile feeds 4 MFMA row-sets, and select with one block per problem.
-  const bool dec = decode_shaped(n_queries);
+  sa.ws_stride = stride; sa.tm_stride = (int32_t)tm_stride_of(max_regions); sa.topk = geom->topk;
   SelectArgs se;
-  se.scores = w.scores; se.hist = dec ? w.hist : nullptr; se.bcnt = w.bcnt; se.cand = w.cand;
-  se.thr = dec ? w.thr : nullptr;
-  se.nblk = collect_blocks(max_regions); se.qpos = q_pos;
+  se.scores = w.scores; se.tilemax = w.tilemax; se.hist = w.hist; se.qpos = q_pos;
   se.sel = sel; se.nsel = n_sel; se.R = tcap / kRegion; se.nq = n_queries; se.max_regions = max_regions;
-  se.ws_stride = stride; se.topk = geom->topk;
-  if (dec) {
-    const int64_t fill_n = (int64_t)n_queries * kGroups * kHistCopies * kHistBins;
-    int64_t fill_blocks = (fill_n + 255) / 256;
-    if (fill_blocks > 4096) fill_blocks = 4096;
-    {
-      ProfScope prof_("k_fill_u32", s);
-      hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)fill_blocks), dim3(256), 0, s, w.hist, fill_n, 0u);
-    }
-    {
-      ProfScope prof_("k_score_decode", s);
-      hipLaunchKernelGGL(k_score_dec, dim3((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries),
-                         dim3(256), 0, s, sa);
-    }
-    st = check_launch("dsa_score_topk: score");
-    if (st != DSA_OK) return st;
-    {
-      ProfScope prof_("k_select_thresh", s);
-      hipLaunchKernelGGL(k_select_thresh, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(kThreshThreads), 0,
-                         s, se);
-    }
-    {
-      ProfScope prof_("k_select_collect", s);
-      hipLaunchKernelGGL(k_select_collect, dim3(se.nblk, kGroups, n_queries), dim3(kCollectThreads), 0, s, se);
-    }
-    st = check_launch("dsa_score_topk: collect");
-    if (st != DSA_OK) return st;
-    {
-      ProfScope prof_("k_select", s);
-      hipLaunchKernelGGL(k_select_dec, dim3((unsigned)((int64_t)n_queries * kGroups)), dim3(kFinalThreads), 0,
-                         s, se);
-    }
+  se.ws_stride = stride; se.tm_stride = sa.tm_stride; se.topk = geom->topk;
+  // Decode-shaped calls (few queries, many regions) score one query per block
+  // over long contiguous tile runs; prefill-shaped calls score 16 queries per
+  // wave so each summary tile feeds 4 MFMA row-sets.
+  if (w.hist) {
+    ProfScope prof_("k_zero", s);
+    const int64_t n16 = (int64_t)(w.hist_bytes / 16);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, (u32x4*)w.hist, n16);
+  }
+  if (decode_shaped(n_queries)) {
+    ProfScope prof_("k_score_decode", s);
+    hipLaunchKernelGGL(k_score_dec, dim3((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries),
+                       dim3(256), 0, s, sa);
   } else {
-    {
-      ProfScope prof_("k_score_prefill", s);
-      hipLaunchKernelGGL(k_score_pre, dim3(ranges, kGroups, (n_queries + 15) / 16), dim3(256), 0, s, sa);
-    }
-    st = check_launch("dsa_score_topk: score");
-    if (st != DSA_OK) return st;
-    {
-      ProfScope prof_("k_select", s);
-      const dim3 grid((unsigned)((int64_t)n_queries * kGroups));
-      if (max_regions <= kPreNT * (8192 / kPreNT))
-        hipLaunchKernelGGL((k_select_pre<kPreNT, 8192 / kPreNT>), grid, dim3(kPreNT), 0, s, se);
-      else if (max_regions <= 1024 * 32)
-        hipLaunchKernelGGL((k_select_pre<1024, 32>), grid, dim3(1024), 0, s, se);
-      else
-        hipLaunchKernelGGL(k_select_long, grid, dim3(512), 0, s, se);
-    }
+    ProfScope prof_("k_score_prefill", s);
+    const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
+    const dim3 grid(ranges, kGroups, (n_queries + 15) / 16);
+    if (tiled_select(max_regions))
+      hipLaunchKernelGGL(k_score_pre<true>, grid, dim3(256), 0, s, sa);
+    else
+      hipLaunchKernelGGL(k_score_pre<false>, grid, dim3(256), 0, s, sa);
+  }
+  st = check_launch("dsa_score_topk: score");
+  if (st != DSA_OK) return st;
+  {
+    ProfScope prof_("k_select", s);
+    const dim3 grid((unsigned)((int64_t)n_queries * kGroups));
+    if (!tiled_select(max_regions))
+      hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>), grid, dim3(kPreNT), 0, s, se);
+    else if (w.hist)
+      hipLaunchKernelGGL(k_select_dec, grid, dim3(kDecNT), 0, s, se);
+    else
+      hipLaunchKernelGGL((k_select_tiles<kTileNT, kMaxTopk * kTile / kTileNT>), grid, dim3(kTileNT), 0, s, se);
   }
   return check_launch("dsa_score_topk: select");
 }

@@ -56,15 +56,40 @@ def test_decode_end_to_end(lens, topk):
     H.assert_decode_parity(r)
 
 
-def test_decode_all_equal_scores_take_the_lowest_regions():
-    """Every score is 0 (z = 0): the level-0 digit holds all candidates, the short list cannot hold
-    them, and the selection falls back to exact narrowing; ties go to the lowest regions."""
-    r = H.run_dsa_decode(0xDE, [40000, 9000], topk=512, zero_z=True)
+@pytest.mark.parametrize("lens", [
+    [40000, 9000],   # <= 8192 regions: every key ranked in registers
+    [70000, 9000],   # > 8192 regions: every tile maximum ties, the lowest 511 tiles are kept
+])
+def test_decode_all_equal_scores_take_the_lowest_regions(lens):
+    """Every score is 0 (z = 0): ties go to the lowest regions."""
+    r = H.run_dsa_decode(0xDE, lens, topk=512, zero_z=True)
     H.assert_decode_parity(r)
-    for b, L in enumerate([40000, 9000]):
+    for b, L in enumerate(lens):
         c = (L - 1) // 8
         for g in range(G):
             assert r["sel"][b, g, :512].tolist() == list(range(511)) + [c]
+
+
+def test_decode_long_contexts_select_through_tile_maxima():
+    """16,384-region capacity: the best 511 tiles by their maxima, then exact ranking inside them
+    (and every tile kept for the 9,000-token sequence)."""
+    r = H.run_dsa_decode(0xD7, [131072, 70001, 9000], topk=512, planted=True)
+    H.assert_decode_parity(r)
+
+
+def test_decode_1m_context_batch_of_4():
+    """The 1,048,576-token batch-4 decode shape with the planted bias, in the launch configuration
+    the benchmark times (8,192 tiles per problem: the tile selection at full capacity); sequences 0
+    and 3 are checked against the oracle."""
+    r = H.run_dsa_decode(0xD8, [1 << 20] * 4, topk=512, planted=True, check_seqs=[0, 3])
+    H.assert_decode_parity(r)
+
+
+def test_decode_beyond_tile_capacity_uses_radix_fallback():
+    """More than 8,192 tiles of 16 regions (a context just over 1M tokens): exact selection by radix
+    narrowing over the scores in global memory."""
+    r = H.run_dsa_decode(0xD9, [(1 << 20) + 72], topk=512, planted=True)
+    H.assert_decode_parity(r)
 
 
 def test_decode_attention_on_oracle_selection():
@@ -171,12 +196,12 @@ def test_prefill_mixed_sequences_and_small_topk():
 
 
 def test_prefill_beyond_8192_regions():
-    # ~8,750 candidate regions per query: the 1024-thread register selection
+    # ~8,750 candidate regions per query: selection through the tile maxima
     _prefill(0xE3, [(69997, 70)], topk=512, check_every=7)
 
 
 def test_prefill_beyond_32768_regions():
-    # ~33,800 candidate regions per query: selection by radix narrowing in global memory
+    # ~33,800 candidate regions per query: 2,110 tiles ranked by their maxima
     _prefill(0xE4, [(270001, 64)], topk=512, check_every=16)
 
 
