@@ -376,7 +376,7 @@ def main():
 
     # ---- decode at 1M
     step, keep = setup_decode(DECODE)
-    kn = ["k_compress", "k_zero", "k_score_decode", "k_select", "k_sgqa_decode", "k_sgqa_merge"]
+    kn = ["k_compress", "k_score_decode", "k_select", "k_sgqa_decode", "k_sgqa_merge"]
     secs, eager, st = timed(step, args.steps, args.warmup, kn, graph=args.graph)
     del keep
     torch.cuda.empty_cache()

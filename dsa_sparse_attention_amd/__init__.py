@@ -128,8 +128,10 @@ def _stream(stream):
 
 
 def workspace(nbytes: int, device=None) -> torch.Tensor:
-    """A 256-byte aligned device buffer (uint8) of at least nbytes."""
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+    """A zero-filled, 256-byte aligned device buffer (uint8) of at least nbytes.  Zero fill only
+    matters for speed: dsa_score_topk's first decode call on a workspace that is not cleared takes
+    the exact fallback selection."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
 
 
 # ---------------------------------------------------------------------------------------------

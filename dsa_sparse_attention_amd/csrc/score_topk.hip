@@ -33,7 +33,10 @@ namespace dsa {
 constexpr int kScoreRange = 1024;  // regions per k_score block
 constexpr int kTile = 16;          // regions per MFMA tile
 constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
-constexpr int kHistCopies = 4;     // decode histogram stripes (by score block index)
+#ifndef DSA_HIST_COPIES
+#define DSA_HIST_COPIES 4
+#endif
+constexpr int kHistCopies = DSA_HIST_COPIES;  // decode histogram stripes (by score block index)
 constexpr int kSelCap = 4096;      // LDS candidate capacity of the radix fallback
 constexpr int kCandCap = 1024;     // decode candidates at or above the level-0 digit
 constexpr int kDirectMax = 8192;   // longest problem selected straight from its scores
@@ -48,7 +51,8 @@ struct ScoreArgs {
   float* scores;        // workspace [Nq][G][ws_stride]
   float* scores_out;    // nullable [Nq][G][max_regions]
   uint32_t* tilemax;    // nullable workspace [Nq][G][tm_stride]: largest key of each 16-region tile
-  uint32_t* hist;       // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts (zeroed beforehand)
+  uint32_t* hist;       // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts, added to
+                        // whatever is there (k_select_dec clears it after reading)
   int64_t R;            // tcap / 8
   int32_t nq, n_seqs, max_regions, ws_stride, tm_stride, topk;
 };
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
 struct SelectArgs {
   const float* scores;      // [Nq][G][ws_stride]
   const uint32_t* tilemax;  // [Nq][G][tm_stride] largest key per 16-region tile, or nullptr
-  const uint32_t* hist;     // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts
+  uint32_t* hist;           // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts (cleared after use)
   const int32_t* qpos;
   int32_t* sel;             // [Nq][G][topk]
   int32_t* nsel;            // [Nq][G]
@@ -997,6 +1001,17 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
+  // The histogram is only a hint for the level-0 digit: it is read here and
+  // cleared for the next call on this workspace, and the digit is checked
+  // against exact counts below.  Thread t holds digits 4095-4t..4092-4t.
+  u32x4 h = {0u, 0u, 0u, 0u};
+  {
+    uint32_t* gh = a.hist + pq * kHistCopies * kHistBins + (kHistBins - 4 - 4 * tid);
+#pragma unroll
+    for (int k = 0; k < kHistCopies; ++k) h += *(const u32x4*)(gh + k * kHistBins);
+#pragma unroll
+    for (int k = 0; k < kHistCopies; ++k) *(u32x4*)(gh + k * kHistBins) = u32x4{0u, 0u, 0u, 0u};
+  }
   if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kDecNT)) return;
   const int64_t ntiles = (c + kTile - 1) / kTile;
   if (ntiles > (int64_t)kDecNT * kDecTilesPT) {
@@ -1013,11 +1028,7 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
 #pragma unroll
   for (int e = 0; e < kDecTilesPT; ++e)
     if ((int64_t)e * kDecNT + tid >= ntiles) tk[e] = 0u;
-  // 1. level-0 digit: thread t holds digits 4095-4t down to 4092-4t
-  const uint32_t* gh = a.hist + pq * kHistCopies * kHistBins + (kHistBins - 4 - 4 * tid);
-  u32x4 h = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int k = 0; k < kHistCopies; ++k) h += *(const u32x4*)(gh + k * kHistBins);
+  // 1. level-0 digit from the histogram
   const uint32_t cnt[4] = {h.w, h.z, h.y, h.x};
   const uint32_t mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
   const uint32_t wi = wave_incl_scan(mine);
@@ -1041,8 +1052,8 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     run += cnt[j];
   }
   __syncthreads();
-  const uint32_t d = sm.res[0], above = sm.res[1], inbin = sm.res[2];
-  if (d == 0xFFFFFFFFu || above + inbin > (uint32_t)kCandCap) {
+  const uint32_t d = sm.res[0], above_h = sm.res[1], inbin_h = sm.res[2];
+  if (d == 0xFFFFFFFFu || above_h + inbin_h > (uint32_t)kCandCap) {
     select_fallback<kDecNT>(a, pq);
     return;
   }
@@ -1058,7 +1069,8 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     for (int e = 0; e < kDecTilesPT; ++e)
       if (f[e] && pos[e] < (uint32_t)kCandCap) sm.tiles[pos[e]] = e * kDecNT + tid;
   }
-  const uint32_t ntl = min(sm.tab[kDecTilesPT * (kDecNT / 64)], (uint32_t)kCandCap);
+  const uint32_t ntl_all = sm.tab[kDecTilesPT * (kDecNT / 64)];
+  const uint32_t ntl = min(ntl_all, (uint32_t)kCandCap);
   __syncthreads();
   uint32_t ncand, nin;
   {
@@ -1096,6 +1108,12 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
       if (fin[e] && pin[e] < (uint32_t)kCandCap) sm.kin[pin[e]] = ck[e];
     }
   }
+  // exact check of the digit: ncand keys are >= Tlo and nin of them in digit d
+  const uint32_t above = ncand - nin;
+  if (ntl_all > (uint32_t)kCandCap || ncand > (uint32_t)kCandCap || above >= need || ncand < need) {
+    select_fallback<kDecNT>(a, pq);
+    return;
+  }
   for (int i = (int)need + 1 + tid; i < a.topk; i += kDecNT) sel[i] = -1;
   if (tid == 0) {
     sel[need] = (int32_t)c;
@@ -1130,10 +1148,6 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   if (pos < need) sel[pos] = sm.ci[tid];
 }
 
-__global__ void k_zero(u32x4* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = u32x4{0u, 0u, 0u, 0u};
-}
 
 #ifndef DSA_TILE_SELECT_NT
 #define DSA_TILE_SELECT_NT 1024
@@ -1234,11 +1248,6 @@ extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries
   // Decode-shaped calls (few queries, many regions) score one query per block
   // over long contiguous tile runs; prefill-shaped calls score 16 queries per
   // wave so each summary tile feeds 4 MFMA row-sets.
-  if (w.hist) {
-    ProfScope prof_("k_zero", s);
-    const int64_t n16 = (int64_t)(w.hist_bytes / 16);
-    hipLaunchKernelGGL(k_zero, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, (u32x4*)w.hist, n16);
-  }
   if (decode_shaped(n_queries)) {
     ProfScope prof_("k_score_decode", s);
     hipLaunchKernelGGL(k_score_dec, dim3((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries),

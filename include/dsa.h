@@ -162,8 +162,14 @@ size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_t n_queries
  *   workspace device buffer of at least dsa_score_topk_workspace_size() bytes
  * Scores are fp32 (bf16 x E4M3 products, fp32 accumulation); on equal fp32
  * scores the lower index wins; a NaN score ranks below every number.
- * The workspace holds the fp32 scores and, when max_regions > 8192, the
- * largest score of every 16-region tile; its contents on entry are ignored.
+ * The workspace holds the fp32 scores, when max_regions > 8192 the largest
+ * score of every 16-region tile, and for decode-shaped calls (n_queries < 64,
+ * max_regions > 8192) a digit histogram that guides the selection.  Results
+ * never depend on the workspace contents on entry: the histogram is checked
+ * against exact counts and the selection falls back to an exact radix pass
+ * when it does not fit.  Each call leaves the histogram cleared, so decode
+ * calls after the first on one workspace (or the first on a zero-filled one)
+ * take the fast path.  Calls sharing a workspace must not overlap.
  */
 dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries, const uint16_t* index_q,
                           const float* z, const int32_t* q_seq, const int32_t* q_pos,
@@ -256,7 +262,7 @@ dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_s
  * earlier records (waiting for them) and switches recording on or off;
  * dsa_profile_kernel_stats waits for the recorded events of one kernel and
  * returns the summed interval (ms) and the number of launches.  Kernel
- * names: k_compress, k_cache_write, k_zero, k_score_decode,
+ * names: k_compress, k_cache_write, k_score_decode,
  * k_score_prefill, k_select, k_sgqa_decode, k_sgqa_merge, k_sgqa_prefill,
  * k_swa_stage, k_swa_attend, k_ring_append.  Host-side state only, guarded
  * by a mutex; at most 8192 launches are recorded between resets.

@@ -92,6 +92,39 @@ def test_decode_beyond_tile_capacity_uses_radix_fallback():
     H.assert_decode_parity(r)
 
 
+def test_decode_selection_does_not_depend_on_workspace_contents():
+    """The digit histogram kept in the workspace only guides the decode selection: a workspace full
+    of random bytes gives the same selection (the digit fails its exact check and the radix fallback
+    runs), the call leaves the histogram cleared, and the next call on that workspace, which takes
+    the fast path, agrees too."""
+    seed, lens = 0xDA, [131072, 100003, 70001]
+    B, tcap = len(lens), H.round128(max(lens))
+    R = tcap // 8
+    geom = dsa.geometry()
+    ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE, True)
+    _, iq, z = H.dev_queries(seed, B)
+    summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
+    lens_np = np.asarray(lens, dtype=np.int32)
+    dsa.dsa_compress_regions(geom, ik, tcap, H.i32(np.zeros(B)), H.i32(lens_np // 8), R, summ, scale)
+    qseq, qpos = H.i32(np.arange(B)), H.i32(lens_np - 1)
+    nbytes = dsa.dsa_score_topk_workspace_size(geom, B, R)
+
+    def run(ws):
+        sel = torch.empty(B * G * 512, dtype=torch.int32, device="cuda")
+        nsel = torch.empty(B * G, dtype=torch.int32, device="cuda")
+        dsa.dsa_score_topk(geom, iq, z, qseq, qpos, B, summ, scale, tcap, R, sel, nsel, workspace=ws)
+        torch.cuda.synchronize()
+        return sel.cpu().numpy(), nsel.cpu().numpy()
+
+    ref_sel, ref_n = run(dsa.workspace(nbytes))
+    junk = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        sel, n = run(junk)
+        assert np.array_equal(n, ref_n)
+        assert np.array_equal(sel, ref_sel)
+
+
 def test_decode_attention_on_oracle_selection():
     """Sparse GQA alone: the oracle's selection is fed to the GPU kernel, every head compared."""
     seed = 0xD7
