@@ -151,11 +151,13 @@ __device__ __forceinline__ void core_compute(CoreState& st, const bf16x8 qb[6], 
   for (int nt = 0; nt < 12; ++nt) st.o[nt] = mfma16x16x32(as_bf16x8(c.v[nt]), pb, st.o[nt]);
 }
 
-// One chunk, loads then compute (no overlap).
+// One chunk, loads then compute (no overlap).  The scheduling barrier keeps
+// every K and V load issued before the first MFMA waits on any of them.
 __device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], const Region& ra,
                                            const Region& rb, float scale_log2) {
   ChunkRegs c;
   core_load(c, ra, rb);
+  __builtin_amdgcn_sched_barrier(0);
   core_compute(st, qb, c, scale_log2);
 }
 
@@ -257,33 +259,39 @@ struct DecodeArgs {
 
 constexpr int kPartStride = 2 + kHeadDim;  // per head: m, l, o[192]
 
+constexpr int kORow = kHeadDim + 4;  // padded LDS row of one head's partial O
+
 __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float sm_o[4][16][kORow];
 
+  // every load that does not depend on the list is issued at once: the
+  // sequence length, the count, this lane's two list entries (clamped index)
+  // and Q; the list decides the K/V addresses afterwards
+  const int64_t sg = (int64_t)b * kGroups + g;
+  const int32_t* lst = a.sel + sg * a.topk;
+  const int e0 = split * kSplitRegions + wave * 4;
+  const int ea = e0 + (n >> 2), eb = e0 + kb;
   int64_t L = a.seq_len[b];
+  int32_t cnt = a.nsel[sg];
+  const int32_t ida = lst[ea < a.topk ? ea : a.topk - 1];
+  const int32_t idb = lst[eb < a.topk ? eb : a.topk - 1];
+  bf16x8 qb[6];
+  load_q(a.q, b, g, qb);
   L = L < 1 ? 1 : (L > a.tcap ? a.tcap : L);
   const int64_t p = L - 1;
-  const int64_t sg = (int64_t)b * kGroups + g;
+  cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
   const uint16_t* kbase = a.k + sg * a.tcap * kHeadDim;
   const uint16_t* vbase = a.v + sg * (a.tcap / kRegion) * kHeadDim * kRegion;
-  const int32_t* lst = a.sel + sg * a.topk;
-  int32_t cnt = a.nsel[sg];
-  cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
 
+  // (a chunk past the count reads the dummy region and contributes nothing)
   CoreState st;
   core_init(st);
-  const int e0 = split * kSplitRegions + wave * 4;
-  if (e0 < cnt) {
-    bf16x8 qb[6];
-    load_q(a.q, b, g, qb);
-    const int ea = e0 + (n >> 2), eb = e0 + kb;
-    const Region ra = dsa_region(kbase, vbase, ea < cnt ? lst[ea] : -1, p);
-    const Region rb = dsa_region(kbase, vbase, eb < cnt ? lst[eb] : -1, p);
-    core_chunk(st, qb, ra, rb, a.scale_log2);
-  }
+  const Region ra = dsa_region(kbase, vbase, ea < cnt ? ida : -1, p);
+  const Region rb = dsa_region(kbase, vbase, eb < cnt ? idb : -1, p);
+  core_chunk(st, qb, ra, rb, a.scale_log2);
   // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i)
   const float lt = core_total_l(st);
   if (kb == 0) {
@@ -291,9 +299,7 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
     sm_l[wave][n] = lt;
   }
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[wave][n][16 * nt + 4 * kb + i] = st.o[nt][i];
+  for (int nt = 0; nt < 12; ++nt) *(f32x4*)&sm_o[wave][n][16 * nt + 4 * kb] = st.o[nt];
   __syncthreads();
   float* part = a.part + ((sg * a.nsplit) + split) * 16 * kPartStride;
   for (int e = threadIdx.x; e < 16 * kHeadDim; e += 256) {
@@ -319,28 +325,37 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
 // One block per (head, group, sequence); thread d owns output channel d.
 // Split weights exp2(m_s - M) are formed once in LDS by the first wave
 // (nsplit <= 64).
+template <int NS>
 __global__ __launch_bounds__(kHeadDim) void k_sgqa_merge(const float* __restrict__ part,
                                                          uint16_t* __restrict__ out, int32_t nsplit) {
+  static_assert(NS <= 64, "one wave forms the split weights");
   const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int64_t sg = (int64_t)b * kGroups + g;
   const float* pp = part + sg * nsplit * 16 * kPartStride + h * kPartStride;
   __shared__ float w[64];
   __shared__ float inv_l;
+  // this thread's partial O of every split, loaded up front (clamped split)
+  float o[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) o[s] = pp[(int64_t)(s < nsplit ? s : 0) * 16 * kPartStride + 2 + d];
   if (d < 64) {
-    const float m = d < nsplit ? pp[(int64_t)d * 16 * kPartStride] : -INFINITY;
+    const int sd = d < nsplit ? d : 0;
+    const float m0 = pp[(int64_t)sd * 16 * kPartStride], l0 = pp[(int64_t)sd * 16 * kPartStride + 1];
+    const float m = d < nsplit ? m0 : -INFINITY;
     float M = m;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float f = (M == -INFINITY || d >= nsplit) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
     w[d] = f;
-    float l = d < nsplit ? f * pp[(int64_t)d * 16 * kPartStride + 1] : 0.0f;
+    float l = d < nsplit ? f * l0 : 0.0f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     if (d == 0) inv_l = l > 0.0f ? 1.0f / l : 0.0f;
   }
   __syncthreads();
   float acc = 0.0f;
-  for (int s = 0; s < nsplit; ++s) acc += w[s] * pp[(int64_t)s * 16 * kPartStride + 2 + d];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc += (s < nsplit ? w[s] : 0.0f) * o[s];
   out[((int64_t)b * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + d] = f32_to_bf16(acc * inv_l);
 }
 
@@ -575,7 +590,8 @@ extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t ba
   if (st != DSA_OK) return st;
   {
     ProfScope prof_("k_sgqa_merge", s);
-    hipLaunchKernelGGL(k_sgqa_merge, dim3(16, kGroups, batch), dim3(kHeadDim), 0, s, (const float*)workspace, out, a.nsplit);
+    hipLaunchKernelGGL(k_sgqa_merge<kMaxTopk / kSplitRegions>, dim3(16, kGroups, batch), dim3(kHeadDim), 0, s,
+                       (const float*)workspace, out, a.nsplit);
   }
   return check_launch("dsa_sparse_gqa_decode: merge");
 }
