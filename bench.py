@@ -149,13 +149,22 @@ def setup_decode(cfg, steps_hint=1):
                p(ws1), ws1.numel())
     a_attn = (gp, B, p(q), p(K), p(V), tcap, p(slen), p(sel), p(nsel), p(out), p(ws2), ws2.numel())
 
+    ws3 = dsa.workspace(dsa.dsa_decode_step_workspace_size(geom, B, R))
+    a_fused = (gp, B, p(q), p(iq), p(z), p(ik), p(K), p(V), tcap, p(slen), p(summ), p(scale), R, p(sel), p(nsel),
+               p(out), p(ws3), ws3.numel())
+
     def step(st):
-        rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
-              or L.dsa_sparse_gqa_decode(*a_attn, st))
+        # the whole step through one entry point (compression folded into the scoring launch), or
+        # the three separate calls
+        if cfg.get("separate"):
+            rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
+                  or L.dsa_sparse_gqa_decode(*a_attn, st))
+        else:
+            rc = L.dsa_decode_step(*a_fused, st)
         if rc:
             raise RuntimeError(f"decode step failed: {rc} {L.dsa_last_error().decode()}")
 
-    keep = (ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, slen, sel, nsel, out, ws1, ws2, geom)
+    keep = (ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, slen, sel, nsel, out, ws1, ws2, ws3, geom)
     return step, keep
 
 
@@ -337,6 +346,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode step as three calls (compress, score_topk, sparse_gqa_decode) instead of dsa_decode_step")
     ap.add_argument("--profile-run", action="store_true",
                     help="setup + a few steps of each workload + a 1 GiB copy kernel, for rocprofv3")
     args = ap.parse_args()
@@ -376,8 +387,10 @@ def main():
 
     # ---- decode at 1M
     step, keep = setup_decode(DECODE)
+    DECODE["separate"] = args.separate
     kn = ["k_compress", "k_score_decode", "k_select", "k_sgqa_decode", "k_sgqa_merge"]
     secs, eager, st = timed(step, args.steps, args.warmup, kn, graph=args.graph)
+    st = {k: v for k, v in st.items() if v[1]}
     del keep
     torch.cuda.empty_cache()
     B, Lc = DECODE["batch"], DECODE["context"]
@@ -385,7 +398,9 @@ def main():
     qps = B * args.steps / secs
     byt = decode_bytes(B, Lc, DECODE["topk"])
     score_ms = st["k_score_decode"][0]
-    achieved = byt["score"] / (score_ms * 1e-3) / 1e9
+    # the fused step folds the compression of the completed regions into the scoring launch
+    score_bytes = byt["score"] + (0 if args.separate else byt["compress"])
+    achieved = score_bytes / (score_ms * 1e-3) / 1e9
     src = source_hash("score_topk.hip")
     traffic = load_traffic("k_score_decode", "decode_b4_1m", src)
     result = {
@@ -395,10 +410,11 @@ def main():
         "eager_ms_per_step": round(eager * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": DECODE["name"], "batch": B, "context_tokens": Lc, "topk": DECODE["topk"],
-                   "regions_per_sequence": Lc // REG},
+                   "regions_per_sequence": Lc // REG,
+                   "entry": "separate calls" if args.separate else "dsa_decode_step"},
         "roofline": {"bound": "hbm", "kernel": "k_score_decode", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": byt["score"],
+                     "traffic": traffic, "algorithmic_bytes_per_launch": score_bytes,
                      "avg_launch_us": round(score_ms * 1e3, 2)},
         "step_hbm": {"algorithmic_bytes": byt["total"],
                      "achieved_GBs": round(byt["total"] / (ms_step * 1e-3) / 1e9, 1),

@@ -26,6 +26,7 @@ ENTRY_POINTS = [
     "dsa_geometry_default", "dsa_status_string", "dsa_last_error", "dsa_cache_write",
     "dsa_compress_regions", "dsa_score_topk_workspace_size", "dsa_score_topk",
     "dsa_sparse_gqa_workspace_size", "dsa_sparse_gqa_decode", "dsa_sparse_gqa_prefill",
+    "dsa_decode_step_workspace_size", "dsa_decode_step",
     "swa_attention_workspace_size", "swa_attention", "swa_ring_append",
     "dsa_profile_enable", "dsa_profile_kernel_stats",
 ]
@@ -70,6 +71,9 @@ def load() -> ctypes.CDLL:
     L.dsa_sparse_gqa_workspace_size.restype = sz
     L.dsa_sparse_gqa_decode.argtypes = [G, i32, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_gqa_prefill.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp]
+    L.dsa_decode_step_workspace_size.argtypes = [G, i32, i32]
+    L.dsa_decode_step_workspace_size.restype = sz
+    L.dsa_decode_step.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     L.swa_attention_workspace_size.argtypes = [G, i32, i32, i32]
     L.swa_attention_workspace_size.restype = sz
     L.swa_attention.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -219,6 +223,41 @@ def dsa_sparse_gqa_decode(geom, q, k_cache, v_cache, tcap, seq_len, sel, n_sel, 
     _check(load().dsa_sparse_gqa_decode(ctypes.byref(geom), batch, _ptr(q), _ptr(k_cache), _ptr(v_cache), tcap,
                                         _ptr(seq_len), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
                                         workspace.numel(), _stream(stream)))
+
+
+def dsa_decode_step_workspace_size(geom, batch, max_regions) -> int:
+    return int(load().dsa_decode_step_workspace_size(ctypes.byref(geom), batch, max_regions))
+
+
+def dsa_decode_step(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_len, summ, scale, max_regions, sel,
+                    n_sel, out, workspace=None, stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (index_q, "index_q"), (index_k, "index_k"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _dt(z, torch.float32, "z")
+    _dt(summ, torch.uint8, "summ")
+    _dt(scale, torch.float32, "scale")
+    R = tcap // REGION
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(index_q, batch * IDX_HEADS * PROXY, "index_q")
+    _numel_at_least(z, batch * IDX_HEADS, "z")
+    _numel_at_least(index_k, batch * GROUPS * tcap * PROXY, "index_k")
+    _numel_at_least(k_cache, batch * GROUPS * tcap * HEAD_DIM, "k_cache")
+    _numel_at_least(v_cache, batch * GROUPS * tcap * HEAD_DIM, "v_cache")
+    _numel_at_least(summ, batch * GROUPS * R * PROXY, "summ")
+    _numel_at_least(scale, batch * GROUPS * R, "scale")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_decode_step_workspace_size(geom, batch, max_regions), q.device)
+    _check(load().dsa_decode_step(ctypes.byref(geom), batch, _ptr(q), _ptr(index_q), _ptr(z), _ptr(index_k),
+                                  _ptr(k_cache), _ptr(v_cache), tcap, _ptr(seq_len), _ptr(summ), _ptr(scale),
+                                  max_regions, _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
 
 
 def dsa_sparse_gqa_prefill(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap, sel, n_sel, out, stream=None):

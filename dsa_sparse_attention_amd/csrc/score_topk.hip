@@ -26,7 +26,7 @@
 //    maxima of need tiles that all rank above it), so at most 511 tiles of 16
 //    regions are then ranked exactly.  A radix fallback in global memory
 //    covers problems beyond the register capacity.
-#include "common.hpp"
+#include "compress_dev.hpp"
 
 namespace dsa {
 
@@ -44,8 +44,9 @@ constexpr int kDirectMax = 8192;   // longest problem selected straight from its
 struct ScoreArgs {
   const uint16_t* iq;   // [Nq][16][P]
   const float* z;       // [Nq][16]
-  const int32_t* qseq;  // [Nq]
-  const int32_t* qpos;  // [Nq]
+  const int32_t* qseq;  // [Nq], or nullptr: query i belongs to sequence i
+  const int32_t* qpos;  // [Nq], or nullptr: position slen[i] - 1
+  const int32_t* slen;  // [Nq] sequence lengths when qpos is nullptr
   const uint8_t* summ;  // [S][G][R][P]
   const float* scale;   // [S][G][R]
   float* scores;        // workspace [Nq][G][ws_stride]
@@ -71,6 +72,15 @@ __device__ __forceinline__ int64_t current_region(int32_t pos, int64_t R, int32_
   if (c > R - 1) c = R - 1;
   if (c > max_regions - 1) c = max_regions - 1;
   return c;
+}
+
+// Position and sequence of query i: explicit arrays, or (decode step) query
+// i is the last token of sequence i.
+__device__ __forceinline__ int32_t query_pos(const int32_t* qpos, const int32_t* slen, int64_t i) {
+  return qpos ? qpos[i] : slen[i] - 1;
+}
+__device__ __forceinline__ int32_t query_seq(const int32_t* qseq, int64_t i) {
+  return qseq ? qseq[i] : (int32_t)i;
 }
 
 // 16 E4M3 codes -> two bf16x8 operands (exact conversion).
@@ -178,9 +188,9 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   if (a.hist)
     for (int i = threadIdx.x; i < kHistBins; i += 256) hist_lds[i] = 0;
 
-  int32_t seq = a.qseq[qi];
+  int32_t seq = query_seq(a.qseq, qi);
   seq = seq < 0 ? 0 : (seq >= a.n_seqs ? a.n_seqs - 1 : seq);
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
   bf16x8 A[8];
   {
     const uint16_t* qp = a.iq + ((int64_t)qi * kIdxHeads + 4 * g + (n & 3)) * kProxy + 16 * kb;
@@ -286,6 +296,7 @@ __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kb = lane >> 4;
   const int q0 = blockIdx.z * QW;
+
   const int64_t range0 = (int64_t)blockIdx.x * kScoreRange;
 
   uint32_t remaining = 0;  // bit j: query q0+j still to process
@@ -294,17 +305,17 @@ __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
 
   while (remaining) {
     const int lead = __builtin_ctz(remaining);
-    int32_t seq = a.qseq[q0 + lead];
+    int32_t seq = query_seq(a.qseq, q0 + lead);
     seq = seq < 0 ? 0 : (seq >= a.n_seqs ? a.n_seqs - 1 : seq);
     uint32_t active = 0;
     int64_t cmax = 0;
     for (int j = 0; j < QW; ++j) {
       if (!(remaining >> j & 1u)) continue;
-      int32_t sj = a.qseq[q0 + j];
+      int32_t sj = query_seq(a.qseq, q0 + j);
       sj = sj < 0 ? 0 : (sj >= a.n_seqs ? a.n_seqs - 1 : sj);
       if (sj == seq) {
         active |= 1u << j;
-        const int64_t cj = current_region(a.qpos[q0 + j], a.R, a.max_regions);
+        const int64_t cj = current_region(query_pos(a.qpos, a.slen, q0 + j), a.R, a.max_regions);
         cmax = cj > cmax ? cj : cmax;
       }
     }
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
       if (ovalid) {
         const f32x4 zz = *(const f32x4*)(a.z + (int64_t)(q0 + jout) * kIdxHeads + 4 * g);
         zq[rs][0] = zz[0]; zq[rs][1] = zz[1]; zq[rs][2] = zz[2]; zq[rs][3] = zz[3];
-        cq[rs] = current_region(a.qpos[q0 + jout], a.R, a.max_regions);
+        cq[rs] = current_region(query_pos(a.qpos, a.slen, q0 + jout), a.R, a.max_regions);
       } else {
         zq[rs][0] = zq[rs][1] = zq[rs][2] = zq[rs][3] = 0.0f;
         cq[rs] = 0;
@@ -392,6 +403,11 @@ __global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
 
 struct SelectArgs {
   const float* scores;      // [Nq][G][ws_stride]
+  const int32_t* slen;      // [Nq] sequence lengths when qpos is nullptr
+  const uint16_t* ik;       // decode step: index_k of the sequences (folded compression), or nullptr
+  uint8_t* csumm;           // decode step: summaries written by the folded compression
+  float* cscale;
+  int32_t n_seqs;
   const uint32_t* tilemax;  // [Nq][G][tm_stride] largest key per 16-region tile, or nullptr
   uint32_t* hist;           // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts (cleared after use)
   const int32_t* qpos;
@@ -587,7 +603,7 @@ __global__ __launch_bounds__(NT) void k_select_pre(SelectArgs a) {
   const int64_t pq = blockIdx.x;
   const int qi = (int)(pq / kGroups);
   __shared__ SelectSmem<NT, KPT> sm;
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
   if (select_trivial(c, need, sel, a.nsel + pq, a.topk, NT)) return;
@@ -630,7 +646,7 @@ __device__ void select_fallback(const SelectArgs& a, int64_t pq) {
     sh_count = 0;
   }
   __syncthreads();
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
   const int64_t need64 = (c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1);
   const uint32_t need = (uint32_t)need64;
   int32_t* sel = a.sel + pq * a.topk;
@@ -771,7 +787,7 @@ __global__ __launch_bounds__(NT) void k_select_tiles(SelectArgs a) {
   const int qi = (int)(pq / kGroups);
   __shared__ SelectSmem<NT, KPT> sm;
   __shared__ int32_t tiles[kMaxTopk];
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
   if (select_trivial(c, need, sel, a.nsel + pq, a.topk, NT)) return;
@@ -922,6 +938,25 @@ __device__ void ordered_positions2(const bool (&fa)[KPT], const bool (&fb)[KPT],
   *nb = tb[n];
 }
 
+// Folded compression (decode step): query qi's token completes region p/8
+// when (p+1) is a multiple of 8; that region is summarised here.  Selection
+// and the scoring before it read only regions before the query's current
+// region, so they never touch the summary being written.
+__device__ __forceinline__ void folded_compress(const SelectArgs& a, int64_t qi, int g) {
+  const int64_t p = query_pos(a.qpos, a.slen, qi);
+  if (p < 0 || (p + 1) % kRegion != 0 || (p + 1) / kRegion > a.R) return;
+  int32_t seq = (int32_t)qi;
+  seq = seq >= a.n_seqs ? a.n_seqs - 1 : seq;
+  compress_region_wave(a.ik, a.R * kRegion, seq, p / kRegion, g, a.csumm, a.cscale);
+}
+
+// Standalone form for the selection paths without folded blocks: one wave per
+// (query, group).
+__global__ __launch_bounds__(256) void k_fold_compress(SelectArgs a) {
+  const int64_t qi = blockIdx.x;
+  folded_compress(a, qi, threadIdx.x >> 6);
+}
+
 constexpr int kDecNT = 1024;
 constexpr int kDecTilesPT = 8;                          // tile keys per thread (8192 tiles)
 constexpr int kDecCandPT = kCandCap * kTile / kDecNT;   // candidate slots per thread
@@ -998,7 +1033,12 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   const int qi = (int)(pq / kGroups);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   __shared__ DecSmem sm;
-  const int64_t c = current_region(a.qpos[qi], a.R, a.max_regions);
+  if (pq >= (int64_t)a.nq * kGroups) {  // folded compression: wave w -> (query, group)
+    const int64_t fq = (pq - (int64_t)a.nq * kGroups) * (kDecNT / 64 / kGroups) + w / kGroups;
+    if (fq < a.nq) folded_compress(a, fq, w % kGroups);
+    return;
+  }
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
   // The histogram is only a hint for the level-0 digit: it is read here and
@@ -1211,6 +1251,68 @@ extern "C" size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_
   return score_ws_layout(nullptr, n_queries, max_regions).bytes;
 }
 
+// Score + select launches shared by dsa_score_topk and dsa_decode_step (which
+// passes q_seq = q_pos = nullptr with seq_len, and index_k for the folded
+// compression).
+static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries, const uint16_t* index_q,
+                                    const float* z, const int32_t* q_seq, const int32_t* q_pos,
+                                    const int32_t* seq_len, int32_t n_seqs, const uint8_t* summ,
+                                    const float* scale, int64_t tcap, int32_t max_regions, int32_t* sel,
+                                    int32_t* n_sel, float* scores_out, const uint16_t* index_k,
+                                    uint8_t* csumm, float* cscale, void* workspace, hipStream_t s) {
+  const ScoreWs w = score_ws_layout(workspace, n_queries, max_regions);
+  const int32_t stride = (int32_t)ws_stride_of(max_regions);
+  ScoreArgs sa;
+  sa.iq = index_q; sa.z = z; sa.qseq = q_seq; sa.qpos = q_pos; sa.slen = seq_len; sa.summ = summ; sa.scale = scale;
+  sa.scores = w.scores; sa.scores_out = scores_out; sa.tilemax = w.tilemax; sa.hist = w.hist;
+  sa.R = tcap / kRegion; sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions;
+  sa.ws_stride = stride; sa.tm_stride = (int32_t)tm_stride_of(max_regions); sa.topk = geom->topk;
+  SelectArgs se;
+  se.scores = w.scores; se.slen = seq_len; se.tilemax = w.tilemax; se.hist = w.hist; se.qpos = q_pos;
+  se.ik = index_k; se.csumm = csumm; se.cscale = cscale; se.n_seqs = n_seqs;
+  se.sel = sel; se.nsel = n_sel; se.R = tcap / kRegion; se.nq = n_queries; se.max_regions = max_regions;
+  se.ws_stride = stride; se.tm_stride = sa.tm_stride; se.topk = geom->topk;
+  // the decode step's compression runs as extra blocks of the decode
+  // selection launch, or as its own small launch on the other paths
+  const bool fold_in_select = index_k && w.hist;
+  if (index_k && !fold_in_select) {
+    ProfScope prof_("k_compress", s);
+    hipLaunchKernelGGL(k_fold_compress, dim3((unsigned)n_queries), dim3(256), 0, s, se);
+  }
+  // Decode-shaped calls (few queries, many regions) score one query per block
+  // over long contiguous tile runs; prefill-shaped calls score 16 queries per
+  // wave so each summary tile feeds 4 MFMA row-sets.
+  if (decode_shaped(n_queries)) {
+    ProfScope prof_("k_score_decode", s);
+    hipLaunchKernelGGL(k_score_dec, dim3((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries),
+                       dim3(256), 0, s, sa);
+  } else {
+    ProfScope prof_("k_score_prefill", s);
+    const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
+    const dim3 grid(ranges, kGroups, (n_queries + 15) / 16);
+    if (tiled_select(max_regions))
+      hipLaunchKernelGGL(k_score_pre<true>, grid, dim3(256), 0, s, sa);
+    else
+      hipLaunchKernelGGL(k_score_pre<false>, grid, dim3(256), 0, s, sa);
+  }
+  dsa_status st = check_launch("dsa_score_topk: score");
+  if (st != DSA_OK) return st;
+  {
+    ProfScope prof_("k_select", s);
+    const dim3 grid((unsigned)((int64_t)n_queries * kGroups));
+    if (!tiled_select(max_regions))
+      hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>), grid, dim3(kPreNT), 0, s, se);
+    else if (w.hist) {
+      const int64_t folds = fold_in_select ? ((int64_t)n_queries * kGroups + kDecNT / 64 - 1) / (kDecNT / 64) : 0;
+      hipLaunchKernelGGL(k_select_dec, dim3((unsigned)((int64_t)n_queries * kGroups + folds)), dim3(kDecNT), 0, s,
+                         se);
+    }
+    else
+      hipLaunchKernelGGL((k_select_tiles<kTileNT, kMaxTopk * kTile / kTileNT>), grid, dim3(kTileNT), 0, s, se);
+  }
+  return check_launch("dsa_score_topk: select");
+}
+
 extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries,
                                      const uint16_t* index_q, const float* z,
                                      const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
@@ -1232,46 +1334,42 @@ extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries
   if (workspace_bytes < dsa_score_topk_workspace_size(geom, n_queries, max_regions))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_score_topk: workspace too small");
   if (n_queries > 65535 * 16) return fail(DSA_ERR_UNSUPPORTED, "dsa_score_topk: too many queries");
-  hipStream_t s = as_stream(stream);
-  const ScoreWs w = score_ws_layout(workspace, n_queries, max_regions);
-  const int32_t stride = (int32_t)ws_stride_of(max_regions);
+  return launch_score_topk(geom, n_queries, index_q, z, q_seq, q_pos, nullptr, n_seqs, summ, scale, tcap,
+                           max_regions, sel, n_sel, scores_out, nullptr, nullptr, nullptr, workspace,
+                           as_stream(stream));
+}
 
-  ScoreArgs sa;
-  sa.iq = index_q; sa.z = z; sa.qseq = q_seq; sa.qpos = q_pos; sa.summ = summ; sa.scale = scale;
-  sa.scores = w.scores; sa.scores_out = scores_out; sa.tilemax = w.tilemax; sa.hist = w.hist;
-  sa.R = tcap / kRegion; sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions;
-  sa.ws_stride = stride; sa.tm_stride = (int32_t)tm_stride_of(max_regions); sa.topk = geom->topk;
-  SelectArgs se;
-  se.scores = w.scores; se.tilemax = w.tilemax; se.hist = w.hist; se.qpos = q_pos;
-  se.sel = sel; se.nsel = n_sel; se.R = tcap / kRegion; se.nq = n_queries; se.max_regions = max_regions;
-  se.ws_stride = stride; se.tm_stride = sa.tm_stride; se.topk = geom->topk;
-  // Decode-shaped calls (few queries, many regions) score one query per block
-  // over long contiguous tile runs; prefill-shaped calls score 16 queries per
-  // wave so each summary tile feeds 4 MFMA row-sets.
-  if (decode_shaped(n_queries)) {
-    ProfScope prof_("k_score_decode", s);
-    hipLaunchKernelGGL(k_score_dec, dim3((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries),
-                       dim3(256), 0, s, sa);
-  } else {
-    ProfScope prof_("k_score_prefill", s);
-    const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
-    const dim3 grid(ranges, kGroups, (n_queries + 15) / 16);
-    if (tiled_select(max_regions))
-      hipLaunchKernelGGL(k_score_pre<true>, grid, dim3(256), 0, s, sa);
-    else
-      hipLaunchKernelGGL(k_score_pre<false>, grid, dim3(256), 0, s, sa);
-  }
-  st = check_launch("dsa_score_topk: score");
+extern "C" size_t dsa_decode_step_workspace_size(const dsa_geometry* geom, int32_t batch, int32_t max_regions) {
+  if (batch <= 0 || max_regions <= 0) return 256;
+  return align256(dsa_score_topk_workspace_size(geom, batch, max_regions)) +
+         align256(dsa_sparse_gqa_workspace_size(geom, batch));
+}
+
+extern "C" dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                      const uint16_t* index_q, const float* z, const uint16_t* index_k,
+                                      const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                                      const int32_t* seq_len, uint8_t* summ, float* scale,
+                                      int32_t max_regions, int32_t* sel, int32_t* n_sel, uint16_t* out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  {
-    ProfScope prof_("k_select", s);
-    const dim3 grid((unsigned)((int64_t)n_queries * kGroups));
-    if (!tiled_select(max_regions))
-      hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>), grid, dim3(kPreNT), 0, s, se);
-    else if (w.hist)
-      hipLaunchKernelGGL(k_select_dec, grid, dim3(kDecNT), 0, s, se);
-    else
-      hipLaunchKernelGGL((k_select_tiles<kTileNT, kMaxTopk * kTile / kTileNT>), grid, dim3(kTileNT), 0, s, se);
-  }
-  return check_launch("dsa_score_topk: select");
+  if (batch < 0 || max_regions < 0 || tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: bad sizes (tcap must be a positive multiple of 128)");
+  if (batch == 0) return DSA_OK;
+  if (max_regions == 0) return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: max_regions must be positive");
+  if (!q || !index_q || !z || !index_k || !k_cache || !v_cache || !seq_len || !summ || !scale || !sel ||
+      !n_sel || !out || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: NULL pointer");
+  if ((size_t)workspace & 255)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: workspace must be 256-byte aligned");
+  if (workspace_bytes < dsa_decode_step_workspace_size(geom, batch, max_regions))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_decode_step: workspace too small");
+  if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, "dsa_decode_step: batch > 65535");
+  hipStream_t s = as_stream(stream);
+  const size_t ws1 = align256(dsa_score_topk_workspace_size(geom, batch, max_regions));
+  st = launch_score_topk(geom, batch, index_q, z, nullptr, nullptr, seq_len, batch, summ, scale, tcap, max_regions,
+                         sel, n_sel, nullptr, index_k, summ, scale, workspace, s);
+  if (st != DSA_OK) return st;
+  return dsa_sparse_gqa_decode(geom, batch, q, k_cache, v_cache, tcap, seq_len, sel, n_sel, out,
+                               (char*)workspace + ws1, workspace_bytes - ws1, stream);
 }

@@ -199,6 +199,35 @@ dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t batch, const 
                                  uint16_t* out, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* Workspace bytes dsa_decode_step needs. */
+size_t dsa_decode_step_workspace_size(const dsa_geometry* geom, int32_t batch, int32_t max_regions);
+
+/*
+ * One decode step of the DSA layer for `batch` sequences, one query token per
+ * sequence ([P1] steps ①-④ in order; [P3] kernel list): the region the
+ * query token completes is compressed, every earlier complete region is
+ * scored, the top-k plus the current region are selected, and sparse GQA runs
+ * over them.  Results are identical to dsa_compress_regions (of region
+ * seq_len/8 - 1 when seq_len is a multiple of 8) + dsa_score_topk (q_seq = b,
+ * q_pos = seq_len[b] - 1) + dsa_sparse_gqa_decode; the compression is folded
+ * into the scoring launch (its region is never scored in the same step).
+ *   q [batch][64][D], index_q [batch][16][P] bf16; z [batch][16] fp32
+ *   index_k, k_cache, v_cache, summ, scale: caches of `batch` sequences with
+ *             capacity tcap (layouts above); summaries of all complete regions
+ *             before the query's region must be present
+ *   seq_len   [batch] int32 device, 1 <= seq_len <= tcap, including the token
+ *   max_regions host bound: seq_len/8 <= max_regions (grid, workspace)
+ *   sel, n_sel, out as for dsa_score_topk and dsa_sparse_gqa_decode
+ *   workspace >= dsa_decode_step_workspace_size() bytes, 256-byte aligned;
+ *             the same contents rules as dsa_score_topk's workspace apply
+ */
+dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                           const uint16_t* index_q, const float* z, const uint16_t* index_k,
+                           const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                           const int32_t* seq_len, uint8_t* summ, float* scale, int32_t max_regions,
+                           int32_t* sel, int32_t* n_sel, uint16_t* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /*
  * Sparse GQA for a chunk of prefill queries ([P3] kernel list:
  * sparse_attention_prefill).  Same maths as decode, per query i of sequence

@@ -104,3 +104,22 @@ def test_swa_window_must_be_512(lib):
     vp = ctypes.c_void_p(256)
     assert lib.swa_attention(ctypes.byref(g), 256, 1, 1, vp, vp, vp, vp, vp, vp, vp, vp, vp, 1 << 20, None) == 2
     assert lib.swa_ring_append(ctypes.byref(g), 1024, 1, 1, vp, vp, vp, vp, vp, vp, None) == 2
+
+
+def test_decode_step_argument_checks(lib):
+    g = dsa.geometry()
+    vp = ctypes.c_void_p(256)
+    need = lib.dsa_decode_step_workspace_size(ctypes.byref(g), 4, 16384)
+    assert need >= lib.dsa_score_topk_workspace_size(ctypes.byref(g), 4, 16384) + \
+        lib.dsa_sparse_gqa_workspace_size(ctypes.byref(g), 4)
+    args = [vp] * 6 + [131072, vp, vp, vp, 16384, vp, vp, vp, vp]
+    assert lib.dsa_decode_step(ctypes.byref(g), 4, *args, need - 1, None) == 3
+    assert lib.dsa_decode_step(ctypes.byref(g), 4, *args[:-1], ctypes.c_void_p(260), need, None) == 1
+    bad = list(args)
+    bad[3] = None  # index_k
+    assert lib.dsa_decode_step(ctypes.byref(g), 4, *bad, need, None) == 1
+    bad = list(args)
+    bad[6] = 131000  # tcap not a multiple of 128
+    assert lib.dsa_decode_step(ctypes.byref(g), 4, *bad, need, None) == 1
+    assert lib.dsa_decode_step(ctypes.byref(g), 0, *([None] * 6 + [128, None, None, None, 8, None, None, None,
+                                                                    None]), 0, None) == 0

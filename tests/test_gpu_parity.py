@@ -125,6 +125,47 @@ def test_decode_selection_does_not_depend_on_workspace_contents():
         assert np.array_equal(sel, ref_sel)
 
 
+@pytest.mark.parametrize("lens", [[1 << 20] * 4, [131072, 70001, 9000, 8192, 17, 1]])
+def test_decode_step_matches_the_separate_calls(lens):
+    """dsa_decode_step, whose compression of the completed region runs inside the scoring launch,
+    gives bit for bit what dsa_compress_regions + dsa_score_topk + dsa_sparse_gqa_decode give,
+    summaries included (only the region a query token completes is written)."""
+    seed = 0xDB + len(lens)
+    B, tcap = len(lens), H.round128(max(lens))
+    R = tcap // 8
+    geom = dsa.geometry()
+    ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE, True)
+    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_KTILED)
+    V = H.dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
+    q, iq, z = H.dev_queries(seed, B)
+    lens_np = np.asarray(lens, dtype=np.int32)
+    slen = H.i32(lens_np)
+
+    def prefix_summaries():
+        summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
+        scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
+        dsa.dsa_compress_regions(geom, ik, tcap, H.i32(np.zeros(B)), H.i32((lens_np - 1) // 8), R, summ, scale)
+        return summ, scale
+
+    def outputs():
+        return (torch.empty(B * G * 512, dtype=torch.int32, device="cuda"),
+                torch.empty(B * G, dtype=torch.int32, device="cuda"),
+                torch.empty(B * HQ * D, dtype=torch.bfloat16, device="cuda"))
+
+    s1, c1 = prefix_summaries()
+    sel1, n1, o1 = outputs()
+    dsa.dsa_compress_regions(geom, ik, tcap, H.i32((lens_np - 1) // 8), H.i32(lens_np // 8), 1, s1, c1)
+    dsa.dsa_score_topk(geom, iq, z, H.i32(np.arange(B)), H.i32(lens_np - 1), B, s1, c1, tcap, R, sel1, n1)
+    dsa.dsa_sparse_gqa_decode(geom, q, K, V, tcap, slen, sel1, n1, o1)
+    s2, c2 = prefix_summaries()
+    sel2, n2, o2 = outputs()
+    dsa.dsa_decode_step(geom, q, iq, z, ik, K, V, tcap, slen, s2, c2, R, sel2, n2, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(n1, n2) and torch.equal(sel1, sel2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(s1, s2) and torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+
+
 def test_decode_attention_on_oracle_selection():
     """Sparse GQA alone: the oracle's selection is fed to the GPU kernel, every head compared."""
     seed = 0xD7
