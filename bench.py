@@ -398,8 +398,8 @@ def main():
     qps = B * args.steps / secs
     byt = decode_bytes(B, Lc, DECODE["topk"])
     score_ms = st["k_score_decode"][0]
-    # the fused step folds the compression of the completed regions into the scoring launch
-    score_bytes = byt["score"] + (0 if args.separate else byt["compress"])
+    # (the fused step's compression runs inside the selection launch, not the scoring one)
+    score_bytes = byt["score"]
     achieved = score_bytes / (score_ms * 1e-3) / 1e9
     src = source_hash("score_topk.hip")
     traffic = load_traffic("k_score_decode", "decode_b4_1m", src)

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
 // stores each tile's largest key (left out of the short-context variant,
 // where its registers would halve the waves per SIMD).
 template <bool TILEMAX>
-__global__ __launch_bounds__(256) void k_score_pre(ScoreArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_pre(ScoreArgs a) {
   constexpr int QW = 16, NRS = 4;
   const int g = blockIdx.y;
   const int wave = threadIdx.x >> 6;
