@@ -165,7 +165,7 @@ __device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], co
 // one computes.  region_of(e, lane) gives the Region for list entry e as seen
 // by this lane; entries >= n are invalid.
 #ifndef DSA_ATTN_PIPELINE
-#define DSA_ATTN_PIPELINE 1
+#define DSA_ATTN_PIPELINE 2
 #endif
 #ifndef DSA_ATTN_WAVES
 #define DSA_ATTN_WAVES 1
@@ -182,7 +182,23 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
   }
   // The prefetch is issued unconditionally (past the end it reads the dummy
   // region of an invalid entry), so the wait before each compute only covers
-  // the chunk being used and not the one in flight behind it.
+  // the chunk being used and not the ones in flight behind it.
+#if DSA_ATTN_PIPELINE >= 2
+  // three chunks in registers: two in flight while one computes
+  ChunkRegs b0, b1, b2;
+  core_load(b0, region_of(nn >> 2), region_of(kb));
+  core_load(b1, region_of(4 + (nn >> 2)), region_of(4 + kb));
+  for (int64_t e0 = 0; e0 < n; e0 += 12) {
+    core_load(b2, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
+    core_compute(st, qb, b0, scale_log2);
+    if (e0 + 4 >= n) break;
+    core_load(b0, region_of(e0 + 12 + (nn >> 2)), region_of(e0 + 12 + kb));
+    core_compute(st, qb, b1, scale_log2);
+    if (e0 + 8 >= n) break;
+    core_load(b1, region_of(e0 + 16 + (nn >> 2)), region_of(e0 + 16 + kb));
+    core_compute(st, qb, b2, scale_log2);
+  }
+#else
   ChunkRegs b0, b1;
   core_load(b0, region_of(nn >> 2), region_of(kb));
   for (int64_t e0 = 0; e0 < n; e0 += 8) {
@@ -192,6 +208,7 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
     core_load(b0, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
     core_compute(st, qb, b1, scale_log2);
   }
+#endif
 }
 
 // Total softmax denominator of the lane's head (sum over the 4 kb lanes).
