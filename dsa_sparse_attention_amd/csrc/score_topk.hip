@@ -31,6 +31,17 @@
 namespace dsa {
 
 constexpr int kScoreRange = 1024;  // regions per k_score block
+constexpr int kRingSlot = 4096 + 256;  // one summary tile in a wave's LDS ring: 4 KB of codes, then the
+                                       // scale copy (4 bytes per lane; lanes 0..15 hold the tile's scales)
+#ifndef DSA_PRE_RING
+#define DSA_PRE_RING 4
+#endif
+#ifndef DSA_PRE_WAVES
+#define DSA_PRE_WAVES 2
+#endif
+constexpr int kPreRing = DSA_PRE_RING;  // tiles in a wave's ring: kPreRing - 1 copies ahead of use
+static_assert(kPreRing >= 3 && kPreRing <= 5, "ring depth with a wait count below");
+typedef __attribute__((address_space(3))) uint8_t* LdsPtr;
 constexpr int kTile = 16;          // regions per MFMA tile
 constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
 #ifndef DSA_HIST_COPIES
@@ -289,15 +300,15 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
 // stores each tile's largest key (left out of the short-context variant,
 // where its registers would halve the waves per SIMD).
 template <bool TILEMAX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_pre(ScoreArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAVES, DSA_PRE_WAVES))) void k_score_pre(ScoreArgs a) {
   constexpr int QW = 16, NRS = 4;
   const int g = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kb = lane >> 4;
   const int q0 = blockIdx.z * QW;
-
   const int64_t range0 = (int64_t)blockIdx.x * kScoreRange;
+  __shared__ __attribute__((aligned(16))) uint8_t ring_all[4][kPreRing][kRingSlot];
 
   uint32_t remaining = 0;  // bit j: query q0+j still to process
   for (int j = 0; j < QW; ++j)
@@ -324,9 +335,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // A operand: rows = (query, head) pairs of group g; channel permutation
     // pi(s, kb, e) = 64*(s/2) + 16*kb + 8*(s%2) + e.
     bf16x8 A[NRS][8];
-    float zq[NRS][4];
-    int64_t cq[NRS];
-    int32_t qidx[NRS];
+    // epilogue data of the lane's output query in each row-set: z of the
+    // group's 4 heads and the current region (-1: not in this pass)
+    f32x4 zq[NRS];
+    int32_t cq[NRS];
+#pragma unroll
+    for (int rs = 0; rs < NRS; ++rs) {
+      const int jout = 4 * rs + kb;
+      const bool ovalid = (active >> jout & 1u);
+      zq[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      cq[rs] = -1;
+      if (ovalid) {
+        zq[rs] = *(const f32x4*)(a.z + (int64_t)(q0 + jout) * kIdxHeads + 4 * g);
+        cq[rs] = (int32_t)current_region(query_pos(a.qpos, a.slen, q0 + jout), a.R, a.max_regions);
+      }
+    }
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
       const int jrow = 4 * rs + (n >> 2);  // query of A row n
@@ -339,47 +362,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (rvalid) v = ld16(qp + 64 * (s >> 1) + 8 * (s & 1));
         A[rs][s] = as_bf16x8(v);
       }
-      // output rows 4kb..4kb+3 of row-set rs belong to query jout
-      const int jout = 4 * rs + kb;
-      const bool ovalid = (active >> jout & 1u);
-      qidx[rs] = ovalid ? q0 + jout : -1;
-      if (ovalid) {
-        const f32x4 zz = *(const f32x4*)(a.z + (int64_t)(q0 + jout) * kIdxHeads + 4 * g);
-        zq[rs][0] = zz[0]; zq[rs][1] = zz[1]; zq[rs][2] = zz[2]; zq[rs][3] = zz[3];
-        cq[rs] = current_region(query_pos(a.qpos, a.slen, q0 + jout), a.R, a.max_regions);
-      } else {
-        zq[rs][0] = zq[rs][1] = zq[rs][2] = zq[rs][3] = 0.0f;
-        cq[rs] = 0;
-      }
     }
 
     const int64_t rend = (range0 + kScoreRange < cmax) ? range0 + kScoreRange : cmax;
     const uint8_t* sbase = a.summ + ((int64_t)seq * kGroups + g) * a.R * kProxy;
     const float* scbase = a.scale + ((int64_t)seq * kGroups + g) * a.R;
-    for (int64_t t0 = range0 + (int64_t)wave * kTile; t0 < rend; t0 += 4 * kTile) {
+    // This wave's tiles k = 0..nk-1 start at region first + 64k.  Each tile
+    // (4 KB of codes + its 16 scales) is copied global -> LDS by the DMA form
+    // of the loads, kPreRing - 1 tiles ahead of use, into a ring of the wave.
+    // Every copy is issued (past the end it re-reads a clamped tile), so
+    // exactly kPreRing - 1 tiles' copies (5 operations each) were issued after
+    // the tile being read, and in-order completion makes a vmcnt wait for
+    // that many leave only them outstanding.
+    const int64_t first = range0 + (int64_t)wave * kTile;
+    const int nk = first < rend ? (int)((rend - first + 4 * kTile - 1) / (4 * kTile)) : 0;
+    uint8_t* ring = &ring_all[wave][0][0];
+    auto issue = [&](int k) {
+      int64_t tr = first + (int64_t)k * 4 * kTile;
+      tr = tr + kTile <= a.R ? tr : a.R - kTile;
+      const uint8_t* rp = sbase + summ_tile_base(tr) + 16 * lane;
+      LdsPtr dst = (LdsPtr)(ring + (k % kPreRing) * kRingSlot);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds((const void*)(rp + 1024 * i), dst + 1024 * i, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(scbase + tr + n), dst + 4096, 4, 0, 0);
+    };
+    if (nk > 0)
+#pragma unroll
+      for (int k = 0; k < kPreRing - 1; ++k) issue(k);
+    for (int k = 0; k < nk; ++k) {
+      issue(k + kPreRing - 1);
+      // the tile's 5 copies are older than the 5 * (kPreRing - 1) issued since
+      if (kPreRing == 3) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else if (kPreRing == 4) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+      const int64_t t0 = first + (int64_t)k * 4 * kTile;
       const int64_t r = t0 + n;
-      const int64_t rl = r < a.R ? r : a.R - 1;
-      const uint8_t* rp = sbase + summ_tile_base(rl) + 16 * lane;
-      u32x4 c0 = ldg16(rp), c1 = ldg16(rp + 1024), c2 = ldg16(rp + 2048), c3 = ldg16(rp + 3072);
-      const float sc = scbase[rl];
-      bf16x8 B[8];
-      codes_to_bf16(c0, B[0], B[1]);
-      codes_to_bf16(c1, B[2], B[3]);
-      codes_to_bf16(c2, B[4], B[5]);
-      codes_to_bf16(c3, B[6], B[7]);
+      const uint8_t* src = ring + (k % kPreRing) * kRingSlot;
+      const u32x4 c0 = *(const u32x4*)(src + 16 * lane), c1 = *(const u32x4*)(src + 1024 + 16 * lane),
+                  c2 = *(const u32x4*)(src + 2048 + 16 * lane), c3 = *(const u32x4*)(src + 3072 + 16 * lane);
+      const float sc = *(const float*)(src + 4096 + 4 * n);
+      // k-steps outer, row-sets inner: one converted pair of B operands is
+      // live at a time (the four accumulators instead of eight B operands)
+      f32x4 accs[NRS];
+#pragma unroll
+      for (int rs = 0; rs < NRS; ++rs) accs[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const u32x4 cc[4] = {c0, c1, c2, c3};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x8 B0, B1;
+        codes_to_bf16(cc[q4], B0, B1);
+#pragma unroll
+        for (int rs = 0; rs < NRS; ++rs) {
+          accs[rs] = mfma16x16x32(A[rs][2 * q4], B0, accs[rs]);
+          accs[rs] = mfma16x16x32(A[rs][2 * q4 + 1], B1, accs[rs]);
+        }
+      }
 #pragma unroll
       for (int rs = 0; rs < NRS; ++rs) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) acc = mfma16x16x32(A[rs][s], B[s], acc);
+        // output rows 4kb..4kb+3 of row-set rs belong to query 4rs + kb
+        const f32x4 acc = accs[rs];
+        const int qj = cq[rs] >= 0 ? q0 + 4 * rs + kb : -1;
+        const int64_t cj = cq[rs];
         uint32_t key = 0;
-        if (qidx[rs] >= 0 && r < cq[rs]) {
-          float sv = zq[rs][0] * fmaxf(acc[0], 0.0f);
-          sv = fmaf(zq[rs][1], fmaxf(acc[1], 0.0f), sv);
-          sv = fmaf(zq[rs][2], fmaxf(acc[2], 0.0f), sv);
-          sv = fmaf(zq[rs][3], fmaxf(acc[3], 0.0f), sv);
+        if (qj >= 0 && r < cj) {
+          const f32x4 zz = zq[rs];
+          float sv = zz[0] * fmaxf(acc[0], 0.0f);
+          sv = fmaf(zz[1], fmaxf(acc[1], 0.0f), sv);
+          sv = fmaf(zz[2], fmaxf(acc[2], 0.0f), sv);
+          sv = fmaf(zz[3], fmaxf(acc[3], 0.0f), sv);
           sv *= sc;
-          const int64_t pq = (int64_t)qidx[rs] * kGroups + g;
+          const int64_t pq = (int64_t)qj * kGroups + g;
           a.scores[pq * a.ws_stride + r] = sv;
           if (a.scores_out) a.scores_out[pq * a.max_regions + r] = sv;
           key = score_key(sv);
@@ -389,11 +441,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           key = max(key, (uint32_t)__shfl_xor((int)key, 4));
           key = max(key, (uint32_t)__shfl_xor((int)key, 2));
           key = max(key, (uint32_t)__shfl_xor((int)key, 1));
-          if (n == 0 && qidx[rs] >= 0 && t0 < cq[rs])
-            a.tilemax[((int64_t)qidx[rs] * kGroups + g) * a.tm_stride + t0 / kTile] = key;
+          if (n == 0 && qj >= 0 && t0 < cj)
+            a.tilemax[((int64_t)qj * kGroups + g) * a.tm_stride + t0 / kTile] = key;
         }
       }
     }
+    // the two copies issued past the last tile must land before the ring is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
 
