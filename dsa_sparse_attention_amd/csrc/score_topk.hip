@@ -645,41 +645,6 @@ __device__ __forceinline__ bool select_trivial(int64_t c, uint32_t need, int32_t
   return false;
 }
 
-#ifndef DSA_PRE_SELECT_NT
-#define DSA_PRE_SELECT_NT 256
-#endif
-constexpr int kPreNT = DSA_PRE_SELECT_NT;  // threads of the prefill selection block (<= 8192 regions)
-
-// Prefill: one block per (query, group); the problem's scores (c <= NT*KPT)
-// are loaded straight into registers in index order.
-template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void k_select_pre(SelectArgs a) {
-  const int64_t pq = blockIdx.x;
-  const int qi = (int)(pq / kGroups);
-  __shared__ SelectSmem<NT, KPT> sm;
-  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
-  const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
-  int32_t* sel = a.sel + pq * a.topk;
-  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, NT)) return;
-  const float* sc = a.scores + pq * a.ws_stride;
-  // unconditional loads (clamped index) so that all of them are in flight at once
-  float v[KPT];
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    const int64_t r = (int64_t)e * NT + threadIdx.x;
-    v[e] = sc[r < c ? r : 0];
-  }
-  uint32_t key[KPT];
-  int32_t idx[KPT];
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    const int64_t r = (int64_t)e * NT + threadIdx.x;
-    key[e] = r < c ? score_key(v[e]) : 0u;
-    idx[e] = (int32_t)r;
-  }
-  select_strided<NT, KPT>(key, idx, need, c, sel, a.nsel + pq, a.topk, sm);
-}
-
 // Problems beyond the register capacity of the tile selection: exact
 // selection by radix narrowing over the scores in global memory (12-bit digits) until the
 // candidates fit in LDS, 8-bit digits in LDS, bitonic sort of the result.
@@ -1242,6 +1207,222 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   if (pos < need) sel[pos] = sm.ci[tid];
 }
 
+
+#ifndef DSA_PRE_SELECT_NT
+#define DSA_PRE_SELECT_NT 256
+#endif
+constexpr int kPreNT = DSA_PRE_SELECT_NT;  // threads of the prefill selection block (<= 8192 regions)
+constexpr int kPreFin = kPreNT;            // bin sizes the prefill selection finishes by ranking
+
+template <int NT, int KPT>
+struct alignas(16) PreSmem {
+  SelectSmem<NT, KPT> s;           // bisection fallback and tie-aware output
+  uint32_t wred[NT / 64];          // per-wave maxima, then per-wave totals
+  uint32_t res[4];
+  uint32_t n_in;
+  alignas(16) uint32_t tab[KPT * (NT / 64)];  // output offsets, [wave][entry]
+  alignas(16) uint32_t hist[kHistBins];       // value histogram
+  uint32_t kin[kPreFin];           // keys of the boundary bin, any order
+  int32_t out[kMaxTopk];           // the selection, staged for a coalesced store
+};
+
+// Largest value over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+
+// Bin of a key in the prefill histogram: keys of positive scores map
+// linearly in score value onto 0..4095 (inv = 4096 / largest score), every
+// other key to bin 0.  The map never decreases as the key grows, so the bins
+// split the ranking into contiguous runs.
+__device__ __forceinline__ uint32_t value_bin(uint32_t key, float inv) {
+  const float s = __uint_as_float(key & 0x7FFFFFFFu);
+  return key > 0x80000000u ? (uint32_t)fminf(s * inv, (float)(kHistBins - 1)) : 0u;
+}
+
+// Prefill: one block per (query, group); the problem's scores (c <= NT*KPT)
+// are loaded straight into registers in index order.
+//  1. A histogram of the scores on a linear scale up to the block's largest
+//     score gives the bin holding the need-th largest key and the count of
+//     keys in higher bins.  Scores are spread over many bins, so the LDS
+//     increments rarely collide and the boundary bin holds a handful of keys.
+//  2. The boundary bin's keys are ranked against each other, which gives the
+//     need-th largest key T.
+//  3. Keys above T are taken, keys equal to T lowest index first, and the
+//     selection is written in ascending index order.
+// A boundary bin holding more than kPreFin keys (many equal scores) falls
+// back to bisection on the keys in registers.
+static_assert(kHistBins == kPreNT * 16, "each thread owns 16 histogram bins");
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void k_select_pre(SelectArgs a) {
+  constexpr int NW = NT / 64;
+  const int64_t pq = blockIdx.x;
+  const int qi = (int)(pq / kGroups);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ PreSmem<NT, KPT> sm;
+  const int64_t c64 = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
+  const uint32_t need = (uint32_t)((c64 < (int64_t)(a.topk - 1)) ? c64 : (int64_t)(a.topk - 1));
+  int32_t* sel = a.sel + pq * a.topk;
+  if (select_trivial(c64, need, sel, a.nsel + pq, a.topk, NT)) return;
+  const int c = (int)c64;             // candidates 0..c-1, c < NT*KPT
+  const int ne = (c + NT - 1) / NT;   // entries holding a candidate in some thread
+  const float* sc = a.scores + pq * a.ws_stride;
+  // unconditional loads (clamped index) so that all of them are in flight at once
+  float v[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) v[e] = sc[min(e * NT + tid, c - 1)];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *(u32x4*)&sm.hist[16 * tid + 4 * i] = u32x4{0u, 0u, 0u, 0u};
+  if (tid == 0) {
+    sm.res[0] = 0xFFFFFFFFu;
+    sm.n_in = 0;
+  }
+  // Present keys are >= 1 (a NaN score, the lowest, gets 1) and absent
+  // entries 0, so no later step needs the entry's index to tell them apart.
+  uint32_t key[KPT], kmax = 0;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const uint32_t k = max(score_key(v[e]), 1u);  // converted unconditionally: no branch per entry
+    key[e] = k & (0u - (uint32_t)(e * NT + tid < c));
+    kmax = max(kmax, key[e]);
+  }
+  kmax = wave_max(kmax);
+  if (lane == 0) sm.wred[w] = kmax;
+  __syncthreads();
+  // 1. histogram and the bin holding the need-th largest key; absent entries
+  // of the last partly filled entry land in bin 0 and are taken out again
+#pragma unroll
+  for (int i = 0; i < NW; ++i) kmax = max(kmax, sm.wred[i]);
+  const float smax = __uint_as_float(kmax & 0x7FFFFFFFu);
+  const float inv = kmax > 0x80000000u ? (float)kHistBins / smax : 0.0f;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e)
+    if (e < ne) atomicAdd(&sm.hist[value_bin(key[e], inv)], 1u);
+  __syncthreads();
+  {
+    // thread t owns bins 4095-16t down to 4080-16t
+    uint32_t cnt[16], mine = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 h = *(const u32x4*)&sm.hist[kHistBins - 16 - 16 * tid + 4 * i];
+      cnt[15 - 4 * i] = h.x;
+      cnt[14 - 4 * i] = h.y;
+      cnt[13 - 4 * i] = h.z;
+      cnt[12 - 4 * i] = h.w;
+    }
+    if (tid == NT - 1) cnt[15] -= (uint32_t)(ne * NT - c);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mine += cnt[j];
+    const uint32_t wi = wave_incl_scan(mine);
+    if (lane == 63) sm.wred[w] = wi;
+    __syncthreads();
+    uint32_t run = wi - mine;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) run += i < w ? sm.wred[i] : 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (run < need && run + cnt[j] >= need) {
+        sm.res[0] = (uint32_t)(kHistBins - 1 - 16 * tid - j);
+        sm.res[1] = run;
+        sm.res[2] = cnt[j];
+      }
+      run += cnt[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t d = sm.res[0], above = sm.res[1], inbin = sm.res[2];
+  Boundary bd;
+  uint32_t n_eq = 0;  // keys equal to T (known on the ranking path)
+  if (d == 0xFFFFFFFFu || inbin > (uint32_t)kPreFin) {
+    bd = block_boundary<NT, KPT>(key, need, sm.s);
+  } else {
+    // 2. gather the boundary bin and rank its keys
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      if (key[e] != 0u && value_bin(key[e], inv) == d) {
+        const uint32_t slot = atomicAdd(&sm.n_in, 1u);
+        if (slot < (uint32_t)kPreFin) sm.kin[slot] = key[e];
+      }
+    }
+    __syncthreads();
+    const uint32_t n = min(sm.n_in, (uint32_t)kPreFin);
+    const uint32_t rem = need - above;  // 1 <= rem <= n
+    if ((uint32_t)tid < n) {
+      const uint32_t k = sm.kin[tid];
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t j = 0; j < n; ++j) {
+        const uint32_t o = sm.kin[j];
+        gt += o > k ? 1u : 0u;
+        ge += o >= k ? 1u : 0u;
+      }
+      if (gt < rem && rem <= ge) {  // every lane holding T writes the same values
+        sm.res[3] = k;
+        sm.res[1] = above + gt;
+        sm.res[2] = ge - gt;
+      }
+    }
+    __syncthreads();
+    bd = Boundary{sm.res[3], sm.res[1]};
+    n_eq = sm.res[2];
+  }
+  // 3. ordered output
+  for (int i = (int)need + 1 + tid; i < a.topk; i += NT) sel[i] = -1;
+  if (tid == 0) {
+    sel[need] = c;
+    a.nsel[pq] = (int32_t)need + 1;
+  }
+  if (n_eq != need - bd.above) {  // only some keys equal to T are taken (or not known)
+    int32_t idx[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) idx[e] = e * NT + tid;
+    emit_top<NT, KPT>(key, idx, bd, need, sel, sm.s);
+    return;
+  }
+  // every key >= T is taken (T >= 1, so no absent entry): one flag per
+  // entry, offsets from a scanned table of per-(entry, wave) counts; the
+  // flags are taken again after the scan rather than held in scalar registers
+  const uint32_t T = bd.T;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const uint64_t m = __ballot(key[e] >= T);
+    if (lane == 0) sm.tab[w * KPT + e] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  if (w == 0) {  // exclusive scan in index order (entry-major, then wave)
+    constexpr int n = KPT * NW, per = (n + 63) / 64;
+    uint32_t val[per], sum = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int o = lane * per + i;  // position o in index order = (entry o / NW, wave o % NW)
+      val[i] = o < n ? sm.tab[(o % NW) * KPT + o / NW] : 0u;
+      sum += val[i];
+    }
+    uint32_t run = wave_incl_scan(sum) - sum;  // each lane rewrites only the entries it read
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int o = lane * per + i;
+      if (o < n) sm.tab[(o % NW) * KPT + o / NW] = run;
+      run += val[i];
+    }
+  }
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int e = 0; e < KPT; e += 4) {
+    const u32x4 off = *(const u32x4*)&sm.tab[w * KPT + e];
+    const uint32_t o4[4] = {off.x, off.y, off.z, off.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool f = key[e + j] >= T;
+      const uint64_t m = __ballot(f);
+      if (f) sm.out[o4[j] + (uint32_t)__popcll(m & lt)] = (e + j) * NT + tid;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < (int)need; i += NT) sel[i] = sm.out[i];
+}
 
 #ifndef DSA_TILE_SELECT_NT
 #define DSA_TILE_SELECT_NT 1024

@@ -185,7 +185,7 @@ def test_decode_attention_on_oracle_selection():
         H.assert_attn(go[b], r["oracle"][b]["out"], f"seq {b}")
 
 
-def _prefill(seed, seqs, topk=512, check_every=1):
+def _prefill(seed, seqs, topk=512, check_every=1, zero_z=False):
     """seqs: list of (P0, n) -- each sequence has a prefix of P0 tokens and a chunk of n new queries.
     Queries of all sequences are interleaved to exercise mixed-sequence query blocks when len(seqs)>1."""
     B = len(seqs)
@@ -209,6 +209,8 @@ def _prefill(seed, seqs, topk=512, check_every=1):
                 qp.append(s0 + i)
     nq = len(qs)
     q, iq, z = H.dev_queries(seed, nq)
+    if zero_z:  # every score 0: selection falls to the lowest regions (tie rule)
+        z.zero_()
     sel = torch.empty(nq * G * topk, dtype=torch.int32, device="cuda")
     nsel = torch.empty(nq * G, dtype=torch.int32, device="cuda")
     scores = torch.full((nq * G * R,), float("nan"), dtype=torch.float32, device="cuda")
@@ -221,6 +223,8 @@ def _prefill(seed, seqs, topk=512, check_every=1):
     gsc = scores.cpu().numpy().reshape(nq, G, R)
     gout = H.bf16_np(out).reshape(nq, HQ, D)
     hq, hiq, hz = H.host_queries(seed, nq)
+    if zero_z:
+        hz = np.zeros_like(hz)
     host = {}
     for b, (s0, n) in enumerate(seqs):
         L = s0 + n
@@ -258,11 +262,31 @@ def _prefill(seed, seqs, topk=512, check_every=1):
         (codes, scales), Kh, Vh = host[b]
         ref = O.attend(hq[i], Kh, Vh, p, [osels[i, g, :onsel[i, g]] for g in range(G)], k=topk)
         H.assert_attn(g2[i], ref, f"query {i} on oracle selection")
+    return gsel, gnsel, qp
 
 
 def test_prefill_chunk_one_sequence():
     # prefix of 4003 tokens (partial region), 300 new queries: several 16-query blocks + a ragged one
     _prefill(0xE0, [(4003, 300)], check_every=7)
+
+
+def test_prefill_64k_chunk_sampled():
+    # the 64K prefill workload as timed: 2048 queries after a 63,488-token prefix; every 64th query
+    # is checked against the oracle
+    _prefill(0xE5, [(63488, 2048)], topk=512, check_every=64)
+
+
+@pytest.mark.parametrize("seqs", [
+    [(8000, 80)],    # ~1000 candidates, all in one digit: finished in LDS
+    [(40000, 80)],   # ~5000 candidates, all in one digit: bisection on the keys in registers
+])
+def test_prefill_all_equal_scores_take_the_lowest_regions(seqs):
+    gsel, gnsel, qp = _prefill(0xE6, seqs, topk=512, check_every=5, zero_z=True)
+    for i, p in enumerate(qp):
+        c = p // 8
+        for g in range(G):
+            want = list(range(c + 1)) if c < 512 else list(range(511)) + [c]
+            assert gsel[i, g, :gnsel[i, g]].tolist() == want
 
 
 def test_prefill_mixed_sequences_and_small_topk():
