@@ -31,16 +31,12 @@
 namespace dsa {
 
 constexpr int kScoreRange = 1024;  // regions per k_score block
-constexpr int kRingSlot = 4096 + 256;  // one summary tile in a wave's LDS ring: 4 KB of codes, then the
-                                       // scale copy (4 bytes per lane; lanes 0..15 hold the tile's scales)
-#ifndef DSA_PRE_RING
-#define DSA_PRE_RING 4
-#endif
+constexpr int kPreQ = 64;          // queries per prefill scoring block (16 per wave)
+constexpr int kPreSlot = 4096 + 4 * 256;  // one summary tile in the block's LDS ring: 4 KB of codes,
+                                          // then one scale copy per wave (lanes 0..15 hold the scales)
 #ifndef DSA_PRE_WAVES
 #define DSA_PRE_WAVES 2
 #endif
-constexpr int kPreRing = DSA_PRE_RING;  // tiles in a wave's ring: kPreRing - 1 copies ahead of use
-static_assert(kPreRing >= 3 && kPreRing <= 5, "ring depth with a wait count below");
 typedef __attribute__((address_space(3))) uint8_t* LdsPtr;
 constexpr int kTile = 16;          // regions per MFMA tile
 constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
@@ -293,47 +289,97 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
 }
 
 // Prefill scoring: 16 queries per wave as four MFMA row-sets (4 queries x
-// 4 heads each), so every summary tile loaded feeds 4 MFMAs per k-step.
-// Block = 4 waves sharing (region range of kScoreRange, group, 16-query
-// block); wave w takes tiles w, w+4, ...  Queries of one block that belong
-// to different sequences are handled one sequence at a time.  TILEMAX also
-// stores each tile's largest key (left out of the short-context variant,
-// where its registers would halve the waves per SIMD).
-template <bool TILEMAX>
+// 4 heads each), so every summary tile feeds 4 MFMAs per k-step.  Block = 4
+// waves = 64 queries sharing (region range of kScoreRange, group); the
+// block's summary tiles stream through one LDS ring (each wave copies a
+// quarter of each tile), so every tile read from L2 feeds 64 queries.
+// Queries of one block that belong to different sequences are handled one
+// sequence at a time.  TILEMAX also stores each tile's largest key; OUT
+// also writes the caller's score array.
+//
+// The copies are the DMA form of the loads (global -> LDS), issued kPreDepth
+// - 1 tiles ahead.  A wave learns that its own copies of tile k landed from
+// its count of outstanding memory operations, which complete in order: every
+// operation of the loop is issued unconditionally (stores of invalid lanes
+// go to an out-of-range buffer offset and are dropped), so the number issued
+// after tile k's copies is known exactly.  A barrier then makes all four
+// quarters visible, and also shows that every wave is done with the slot the
+// next copy overwrites.
+template <bool TILEMAX, bool OUT>
+struct PreScoreCfg {
+  static constexpr int S = 4 * (1 + (TILEMAX ? 1 : 0) + (OUT ? 1 : 0));  // stores per tile
+  static constexpr int D = S == 4 ? 8 : (S == 8 ? 6 : 4);                // ring depth
+  static constexpr int W_EARLY = 2 * (D - 2);                            // wait counts
+  static constexpr int W_FULL = 2 * (D - 2) + (D - 1) * S;
+  static_assert(W_FULL + 2 + S <= 63, "the outstanding-operation counter holds 63");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  // the immediate must be a literal: dispatch over the counts in use
+  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if constexpr (N == 40) asm volatile("s_waitcnt vmcnt(40)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else static_assert(N < 0, "add this count");
+}
+
+// Buffer view of rows [first row of the wave, +16 queries) of a [Nq][G][stride]
+// array for group g: offsets are bytes from the wave's first row; rows past
+// the last query are outside the view.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void* base, int64_t qw, int g, int64_t stride,
+                                                           int32_t nq) {
+  int64_t rows = nq - qw;
+  rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
+  const int64_t bytes = rows ? ((rows - 1) * kGroups + 1) * stride * 4 : 0;
+  char* p = (char*)base + ((qw < nq ? qw : 0) * kGroups + g) * stride * 4;
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfView = 0x80000000u;  // byte offset past every view (views stay below 2 GiB)
+
+template <bool TILEMAX, bool OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAVES, DSA_PRE_WAVES))) void k_score_pre(ScoreArgs a) {
-  constexpr int QW = 16, NRS = 4;
+  using Cfg = PreScoreCfg<TILEMAX, OUT>;
+  constexpr int NRS = 4, D = Cfg::D;
   const int g = blockIdx.y;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: buffer views in scalars
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kb = lane >> 4;
-  const int q0 = blockIdx.z * QW;
+  const int qb = blockIdx.z * kPreQ;   // the block's first query
+  const int qw = qb + 16 * wave;       // the wave's first query
   const int64_t range0 = (int64_t)blockIdx.x * kScoreRange;
-  __shared__ __attribute__((aligned(16))) uint8_t ring_all[4][kPreRing][kRingSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[D][kPreSlot];
 
-  uint32_t remaining = 0;  // bit j: query q0+j still to process
-  for (int j = 0; j < QW; ++j)
-    if (q0 + j < a.nq) remaining |= 1u << j;
+  // Query metadata, one round of loads: lane l holds query qb + l (clamped
+  // into range); bit l of `remaining` says whether it exists and is still
+  // to process.  Every wave computes the same passes.
+  const int64_t qm = (qb + lane < a.nq) ? qb + lane : a.nq - 1;
+  int32_t sq = query_seq(a.qseq, qm);
+  sq = sq < 0 ? 0 : (sq >= a.n_seqs ? a.n_seqs - 1 : sq);
+  const int32_t cqm = (int32_t)current_region(query_pos(a.qpos, a.slen, qm), a.R, a.max_regions);
+  uint64_t remaining = __ballot(qb + lane < a.nq);
+
+  const __amdgpu_buffer_rsrc_t ws_view = rows_rsrc(a.scores, qw, g, a.ws_stride, a.nq);
+  const __amdgpu_buffer_rsrc_t out_view = rows_rsrc(OUT ? (void*)a.scores_out : (void*)a.scores, qw, g,
+                                                    OUT ? a.max_regions : a.ws_stride, a.nq);
+  const __amdgpu_buffer_rsrc_t tm_view = rows_rsrc(TILEMAX ? (void*)a.tilemax : (void*)a.scores, qw, g,
+                                                   TILEMAX ? a.tm_stride : a.ws_stride, a.nq);
 
   while (remaining) {
-    const int lead = __builtin_ctz(remaining);
-    int32_t seq = query_seq(a.qseq, q0 + lead);
-    seq = seq < 0 ? 0 : (seq >= a.n_seqs ? a.n_seqs - 1 : seq);
-    uint32_t active = 0;
-    int64_t cmax = 0;
-    for (int j = 0; j < QW; ++j) {
-      if (!(remaining >> j & 1u)) continue;
-      int32_t sj = query_seq(a.qseq, q0 + j);
-      sj = sj < 0 ? 0 : (sj >= a.n_seqs ? a.n_seqs - 1 : sj);
-      if (sj == seq) {
-        active |= 1u << j;
-        const int64_t cj = current_region(query_pos(a.qpos, a.slen, q0 + j), a.R, a.max_regions);
-        cmax = cj > cmax ? cj : cmax;
-      }
-    }
+    // one pass per sequence among the block's queries
+    const int lead = __builtin_ctzll(remaining);
+    const int32_t seq = __builtin_amdgcn_readlane(sq, lead);
+    const uint64_t active = __ballot(sq == seq) & remaining;
     remaining &= ~active;
+    int32_t cm = (active >> lane & 1ull) ? cqm : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cm = max(cm, __shfl_xor(cm, o));
 
     // A operand: rows = (query, head) pairs of group g; channel permutation
-    // pi(s, kb, e) = 64*(s/2) + 16*kb + 8*(s%2) + e.
+    // pi(s, kb, e) = 64*(s/2) + 16*kb + 8*(s%2) + e.  Rows of queries outside
+    // this pass (or past the end, clamped) are loaded too and never stored.
     bf16x8 A[NRS][8];
     // epilogue data of the lane's output query in each row-set: z of the
     // group's 4 heads and the current region (-1: not in this pass)
@@ -341,66 +387,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
     int32_t cq[NRS];
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
-      const int jout = 4 * rs + kb;
-      const bool ovalid = (active >> jout & 1u);
-      zq[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
-      cq[rs] = -1;
-      if (ovalid) {
-        zq[rs] = *(const f32x4*)(a.z + (int64_t)(q0 + jout) * kIdxHeads + 4 * g);
-        cq[rs] = (int32_t)current_region(query_pos(a.qpos, a.slen, q0 + jout), a.R, a.max_regions);
-      }
+      const int jout = 16 * wave + 4 * rs + kb;
+      const int64_t qo = (qb + jout < a.nq) ? qb + jout : a.nq - 1;
+      zq[rs] = *(const f32x4*)(a.z + qo * kIdxHeads + 4 * g);
+      const int32_t cj = __shfl(cqm, jout);
+      cq[rs] = (active >> jout & 1ull) ? cj : -1;
     }
 #pragma unroll
     for (int rs = 0; rs < NRS; ++rs) {
       const int jrow = 4 * rs + (n >> 2);  // query of A row n
-      const bool rvalid = (active >> jrow & 1u);
+      const int64_t qr = (qw + jrow < a.nq) ? qw + jrow : a.nq - 1;
       const int hh = 4 * g + (n & 3);
-      const uint16_t* qp = a.iq + ((int64_t)(q0 + jrow) * kIdxHeads + hh) * kProxy + 16 * kb;
+      const uint16_t* qp = a.iq + (qr * kIdxHeads + hh) * kProxy + 16 * kb;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        u32x4 v = {0, 0, 0, 0};
-        if (rvalid) v = ld16(qp + 64 * (s >> 1) + 8 * (s & 1));
-        A[rs][s] = as_bf16x8(v);
-      }
+      for (int s = 0; s < 8; ++s) A[rs][s] = as_bf16x8(ld16(qp + 64 * (s >> 1) + 8 * (s & 1)));
     }
 
-    const int64_t rend = (range0 + kScoreRange < cmax) ? range0 + kScoreRange : cmax;
+    const int64_t rend = (range0 + kScoreRange < cm) ? range0 + kScoreRange : (int64_t)cm;
+    const int nk = rend > range0 ? (int)((rend - range0 + kTile - 1) / kTile) : 0;  // tiles of the block
     const uint8_t* sbase = a.summ + ((int64_t)seq * kGroups + g) * a.R * kProxy;
     const float* scbase = a.scale + ((int64_t)seq * kGroups + g) * a.R;
-    // This wave's tiles k = 0..nk-1 start at region first + 64k.  Each tile
-    // (4 KB of codes + its 16 scales) is copied global -> LDS by the DMA form
-    // of the loads, kPreRing - 1 tiles ahead of use, into a ring of the wave.
-    // Every copy is issued (past the end it re-reads a clamped tile), so
-    // exactly kPreRing - 1 tiles' copies (5 operations each) were issued after
-    // the tile being read, and in-order completion makes a vmcnt wait for
-    // that many leave only them outstanding.
-    const int64_t first = range0 + (int64_t)wave * kTile;
-    const int nk = first < rend ? (int)((rend - first + 4 * kTile - 1) / (4 * kTile)) : 0;
-    uint8_t* ring = &ring_all[wave][0][0];
+    // tile k = regions range0 + 16k ..; wave w copies its codes' quarter w
+    // and its own copy of the 16 scales (copies past the end re-read a
+    // clamped tile so every iteration issues the same operations)
     auto issue = [&](int k) {
-      int64_t tr = first + (int64_t)k * 4 * kTile;
+      int64_t tr = range0 + (int64_t)k * kTile;
       tr = tr + kTile <= a.R ? tr : a.R - kTile;
-      const uint8_t* rp = sbase + summ_tile_base(tr) + 16 * lane;
-      LdsPtr dst = (LdsPtr)(ring + (k % kPreRing) * kRingSlot);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds((const void*)(rp + 1024 * i), dst + 1024 * i, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(scbase + tr + n), dst + 4096, 4, 0, 0);
+      LdsPtr dst = (LdsPtr)&ring[k % D][0];
+      __builtin_amdgcn_global_load_lds((const void*)(sbase + summ_tile_base(tr) + 1024 * wave + 16 * lane),
+                                       dst + 1024 * wave, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(scbase + tr + n), dst + 4096 + 256 * wave, 4, 0, 0);
     };
     if (nk > 0)
 #pragma unroll
-      for (int k = 0; k < kPreRing - 1; ++k) issue(k);
+      for (int k = 0; k < D - 1; ++k) issue(k);
     for (int k = 0; k < nk; ++k) {
-      issue(k + kPreRing - 1);
-      // the tile's 5 copies are older than the 5 * (kPreRing - 1) issued since
-      if (kPreRing == 3) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else if (kPreRing == 4) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-      const int64_t t0 = first + (int64_t)k * 4 * kTile;
-      const int64_t r = t0 + n;
-      const uint8_t* src = ring + (k % kPreRing) * kRingSlot;
+      if (k < D - 1) wait_vm<Cfg::W_EARLY>();
+      else wait_vm<Cfg::W_FULL>();
+      __syncthreads();
+      issue(k + D - 1);
+      const int t0 = (int)range0 + k * kTile;  // region indices fit 32 bits (max_regions is int32)
+      const int r = t0 + n;
+      const uint8_t* src = &ring[k % D][0];
       const u32x4 c0 = *(const u32x4*)(src + 16 * lane), c1 = *(const u32x4*)(src + 1024 + 16 * lane),
                   c2 = *(const u32x4*)(src + 2048 + 16 * lane), c3 = *(const u32x4*)(src + 3072 + 16 * lane);
-      const float sc = *(const float*)(src + 4096 + 4 * n);
+      const float sc = *(const float*)(src + 4096 + 256 * wave + 4 * n);
       // k-steps outer, row-sets inner: one converted pair of B operands is
       // live at a time (the four accumulators instead of eight B operands)
       f32x4 accs[NRS];
@@ -419,35 +450,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
       }
 #pragma unroll
       for (int rs = 0; rs < NRS; ++rs) {
-        // output rows 4kb..4kb+3 of row-set rs belong to query 4rs + kb
+        // output rows 4kb..4kb+3 of row-set rs belong to query qw + 4rs + kb
         const f32x4 acc = accs[rs];
-        const int qj = cq[rs] >= 0 ? q0 + 4 * rs + kb : -1;
-        const int64_t cj = cq[rs];
-        uint32_t key = 0;
-        if (qj >= 0 && r < cj) {
-          const f32x4 zz = zq[rs];
-          float sv = zz[0] * fmaxf(acc[0], 0.0f);
-          sv = fmaf(zz[1], fmaxf(acc[1], 0.0f), sv);
-          sv = fmaf(zz[2], fmaxf(acc[2], 0.0f), sv);
-          sv = fmaf(zz[3], fmaxf(acc[3], 0.0f), sv);
-          sv *= sc;
-          const int64_t pq = (int64_t)qj * kGroups + g;
-          a.scores[pq * a.ws_stride + r] = sv;
-          if (a.scores_out) a.scores_out[pq * a.max_regions + r] = sv;
-          key = score_key(sv);
+        const f32x4 zz = zq[rs];
+        float sv = zz[0] * fmaxf(acc[0], 0.0f);
+        sv = fmaf(zz[1], fmaxf(acc[1], 0.0f), sv);
+        sv = fmaf(zz[2], fmaxf(acc[2], 0.0f), sv);
+        sv = fmaf(zz[3], fmaxf(acc[3], 0.0f), sv);
+        sv *= sc;
+        const bool ok = r < cq[rs];  // cq = -1 outside the pass
+        const uint32_t row = (uint32_t)((4 * rs + kb) * kGroups);
+        const uint32_t o_ws = ok ? (row * (uint32_t)a.ws_stride + (uint32_t)r) * 4u : kOutOfView;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), ws_view, o_ws, 0, 0);
+        if (OUT) {
+          const uint32_t o_out = ok ? (row * (uint32_t)a.max_regions + (uint32_t)r) * 4u : kOutOfView;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), out_view, o_out, 0, 0);
         }
         if (TILEMAX) {  // lanes 16kb..16kb+15 hold one query's tile
+          uint32_t key = ok ? score_key(sv) : 0u;
           key = max(key, (uint32_t)__shfl_xor((int)key, 8));
           key = max(key, (uint32_t)__shfl_xor((int)key, 4));
           key = max(key, (uint32_t)__shfl_xor((int)key, 2));
           key = max(key, (uint32_t)__shfl_xor((int)key, 1));
-          if (n == 0 && qj >= 0 && t0 < cj)
-            a.tilemax[((int64_t)qj * kGroups + g) * a.tm_stride + t0 / kTile] = key;
+          const bool tok = n == 0 && t0 < cq[rs];
+          const uint32_t o_tm = tok ? (row * (uint32_t)a.tm_stride + (uint32_t)(t0 / kTile)) * 4u : kOutOfView;
+          __builtin_amdgcn_raw_buffer_store_b32(key, tm_view, o_tm, 0, 0);
         }
       }
     }
-    // the two copies issued past the last tile must land before the ring is reused
+    // the copies issued past the last tile must land before the ring is reused
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 }
 
@@ -1524,11 +1557,12 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   } else {
     ProfScope prof_("k_score_prefill", s);
     const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
-    const dim3 grid(ranges, kGroups, (n_queries + 15) / 16);
-    if (tiled_select(max_regions))
-      hipLaunchKernelGGL(k_score_pre<true>, grid, dim3(256), 0, s, sa);
-    else
-      hipLaunchKernelGGL(k_score_pre<false>, grid, dim3(256), 0, s, sa);
+    const dim3 grid(ranges, kGroups, (n_queries + kPreQ - 1) / kPreQ);
+    const bool tm = tiled_select(max_regions), out = scores_out != nullptr;
+    if (tm && out) hipLaunchKernelGGL((k_score_pre<true, true>), grid, dim3(256), 0, s, sa);
+    else if (tm) hipLaunchKernelGGL((k_score_pre<true, false>), grid, dim3(256), 0, s, sa);
+    else if (out) hipLaunchKernelGGL((k_score_pre<false, true>), grid, dim3(256), 0, s, sa);
+    else hipLaunchKernelGGL((k_score_pre<false, false>), grid, dim3(256), 0, s, sa);
   }
   dsa_status st = check_launch("dsa_score_topk: score");
   if (st != DSA_OK) return st;

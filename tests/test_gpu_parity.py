@@ -215,6 +215,15 @@ def _prefill(seed, seqs, topk=512, check_every=1, zero_z=False):
     nsel = torch.empty(nq * G, dtype=torch.int32, device="cuda")
     scores = torch.full((nq * G * R,), float("nan"), dtype=torch.float32, device="cuda")
     dsa.dsa_score_topk(geom, iq, z, H.i32(qs), H.i32(qp), B, summ, scale, tcap, R, sel, nsel, scores_out=scores)
+    # the same call without the caller's score array takes the other scoring variant
+    sel_b = torch.empty_like(sel)
+    nsel_b = torch.empty_like(nsel)
+    dsa.dsa_score_topk(geom, iq, z, H.i32(qs), H.i32(qp), B, summ, scale, tcap, R, sel_b, nsel_b)
+    na, nb = nsel.cpu().numpy(), nsel_b.cpu().numpy()
+    assert np.array_equal(na, nb)
+    sa, sb = sel.cpu().numpy().reshape(-1, topk), sel_b.cpu().numpy().reshape(-1, topk)
+    live = np.arange(topk)[None, :] < na[:, None]
+    assert np.array_equal(np.where(live, sa, -1), np.where(live, sb, -1))
     out = torch.empty(nq * HQ * D, dtype=H.BF16, device="cuda")
     dsa.dsa_sparse_gqa_prefill(geom, q, H.i32(qs), H.i32(qp), B, K, V, tcap, sel, nsel, out)
     torch.cuda.synchronize()
