@@ -204,13 +204,14 @@ def setup_prefill(cfg):
     nsel = torch.empty(n * G, dtype=torch.int32, device="cuda")
     out = torch.empty(n * HQ * D, dtype=torch.bfloat16, device="cuda")
     ws1 = dsa.workspace(dsa.dsa_score_topk_workspace_size(geom, n, R))
+    ws3 = dsa.workspace(dsa.dsa_sparse_gqa_prefill_workspace_size(geom, n))
     L = dsa.load()
     p = Calls.p
     gp = ctypes.byref(geom)
     a_comp = (gp, 1, p(ik), tcap, p(rb), p(re_), span, p(summ), p(scale))
     a_score = (gp, n, p(iq), p(z), p(qseq), p(qpos), 1, p(summ), p(scale), tcap, R, p(sel), p(nsel), None,
                p(ws1), ws1.numel())
-    a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, p(K), p(V), tcap, p(sel), p(nsel), p(out))
+    a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, p(K), p(V), tcap, p(sel), p(nsel), p(out), p(ws3), ws3.numel())
 
     def step(st):
         rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
@@ -218,7 +219,7 @@ def setup_prefill(cfg):
         if rc:
             raise RuntimeError(f"prefill step failed: {rc} {L.dsa_last_error().decode()}")
 
-    keep = (ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, sel, nsel, out, ws1, geom)
+    keep = (ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, sel, nsel, out, ws1, ws3, geom)
     return step, keep
 
 
@@ -426,7 +427,7 @@ def main():
     # ---- prefill at 64K
     if not args.no_prefill:
         step, keep = setup_prefill(PREFILL)
-        kp = ["k_compress", "k_score_prefill", "k_select", "k_sgqa_prefill"]
+        kp = ["k_compress", "k_score_prefill", "k_select", "k_sgqa_prefill", "k_sgqa_merge"]
         psteps = max(3, args.steps // 3)
         psecs, peager, pst = timed(step, psteps, max(1, args.warmup // 2), kp, graph=args.graph)
         del keep

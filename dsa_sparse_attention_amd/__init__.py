@@ -25,7 +25,8 @@ REGION, PROXY, GROUPS, IDX_HEADS, Q_HEADS, HEAD_DIM, MAX_TOPK, WINDOW = 8, 256, 
 ENTRY_POINTS = [
     "dsa_geometry_default", "dsa_status_string", "dsa_last_error", "dsa_cache_write",
     "dsa_compress_regions", "dsa_score_topk_workspace_size", "dsa_score_topk",
-    "dsa_sparse_gqa_workspace_size", "dsa_sparse_gqa_decode", "dsa_sparse_gqa_prefill",
+    "dsa_sparse_gqa_workspace_size", "dsa_sparse_gqa_decode",
+    "dsa_sparse_gqa_prefill_workspace_size", "dsa_sparse_gqa_prefill",
     "dsa_decode_step_workspace_size", "dsa_decode_step",
     "swa_attention_workspace_size", "swa_attention", "swa_ring_append",
     "dsa_profile_enable", "dsa_profile_kernel_stats",
@@ -70,7 +71,9 @@ def load() -> ctypes.CDLL:
     L.dsa_sparse_gqa_workspace_size.argtypes = [G, i32]
     L.dsa_sparse_gqa_workspace_size.restype = sz
     L.dsa_sparse_gqa_decode.argtypes = [G, i32, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
-    L.dsa_sparse_gqa_prefill.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp]
+    L.dsa_sparse_gqa_prefill_workspace_size.argtypes = [G, i32]
+    L.dsa_sparse_gqa_prefill_workspace_size.restype = sz
+    L.dsa_sparse_gqa_prefill.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     L.dsa_decode_step_workspace_size.argtypes = [G, i32, i32]
     L.dsa_decode_step_workspace_size.restype = sz
     L.dsa_decode_step.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
@@ -260,7 +263,12 @@ def dsa_decode_step(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_le
                                   workspace.numel(), _stream(stream)))
 
 
-def dsa_sparse_gqa_prefill(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap, sel, n_sel, out, stream=None):
+def dsa_sparse_gqa_prefill_workspace_size(geom, n_queries) -> int:
+    return int(load().dsa_sparse_gqa_prefill_workspace_size(ctypes.byref(geom), n_queries))
+
+
+def dsa_sparse_gqa_prefill(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap, sel, n_sel, out, workspace=None,
+                           stream=None):
     nq = q_seq.numel()
     for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
         _dt(t, torch.bfloat16, nm)
@@ -272,9 +280,11 @@ def dsa_sparse_gqa_prefill(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap
     _numel_at_least(v_cache, n_seqs * GROUPS * tcap * HEAD_DIM, "v_cache")
     _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
     _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_prefill_workspace_size(geom, nq), q.device)
     _check(load().dsa_sparse_gqa_prefill(ctypes.byref(geom), nq, _ptr(q), _ptr(q_seq), _ptr(q_pos), n_seqs,
                                          _ptr(k_cache), _ptr(v_cache), tcap, _ptr(sel), _ptr(n_sel), _ptr(out),
-                                         _stream(stream)))
+                                         _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def swa_attention_workspace_size(geom, window, n_seqs, max_new_per_seq) -> int:

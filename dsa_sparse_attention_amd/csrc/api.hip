@@ -57,8 +57,10 @@ static hipEvent_t prof_event() {
     g_prof_pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence on record, which would write back and
+  // invalidate the caches between the kernels being timed
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

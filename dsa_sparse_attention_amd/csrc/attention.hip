@@ -161,21 +161,17 @@ __device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], co
   core_compute(st, qb, c, scale_log2);
 }
 
-// A run of chunks with the next chunk's loads in flight while the current
-// one computes.  region_of(e, lane) gives the Region for list entry e as seen
-// by this lane; entries >= n are invalid.
-#ifndef DSA_ATTN_PIPELINE
-#define DSA_ATTN_PIPELINE 2
-#endif
-#ifndef DSA_ATTN_WAVES
-#define DSA_ATTN_WAVES 1
-#endif
-template <class RegionOf>
+// A run of chunks.  region_of(e, lane) gives the Region for list entry e as
+// seen by this lane; entries >= n are invalid.  DEPTH 0: one chunk in
+// registers (for kernels running several waves per SIMD, which overlap each
+// other's loads); DEPTH 1 and 2: one and two chunks' loads in flight while a
+// chunk computes (one wave per SIMD).
+template <int DEPTH, class RegionOf>
 __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int64_t n, const RegionOf& region_of,
                                          float scale_log2) {
   const int lane = threadIdx.x & 63, nn = lane & 15, kb = lane >> 4;
   if (n <= 0) return;
-  if (!DSA_ATTN_PIPELINE) {
+  if constexpr (DEPTH == 0) {
     // one chunk in registers per wave; several waves per SIMD overlap the loads
     for (int64_t e0 = 0; e0 < n; e0 += 4) core_chunk(st, qb, region_of(e0 + (nn >> 2)), region_of(e0 + kb), scale_log2);
     return;
@@ -183,7 +179,7 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
   // The prefetch is issued unconditionally (past the end it reads the dummy
   // region of an invalid entry), so the wait before each compute only covers
   // the chunk being used and not the ones in flight behind it.
-#if DSA_ATTN_PIPELINE >= 2
+  if constexpr (DEPTH >= 2) {
   // three chunks in registers: two in flight while one computes
   ChunkRegs b0, b1, b2;
   core_load(b0, region_of(nn >> 2), region_of(kb));
@@ -198,7 +194,7 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
     core_load(b1, region_of(e0 + 16 + (nn >> 2)), region_of(e0 + 16 + kb));
     core_compute(st, qb, b2, scale_log2);
   }
-#else
+  } else {
   ChunkRegs b0, b1;
   core_load(b0, region_of(nn >> 2), region_of(kb));
   for (int64_t e0 = 0; e0 < n; e0 += 8) {
@@ -208,7 +204,7 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
     core_load(b0, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
     core_compute(st, qb, b1, scale_log2);
   }
-#endif
+  }
 }
 
 // Total softmax denominator of the lane's head (sum over the 4 kb lanes).
@@ -268,13 +264,13 @@ struct DecodeArgs {
   const int32_t* seq_len;
   const int32_t* sel;
   const int32_t* nsel;
-  float* part;  // [B][G][nsplit][16][2 + 192]
+  float* part;  // [B][G][nsplit][16][kPartStride]
   int64_t tcap;
   int32_t topk, nsplit;
   float scale_log2;
 };
 
-constexpr int kPartStride = 2 + kHeadDim;  // per head: m, l, o[192]
+constexpr int kPartStride = 4 + kHeadDim;  // per head: m, l, 2 unused, o[192] (16-byte aligned)
 
 constexpr int kORow = kHeadDim + 4;  // padded LDS row of one head's partial O
 
@@ -331,7 +327,7 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
         lsum += f * sm_l[w][h];
       }
     }
-    part[h * kPartStride + 2 + d] = acc;
+    part[h * kPartStride + 4 + d] = acc;
     if (d == 0) {
       part[h * kPartStride] = M;
       part[h * kPartStride + 1] = lsum;
@@ -339,14 +335,15 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   }
 }
 
-// One block per (head, group, sequence); thread d owns output channel d.
-// Split weights exp2(m_s - M) are formed once in LDS by the first wave
-// (nsplit <= 64).
+// One block per (head, group, query): block index h + 16 (g + G b); thread d
+// owns output channel d.  Split weights exp2(m_s - M) are formed once in LDS
+// by the first wave (nsplit <= 64).
 template <int NS>
 __global__ __launch_bounds__(kHeadDim) void k_sgqa_merge(const float* __restrict__ part,
                                                          uint16_t* __restrict__ out, int32_t nsplit) {
   static_assert(NS <= 64, "one wave forms the split weights");
-  const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int h = blockIdx.x % 16, g = (blockIdx.x / 16) % kGroups, d = threadIdx.x;
+  const int64_t b = blockIdx.x / (16 * kGroups);
   const int64_t sg = (int64_t)b * kGroups + g;
   const float* pp = part + sg * nsplit * 16 * kPartStride + h * kPartStride;
   __shared__ float w[64];
@@ -354,7 +351,7 @@ __global__ __launch_bounds__(kHeadDim) void k_sgqa_merge(const float* __restrict
   // this thread's partial O of every split, loaded up front (clamped split)
   float o[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) o[s] = pp[(int64_t)(s < nsplit ? s : 0) * 16 * kPartStride + 2 + d];
+  for (int s = 0; s < NS; ++s) o[s] = pp[(int64_t)(s < nsplit ? s : 0) * 16 * kPartStride + 4 + d];
   if (d < 64) {
     const int sd = d < nsplit ? d : 0;
     const float m0 = pp[(int64_t)sd * 16 * kPartStride], l0 = pp[(int64_t)sd * 16 * kPartStride + 1];
@@ -373,12 +370,23 @@ __global__ __launch_bounds__(kHeadDim) void k_sgqa_merge(const float* __restrict
   float acc = 0.0f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) acc += (s < nsplit ? w[s] : 0.0f) * o[s];
-  out[((int64_t)b * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + d] = f32_to_bf16(acc * inv_l);
+  out[(b * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + d] = f32_to_bf16(acc * inv_l);
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: one wave per (query, group) over its whole selection.
+// Prefill: the candidate regions are cut into kPreSplits ranges, and one wave
+// takes the entries of one (query, group)'s selection that fall in one range;
+// k_sgqa_merge combines the ranges' partial results.  Blocks of one range
+// are kPreSplits apart in launch order, and the GPU hands consecutive blocks
+// to its 8 L2 slices (XCDs) in turn, so each slice only ever reads the K/V
+// of one range: an eighth of a group's cache instead of all of it, which
+// mostly stays in that slice's L2.
 // ---------------------------------------------------------------------------
+#ifndef DSA_PRE_SPLITS
+#define DSA_PRE_SPLITS 8
+#endif
+constexpr int kPreSplits = DSA_PRE_SPLITS;
+
 struct PrefillArgs {
   const uint16_t* q;
   const int32_t* qseq;
@@ -387,22 +395,24 @@ struct PrefillArgs {
   const uint16_t* v;
   const int32_t* sel;
   const int32_t* nsel;
-  uint16_t* out;
+  uint16_t* part_o;  // [Nq][G][kPreSplits][16][D] bf16, unnormalised O
+  float* part_ml;    // [Nq][G][kPreSplits][16][2] fp32, (max, sum)
   int64_t tcap;
-  int32_t nq, n_seqs, topk;
+  int32_t nq, n_seqs, topk, rsplit;  // rsplit: regions per range
   float scale_log2;
 };
 
-// Block = 4 waves = 4 consecutive queries of one KV group; blocks are ordered
-// group-major, so at any time the GPU works through one group's K/V (a
-// quarter of the cache), which keeps the gathered regions cache-resident.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES, DSA_ATTN_WAVES)))
-void k_sgqa_prefill(PrefillArgs a) {
+// Block = 4 waves = 4 consecutive queries of one KV group and one region
+// range; block index = range + kPreSplits * (query block + nqb * group), so
+// the GPU works through one group's K/V at a time.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sgqa_prefill(PrefillArgs a) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int nqb = (a.nq + 3) / 4;
-  const int g = blockIdx.x / nqb;
-  const int64_t qi = (int64_t)(blockIdx.x % nqb) * 4 + wave;
+  const int split = blockIdx.x % kPreSplits;
+  const int rest = blockIdx.x / kPreSplits;
+  const int g = rest / nqb;
+  const int64_t qi = (int64_t)(rest % nqb) * 4 + wave;
   __shared__ int32_t ids[4][kMaxTopk];
   const bool live = qi < a.nq;
   int32_t s = live ? a.qseq[qi] : 0;
@@ -415,8 +425,26 @@ void k_sgqa_prefill(PrefillArgs a) {
   const int64_t pg = qi * kGroups + g;
   int32_t cnt = live ? a.nsel[pg] : 0;
   cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
-  const int32_t* lst = a.sel + pg * a.topk;
-  for (int i = lane; i < cnt; i += 64) ids[wave][i] = lst[i];  // wave-private slice
+  // this range's entries of the list, in list order (any order and repeats
+  // are kept as they are; ids outside every range are dropped, as they are
+  // outside [0, p/8] and would be ignored anyway)
+  const int32_t* lst = a.sel + (live ? pg : 0) * a.topk;
+  const int32_t r0 = split * a.rsplit, r1 = r0 + a.rsplit;
+  int32_t mine[kMaxTopk / 64];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk / 64; ++j) {
+    const int i = 64 * j + lane;
+    mine[j] = lst[i < cnt ? i : 0];
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int32_t n = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxTopk / 64; ++j) {
+    const bool in = 64 * j + lane < cnt && mine[j] >= r0 && mine[j] < r1;
+    const uint64_t m = __ballot(in);
+    if (in) ids[wave][n + __popcll(m & lt)] = mine[j];
+    n += __popcll(m);
+  }
   __syncthreads();
   if (!live) return;
 
@@ -426,10 +454,70 @@ void k_sgqa_prefill(PrefillArgs a) {
   core_init(st);
   const int32_t* my = ids[wave];
   auto region_of = [&](int64_t e) -> Region {
-    return dsa_region(kbase, vbase, e < cnt ? my[e] : -1, p);
+    return dsa_region(kbase, vbase, e < n ? my[e] : -1, p);
   };
-  core_run(st, qb, cnt, region_of, a.scale_log2);
-  core_store(st, a.out, qi, g);
+  core_run<0>(st, qb, n, region_of, a.scale_log2);
+  // partial (max, sum, unnormalised O^T in bf16) of this range; an empty
+  // range leaves (-inf, 0, 0), which the merge weighs 0
+  const int hn = lane & 15, kb = lane >> 4;
+  const int64_t pr = ((pg * kPreSplits) + split) * 16 + hn;  // partial row of head hn
+  const float l = core_total_l(st);
+  if (kb == 0) *(float2*)&a.part_ml[2 * pr] = make_float2(st.m, l);
+  uint16_t* po = a.part_o + pr * kHeadDim + 4 * kb;
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) {
+    uint2 w;
+    w.x = pack_bf16x2(st.o[nt][0], st.o[nt][1]);
+    w.y = pack_bf16x2(st.o[nt][2], st.o[nt][3]);
+    *(uint2*)(po + 16 * nt) = w;
+  }
+}
+
+// Prefill merge: block = (query, group), thread t = head t/16, channels
+// 12(t%16) .. +11 of that head, over the kPreSplits partials.
+__global__ __launch_bounds__(256) void k_sgqa_merge_pre(const uint16_t* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        uint16_t* __restrict__ out) {
+  const int64_t pg = blockIdx.x;  // query * G + group
+  const int h = threadIdx.x >> 4, c0 = 12 * (threadIdx.x & 15);
+  float2 ml[kPreSplits];
+  uint2 o[kPreSplits][3];
+#pragma unroll
+  for (int sp = 0; sp < kPreSplits; ++sp) {
+    const int64_t pr = (pg * kPreSplits + sp) * 16 + h;
+    ml[sp] = *(const float2*)&part_ml[2 * pr];
+    const uint16_t* po = part_o + pr * kHeadDim + c0;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) o[sp][j] = *(const uint2*)(po + 4 * j);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kPreSplits; ++sp) M = fmaxf(M, ml[sp].x);
+  float acc[12], L = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int sp = 0; sp < kPreSplits; ++sp) {
+    const float f = (ml[sp].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml[sp].x - M);
+    L += f * ml[sp].y;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      acc[4 * j + 0] += f * bf16_lo(o[sp][j].x);
+      acc[4 * j + 1] += f * bf16_hi(o[sp][j].x);
+      acc[4 * j + 2] += f * bf16_lo(o[sp][j].y);
+      acc[4 * j + 3] += f * bf16_hi(o[sp][j].y);
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const int64_t q = pg / kGroups, g = pg % kGroups;
+  uint16_t* op = out + (q * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + c0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    uint2 w;
+    w.x = pack_bf16x2(acc[4 * j] * inv, acc[4 * j + 1] * inv);
+    w.y = pack_bf16x2(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+    *(uint2*)(op + 4 * j) = w;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -540,7 +628,7 @@ __global__ __launch_bounds__(256) void k_swa_attend(SwaArgs a) {
     rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
     return rg;
   };
-  core_run(st, qb, nreg, region_of, a.scale_log2);
+  core_run<2>(st, qb, nreg, region_of, a.scale_log2);
   core_store(st, a.out, row, g);
 }
 
@@ -564,6 +652,7 @@ __global__ __launch_bounds__(256) void k_ring_append(SwaArgs a, uint16_t* k_ring
   }
 }
 
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static int32_t nsplit_of(int32_t topk) { return (topk + kSplitRegions - 1) / kSplitRegions; }
 static int32_t nstage_of(int32_t max_new) { return (max_new + kRegion - 1) / kRegion + 1; }
 
@@ -607,35 +696,60 @@ extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t ba
   if (st != DSA_OK) return st;
   {
     ProfScope prof_("k_sgqa_merge", s);
-    hipLaunchKernelGGL(k_sgqa_merge<kMaxTopk / kSplitRegions>, dim3(16, kGroups, batch), dim3(kHeadDim), 0, s,
-                       (const float*)workspace, out, a.nsplit);
+    hipLaunchKernelGGL(k_sgqa_merge<kMaxTopk / kSplitRegions>, dim3((unsigned)(16 * kGroups * batch)),
+                       dim3(kHeadDim), 0, s, (const float*)workspace, out, a.nsplit);
   }
   return check_launch("dsa_sparse_gqa_decode: merge");
+}
+
+extern "C" size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries) {
+  (void)geom;
+  if (n_queries <= 0) return 256;
+  const size_t rows = (size_t)n_queries * kGroups * kPreSplits * 16;
+  return align256(rows * kHeadDim * sizeof(uint16_t)) + rows * 2 * sizeof(float) + 256;
 }
 
 extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
                                              const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
                                              const uint16_t* k_cache, const uint16_t* v_cache,
                                              int64_t tcap, const int32_t* sel, const int32_t* n_sel,
-                                             uint16_t* out, void* stream) {
+                                             uint16_t* out, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
   if (n_queries < 0 || n_seqs < 0 || tcap <= 0 || tcap % kTcapAlign)
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: bad sizes (tcap must be a positive multiple of 128)");
   if (n_queries == 0) return DSA_OK;
   if (n_seqs == 0) return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: n_seqs must be positive");
-  if (!q || !q_seq || !q_pos || !k_cache || !v_cache || !sel || !n_sel || !out)
+  if (!q || !q_seq || !q_pos || !k_cache || !v_cache || !sel || !n_sel || !out || !workspace)
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: NULL pointer");
+  if ((size_t)workspace & 255)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: workspace must be 256-byte aligned");
+  if (workspace_bytes < dsa_sparse_gqa_prefill_workspace_size(geom, n_queries))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_sparse_gqa_prefill: workspace too small");
+  if (n_queries > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_gqa_prefill: more than 2^24 queries");
   PrefillArgs a;
   a.q = q; a.qseq = q_seq; a.qpos = q_pos; a.k = k_cache; a.v = v_cache; a.sel = sel; a.nsel = n_sel;
-  a.out = out; a.tcap = tcap; a.nq = n_queries; a.n_seqs = n_seqs; a.topk = geom->topk;
+  const size_t rows = (size_t)n_queries * kGroups * kPreSplits * 16;
+  a.part_o = (uint16_t*)workspace;
+  a.part_ml = (float*)((char*)workspace + align256(rows * kHeadDim * sizeof(uint16_t)));
+  a.tcap = tcap; a.nq = n_queries; a.n_seqs = n_seqs; a.topk = geom->topk;
+  a.rsplit = (int32_t)((tcap / kRegion + kPreSplits - 1) / kPreSplits);
   a.scale_log2 = geom->softmax_scale * kLog2e;
+  hipStream_t s = as_stream(stream);
   {
-    ProfScope prof_("k_sgqa_prefill", as_stream(stream));
-    hipLaunchKernelGGL(k_sgqa_prefill, dim3((unsigned)(kGroups * ((n_queries + 3) / 4))), dim3(256), 0,
-                       as_stream(stream), a);
+    ProfScope prof_("k_sgqa_prefill", s);
+    hipLaunchKernelGGL(k_sgqa_prefill, dim3((unsigned)(kPreSplits * kGroups * ((n_queries + 3) / 4))), dim3(256),
+                       0, s, a);
   }
-  return check_launch("dsa_sparse_gqa_prefill");
+  st = check_launch("dsa_sparse_gqa_prefill");
+  if (st != DSA_OK) return st;
+  {
+    ProfScope prof_("k_sgqa_merge", s);
+    hipLaunchKernelGGL(k_sgqa_merge_pre, dim3((unsigned)(kGroups * (int64_t)n_queries)), dim3(256), 0, s,
+                       (const uint16_t*)a.part_o, (const float*)a.part_ml, out);
+  }
+  return check_launch("dsa_sparse_gqa_prefill: merge");
 }
 
 extern "C" size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

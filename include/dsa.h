@@ -228,18 +228,26 @@ dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16
                            int32_t* sel, int32_t* n_sel, uint16_t* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Workspace bytes dsa_sparse_gqa_prefill needs for n_queries queries. */
+size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries);
+
 /*
  * Sparse GQA for a chunk of prefill queries ([P3] kernel list:
  * sparse_attention_prefill).  Same maths as decode, per query i of sequence
  * q_seq[i] at position q_pos[i] (the current region may be partial; tokens
  * after p are masked).  The chunk's own K/V must already be in the caches.
+ * The list entries need not be sorted; each entry counts once (repeats
+ * count again), and ids outside [0, p/8] are ignored.
  *   q, out [n_queries][64][D] bf16;  caches of n_seqs sequences, capacity tcap
+ *   workspace >= dsa_sparse_gqa_prefill_workspace_size() bytes, 256-byte
+ *             aligned: per-(query, group) partial results over 8 ranges of
+ *             regions, merged into out by the same call
  */
 dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
                                   const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
                                   const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
                                   const int32_t* sel, const int32_t* n_sel, uint16_t* out,
-                                  void* stream);
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes swa_attention needs. */
 size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

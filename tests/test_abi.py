@@ -80,7 +80,7 @@ def test_empty_work_is_a_no_op(lib):
     assert lib.dsa_score_topk(ctypes.byref(g), 0, None, None, None, None, 1, None, None, 128, 8, None, None, None,
                               None, 0, None) == 0
     assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 0, None, None, None, 1, None, None, 128, None, None, None,
-                                      None) == 0
+                                      None, 0, None) == 0
 
 
 def test_workspace_checks(lib):
@@ -97,6 +97,12 @@ def test_workspace_checks(lib):
     need = lib.dsa_sparse_gqa_workspace_size(ctypes.byref(g), 3)
     rc = lib.dsa_sparse_gqa_decode(ctypes.byref(g), 3, vp, vp, vp, 128, vp, vp, vp, vp, vp, need - 1, None)
     assert rc == 3
+    need = lib.dsa_sparse_gqa_prefill_workspace_size(ctypes.byref(g), 300)
+    assert need >= 300 * 4 * 8 * 16 * 192 * 4  # a partial O per (query, group, region range)
+    args = [vp, vp, vp, 1, vp, vp, 8192, vp, vp, vp]
+    assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 300, *args, vp, need - 1, None) == 3
+    assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 300, *args, ctypes.c_void_p(260), need, None) == 1
+    assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 300, *args, None, need, None) == 1
 
 
 def test_swa_window_must_be_512(lib):
