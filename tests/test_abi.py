@@ -98,7 +98,7 @@ def test_workspace_checks(lib):
     rc = lib.dsa_sparse_gqa_decode(ctypes.byref(g), 3, vp, vp, vp, 128, vp, vp, vp, vp, vp, need - 1, None)
     assert rc == 3
     need = lib.dsa_sparse_gqa_prefill_workspace_size(ctypes.byref(g), 300)
-    assert need >= 300 * 4 * 8 * 16 * 192 * 4  # a partial O per (query, group, region range)
+    assert need >= 300 * 4 * 8 * 16 * (192 * 2 + 8)  # a bf16 partial O + (max, sum) per (query, group, range)
     args = [vp, vp, vp, 1, vp, vp, 8192, vp, vp, vp]
     assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 300, *args, vp, need - 1, None) == 3
     assert lib.dsa_sparse_gqa_prefill(ctypes.byref(g), 300, *args, ctypes.c_void_p(260), need, None) == 1
