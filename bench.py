@@ -59,13 +59,14 @@ def decode_bytes(B, L, topk):
 def prefill_flops(prefix, chunk, topk):
     """Per chunk: indexer dot products (4 heads x 256 channels per candidate region and group) and
     sparse attention (QK^T and PV over the attended tokens, 16 heads per group)."""
-    score = attend = 0
+    score = attend = gather = 0
     for p in range(prefix, prefix + chunk):
         c = p // REG
         score += c * G * 4 * P * 2
         tokens = min(topk - 1, c) * REG + (p % REG + 1)
         attend += G * tokens * 16 * D * 2 * 2
-    return dict(score=score, attend=attend, total=score + attend)
+        gather += G * tokens * D * 2 * 2  # bf16 K and V rows of the attended tokens
+    return dict(score=score, attend=attend, total=score + attend, gather=gather)
 
 
 def source_hash(*names):
@@ -435,7 +436,7 @@ def main():
         n = PREFILL["chunk"]
         fl = prefill_flops(PREFILL["prefix"], n, PREFILL["topk"])
         pms = psecs * 1e3 / psteps
-        att_ms, sc_ms = pst["k_sgqa_prefill"][0], pst["k_score_prefill"][0]
+        att_ms, sc_ms, mg_ms = pst["k_sgqa_prefill"][0], pst["k_score_prefill"][0], pst["k_sgqa_merge"][0]
         att_tf = fl["attend"] / (att_ms * 1e-3) / 1e12
         sc_tf = fl["score"] / (sc_ms * 1e-3) / 1e12
         step_tf = fl["total"] / (pms * 1e-3) / 1e12
@@ -446,6 +447,12 @@ def main():
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": load_traffic("k_sgqa_prefill", "prefill_64k", source_hash("attention.hip")),
                          "algorithmic_flops_per_launch": fl["attend"], "avg_launch_us": round(att_ms * 1e3, 1)},
+            "attention_with_merge": {
+                "kernels": ["k_sgqa_prefill", "k_sgqa_merge"],
+                "achieved_TFLOPs": round(fl["attend"] / ((att_ms + mg_ms) * 1e-3) / 1e12, 2),
+                "frac": round(fl["attend"] / ((att_ms + mg_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "gathered_kv_bytes": fl["gather"],
+                "gather_GBs": round(fl["gather"] / (att_ms * 1e-3) / 1e9, 1)},
             "score_kernel": {"kernel": "k_score_prefill", "achieved_TFLOPs": round(sc_tf, 2),
                              "frac": round(sc_tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl["score"],
                              "avg_launch_us": round(sc_ms * 1e3, 1)},

@@ -462,14 +462,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hn = lane & 15, kb = lane >> 4;
   const int64_t pr = ((pg * kPreSplits) + split) * 16 + hn;  // partial row of head hn
   const float l = core_total_l(st);
-  if (kb == 0) *(float2*)&a.part_ml[2 * pr] = make_float2(st.m, l);
-  uint16_t* po = a.part_o + pr * kHeadDim + 4 * kb;
+  // (streaming stores: the partials are read once, by the merge, and should
+  // not displace this range's K/V from the L2)
+  if (kb == 0) {
+    __builtin_nontemporal_store(st.m, &a.part_ml[2 * pr]);
+    __builtin_nontemporal_store(l, &a.part_ml[2 * pr + 1]);
+  }
+  uint32_t* po = (uint32_t*)(a.part_o + pr * kHeadDim + 4 * kb);
 #pragma unroll
   for (int nt = 0; nt < 12; ++nt) {
-    uint2 w;
-    w.x = pack_bf16x2(st.o[nt][0], st.o[nt][1]);
-    w.y = pack_bf16x2(st.o[nt][2], st.o[nt][3]);
-    *(uint2*)(po + 16 * nt) = w;
+    __builtin_nontemporal_store(pack_bf16x2(st.o[nt][0], st.o[nt][1]), po + 8 * nt);
+    __builtin_nontemporal_store(pack_bf16x2(st.o[nt][2], st.o[nt][3]), po + 8 * nt + 1);
   }
 }
 
