@@ -33,6 +33,12 @@ DECODE = dict(name="DSA decode, batch 4, 1,048,576-token context, top-512, plant
               batch=4, context=1048576, topk=TOPK, planted=True, seed_index=3)
 PREFILL = dict(name="DSA chunked prefill, 2048 new tokens after a 63,488-token prefix (64K), top-512",
                prefix=63488, chunk=2048, topk=TOPK, seed_index=2)
+MIX = dict(name="3:1 layer mix, decode: three sliding-window layers (512-token rings) then one DSA layer, "
+                "batch 8, 262,144-token context, top-512",
+           batch=8, context=262144, topk=TOPK, planted=False, seed_index=4, swa_layers=3)
+SWA_PREFILL = dict(name="sliding-window layer, chunked prefill: 2048 new tokens after 63,488 (512-token ring)",
+                   prefix=63488, chunk=2048, seed_index=4)
+W = 512
 
 
 def log(*a):
@@ -67,6 +73,17 @@ def prefill_flops(prefix, chunk, topk):
         attend += G * tokens * 16 * D * 2 * 2
         gather += G * tokens * D * 2 * 2  # bf16 K and V rows of the attended tokens
     return dict(score=score, attend=attend, total=score + attend, gather=gather)
+
+
+def swa_decode_bytes(B):
+    """Per sliding-window layer and decode step: the window's K and V (511 ring rows + the new one) for
+    4 groups, q in and out, the new row's K/V in and its ring write."""
+    return B * (W * G * D * 2 * 2 + HQ * D * 2 * 2 + G * D * 2 * 2 * 2)
+
+
+def swa_prefill_flops(prefix, chunk):
+    """QK^T and PV over each query's band of min(512, p+1) keys, 64 heads."""
+    return sum(min(W, p + 1) for p in range(prefix, prefix + chunk)) * HQ * D * 2 * 2
 
 
 def source_hash(*names):
@@ -224,6 +241,83 @@ def setup_prefill(cfg):
     return step, keep
 
 
+def setup_swa(seed, layer, n_seqs, p0, n_new, geom):
+    """One sliding-window layer: rings holding positions p0-512..p0-1 of every sequence (written by the
+    generator in the ring layouts), n_new new rows per sequence at p0.. (token-major K/V, q), output and
+    workspace.  Returns the marshalled swa_attention and swa_ring_append arguments and the tensors."""
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+
+    s = torch.cuda.current_stream().cuda_stream
+    tq, tk, tv = (gi.tid_swa(t, layer) for t in (gi.TID_Q, gi.TID_K, gi.TID_V))
+    T = p0 + n_new
+    kr = torch.empty(n_seqs * G * W * D, dtype=torch.bfloat16, device="cuda")
+    vr = torch.empty(n_seqs * G * W * D, dtype=torch.bfloat16, device="cuda")
+    t0 = max(0, p0 - W)
+    if p0 > t0:
+        gi.dev_tokens(kr.data_ptr(), s, seed, tk, n_seqs, T, G, D, t0, p0 - t0, W, W, gi.LAYOUT_KTILED)
+        gi.dev_tokens(vr.data_ptr(), s, seed, tv, n_seqs, T, G, D, t0, p0 - t0, W, W, gi.LAYOUT_REGION_T)
+    rows = n_seqs * n_new
+    kn = torch.empty(rows * G * D, dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty(rows * G * D, dtype=torch.bfloat16, device="cuda")
+    gi.dev_tokens(kn.data_ptr(), s, seed, tk, n_seqs, T, G, D, p0, n_new, n_new, n_new, gi.LAYOUT_TOKEN_MAJOR)
+    gi.dev_tokens(vn.data_ptr(), s, seed, tv, n_seqs, T, G, D, p0, n_new, n_new, n_new, gi.LAYOUT_TOKEN_MAJOR)
+    q = torch.empty(rows * HQ * D, dtype=torch.bfloat16, device="cuda")
+    gi.dev_flat(q.data_ptr(), s, seed, tq, q.numel(), 0, 1.0)
+    out = torch.empty(rows * HQ * D, dtype=torch.bfloat16, device="cuda")
+    pos0 = torch.tensor([p0] * n_seqs, dtype=torch.int32, device="cuda")
+    row0 = torch.tensor([n_new * i for i in range(n_seqs + 1)], dtype=torch.int32, device="cuda")
+    ws = dsa.workspace(dsa.swa_attention_workspace_size(geom, W, n_seqs, n_new))
+    p = Calls.p
+    gp = ctypes.byref(geom)
+    a_att = (gp, W, n_seqs, n_new, p(pos0), p(row0), p(q), p(kn), p(vn), p(kr), p(vr), p(out), p(ws), ws.numel())
+    a_app = (gp, W, n_seqs, n_new, p(pos0), p(row0), p(kn), p(vn), p(kr), p(vr))
+    return a_att, a_app, (kr, vr, kn, vn, q, out, pos0, row0, ws)
+
+
+def setup_mix(cfg):
+    """The 3:1 stack: three sliding-window layers (decode: one new token per sequence at L-1, rings
+    holding L-513..L-2), then the DSA decode step of the same batch.  Each layer's ring append rewrites
+    the same slot every step, so repeated steps see identical inputs."""
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+
+    B, Lc = cfg["batch"], cfg["context"]
+    seed = gi.SEED_BASE + cfg["seed_index"]
+    dsa_step, keep = setup_decode(cfg)
+    geom = keep[-1]
+    L = dsa.load()
+    layers = [setup_swa(seed, l, B, Lc - 1, 1, geom) for l in range(cfg["swa_layers"])]
+
+    def step(st):
+        for a_att, a_app, _ in layers:
+            rc = L.swa_attention(*a_att, st) or L.swa_ring_append(*a_app, st)
+            if rc:
+                raise RuntimeError(f"sliding-window layer failed: {rc} {L.dsa_last_error().decode()}")
+        dsa_step(st)
+
+    return step, (keep, layers)
+
+
+def setup_swa_prefill(cfg):
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+
+    seed = gi.SEED_BASE + cfg["seed_index"]
+    geom = dsa.geometry()
+    a_att, a_app, tens = setup_swa(seed, 0, 1, cfg["prefix"], cfg["chunk"], geom)
+    L = dsa.load()
+
+    def step(st):
+        rc = L.swa_attention(*a_att, st) or L.swa_ring_append(*a_app, st)
+        if rc:
+            raise RuntimeError(f"sliding-window prefill failed: {rc} {L.dsa_last_error().decode()}")
+
+    return step, (tens, geom)
+
+
 def cur_stream():
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -346,6 +440,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-swa", action="store_true", help="skip the 3:1 layer mix and sliding-window prefill lines")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
     ap.add_argument("--separate", action="store_true",
@@ -376,6 +471,13 @@ def main():
                 step(cur_stream())
             torch.cuda.synchronize()
             del keep
+        if not args.no_swa:
+            for setup, cfg in ((setup_mix, MIX), (setup_swa_prefill, SWA_PREFILL)):
+                step, keep = setup(cfg)
+                for _ in range(2):
+                    step(cur_stream())
+                torch.cuda.synchronize()
+                del keep
         # calibration: a plain elementwise shader kernel that reads exactly 1 GiB and writes
         # exactly 1 GiB (torch.bitwise_not on uint8), for scaling the FETCH/WRITE counters
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -461,6 +563,54 @@ def main():
             "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in pst.items()},
         }
         log(f"prefill: {n * psteps / psecs:.0f} tok/s, {pms:.3f} ms/step")
+
+    # ---- the 3:1 sliding-window / DSA stack (decode) and a sliding-window prefill chunk
+    if not args.no_swa:
+        step, keep = setup_mix(MIX)
+        km = ["k_swa_stage", "k_swa_attend", "k_ring_append", "k_score_decode", "k_select", "k_sgqa_decode",
+              "k_sgqa_merge"]
+        msteps = max(3, args.steps // 3)
+        msecs, meager, mst = timed(step, msteps, max(1, args.warmup // 2), km, graph=args.graph)
+        del keep
+        torch.cuda.empty_cache()
+        B, Lc = MIX["batch"], MIX["context"]
+        mms = msecs * 1e3 / msteps
+        sbytes = swa_decode_bytes(B)
+        dbytes = decode_bytes(B, Lc, MIX["topk"])["total"]
+        tot = MIX["swa_layers"] * sbytes + dbytes
+        swa_us = sum(mst[k][0] for k in ("k_swa_stage", "k_swa_attend", "k_ring_append")) * 1e3  # per layer
+        result["mix_decode"] = {
+            "workload": MIX["name"], "value": round(B * msteps / msecs, 1), "unit": "queries/s (4-layer stack)",
+            "steps": msteps, "ms_per_step": round(mms, 4), "eager_ms_per_step": round(meager * 1e3 / msteps, 4),
+            "roofline": {"bound": "hbm", "kernel": "whole stack", "achieved": round(tot / (mms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(tot / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_step": tot},
+            "swa_layer": {"algorithmic_bytes": sbytes, "us_per_layer": round(swa_us, 2),
+                          "achieved_GBs": round(sbytes / (swa_us * 1e-6) / 1e9, 1)},
+            "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in mst.items()},
+        }
+        log(f"mix decode: {B * msteps / msecs:.0f} q/s, {mms:.3f} ms/step")
+        step, keep = setup_swa_prefill(SWA_PREFILL)
+        ks = ["k_swa_stage", "k_swa_attend", "k_ring_append"]
+        ssteps = max(3, args.steps // 3)
+        ssecs, seager, sst = timed(step, ssteps, max(1, args.warmup // 2), ks, graph=args.graph)
+        del keep
+        torch.cuda.empty_cache()
+        n = SWA_PREFILL["chunk"]
+        fl = swa_prefill_flops(SWA_PREFILL["prefix"], n)
+        sms = ssecs * 1e3 / ssteps
+        att_ms = sst["k_swa_attend"][0]
+        result["swa_prefill"] = {
+            "workload": SWA_PREFILL["name"], "value": round(n * ssteps / ssecs, 1), "unit": "tokens/s",
+            "steps": ssteps, "ms_per_step": round(sms, 4), "eager_ms_per_step": round(seager * 1e3 / ssteps, 4),
+            "roofline": {"bound": "mfma", "kernel": "k_swa_attend",
+                         "achieved": round(fl / (att_ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(fl / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": fl, "avg_launch_us": round(att_ms * 1e3, 1)},
+            "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in sst.items()},
+        }
+        log(f"swa prefill: {n * ssteps / ssecs:.0f} tok/s, {sms:.3f} ms/step")
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline_decode(DECODE)

@@ -556,43 +556,77 @@ __device__ __forceinline__ void seq_rows(const SwaArgs& a, int s, int64_t& p0, i
   if (nnew > a.max_new) nnew = a.max_new;
 }
 
-// block = (staged region j, sequence s); threads cover (group, channel).
+// block = (staged region j, sequence s).  A staged region has the ring's
+// layouts, so K is 192 units of 8 channels of one token and V 192 units of
+// one channel's 8 tokens, per group; thread t owns units t, t+256, ... of the
+// 4 groups' 384 units each, and every load is issued before the first store.
 __global__ __launch_bounds__(256) void k_swa_stage(SwaArgs a) {
+  constexpr int kUnits = kGroups * 2 * kHeadDim, kPer = kUnits / 256;
   const int j = blockIdx.x, s = blockIdx.y;
   int64_t p0, r0, nnew;
   seq_rows(a, s, p0, r0, nnew);
   const int64_t base_pos = (p0 / kRegion) * kRegion + (int64_t)j * kRegion;
-  if (base_pos >= p0 + nnew) return;
+  if (nnew <= 0 || base_pos >= p0 + nnew) return;
   const int W = a.window;
-  for (int e = threadIdx.x; e < kGroups * kHeadDim; e += 256) {
-    const int g = e / kHeadDim, d = e - g * kHeadDim;
+  const int64_t rslot = (base_pos % W) / kRegion;  // ring region of the old positions of this region
+  u32x4 val[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int u = threadIdx.x + 256 * k;
+    const int g = u / (2 * kHeadDim), rest = u - g * 2 * kHeadDim;
     const int64_t sg = (int64_t)s * kGroups + g;
-    uint16_t* sk = a.st_k + (sg * a.nst + j) * kRegionElems;
-    uint16_t* sv = a.st_v + ((sg * a.nst + j) * kHeadDim + d) * kRegion;
-    for (int t = 0; t < kRegion; ++t) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (rest < kHeadDim) {  // K unit: token t, channels d0 .. d0+7
+      const int q = rest;
+      const int t = (q / 96) * 4 + (q & 3), d0 = 48 * ((q >> 2) & 3) + 8 * ((q >> 4) % 6);
       const int64_t pos = base_pos + t;
-      uint16_t kv = 0, vv = 0;
-      if (pos < p0) {
-        const int64_t slot = pos % W;
-        kv = a.k_ring[(sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, d)];
-        vv = a.v_ring[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion];
-      } else if (pos < p0 + nnew) {
-        const int64_t row = r0 + (pos - p0);
-        kv = a.k_new[(row * kGroups + g) * kHeadDim + d];
-        vv = a.v_new[(row * kGroups + g) * kHeadDim + d];
+      if (pos < p0) v = ld16(a.k_ring + (sg * (W / kRegion) + rslot) * kRegionElems + 8 * q);
+      else if (pos < p0 + nnew) v = ld16(a.k_new + ((r0 + pos - p0) * kGroups + g) * kHeadDim + d0);
+    } else {  // V unit: channel d, tokens 0..7
+      const int d = rest - kHeadDim;
+      if (base_pos < p0) v = ld16(a.v_ring + ((sg * (W / kRegion) + rslot) * kHeadDim + d) * kRegion);
+      uint16_t e[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int64_t pos = base_pos + t;
+        const int64_t off = pos - p0;
+        const int64_t row = r0 + (off >= 0 && off < nnew ? off : 0);  // a new row (clamped otherwise)
+        const uint16_t nv = a.v_new[(row * kGroups + g) * kHeadDim + d];
+        const uint32_t w = t < 2 ? v.x : t < 4 ? v.y : t < 6 ? v.z : v.w;
+        const uint16_t ov = (uint16_t)(t & 1 ? w >> 16 : w & 0xFFFFu);
+        e[t] = pos < p0 ? ov : (pos < p0 + nnew ? nv : (uint16_t)0);
       }
-      sk[k_tile_offset(t, d)] = kv;
-      sv[t] = vv;
+      v.x = e[0] | ((uint32_t)e[1] << 16);
+      v.y = e[2] | ((uint32_t)e[3] << 16);
+      v.z = e[4] | ((uint32_t)e[5] << 16);
+      v.w = e[6] | ((uint32_t)e[7] << 16);
     }
+    val[k] = v;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int u = threadIdx.x + 256 * k;
+    const int g = u / (2 * kHeadDim), rest = u - g * 2 * kHeadDim;
+    const int64_t sg = (int64_t)s * kGroups + g;
+    uint16_t* dst = rest < kHeadDim ? a.st_k + (sg * a.nst + j) * kRegionElems + 8 * rest
+                                    : a.st_v + ((sg * a.nst + j) * kHeadDim + (rest - kHeadDim)) * kRegion;
+    *(u32x4*)dst = val[k];
   }
 }
 
-// block = (new token i of sequence s); 4 waves = 4 groups.
-__global__ __launch_bounds__(256) void k_swa_attend(SwaArgs a) {
+// block = (new token i of sequence s, group g); the window's regions go to
+// the 4 waves in chunks of 4 (wave w: chunks w, w+4, ...), whose partial
+// (max, sum, O) merge through LDS.  DEPTH as for core_run: 2 for few blocks
+// (decode: latency), 0 with two blocks per CU for many (chunked prefill).
+template <int DEPTH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEPTH == 0 ? 2 : 1, DEPTH == 0 ? 2 : 1)))
+void k_swa_attend(SwaArgs a) {
   const int64_t i = blockIdx.x;
-  const int s = blockIdx.y;
-  const int g = threadIdx.x >> 6;
+  const int s = blockIdx.y, g = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[4][16][kORow];
   int64_t p0, r0, nnew;
   seq_rows(a, s, p0, r0, nnew);
   if (i >= nnew) return;
@@ -611,13 +645,16 @@ __global__ __launch_bounds__(256) void k_swa_attend(SwaArgs a) {
   CoreState st;
   core_init(st);
   const int64_t nreg = rhi - rlo + 1;
+  const int64_t nch = (nreg + 3) / 4;
+  const int64_t mine = wave < nch ? 4 * ((nch - wave + 3) / 4) : 0;  // this wave's list entries
   auto region_of = [&](int64_t e) -> Region {
+    const int64_t er = 4 * (wave + 4 * (e >> 2)) + (e & 3);  // window region index of entry e
     Region rg;
-    if (e >= nreg) {
+    if (e >= mine || er >= nreg) {
       rg.k = rk; rg.v = rv; rg.lo = 1; rg.hi = 0;
       return rg;
     }
-    const int64_t r = rlo + e;
+    const int64_t r = rlo + er;
     if (r < rst) {
       const int64_t pk = r % (W / kRegion);
       rg.k = rk + pk * kRegion * kHeadDim;
@@ -631,12 +668,37 @@ __global__ __launch_bounds__(256) void k_swa_attend(SwaArgs a) {
     rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
     return rg;
   };
-  core_run<2>(st, qb, nreg, region_of, a.scale_log2);
-  core_store(st, a.out, row, g);
+  core_run<DEPTH>(st, qb, mine, region_of, a.scale_log2);
+  // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i), then the merged,
+  // normalised output
+  const float lt = core_total_l(st);
+  if (kb == 0) {
+    sm_m[wave][n] = st.m;
+    sm_l[wave][n] = lt;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) *(f32x4*)&sm_o[wave][n][16 * nt + 4 * kb] = st.o[nt];
+  __syncthreads();
+  uint16_t* op = a.out + (row * kQHeads + kHeadsPerGroup * g) * kHeadDim;
+  for (int e = threadIdx.x; e < 16 * kHeadDim; e += 256) {
+    const int h = e / kHeadDim, d = e - h * kHeadDim;
+    const float M = fmaxf(fmaxf(sm_m[0][h], sm_m[1][h]), fmaxf(sm_m[2][h], sm_m[3][h]));
+    float acc = 0.0f, lsum = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
+        acc += f * sm_o[w][h][d];
+        lsum += f * sm_l[w][h];
+      }
+    }
+    op[h * kHeadDim + d] = f32_to_bf16(lsum > 0.0f ? acc / lsum : 0.0f);
+  }
 }
 
 // block = (new token i of sequence s): writes it to the ring if it is among
-// the last `window` new tokens of its sequence.
+// the last `window` new tokens of its sequence (K as 96 units of 8 channels,
+// V element-wise; all loads issued before the stores).
 __global__ __launch_bounds__(256) void k_ring_append(SwaArgs a, uint16_t* k_ring, uint16_t* v_ring) {
   const int64_t i = blockIdx.x;
   const int s = blockIdx.y;
@@ -645,13 +707,26 @@ __global__ __launch_bounds__(256) void k_ring_append(SwaArgs a, uint16_t* k_ring
   if (i >= nnew || i < nnew - a.window) return;
   const int W = a.window;
   const int64_t pos = p0 + i, row = r0 + i, slot = pos % W;
-  for (int e = threadIdx.x; e < kGroups * kHeadDim; e += 256) {
-    const int g = e / kHeadDim, d = e - g * kHeadDim;
+  const int t = threadIdx.x;
+  // K: 4 groups x 24 units of 8 channels (threads 0..95)
+  if (t < kGroups * kHeadDim / 8) {
+    const int g = t / (kHeadDim / 8), d0 = 8 * (t % (kHeadDim / 8));
     const int64_t sg = (int64_t)s * kGroups + g;
-    k_ring[(sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, d)] =
-        a.k_new[(row * kGroups + g) * kHeadDim + d];
-    v_ring[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion] =
-        a.v_new[(row * kGroups + g) * kHeadDim + d];
+    const u32x4 v = ld16(a.k_new + (row * kGroups + g) * kHeadDim + d0);
+    *(u32x4*)(k_ring + (sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, d0)) = v;
+  }
+  // V: 768 elements, 3 per thread
+  uint16_t vv[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int e = t + 256 * k, g = e / kHeadDim, d = e - g * kHeadDim;
+    vv[k] = a.v_new[(row * kGroups + g) * kHeadDim + d];
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int e = t + 256 * k, g = e / kHeadDim, d = e - g * kHeadDim;
+    const int64_t sg = (int64_t)s * kGroups + g;
+    v_ring[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion] = vv[k];
   }
 }
 
@@ -805,8 +880,13 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   st = check_launch("swa_attention: stage");
   if (st != DSA_OK) return st;
   {
+    // few blocks: keep two chunks in flight per wave; many: two blocks per CU instead
     ProfScope prof_("k_swa_attend", s);
-    hipLaunchKernelGGL(k_swa_attend, dim3(max_new_per_seq, n_seqs), dim3(256), 0, s, a);
+    const dim3 grid(max_new_per_seq, n_seqs, kGroups);
+    if ((int64_t)max_new_per_seq * n_seqs * kGroups < 1024)
+      hipLaunchKernelGGL(k_swa_attend<2>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_swa_attend<0>, grid, dim3(256), 0, s, a);
   }
   return check_launch("swa_attention");
 }
