@@ -11,9 +11,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "lib", "libdsa_mi355x.so")
 SOURCES = ["api.hip", "compress.hip", "score_topk.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU ops are kept off: the compiler must not form v_pk_* fp32 math.
+# Packed fp32 VALU ops are kept off: the compiler must not form v_pk_* fp32 math.  MFMA results are
+# allocated in ordinary VGPRs where they fit (instead of accumulation registers with copies around
+# every VALU use): the multi-query sliding-window kernel then fits its 4 queries' state without spills.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -103,8 +103,7 @@ __device__ __forceinline__ void core_compute(CoreState& st, const bf16x8 qb[6], 
   float cmax = sv[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[i]);
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+  cmax = max_across_rows(cmax);
   // Lazy rescaling: the reference max m only moves (and O, l are rescaled)
   // when some head's running max exceeds it by more than 8 (log2 units), so
   // every weight exp2(s - m) stays <= 256 and most chunks skip the rescale.
@@ -209,10 +208,7 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
 
 // Total softmax denominator of the lane's head (sum over the 4 kb lanes).
 __device__ __forceinline__ float core_total_l(const CoreState& st) {
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  return l;
+  return sum_across_rows(st.l);
 }
 
 // Writes the normalised output of head (16g + n) of query row qrow.
@@ -696,6 +692,217 @@ void k_swa_attend(SwaArgs a) {
   }
 }
 
+// S^T tiles, online softmax and O^T += V^T P^T of one chunk for NQ queries
+// that share its K/V registers (the band kernel: neighbouring queries of
+// one group read the same window).  lo[j]/hi[j]: query j's valid positions
+// in the lane's softmax region.  Positions no query of the wave uses get
+// their V zeroed; a position one query uses and another masks holds real
+// data and gets weight 0 from the latter.
+template <int NQ>
+__device__ __forceinline__ void core_compute_band(CoreState (&st)[NQ], const bf16x8 (&qb)[NQ][6], ChunkRegs& c,
+                                                  const int (&lo)[NQ], const int (&hi)[NQ], float scale_log2) {
+  int ulo = lo[0], uhi = hi[0];
+#pragma unroll
+  for (int j = 1; j < NQ; ++j) {
+    ulo = lo[j] < ulo ? lo[j] : ulo;
+    uhi = hi[j] > uhi ? hi[j] : uhi;
+  }
+  const bool full = (ulo <= 0 && uhi >= 7);
+  if (__any(!full)) {
+    uint32_t mk[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bool a0 = (2 * w >= ulo && 2 * w <= uhi);
+      const bool a1 = (2 * w + 1 >= ulo && 2 * w + 1 <= uhi);
+      mk[w] = (a0 ? 0x0000FFFFu : 0u) | (a1 ? 0xFFFF0000u : 0u);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) {
+      c.v[nt].x &= mk[0];
+      c.v[nt].y &= mk[1];
+      c.v[nt].z &= mk[2];
+      c.v[nt].w &= mk[3];
+    }
+  }
+  // three phases over the NQ queries (S tiles, softmax, P.V) so that one
+  // query's MFMAs overlap another's VALU work
+  f32x4 s0[NQ], s1[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    s0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int q = 0; q < 6; ++q)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      s0[j] = mfma16x16x32(as_bf16x8(c.k0[q]), qb[j][q], s0[j]);
+      s1[j] = mfma16x16x32(as_bf16x8(c.k1[q]), qb[j][q], s1[j]);
+    }
+  float sv[NQ][8], m_new[NQ];
+  bool grow = false;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[j][i] = (i >= lo[j] && i <= hi[j]) ? s0[j][i] * scale_log2 : -INFINITY;
+      sv[j][4 + i] = (4 + i >= lo[j] && 4 + i <= hi[j]) ? s1[j][i] * scale_log2 : -INFINITY;
+    }
+    float cmax = sv[j][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[j][i]);
+    m_new[j] = fmaxf(st[j].m, max_across_rows(cmax));
+    grow |= m_new[j] > st[j].m + 8.0f;
+  }
+  // lazy rescaling as in core_compute, one branch for the wave's queries
+  if (__any(grow)) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      if (__any(m_new[j] > st[j].m + 8.0f)) {
+        const float alpha = __builtin_amdgcn_exp2f(st[j].m - m_new[j]);
+        st[j].l *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 12; ++nt) st[j].o[nt] *= alpha;
+        st[j].m = m_new[j];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const float m_use = st[j].m == -INFINITY ? 0.0f : st[j].m;
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(sv[j][i] - m_use);
+    st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+    u32x4 pp;
+    pp.x = pack_bf16x2(pr[0], pr[1]);
+    pp.y = pack_bf16x2(pr[2], pr[3]);
+    pp.z = pack_bf16x2(pr[4], pr[5]);
+    pp.w = pack_bf16x2(pr[6], pr[7]);
+    const bf16x8 pb = as_bf16x8(pp);
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) st[j].o[nt] = mfma16x16x32(as_bf16x8(c.v[nt]), pb, st[j].o[nt]);
+  }
+}
+
+// Chunked prefill: block = (16 consecutive new tokens of sequence s, group
+// g), 4 waves of 4 tokens each.  The tokens' windows nearly coincide, so the
+// block streams the union of the windows (≈67 regions) through an LDS ring
+// of 4-region chunks once; each wave loads a chunk's K/V into registers
+// once and applies it to its 4 tokens under their band masks, so a K/V byte
+// read from L2 feeds 16 queries and a byte read from LDS feeds 4.  Each
+// chunk is 24 copies of 1 KB (the DMA form of the loads, global -> LDS):
+// wave w copies region w of it.  Copies run kBandDepth - 1 chunks ahead; a
+// wave's count of outstanding memory operations (the loop issues nothing
+// else) tells when its copies landed, and a barrier makes the whole chunk
+// visible and frees the slot refilled next.
+#ifndef DSA_BAND_NQ
+#define DSA_BAND_NQ 4
+#endif
+constexpr int kBandNQ = DSA_BAND_NQ;              // tokens per wave
+constexpr int kBandQ = 4 * kBandNQ;               // tokens per block
+constexpr int kBandDepth = 4;                     // chunks in the LDS ring
+constexpr int kRegionBytes = kRegionElems * 2;    // K (or V) of one region
+constexpr int kBandRegion = 2 * kRegionBytes + 64;  // a region's K then V in LDS; the 64-byte pad puts
+                                                     // the 4 regions' K rows a wave reads together in
+                                                     // different banks
+constexpr int kChunkBytes = 4 * kBandRegion;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_swa_band(SwaArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const int s = blockIdx.y, g = blockIdx.z;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kBandDepth][kChunkBytes];
+  int64_t p0, r0, nnew;
+  seq_rows(a, s, p0, r0, nnew);
+  // gridDim.x is a multiple of 8 and consecutive blocks go to the 8 XCDs in
+  // turn, so XCD x gets blocks x, x+8, ...: give it a contiguous run of
+  // query tiles, whose windows overlap and stay in its L2
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int64_t i0 = tile * kBandQ;
+  if (i0 >= nnew) return;  // the same for the whole block
+  const int W = a.window;
+  const int64_t i1 = (i0 + kBandQ < nnew ? i0 + kBandQ : nnew) - 1;
+  const int64_t ulo = p0 + i0 - W + 1 < 0 ? 0 : p0 + i0 - W + 1;  // union of the block's windows
+  const int64_t rlo = ulo / kRegion, rhi = (p0 + i1) / kRegion, rst = p0 / kRegion;
+  const int nch = (int)((rhi - rlo + 1 + 3) / 4);
+  const int64_t sg = (int64_t)s * kGroups + g;
+  // wave w copies region w of each chunk (past rhi: a re-read of region rhi, masked)
+  const uint8_t* rk = (const uint8_t*)(a.k_ring + sg * W * kHeadDim);
+  const uint8_t* rv = (const uint8_t*)(a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion);
+  const uint8_t* sk = (const uint8_t*)(a.st_k + sg * a.nst * kRegionElems);
+  const uint8_t* sv = (const uint8_t*)(a.st_v + sg * a.nst * kRegionElems);
+#define DSA_BAND_ISSUE(c_)                                                                                  \
+  do {                                                                                                      \
+    int64_t r_ = rlo + 4 * (int64_t)(c_) + wave;                                                            \
+    r_ = r_ > rhi ? rhi : r_;                                                                               \
+    const int64_t o_ = r_ < rst ? (r_ % (W / kRegion)) * kRegionBytes : (r_ - rst) * kRegionBytes;          \
+    const uint8_t* bk_ = (r_ < rst ? rk : sk) + o_;                                                         \
+    const uint8_t* bv_ = (r_ < rst ? rv : sv) + o_;                                                         \
+    LdsPtr d_ = (LdsPtr)(&ring[(c_) % kBandDepth][0] + wave * kBandRegion);                                 \
+    _Pragma("unroll") for (int k_ = 0; k_ < 3; ++k_) {                                                      \
+      __builtin_amdgcn_global_load_lds((const void*)(bk_ + 1024 * k_ + 16 * lane), d_ + 1024 * k_, 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds((const void*)(bv_ + 1024 * k_ + 16 * lane), d_ + kRegionBytes + 1024 * k_, \
+                                       16, 0, 0);                                                           \
+    }                                                                                                       \
+  } while (0)
+  // this wave's tokens (idle ones shadow the last token and store nothing);
+  // Q first: its loads are then older than the copies, and waiting for them
+  // does not wait for the copies
+  bf16x8 qb[kBandNQ][6];
+  CoreState st[kBandNQ];
+  int64_t pj[kBandNQ];
+#pragma unroll
+  for (int j = 0; j < kBandNQ; ++j) {
+    const int64_t i = i0 + kBandNQ * wave + j;
+    const int64_t ic = i < nnew ? i : nnew - 1;
+    pj[j] = p0 + ic;
+    load_q(a.q, r0 + ic, g, qb[j]);
+    core_init(st[j]);
+  }
+  if (nch > 0)
+#pragma unroll
+    for (int c = 0; c < kBandDepth - 1; ++c) DSA_BAND_ISSUE(c);
+  for (int c = 0; c < nch; ++c) {
+    // the chunk's 6 copies are older than the 6 * (kBandDepth - 2) issued since
+    static_assert(kBandDepth == 4, "wait count below");
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    __syncthreads();
+    DSA_BAND_ISSUE(c + kBandDepth - 1);
+    const uint8_t* ch = &ring[c % kBandDepth][0];
+    ChunkRegs cr;
+    // K rows of region n/4 (tile layout as in memory), V^T of region kb
+    const uint8_t* kp = ch + (n >> 2) * kBandRegion + ((kb * 4 + (n & 3)) * 8) * 2;
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      cr.k0[q] = *(const u32x4*)(kp + (q * 16) * 16);
+      cr.k1[q] = *(const u32x4*)(kp + ((6 + q) * 16) * 16);
+    }
+    const uint8_t* vp = ch + kb * kBandRegion + kRegionBytes;
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) cr.v[nt] = *(const u32x4*)(vp + (16 * nt + n) * 16);
+    const int64_t r = rlo + 4 * c + kb, first = r * kRegion;
+    int lo[kBandNQ], hi[kBandNQ];
+#pragma unroll
+    for (int j = 0; j < kBandNQ; ++j) {
+      const int64_t qlo = pj[j] - W + 1;
+      const bool in = r <= pj[j] / kRegion && first + 7 >= qlo;
+      lo[j] = in ? (int)((qlo > first ? qlo : first) - first) : 1;
+      hi[j] = in ? (int)((pj[j] < first + 7 ? pj[j] : first + 7) - first) : 0;
+    }
+    core_compute_band<kBandNQ>(st, qb, cr, lo, hi, a.scale_log2);
+  }
+  // copies issued past the last chunk must land before the block's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < kBandNQ; ++j) {
+    const int64_t i = i0 + kBandNQ * wave + j;
+    if (i < nnew) core_store(st[j], a.out, r0 + i, g);
+  }
+#undef DSA_BAND_ISSUE
+}
+
 // block = (new token i of sequence s): writes it to the ring if it is among
 // the last `window` new tokens of its sequence (K as 96 units of 8 channels,
 // V element-wise; all loads issued before the stores).
@@ -882,11 +1089,16 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   {
     // few blocks: keep two chunks in flight per wave; many: two blocks per CU instead
     ProfScope prof_("k_swa_attend", s);
-    const dim3 grid(max_new_per_seq, n_seqs, kGroups);
-    if ((int64_t)max_new_per_seq * n_seqs * kGroups < 1024)
-      hipLaunchKernelGGL(k_swa_attend<2>, grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(k_swa_attend<0>, grid, dim3(256), 0, s, a);
+    if (max_new_per_seq >= 2 * kBandQ) {  // chunks: the band kernel shares each window across 16 tokens
+      const unsigned tiles = (unsigned)((max_new_per_seq + kBandQ - 1) / kBandQ);
+      hipLaunchKernelGGL(k_swa_band, dim3((tiles + 7) / 8 * 8, n_seqs, kGroups), dim3(256), 0, s, a);
+    } else {
+      const dim3 grid(max_new_per_seq, n_seqs, kGroups);
+      if ((int64_t)max_new_per_seq * n_seqs * kGroups < 1024)
+        hipLaunchKernelGGL(k_swa_attend<2>, grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL(k_swa_attend<0>, grid, dim3(256), 0, s, a);
+    }
   }
   return check_launch("swa_attention");
 }

@@ -37,7 +37,6 @@ constexpr int kPreSlot = 4096 + 4 * 256;  // one summary tile in the block's LDS
 #ifndef DSA_PRE_WAVES
 #define DSA_PRE_WAVES 2
 #endif
-typedef __attribute__((address_space(3))) uint8_t* LdsPtr;
 constexpr int kTile = 16;          // regions per MFMA tile
 constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
 #ifndef DSA_HIST_COPIES
