@@ -37,6 +37,12 @@ struct Region {
   const uint16_t* k;
   const uint16_t* v;
   int lo, hi;
+  // patched loads only (sliding-window decode): token tn of the region (-1:
+  // none) is read from the new K/V row kn/vn (token-major [D]) instead; vn
+  // must be readable whenever any lane of the wave patches
+  const uint16_t* kn;
+  const uint16_t* vn;
+  int tn;
 };
 
 struct CoreState {
@@ -66,24 +72,58 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int64_t qrow, int g, b
 struct ChunkRegs {
   u32x4 k0[6], k1[6], v[12];
   int lo, hi;
+  uint32_t vpatch[12];  // patched loads only: the new token's V (channel 16nt + n) and its slot
+  int tn;
 };
 
 // Issues the chunk's loads. ra = region of this lane's K rows (entry n/4),
-// rb = region of this lane's softmax weights and V pack (entry kb).
+// rb = region of this lane's softmax weights and V pack (entry kb).  PATCH:
+// Region::tn / kn / vn are honoured.
+template <bool PATCH = false>
 __device__ __forceinline__ void core_load(ChunkRegs& c, const Region& ra, const Region& rb) {
   const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
   // region-tiled K: unit ((t*6 + s)*4 + kb)*4 + (n&3) holds token 4t + n%4,
   // channels 48kb + 8s .. +7
   const uint16_t* kp = ra.k + (kb * 4 + (n & 3)) * 8;
+  if constexpr (PATCH) {
+    const bool p0 = ra.tn == (n & 3), p1 = ra.tn == 4 + (n & 3);
+    const uint16_t* kn = ra.kn + 48 * kb;
 #pragma unroll
-  for (int s = 0; s < 6; ++s) {
-    c.k0[s] = ld16(kp + (s * 16) * 8);
-    c.k1[s] = ld16(kp + ((6 + s) * 16) * 8);
+    for (int s = 0; s < 6; ++s) {
+      c.k0[s] = ld16(p0 ? kn + 8 * s : kp + (s * 16) * 8);
+      c.k1[s] = ld16(p1 ? kn + 8 * s : kp + ((6 + s) * 16) * 8);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+      c.k0[s] = ld16(kp + (s * 16) * 8);
+      c.k1[s] = ld16(kp + ((6 + s) * 16) * 8);
+    }
   }
 #pragma unroll
   for (int nt = 0; nt < 12; ++nt) c.v[nt] = ld16(rb.v + (16 * nt + n) * 8);
+  if constexpr (PATCH) {  // the new token's V, put into element tn when the chunk is used
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) c.vpatch[nt] = rb.vn[16 * nt + n];
+    c.tn = rb.tn;
+  }
   c.lo = rb.lo;
   c.hi = rb.hi;
+}
+
+// Puts the new token's V (patched loads) into element tn of the lane's V
+// units; nothing when tn < 0.
+__device__ __forceinline__ void core_apply_patch(ChunkRegs& c) {
+  const int t = c.tn;
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) {
+    const uint32_t x = c.vpatch[nt];
+    const uint32_t keep = (t & 1) ? 0x0000FFFFu : 0xFFFF0000u, put = (t & 1) ? x << 16 : x;
+    c.v[nt].x = (t >> 1 == 0) ? (c.v[nt].x & keep) | put : c.v[nt].x;
+    c.v[nt].y = (t >> 1 == 1) ? (c.v[nt].y & keep) | put : c.v[nt].y;
+    c.v[nt].z = (t >> 1 == 2) ? (c.v[nt].z & keep) | put : c.v[nt].z;
+    c.v[nt].w = (t >> 1 == 3) ? (c.v[nt].w & keep) | put : c.v[nt].w;
+  }
 }
 
 // S^T tiles, online softmax update, O^T += V^T P^T for one loaded chunk.
@@ -165,14 +205,20 @@ __device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], co
 // registers (for kernels running several waves per SIMD, which overlap each
 // other's loads); DEPTH 1 and 2: one and two chunks' loads in flight while a
 // chunk computes (one wave per SIMD).
-template <int DEPTH, class RegionOf>
+template <int DEPTH, bool PATCH = false, class RegionOf>
 __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int64_t n, const RegionOf& region_of,
                                          float scale_log2) {
   const int lane = threadIdx.x & 63, nn = lane & 15, kb = lane >> 4;
   if (n <= 0) return;
   if constexpr (DEPTH == 0) {
     // one chunk in registers per wave; several waves per SIMD overlap the loads
-    for (int64_t e0 = 0; e0 < n; e0 += 4) core_chunk(st, qb, region_of(e0 + (nn >> 2)), region_of(e0 + kb), scale_log2);
+    for (int64_t e0 = 0; e0 < n; e0 += 4) {
+      ChunkRegs c;
+      core_load<PATCH>(c, region_of(e0 + (nn >> 2)), region_of(e0 + kb));
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PATCH) core_apply_patch(c);
+      core_compute(st, qb, c, scale_log2);
+    }
     return;
   }
   // The prefetch is issued unconditionally (past the end it reads the dummy
@@ -181,26 +227,31 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
   if constexpr (DEPTH >= 2) {
   // three chunks in registers: two in flight while one computes
   ChunkRegs b0, b1, b2;
-  core_load(b0, region_of(nn >> 2), region_of(kb));
-  core_load(b1, region_of(4 + (nn >> 2)), region_of(4 + kb));
+  core_load<PATCH>(b0, region_of(nn >> 2), region_of(kb));
+  core_load<PATCH>(b1, region_of(4 + (nn >> 2)), region_of(4 + kb));
   for (int64_t e0 = 0; e0 < n; e0 += 12) {
-    core_load(b2, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
+    core_load<PATCH>(b2, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
+    if constexpr (PATCH) core_apply_patch(b0);
     core_compute(st, qb, b0, scale_log2);
     if (e0 + 4 >= n) break;
-    core_load(b0, region_of(e0 + 12 + (nn >> 2)), region_of(e0 + 12 + kb));
+    core_load<PATCH>(b0, region_of(e0 + 12 + (nn >> 2)), region_of(e0 + 12 + kb));
+    if constexpr (PATCH) core_apply_patch(b1);
     core_compute(st, qb, b1, scale_log2);
     if (e0 + 8 >= n) break;
-    core_load(b1, region_of(e0 + 16 + (nn >> 2)), region_of(e0 + 16 + kb));
+    core_load<PATCH>(b1, region_of(e0 + 16 + (nn >> 2)), region_of(e0 + 16 + kb));
+    if constexpr (PATCH) core_apply_patch(b2);
     core_compute(st, qb, b2, scale_log2);
   }
   } else {
   ChunkRegs b0, b1;
-  core_load(b0, region_of(nn >> 2), region_of(kb));
+  core_load<PATCH>(b0, region_of(nn >> 2), region_of(kb));
   for (int64_t e0 = 0; e0 < n; e0 += 8) {
-    core_load(b1, region_of(e0 + 4 + (nn >> 2)), region_of(e0 + 4 + kb));
+    core_load<PATCH>(b1, region_of(e0 + 4 + (nn >> 2)), region_of(e0 + 4 + kb));
+    if constexpr (PATCH) core_apply_patch(b0);
     core_compute(st, qb, b0, scale_log2);
     if (e0 + 4 >= n) break;
-    core_load(b0, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
+    core_load<PATCH>(b0, region_of(e0 + 8 + (nn >> 2)), region_of(e0 + 8 + kb));
+    if constexpr (PATCH) core_apply_patch(b1);
     core_compute(st, qb, b1, scale_log2);
   }
   }
@@ -614,7 +665,7 @@ __global__ __launch_bounds__(256) void k_swa_stage(SwaArgs a) {
 // the 4 waves in chunks of 4 (wave w: chunks w, w+4, ...), whose partial
 // (max, sum, O) merge through LDS.  DEPTH as for core_run: 2 for few blocks
 // (decode: latency), 0 with two blocks per CU for many (chunked prefill).
-template <int DEPTH>
+template <int DEPTH, bool DIRECT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEPTH == 0 ? 2 : 1, DEPTH == 0 ? 2 : 1)))
 void k_swa_attend(SwaArgs a) {
   const int64_t i = blockIdx.x;
@@ -635,6 +686,8 @@ void k_swa_attend(SwaArgs a) {
   const uint16_t* rv = a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion;
   const uint16_t* sk = a.st_k + sg * a.nst * kRegion * kHeadDim;
   const uint16_t* sv = a.st_v + sg * a.nst * kHeadDim * kRegion;
+  const uint16_t* knew = a.k_new + (row * kGroups + g) * kHeadDim;
+  const uint16_t* vnew = a.v_new + (row * kGroups + g) * kHeadDim;
 
   bf16x8 qb[6];
   load_q(a.q, row, g, qb);
@@ -651,7 +704,9 @@ void k_swa_attend(SwaArgs a) {
       return rg;
     }
     const int64_t r = rlo + er;
-    if (r < rst) {
+    if (r < rst || DIRECT) {
+      // DIRECT (one new token per sequence): the current region is the ring's,
+      // with the new token patched in from k_new / v_new at load time
       const int64_t pk = r % (W / kRegion);
       rg.k = rk + pk * kRegion * kHeadDim;
       rg.v = rv + pk * kHeadDim * kRegion;
@@ -659,12 +714,15 @@ void k_swa_attend(SwaArgs a) {
       rg.k = sk + (r - rst) * kRegion * kHeadDim;
       rg.v = sv + (r - rst) * kHeadDim * kRegion;
     }
+    rg.kn = knew;
+    rg.vn = vnew;
+    rg.tn = (DIRECT && r == p / kRegion) ? (int)(p % kRegion) : -1;
     const int64_t first = r * kRegion;
     rg.lo = (int)((lo > first ? lo : first) - first);
     rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
     return rg;
   };
-  core_run<DEPTH>(st, qb, mine, region_of, a.scale_log2);
+  core_run<DEPTH, DIRECT>(st, qb, mine, region_of, a.scale_log2);
   // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i), then the merged,
   // normalised output
   const float lt = core_total_l(st);
@@ -1080,6 +1138,11 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   a.st_k = (uint16_t*)workspace;
   a.st_v = (uint16_t*)((char*)workspace + (one + 255) / 256 * 256);
   hipStream_t s = as_stream(stream);
+  if (max_new_per_seq == 1) {  // decode: the attention kernel patches the new token in itself
+    ProfScope prof_("k_swa_attend", s);
+    hipLaunchKernelGGL((k_swa_attend<2, true>), dim3(1, n_seqs, kGroups), dim3(256), 0, s, a);
+    return check_launch("swa_attention");
+  }
   {
     ProfScope prof_("k_swa_stage", s);
     hipLaunchKernelGGL(k_swa_stage, dim3(a.nst, n_seqs), dim3(256), 0, s, a);
@@ -1095,9 +1158,9 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
     } else {
       const dim3 grid(max_new_per_seq, n_seqs, kGroups);
       if ((int64_t)max_new_per_seq * n_seqs * kGroups < 1024)
-        hipLaunchKernelGGL(k_swa_attend<2>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_swa_attend<2, false>), grid, dim3(256), 0, s, a);
       else
-        hipLaunchKernelGGL(k_swa_attend<0>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_swa_attend<0, false>), grid, dim3(256), 0, s, a);
     }
   }
   return check_launch("swa_attention");
