@@ -375,6 +375,52 @@ def test_swa_batched_decode_with_prefilled_rings():
             assert np.array_equal(kr[s, :, t % H.W, :], Kh[t])
 
 
+def test_swa_prefill_chunks_of_several_sequences_in_one_call():
+    """Chunks of different lengths for sequences at different positions in one call (the banded
+    prefill kernel: tiles of 16 tokens, partial last tiles, short and full rings)."""
+    seed = 0xF7
+    p0s, ns = [0, 300, 1000, 4093], [50, 37, 64, 17]
+    S, M = len(p0s), max(ns)
+    T = max(p + n for p, n in zip(p0s, ns))
+    tq, tk, tv = H.swa_tids(1)
+    geom = dsa.geometry()
+    per = G * H.W * D
+    k_ring = torch.full((S * per,), float("nan"), dtype=H.BF16, device="cuda")
+    v_ring = torch.full((S * per,), float("nan"), dtype=H.BF16, device="cuda")
+    for s, p in enumerate(p0s):
+        t0 = max(0, p - H.W)
+        if p > t0:
+            for layout, ring, tid in ((gi.LAYOUT_KTILED, k_ring, tk), (gi.LAYOUT_REGION_T, v_ring, tv)):
+                tmp = torch.empty((s + 1) * per, dtype=H.BF16, device="cuda")
+                gi.dev_tokens(tmp.data_ptr(), H.stream_ptr(), seed, tid, s + 1, T, G, D, t0, p - t0, H.W, H.W,
+                              layout, 1.0)
+                ring[s * per:(s + 1) * per] = tmp[s * per:(s + 1) * per]
+    row0 = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    rows = int(row0[-1])
+    q = torch.empty(S * M * HQ * D, dtype=H.BF16, device="cuda")
+    kn = torch.empty(S * M * G * D, dtype=H.BF16, device="cuda")
+    vn = torch.empty(S * M * G * D, dtype=H.BF16, device="cuda")
+    for s, (p, n) in enumerate(zip(p0s, ns)):
+        r = int(row0[s])
+        gi.dev_flat(q[r * HQ * D:].data_ptr(), H.stream_ptr(), seed, tq, n * HQ * D, 0, 1.0,
+                    start=(s * T + p) * HQ * D)
+        tmpk = H.dev_cache(seed, tk, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=n)
+        tmpv = H.dev_cache(seed, tv, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=n)
+        kn[r * G * D:(r + n) * G * D] = tmpk[s * n * G * D:(s + 1) * n * G * D]
+        vn[r * G * D:(r + n) * G * D] = tmpv[s * n * G * D:(s + 1) * n * G * D]
+    out = torch.empty(S * M * HQ * D, dtype=H.BF16, device="cuda")
+    dsa.swa_attention(geom, H.W, M, H.i32(p0s), H.i32(row0), q, kn, vn, k_ring, v_ring, out)
+    torch.cuda.synchronize()
+    go = H.bf16_np(out)[:rows * HQ * D].reshape(rows, HQ, D)
+    for s, (p, n) in enumerate(zip(p0s, ns)):
+        Kh = gi.host_tokens_bf16(seed, tk, T, G, D, s, 0, p + n)
+        Vh = gi.host_tokens_bf16(seed, tv, T, G, D, s, 0, p + n)
+        hq = gi.host_normal_bf16(seed, tq, n * HQ * D, 1.0, start=(s * T + p) * HQ * D).reshape(n, HQ, D)
+        for i in sorted(set([0, 1, 15, 16, n // 2, n - 1])):
+            if i < n:
+                H.assert_attn(go[int(row0[s]) + i], O.swa(hq[i], Kh, Vh, p + i, H.W), f"seq {s} token {p + i}")
+
+
 def test_decode_is_deterministic():
     a = H.run_dsa_decode(0xAA, [6000, 3001], topk=512, check_seqs=[])
     b = H.run_dsa_decode(0xAA, [6000, 3001], topk=512, check_seqs=[])
