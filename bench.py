@@ -441,6 +441,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-swa", action="store_true", help="skip the 3:1 layer mix and sliding-window prefill lines")
+    ap.add_argument("--swa-only", action="store_true",
+                    help="only the 3:1 layer mix and sliding-window prefill (for per-workload profiles)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
     ap.add_argument("--separate", action="store_true",
@@ -459,12 +461,15 @@ def main():
     torch.cuda.set_device(0)
     dsa.load()
 
+    if args.swa_only:
+        args.no_prefill, args.no_swa = True, False
     if args.profile_run:
-        step, keep = setup_decode(DECODE)
-        for _ in range(3):
-            step(cur_stream())
-        torch.cuda.synchronize()
-        del keep
+        if not args.swa_only:
+            step, keep = setup_decode(DECODE)
+            for _ in range(3):
+                step(cur_stream())
+            torch.cuda.synchronize()
+            del keep
         if not args.no_prefill:
             step, keep = setup_prefill(PREFILL)
             for _ in range(2):
@@ -489,7 +494,22 @@ def main():
         log("profile run done")
         return
 
-    # ---- decode at 1M
+    result = {} if args.swa_only else measure_decode(args)
+    # ---- prefill at 64K
+    if not args.no_prefill:
+        measure_prefill(args, result)
+    # ---- the 3:1 sliding-window / DSA stack (decode) and a sliding-window prefill chunk
+    if not args.no_swa:
+        measure_swa(args, result)
+    if not args.no_cpu and not args.swa_only:
+        result["cpu_baseline"] = cpu_baseline_decode(DECODE)
+        if "prefill" in result:
+            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(PREFILL)
+    print(json.dumps(result), flush=True)
+
+
+def measure_decode(args):
+    import torch
     step, keep = setup_decode(DECODE)
     DECODE["separate"] = args.separate
     kn = ["k_compress", "k_score_decode", "k_select", "k_sgqa_decode", "k_sgqa_merge"]
@@ -526,97 +546,94 @@ def main():
         "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in st.items()},
     }
     log(f"decode: {qps:.1f} q/s, {ms_step:.3f} ms/step, score kernel {achieved:.0f} GB/s")
+    return result
 
-    # ---- prefill at 64K
-    if not args.no_prefill:
-        step, keep = setup_prefill(PREFILL)
-        kp = ["k_compress", "k_score_prefill", "k_select", "k_sgqa_prefill", "k_sgqa_merge"]
-        psteps = max(3, args.steps // 3)
-        psecs, peager, pst = timed(step, psteps, max(1, args.warmup // 2), kp, graph=args.graph)
-        del keep
-        torch.cuda.empty_cache()
-        n = PREFILL["chunk"]
-        fl = prefill_flops(PREFILL["prefix"], n, PREFILL["topk"])
-        pms = psecs * 1e3 / psteps
-        att_ms, sc_ms, mg_ms = pst["k_sgqa_prefill"][0], pst["k_score_prefill"][0], pst["k_sgqa_merge"][0]
-        att_tf = fl["attend"] / (att_ms * 1e-3) / 1e12
-        sc_tf = fl["score"] / (sc_ms * 1e-3) / 1e12
-        step_tf = fl["total"] / (pms * 1e-3) / 1e12
-        result["prefill"] = {
-            "workload": PREFILL["name"], "value": round(n * psteps / psecs, 1), "unit": "tokens/s",
-            "steps": psteps, "ms_per_step": round(pms, 3), "eager_ms_per_step": round(peager * 1e3 / psteps, 3),
-            "roofline": {"bound": "mfma", "kernel": "k_sgqa_prefill", "achieved": round(att_tf, 2),
-                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": load_traffic("k_sgqa_prefill", "prefill_64k", source_hash("attention.hip")),
-                         "algorithmic_flops_per_launch": fl["attend"], "avg_launch_us": round(att_ms * 1e3, 1)},
-            "attention_with_merge": {
-                "kernels": ["k_sgqa_prefill", "k_sgqa_merge"],
-                "achieved_TFLOPs": round(fl["attend"] / ((att_ms + mg_ms) * 1e-3) / 1e12, 2),
-                "frac": round(fl["attend"] / ((att_ms + mg_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "gathered_kv_bytes": fl["gather"],
-                "gather_GBs": round(fl["gather"] / (att_ms * 1e-3) / 1e9, 1)},
-            "score_kernel": {"kernel": "k_score_prefill", "achieved_TFLOPs": round(sc_tf, 2),
-                             "frac": round(sc_tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl["score"],
-                             "avg_launch_us": round(sc_ms * 1e3, 1)},
-            "step_mfma": {"algorithmic_flops": fl["total"], "achieved_TFLOPs": round(step_tf, 2),
-                          "frac": round(step_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
-            "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in pst.items()},
-        }
-        log(f"prefill: {n * psteps / psecs:.0f} tok/s, {pms:.3f} ms/step")
 
-    # ---- the 3:1 sliding-window / DSA stack (decode) and a sliding-window prefill chunk
-    if not args.no_swa:
-        step, keep = setup_mix(MIX)
-        km = ["k_swa_stage", "k_swa_attend", "k_ring_append", "k_score_decode", "k_select", "k_sgqa_decode",
-              "k_sgqa_merge"]
-        msteps = max(3, args.steps // 3)
-        msecs, meager, mst = timed(step, msteps, max(1, args.warmup // 2), km, graph=args.graph)
-        del keep
-        torch.cuda.empty_cache()
-        B, Lc = MIX["batch"], MIX["context"]
-        mms = msecs * 1e3 / msteps
-        sbytes = swa_decode_bytes(B)
-        dbytes = decode_bytes(B, Lc, MIX["topk"])["total"]
-        tot = MIX["swa_layers"] * sbytes + dbytes
-        swa_us = sum(mst[k][0] for k in ("k_swa_stage", "k_swa_attend", "k_ring_append")) * 1e3  # per layer
-        result["mix_decode"] = {
-            "workload": MIX["name"], "value": round(B * msteps / msecs, 1), "unit": "queries/s (4-layer stack)",
-            "steps": msteps, "ms_per_step": round(mms, 4), "eager_ms_per_step": round(meager * 1e3 / msteps, 4),
-            "roofline": {"bound": "hbm", "kernel": "whole stack", "achieved": round(tot / (mms * 1e-3) / 1e9, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(tot / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes_per_step": tot},
-            "swa_layer": {"algorithmic_bytes": sbytes, "us_per_layer": round(swa_us, 2),
-                          "achieved_GBs": round(sbytes / (swa_us * 1e-6) / 1e9, 1)},
-            "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in mst.items()},
-        }
-        log(f"mix decode: {B * msteps / msecs:.0f} q/s, {mms:.3f} ms/step")
-        step, keep = setup_swa_prefill(SWA_PREFILL)
-        ks = ["k_swa_stage", "k_swa_attend", "k_ring_append"]
-        ssteps = max(3, args.steps // 3)
-        ssecs, seager, sst = timed(step, ssteps, max(1, args.warmup // 2), ks, graph=args.graph)
-        del keep
-        torch.cuda.empty_cache()
-        n = SWA_PREFILL["chunk"]
-        fl = swa_prefill_flops(SWA_PREFILL["prefix"], n)
-        sms = ssecs * 1e3 / ssteps
-        att_ms = sst["k_swa_attend"][0]
-        result["swa_prefill"] = {
-            "workload": SWA_PREFILL["name"], "value": round(n * ssteps / ssecs, 1), "unit": "tokens/s",
-            "steps": ssteps, "ms_per_step": round(sms, 4), "eager_ms_per_step": round(seager * 1e3 / ssteps, 4),
-            "roofline": {"bound": "mfma", "kernel": "k_swa_attend",
-                         "achieved": round(fl / (att_ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(fl / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "algorithmic_flops_per_launch": fl, "avg_launch_us": round(att_ms * 1e3, 1)},
-            "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in sst.items()},
-        }
-        log(f"swa prefill: {n * ssteps / ssecs:.0f} tok/s, {sms:.3f} ms/step")
+def measure_prefill(args, result):
+    import torch
+    step, keep = setup_prefill(PREFILL)
+    kp = ["k_compress", "k_score_prefill", "k_select", "k_sgqa_prefill", "k_sgqa_merge"]
+    psteps = max(3, args.steps // 3)
+    psecs, peager, pst = timed(step, psteps, max(1, args.warmup // 2), kp, graph=args.graph)
+    del keep
+    torch.cuda.empty_cache()
+    n = PREFILL["chunk"]
+    fl = prefill_flops(PREFILL["prefix"], n, PREFILL["topk"])
+    pms = psecs * 1e3 / psteps
+    att_ms, sc_ms, mg_ms = pst["k_sgqa_prefill"][0], pst["k_score_prefill"][0], pst["k_sgqa_merge"][0]
+    att_tf = fl["attend"] / (att_ms * 1e-3) / 1e12
+    sc_tf = fl["score"] / (sc_ms * 1e-3) / 1e12
+    step_tf = fl["total"] / (pms * 1e-3) / 1e12
+    result["prefill"] = {
+        "workload": PREFILL["name"], "value": round(n * psteps / psecs, 1), "unit": "tokens/s",
+        "steps": psteps, "ms_per_step": round(pms, 3), "eager_ms_per_step": round(peager * 1e3 / psteps, 3),
+        "roofline": {"bound": "mfma", "kernel": "k_sgqa_prefill", "achieved": round(att_tf, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic("k_sgqa_prefill", "prefill_64k", source_hash("attention.hip")),
+                     "algorithmic_flops_per_launch": fl["attend"], "avg_launch_us": round(att_ms * 1e3, 1)},
+        "attention_with_merge": {
+            "kernels": ["k_sgqa_prefill", "k_sgqa_merge"],
+            "achieved_TFLOPs": round(fl["attend"] / ((att_ms + mg_ms) * 1e-3) / 1e12, 2),
+            "frac": round(fl["attend"] / ((att_ms + mg_ms) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "gathered_kv_bytes": fl["gather"],
+            "gather_GBs": round(fl["gather"] / (att_ms * 1e-3) / 1e9, 1)},
+        "score_kernel": {"kernel": "k_score_prefill", "achieved_TFLOPs": round(sc_tf, 2),
+                         "frac": round(sc_tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl["score"],
+                         "avg_launch_us": round(sc_ms * 1e3, 1)},
+        "step_mfma": {"algorithmic_flops": fl["total"], "achieved_TFLOPs": round(step_tf, 2),
+                      "frac": round(step_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in pst.items()},
+    }
+    log(f"prefill: {n * psteps / psecs:.0f} tok/s, {pms:.3f} ms/step")
 
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline_decode(DECODE)
-        if "prefill" in result:
-            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(PREFILL)
-    print(json.dumps(result), flush=True)
+
+def measure_swa(args, result):
+    import torch
+    step, keep = setup_mix(MIX)
+    km = ["k_swa_stage", "k_swa_attend", "k_ring_append", "k_score_decode", "k_select", "k_sgqa_decode",
+          "k_sgqa_merge"]
+    msteps = max(3, args.steps // 3)
+    msecs, meager, mst = timed(step, msteps, max(1, args.warmup // 2), km, graph=args.graph)
+    del keep
+    torch.cuda.empty_cache()
+    B, Lc = MIX["batch"], MIX["context"]
+    mms = msecs * 1e3 / msteps
+    sbytes = swa_decode_bytes(B)
+    dbytes = decode_bytes(B, Lc, MIX["topk"])["total"]
+    tot = MIX["swa_layers"] * sbytes + dbytes
+    swa_us = sum(mst[k][0] for k in ("k_swa_stage", "k_swa_attend", "k_ring_append")) * 1e3  # per layer
+    result["mix_decode"] = {
+        "workload": MIX["name"], "value": round(B * msteps / msecs, 1), "unit": "queries/s (4-layer stack)",
+        "steps": msteps, "ms_per_step": round(mms, 4), "eager_ms_per_step": round(meager * 1e3 / msteps, 4),
+        "roofline": {"bound": "hbm", "kernel": "whole stack", "achieved": round(tot / (mms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(tot / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_step": tot},
+        "swa_layer": {"algorithmic_bytes": sbytes, "us_per_layer": round(swa_us, 2),
+                      "achieved_GBs": round(sbytes / (swa_us * 1e-6) / 1e9, 1)},
+        "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in mst.items()},
+    }
+    log(f"mix decode: {B * msteps / msecs:.0f} q/s, {mms:.3f} ms/step")
+    step, keep = setup_swa_prefill(SWA_PREFILL)
+    ks = ["k_swa_stage", "k_swa_attend", "k_ring_append"]
+    ssteps = max(3, args.steps // 3)
+    ssecs, seager, sst = timed(step, ssteps, max(1, args.warmup // 2), ks, graph=args.graph)
+    del keep
+    torch.cuda.empty_cache()
+    n = SWA_PREFILL["chunk"]
+    fl = swa_prefill_flops(SWA_PREFILL["prefix"], n)
+    sms = ssecs * 1e3 / ssteps
+    att_ms = sst["k_swa_attend"][0]
+    result["swa_prefill"] = {
+        "workload": SWA_PREFILL["name"], "value": round(n * ssteps / ssecs, 1), "unit": "tokens/s",
+        "steps": ssteps, "ms_per_step": round(sms, 4), "eager_ms_per_step": round(seager * 1e3 / ssteps, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_swa_attend",
+                     "achieved": round(fl / (att_ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fl / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_launch": fl, "avg_launch_us": round(att_ms * 1e3, 1)},
+        "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in sst.items()},
+    }
+    log(f"swa prefill: {n * ssteps / ssecs:.0f} tok/s, {sms:.3f} ms/step")
 
 
 if __name__ == "__main__":
