@@ -85,6 +85,13 @@ def test_decode_1m_context_batch_of_4():
     H.assert_decode_parity(r)
 
 
+def test_decode_layer_mix_shape_batch_8_at_256k():
+    """The DSA layer of the 3:1 layer-mix workload as the benchmark times it: batch 8 at 262,144
+    tokens (2,048 tiles per problem); sequences 0 and 7 are checked against the oracle."""
+    r = H.run_dsa_decode(0xDA, [262144] * 8, topk=512, check_seqs=[0, 7])
+    H.assert_decode_parity(r)
+
+
 def test_decode_beyond_tile_capacity_uses_radix_fallback():
     """More than 8,192 tiles of 16 regions (a context just over 1M tokens): exact selection by radix
     narrowing over the scores in global memory."""
@@ -324,6 +331,14 @@ def test_prefill_short_chunk_uses_decode_tiling():
 @pytest.mark.parametrize("chunks", [[530, 40, 1], [1, 1, 1, 600], [700, 513, 3]])
 def test_swa_chunks_and_decode(chunks):
     H.check_swa_sequence(0xF0 + sum(chunks), chunks, check_from=0, sample=48)
+
+
+def test_swa_prefill_chunk_at_64k_sampled():
+    """The sliding-window prefill workload as the benchmark times it: a 2048-token chunk after
+    63,488 tokens (the prefix itself is run as one chunk first to fill the ring); 24 sampled
+    queries of the timed chunk are checked."""
+    worst = H.check_swa_sequence(0xF8, [63488, 2048], check_from=1, sample=24)
+    print(f"swa 64K chunk: worst max abs {worst[0]:.3e}, rel rms {worst[1]:.3e}")
 
 
 def test_swa_batched_decode_with_prefilled_rings():
