@@ -66,6 +66,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Workgroup barrier for hand-offs through LDS only: waits for this wave's LDS
+// operations, but not for its global loads still in flight, which
+// __syncthreads() (a workgroup fence) would drain first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Max / sum of x over lanes l, l^16, l^32 and l^48 of the wave with gfx950's
 // row swaps (each leaves lane l holding x_l and x_{l^16}, or x_l and
 // x_{l^32}, in its two results): VALU only, no LDS round trip.

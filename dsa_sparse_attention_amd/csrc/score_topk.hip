@@ -1010,12 +1010,12 @@ __global__ __launch_bounds__(256) void k_fold_compress(SelectArgs a) {
 
 constexpr int kDecNT = 1024;
 constexpr int kDecTilesPT = 8;                          // tile keys per thread (8192 tiles)
-constexpr int kDecCandPT = kCandCap * kTile / kDecNT;   // candidate slots per thread
+static_assert(kDecTilesPT * (kDecNT / 64) + 1 >= 2 * (kDecNT / 64 + 1), "table holds both passes");
 
 struct alignas(16) DecSmem {
   uint32_t wtot[kDecNT / 64];
   uint32_t res[4];
-  uint32_t tab[2 * (kDecCandPT * (kDecNT / 64) + 1)];
+  uint32_t tab[kDecTilesPT * (kDecNT / 64) + 1];  // ordered positions of the tiles, then of the final pass
   union {
     int32_t tiles[kCandCap];  // kept tiles (step 2)
     uint32_t hh[1024];        // 10-bit digit histogram of the finishing wave (step 3)
@@ -1023,6 +1023,7 @@ struct alignas(16) DecSmem {
   uint32_t ck[kCandCap];      // candidate keys, index order
   int32_t ci[kCandCap];       // candidate regions
   uint32_t kin[kCandCap];     // keys in the level-0 digit, any order
+  uint32_t stage[kTile][kDecNT];  // each thread's 16 tile keys (a column per thread)
 };
 
 // One wave: the digit (of `bits` bits at `shift`) holding the rem-th largest
@@ -1089,43 +1090,59 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     if (fq < a.nq) folded_compress(a, fq, w % kGroups);
     return;
   }
-  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
-  const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
-  int32_t* sel = a.sel + pq * a.topk;
+  // Every load that needs only the block index is issued before any of them
+  // is waited for: the query's position first (so that waiting for it leaves
+  // the others in flight), then the hint and the tile maxima.
+  const int32_t qraw = *(a.qpos ? a.qpos + qi : a.slen + qi);  // (one load, no branch)
   // The histogram is only a hint for the level-0 digit: it is read here and
-  // cleared for the next call on this workspace, and the digit is checked
-  // against exact counts below.  Thread t holds digits 4095-4t..4092-4t.
+  // cleared for the next call on this workspace at every exit (global stores
+  // issued before a barrier would make the barrier wait for them), and the
+  // digit is checked against exact counts below.  Thread t holds digits
+  // 4095-4t..4092-4t.
   u32x4 h = {0u, 0u, 0u, 0u};
-  {
-    uint32_t* gh = a.hist + pq * kHistCopies * kHistBins + (kHistBins - 4 - 4 * tid);
+  uint32_t* const gh = a.hist + pq * kHistCopies * kHistBins + (kHistBins - 4 - 4 * tid);
 #pragma unroll
-    for (int k = 0; k < kHistCopies; ++k) h += *(const u32x4*)(gh + k * kHistBins);
-#pragma unroll
-    for (int k = 0; k < kHistCopies; ++k) *(u32x4*)(gh + k * kHistBins) = u32x4{0u, 0u, 0u, 0u};
-  }
-  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kDecNT)) return;
-  const int64_t ntiles = (c + kTile - 1) / kTile;
-  if (ntiles > (int64_t)kDecNT * kDecTilesPT) {
-    select_fallback<kDecNT>(a, pq);
-    return;
-  }
+  for (int k = 0; k < kHistCopies; ++k) h += *(const u32x4*)(gh + k * kHistBins);
+  // every tile maximum the block can hold, loaded with the hint (they do not
+  // wait for the query's position; tiles past the problem are masked below)
   const uint32_t* tm = a.tilemax + pq * a.tm_stride;
   uint32_t tk[kDecTilesPT];
 #pragma unroll
   for (int e = 0; e < kDecTilesPT; ++e) {
     const int64_t j = (int64_t)e * kDecNT + tid;
-    tk[e] = tm[j < ntiles ? j : 0];
+    tk[e] = tm[j < a.tm_stride ? j : 0];
   }
-#pragma unroll
-  for (int e = 0; e < kDecTilesPT; ++e)
-    if ((int64_t)e * kDecNT + tid >= ntiles) tk[e] = 0u;
-  // 1. level-0 digit from the histogram
+#define DSA_CLEAR_HINT()                                                                  \
+  do {                                                                                    \
+    _Pragma("unroll") for (int k = 0; k < kHistCopies; ++k) *(u32x4*)(gh + k * kHistBins) = \
+        u32x4{0u, 0u, 0u, 0u};                                                            \
+  } while (0)
+  // 1. level-0 digit from the histogram: the hint's wave totals go to LDS
+  // before anything depends on the position, so the loads above stay issued
+  // together (the LDS barrier keeps them before it and does not wait for the
+  // tile maxima)
   const uint32_t cnt[4] = {h.w, h.z, h.y, h.x};
   const uint32_t mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
   const uint32_t wi = wave_incl_scan(mine);
   if (lane == 63) sm.wtot[w] = wi;
   if (tid == 0) sm.res[0] = 0xFFFFFFFFu;
-  __syncthreads();
+  lds_barrier();
+  const int64_t c = current_region(a.qpos ? qraw : qraw - 1, a.R, a.max_regions);
+  const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
+  int32_t* sel = a.sel + pq * a.topk;
+  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kDecNT)) {
+    DSA_CLEAR_HINT();
+    return;
+  }
+  const int64_t ntiles = (c + kTile - 1) / kTile;
+  if (ntiles > (int64_t)kDecNT * kDecTilesPT) {
+    DSA_CLEAR_HINT();
+    select_fallback<kDecNT>(a, pq);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < kDecTilesPT; ++e)
+    if ((int64_t)e * kDecNT + tid >= ntiles) tk[e] = 0u;
   uint32_t run = wi - mine;
 #pragma unroll
   for (int i = 0; i < kDecNT / 256; ++i) {
@@ -1142,9 +1159,10 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     }
     run += cnt[j];
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t d = sm.res[0], above_h = sm.res[1], inbin_h = sm.res[2];
   if (d == 0xFFFFFFFFu || above_h + inbin_h > (uint32_t)kCandCap) {
+    DSA_CLEAR_HINT();
     select_fallback<kDecNT>(a, pq);
     return;
   }
@@ -1162,55 +1180,75 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   }
   const uint32_t ntl_all = sm.tab[kDecTilesPT * (kDecNT / 64)];
   const uint32_t ntl = min(ntl_all, (uint32_t)kCandCap);
-  __syncthreads();
+  lds_barrier();
+  // One kept tile per thread (ntl <= kCandCap == kDecNT): its 16 scores in
+  // one 64-byte row, the candidates among them (and those inside digit d)
+  // counted, a block scan of the counts in thread order (= index order), and
+  // the candidates written to LDS in index order.
+  static_assert(kCandCap == kDecNT, "one kept tile per thread");
   uint32_t ncand, nin;
   {
-    const float* sc = a.scores + pq * a.ws_stride;
-    const uint32_t m = ntl * kTile;
-    uint32_t ck[kDecCandPT], pos[kDecCandPT];
-    int32_t ci[kDecCandPT];
-    bool f[kDecCandPT];
-    float v[kDecCandPT];
-    // unconditional loads (clamped index) so that all of them are in flight at once
+    const bool have = (uint32_t)tid < ntl;
+    const int64_t t = have ? sm.tiles[tid] : 0;
+    const u32x4* tp = (const u32x4*)(a.scores + pq * a.ws_stride + t * kTile);
+    u32x4 q4[4];
 #pragma unroll
-    for (int e = 0; e < kDecCandPT; ++e) {
-      const uint32_t i = (uint32_t)e * kDecNT + tid;
-      const int64_t r = (int64_t)sm.tiles[i < m ? i / kTile : 0] * kTile + (i % kTile);
-      ci[e] = (int32_t)r;
-      v[e] = sc[r < c ? r : 0];
+    for (int j = 0; j < 4; ++j) q4[j] = tp[j];
+    uint32_t key[kTile], fa = 0u, fb = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      key[4 * j + 0] = score_key(__uint_as_float(q4[j].x));
+      key[4 * j + 1] = score_key(__uint_as_float(q4[j].y));
+      key[4 * j + 2] = score_key(__uint_as_float(q4[j].z));
+      key[4 * j + 3] = score_key(__uint_as_float(q4[j].w));
     }
-    bool fin[kDecCandPT];
-    uint32_t pin[kDecCandPT];
 #pragma unroll
-    for (int e = 0; e < kDecCandPT; ++e) {
-      const uint32_t i = (uint32_t)e * kDecNT + tid;
-      const bool ok = i < m && ci[e] < c;
-      ck[e] = ok ? score_key(v[e]) : 0u;
-      f[e] = ok && ck[e] >= Tlo;
-      fin[e] = f[e] && (ck[e] >> 20) == d;
+    for (int i = 0; i < kTile; ++i) sm.stage[i][tid] = key[i];
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) {
+      const bool ok = have && t * kTile + i < c && key[i] >= Tlo;
+      fa |= (ok ? 1u : 0u) << i;
+      fb |= (ok && (key[i] >> 20) == d ? 1u : 0u) << i;
     }
-    ordered_positions2<kDecNT, kDecCandPT>(f, fin, pos, pin, sm.tab, &ncand, &nin);
+    // both counts in one word: each total is at most 16 * kDecNT < 2^16
+    const uint32_t packed = ((uint32_t)__popc(fa) << 16) | (uint32_t)__popc(fb);
+    const uint32_t incl = wave_incl_scan(packed);
+    if (lane == 63) sm.wtot[w] = incl;
+    lds_barrier();
+    uint32_t base = incl - packed, total = 0;
 #pragma unroll
-    for (int e = 0; e < kDecCandPT; ++e) {
-      if (f[e] && pos[e] < (uint32_t)kCandCap) {
-        sm.ck[pos[e]] = ck[e];
-        sm.ci[pos[e]] = ci[e];
+    for (int i = 0; i < kDecNT / 256; ++i) {
+      const u32x4 v = *(const u32x4*)&sm.wtot[4 * i];
+      base += (4 * i < w ? v.x : 0u) + (4 * i + 1 < w ? v.y : 0u) + (4 * i + 2 < w ? v.z : 0u) +
+              (4 * i + 3 < w ? v.w : 0u);
+      total += v.x + v.y + v.z + v.w;
+    }
+    ncand = total >> 16;
+    nin = total & 0xFFFFu;
+    // the thread's keys go through its own LDS column so that the loop over
+    // its candidates (about one) can index them
+    uint32_t oa = base >> 16, ob = base & 0xFFFFu;
+    for (uint32_t m = fa; m; m &= m - 1u, ++oa) {
+      const int i = __ffs((int)m) - 1;
+      const uint32_t k = sm.stage[i][tid];
+      if (oa < (uint32_t)kCandCap) {
+        sm.ck[oa] = k;
+        sm.ci[oa] = (int32_t)(t * kTile + i);
       }
-      if (fin[e] && pin[e] < (uint32_t)kCandCap) sm.kin[pin[e]] = ck[e];
+      if ((fb >> i) & 1u) {
+        if (ob < (uint32_t)kCandCap) sm.kin[ob] = k;
+        ++ob;
+      }
     }
   }
   // exact check of the digit: ncand keys are >= Tlo and nin of them in digit d
   const uint32_t above = ncand - nin;
   if (ntl_all > (uint32_t)kCandCap || ncand > (uint32_t)kCandCap || above >= need || ncand < need) {
+    DSA_CLEAR_HINT();
     select_fallback<kDecNT>(a, pq);
     return;
   }
-  for (int i = (int)need + 1 + tid; i < a.topk; i += kDecNT) sel[i] = -1;
-  if (tid == 0) {
-    sel[need] = (int32_t)c;
-    a.nsel[pq] = (int32_t)need + 1;
-  }
-  __syncthreads();
+  lds_barrier();
   // 3. wave 0: the need-th largest key T lies in digit d; its next 10 bits,
   // then its last 10, from histograms of the in-digit keys
   const uint32_t M = min(ncand, (uint32_t)kCandCap);
@@ -1237,6 +1275,15 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   if (fg[0]) pos = pg[0] + (pe[0] < need_eq ? pe[0] : need_eq);
   else if (fe[0] && pe[0] < need_eq) pos = pg[0] + pe[0];
   if (pos < need) sel[pos] = sm.ci[tid];
+  // the forced current region, the padding and the count (after the last
+  // barrier, like the hint's clearing)
+  for (int i = (int)need + 1 + tid; i < a.topk; i += kDecNT) sel[i] = -1;
+  if (tid == 0) {
+    sel[need] = (int32_t)c;
+    a.nsel[pq] = (int32_t)need + 1;
+  }
+  DSA_CLEAR_HINT();
+#undef DSA_CLEAR_HINT
 }
 
 
