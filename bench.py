@@ -186,6 +186,125 @@ def setup_decode(cfg, steps_hint=1):
     return step, keep
 
 
+PAGE = 128  # positions per page of the paged caches
+PAGE_ELEMS = {"k": 16 * 1536, "v": 16 * 1536, "ik": PAGE * P, "summ": 4096, "scale": 16}  # per (page, group)
+
+
+def to_pools(tensors, n_seqs, tcap, seed, n_extra=64, order="interleaved"):
+    """Copies contiguous caches into paged pools of n_seqs*pages + n_extra pages.  order "interleaved":
+    page ids in the order a serving cache hands them out when the sequences of a batch grow together
+    (page n of sequence s is id n*n_seqs + s); "shuffled": random distinct ids (a cache after heavy
+    churn, the worst case for locality).  Returns (pools, Pages)."""
+    import numpy as np
+    import torch
+    import dsa_sparse_attention_amd as dsa
+    npg = tcap // PAGE
+    n_pages = n_seqs * npg + n_extra
+    if order == "shuffled":
+        ids = np.random.default_rng(seed).permutation(n_pages)[:n_seqs * npg].reshape(n_seqs, npg)
+    else:
+        ids = (np.arange(npg)[None, :] * n_seqs + np.arange(n_seqs)[:, None]).astype(np.int64)
+    bt = torch.tensor(ids, dtype=torch.int32, device="cuda")
+    pools = dsa.paged_pools(n_pages, index_k="ik" in tensors)
+    idx = bt.reshape(-1).long()
+    for name, t in tensors.items():
+        per = PAGE_ELEMS[name]
+        src = t.view(n_seqs, G, npg, per).permute(0, 2, 1, 3).reshape(n_seqs * npg, G * per)
+        pools[name].view(-1, G * per)[idx] = src
+        del src
+    torch.cuda.synchronize()
+    return pools, dsa.Pages(bt, n_pages)
+
+
+def paged_decode(cfg, order="interleaved"):
+    """The decode workload with every cache of the layer in 128-position pages
+    (dsa_decode_step_paged)."""
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+    _, keep = setup_decode(cfg)
+    ik, K, V, q, iq, z, summ, scale = keep[:8]
+    slen, sel, nsel, out = keep[12], keep[13], keep[14], keep[15]
+    B, tcap = cfg["batch"], cfg["context"]
+    R = tcap // REG
+    pools, pages = to_pools(dict(ik=ik, k=K, v=V, summ=summ, scale=scale), B, tcap, gi.SEED_BASE + 99, order=order)
+    del keep, ik, K, V, summ, scale
+    torch.cuda.empty_cache()
+    geom = dsa.geometry(topk=cfg["topk"])
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(geom, B, R))
+    L = dsa.load()
+    p = Calls.p
+    args = (ctypes.byref(geom), B, p(q), p(iq), p(z), ctypes.byref(pages.struct), p(pools["ik"]), p(pools["k"]),
+            p(pools["v"]), p(slen), p(pools["summ"]), p(pools["scale"]), R, p(sel), p(nsel), p(out), p(ws), ws.numel())
+
+    def step(st):
+        rc = L.dsa_decode_step_paged(*args, st)
+        if rc:
+            raise RuntimeError(f"paged decode step failed: {rc} {L.dsa_last_error().decode()}")
+
+    return step, (pools, pages, q, iq, z, slen, sel, nsel, out, ws, geom)
+
+
+def paged_prefill(cfg, order="interleaved"):
+    """The prefill workload over 128-position pages (compress, score_topk and sparse GQA through
+    their _paged entry points)."""
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+    _, keep = setup_prefill(cfg)
+    ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, sel, nsel, out = keep[:15]
+    P0, n, topk = cfg["prefix"], cfg["chunk"], cfg["topk"]
+    tcap = P0 + n
+    R = tcap // REG
+    pools, pages = to_pools(dict(ik=ik, k=K, v=V, summ=summ, scale=scale), 1, tcap, gi.SEED_BASE + 98, order=order)
+    del keep, ik, K, V, summ, scale
+    torch.cuda.empty_cache()
+    geom = dsa.geometry(topk=topk)
+    ws1 = dsa.workspace(dsa.dsa_score_topk_workspace_size(geom, n, R))
+    ws3 = dsa.workspace(dsa.dsa_sparse_gqa_prefill_workspace_size(geom, n))
+    L = dsa.load()
+    p = Calls.p
+    gp, pt = ctypes.byref(geom), ctypes.byref(pages.struct)
+    a_comp = (gp, 1, pt, p(pools["ik"]), p(rb), p(re_), tcap // REG - P0 // REG, p(pools["summ"]), p(pools["scale"]))
+    a_score = (gp, n, p(iq), p(z), p(qseq), p(qpos), 1, pt, p(pools["summ"]), p(pools["scale"]), R, p(sel), p(nsel),
+               None, p(ws1), ws1.numel())
+    a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, pt, p(pools["k"]), p(pools["v"]), p(sel), p(nsel), p(out), p(ws3),
+              ws3.numel())
+
+    def step(st):
+        rc = (L.dsa_compress_regions_paged(*a_comp, st) or L.dsa_score_topk_paged(*a_score, st)
+              or L.dsa_sparse_gqa_prefill_paged(*a_attn, st))
+        if rc:
+            raise RuntimeError(f"paged prefill step failed: {rc} {L.dsa_last_error().decode()}")
+
+    return step, (pools, pages, q, iq, z, rb, re_, qseq, qpos, sel, nsel, out, ws1, ws3, geom)
+
+
+def measure_paged(args, result):
+    """Both headline workloads again with the caches in 128-position pages handed out in batch
+    order, and the decode step once more with shuffled pages: the cost of the block-table
+    indirection."""
+    import torch
+    res = {}
+    for key, setup, cfg, unit_n, order in (("decode", paged_decode, DECODE, DECODE["batch"], "interleaved"),
+                                           ("decode_shuffled", paged_decode, DECODE, DECODE["batch"], "shuffled"),
+                                           ("prefill", paged_prefill, PREFILL, PREFILL["chunk"], "interleaved")):
+        if key == "prefill" and args.no_prefill:
+            continue
+        step, keep = setup(cfg, order)
+        steps = args.steps if key == "decode" else max(3, args.steps // 3)
+        secs, eager, _ = timed(step, steps, max(1, args.warmup // 2), [], graph=args.graph)
+        del keep
+        torch.cuda.empty_cache()
+        ms = secs * 1e3 / steps
+        base = result.get("ms_per_step") if key != "prefill" else result.get("prefill", {}).get("ms_per_step")
+        res[key] = {"workload": cfg["name"] + f", caches in 128-position pages ({order} page ids)",
+                    "value": round(unit_n * steps / secs, 1), "unit": "queries/s" if key == "decode" else "tokens/s",
+                    "ms_per_step": round(ms, 4), "vs_contiguous": round(base / ms, 4) if base else None}
+        log(f"paged {key}: {unit_n * steps / secs:.0f}/s, {ms:.3f} ms/step")
+    result["paged"] = res
+
+
 def setup_prefill(cfg):
     import torch
     import dsa_inputs as gi
@@ -444,6 +563,7 @@ def main():
     ap.add_argument("--swa-only", action="store_true",
                     help="only the 3:1 layer mix and sliding-window prefill (for per-workload profiles)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache runs of the two headline workloads")
     ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
     ap.add_argument("--separate", action="store_true",
                     help="decode step as three calls (compress, score_topk, sparse_gqa_decode) instead of dsa_decode_step")
@@ -498,6 +618,9 @@ def main():
     # ---- prefill at 64K
     if not args.no_prefill:
         measure_prefill(args, result)
+    # ---- the same two workloads over paged caches
+    if not args.no_paged and not args.swa_only:
+        measure_paged(args, result)
     # ---- the 3:1 sliding-window / DSA stack (decode) and a sliding-window prefill chunk
     if not args.no_swa:
         measure_swa(args, result)

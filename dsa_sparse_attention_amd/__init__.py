@@ -30,6 +30,8 @@ ENTRY_POINTS = [
     "dsa_decode_step_workspace_size", "dsa_decode_step",
     "swa_attention_workspace_size", "swa_attention", "swa_ring_append",
     "dsa_profile_enable", "dsa_profile_kernel_stats",
+    "dsa_cache_write_paged", "dsa_compress_regions_paged", "dsa_score_topk_paged", "dsa_sparse_gqa_decode_paged",
+    "dsa_sparse_gqa_prefill_paged", "dsa_decode_step_paged",
 ]
 
 
@@ -44,6 +46,40 @@ class Geometry(ctypes.Structure):
                 ("n_groups", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class PageTable(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+
+
+PAGE_POSITIONS = 128  # positions per page of the paged caches (16 regions, one summary tile)
+
+
+class Pages:
+    """A block table [n_seqs][max_pages] int32 on the device plus the pool size; keeps the tensor alive
+    for as long as the C struct that points at it."""
+
+    def __init__(self, block_table: torch.Tensor, n_pages: int):
+        if block_table.dim() != 2 or block_table.dtype != torch.int32:
+            raise TypeError("block_table must be a 2-D int32 tensor [n_seqs][max_pages]")
+        self.table = block_table.contiguous()
+        self.n_seqs, self.max_pages = self.table.shape
+        self.n_pages = int(n_pages)
+        self.struct = PageTable(ctypes.c_void_p(self.table.data_ptr()), self.max_pages, self.n_pages)
+
+    @property
+    def tcap(self) -> int:
+        return self.max_pages * PAGE_POSITIONS
+
+
+def paged_pools(n_pages: int, device="cuda", index_k: bool = True):
+    """Zero-filled pools of n_pages pages in the documented paged layouts."""
+    z = lambda n, dt: torch.zeros(n, dtype=dt, device=device)
+    per = PAGE_POSITIONS * GROUPS
+    return {"k": z(n_pages * per * HEAD_DIM, torch.bfloat16), "v": z(n_pages * per * HEAD_DIM, torch.bfloat16),
+            "ik": z(n_pages * per * PROXY, torch.bfloat16) if index_k else None,
+            "summ": z(n_pages * GROUPS * 4096, torch.uint8),
+            "scale": z(n_pages * GROUPS * (PAGE_POSITIONS // REGION), torch.float32)}
 
 
 _lib = None
@@ -81,6 +117,13 @@ def load() -> ctypes.CDLL:
     L.swa_attention_workspace_size.restype = sz
     L.swa_attention.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.swa_ring_append.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    P = ctypes.POINTER(PageTable)
+    L.dsa_cache_write_paged.argtypes = [G, i32, vp, vp, vp, vp, vp, P, i32, vp, vp, vp, vp]
+    L.dsa_compress_regions_paged.argtypes = [G, i32, P, vp, vp, vp, i32, vp, vp, vp]
+    L.dsa_score_topk_paged.argtypes = [G, i32, vp, vp, vp, vp, i32, P, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_gqa_decode_paged.argtypes = [G, i32, vp, P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_gqa_prefill_paged.argtypes = [G, i32, vp, vp, vp, i32, P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_decode_step_paged.argtypes = [G, i32, vp, vp, vp, P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     L.dsa_profile_enable.argtypes = [ctypes.c_int]
     L.dsa_profile_kernel_stats.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int32)]
@@ -327,6 +370,142 @@ def swa_ring_append(geom, window, max_new_per_seq, seq_pos0, seq_row0, k_new, v_
     _check(load().swa_ring_append(ctypes.byref(geom), window, n_seqs, max_new_per_seq, _ptr(seq_pos0),
                                   _ptr(seq_row0), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
                                   _stream(stream)))
+
+
+# ---- paged caches ----------------------------------------------------------------------------
+def _pools_check(pages: Pages, k_pool, v_pool, ik_pool=None, summ_pool=None, scale_pool=None):
+    per = pages.n_pages * PAGE_POSITIONS * GROUPS
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool"), (ik_pool, "ik_pool")):
+        _dt(t, torch.bfloat16, nm)
+    _numel_at_least(k_pool, per * HEAD_DIM, "k_pool")
+    _numel_at_least(v_pool, per * HEAD_DIM, "v_pool")
+    _numel_at_least(ik_pool, per * PROXY, "ik_pool")
+    _dt(summ_pool, torch.uint8, "summ_pool")
+    _dt(scale_pool, torch.float32, "scale_pool")
+    _numel_at_least(summ_pool, pages.n_pages * GROUPS * 4096, "summ_pool")
+    _numel_at_least(scale_pool, pages.n_pages * GROUPS * (PAGE_POSITIONS // REGION), "scale_pool")
+
+
+def _pages(pages: Pages, n_seqs: int):
+    if pages.n_seqs < n_seqs:
+        raise ValueError(f"block table has {pages.n_seqs} rows, needs {n_seqs}")
+    if not pages.table.is_cuda:
+        raise ValueError("the block table must live on the GPU")
+    return ctypes.byref(pages.struct)
+
+
+def dsa_cache_write_paged(geom, tok_seq, tok_pos, k_new, v_new, ik_new, pages: Pages, n_seqs, k_pool, v_pool,
+                          ik_pool=None, stream=None):
+    n = tok_seq.numel()
+    for t, nm in ((tok_seq, "tok_seq"), (tok_pos, "tok_pos")):
+        _dt(t, torch.int32, nm)
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (ik_new, "ik_new")):
+        _dt(t, torch.bfloat16, nm)
+    _numel_at_least(k_new, n * GROUPS * HEAD_DIM, "k_new")
+    _numel_at_least(v_new, n * GROUPS * HEAD_DIM, "v_new")
+    _numel_at_least(ik_new, n * GROUPS * PROXY, "ik_new")
+    _pools_check(pages, k_pool, v_pool, ik_pool)
+    _check(load().dsa_cache_write_paged(ctypes.byref(geom), n, _ptr(tok_seq), _ptr(tok_pos), _ptr(k_new),
+                                        _ptr(v_new), _ptr(ik_new), _pages(pages, n_seqs), n_seqs, _ptr(k_pool),
+                                        _ptr(v_pool), _ptr(ik_pool), _stream(stream)))
+
+
+def dsa_compress_regions_paged(geom, pages: Pages, ik_pool, region_begin, region_end, max_span, summ_pool,
+                               scale_pool, stream=None):
+    batch = region_begin.numel()
+    _dt(region_begin, torch.int32, "region_begin")
+    _dt(region_end, torch.int32, "region_end")
+    _dt(ik_pool, torch.bfloat16, "ik_pool")
+    _numel_at_least(ik_pool, pages.n_pages * PAGE_POSITIONS * GROUPS * PROXY, "ik_pool")
+    _pools_check(pages, None, None, None, summ_pool, scale_pool)
+    _check(load().dsa_compress_regions_paged(ctypes.byref(geom), batch, _pages(pages, batch), _ptr(ik_pool),
+                                             _ptr(region_begin), _ptr(region_end), max_span, _ptr(summ_pool),
+                                             _ptr(scale_pool), _stream(stream)))
+
+
+def dsa_score_topk_paged(geom, index_q, z, q_seq, q_pos, n_seqs, pages: Pages, summ_pool, scale_pool, max_regions,
+                         sel, n_sel, scores_out=None, workspace=None, stream=None):
+    nq = q_seq.numel()
+    _dt(index_q, torch.bfloat16, "index_q")
+    _dt(z, torch.float32, "z")
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _dt(scores_out, torch.float32, "scores_out")
+    _numel_at_least(index_q, nq * IDX_HEADS * PROXY, "index_q")
+    _numel_at_least(z, nq * IDX_HEADS, "z")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _numel_at_least(scores_out, nq * GROUPS * max_regions, "scores_out")
+    _pools_check(pages, None, None, None, summ_pool, scale_pool)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_score_topk_workspace_size(geom, nq, max_regions), q_seq.device)
+    _check(load().dsa_score_topk_paged(ctypes.byref(geom), nq, _ptr(index_q), _ptr(z), _ptr(q_seq), _ptr(q_pos),
+                                       n_seqs, _pages(pages, n_seqs), _ptr(summ_pool), _ptr(scale_pool), max_regions,
+                                       _ptr(sel), _ptr(n_sel), _ptr(scores_out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+
+
+def dsa_sparse_gqa_decode_paged(geom, q, pages: Pages, k_pool, v_pool, seq_len, sel, n_sel, out, workspace=None,
+                                stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    _pools_check(pages, k_pool, v_pool)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_workspace_size(geom, batch), q.device)
+    _check(load().dsa_sparse_gqa_decode_paged(ctypes.byref(geom), batch, _ptr(q), _pages(pages, batch),
+                                              _ptr(k_pool), _ptr(v_pool), _ptr(seq_len), _ptr(sel), _ptr(n_sel),
+                                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dsa_sparse_gqa_prefill_paged(geom, q, q_seq, q_pos, n_seqs, pages: Pages, k_pool, v_pool, sel, n_sel, out,
+                                 workspace=None, stream=None):
+    nq = q_seq.numel()
+    for t, nm in ((q, "q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, nq * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, nq * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _pools_check(pages, k_pool, v_pool)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_prefill_workspace_size(geom, nq), q.device)
+    _check(load().dsa_sparse_gqa_prefill_paged(ctypes.byref(geom), nq, _ptr(q), _ptr(q_seq), _ptr(q_pos), n_seqs,
+                                               _pages(pages, n_seqs), _ptr(k_pool), _ptr(v_pool), _ptr(sel),
+                                               _ptr(n_sel), _ptr(out), _ptr(workspace), workspace.numel(),
+                                               _stream(stream)))
+
+
+def dsa_decode_step_paged(geom, q, index_q, z, pages: Pages, ik_pool, k_pool, v_pool, seq_len, summ_pool,
+                          scale_pool, max_regions, sel, n_sel, out, workspace=None, stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (index_q, "index_q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _dt(z, torch.float32, "z")
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(index_q, batch * IDX_HEADS * PROXY, "index_q")
+    _numel_at_least(z, batch * IDX_HEADS, "z")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    _pools_check(pages, k_pool, v_pool, ik_pool, summ_pool, scale_pool)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_decode_step_workspace_size(geom, batch, max_regions), q.device)
+    _check(load().dsa_decode_step_paged(ctypes.byref(geom), batch, _ptr(q), _ptr(index_q), _ptr(z),
+                                        _pages(pages, batch), _ptr(ik_pool), _ptr(k_pool), _ptr(v_pool),
+                                        _ptr(seq_len), _ptr(summ_pool), _ptr(scale_pool), max_regions, _ptr(sel),
+                                        _ptr(n_sel), _ptr(out), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)))
 
 
 def profile_enable(on: bool = True):

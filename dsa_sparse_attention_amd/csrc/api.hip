@@ -32,6 +32,19 @@ dsa_status check_geometry(const dsa_geometry* g) {
   return DSA_OK;
 }
 
+dsa_status paged_map(const char* who, const dsa_page_table* pt, CacheMap* m) {
+  if (!pt || !pt->block_table) return fail(DSA_ERR_INVALID_ARGUMENT, std::string(who) + ": page table or block table is NULL");
+  if (pt->max_pages <= 0 || pt->n_pages <= 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, std::string(who) + ": max_pages and n_pages must be positive");
+  if (pt->n_pages > kMaxPages || (int64_t)pt->max_pages * kPageRegions * kRegion > (int64_t)1 << 31)
+    return fail(DSA_ERR_UNSUPPORTED, std::string(who) + ": more than 2^25 pages or 2^31 positions per sequence");
+  m->bt = pt->block_table;
+  m->R = (int64_t)pt->max_pages * kPageRegions;
+  m->bt_stride = pt->max_pages;
+  m->n_pages = pt->n_pages;
+  return DSA_OK;
+}
+
 dsa_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)

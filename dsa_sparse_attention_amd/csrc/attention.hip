@@ -278,19 +278,21 @@ __device__ __forceinline__ void core_store(const CoreState& st, uint16_t* out, i
 }
 
 // Region r of a DSA cache (sequence/group bases given), valid up to position p.
-__device__ __forceinline__ Region dsa_region(const uint16_t* kbase, const uint16_t* vbase,
-                                             int32_t rid, int64_t p) {
+__device__ __forceinline__ Region dsa_region(const uint16_t* k, const uint16_t* v, int64_t slot, int32_t rid,
+                                             int64_t p) {
+  // region rid (its cache slot given) of a query at position p; ids outside
+  // [0, p/8] give an empty region at the start of the cache
   Region rg;
   const int64_t c = p / kRegion;
   if (rid < 0 || rid > c) {
-    rg.k = kbase;
-    rg.v = vbase;
+    rg.k = k;
+    rg.v = v;
     rg.lo = 1;
     rg.hi = 0;
     return rg;
   }
-  rg.k = kbase + (int64_t)rid * kRegion * kHeadDim;
-  rg.v = vbase + (int64_t)rid * kHeadDim * kRegion;
+  rg.k = k + slot * kRegionElems;
+  rg.v = v + slot * kRegionElems;
   rg.lo = 0;
   const int64_t last = p - (int64_t)rid * kRegion;
   rg.hi = last >= 7 ? 7 : (int)last;
@@ -312,7 +314,7 @@ struct DecodeArgs {
   const int32_t* sel;
   const int32_t* nsel;
   float* part;  // [B][G][nsplit][16][kPartStride]
-  int64_t tcap;
+  CacheMap cm;  // where the K/V of each sequence live (capacity cm.R*8)
   int32_t topk, nsplit;
   float scale_log2;
 };
@@ -340,17 +342,18 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   const int32_t idb = lst[eb < a.topk ? eb : a.topk - 1];
   bf16x8 qb[6];
   load_q(a.q, b, g, qb);
-  L = L < 1 ? 1 : (L > a.tcap ? a.tcap : L);
+  const int64_t tcap = a.cm.R * kRegion;
+  L = L < 1 ? 1 : (L > tcap ? tcap : L);
   const int64_t p = L - 1;
   cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
-  const uint16_t* kbase = a.k + sg * a.tcap * kHeadDim;
-  const uint16_t* vbase = a.v + sg * (a.tcap / kRegion) * kHeadDim * kRegion;
 
   // (a chunk past the count reads the dummy region and contributes nothing)
   CoreState st;
   core_init(st);
-  const Region ra = dsa_region(kbase, vbase, ea < cnt ? ida : -1, p);
-  const Region rb = dsa_region(kbase, vbase, eb < cnt ? idb : -1, p);
+  const int32_t ra_id = ea < cnt ? ida : -1, rb_id = eb < cnt ? idb : -1;
+  const int64_t cr = p / kRegion;
+  const Region ra = dsa_region(a.k, a.v, region_slot(a.cm, b, g, ra_id >= 0 && ra_id <= cr ? ra_id : 0), ra_id, p);
+  const Region rb = dsa_region(a.k, a.v, region_slot(a.cm, b, g, rb_id >= 0 && rb_id <= cr ? rb_id : 0), rb_id, p);
   core_chunk(st, qb, ra, rb, a.scale_log2);
   // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i)
   const float lt = core_total_l(st);
@@ -444,7 +447,7 @@ struct PrefillArgs {
   const int32_t* nsel;
   uint16_t* part_o;  // [Nq][G][kPreSplits][16][D] bf16, unnormalised O
   float* part_ml;    // [Nq][G][kPreSplits][16][2] fp32, (max, sum)
-  int64_t tcap;
+  CacheMap cm;       // where the K/V of each sequence live (capacity cm.R*8)
   int32_t nq, n_seqs, topk, rsplit;  // rsplit: regions per range
   float scale_log2;
 };
@@ -460,15 +463,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rest = blockIdx.x / kPreSplits;
   const int g = rest / nqb;
   const int64_t qi = (int64_t)(rest % nqb) * 4 + wave;
-  __shared__ int32_t ids[4][kMaxTopk];
+  __shared__ int32_t ids[4][kMaxTopk];    // region ids of the wave's entries in this range
+  __shared__ int32_t slots[4][kMaxTopk];  // their cache slots
   const bool live = qi < a.nq;
   int32_t s = live ? a.qseq[qi] : 0;
   s = s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
+  const int64_t tcap = a.cm.R * kRegion;
   int64_t p = live ? a.qpos[qi] : 0;
-  p = p < 0 ? 0 : (p >= a.tcap ? a.tcap - 1 : p);
-  const int64_t sg = (int64_t)s * kGroups + g;
-  const uint16_t* kbase = a.k + sg * a.tcap * kHeadDim;
-  const uint16_t* vbase = a.v + sg * (a.tcap / kRegion) * kHeadDim * kRegion;
+  p = p < 0 ? 0 : (p >= tcap ? tcap - 1 : p);
   const int64_t pg = qi * kGroups + g;
   int32_t cnt = live ? a.nsel[pg] : 0;
   cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
@@ -483,13 +485,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int i = 64 * j + lane;
     mine[j] = lst[i < cnt ? i : 0];
   }
+  // paged caches: every entry's page, all lookups in flight at once
+  int32_t pgs[kMaxTopk / 64];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk / 64; ++j) {
+    const int64_t r = mine[j] < 0 ? 0 : (mine[j] >= a.cm.R ? a.cm.R - 1 : mine[j]);
+    pgs[j] = a.cm.bt ? page_of(a.cm, s, r) : 0;
+  }
   const uint64_t lt = (1ull << lane) - 1ull;
   int32_t n = 0;
 #pragma unroll
   for (int j = 0; j < kMaxTopk / 64; ++j) {
-    const bool in = 64 * j + lane < cnt && mine[j] >= r0 && mine[j] < r1;
+    const bool in = 64 * j + lane < cnt && mine[j] >= r0 && mine[j] < r1 && mine[j] < a.cm.R;
     const uint64_t m = __ballot(in);
-    if (in) ids[wave][n + __popcll(m & lt)] = mine[j];
+    if (in) {
+      ids[wave][n + __popcll(m & lt)] = mine[j];
+      slots[wave][n + __popcll(m & lt)] = (int32_t)slot_in(a.cm, pgs[j], s, g, mine[j]);
+    }
     n += __popcll(m);
   }
   __syncthreads();
@@ -500,8 +512,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   CoreState st;
   core_init(st);
   const int32_t* my = ids[wave];
+  const int32_t* myslot = slots[wave];
   auto region_of = [&](int64_t e) -> Region {
-    return dsa_region(kbase, vbase, e < n ? my[e] : -1, p);
+    return dsa_region(a.k, a.v, e < n ? myslot[e] : 0, e < n ? my[e] : -1, p);
   };
   core_run<0>(st, qb, n, region_of, a.scale_log2);
   // partial (max, sum, unnormalised O^T in bf16) of this range; an empty
@@ -1009,6 +1022,40 @@ extern "C" size_t dsa_sparse_gqa_workspace_size(const dsa_geometry* geom, int32_
   return (size_t)batch * kGroups * nsplit_of(topk) * 16 * kPartStride * sizeof(float) + 256;
 }
 
+namespace dsa {
+dsa_status sparse_gqa_decode(const char* who, const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                             const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
+                             const int32_t* seq_len, const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const std::string w(who);
+  if (batch < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": batch must be >= 0");
+  if (batch == 0) return DSA_OK;
+  if (!q || !k_cache || !v_cache || !seq_len || !sel || !n_sel || !out || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, w + ": NULL pointer");
+  if ((size_t)workspace & 255) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": workspace must be 256-byte aligned");
+  if (workspace_bytes < dsa_sparse_gqa_workspace_size(geom, batch))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, w + ": workspace too small");
+  if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, w + ": batch > 65535");
+  DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.seq_len = seq_len; a.sel = sel; a.nsel = n_sel;
+  a.part = (float*)workspace; a.cm = cm; a.topk = geom->topk; a.nsplit = nsplit_of(geom->topk);
+  a.scale_log2 = geom->softmax_scale * kLog2e;
+  hipStream_t s = as_stream(stream);
+  {
+    ProfScope prof_("k_sgqa_decode", s);
+    hipLaunchKernelGGL(k_sgqa_decode, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
+  }
+  dsa_status st = check_launch(who);
+  if (st != DSA_OK) return st;
+  {
+    ProfScope prof_("k_sgqa_merge", s);
+    hipLaunchKernelGGL(k_sgqa_merge<kMaxTopk / kSplitRegions>, dim3((unsigned)(16 * kGroups * batch)),
+                       dim3(kHeadDim), 0, s, (const float*)workspace, out, a.nsplit);
+  }
+  return check_launch(who);
+}
+}  // namespace dsa
+
 extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
                                             const uint16_t* k_cache, const uint16_t* v_cache,
                                             int64_t tcap, const int32_t* seq_len,
@@ -1016,33 +1063,24 @@ extern "C" dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t ba
                                             void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (batch < 0 || tcap <= 0 || tcap % kTcapAlign)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: bad sizes (tcap must be a positive multiple of 128)");
-  if (batch == 0) return DSA_OK;
-  if (!q || !k_cache || !v_cache || !seq_len || !sel || !n_sel || !out || !workspace)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: NULL pointer");
-  if ((size_t)workspace & 255)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: workspace must be 256-byte aligned");
-  if (workspace_bytes < dsa_sparse_gqa_workspace_size(geom, batch))
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_sparse_gqa_decode: workspace too small");
-  if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_gqa_decode: batch > 65535");
-  DecodeArgs a;
-  a.q = q; a.k = k_cache; a.v = v_cache; a.seq_len = seq_len; a.sel = sel; a.nsel = n_sel;
-  a.part = (float*)workspace; a.tcap = tcap; a.topk = geom->topk; a.nsplit = nsplit_of(geom->topk);
-  a.scale_log2 = geom->softmax_scale * kLog2e;
-  hipStream_t s = as_stream(stream);
-  {
-    ProfScope prof_("k_sgqa_decode", s);
-    hipLaunchKernelGGL(k_sgqa_decode, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
-  }
-  st = check_launch("dsa_sparse_gqa_decode");
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode: tcap must be a positive multiple of 128");
+  return sparse_gqa_decode("dsa_sparse_gqa_decode", geom, batch, q, k_cache, v_cache, contiguous_map(tcap), seq_len,
+                           sel, n_sel, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" dsa_status dsa_sparse_gqa_decode_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                                  const dsa_page_table* pages, const uint16_t* k_pool,
+                                                  const uint16_t* v_pool, const int32_t* seq_len,
+                                                  const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                                  void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  {
-    ProfScope prof_("k_sgqa_merge", s);
-    hipLaunchKernelGGL(k_sgqa_merge<kMaxTopk / kSplitRegions>, dim3((unsigned)(16 * kGroups * batch)),
-                       dim3(kHeadDim), 0, s, (const float*)workspace, out, a.nsplit);
-  }
-  return check_launch("dsa_sparse_gqa_decode: merge");
+  CacheMap cm;
+  st = paged_map("dsa_sparse_gqa_decode_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  return sparse_gqa_decode("dsa_sparse_gqa_decode_paged", geom, batch, q, k_pool, v_pool, cm, seq_len, sel, n_sel,
+                           out, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries) {
@@ -1050,6 +1088,48 @@ extern "C" size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom
   if (n_queries <= 0) return 256;
   const size_t rows = (size_t)n_queries * kGroups * kPreSplits * 16;
   return align256(rows * kHeadDim * sizeof(uint16_t)) + rows * 2 * sizeof(float) + 256;
+}
+
+static dsa_status sparse_gqa_prefill(const char* who, const dsa_geometry* geom, int32_t n_queries,
+                                     const uint16_t* q, const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                     const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
+                                     const int32_t* sel, const int32_t* n_sel, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const std::string w(who);
+  if (n_queries < 0 || n_seqs < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": bad sizes");
+  if (n_queries == 0) return DSA_OK;
+  if (n_seqs == 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": n_seqs must be positive");
+  if (!q || !q_seq || !q_pos || !k_cache || !v_cache || !sel || !n_sel || !out || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, w + ": NULL pointer");
+  if ((size_t)workspace & 255) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": workspace must be 256-byte aligned");
+  if (workspace_bytes < dsa_sparse_gqa_prefill_workspace_size(geom, n_queries))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, w + ": workspace too small");
+  if (n_queries > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, w + ": more than 2^24 queries");
+  // region slots are kept as 32-bit values
+  if (!cm.bt && (int64_t)n_seqs * kGroups * cm.R > ((int64_t)1 << 31))
+    return fail(DSA_ERR_UNSUPPORTED, w + ": n_seqs * 4 * tcap/8 must stay below 2^31");
+  PrefillArgs a;
+  a.q = q; a.qseq = q_seq; a.qpos = q_pos; a.k = k_cache; a.v = v_cache; a.sel = sel; a.nsel = n_sel;
+  const size_t rows = (size_t)n_queries * kGroups * kPreSplits * 16;
+  a.part_o = (uint16_t*)workspace;
+  a.part_ml = (float*)((char*)workspace + align256(rows * kHeadDim * sizeof(uint16_t)));
+  a.cm = cm; a.nq = n_queries; a.n_seqs = n_seqs; a.topk = geom->topk;
+  a.rsplit = (int32_t)((cm.R + kPreSplits - 1) / kPreSplits);
+  a.scale_log2 = geom->softmax_scale * kLog2e;
+  hipStream_t s = as_stream(stream);
+  {
+    ProfScope prof_("k_sgqa_prefill", s);
+    hipLaunchKernelGGL(k_sgqa_prefill, dim3((unsigned)(kPreSplits * kGroups * ((n_queries + 3) / 4))), dim3(256),
+                       0, s, a);
+  }
+  dsa_status st = check_launch(who);
+  if (st != DSA_OK) return st;
+  {
+    ProfScope prof_("k_sgqa_merge", s);
+    hipLaunchKernelGGL(k_sgqa_merge_pre, dim3((unsigned)(kGroups * (int64_t)n_queries)), dim3(256), 0, s,
+                       (const uint16_t*)a.part_o, (const float*)a.part_ml, out);
+  }
+  return check_launch(who);
 }
 
 extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
@@ -1060,39 +1140,25 @@ extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n
                                              void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (n_queries < 0 || n_seqs < 0 || tcap <= 0 || tcap % kTcapAlign)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: bad sizes (tcap must be a positive multiple of 128)");
-  if (n_queries == 0) return DSA_OK;
-  if (n_seqs == 0) return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: n_seqs must be positive");
-  if (!q || !q_seq || !q_pos || !k_cache || !v_cache || !sel || !n_sel || !out || !workspace)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: NULL pointer");
-  if ((size_t)workspace & 255)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: workspace must be 256-byte aligned");
-  if (workspace_bytes < dsa_sparse_gqa_prefill_workspace_size(geom, n_queries))
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_sparse_gqa_prefill: workspace too small");
-  if (n_queries > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_gqa_prefill: more than 2^24 queries");
-  PrefillArgs a;
-  a.q = q; a.qseq = q_seq; a.qpos = q_pos; a.k = k_cache; a.v = v_cache; a.sel = sel; a.nsel = n_sel;
-  const size_t rows = (size_t)n_queries * kGroups * kPreSplits * 16;
-  a.part_o = (uint16_t*)workspace;
-  a.part_ml = (float*)((char*)workspace + align256(rows * kHeadDim * sizeof(uint16_t)));
-  a.tcap = tcap; a.nq = n_queries; a.n_seqs = n_seqs; a.topk = geom->topk;
-  a.rsplit = (int32_t)((tcap / kRegion + kPreSplits - 1) / kPreSplits);
-  a.scale_log2 = geom->softmax_scale * kLog2e;
-  hipStream_t s = as_stream(stream);
-  {
-    ProfScope prof_("k_sgqa_prefill", s);
-    hipLaunchKernelGGL(k_sgqa_prefill, dim3((unsigned)(kPreSplits * kGroups * ((n_queries + 3) / 4))), dim3(256),
-                       0, s, a);
-  }
-  st = check_launch("dsa_sparse_gqa_prefill");
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: tcap must be a positive multiple of 128");
+  return sparse_gqa_prefill("dsa_sparse_gqa_prefill", geom, n_queries, q, q_seq, q_pos, n_seqs, k_cache, v_cache,
+                            contiguous_map(tcap), sel, n_sel, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" dsa_status dsa_sparse_gqa_prefill_paged(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                                   const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                                   const dsa_page_table* pages, const uint16_t* k_pool,
+                                                   const uint16_t* v_pool, const int32_t* sel, const int32_t* n_sel,
+                                                   uint16_t* out, void* workspace, size_t workspace_bytes,
+                                                   void* stream) {
+  dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  {
-    ProfScope prof_("k_sgqa_merge", s);
-    hipLaunchKernelGGL(k_sgqa_merge_pre, dim3((unsigned)(kGroups * (int64_t)n_queries)), dim3(256), 0, s,
-                       (const uint16_t*)a.part_o, (const float*)a.part_ml, out);
-  }
-  return check_launch("dsa_sparse_gqa_prefill: merge");
+  CacheMap cm;
+  st = paged_map("dsa_sparse_gqa_prefill_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  return sparse_gqa_prefill("dsa_sparse_gqa_prefill_paged", geom, n_queries, q, q_seq, q_pos, n_seqs, k_pool,
+                            v_pool, cm, sel, n_sel, out, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

@@ -31,6 +31,44 @@ constexpr int kTcapAlign = 128;  // cache capacity granule: 16 regions = one sum
 // B operand (lane 16*kb + n <- region n, channels 64q + 16kb .. +15).
 __device__ __forceinline__ int64_t summ_tile_base(int64_t r) { return (r >> 4) * 4096; }
 
+// Where the caches of a sequence live.  Every cached tensor of the layer is
+// stored per region slot: one region of one group (1536 bf16 of K, 1536 of
+// V, 8 index_k rows, 256 summary bytes, one scale).
+//   contiguous caches (capacity tcap, R = tcap/8 regions per sequence):
+//     slot(s, g, r) = (s*G + g)*R + r
+//   paged caches (pages of 128 positions = 16 regions, one page id for every
+//   tensor of the cache, block table bt[n_seqs][max_pages]):
+//     slot(s, g, r) = (bt[s][r/16]*G + g)*16 + r%16
+// In both, summary tile slot(s, g, r)/16 holds region r's summary at
+// position slot%16 == r%16, and index_k row t of region r is row 8*slot + t.
+constexpr int kPageRegions = 16;  // regions per page (128 positions, one summary tile)
+struct CacheMap {
+  const int32_t* bt;  // block table, or nullptr for contiguous caches
+  int64_t R;          // regions per sequence: tcap/8, or max_pages*16
+  int32_t bt_stride;  // max_pages (row length of the block table)
+  int32_t n_pages;    // pages in every pool; page ids are clamped into [0, n_pages)
+};
+__device__ __forceinline__ int32_t clamp_page(const CacheMap& m, int32_t pg) {
+  return pg < 0 ? 0 : (pg >= m.n_pages ? m.n_pages - 1 : pg);
+}
+// Block-table entry of region r of sequence s (paged caches; r in [0, R)),
+// unclamped, so that a caller can issue the load early and clamp at use.
+__device__ __forceinline__ int32_t page_entry(const CacheMap& m, int64_t s, int64_t r) {
+  return m.bt[s * m.bt_stride + (r >> 4)];
+}
+// Page id of region r of sequence s (paged caches; r in [0, R)).
+__device__ __forceinline__ int32_t page_of(const CacheMap& m, int64_t s, int64_t r) {
+  return clamp_page(m, page_entry(m, s, r));
+}
+// Slot of region r given its page id (ignored for contiguous caches).
+__device__ __forceinline__ int64_t slot_in(const CacheMap& m, int32_t pg, int64_t s, int g, int64_t r) {
+  return m.bt ? ((int64_t)pg * kGroups + g) * kPageRegions + (r & (kPageRegions - 1))
+              : (s * kGroups + g) * m.R + r;
+}
+__device__ __forceinline__ int64_t region_slot(const CacheMap& m, int64_t s, int g, int64_t r) {
+  return slot_in(m, m.bt ? page_of(m, s, r) : 0, s, g, r);
+}
+
 // Keys are stored per region of 8 tokens (1536 bf16) in MFMA A-operand
 // order: element (token pos of the region, channel d) lives at
 //   ((((pos/4)*6 + (d%48)/8)*4 + d/48)*4 + pos%4)*8 + d%8,
@@ -115,6 +153,25 @@ dsa_status fail(dsa_status s, const std::string& msg);
 dsa_status check_geometry(const dsa_geometry* g);
 dsa_status check_launch(const char* what);
 inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Cache maps of the two cache arrangements (host side).
+inline CacheMap contiguous_map(int64_t tcap) {
+  CacheMap m;
+  m.bt = nullptr;
+  m.R = tcap / kRegion;
+  m.bt_stride = 0;
+  m.n_pages = 0;
+  return m;
+}
+// Checks a page table (non-NULL block table, max_pages and n_pages > 0,
+// n_pages <= kMaxPages so that region slots fit 31 bits) and builds its map.
+constexpr int32_t kMaxPages = 1 << 25;
+dsa_status paged_map(const char* who, const dsa_page_table* pt, CacheMap* m);
+// Sparse GQA decode over either cache arrangement (the decode step calls it).
+dsa_status sparse_gqa_decode(const char* who, const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                             const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
+                             const int32_t* seq_len, const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 // Instrumentation: while enabled (dsa_profile_enable), a ProfScope brackets
 // the kernel launched inside its lifetime with two hipEvents on the launch

@@ -30,14 +30,14 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
 }
 
 // One wave compresses region r of group g of sequence b: lane l owns
-// channels 4l..4l+3.  index_k is [B][G][tcap][P]; summ/scale use the tiled
-// summary layout of sequences with capacity tcap.
-__device__ __forceinline__ void compress_region_wave(const uint16_t* __restrict__ ik, int64_t tcap, int64_t b,
-                                                     int64_t r, int g, uint8_t* __restrict__ summ,
+// channels 4l..4l+3.  index_k rows, summaries (tiled layout) and scales are
+// found through the cache map (contiguous or paged).
+__device__ __forceinline__ void compress_region_wave(const uint16_t* __restrict__ ik, const CacheMap& cm,
+                                                     int64_t b, int64_t r, int g, uint8_t* __restrict__ summ,
                                                      float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  const int64_t R = tcap / kRegion;
-  const uint16_t* src = ik + ((b * kGroups + g) * tcap + (int64_t)kRegion * r) * kProxy + 4 * lane;
+  const int64_t slot = region_slot(cm, b, g, r);
+  const uint16_t* src = ik + slot * kRegion * kProxy + 4 * lane;
   uint2 row[kRegion];
 #pragma unroll
   for (int t = 0; t < kRegion; ++t) row[t] = *(const uint2*)(src + (int64_t)t * kProxy);
@@ -62,12 +62,11 @@ __device__ __forceinline__ void compress_region_wave(const uint16_t* __restrict_
 #pragma unroll
     for (int e = 0; e < 4; ++e) packed |= e4m3_rne_sat(__fdiv_rn(m[e], sc)) << (8 * e);
   }
-  const int64_t sg = b * kGroups + g;
-  // channels 4l..4l+3 of region r in the tiled summary layout
-  const int64_t off = summ_tile_base(r) + (lane >> 4) * 1024 + ((lane & 15) >> 2) * 256 + (r & 15) * 16 +
+  // channels 4l..4l+3 of the region in its summary tile (slot/16)
+  const int64_t off = summ_tile_base(slot) + (lane >> 4) * 1024 + ((lane & 15) >> 2) * 256 + (slot & 15) * 16 +
                       4 * (lane & 3);
-  *(uint32_t*)(summ + sg * R * kProxy + off) = packed;
-  if (lane == 0) scale[sg * R + r] = sc;
+  *(uint32_t*)(summ + off) = packed;
+  if (lane == 0) scale[slot] = sc;
 }
 
 }  // namespace dsa

@@ -53,14 +53,14 @@ struct ScoreArgs {
   const int32_t* qseq;  // [Nq], or nullptr: query i belongs to sequence i
   const int32_t* qpos;  // [Nq], or nullptr: position slen[i] - 1
   const int32_t* slen;  // [Nq] sequence lengths when qpos is nullptr
-  const uint8_t* summ;  // [S][G][R][P]
-  const float* scale;   // [S][G][R]
+  const uint8_t* summ;  // summary tiles, found through cm
+  const float* scale;   // scales, found through cm
   float* scores;        // workspace [Nq][G][ws_stride]
   float* scores_out;    // nullable [Nq][G][max_regions]
   uint32_t* tilemax;    // nullable workspace [Nq][G][tm_stride]: largest key of each 16-region tile
   uint32_t* hist;       // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts, added to
                         // whatever is there (k_select_dec clears it after reading)
-  int64_t R;            // tcap / 8
+  CacheMap cm;          // where the sequences' summaries live (cm.R regions each)
   int32_t nq, n_seqs, max_regions, ws_stride, tm_stride, topk;
 };
 
@@ -184,6 +184,7 @@ constexpr int kDecDepth = DSA_SCORE_DEC_DEPTH;  // tiles in flight per wave
 // it; the tile's largest key is reduced over those 16 lanes and stored too.
 // When a.hist is set, the level-0 digits of the scores are counted in LDS
 // and added to one stripe of the (query, group) histogram at the end.
+template <bool PAGED>
 __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   const int g = blockIdx.y;
   const int qi = blockIdx.z;
@@ -194,9 +195,19 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   if (a.hist)
     for (int i = threadIdx.x; i < kHistBins; i += 256) hist_lds[i] = 0;
 
+  constexpr int kWaveRegions = kDecRange / 4;
+  const int64_t w0 = (int64_t)blockIdx.x * kDecRange + (int64_t)wave * kWaveRegions;
   int32_t seq = query_seq(a.qseq, qi);
   seq = seq < 0 ? 0 : (seq >= a.n_seqs ? a.n_seqs - 1 : seq);
-  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.cm.R, a.max_regions);
+  // paged caches: lane l holds the page id of the wave's tile l (clamped when
+  // used); the barrier below waits for it together with the query's loads
+  const int64_t ntile_all = a.cm.R / kTile;
+  int32_t pgv = 0;
+  if constexpr (PAGED) {
+    const int64_t tl = (w0 >> 4) + lane;
+    pgv = a.cm.bt[(int64_t)seq * a.cm.bt_stride + (tl < ntile_all ? tl : ntile_all - 1)];
+  }
   bf16x8 A[8];
   {
     const uint16_t* qp = a.iq + ((int64_t)qi * kIdxHeads + 4 * g + (n & 3)) * kProxy + 16 * kb;
@@ -209,15 +220,14 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   }
   const f32x4 zz = *(const f32x4*)(a.z + (int64_t)qi * kIdxHeads + 4 * g);
   __syncthreads();
+  // (the page ids are waited for once, here, instead of before every tile's
+  // loads)
+  if constexpr (PAGED) asm volatile("" ::"v"(pgv));
 
   // this wave's tiles: contiguous quarter of the block's range
-  constexpr int kWaveRegions = kDecRange / 4;
-  const int64_t w0 = (int64_t)blockIdx.x * kDecRange + (int64_t)wave * kWaveRegions;
   int64_t w1 = w0 + kWaveRegions;
   if (w1 > c) w1 = c;
   const int ntile = w0 < w1 ? (int)((w1 - w0 + kTile - 1) / kTile) : 0;
-  const uint8_t* sbase = a.summ + ((int64_t)seq * kGroups + g) * a.R * kProxy;
-  const float* scbase = a.scale + ((int64_t)seq * kGroups + g) * a.R;
   const int64_t pq = (int64_t)qi * kGroups + g;
   float* scores = a.scores + pq * a.ws_stride;
   float* scores_out = a.scores_out ? a.scores_out + pq * a.max_regions : nullptr;
@@ -225,15 +235,18 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
 
   u32x4 buf[kDecDepth][4];
   float bsc[kDecDepth];
+  static_assert(kDecRange / 4 / kTile <= 64, "a lane per tile of the wave");
   auto issue = [&](int t, int slot) {
-    const int64_t r = w0 + (int64_t)t * kTile + n;
-    const int64_t rl = r < a.R ? r : a.R - 1;
-    const uint8_t* rp = sbase + summ_tile_base(rl) + 16 * lane;
+    int64_t tt = (w0 >> 4) + t;  // tile index (uniform)
+    tt = tt < ntile_all ? tt : ntile_all - 1;
+    const int64_t ts = PAGED ? ((int64_t)clamp_page(a.cm, __builtin_amdgcn_readlane(pgv, t)) * kGroups + g)
+                             : ((int64_t)seq * kGroups + g) * ntile_all + tt;  // tile slot
+    const uint8_t* rp = a.summ + ts * 4096 + 16 * lane;
     buf[slot][0] = ldg16(rp);
     buf[slot][1] = ldg16(rp + 1024);
     buf[slot][2] = ldg16(rp + 2048);
     buf[slot][3] = ldg16(rp + 3072);
-    bsc[slot] = scbase[rl];
+    bsc[slot] = a.scale[ts * kTile + n];
   };
 #pragma unroll
   for (int t = 0; t < kDecDepth - 1; ++t)
@@ -338,7 +351,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void* base, int64_t 
 }
 constexpr uint32_t kOutOfView = 0x80000000u;  // byte offset past every view (views stay below 2 GiB)
 
-template <bool TILEMAX, bool OUT>
+template <bool TILEMAX, bool OUT, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAVES, DSA_PRE_WAVES))) void k_score_pre(ScoreArgs a) {
   using Cfg = PreScoreCfg<TILEMAX, OUT>;
   constexpr int NRS = 4, D = Cfg::D;
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
   const int64_t qm = (qb + lane < a.nq) ? qb + lane : a.nq - 1;
   int32_t sq = query_seq(a.qseq, qm);
   sq = sq < 0 ? 0 : (sq >= a.n_seqs ? a.n_seqs - 1 : sq);
-  const int32_t cqm = (int32_t)current_region(query_pos(a.qpos, a.slen, qm), a.R, a.max_regions);
+  const int32_t cqm = (int32_t)current_region(query_pos(a.qpos, a.slen, qm), a.cm.R, a.max_regions);
   uint64_t remaining = __ballot(qb + lane < a.nq);
 
   const __amdgpu_buffer_rsrc_t ws_view = rows_rsrc(a.scores, qw, g, a.ws_stride, a.nq);
@@ -404,18 +417,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
 
     const int64_t rend = (range0 + kScoreRange < cm) ? range0 + kScoreRange : (int64_t)cm;
     const int nk = rend > range0 ? (int)((rend - range0 + kTile - 1) / kTile) : 0;  // tiles of the block
-    const uint8_t* sbase = a.summ + ((int64_t)seq * kGroups + g) * a.R * kProxy;
-    const float* scbase = a.scale + ((int64_t)seq * kGroups + g) * a.R;
+    // page ids of the block's tiles (paged caches): lane l holds tile l's
+    static_assert(kScoreRange / kTile <= 64, "a lane per tile of the block");
+    const int64_t ntile_all = a.cm.R / kTile;
+    int32_t pgv = 0;  // (clamped when used)
+    if constexpr (PAGED) {
+      const int64_t tl = (range0 >> 4) + lane;
+      pgv = a.cm.bt[(int64_t)seq * a.cm.bt_stride + (tl < ntile_all ? tl : ntile_all - 1)];
+      asm volatile("" ::"v"(pgv));  // waited for here, once, so that no copy below waits for it
+    }
     // tile k = regions range0 + 16k ..; wave w copies its codes' quarter w
-    // and its own copy of the 16 scales (copies past the end re-read a
-    // clamped tile so every iteration issues the same operations)
+    // and its own copy of the 16 scales (copies past the end re-read the
+    // last tile so every iteration issues the same operations)
     auto issue = [&](int k) {
-      int64_t tr = range0 + (int64_t)k * kTile;
-      tr = tr + kTile <= a.R ? tr : a.R - kTile;
+      const int kk = k < nk ? k : nk - 1;
+      const int64_t ts = PAGED ? ((int64_t)clamp_page(a.cm, __builtin_amdgcn_readlane(pgv, kk)) * kGroups + g)
+                               : ((int64_t)seq * kGroups + g) * ntile_all + (range0 >> 4) + kk;  // tile slot
       LdsPtr dst = (LdsPtr)&ring[k % D][0];
-      __builtin_amdgcn_global_load_lds((const void*)(sbase + summ_tile_base(tr) + 1024 * wave + 16 * lane),
+      __builtin_amdgcn_global_load_lds((const void*)(a.summ + ts * 4096 + 1024 * wave + 16 * lane),
                                        dst + 1024 * wave, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(scbase + tr + n), dst + 4096 + 256 * wave, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(a.scale + ts * kTile + n), dst + 4096 + 256 * wave, 4, 0, 0);
     };
     if (nk > 0)
 #pragma unroll
@@ -423,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
     for (int k = 0; k < nk; ++k) {
       if (k < D - 1) wait_vm<Cfg::W_EARLY>();
       else wait_vm<Cfg::W_FULL>();
-      __syncthreads();
+      lds_barrier();  // (a workgroup fence here would drain every copy in flight)
       issue(k + D - 1);
       const int t0 = (int)range0 + k * kTile;  // region indices fit 32 bits (max_regions is int32)
       const int r = t0 + n;
@@ -499,7 +520,7 @@ struct SelectArgs {
   const int32_t* qpos;
   int32_t* sel;             // [Nq][G][topk]
   int32_t* nsel;            // [Nq][G]
-  int64_t R;
+  CacheMap cm;              // the sequences' caches (the folded compression's index_k and summaries)
   int32_t nq, max_regions, ws_stride, tm_stride, topk;
 };
 
@@ -697,7 +718,7 @@ __device__ void select_fallback(const SelectArgs& a, int64_t pq) {
     sh_count = 0;
   }
   __syncthreads();
-  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.cm.R, a.max_regions);
   const int64_t need64 = (c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1);
   const uint32_t need = (uint32_t)need64;
   int32_t* sel = a.sel + pq * a.topk;
@@ -838,7 +859,7 @@ __global__ __launch_bounds__(NT) void k_select_tiles(SelectArgs a) {
   const int qi = (int)(pq / kGroups);
   __shared__ SelectSmem<NT, KPT> sm;
   __shared__ int32_t tiles[kMaxTopk];
-  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
+  const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.cm.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
   if (select_trivial(c, need, sel, a.nsel + pq, a.topk, NT)) return;
@@ -995,10 +1016,10 @@ __device__ void ordered_positions2(const bool (&fa)[KPT], const bool (&fb)[KPT],
 // region, so they never touch the summary being written.
 __device__ __forceinline__ void folded_compress(const SelectArgs& a, int64_t qi, int g) {
   const int64_t p = query_pos(a.qpos, a.slen, qi);
-  if (p < 0 || (p + 1) % kRegion != 0 || (p + 1) / kRegion > a.R) return;
+  if (p < 0 || (p + 1) % kRegion != 0 || (p + 1) / kRegion > a.cm.R) return;
   int32_t seq = (int32_t)qi;
   seq = seq >= a.n_seqs ? a.n_seqs - 1 : seq;
-  compress_region_wave(a.ik, a.R * kRegion, seq, p / kRegion, g, a.csumm, a.cscale);
+  compress_region_wave(a.ik, a.cm, seq, p / kRegion, g, a.csumm, a.cscale);
 }
 
 // Standalone form for the selection paths without folded blocks: one wave per
@@ -1127,7 +1148,7 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   if (lane == 63) sm.wtot[w] = wi;
   if (tid == 0) sm.res[0] = 0xFFFFFFFFu;
   lds_barrier();
-  const int64_t c = current_region(a.qpos ? qraw : qraw - 1, a.R, a.max_regions);
+  const int64_t c = current_region(a.qpos ? qraw : qraw - 1, a.cm.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
   if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kDecNT)) {
@@ -1341,7 +1362,7 @@ __global__ __launch_bounds__(NT) void k_select_pre(SelectArgs a) {
   const int qi = (int)(pq / kGroups);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   __shared__ PreSmem<NT, KPT> sm;
-  const int64_t c64 = current_region(query_pos(a.qpos, a.slen, qi), a.R, a.max_regions);
+  const int64_t c64 = current_region(query_pos(a.qpos, a.slen, qi), a.cm.R, a.max_regions);
   const uint32_t need = (uint32_t)((c64 < (int64_t)(a.topk - 1)) ? c64 : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
   if (select_trivial(c64, need, sel, a.nsel + pq, a.topk, NT)) return;
@@ -1571,7 +1592,7 @@ extern "C" size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_
 static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries, const uint16_t* index_q,
                                     const float* z, const int32_t* q_seq, const int32_t* q_pos,
                                     const int32_t* seq_len, int32_t n_seqs, const uint8_t* summ,
-                                    const float* scale, int64_t tcap, int32_t max_regions, int32_t* sel,
+                                    const float* scale, const CacheMap& cm, int32_t max_regions, int32_t* sel,
                                     int32_t* n_sel, float* scores_out, const uint16_t* index_k,
                                     uint8_t* csumm, float* cscale, void* workspace, hipStream_t s) {
   const ScoreWs w = score_ws_layout(workspace, n_queries, max_regions);
@@ -1579,12 +1600,12 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   ScoreArgs sa;
   sa.iq = index_q; sa.z = z; sa.qseq = q_seq; sa.qpos = q_pos; sa.slen = seq_len; sa.summ = summ; sa.scale = scale;
   sa.scores = w.scores; sa.scores_out = scores_out; sa.tilemax = w.tilemax; sa.hist = w.hist;
-  sa.R = tcap / kRegion; sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions;
+  sa.cm = cm; sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions;
   sa.ws_stride = stride; sa.tm_stride = (int32_t)tm_stride_of(max_regions); sa.topk = geom->topk;
   SelectArgs se;
   se.scores = w.scores; se.slen = seq_len; se.tilemax = w.tilemax; se.hist = w.hist; se.qpos = q_pos;
   se.ik = index_k; se.csumm = csumm; se.cscale = cscale; se.n_seqs = n_seqs;
-  se.sel = sel; se.nsel = n_sel; se.R = tcap / kRegion; se.nq = n_queries; se.max_regions = max_regions;
+  se.sel = sel; se.nsel = n_sel; se.cm = cm; se.nq = n_queries; se.max_regions = max_regions;
   se.ws_stride = stride; se.tm_stride = sa.tm_stride; se.topk = geom->topk;
   // the decode step's compression runs as extra blocks of the decode
   // selection launch, or as its own small launch on the other paths
@@ -1598,17 +1619,27 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   // wave so each summary tile feeds 4 MFMA row-sets.
   if (decode_shaped(n_queries)) {
     ProfScope prof_("k_score_decode", s);
-    hipLaunchKernelGGL(k_score_dec, dim3((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries),
-                       dim3(256), 0, s, sa);
+    const dim3 grid((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries);
+    if (cm.bt) hipLaunchKernelGGL(k_score_dec<true>, grid, dim3(256), 0, s, sa);
+    else hipLaunchKernelGGL(k_score_dec<false>, grid, dim3(256), 0, s, sa);
   } else {
     ProfScope prof_("k_score_prefill", s);
     const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
     const dim3 grid(ranges, kGroups, (n_queries + kPreQ - 1) / kPreQ);
     const bool tm = tiled_select(max_regions), out = scores_out != nullptr;
-    if (tm && out) hipLaunchKernelGGL((k_score_pre<true, true>), grid, dim3(256), 0, s, sa);
-    else if (tm) hipLaunchKernelGGL((k_score_pre<true, false>), grid, dim3(256), 0, s, sa);
-    else if (out) hipLaunchKernelGGL((k_score_pre<false, true>), grid, dim3(256), 0, s, sa);
-    else hipLaunchKernelGGL((k_score_pre<false, false>), grid, dim3(256), 0, s, sa);
+    // (paged and contiguous caches are separate instantiations: the page-id
+    // loads stay out of the contiguous kernels)
+    if (cm.bt) {
+      if (tm && out) hipLaunchKernelGGL((k_score_pre<true, true, true>), grid, dim3(256), 0, s, sa);
+      else if (tm) hipLaunchKernelGGL((k_score_pre<true, false, true>), grid, dim3(256), 0, s, sa);
+      else if (out) hipLaunchKernelGGL((k_score_pre<false, true, true>), grid, dim3(256), 0, s, sa);
+      else hipLaunchKernelGGL((k_score_pre<false, false, true>), grid, dim3(256), 0, s, sa);
+    } else {
+      if (tm && out) hipLaunchKernelGGL((k_score_pre<true, true, false>), grid, dim3(256), 0, s, sa);
+      else if (tm) hipLaunchKernelGGL((k_score_pre<true, false, false>), grid, dim3(256), 0, s, sa);
+      else if (out) hipLaunchKernelGGL((k_score_pre<false, true, false>), grid, dim3(256), 0, s, sa);
+      else hipLaunchKernelGGL((k_score_pre<false, false, false>), grid, dim3(256), 0, s, sa);
+    }
   }
   dsa_status st = check_launch("dsa_score_topk: score");
   if (st != DSA_OK) return st;
@@ -1628,6 +1659,27 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   return check_launch("dsa_score_topk: select");
 }
 
+static dsa_status score_topk(const char* who, const dsa_geometry* geom, int32_t n_queries, const uint16_t* index_q,
+                             const float* z, const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                             const uint8_t* summ, const float* scale, const CacheMap& cm, int32_t max_regions,
+                             int32_t* sel, int32_t* n_sel, float* scores_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const std::string w(who);
+  if (n_queries < 0 || n_seqs < 0 || max_regions < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": bad sizes");
+  if (n_queries == 0) return DSA_OK;
+  if (n_seqs == 0 || max_regions == 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, w + ": n_seqs and max_regions must be positive");
+  if (!index_q || !z || !q_seq || !q_pos || !summ || !scale || !sel || !n_sel || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, w + ": NULL pointer");
+  if ((size_t)workspace & 255) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": workspace must be 256-byte aligned");
+  if (workspace_bytes < dsa_score_topk_workspace_size(geom, n_queries, max_regions))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, w + ": workspace too small");
+  if (n_queries > 65535 * 16) return fail(DSA_ERR_UNSUPPORTED, w + ": too many queries");
+  return launch_score_topk(geom, n_queries, index_q, z, q_seq, q_pos, nullptr, n_seqs, summ, scale, cm,
+                           max_regions, sel, n_sel, scores_out, nullptr, nullptr, nullptr, workspace,
+                           as_stream(stream));
+}
+
 extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries,
                                      const uint16_t* index_q, const float* z,
                                      const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
@@ -1637,27 +1689,57 @@ extern "C" dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries
                                      void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (n_queries < 0 || n_seqs < 0 || max_regions < 0 || tcap <= 0 || tcap % kTcapAlign)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_score_topk: bad sizes (tcap must be a positive multiple of 128)");
-  if (n_queries == 0) return DSA_OK;
-  if (n_seqs == 0 || max_regions == 0)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_score_topk: n_seqs and max_regions must be positive");
-  if (!index_q || !z || !q_seq || !q_pos || !summ || !scale || !sel || !n_sel || !workspace)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_score_topk: NULL pointer");
-  if ((size_t)workspace & 255)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_score_topk: workspace must be 256-byte aligned");
-  if (workspace_bytes < dsa_score_topk_workspace_size(geom, n_queries, max_regions))
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_score_topk: workspace too small");
-  if (n_queries > 65535 * 16) return fail(DSA_ERR_UNSUPPORTED, "dsa_score_topk: too many queries");
-  return launch_score_topk(geom, n_queries, index_q, z, q_seq, q_pos, nullptr, n_seqs, summ, scale, tcap,
-                           max_regions, sel, n_sel, scores_out, nullptr, nullptr, nullptr, workspace,
-                           as_stream(stream));
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_score_topk: tcap must be a positive multiple of 128");
+  return score_topk("dsa_score_topk", geom, n_queries, index_q, z, q_seq, q_pos, n_seqs, summ, scale,
+                    contiguous_map(tcap), max_regions, sel, n_sel, scores_out, workspace, workspace_bytes, stream);
+}
+
+extern "C" dsa_status dsa_score_topk_paged(const dsa_geometry* geom, int32_t n_queries,
+                                           const uint16_t* index_q, const float* z, const int32_t* q_seq,
+                                           const int32_t* q_pos, int32_t n_seqs, const dsa_page_table* pages,
+                                           const uint8_t* summ_pool, const float* scale_pool,
+                                           int32_t max_regions, int32_t* sel, int32_t* n_sel, float* scores_out,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  CacheMap cm;
+  st = paged_map("dsa_score_topk_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  return score_topk("dsa_score_topk_paged", geom, n_queries, index_q, z, q_seq, q_pos, n_seqs, summ_pool,
+                    scale_pool, cm, max_regions, sel, n_sel, scores_out, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t dsa_decode_step_workspace_size(const dsa_geometry* geom, int32_t batch, int32_t max_regions) {
   if (batch <= 0 || max_regions <= 0) return 256;
   return align256(dsa_score_topk_workspace_size(geom, batch, max_regions)) +
          align256(dsa_sparse_gqa_workspace_size(geom, batch));
+}
+
+static dsa_status decode_step(const char* who, const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                              const uint16_t* index_q, const float* z, const uint16_t* index_k,
+                              const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
+                              const int32_t* seq_len, uint8_t* summ, float* scale, int32_t max_regions,
+                              int32_t* sel, int32_t* n_sel, uint16_t* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const std::string w(who);
+  if (batch < 0 || max_regions < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": bad sizes");
+  if (batch == 0) return DSA_OK;
+  if (max_regions == 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": max_regions must be positive");
+  if (!q || !index_q || !z || !index_k || !k_cache || !v_cache || !seq_len || !summ || !scale || !sel ||
+      !n_sel || !out || !workspace)
+    return fail(DSA_ERR_INVALID_ARGUMENT, w + ": NULL pointer");
+  if ((size_t)workspace & 255) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": workspace must be 256-byte aligned");
+  if (workspace_bytes < dsa_decode_step_workspace_size(geom, batch, max_regions))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, w + ": workspace too small");
+  if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, w + ": batch > 65535");
+  hipStream_t s = as_stream(stream);
+  const size_t ws1 = align256(dsa_score_topk_workspace_size(geom, batch, max_regions));
+  dsa_status st = launch_score_topk(geom, batch, index_q, z, nullptr, nullptr, seq_len, batch, summ, scale, cm,
+                                    max_regions, sel, n_sel, nullptr, index_k, summ, scale, workspace, s);
+  if (st != DSA_OK) return st;
+  return sparse_gqa_decode(who, geom, batch, q, k_cache, v_cache, cm, seq_len, sel, n_sel, out,
+                           (char*)workspace + ws1, workspace_bytes - ws1, stream);
 }
 
 extern "C" dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
@@ -1668,23 +1750,23 @@ extern "C" dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, c
                                       void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (batch < 0 || max_regions < 0 || tcap <= 0 || tcap % kTcapAlign)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: bad sizes (tcap must be a positive multiple of 128)");
-  if (batch == 0) return DSA_OK;
-  if (max_regions == 0) return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: max_regions must be positive");
-  if (!q || !index_q || !z || !index_k || !k_cache || !v_cache || !seq_len || !summ || !scale || !sel ||
-      !n_sel || !out || !workspace)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: NULL pointer");
-  if ((size_t)workspace & 255)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: workspace must be 256-byte aligned");
-  if (workspace_bytes < dsa_decode_step_workspace_size(geom, batch, max_regions))
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_decode_step: workspace too small");
-  if (batch > 65535) return fail(DSA_ERR_UNSUPPORTED, "dsa_decode_step: batch > 65535");
-  hipStream_t s = as_stream(stream);
-  const size_t ws1 = align256(dsa_score_topk_workspace_size(geom, batch, max_regions));
-  st = launch_score_topk(geom, batch, index_q, z, nullptr, nullptr, seq_len, batch, summ, scale, tcap, max_regions,
-                         sel, n_sel, nullptr, index_k, summ, scale, workspace, s);
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step: tcap must be a positive multiple of 128");
+  return decode_step("dsa_decode_step", geom, batch, q, index_q, z, index_k, k_cache, v_cache, contiguous_map(tcap),
+                     seq_len, summ, scale, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" dsa_status dsa_decode_step_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                            const uint16_t* index_q, const float* z, const dsa_page_table* pages,
+                                            const uint16_t* ik_pool, const uint16_t* k_pool, const uint16_t* v_pool,
+                                            const int32_t* seq_len, uint8_t* summ_pool, float* scale_pool,
+                                            int32_t max_regions, int32_t* sel, int32_t* n_sel, uint16_t* out,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  return dsa_sparse_gqa_decode(geom, batch, q, k_cache, v_cache, tcap, seq_len, sel, n_sel, out,
-                               (char*)workspace + ws1, workspace_bytes - ws1, stream);
+  CacheMap cm;
+  st = paged_map("dsa_decode_step_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  return decode_step("dsa_decode_step_paged", geom, batch, q, index_q, z, ik_pool, k_pool, v_pool, cm, seq_len,
+                     summ_pool, scale_pool, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream);
 }

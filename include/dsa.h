@@ -54,6 +54,22 @@
  * Sliding-window ring (window W = 512, slot of position t = t mod W):
  *   k_ring   [S][G][W/8][1536]  bf16   region-tiled like K (8-slot regions)
  *   v_ring   [S][G][W/8][D][8]  bf16   region-transposed like V
+ *
+ * Paged caches ([P3] section 一, kernel list: prefill_sparse_meta and
+ * decode_sparse_meta pack the selected tokens over a PagedAttention block
+ * table).  A page holds 128 consecutive positions (16 regions, one summary
+ * tile) of one sequence for every tensor above, in pools that share the page
+ * numbering:
+ *   ik_pool    [n_pages][G][128][P]   bf16
+ *   k_pool     [n_pages][G][16][1536] bf16   (region-tiled as K)
+ *   v_pool     [n_pages][G][16][D][8] bf16   (region-transposed as V)
+ *   summ_pool  [n_pages][G][4096]     uint8  (one summary tile)
+ *   scale_pool [n_pages][G][16]       fp32
+ * Position t of sequence s lives in page block_table[s*max_pages + t/128],
+ * at t%128 within it; a sequence's capacity is max_pages*128 positions.
+ * Pages may be shared or reused by the caller in any way; page ids are
+ * clamped into [0, n_pages), so a bad id reads or writes a wrong page of the
+ * pools, never memory outside them.
  */
 #ifndef DSA_MI355X_H
 #define DSA_MI355X_H
@@ -88,6 +104,15 @@ typedef struct {
   float softmax_scale; /* 1/sqrt(192) */
 } dsa_geometry;
 
+/* Block table of paged caches (HOST struct; the table itself is device
+ * memory, [n_seqs][max_pages] int32 page ids).  n_pages <= 2^25 and
+ * max_pages*128 <= 2^31. */
+typedef struct {
+  const int32_t* block_table;
+  int32_t max_pages; /* pages per sequence (row length of the table) */
+  int32_t n_pages;   /* pages in every pool */
+} dsa_page_table;
+
 /* Fills the default geometry.  Never fails for a non-NULL pointer. */
 dsa_status dsa_geometry_default(dsa_geometry* geom);
 /* Static English text for a status code. */
@@ -113,6 +138,17 @@ dsa_status dsa_cache_write(const dsa_geometry* geom, int32_t n_tokens, const int
                            uint16_t* ik_cache, int32_t n_seqs, int64_t tcap, void* stream);
 
 /*
+ * dsa_cache_write into paged pools (layouts above): the same rows, written at
+ * the page the block table gives for each token's position.  Rows whose
+ * sequence is outside [0, n_seqs) or whose position is outside the
+ * sequence's capacity (max_pages*128) are skipped.
+ */
+dsa_status dsa_cache_write_paged(const dsa_geometry* geom, int32_t n_tokens, const int32_t* tok_seq,
+                                 const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
+                                 const uint16_t* ik_new, const dsa_page_table* pages, int32_t n_seqs,
+                                 uint16_t* k_pool, uint16_t* v_pool, uint16_t* ik_pool, void* stream);
+
+/*
  * Region compression ([P1] steps ①②; [P2] section 区域压缩（CSA）; [P3] kernel
  * list: csa_compress_regions).  For every sequence b and region r in
  * [region_begin[b], region_end[b]) (clamped to [0, tcap/8) and to at most
@@ -135,6 +171,16 @@ dsa_status dsa_compress_regions(const dsa_geometry* geom, int32_t batch, const u
                                 int64_t tcap, const int32_t* region_begin,
                                 const int32_t* region_end, int32_t max_span, uint8_t* summ,
                                 float* scale, void* stream);
+
+/* dsa_compress_regions over paged pools: index_k rows are read from ik_pool
+ * and the summaries and scales written to summ_pool and scale_pool, all at
+ * the pages of sequence b's block-table row (b < batch).  Bit-exact with the
+ * contiguous call on the same data. */
+dsa_status dsa_compress_regions_paged(const dsa_geometry* geom, int32_t batch,
+                                      const dsa_page_table* pages, const uint16_t* ik_pool,
+                                      const int32_t* region_begin, const int32_t* region_end,
+                                      int32_t max_span, uint8_t* summ_pool, float* scale_pool,
+                                      void* stream);
 
 /* Workspace bytes dsa_score_topk needs for n_queries and max_regions. */
 size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_t n_queries,
@@ -177,6 +223,17 @@ dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries, const uin
                           int32_t max_regions, int32_t* sel, int32_t* n_sel, float* scores_out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* dsa_score_topk over paged summaries: the summary tiles and scales of query
+ * i's sequence are read from summ_pool/scale_pool at the pages of its
+ * block-table row.  Bit-identical to the contiguous call on the same data
+ * (same workspace rules). */
+dsa_status dsa_score_topk_paged(const dsa_geometry* geom, int32_t n_queries, const uint16_t* index_q,
+                                const float* z, const int32_t* q_seq, const int32_t* q_pos,
+                                int32_t n_seqs, const dsa_page_table* pages, const uint8_t* summ_pool,
+                                const float* scale_pool, int32_t max_regions, int32_t* sel,
+                                int32_t* n_sel, float* scores_out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dsa_sparse_gqa_decode needs for `batch` queries. */
 size_t dsa_sparse_gqa_workspace_size(const dsa_geometry* geom, int32_t batch);
 
@@ -198,6 +255,15 @@ dsa_status dsa_sparse_gqa_decode(const dsa_geometry* geom, int32_t batch, const 
                                  const int32_t* seq_len, const int32_t* sel, const int32_t* n_sel,
                                  uint16_t* out, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* dsa_sparse_gqa_decode over paged K/V pools (sequence b's block-table row,
+ * capacity max_pages*128).  Bit-identical to the contiguous call on the same
+ * data. */
+dsa_status dsa_sparse_gqa_decode_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                       const dsa_page_table* pages, const uint16_t* k_pool,
+                                       const uint16_t* v_pool, const int32_t* seq_len,
+                                       const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes dsa_decode_step needs. */
 size_t dsa_decode_step_workspace_size(const dsa_geometry* geom, int32_t batch, int32_t max_regions);
@@ -228,6 +294,17 @@ dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16
                            int32_t* sel, int32_t* n_sel, uint16_t* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* dsa_decode_step over paged pools (sequence b = block-table row b): the
+ * folded compression reads ik_pool and writes summ_pool/scale_pool; scoring
+ * and attention read the pools.  Bit-identical to the contiguous call on the
+ * same data. */
+dsa_status dsa_decode_step_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                 const uint16_t* index_q, const float* z, const dsa_page_table* pages,
+                                 const uint16_t* ik_pool, const uint16_t* k_pool,
+                                 const uint16_t* v_pool, const int32_t* seq_len, uint8_t* summ_pool,
+                                 float* scale_pool, int32_t max_regions, int32_t* sel, int32_t* n_sel,
+                                 uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dsa_sparse_gqa_prefill needs for n_queries queries. */
 size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries);
 
@@ -248,6 +325,15 @@ dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n_queries, c
                                   const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
                                   const int32_t* sel, const int32_t* n_sel, uint16_t* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* dsa_sparse_gqa_prefill over paged K/V pools (query i reads its sequence's
+ * block-table row).  Bit-identical to the contiguous call on the same data. */
+dsa_status dsa_sparse_gqa_prefill_paged(const dsa_geometry* geom, int32_t n_queries,
+                                        const uint16_t* q, const int32_t* q_seq, const int32_t* q_pos,
+                                        int32_t n_seqs, const dsa_page_table* pages,
+                                        const uint16_t* k_pool, const uint16_t* v_pool,
+                                        const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes swa_attention needs. */
 size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

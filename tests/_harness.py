@@ -164,7 +164,7 @@ def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=No
                summ=summ_logical(summ.cpu().numpy(), B, R), scale=scale.cpu().numpy().reshape(B, G, R),
                sel=sel.cpu().numpy().reshape(B, G, topk), nsel=nsel.cpu().numpy().reshape(B, G),
                scores=scores.cpu().numpy().reshape(B, G, R), out=bf16_np(out).reshape(B, HQ, D),
-               oracle={}, dev=dict(K=K, V=V, q=q, geom=geom))
+               oracle={}, dev=dict(K=K, V=V, q=q, geom=geom, ik=ik, iq=iq, z=z, summ=summ, scale=scale))
     hq, hiq, hz = host_queries(seed, B)
     if zero_z:
         hz = np.zeros_like(hz)
