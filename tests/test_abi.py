@@ -129,3 +129,54 @@ def test_decode_step_argument_checks(lib):
     assert lib.dsa_decode_step(ctypes.byref(g), 4, *bad, need, None) == 1
     assert lib.dsa_decode_step(ctypes.byref(g), 0, *([None] * 6 + [128, None, None, None, 8, None, None, None,
                                                                     None]), 0, None) == 0
+
+
+def _pages(bt=16, max_pages=4, n_pages=8):
+    return dsa.PageTable(ctypes.c_void_p(bt) if bt else None, max_pages, n_pages)
+
+
+PAGED_CALLS = {
+    "dsa_cache_write_paged": lambda L, g, pt, vp: L.dsa_cache_write_paged(g, 1, vp, vp, vp, vp, None, pt, 1, vp, vp,
+                                                                         None, None),
+    "dsa_compress_regions_paged": lambda L, g, pt, vp: L.dsa_compress_regions_paged(g, 1, pt, vp, vp, vp, 1, vp, vp,
+                                                                                   None),
+    "dsa_score_topk_paged": lambda L, g, pt, vp: L.dsa_score_topk_paged(g, 1, vp, vp, vp, vp, 1, pt, vp, vp, 8, vp,
+                                                                       vp, None, ctypes.c_void_p(256), 1 << 30,
+                                                                       None),
+    "dsa_sparse_gqa_decode_paged": lambda L, g, pt, vp: L.dsa_sparse_gqa_decode_paged(
+        g, 1, vp, pt, vp, vp, vp, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
+    "dsa_sparse_gqa_prefill_paged": lambda L, g, pt, vp: L.dsa_sparse_gqa_prefill_paged(
+        g, 1, vp, vp, vp, 1, pt, vp, vp, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
+    "dsa_decode_step_paged": lambda L, g, pt, vp: L.dsa_decode_step_paged(
+        g, 1, vp, vp, vp, pt, vp, vp, vp, vp, vp, vp, 8, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_CALLS))
+@pytest.mark.parametrize("pt,status", [
+    (None, 1),                                 # no page table
+    (dict(bt=0), 1),                           # no block table
+    (dict(max_pages=0), 1), (dict(n_pages=0), 1),
+    (dict(n_pages=(1 << 25) + 1), 2),          # region slots would overflow 31 bits
+    (dict(max_pages=(1 << 24) + 1), 2),        # more than 2^31 positions per sequence
+])
+def test_paged_calls_check_the_page_table(lib, name, pt, status):
+    g = dsa.geometry()
+    vp = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    p = None if pt is None else ctypes.byref(_pages(**pt))
+    assert PAGED_CALLS[name](lib, ctypes.byref(g), p, vp) == status
+    assert lib.dsa_last_error()
+
+
+def test_paged_calls_with_no_work_are_no_ops(lib):
+    g = ctypes.byref(dsa.geometry())
+    pt = ctypes.byref(_pages())
+    assert lib.dsa_cache_write_paged(g, 0, None, None, None, None, None, pt, 1, None, None, None, None) == 0
+    assert lib.dsa_compress_regions_paged(g, 0, pt, None, None, None, 1, None, None, None) == 0
+    assert lib.dsa_score_topk_paged(g, 0, None, None, None, None, 1, pt, None, None, 8, None, None, None, None, 0,
+                                    None) == 0
+    assert lib.dsa_sparse_gqa_decode_paged(g, 0, None, pt, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.dsa_sparse_gqa_prefill_paged(g, 0, None, None, None, 1, pt, None, None, None, None, None, None, 0,
+                                            None) == 0
+    assert lib.dsa_decode_step_paged(g, 0, None, None, None, pt, None, None, None, None, None, None, 8, None, None,
+                                     None, None, 0, None) == 0
