@@ -59,6 +59,8 @@ def lib():
         L.or_select.restype = i32
         L.or_attend.argtypes = [vp, vp, vp, i32, i32, i32, i64, vp, vp, i32, f64, vp]
         L.or_swa.argtypes = [vp, vp, vp, i32, i32, i32, i64, i64, f64, vp]
+        L.or_quantize_rows.argtypes = [vp, i64, i32, vp, vp]
+        L.or_attend_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, i32, f64, vp]
         L.or_dsa_query.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, i64,
                                    vp, vp, vp, vp]
         _lib = L
@@ -136,6 +138,36 @@ def attend(q, K, V, p, sel_lists, k=TOPK, tau=TAU):
         nsel[g] = lst.size
     out = np.zeros((Hq, D), dtype=np.float64)
     lib().or_attend(_p(q), _p(K), _p(V), G, D, Hq, int(p), _p(sel), _p(nsel), k, float(tau), _p(out))
+    return out
+
+
+def quantize_rows(X):
+    """FP8 cache rows: X [..][C] bf16 bits -> (E4M3 codes, same shape; fp32 scales [..])."""
+    X = _c(X, np.uint16)
+    C = X.shape[-1]
+    rows = X.reshape(-1, C)
+    codes = np.zeros(rows.shape, dtype=np.uint8)
+    scales = np.zeros(rows.shape[0], dtype=np.float32)
+    lib().or_quantize_rows(_p(rows), rows.shape[0], C, _p(codes), _p(scales))
+    return codes.reshape(X.shape), scales.reshape(X.shape[:-1])
+
+
+def attend_fp8(q, Kc, Ks, Vc, Vs, p, sel_lists, k=TOPK, tau=TAU):
+    """attend() over an FP8 cache: Kc/Vc [T][G][D] codes, Ks/Vs [T][G] row scales."""
+    q = _c(q, np.uint16)
+    Kc, Vc = _c(Kc, np.uint8), _c(Vc, np.uint8)
+    Ks, Vs = _c(Ks, np.float32), _c(Vs, np.float32)
+    Hq, D = q.shape
+    G = Kc.shape[1]
+    sel = np.full((G, k), -1, dtype=np.int32)
+    nsel = np.zeros(G, dtype=np.int32)
+    for g, lst in enumerate(sel_lists):
+        lst = np.asarray(lst, dtype=np.int32)
+        sel[g, :lst.size] = lst
+        nsel[g] = lst.size
+    out = np.zeros((Hq, D), dtype=np.float64)
+    lib().or_attend_fp8(_p(q), _p(Kc), _p(Ks), _p(Vc), _p(Vs), G, D, Hq, int(p), _p(sel), _p(nsel), k, float(tau),
+                        _p(out))
     return out
 
 

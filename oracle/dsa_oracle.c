@@ -241,6 +241,73 @@ void or_attend(const uint16_t* q, const uint16_t* K, const uint16_t* V, int G, i
 }
 
 /* ---------------------------------------------------------------------------
+ * FP8 K/V cache ([P3] section 一: keeping the KV cache in FP8 halves its size).
+ * The pages give no quantisation rule for it; the stand-in is the summary
+ * rule applied to every cached row: one fp32 scale per (token, group) row of
+ * K or V equal to amax / 448 over the row's bf16 values, each value divided
+ * by the scale in fp32 and rounded once to E4M3; scale 0 gives zero codes.
+ * X is [n_rows][C] bf16 bits; codes [n_rows][C], scales [n_rows].
+ * ------------------------------------------------------------------------- */
+void or_quantize_rows(const uint16_t* X, int64_t n_rows, int C, uint8_t* codes, float* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    float amax = 0.0f;
+    for (int d = 0; d < C; ++d) {
+      float a = fabsf(bf16_value_f(X[i * C + d]));
+      if (a > amax) amax = a;
+    }
+    float sc = amax / 448.0f;
+    scales[i] = sc;
+    for (int d = 0; d < C; ++d)
+      codes[i * C + d] = (sc == 0.0f) ? 0x00 : or_e4m3_encode(bf16_value_f(X[i * C + d]) / sc);
+  }
+}
+
+/* Sparse GQA over an FP8 cache: the sum of or_attend with every K and V value
+ * taken as the E4M3 value of its code times its row's scale (fp64).
+ * Kc, Vc [T][G][D] codes; Ks, Vs [T][G] scales. */
+void or_attend_fp8(const uint16_t* q, const uint8_t* Kc, const float* Ks, const uint8_t* Vc, const float* Vs,
+                   int G, int D, int Hq, int64_t p, const int32_t* sel, const int32_t* nsel, int k, double tau,
+                   double* out) {
+  int hpg = Hq / G;
+  int64_t cap = (int64_t)k * 8;
+  double* s = (double*)malloc(sizeof(double) * (size_t)cap);
+  int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+  for (int h = 0; h < Hq; ++h) {
+    int g = h / hpg;
+    int64_t n = 0;
+    for (int i = 0; i < nsel[g]; ++i) {
+      int64_t r = sel[(int64_t)g * k + i];
+      for (int64_t j = 8 * r; j <= 8 * r + 7 && j <= p; ++j) tok[n++] = j;
+    }
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < n; ++t) {
+      int64_t row = tok[t] * G + g;
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += bf16_value(q[(int64_t)h * D + d]) * (or_e4m3_value(Kc[row * D + d]) * (double)Ks[row]);
+      s[t] = tau * dot;
+      if (s[t] > mx) mx = s[t];
+    }
+    double den = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+      s[t] = exp(s[t] - mx);
+      den += s[t];
+    }
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < n; ++t) {
+        int64_t row = tok[t] * G + g;
+        acc += s[t] * (or_e4m3_value(Vc[row * D + d]) * (double)Vs[row]);
+      }
+      out[(int64_t)h * D + d] = n ? acc / den : 0.0;
+    }
+  }
+  free(s);
+  free(tok);
+}
+
+/* ---------------------------------------------------------------------------
  * Sliding-window attention ([P1] section 滑窗注意力只读最近 512 个 token:
  * a 512-token window; [P2] section 512 Token 的环形缓冲区): the query at position p attends to positions
  * max(0, p-W+1) .. p (W keys including itself), read here from the full K/V
