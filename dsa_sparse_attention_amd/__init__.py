@@ -32,6 +32,7 @@ ENTRY_POINTS = [
     "dsa_profile_enable", "dsa_profile_kernel_stats",
     "dsa_cache_write_paged", "dsa_compress_regions_paged", "dsa_score_topk_paged", "dsa_sparse_gqa_decode_paged",
     "dsa_sparse_gqa_prefill_paged", "dsa_decode_step_paged",
+    "dsa_cache_write_fp8", "dsa_sparse_gqa_decode_fp8", "dsa_sparse_gqa_prefill_fp8", "dsa_decode_step_fp8",
 ]
 
 
@@ -124,6 +125,11 @@ def load() -> ctypes.CDLL:
     L.dsa_sparse_gqa_decode_paged.argtypes = [G, i32, vp, P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_gqa_prefill_paged.argtypes = [G, i32, vp, vp, vp, i32, P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_decode_step_paged.argtypes = [G, i32, vp, vp, vp, P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.dsa_cache_write_fp8.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, vp, i32, i64, vp]
+    L.dsa_sparse_gqa_decode_fp8.argtypes = [G, i32, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_gqa_prefill_fp8.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.dsa_decode_step_fp8.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz,
+                                      vp]
     L.dsa_profile_enable.argtypes = [ctypes.c_int]
     L.dsa_profile_kernel_stats.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int32)]
@@ -506,6 +512,103 @@ def dsa_decode_step_paged(geom, q, index_q, z, pages: Pages, ik_pool, k_pool, v_
                                         _ptr(seq_len), _ptr(summ_pool), _ptr(scale_pool), max_regions, _ptr(sel),
                                         _ptr(n_sel), _ptr(out), _ptr(workspace), workspace.numel(),
                                         _stream(stream)))
+
+
+# ---- FP8 K/V caches ---------------------------------------------------------------------------
+def fp8_caches(n_seqs: int, tcap: int, device="cuda"):
+    """Zero-filled FP8 K/V caches (k8, v8 uint8 and kv_scale fp32) of n_seqs sequences, capacity tcap."""
+    R = tcap // REGION
+    return (torch.zeros(n_seqs * GROUPS * tcap * HEAD_DIM, dtype=torch.uint8, device=device),
+            torch.zeros(n_seqs * GROUPS * tcap * HEAD_DIM, dtype=torch.uint8, device=device),
+            torch.zeros(n_seqs * GROUPS * R * 16, dtype=torch.float32, device=device))
+
+
+def _fp8_check(k8, v8, kvs, n_seqs, tcap):
+    _dt(k8, torch.uint8, "k8_cache")
+    _dt(v8, torch.uint8, "v8_cache")
+    _dt(kvs, torch.float32, "kv_scale")
+    _numel_at_least(k8, n_seqs * GROUPS * tcap * HEAD_DIM, "k8_cache")
+    _numel_at_least(v8, n_seqs * GROUPS * tcap * HEAD_DIM, "v8_cache")
+    _numel_at_least(kvs, n_seqs * GROUPS * (tcap // REGION) * 16, "kv_scale")
+
+
+def dsa_cache_write_fp8(geom, tok_seq, tok_pos, k_new, v_new, k8, v8, kvs, n_seqs, tcap, stream=None):
+    n = tok_seq.numel()
+    for t, nm in ((tok_seq, "tok_seq"), (tok_pos, "tok_pos")):
+        _dt(t, torch.int32, nm)
+    _dt(k_new, torch.bfloat16, "k_new")
+    _dt(v_new, torch.bfloat16, "v_new")
+    _numel_at_least(k_new, n * GROUPS * HEAD_DIM, "k_new")
+    _numel_at_least(v_new, n * GROUPS * HEAD_DIM, "v_new")
+    _fp8_check(k8, v8, kvs, n_seqs, tcap)
+    _check(load().dsa_cache_write_fp8(ctypes.byref(geom), n, _ptr(tok_seq), _ptr(tok_pos), _ptr(k_new), _ptr(v_new),
+                                      _ptr(k8), _ptr(v8), _ptr(kvs), n_seqs, tcap, _stream(stream)))
+
+
+def dsa_sparse_gqa_decode_fp8(geom, q, k8, v8, kvs, tcap, seq_len, sel, n_sel, out, workspace=None, stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    _fp8_check(k8, v8, kvs, batch, tcap)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_workspace_size(geom, batch), q.device)
+    _check(load().dsa_sparse_gqa_decode_fp8(ctypes.byref(geom), batch, _ptr(q), _ptr(k8), _ptr(v8), _ptr(kvs), tcap,
+                                            _ptr(seq_len), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
+                                            workspace.numel(), _stream(stream)))
+
+
+def dsa_sparse_gqa_prefill_fp8(geom, q, q_seq, q_pos, n_seqs, k8, v8, kvs, tcap, sel, n_sel, out, workspace=None,
+                               stream=None):
+    nq = q_seq.numel()
+    for t, nm in ((q, "q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, nq * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, nq * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _fp8_check(k8, v8, kvs, n_seqs, tcap)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_prefill_workspace_size(geom, nq), q.device)
+    _check(load().dsa_sparse_gqa_prefill_fp8(ctypes.byref(geom), nq, _ptr(q), _ptr(q_seq), _ptr(q_pos), n_seqs,
+                                             _ptr(k8), _ptr(v8), _ptr(kvs), tcap, _ptr(sel), _ptr(n_sel), _ptr(out),
+                                             _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dsa_decode_step_fp8(geom, q, index_q, z, index_k, k8, v8, kvs, tcap, seq_len, summ, scale, max_regions, sel,
+                        n_sel, out, workspace=None, stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (index_q, "index_q"), (index_k, "index_k"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _dt(z, torch.float32, "z")
+    _dt(summ, torch.uint8, "summ")
+    _dt(scale, torch.float32, "scale")
+    R = tcap // REGION
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(index_q, batch * IDX_HEADS * PROXY, "index_q")
+    _numel_at_least(z, batch * IDX_HEADS, "z")
+    _numel_at_least(index_k, batch * GROUPS * tcap * PROXY, "index_k")
+    _numel_at_least(summ, batch * GROUPS * R * PROXY, "summ")
+    _numel_at_least(scale, batch * GROUPS * R, "scale")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    _fp8_check(k8, v8, kvs, batch, tcap)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_decode_step_workspace_size(geom, batch, max_regions), q.device)
+    _check(load().dsa_decode_step_fp8(ctypes.byref(geom), batch, _ptr(q), _ptr(index_q), _ptr(z), _ptr(index_k),
+                                      _ptr(k8), _ptr(v8), _ptr(kvs), tcap, _ptr(seq_len), _ptr(summ), _ptr(scale),
+                                      max_regions, _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
 
 
 def profile_enable(on: bool = True):

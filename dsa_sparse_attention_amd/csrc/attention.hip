@@ -300,6 +300,143 @@ __device__ __forceinline__ Region dsa_region(const uint16_t* k, const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------
+// FP8 K/V caches ([P3] section 一: an FP8 KV cache halves it).  Same core with
+// E4M3 codes: the codes are turned into bf16 exactly (v_cvt_scalef32_pk_bf16_fp8,
+// scale 1) right before their MFMA, the per-token K scale multiplies the
+// token's scores, and the per-token V scale multiplies the token's softmax
+// weight before P.V.  A 4-region chunk is 12 KB instead of 24 KB.
+// ---------------------------------------------------------------------------
+struct Region8 {
+  const uint8_t* k;  // the region's K8 (1536 bytes, region-tiled)
+  const uint8_t* v;  // its V8 ([D][8] bytes)
+  const float* sc;   // its 16 scales: K of tokens 0..7, then V
+  int lo, hi;
+};
+
+struct ChunkRegs8 {
+  u32x4 k[2][3];  // tile t, channel block s2: 16 channels of the lane's K token
+  uint2 v[12];    // the 8 tokens of region kb for channel 16nt + n
+  f32x4 ks[2], vs[2];
+  int lo, hi;
+};
+
+// 8 E4M3 codes (two dwords, channel order) -> bf16x8, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ Region8 dsa_region8(const uint8_t* k8, const uint8_t* v8, const float* kvs, int64_t slot,
+                                               int32_t rid, int64_t p) {
+  Region8 rg;
+  const int64_t c = p / kRegion;
+  if (rid < 0 || rid > c) {  // an empty region at the start of the cache
+    rg.k = k8;
+    rg.v = v8;
+    rg.sc = kvs;
+    rg.lo = 1;
+    rg.hi = 0;
+    return rg;
+  }
+  rg.k = k8 + slot * kRegionElems;
+  rg.v = v8 + slot * kRegionElems;
+  rg.sc = kvs + slot * kKvsPerRegion;
+  rg.lo = 0;
+  const int64_t last = p - (int64_t)rid * kRegion;
+  rg.hi = last >= 7 ? 7 : (int)last;
+  return rg;
+}
+
+// ra = region of this lane's K rows (entry n/4), rb = region of its softmax
+// weights, V and scales (entry kb), as in core_load.
+__device__ __forceinline__ void core_load8(ChunkRegs8& c, const Region8& ra, const Region8& rb) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const uint8_t* kp = ra.k + (kb * 4 + (n & 3)) * 16;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 3; ++s2) c.k[t][s2] = *(const u32x4*)(kp + (t * 3 + s2) * 256);
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) c.v[nt] = *(const uint2*)(rb.v + (16 * nt + n) * 8);
+  c.ks[0] = *(const f32x4*)(rb.sc);
+  c.ks[1] = *(const f32x4*)(rb.sc + 4);
+  c.vs[0] = *(const f32x4*)(rb.sc + 8);
+  c.vs[1] = *(const f32x4*)(rb.sc + 12);
+  c.lo = rb.lo;
+  c.hi = rb.hi;
+}
+
+__device__ __forceinline__ void core_compute8(CoreState& st, const bf16x8 qb[6], ChunkRegs8& c, float scale_log2) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    const u32x4 a = c.k[0][s >> 1], b = c.k[1][s >> 1];
+    const bf16x8 a0 = (s & 1) ? fp8x8_to_bf16(a.z, a.w) : fp8x8_to_bf16(a.x, a.y);
+    const bf16x8 a1 = (s & 1) ? fp8x8_to_bf16(b.z, b.w) : fp8x8_to_bf16(b.x, b.y);
+    s0 = mfma16x16x32(a0, qb[s], s0);
+    s1 = mfma16x16x32(a1, qb[s], s1);
+  }
+  bool ok[8];
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ok[i] = i >= c.lo && i <= c.hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = ok[i] ? s0[i] * c.ks[0][i] * scale_log2 : -INFINITY;
+    sv[4 + i] = ok[4 + i] ? s1[i] * c.ks[1][i] * scale_log2 : -INFINITY;
+  }
+  float cmax = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[i]);
+  cmax = max_across_rows(cmax);
+  const float m_new = fmaxf(st.m, cmax);
+  if (__any(m_new > st.m + 8.0f)) {  // lazy rescaling, as in core_compute
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) st.o[nt] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = st.m == -INFINITY ? 0.0f : st.m;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  // zero the V codes of masked positions (a stale code may be NaN) and take
+  // each weight times its token's V scale (0 where masked)
+  if (__any(!(c.lo <= 0 && c.hi >= 7))) {
+    uint32_t mx = 0, my = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mx |= ok[i] ? 0xFFu << (8 * i) : 0u;
+      my |= ok[4 + i] ? 0xFFu << (8 * i) : 0u;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) {
+      c.v[nt].x &= mx;
+      c.v[nt].y &= my;
+    }
+  }
+  float pw[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pw[i] = ok[i] ? p[i] * c.vs[0][i] : 0.0f;
+    pw[4 + i] = ok[4 + i] ? p[4 + i] * c.vs[1][i] : 0.0f;
+  }
+  u32x4 pp;
+  pp.x = pack_bf16x2(pw[0], pw[1]);
+  pp.y = pack_bf16x2(pw[2], pw[3]);
+  pp.z = pack_bf16x2(pw[4], pw[5]);
+  pp.w = pack_bf16x2(pw[6], pw[7]);
+  const bf16x8 pb = as_bf16x8(pp);
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) st.o[nt] = mfma16x16x32(fp8x8_to_bf16(c.v[nt].x, c.v[nt].y), pb, st.o[nt]);
+}
+
+// ---------------------------------------------------------------------------
 // Decode: block = (sequence b, group g, split s of 16 selected regions); its
 // 4 waves take one chunk of 4 regions each and are merged through LDS into
 // one partial (max, sum, unnormalised O) per split; k_merge combines splits.
@@ -315,6 +452,9 @@ struct DecodeArgs {
   const int32_t* nsel;
   float* part;  // [B][G][nsplit][16][kPartStride]
   CacheMap cm;  // where the K/V of each sequence live (capacity cm.R*8)
+  const uint8_t* k8;  // FP8 caches (FP8 instances only)
+  const uint8_t* v8;
+  const float* kvs;
   int32_t topk, nsplit;
   float scale_log2;
 };
@@ -323,6 +463,7 @@ constexpr int kPartStride = 4 + kHeadDim;  // per head: m, l, 2 unused, o[192] (
 
 constexpr int kORow = kHeadDim + 4;  // padded LDS row of one head's partial O
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
@@ -352,9 +493,16 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   core_init(st);
   const int32_t ra_id = ea < cnt ? ida : -1, rb_id = eb < cnt ? idb : -1;
   const int64_t cr = p / kRegion;
-  const Region ra = dsa_region(a.k, a.v, region_slot(a.cm, b, g, ra_id >= 0 && ra_id <= cr ? ra_id : 0), ra_id, p);
-  const Region rb = dsa_region(a.k, a.v, region_slot(a.cm, b, g, rb_id >= 0 && rb_id <= cr ? rb_id : 0), rb_id, p);
-  core_chunk(st, qb, ra, rb, a.scale_log2);
+  const int64_t slot_a = region_slot(a.cm, b, g, ra_id >= 0 && ra_id <= cr ? ra_id : 0);
+  const int64_t slot_b = region_slot(a.cm, b, g, rb_id >= 0 && rb_id <= cr ? rb_id : 0);
+  if constexpr (FP8) {
+    ChunkRegs8 c;
+    core_load8(c, dsa_region8(a.k8, a.v8, a.kvs, slot_a, ra_id, p), dsa_region8(a.k8, a.v8, a.kvs, slot_b, rb_id, p));
+    __builtin_amdgcn_sched_barrier(0);
+    core_compute8(st, qb, c, a.scale_log2);
+  } else {
+    core_chunk(st, qb, dsa_region(a.k, a.v, slot_a, ra_id, p), dsa_region(a.k, a.v, slot_b, rb_id, p), a.scale_log2);
+  }
   // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i)
   const float lt = core_total_l(st);
   if (kb == 0) {
@@ -448,6 +596,9 @@ struct PrefillArgs {
   uint16_t* part_o;  // [Nq][G][kPreSplits][16][D] bf16, unnormalised O
   float* part_ml;    // [Nq][G][kPreSplits][16][2] fp32, (max, sum)
   CacheMap cm;       // where the K/V of each sequence live (capacity cm.R*8)
+  const uint8_t* k8;  // FP8 caches (FP8 instances only)
+  const uint8_t* v8;
+  const float* kvs;
   int32_t nq, n_seqs, topk, rsplit;  // rsplit: regions per range
   float scale_log2;
 };
@@ -455,6 +606,7 @@ struct PrefillArgs {
 // Block = 4 waves = 4 consecutive queries of one KV group and one region
 // range; block index = range + kPreSplits * (query block + nqb * group), so
 // the GPU works through one group's K/V at a time.
+template <bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sgqa_prefill(PrefillArgs a) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -513,10 +665,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   core_init(st);
   const int32_t* my = ids[wave];
   const int32_t* myslot = slots[wave];
-  auto region_of = [&](int64_t e) -> Region {
-    return dsa_region(a.k, a.v, e < n ? myslot[e] : 0, e < n ? my[e] : -1, p);
-  };
-  core_run<0>(st, qb, n, region_of, a.scale_log2);
+  if constexpr (FP8) {
+    const int nn = lane & 15, kb = lane >> 4;
+    auto region8_of = [&](int64_t e) -> Region8 {
+      return dsa_region8(a.k8, a.v8, a.kvs, e < n ? myslot[e] : 0, e < n ? my[e] : -1, p);
+    };
+    // one chunk in registers per wave (two waves per SIMD overlap the loads)
+    for (int64_t e0 = 0; e0 < n; e0 += 4) {
+      ChunkRegs8 c;
+      core_load8(c, region8_of(e0 + (nn >> 2)), region8_of(e0 + kb));
+      __builtin_amdgcn_sched_barrier(0);
+      core_compute8(st, qb, c, a.scale_log2);
+    }
+  } else {
+    auto region_of = [&](int64_t e) -> Region {
+      return dsa_region(a.k, a.v, e < n ? myslot[e] : 0, e < n ? my[e] : -1, p);
+    };
+    core_run<0>(st, qb, n, region_of, a.scale_log2);
+  }
   // partial (max, sum, unnormalised O^T in bf16) of this range; an empty
   // range leaves (-inf, 0, 0), which the merge weighs 0
   const int hn = lane & 15, kb = lane >> 4;
@@ -1026,11 +1192,12 @@ namespace dsa {
 dsa_status sparse_gqa_decode(const char* who, const dsa_geometry* geom, int32_t batch, const uint16_t* q,
                              const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
                              const int32_t* seq_len, const int32_t* sel, const int32_t* n_sel, uint16_t* out,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream, const Fp8Kv* f8) {
   const std::string w(who);
   if (batch < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": batch must be >= 0");
   if (batch == 0) return DSA_OK;
-  if (!q || !k_cache || !v_cache || !seq_len || !sel || !n_sel || !out || !workspace)
+  const bool kv_ok = f8 ? (f8->k8 && f8->v8 && f8->kvs) : (k_cache && v_cache);
+  if (!q || !kv_ok || !seq_len || !sel || !n_sel || !out || !workspace)
     return fail(DSA_ERR_INVALID_ARGUMENT, w + ": NULL pointer");
   if ((size_t)workspace & 255) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": workspace must be 256-byte aligned");
   if (workspace_bytes < dsa_sparse_gqa_workspace_size(geom, batch))
@@ -1039,11 +1206,13 @@ dsa_status sparse_gqa_decode(const char* who, const dsa_geometry* geom, int32_t 
   DecodeArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache; a.seq_len = seq_len; a.sel = sel; a.nsel = n_sel;
   a.part = (float*)workspace; a.cm = cm; a.topk = geom->topk; a.nsplit = nsplit_of(geom->topk);
+  a.k8 = f8 ? f8->k8 : nullptr; a.v8 = f8 ? f8->v8 : nullptr; a.kvs = f8 ? f8->kvs : nullptr;
   a.scale_log2 = geom->softmax_scale * kLog2e;
   hipStream_t s = as_stream(stream);
   {
     ProfScope prof_("k_sgqa_decode", s);
-    hipLaunchKernelGGL(k_sgqa_decode, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
+    if (f8) hipLaunchKernelGGL(k_sgqa_decode<true>, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_sgqa_decode<false>, dim3(a.nsplit, kGroups, batch), dim3(256), 0, s, a);
   }
   dsa_status st = check_launch(who);
   if (st != DSA_OK) return st;
@@ -1083,6 +1252,20 @@ extern "C" dsa_status dsa_sparse_gqa_decode_paged(const dsa_geometry* geom, int3
                            out, workspace, workspace_bytes, stream);
 }
 
+extern "C" dsa_status dsa_sparse_gqa_decode_fp8(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                                const uint8_t* k8_cache, const uint8_t* v8_cache, const float* kv_scale,
+                                                int64_t tcap, const int32_t* seq_len, const int32_t* sel,
+                                                const int32_t* n_sel, uint16_t* out, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_decode_fp8: tcap must be a positive multiple of 128");
+  const Fp8Kv f8{k8_cache, v8_cache, kv_scale};
+  return sparse_gqa_decode("dsa_sparse_gqa_decode_fp8", geom, batch, q, nullptr, nullptr, contiguous_map(tcap),
+                           seq_len, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
+}
+
 extern "C" size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries) {
   (void)geom;
   if (n_queries <= 0) return 256;
@@ -1094,12 +1277,13 @@ static dsa_status sparse_gqa_prefill(const char* who, const dsa_geometry* geom, 
                                      const uint16_t* q, const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
                                      const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
                                      const int32_t* sel, const int32_t* n_sel, uint16_t* out, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     size_t workspace_bytes, void* stream, const Fp8Kv* f8 = nullptr) {
   const std::string w(who);
   if (n_queries < 0 || n_seqs < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": bad sizes");
   if (n_queries == 0) return DSA_OK;
   if (n_seqs == 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": n_seqs must be positive");
-  if (!q || !q_seq || !q_pos || !k_cache || !v_cache || !sel || !n_sel || !out || !workspace)
+  const bool kv_ok = f8 ? (f8->k8 && f8->v8 && f8->kvs) : (k_cache && v_cache);
+  if (!q || !q_seq || !q_pos || !kv_ok || !sel || !n_sel || !out || !workspace)
     return fail(DSA_ERR_INVALID_ARGUMENT, w + ": NULL pointer");
   if ((size_t)workspace & 255) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": workspace must be 256-byte aligned");
   if (workspace_bytes < dsa_sparse_gqa_prefill_workspace_size(geom, n_queries))
@@ -1114,13 +1298,15 @@ static dsa_status sparse_gqa_prefill(const char* who, const dsa_geometry* geom, 
   a.part_o = (uint16_t*)workspace;
   a.part_ml = (float*)((char*)workspace + align256(rows * kHeadDim * sizeof(uint16_t)));
   a.cm = cm; a.nq = n_queries; a.n_seqs = n_seqs; a.topk = geom->topk;
+  a.k8 = f8 ? f8->k8 : nullptr; a.v8 = f8 ? f8->v8 : nullptr; a.kvs = f8 ? f8->kvs : nullptr;
   a.rsplit = (int32_t)((cm.R + kPreSplits - 1) / kPreSplits);
   a.scale_log2 = geom->softmax_scale * kLog2e;
   hipStream_t s = as_stream(stream);
   {
     ProfScope prof_("k_sgqa_prefill", s);
-    hipLaunchKernelGGL(k_sgqa_prefill, dim3((unsigned)(kPreSplits * kGroups * ((n_queries + 3) / 4))), dim3(256),
-                       0, s, a);
+    const dim3 grid((unsigned)(kPreSplits * kGroups * ((n_queries + 3) / 4)));
+    if (f8) hipLaunchKernelGGL(k_sgqa_prefill<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_sgqa_prefill<false>, grid, dim3(256), 0, s, a);
   }
   dsa_status st = check_launch(who);
   if (st != DSA_OK) return st;
@@ -1159,6 +1345,21 @@ extern "C" dsa_status dsa_sparse_gqa_prefill_paged(const dsa_geometry* geom, int
   if (st != DSA_OK) return st;
   return sparse_gqa_prefill("dsa_sparse_gqa_prefill_paged", geom, n_queries, q, q_seq, q_pos, n_seqs, k_pool,
                             v_pool, cm, sel, n_sel, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" dsa_status dsa_sparse_gqa_prefill_fp8(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                                 const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                                 const uint8_t* k8_cache, const uint8_t* v8_cache,
+                                                 const float* kv_scale, int64_t tcap, const int32_t* sel,
+                                                 const int32_t* n_sel, uint16_t* out, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill_fp8: tcap must be a positive multiple of 128");
+  const Fp8Kv f8{k8_cache, v8_cache, kv_scale};
+  return sparse_gqa_prefill("dsa_sparse_gqa_prefill_fp8", geom, n_queries, q, q_seq, q_pos, n_seqs, nullptr, nullptr,
+                            contiguous_map(tcap), sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
 }
 
 extern "C" size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

@@ -80,6 +80,15 @@ __device__ __forceinline__ int k_tile_offset(int pos, int d) {
   return ((((pos >> 2) * 6 + (d % 48) / 8) * 4 + d / 48) * 4 + (pos & 3)) * 8 + (d & 7);
 }
 
+// FP8 K/V caches (per region slot): K8 [1536] bytes, region-tiled: the
+// 16-byte unit ((t*3 + s2)*4 + kb)*4 + pos%4 holds token pos (t = pos/4),
+// channels 48kb + 16s2 .. +15; V8 [D][8] bytes, region-transposed; KVS [16]
+// fp32: the K scales of the 8 tokens, then their V scales.
+__device__ __forceinline__ int k8_tile_offset(int pos, int d) {
+  return ((((pos >> 2) * 3 + (d % 48) / 16) * 4 + d / 48) * 4 + (pos & 3)) * 16 + (d & 15);
+}
+constexpr int kKvsPerRegion = 16;
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -167,11 +176,18 @@ inline CacheMap contiguous_map(int64_t tcap) {
 // n_pages <= kMaxPages so that region slots fit 31 bits) and builds its map.
 constexpr int32_t kMaxPages = 1 << 25;
 dsa_status paged_map(const char* who, const dsa_page_table* pt, CacheMap* m);
-// Sparse GQA decode over either cache arrangement (the decode step calls it).
+// FP8 K/V caches (K8, V8, scales; layouts above).
+struct Fp8Kv {
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* kvs;
+};
+// Sparse GQA decode over either cache arrangement, bf16 K/V (k_cache, v_cache)
+// or, when f8 is given, FP8 K/V (the decode steps call it).
 dsa_status sparse_gqa_decode(const char* who, const dsa_geometry* geom, int32_t batch, const uint16_t* q,
                              const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
                              const int32_t* seq_len, const int32_t* sel, const int32_t* n_sel, uint16_t* out,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream, const Fp8Kv* f8 = nullptr);
 
 // Instrumentation: while enabled (dsa_profile_enable), a ProfScope brackets
 // the kernel launched inside its lifetime with two hipEvents on the launch

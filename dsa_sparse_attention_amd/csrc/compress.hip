@@ -51,9 +51,67 @@ __global__ __launch_bounds__(256) void k_cache_write(
   }
 }
 
+// FP8 cache write: block = one token row, wave g = group g; lane l owns
+// channels 3l..3l+2.  Each (token, group) row of K and of V gets one fp32
+// scale amax/448 and its values x/scale (fp32) rounded once to E4M3 (the
+// summary rule applied per cached row; the pages only say an FP8 KV cache
+// halves it).
+__global__ __launch_bounds__(256) void k_cache_write_fp8(const int32_t* __restrict__ tok_seq,
+                                                         const int32_t* __restrict__ tok_pos,
+                                                         const uint16_t* __restrict__ k_new,
+                                                         const uint16_t* __restrict__ v_new, uint8_t* __restrict__ k8,
+                                                         uint8_t* __restrict__ v8, float* __restrict__ kvs,
+                                                         int32_t n_seqs, CacheMap cm) {
+  const int64_t i = blockIdx.x;
+  const int s = tok_seq[i];
+  const int64_t t = tok_pos[i];
+  if (s < 0 || s >= n_seqs || t < 0 || t >= cm.R * kRegion) return;
+  const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pos = (int)(t % kRegion);
+  const int64_t slot = region_slot(cm, s, g, t / kRegion);
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t* src = (which ? v_new : k_new) + (i * kGroups + g) * kHeadDim + 3 * lane;
+    float x[3];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) x[e] = bf16_to_f32(src[e]);
+    float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fabsf(x[2]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float sc = __fdiv_rn(amax, 448.0f);
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const int d = 3 * lane + e;
+      const uint8_t code = sc == 0.0f ? 0 : (uint8_t)e4m3_rne_sat(__fdiv_rn(x[e], sc));
+      if (which == 0) k8[slot * kRegionElems + k8_tile_offset(pos, d)] = code;
+      else v8[slot * kRegionElems + d * kRegion + pos] = code;
+    }
+    if (lane == 0) kvs[slot * kKvsPerRegion + which * kRegion + pos] = sc;
+  }
+}
+
 }  // namespace dsa
 
 using namespace dsa;
+
+extern "C" dsa_status dsa_cache_write_fp8(const dsa_geometry* geom, int32_t n_tokens, const int32_t* tok_seq,
+                                          const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
+                                          uint8_t* k8_cache, uint8_t* v8_cache, float* kv_scale, int32_t n_seqs,
+                                          int64_t tcap, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (n_tokens < 0 || n_seqs < 0 || tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write_fp8: bad sizes (tcap must be a positive multiple of 128)");
+  if (n_tokens == 0 || n_seqs == 0) return DSA_OK;
+  if (!tok_seq || !tok_pos || !k_new || !v_new || !k8_cache || !v8_cache || !kv_scale)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write_fp8: NULL pointer");
+  {
+    ProfScope prof_("k_cache_write", as_stream(stream));
+    hipLaunchKernelGGL(k_cache_write_fp8, dim3(n_tokens), dim3(256), 0, as_stream(stream), tok_seq, tok_pos, k_new,
+                       v_new, k8_cache, v8_cache, kv_scale, n_seqs, contiguous_map(tcap));
+  }
+  return check_launch("dsa_cache_write_fp8");
+}
 
 // Host: shared bodies of the contiguous and paged entry points.
 static dsa_status compress_regions(const char* who, const dsa_geometry* geom, int32_t batch,

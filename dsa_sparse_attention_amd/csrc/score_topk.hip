@@ -1721,13 +1721,14 @@ static dsa_status decode_step(const char* who, const dsa_geometry* geom, int32_t
                               const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
                               const int32_t* seq_len, uint8_t* summ, float* scale, int32_t max_regions,
                               int32_t* sel, int32_t* n_sel, uint16_t* out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              size_t workspace_bytes, void* stream, const Fp8Kv* f8 = nullptr) {
   const std::string w(who);
   if (batch < 0 || max_regions < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": bad sizes");
   if (batch == 0) return DSA_OK;
   if (max_regions == 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": max_regions must be positive");
-  if (!q || !index_q || !z || !index_k || !k_cache || !v_cache || !seq_len || !summ || !scale || !sel ||
-      !n_sel || !out || !workspace)
+  const bool kv_ok = f8 ? (f8->k8 && f8->v8 && f8->kvs) : (k_cache && v_cache);
+  if (!q || !index_q || !z || !index_k || !kv_ok || !seq_len || !summ || !scale || !sel || !n_sel || !out ||
+      !workspace)
     return fail(DSA_ERR_INVALID_ARGUMENT, w + ": NULL pointer");
   if ((size_t)workspace & 255) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": workspace must be 256-byte aligned");
   if (workspace_bytes < dsa_decode_step_workspace_size(geom, batch, max_regions))
@@ -1739,7 +1740,7 @@ static dsa_status decode_step(const char* who, const dsa_geometry* geom, int32_t
                                     max_regions, sel, n_sel, nullptr, index_k, summ, scale, workspace, s);
   if (st != DSA_OK) return st;
   return sparse_gqa_decode(who, geom, batch, q, k_cache, v_cache, cm, seq_len, sel, n_sel, out,
-                           (char*)workspace + ws1, workspace_bytes - ws1, stream);
+                           (char*)workspace + ws1, workspace_bytes - ws1, stream, f8);
 }
 
 extern "C" dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
@@ -1769,4 +1770,19 @@ extern "C" dsa_status dsa_decode_step_paged(const dsa_geometry* geom, int32_t ba
   if (st != DSA_OK) return st;
   return decode_step("dsa_decode_step_paged", geom, batch, q, index_q, z, ik_pool, k_pool, v_pool, cm, seq_len,
                      summ_pool, scale_pool, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" dsa_status dsa_decode_step_fp8(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                          const uint16_t* index_q, const float* z, const uint16_t* index_k,
+                                          const uint8_t* k8_cache, const uint8_t* v8_cache, const float* kv_scale,
+                                          int64_t tcap, const int32_t* seq_len, uint8_t* summ, float* scale,
+                                          int32_t max_regions, int32_t* sel, int32_t* n_sel, uint16_t* out,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step_fp8: tcap must be a positive multiple of 128");
+  const Fp8Kv f8{k8_cache, v8_cache, kv_scale};
+  return decode_step("dsa_decode_step_fp8", geom, batch, q, index_q, z, index_k, nullptr, nullptr, contiguous_map(tcap),
+                     seq_len, summ, scale, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
 }

@@ -70,6 +70,19 @@
  * Pages may be shared or reused by the caller in any way; page ids are
  * clamped into [0, n_pages), so a bad id reads or writes a wrong page of the
  * pools, never memory outside them.
+ *
+ * FP8 K/V caches ([P3] section 一: an FP8 KV cache halves it; the per-row
+ * rule is the summary stand-in applied to each cached row): every (token,
+ * group) row of K and of V is stored as E4M3 codes of x/s with one fp32
+ * scale s = amax/448 of the row (fp32 IEEE division, one rounding to nearest
+ * even, saturating; s = 0 gives zero codes).  Per region slot (contiguous
+ * order [B][G][R] as above):
+ *   k8_cache [B][G][R][1536] uint8 region-tiled: the 16-byte unit
+ *            ((t*3 + s2)*4 + kb)*4 + p%4 holds token p (t = p/4), channels
+ *            48kb + 16s2 .. +15
+ *   v8_cache [B][G][R][D][8] uint8 region-transposed
+ *   kv_scale [B][G][R][16]   fp32: the K scales of tokens 0..7, then their
+ *            V scales
  */
 #ifndef DSA_MI355X_H
 #define DSA_MI355X_H
@@ -147,6 +160,17 @@ dsa_status dsa_cache_write_paged(const dsa_geometry* geom, int32_t n_tokens, con
                                  const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
                                  const uint16_t* ik_new, const dsa_page_table* pages, int32_t n_seqs,
                                  uint16_t* k_pool, uint16_t* v_pool, uint16_t* ik_pool, void* stream);
+
+/*
+ * dsa_cache_write for FP8 K/V caches: the K and V rows of the new tokens are
+ * quantised (rule above; bit-exact) and stored in k8_cache, v8_cache and
+ * kv_scale of n_seqs sequences with capacity tcap.  index_k stays bf16
+ * (write it with dsa_cache_write).  Rows out of range are skipped.
+ */
+dsa_status dsa_cache_write_fp8(const dsa_geometry* geom, int32_t n_tokens, const int32_t* tok_seq,
+                               const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
+                               uint8_t* k8_cache, uint8_t* v8_cache, float* kv_scale, int32_t n_seqs,
+                               int64_t tcap, void* stream);
 
 /*
  * Region compression ([P1] steps ①②; [P2] section 区域压缩（CSA）; [P3] kernel
@@ -265,6 +289,16 @@ dsa_status dsa_sparse_gqa_decode_paged(const dsa_geometry* geom, int32_t batch, 
                                        const int32_t* sel, const int32_t* n_sel, uint16_t* out,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* dsa_sparse_gqa_decode over FP8 K/V caches: each K and V value is the E4M3
+ * value of its code times its row's scale; the codes enter bf16 MFMAs
+ * exactly, K scales multiply the scores and V scales the softmax weights
+ * (fp32), weights rounded to bf16 for P.V.  Same workspace. */
+dsa_status dsa_sparse_gqa_decode_fp8(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                     const uint8_t* k8_cache, const uint8_t* v8_cache,
+                                     const float* kv_scale, int64_t tcap, const int32_t* seq_len,
+                                     const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dsa_decode_step needs. */
 size_t dsa_decode_step_workspace_size(const dsa_geometry* geom, int32_t batch, int32_t max_regions);
 
@@ -305,6 +339,15 @@ dsa_status dsa_decode_step_paged(const dsa_geometry* geom, int32_t batch, const 
                                  float* scale_pool, int32_t max_regions, int32_t* sel, int32_t* n_sel,
                                  uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* dsa_decode_step with FP8 K/V caches (index_k, summaries and scales as in
+ * dsa_decode_step); the attention is dsa_sparse_gqa_decode_fp8's. */
+dsa_status dsa_decode_step_fp8(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                               const uint16_t* index_q, const float* z, const uint16_t* index_k,
+                               const uint8_t* k8_cache, const uint8_t* v8_cache, const float* kv_scale,
+                               int64_t tcap, const int32_t* seq_len, uint8_t* summ, float* scale,
+                               int32_t max_regions, int32_t* sel, int32_t* n_sel, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dsa_sparse_gqa_prefill needs for n_queries queries. */
 size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries);
 
@@ -334,6 +377,15 @@ dsa_status dsa_sparse_gqa_prefill_paged(const dsa_geometry* geom, int32_t n_quer
                                         const uint16_t* k_pool, const uint16_t* v_pool,
                                         const int32_t* sel, const int32_t* n_sel, uint16_t* out,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* dsa_sparse_gqa_prefill over FP8 K/V caches (maths as in
+ * dsa_sparse_gqa_decode_fp8). */
+dsa_status dsa_sparse_gqa_prefill_fp8(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                      const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                      const uint8_t* k8_cache, const uint8_t* v8_cache,
+                                      const float* kv_scale, int64_t tcap, const int32_t* sel,
+                                      const int32_t* n_sel, uint16_t* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Workspace bytes swa_attention needs. */
 size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
