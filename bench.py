@@ -280,6 +280,116 @@ def paged_prefill(cfg, order="interleaved"):
     return step, (pools, pages, q, iq, z, rb, re_, qseq, qpos, sel, nsel, out, ws1, ws3, geom)
 
 
+def fp8_kv(seed, B, tcap):
+    """FP8 K/V caches of B sequences filled through dsa_cache_write_fp8 with the generator's K/V rows
+    (token-major rows generated on the GPU, written, then freed)."""
+    import numpy as np
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+    s = torch.cuda.current_stream().cuda_stream
+    geom = dsa.geometry()
+    k8, v8, kvs = dsa.fp8_caches(B, tcap)
+    tok_seq = torch.tensor(np.repeat(np.arange(B), tcap).astype(np.int32), device="cuda")
+    tok_pos = torch.tensor(np.tile(np.arange(tcap), B).astype(np.int32), device="cuda")
+    rows = {}
+    for tid in (gi.TID_K, gi.TID_V):
+        t = torch.empty(B * tcap * G * D, dtype=torch.bfloat16, device="cuda")
+        gi.dev_tokens(t.data_ptr(), s, seed, tid, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_TOKEN_MAJOR)
+        rows[tid] = t
+    dsa.dsa_cache_write_fp8(geom, tok_seq, tok_pos, rows[gi.TID_K], rows[gi.TID_V], k8, v8, kvs, B, tcap)
+    torch.cuda.synchronize()
+    del rows, tok_seq, tok_pos
+    torch.cuda.empty_cache()
+    return k8, v8, kvs
+
+
+def fp8_decode(cfg):
+    """The decode workload with FP8 K/V caches (dsa_decode_step_fp8)."""
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+    _, keep = setup_decode(cfg)
+    ik, K, V, q, iq, z, summ, scale = keep[:8]
+    slen, sel, nsel, out = keep[12], keep[13], keep[14], keep[15]
+    B, tcap = cfg["batch"], cfg["context"]
+    R = tcap // REG
+    del keep, K, V
+    torch.cuda.empty_cache()
+    k8, v8, kvs = fp8_kv(gi.SEED_BASE + cfg["seed_index"], B, tcap)
+    geom = dsa.geometry(topk=cfg["topk"])
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(geom, B, R))
+    L = dsa.load()
+    p = Calls.p
+    args = (ctypes.byref(geom), B, p(q), p(iq), p(z), p(ik), p(k8), p(v8), p(kvs), tcap, p(slen), p(summ), p(scale),
+            R, p(sel), p(nsel), p(out), p(ws), ws.numel())
+
+    def step(st):
+        rc = L.dsa_decode_step_fp8(*args, st)
+        if rc:
+            raise RuntimeError(f"fp8 decode step failed: {rc} {L.dsa_last_error().decode()}")
+
+    return step, (ik, q, iq, z, summ, scale, slen, sel, nsel, out, k8, v8, kvs, ws, geom)
+
+
+def fp8_prefill(cfg):
+    """The prefill workload with FP8 K/V caches (dsa_sparse_gqa_prefill_fp8)."""
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+    _, keep = setup_prefill(cfg)
+    ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, sel, nsel, out = keep[:15]
+    P0, n, topk = cfg["prefix"], cfg["chunk"], cfg["topk"]
+    tcap = P0 + n
+    R = tcap // REG
+    del keep, K, V
+    torch.cuda.empty_cache()
+    k8, v8, kvs = fp8_kv(gi.SEED_BASE + cfg["seed_index"], 1, tcap)
+    geom = dsa.geometry(topk=topk)
+    ws1 = dsa.workspace(dsa.dsa_score_topk_workspace_size(geom, n, R))
+    ws3 = dsa.workspace(dsa.dsa_sparse_gqa_prefill_workspace_size(geom, n))
+    L = dsa.load()
+    p = Calls.p
+    gp = ctypes.byref(geom)
+    a_comp = (gp, 1, p(ik), tcap, p(rb), p(re_), tcap // REG - P0 // REG, p(summ), p(scale))
+    a_score = (gp, n, p(iq), p(z), p(qseq), p(qpos), 1, p(summ), p(scale), tcap, R, p(sel), p(nsel), None, p(ws1),
+               ws1.numel())
+    a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, p(k8), p(v8), p(kvs), tcap, p(sel), p(nsel), p(out), p(ws3),
+              ws3.numel())
+
+    def step(st):
+        rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
+              or L.dsa_sparse_gqa_prefill_fp8(*a_attn, st))
+        if rc:
+            raise RuntimeError(f"fp8 prefill step failed: {rc} {L.dsa_last_error().decode()}")
+
+    return step, (ik, q, iq, z, summ, scale, rb, re_, qseq, qpos, sel, nsel, out, k8, v8, kvs, ws1, ws3, geom)
+
+
+def measure_fp8(args, result):
+    """Both headline workloads with FP8 K/V caches (the attention gathers half the bytes; results
+    differ from the bf16 ones by the E4M3 rounding of K and V, ~4% rel-RMS)."""
+    import torch
+    res = {}
+    for key, setup, cfg, unit_n, kern in (("decode", fp8_decode, DECODE, DECODE["batch"], "k_sgqa_decode"),
+                                          ("prefill", fp8_prefill, PREFILL, PREFILL["chunk"], "k_sgqa_prefill")):
+        if key == "prefill" and args.no_prefill:
+            continue
+        step, keep = setup(cfg)
+        steps = args.steps if key == "decode" else max(3, args.steps // 3)
+        secs, eager, st = timed(step, steps, max(1, args.warmup // 2), [kern], graph=args.graph)
+        del keep
+        torch.cuda.empty_cache()
+        ms = secs * 1e3 / steps
+        base = result.get("ms_per_step") if key == "decode" else result.get("prefill", {}).get("ms_per_step")
+        res[key] = {"workload": cfg["name"] + ", K/V caches in FP8 (E4M3, one scale per token row)",
+                    "value": round(unit_n * steps / secs, 1), "unit": "queries/s" if key == "decode" else "tokens/s",
+                    "ms_per_step": round(ms, 4), "vs_bf16": round(base / ms, 4) if base else None,
+                    "attention_us": round(st[kern][0] * 1e3, 2)}
+        log(f"fp8 {key}: {unit_n * steps / secs:.0f}/s, {ms:.3f} ms/step")
+    result["fp8_kv"] = res
+
+
 def measure_paged(args, result):
     """Both headline workloads again with the caches in 128-position pages handed out in batch
     order, and the decode step once more with shuffled pages: the cost of the block-table
@@ -564,6 +674,7 @@ def main():
                     help="only the 3:1 layer mix and sliding-window prefill (for per-workload profiles)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache runs of the two headline workloads")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 K/V cache runs of the two headline workloads")
     ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
     ap.add_argument("--separate", action="store_true",
                     help="decode step as three calls (compress, score_topk, sparse_gqa_decode) instead of dsa_decode_step")
@@ -618,9 +729,11 @@ def main():
     # ---- prefill at 64K
     if not args.no_prefill:
         measure_prefill(args, result)
-    # ---- the same two workloads over paged caches
+    # ---- the same two workloads over paged caches, and with FP8 K/V caches
     if not args.no_paged and not args.swa_only:
         measure_paged(args, result)
+    if not args.no_fp8 and not args.swa_only:
+        measure_fp8(args, result)
     # ---- the 3:1 sliding-window / DSA stack (decode) and a sliding-window prefill chunk
     if not args.no_swa:
         measure_swa(args, result)
