@@ -409,7 +409,7 @@ def measure_paged(args, result):
         ms = secs * 1e3 / steps
         base = result.get("ms_per_step") if key != "prefill" else result.get("prefill", {}).get("ms_per_step")
         res[key] = {"workload": cfg["name"] + f", caches in 128-position pages ({order} page ids)",
-                    "value": round(unit_n * steps / secs, 1), "unit": "queries/s" if key == "decode" else "tokens/s",
+                    "value": round(unit_n * steps / secs, 1), "unit": "tokens/s" if key == "prefill" else "queries/s",
                     "ms_per_step": round(ms, 4), "vs_contiguous": round(base / ms, 4) if base else None}
         log(f"paged {key}: {unit_n * steps / secs:.0f}/s, {ms:.3f} ms/step")
     result["paged"] = res
