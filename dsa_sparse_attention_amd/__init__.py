@@ -33,6 +33,8 @@ ENTRY_POINTS = [
     "dsa_cache_write_paged", "dsa_compress_regions_paged", "dsa_score_topk_paged", "dsa_sparse_gqa_decode_paged",
     "dsa_sparse_gqa_prefill_paged", "dsa_decode_step_paged",
     "dsa_cache_write_fp8", "dsa_sparse_gqa_decode_fp8", "dsa_sparse_gqa_prefill_fp8", "dsa_decode_step_fp8",
+    "dsa_cache_write_fp8_paged", "dsa_sparse_gqa_decode_fp8_paged", "dsa_sparse_gqa_prefill_fp8_paged",
+    "dsa_decode_step_fp8_paged",
 ]
 
 
@@ -130,6 +132,11 @@ def load() -> ctypes.CDLL:
     L.dsa_sparse_gqa_prefill_fp8.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     L.dsa_decode_step_fp8.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz,
                                       vp]
+    L.dsa_cache_write_fp8_paged.argtypes = [G, i32, vp, vp, vp, vp, P, i32, vp, vp, vp, vp]
+    L.dsa_sparse_gqa_decode_fp8_paged.argtypes = [G, i32, vp, P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_gqa_prefill_fp8_paged.argtypes = [G, i32, vp, vp, vp, i32, P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_decode_step_fp8_paged.argtypes = [G, i32, vp, vp, vp, P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                            sz, vp]
     L.dsa_profile_enable.argtypes = [ctypes.c_int]
     L.dsa_profile_kernel_stats.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int32)]
@@ -609,6 +616,98 @@ def dsa_decode_step_fp8(geom, q, index_q, z, index_k, k8, v8, kvs, tcap, seq_len
                                       _ptr(k8), _ptr(v8), _ptr(kvs), tcap, _ptr(seq_len), _ptr(summ), _ptr(scale),
                                       max_regions, _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
                                       workspace.numel(), _stream(stream)))
+
+
+# ---- FP8 K/V caches in pages ------------------------------------------------------------------
+def fp8_pools(n_pages: int, device="cuda"):
+    """Zero-filled paged FP8 pools (k8, v8 uint8 and kv_scale fp32) of n_pages pages."""
+    per = n_pages * GROUPS * PAGE_POSITIONS
+    return (torch.zeros(per * HEAD_DIM, dtype=torch.uint8, device=device),
+            torch.zeros(per * HEAD_DIM, dtype=torch.uint8, device=device),
+            torch.zeros(per // REGION * 16, dtype=torch.float32, device=device))
+
+
+def _fp8_pools_check(pages: Pages, k8, v8, kvs):
+    _fp8_check(k8, v8, kvs, 1, pages.n_pages * PAGE_POSITIONS)
+
+
+def dsa_cache_write_fp8_paged(geom, tok_seq, tok_pos, k_new, v_new, pages: Pages, n_seqs, k8, v8, kvs, stream=None):
+    n = tok_seq.numel()
+    for t, nm in ((tok_seq, "tok_seq"), (tok_pos, "tok_pos")):
+        _dt(t, torch.int32, nm)
+    _dt(k_new, torch.bfloat16, "k_new")
+    _dt(v_new, torch.bfloat16, "v_new")
+    _numel_at_least(k_new, n * GROUPS * HEAD_DIM, "k_new")
+    _numel_at_least(v_new, n * GROUPS * HEAD_DIM, "v_new")
+    _fp8_pools_check(pages, k8, v8, kvs)
+    _check(load().dsa_cache_write_fp8_paged(ctypes.byref(geom), n, _ptr(tok_seq), _ptr(tok_pos), _ptr(k_new),
+                                            _ptr(v_new), _pages(pages, n_seqs), n_seqs, _ptr(k8), _ptr(v8), _ptr(kvs),
+                                            _stream(stream)))
+
+
+def dsa_sparse_gqa_decode_fp8_paged(geom, q, pages: Pages, k8, v8, kvs, seq_len, sel, n_sel, out, workspace=None,
+                                    stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    _fp8_pools_check(pages, k8, v8, kvs)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_workspace_size(geom, batch), q.device)
+    _check(load().dsa_sparse_gqa_decode_fp8_paged(ctypes.byref(geom), batch, _ptr(q), _pages(pages, batch), _ptr(k8),
+                                                  _ptr(v8), _ptr(kvs), _ptr(seq_len), _ptr(sel), _ptr(n_sel),
+                                                  _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dsa_sparse_gqa_prefill_fp8_paged(geom, q, q_seq, q_pos, n_seqs, pages: Pages, k8, v8, kvs, sel, n_sel, out,
+                                     workspace=None, stream=None):
+    nq = q_seq.numel()
+    for t, nm in ((q, "q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, nq * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, nq * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _fp8_pools_check(pages, k8, v8, kvs)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_prefill_workspace_size(geom, nq), q.device)
+    _check(load().dsa_sparse_gqa_prefill_fp8_paged(ctypes.byref(geom), nq, _ptr(q), _ptr(q_seq), _ptr(q_pos), n_seqs,
+                                                   _pages(pages, n_seqs), _ptr(k8), _ptr(v8), _ptr(kvs), _ptr(sel),
+                                                   _ptr(n_sel), _ptr(out), _ptr(workspace), workspace.numel(),
+                                                   _stream(stream)))
+
+
+def dsa_decode_step_fp8_paged(geom, q, index_q, z, pages: Pages, ik_pool, k8, v8, kvs, seq_len, summ_pool,
+                              scale_pool, max_regions, sel, n_sel, out, workspace=None, stream=None):
+    batch = seq_len.numel()
+    for t, nm in ((q, "q"), (index_q, "index_q"), (ik_pool, "ik_pool"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((seq_len, "seq_len"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _dt(z, torch.float32, "z")
+    _numel_at_least(q, batch * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, batch * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(index_q, batch * IDX_HEADS * PROXY, "index_q")
+    _numel_at_least(z, batch * IDX_HEADS, "z")
+    _numel_at_least(ik_pool, pages.n_pages * PAGE_POSITIONS * GROUPS * PROXY, "ik_pool")
+    _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    _pools_check(pages, None, None, None, summ_pool, scale_pool)
+    _fp8_pools_check(pages, k8, v8, kvs)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_decode_step_workspace_size(geom, batch, max_regions), q.device)
+    _check(load().dsa_decode_step_fp8_paged(ctypes.byref(geom), batch, _ptr(q), _ptr(index_q), _ptr(z),
+                                            _pages(pages, batch), _ptr(ik_pool), _ptr(k8), _ptr(v8), _ptr(kvs),
+                                            _ptr(seq_len), _ptr(summ_pool), _ptr(scale_pool), max_regions, _ptr(sel),
+                                            _ptr(n_sel), _ptr(out), _ptr(workspace), workspace.numel(),
+                                            _stream(stream)))
 
 
 def profile_enable(on: bool = True):

@@ -1266,6 +1266,22 @@ extern "C" dsa_status dsa_sparse_gqa_decode_fp8(const dsa_geometry* geom, int32_
                            seq_len, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
 }
 
+extern "C" dsa_status dsa_sparse_gqa_decode_fp8_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                                      const dsa_page_table* pages, const uint8_t* k8_pool,
+                                                      const uint8_t* v8_pool, const float* kvs_pool,
+                                                      const int32_t* seq_len, const int32_t* sel, const int32_t* n_sel,
+                                                      uint16_t* out, void* workspace, size_t workspace_bytes,
+                                                      void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  CacheMap cm;
+  st = paged_map("dsa_sparse_gqa_decode_fp8_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  const Fp8Kv f8{k8_pool, v8_pool, kvs_pool};
+  return sparse_gqa_decode("dsa_sparse_gqa_decode_fp8_paged", geom, batch, q, nullptr, nullptr, cm, seq_len, sel,
+                           n_sel, out, workspace, workspace_bytes, stream, &f8);
+}
+
 extern "C" size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries) {
   (void)geom;
   if (n_queries <= 0) return 256;
@@ -1360,6 +1376,22 @@ extern "C" dsa_status dsa_sparse_gqa_prefill_fp8(const dsa_geometry* geom, int32
   const Fp8Kv f8{k8_cache, v8_cache, kv_scale};
   return sparse_gqa_prefill("dsa_sparse_gqa_prefill_fp8", geom, n_queries, q, q_seq, q_pos, n_seqs, nullptr, nullptr,
                             contiguous_map(tcap), sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
+}
+
+extern "C" dsa_status dsa_sparse_gqa_prefill_fp8_paged(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                                       const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                                       const dsa_page_table* pages, const uint8_t* k8_pool,
+                                                       const uint8_t* v8_pool, const float* kvs_pool,
+                                                       const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                                       void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  CacheMap cm;
+  st = paged_map("dsa_sparse_gqa_prefill_fp8_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  const Fp8Kv f8{k8_pool, v8_pool, kvs_pool};
+  return sparse_gqa_prefill("dsa_sparse_gqa_prefill_fp8_paged", geom, n_queries, q, q_seq, q_pos, n_seqs, nullptr,
+                            nullptr, cm, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
 }
 
 extern "C" size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

@@ -94,23 +94,44 @@ __global__ __launch_bounds__(256) void k_cache_write_fp8(const int32_t* __restri
 
 using namespace dsa;
 
+static dsa_status cache_write_fp8(const char* who, int32_t n_tokens, const int32_t* tok_seq, const int32_t* tok_pos,
+                                  const uint16_t* k_new, const uint16_t* v_new, uint8_t* k8, uint8_t* v8, float* kvs,
+                                  int32_t n_seqs, const CacheMap& cm, void* stream) {
+  if (n_tokens < 0 || n_seqs < 0) return fail(DSA_ERR_INVALID_ARGUMENT, std::string(who) + ": bad sizes");
+  if (n_tokens == 0 || n_seqs == 0) return DSA_OK;
+  if (!tok_seq || !tok_pos || !k_new || !v_new || !k8 || !v8 || !kvs)
+    return fail(DSA_ERR_INVALID_ARGUMENT, std::string(who) + ": NULL pointer");
+  {
+    ProfScope prof_("k_cache_write", as_stream(stream));
+    hipLaunchKernelGGL(k_cache_write_fp8, dim3(n_tokens), dim3(256), 0, as_stream(stream), tok_seq, tok_pos, k_new,
+                       v_new, k8, v8, kvs, n_seqs, cm);
+  }
+  return check_launch(who);
+}
+
 extern "C" dsa_status dsa_cache_write_fp8(const dsa_geometry* geom, int32_t n_tokens, const int32_t* tok_seq,
                                           const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
                                           uint8_t* k8_cache, uint8_t* v8_cache, float* kv_scale, int32_t n_seqs,
                                           int64_t tcap, void* stream) {
   dsa_status st = check_geometry(geom);
   if (st != DSA_OK) return st;
-  if (n_tokens < 0 || n_seqs < 0 || tcap <= 0 || tcap % kTcapAlign)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write_fp8: bad sizes (tcap must be a positive multiple of 128)");
-  if (n_tokens == 0 || n_seqs == 0) return DSA_OK;
-  if (!tok_seq || !tok_pos || !k_new || !v_new || !k8_cache || !v8_cache || !kv_scale)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write_fp8: NULL pointer");
-  {
-    ProfScope prof_("k_cache_write", as_stream(stream));
-    hipLaunchKernelGGL(k_cache_write_fp8, dim3(n_tokens), dim3(256), 0, as_stream(stream), tok_seq, tok_pos, k_new,
-                       v_new, k8_cache, v8_cache, kv_scale, n_seqs, contiguous_map(tcap));
-  }
-  return check_launch("dsa_cache_write_fp8");
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_cache_write_fp8: tcap must be a positive multiple of 128");
+  return cache_write_fp8("dsa_cache_write_fp8", n_tokens, tok_seq, tok_pos, k_new, v_new, k8_cache, v8_cache, kv_scale,
+                         n_seqs, contiguous_map(tcap), stream);
+}
+
+extern "C" dsa_status dsa_cache_write_fp8_paged(const dsa_geometry* geom, int32_t n_tokens, const int32_t* tok_seq,
+                                                const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
+                                                const dsa_page_table* pages, int32_t n_seqs, uint8_t* k8_pool,
+                                                uint8_t* v8_pool, float* kvs_pool, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  CacheMap cm;
+  st = paged_map("dsa_cache_write_fp8_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  return cache_write_fp8("dsa_cache_write_fp8_paged", n_tokens, tok_seq, tok_pos, k_new, v_new, k8_pool, v8_pool,
+                         kvs_pool, n_seqs, cm, stream);
 }
 
 // Host: shared bodies of the contiguous and paged entry points.

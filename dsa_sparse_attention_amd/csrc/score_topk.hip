@@ -1786,3 +1786,19 @@ extern "C" dsa_status dsa_decode_step_fp8(const dsa_geometry* geom, int32_t batc
   return decode_step("dsa_decode_step_fp8", geom, batch, q, index_q, z, index_k, nullptr, nullptr, contiguous_map(tcap),
                      seq_len, summ, scale, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
 }
+
+extern "C" dsa_status dsa_decode_step_fp8_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                                const uint16_t* index_q, const float* z, const dsa_page_table* pages,
+                                                const uint16_t* ik_pool, const uint8_t* k8_pool, const uint8_t* v8_pool,
+                                                const float* kvs_pool, const int32_t* seq_len, uint8_t* summ_pool,
+                                                float* scale_pool, int32_t max_regions, int32_t* sel, int32_t* n_sel,
+                                                uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  CacheMap cm;
+  st = paged_map("dsa_decode_step_fp8_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  const Fp8Kv f8{k8_pool, v8_pool, kvs_pool};
+  return decode_step("dsa_decode_step_fp8_paged", geom, batch, q, index_q, z, ik_pool, nullptr, nullptr, cm, seq_len,
+                     summ_pool, scale_pool, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
+}

@@ -83,6 +83,9 @@
  *   v8_cache [B][G][R][D][8] uint8 region-transposed
  *   kv_scale [B][G][R][16]   fp32: the K scales of tokens 0..7, then their
  *            V scales
+ * In paged form the same per-slot blocks live in pools sharing the page
+ * numbering above: k8_pool [n_pages][G][16][1536], v8_pool
+ * [n_pages][G][16][D][8] (uint8), kvs_pool [n_pages][G][16][16] (fp32).
  */
 #ifndef DSA_MI355X_H
 #define DSA_MI355X_H
@@ -171,6 +174,13 @@ dsa_status dsa_cache_write_fp8(const dsa_geometry* geom, int32_t n_tokens, const
                                const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
                                uint8_t* k8_cache, uint8_t* v8_cache, float* kv_scale, int32_t n_seqs,
                                int64_t tcap, void* stream);
+
+/* dsa_cache_write_fp8 into paged FP8 pools (page of each position from the
+ * block table). */
+dsa_status dsa_cache_write_fp8_paged(const dsa_geometry* geom, int32_t n_tokens, const int32_t* tok_seq,
+                                     const int32_t* tok_pos, const uint16_t* k_new, const uint16_t* v_new,
+                                     const dsa_page_table* pages, int32_t n_seqs, uint8_t* k8_pool,
+                                     uint8_t* v8_pool, float* kvs_pool, void* stream);
 
 /*
  * Region compression ([P1] steps ①②; [P2] section 区域压缩（CSA）; [P3] kernel
@@ -299,6 +309,15 @@ dsa_status dsa_sparse_gqa_decode_fp8(const dsa_geometry* geom, int32_t batch, co
                                      const int32_t* sel, const int32_t* n_sel, uint16_t* out,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* dsa_sparse_gqa_decode_fp8 over paged FP8 pools; bit-identical to the
+ * contiguous call on the same data. */
+dsa_status dsa_sparse_gqa_decode_fp8_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                           const dsa_page_table* pages, const uint8_t* k8_pool,
+                                           const uint8_t* v8_pool, const float* kvs_pool,
+                                           const int32_t* seq_len, const int32_t* sel,
+                                           const int32_t* n_sel, uint16_t* out, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dsa_decode_step needs. */
 size_t dsa_decode_step_workspace_size(const dsa_geometry* geom, int32_t batch, int32_t max_regions);
 
@@ -348,6 +367,16 @@ dsa_status dsa_decode_step_fp8(const dsa_geometry* geom, int32_t batch, const ui
                                int32_t max_regions, int32_t* sel, int32_t* n_sel, uint16_t* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* dsa_decode_step_fp8 over paged pools (index_k, summaries and scales as in
+ * dsa_decode_step_paged, K/V in FP8 pools). */
+dsa_status dsa_decode_step_fp8_paged(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                     const uint16_t* index_q, const float* z, const dsa_page_table* pages,
+                                     const uint16_t* ik_pool, const uint8_t* k8_pool,
+                                     const uint8_t* v8_pool, const float* kvs_pool,
+                                     const int32_t* seq_len, uint8_t* summ_pool, float* scale_pool,
+                                     int32_t max_regions, int32_t* sel, int32_t* n_sel, uint16_t* out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes dsa_sparse_gqa_prefill needs for n_queries queries. */
 size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n_queries);
 
@@ -386,6 +415,16 @@ dsa_status dsa_sparse_gqa_prefill_fp8(const dsa_geometry* geom, int32_t n_querie
                                       const float* kv_scale, int64_t tcap, const int32_t* sel,
                                       const int32_t* n_sel, uint16_t* out, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/* dsa_sparse_gqa_prefill_fp8 over paged FP8 pools; bit-identical to the
+ * contiguous call on the same data. */
+dsa_status dsa_sparse_gqa_prefill_fp8_paged(const dsa_geometry* geom, int32_t n_queries,
+                                            const uint16_t* q, const int32_t* q_seq,
+                                            const int32_t* q_pos, int32_t n_seqs,
+                                            const dsa_page_table* pages, const uint8_t* k8_pool,
+                                            const uint8_t* v8_pool, const float* kvs_pool,
+                                            const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes swa_attention needs. */
 size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

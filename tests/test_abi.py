@@ -149,6 +149,14 @@ PAGED_CALLS = {
         g, 1, vp, vp, vp, 1, pt, vp, vp, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
     "dsa_decode_step_paged": lambda L, g, pt, vp: L.dsa_decode_step_paged(
         g, 1, vp, vp, vp, pt, vp, vp, vp, vp, vp, vp, 8, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
+    "dsa_cache_write_fp8_paged": lambda L, g, pt, vp: L.dsa_cache_write_fp8_paged(g, 1, vp, vp, vp, vp, pt, 1, vp, vp,
+                                                                                 vp, None),
+    "dsa_sparse_gqa_decode_fp8_paged": lambda L, g, pt, vp: L.dsa_sparse_gqa_decode_fp8_paged(
+        g, 1, vp, pt, vp, vp, vp, vp, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
+    "dsa_sparse_gqa_prefill_fp8_paged": lambda L, g, pt, vp: L.dsa_sparse_gqa_prefill_fp8_paged(
+        g, 1, vp, vp, vp, 1, pt, vp, vp, vp, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
+    "dsa_decode_step_fp8_paged": lambda L, g, pt, vp: L.dsa_decode_step_fp8_paged(
+        g, 1, vp, vp, vp, pt, vp, vp, vp, vp, vp, vp, vp, 8, vp, vp, vp, ctypes.c_void_p(256), 1 << 30, None),
 }
 
 
@@ -180,3 +188,10 @@ def test_paged_calls_with_no_work_are_no_ops(lib):
                                             None) == 0
     assert lib.dsa_decode_step_paged(g, 0, None, None, None, pt, None, None, None, None, None, None, 8, None, None,
                                      None, None, 0, None) == 0
+    assert lib.dsa_cache_write_fp8_paged(g, 0, None, None, None, None, pt, 1, None, None, None, None) == 0
+    assert lib.dsa_sparse_gqa_decode_fp8_paged(g, 0, None, pt, None, None, None, None, None, None, None, None, 0,
+                                               None) == 0
+    assert lib.dsa_sparse_gqa_prefill_fp8_paged(g, 0, None, None, None, 1, pt, None, None, None, None, None, None,
+                                                None, 0, None) == 0
+    assert lib.dsa_decode_step_fp8_paged(g, 0, None, None, None, pt, None, None, None, None, None, None, None, 8,
+                                         None, None, None, None, 0, None) == 0
