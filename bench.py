@@ -39,6 +39,9 @@ MIX = dict(name="3:1 layer mix, decode: three sliding-window layers (512-token r
 SWA_PREFILL = dict(name="sliding-window layer, chunked prefill: 2048 new tokens after 63,488 (512-token ring)",
                    prefix=63488, chunk=2048, seed_index=4)
 W = 512
+# correlated variant of the prefill chunk: anchors every 64 queries, 10% of each query's own i.i.d.
+# index_q mixed in (adjacent selections then share ~88% of their regions)
+CORRELATED = dict(every=64, noise=0.1)
 
 
 def log(*a):
@@ -415,7 +418,7 @@ def measure_paged(args, result):
     result["paged"] = res
 
 
-def setup_prefill(cfg):
+def setup_prefill(cfg, correlated=False, merged=False):
     import torch
     import dsa_inputs as gi
     import dsa_sparse_attention_amd as dsa
@@ -439,6 +442,10 @@ def setup_prefill(cfg):
     gi.dev_flat(q.data_ptr(), s, seed, gi.TID_Q, q.numel(), 0, 1.0)
     gi.dev_flat(iq.data_ptr(), s, seed, gi.TID_IQ, iq.numel(), 0, gi.IK_SCALE)
     gi.dev_flat(z.data_ptr(), s, seed, gi.TID_Z, z.numel(), 1)
+    if correlated:  # neighbouring queries select overlapping regions
+        iqh, zh = gi.host_correlated_index_queries(seed, n, HI, P, **CORRELATED)
+        iq.copy_(torch.from_numpy(iqh.view("int16").ravel()).view(torch.bfloat16))
+        z.copy_(torch.from_numpy(zh.ravel()))
     summ = torch.zeros(G * R * P, dtype=torch.uint8, device="cuda")
     scale = torch.zeros(G * R, dtype=torch.float32, device="cuda")
     i32 = lambda v: torch.tensor(v, dtype=torch.int32, device="cuda")
@@ -460,9 +467,10 @@ def setup_prefill(cfg):
                p(ws1), ws1.numel())
     a_attn = (gp, n, p(q), p(qseq), p(qpos), 1, p(K), p(V), tcap, p(sel), p(nsel), p(out), p(ws3), ws3.numel())
 
+    attend = L.dsa_sparse_gqa_prefill_merged if merged else L.dsa_sparse_gqa_prefill
+
     def step(st):
-        rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
-              or L.dsa_sparse_gqa_prefill(*a_attn, st))
+        rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st) or attend(*a_attn, st))
         if rc:
             raise RuntimeError(f"prefill step failed: {rc} {L.dsa_last_error().decode()}")
 
@@ -675,6 +683,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache runs of the two headline workloads")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 K/V cache runs of the two headline workloads")
+    ap.add_argument("--no-merged", action="store_true",
+                    help="skip the neighbour-merged prefill runs (correlated and i.i.d. chunks)")
     ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
     ap.add_argument("--separate", action="store_true",
                     help="decode step as three calls (compress, score_topk, sparse_gqa_decode) instead of dsa_decode_step")
@@ -734,6 +744,8 @@ def main():
         measure_paged(args, result)
     if not args.no_fp8 and not args.swa_only:
         measure_fp8(args, result)
+    if not args.no_merged and not args.no_prefill:
+        measure_merged(args, result)
     # ---- the 3:1 sliding-window / DSA stack (decode) and a sliding-window prefill chunk
     if not args.no_swa:
         measure_swa(args, result)
@@ -821,6 +833,48 @@ def measure_prefill(args, result):
         "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in pst.items()},
     }
     log(f"prefill: {n * psteps / psecs:.0f} tok/s, {pms:.3f} ms/step")
+
+
+def union_of_neighbours(sel, nsel, n, topk, width=4):
+    """Mean number of distinct regions per group in the selections of `width` consecutive queries."""
+    import numpy as np
+    s = sel.view(n, G, topk).cpu().numpy()
+    c = nsel.view(n, G).cpu().numpy()
+    us = [len(set().union(*[set(s[i, g, :c[i, g]].tolist()) for i in range(i0, i0 + width)]))
+          for i0 in range(0, n - width + 1, width) for g in range(G)]
+    return float(np.mean(us))
+
+
+def measure_merged(args, result):
+    """Neighbour-merged prefill (dsa_sparse_gqa_prefill_merged) against the per-query attention on the
+    prefill chunk with correlated neighbouring queries, and on the unrelated (i.i.d.) chunk."""
+    import torch
+    n = PREFILL["chunk"]
+    fl = prefill_flops(PREFILL["prefix"], n, PREFILL["topk"])
+    res = {}
+    for key, corr, merged in (("correlated_per_query", True, False), ("correlated_merged", True, True),
+                              ("iid_merged", False, True)):
+        step, keep = setup_prefill(PREFILL, correlated=corr, merged=merged)
+        kern = "k_sgqa_prefill_merged" if merged else "k_sgqa_prefill"
+        steps = max(3, args.steps // 3)
+        secs, _, st = timed(step, steps, max(1, args.warmup // 2), [kern, "k_sgqa_merge"], graph=args.graph)
+        sel, nsel = keep[12], keep[13]
+        union = union_of_neighbours(sel, nsel, n, PREFILL["topk"]) if merged else None
+        del keep
+        torch.cuda.empty_cache()
+        att_ms = st[kern][0]
+        tf = fl["attend"] / (att_ms * 1e-3) / 1e12
+        res[key] = {"workload": PREFILL["name"] + (", correlated neighbouring queries (anchors every "
+                                                   f"{CORRELATED['every']}, noise {CORRELATED['noise']})"
+                                                   if corr else ", i.i.d. queries"),
+                    "value": round(n * steps / secs, 1), "unit": "tokens/s", "ms_per_step": round(secs * 1e3 / steps, 3),
+                    "attention": {"kernel": kern, "avg_launch_us": round(att_ms * 1e3, 1),
+                                  "achieved_TFLOPs": round(tf, 2), "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                  "merge_us": round(st["k_sgqa_merge"][0] * 1e3, 1)}}
+        if union is not None:
+            res[key]["mean_union_of_4_neighbours_per_group"] = round(union, 1)
+        log(f"{key}: {n * steps / secs:.0f} tok/s, attention {att_ms * 1e3:.0f} us")
+    result["merged_prefill"] = res
 
 
 def measure_swa(args, result):

@@ -15,6 +15,11 @@ Workload recipe (tensor ids; the seed of workload i is ``SEED_BASE + i``):
   Q=1, K=2, V=3 ~ N(0,1) bf16; index_k=4, index_q=5 ~ N(0,1)/16 bf16;
   z=6 ~ U(0,1) fp32; planted-region mask=7, planted coefficients=9;
   sliding-window layer l (0-based) uses ids + 16*(l+1).
+Correlated prefill chunk (neighbouring queries select overlapping regions):
+  anchors of index_q (id 10, N(0,1)/16) and of z (id 11, U(0,1)) every ``every``
+  queries; query i blends anchors a = i // every and a + 1 with t = (i mod every)
+  / every (norm-preserving weights for index_q, linear for z) and mixes in
+  ``noise`` of its own i.i.d. index_q (id 5).  See ``host_correlated_index_queries``.
 """
 from __future__ import annotations
 
@@ -26,6 +31,7 @@ import numpy as np
 
 SEED_BASE = 0xD5A00000
 TID_Q, TID_K, TID_V, TID_IK, TID_IQ, TID_Z, TID_MASK, TID_COEF = 1, 2, 3, 4, 5, 6, 7, 9
+TID_IQ_ANCHOR, TID_Z_ANCHOR = 10, 11
 IK_SCALE = 1.0 / 16.0
 
 LAYOUT_GROUP_MAJOR, LAYOUT_REGION_T, LAYOUT_TOKEN_MAJOR, LAYOUT_KTILED = 0, 1, 2, 3
@@ -202,6 +208,28 @@ def host_index_k(seed, T, G, P, b, t0, nt, planted=False) -> np.ndarray:
     out = np.empty((nt, G, P), dtype=np.uint16)
     _host_lib().dsagen_index_k(seed, TID_IK, TID_MASK, TID_COEF, int(planted), T, G, P, b, t0, nt, _ptr(out))
     return out
+
+
+def host_correlated_index_queries(seed, nq, heads=16, P=256, every=64, noise=0.1):
+    """index_q [nq][heads][P] (bf16 bits) and z [nq][heads] (fp32) of a prefill chunk whose neighbouring
+    queries are correlated: a smooth path between anchor queries every ``every`` queries, plus ``noise``
+    of each query's own i.i.d. index_q (noise = 1 gives the i.i.d. workload back).  float32 arithmetic,
+    one bf16 rounding at the end."""
+    na = nq // every + 2
+    A = bf16_to_f32(host_normal_bf16(seed, TID_IQ_ANCHOR, na * heads * P, IK_SCALE)).reshape(na, heads, P)
+    Z = host_uniform_f32(seed, TID_Z_ANCHOR, na * heads).reshape(na, heads)
+    own = bf16_to_f32(host_normal_bf16(seed, TID_IQ, nq * heads * P, IK_SCALE)).reshape(nq, heads, P)
+    i = np.arange(nq)
+    a = i // every
+    t = ((i % every) / np.float32(every)).astype(np.float32)
+    nrm = np.sqrt((np.float32(1) - t) * (np.float32(1) - t) + t * t).astype(np.float32)
+    w0 = ((np.float32(1) - t) / nrm).astype(np.float32)[:, None, None]
+    w1 = (t / nrm).astype(np.float32)[:, None, None]
+    path = w0 * A[a] + w1 * A[a + 1]
+    c_path = np.float32(np.sqrt(np.float32(1) - np.float32(noise) * np.float32(noise)))
+    iq = c_path * path + np.float32(noise) * own
+    z = ((np.float32(1) - t)[:, None] * Z[a] + t[:, None] * Z[a + 1]).astype(np.float32)
+    return bf16_rne(iq.astype(np.float32)), z
 
 
 # ----------------------------------------------------------------------------------------------

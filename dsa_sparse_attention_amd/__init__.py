@@ -34,7 +34,7 @@ ENTRY_POINTS = [
     "dsa_sparse_gqa_prefill_paged", "dsa_decode_step_paged",
     "dsa_cache_write_fp8", "dsa_sparse_gqa_decode_fp8", "dsa_sparse_gqa_prefill_fp8", "dsa_decode_step_fp8",
     "dsa_cache_write_fp8_paged", "dsa_sparse_gqa_decode_fp8_paged", "dsa_sparse_gqa_prefill_fp8_paged",
-    "dsa_decode_step_fp8_paged",
+    "dsa_decode_step_fp8_paged", "dsa_sparse_gqa_prefill_merged", "dsa_sparse_gqa_prefill_merged_paged",
 ]
 
 
@@ -132,6 +132,8 @@ def load() -> ctypes.CDLL:
     L.dsa_sparse_gqa_prefill_fp8.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     L.dsa_decode_step_fp8.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz,
                                       vp]
+    L.dsa_sparse_gqa_prefill_merged.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_gqa_prefill_merged_paged.argtypes = [G, i32, vp, vp, vp, i32, P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_cache_write_fp8_paged.argtypes = [G, i32, vp, vp, vp, vp, P, i32, vp, vp, vp, vp]
     L.dsa_sparse_gqa_decode_fp8_paged.argtypes = [G, i32, vp, P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_gqa_prefill_fp8_paged.argtypes = [G, i32, vp, vp, vp, i32, P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -343,6 +345,28 @@ def dsa_sparse_gqa_prefill(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap
                                          _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def dsa_sparse_gqa_prefill_merged(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap, sel, n_sel, out,
+                                  workspace=None, stream=None):
+    """Neighbour-merged prefill: the result of dsa_sparse_gqa_prefill, 4 consecutive queries sharing each
+    region of their selections' union."""
+    nq = q_seq.numel()
+    for t, nm in ((q, "q"), (out, "out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, nq * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, nq * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _numel_at_least(k_cache, n_seqs * GROUPS * tcap * HEAD_DIM, "k_cache")
+    _numel_at_least(v_cache, n_seqs * GROUPS * tcap * HEAD_DIM, "v_cache")
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_prefill_workspace_size(geom, nq), q.device)
+    _check(load().dsa_sparse_gqa_prefill_merged(ctypes.byref(geom), nq, _ptr(q), _ptr(q_seq), _ptr(q_pos), n_seqs,
+                                                _ptr(k_cache), _ptr(v_cache), tcap, _ptr(sel), _ptr(n_sel),
+                                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 def swa_attention_workspace_size(geom, window, n_seqs, max_new_per_seq) -> int:
     return int(load().swa_attention_workspace_size(ctypes.byref(geom), window, n_seqs, max_new_per_seq))
 
@@ -495,6 +519,26 @@ def dsa_sparse_gqa_prefill_paged(geom, q, q_seq, q_pos, n_seqs, pages: Pages, k_
                                                _pages(pages, n_seqs), _ptr(k_pool), _ptr(v_pool), _ptr(sel),
                                                _ptr(n_sel), _ptr(out), _ptr(workspace), workspace.numel(),
                                                _stream(stream)))
+
+
+def dsa_sparse_gqa_prefill_merged_paged(geom, q, q_seq, q_pos, n_seqs, pages: Pages, k_pool, v_pool, sel, n_sel,
+                                        out, workspace=None, stream=None):
+    nq = q_seq.numel()
+    for t, nm in ((q, "q"), (out, "out")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((q_seq, "q_seq"), (q_pos, "q_pos"), (sel, "sel"), (n_sel, "n_sel")):
+        _dt(t, torch.int32, nm)
+    _numel_at_least(q, nq * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(out, nq * Q_HEADS * HEAD_DIM, "out")
+    _numel_at_least(sel, nq * GROUPS * geom.topk, "sel")
+    _numel_at_least(n_sel, nq * GROUPS, "n_sel")
+    _pools_check(pages, k_pool, v_pool)
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_gqa_prefill_workspace_size(geom, nq), q.device)
+    _check(load().dsa_sparse_gqa_prefill_merged_paged(ctypes.byref(geom), nq, _ptr(q), _ptr(q_seq), _ptr(q_pos),
+                                                      n_seqs, _pages(pages, n_seqs), _ptr(k_pool), _ptr(v_pool),
+                                                      _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
+                                                      workspace.numel(), _stream(stream)))
 
 
 def dsa_decode_step_paged(geom, q, index_q, z, pages: Pages, ik_pool, k_pool, v_pool, seq_len, summ_pool,

@@ -1140,6 +1140,194 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #undef DSA_BAND_ISSUE
 }
 
+// ---------------------------------------------------------------------------
+// Neighbour-merged prefill ([P5], Sparse GQA paragraph: the selections of
+// neighbouring tokens are merged so that the GPU is used better).  Exact
+// form: a wave takes 4 consecutive queries of one KV group and walks the
+// union of their selections inside one region range, ascending; each union
+// region's K/V is read once and applied to the 4 queries under their
+// membership bits (a query that did not select the region gives it weight
+// 0), so every query gets the attention over its own selection.  A query's
+// list is taken as a set (a repeated id counts once).  When the 4 queries
+// belong to different sequences, the wave makes one pass per sequence.
+//
+// The union of the range is built in windows of kMrgWin regions: a byte per
+// region collects the membership bits (LDS atomics), a wave-wide scan of the
+// nonzero bytes lists the union in ascending order, then the entries' cache
+// slots are looked up.  The walk prefetches the next 4-region chunk into the
+// wave's own LDS slot with direct-to-LDS copies while the current chunk
+// computes from registers, so no barrier is shared with other waves.
+// Partials go to the layout of k_sgqa_prefill and k_sgqa_merge_pre merges.
+// ---------------------------------------------------------------------------
+constexpr int kMrgQ = 4;        // queries per wave
+constexpr int kMrgWin = 1024;   // regions per union window (64 lanes x 16 bytes)
+
+struct MergeWave {
+  uint8_t chunk[kChunkBytes];   // the prefetched chunk: 4 regions, K then V, as in the band ring
+  uint32_t bits[kMrgWin / 4];   // membership byte of each region of the window
+  int32_t rid[kMrgWin];         // the window's union, ascending
+  int32_t slot[kMrgWin];        // its cache slots
+  uint8_t msk[kMrgWin];         // its membership bytes
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_sgqa_prefill_merged(
+    PrefillArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, nn = lane & 15, kb = lane >> 4;
+  const int nqb = (a.nq + 4 * kMrgQ - 1) / (4 * kMrgQ);
+  const int split = blockIdx.x % kPreSplits;
+  const int rest = blockIdx.x / kPreSplits;
+  const int g = rest / nqb;
+  const int64_t q0 = ((int64_t)(rest % nqb) * 4 + wave) * kMrgQ;
+  __shared__ __attribute__((aligned(16))) MergeWave lds_all[4];
+  MergeWave& L = lds_all[wave];
+  if (q0 >= a.nq) return;  // the whole wave; no barrier is shared with the others
+  const int64_t tcap = a.cm.R * kRegion;
+  int32_t sq[kMrgQ], cq[kMrgQ];
+  int64_t pq[kMrgQ];
+  uint32_t todo = 0;
+  bf16x8 qb[kMrgQ][6];
+  CoreState st[kMrgQ];
+#pragma unroll
+  for (int j = 0; j < kMrgQ; ++j) {
+    const int64_t qi = q0 + j;
+    const bool live = qi < a.nq;
+    const int64_t qc = live ? qi : q0;
+    int32_t s = a.qseq[qc];
+    sq[j] = s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
+    int64_t p = a.qpos[qc];
+    pq[j] = p < 0 ? 0 : (p >= tcap ? tcap - 1 : p);
+    int32_t c = live ? a.nsel[qc * kGroups + g] : 0;
+    cq[j] = c < 0 ? 0 : (c > a.topk ? a.topk : c);
+    todo |= live ? 1u << j : 0u;
+    load_q(a.q, qc, g, qb[j]);
+    core_init(st[j]);
+  }
+  const int64_t r0 = (int64_t)split * a.rsplit;
+  const int64_t r1 = r0 + a.rsplit < a.cm.R ? r0 + a.rsplit : a.cm.R;
+  while (todo) {
+    // one pass per sequence among the wave's queries
+    const int lead = __builtin_ctz(todo);
+    int32_t sp = sq[0];
+#pragma unroll
+    for (int j = 1; j < kMrgQ; ++j) sp = lead == j ? sq[j] : sp;
+    uint32_t mem = 0;
+#pragma unroll
+    for (int j = 0; j < kMrgQ; ++j) mem |= ((todo >> j) & 1u) && sq[j] == sp ? 1u << j : 0u;
+    todo &= ~mem;
+    for (int64_t w0 = r0; w0 < r1; w0 += kMrgWin) {
+      const int64_t w1 = w0 + kMrgWin < r1 ? w0 + kMrgWin : r1;
+      // membership bytes (a wave's LDS operations complete in issue order)
+#pragma unroll
+      for (int i = 0; i < kMrgWin / 4 / 64; ++i) L.bits[64 * i + lane] = 0u;
+#pragma unroll
+      for (int j = 0; j < kMrgQ; ++j) {
+        if (!((mem >> j) & 1u)) continue;
+        const int32_t* lst = a.sel + ((q0 + j) * kGroups + g) * a.topk;
+        const int64_t cur = pq[j] / kRegion;
+        for (int e = lane; e < cq[j]; e += 64) {
+          const int64_t r = lst[e];
+          if (r >= w0 && r < w1 && r <= cur) {
+            const int o = (int)(r - w0);
+            atomicOr(&L.bits[o >> 2], (1u << j) << (8 * (o & 3)));
+          }
+        }
+      }
+      // the union in ascending order: lane l owns regions w0 + 16l .. +15
+      const u32x4 mb = *(const u32x4*)&L.bits[4 * lane];
+      const uint32_t words[4] = {mb.x, mb.y, mb.z, mb.w};
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cnt += ((words[w] >> (8 * b)) & 0xffu) ? 1u : 0u;
+      const uint32_t incl = wave_incl_scan(cnt);
+      const int nu = __builtin_amdgcn_readlane((int)incl, 63);
+      uint32_t at = incl - cnt;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t m = (words[w] >> (8 * b)) & 0xffu;
+          if (m) {
+            L.rid[at] = (int32_t)(w0 + 16 * lane + 4 * w + b);
+            L.msk[at] = (uint8_t)m;
+            ++at;
+          }
+        }
+      if (nu == 0) continue;
+      for (int e = lane; e < nu; e += 64) {
+        const int32_t r = L.rid[e];
+        L.slot[e] = (int32_t)slot_in(a.cm, a.cm.bt ? page_of(a.cm, sp, r) : 0, sp, g, r);
+      }
+      // walk the union 4 regions at a time; the copy of the next chunk runs
+      // while the current one computes
+      auto issue = [&](int e0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = e0 + i < nu ? e0 + i : nu - 1;  // past the end: a re-read, masked
+          const int64_t sl = L.slot[e];
+          const uint8_t* bk = (const uint8_t*)(a.k + sl * kRegionElems);
+          const uint8_t* bv = (const uint8_t*)(a.v + sl * kRegionElems);
+          LdsPtr d = (LdsPtr)(&L.chunk[0] + i * kBandRegion);
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            __builtin_amdgcn_global_load_lds((const void*)(bk + 1024 * k + 16 * lane), d + 1024 * k, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(bv + 1024 * k + 16 * lane), d + kRegionBytes + 1024 * k,
+                                             16, 0, 0);
+          }
+        }
+      };
+      issue(0);
+      for (int e0 = 0; e0 < nu; e0 += 4) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the chunk's copies have landed
+        ChunkRegs cr;
+        const uint8_t* kp = &L.chunk[0] + (nn >> 2) * kBandRegion + ((kb * 4 + (nn & 3)) * 8) * 2;
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+          cr.k0[q] = *(const u32x4*)(kp + (q * 16) * 16);
+          cr.k1[q] = *(const u32x4*)(kp + ((6 + q) * 16) * 16);
+        }
+        const uint8_t* vp = &L.chunk[0] + kb * kBandRegion + kRegionBytes;
+#pragma unroll
+        for (int nt = 0; nt < 12; ++nt) cr.v[nt] = *(const u32x4*)(vp + (16 * nt + nn) * 16);
+        const int e = e0 + kb;
+        const int m = e < nu ? L.msk[e] : 0;
+        const int64_t first = (int64_t)(e < nu ? L.rid[e] : 0) * kRegion;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is free for the next copies
+        if (e0 + 4 < nu) issue(e0 + 4);
+        int lo[kMrgQ], hi[kMrgQ];
+#pragma unroll
+        for (int j = 0; j < kMrgQ; ++j) {
+          const bool in = (m >> j) & 1;
+          const int64_t last = pq[j] - first;
+          lo[j] = in ? 0 : 1;
+          hi[j] = in ? (last >= 7 ? 7 : (int)last) : 0;
+        }
+        core_compute_band<kMrgQ>(st, qb, cr, lo, hi, a.scale_log2);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // partials of this range for the live queries (layout of k_sgqa_prefill)
+#pragma unroll
+  for (int j = 0; j < kMrgQ; ++j) {
+    if (q0 + j >= a.nq) continue;
+    const int64_t pr = (((q0 + j) * kGroups + g) * kPreSplits + split) * 16 + nn;
+    const float l = core_total_l(st[j]);
+    if (kb == 0) {
+      __builtin_nontemporal_store(st[j].m, &a.part_ml[2 * pr]);
+      __builtin_nontemporal_store(l, &a.part_ml[2 * pr + 1]);
+    }
+    uint32_t* po = (uint32_t*)(a.part_o + pr * kHeadDim + 4 * kb);
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) {
+      __builtin_nontemporal_store(pack_bf16x2(st[j].o[nt][0], st[j].o[nt][1]), po + 8 * nt);
+      __builtin_nontemporal_store(pack_bf16x2(st[j].o[nt][2], st[j].o[nt][3]), po + 8 * nt + 1);
+    }
+  }
+}
+
 // block = (new token i of sequence s): writes it to the ring if it is among
 // the last `window` new tokens of its sequence (K as 96 units of 8 channels,
 // V element-wise; all loads issued before the stores).
@@ -1293,7 +1481,8 @@ static dsa_status sparse_gqa_prefill(const char* who, const dsa_geometry* geom, 
                                      const uint16_t* q, const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
                                      const uint16_t* k_cache, const uint16_t* v_cache, const CacheMap& cm,
                                      const int32_t* sel, const int32_t* n_sel, uint16_t* out, void* workspace,
-                                     size_t workspace_bytes, void* stream, const Fp8Kv* f8 = nullptr) {
+                                     size_t workspace_bytes, void* stream, const Fp8Kv* f8 = nullptr,
+                                     bool merged = false) {
   const std::string w(who);
   if (n_queries < 0 || n_seqs < 0) return fail(DSA_ERR_INVALID_ARGUMENT, w + ": bad sizes");
   if (n_queries == 0) return DSA_OK;
@@ -1318,7 +1507,11 @@ static dsa_status sparse_gqa_prefill(const char* who, const dsa_geometry* geom, 
   a.rsplit = (int32_t)((cm.R + kPreSplits - 1) / kPreSplits);
   a.scale_log2 = geom->softmax_scale * kLog2e;
   hipStream_t s = as_stream(stream);
-  {
+  if (merged) {
+    ProfScope prof_("k_sgqa_prefill_merged", s);
+    const dim3 grid((unsigned)(kPreSplits * kGroups * ((n_queries + 4 * kMrgQ - 1) / (4 * kMrgQ))));
+    hipLaunchKernelGGL(k_sgqa_prefill_merged, grid, dim3(256), 0, s, a);
+  } else {
     ProfScope prof_("k_sgqa_prefill", s);
     const dim3 grid((unsigned)(kPreSplits * kGroups * ((n_queries + 3) / 4)));
     if (f8) hipLaunchKernelGGL(k_sgqa_prefill<true>, grid, dim3(256), 0, s, a);
@@ -1346,6 +1539,36 @@ extern "C" dsa_status dsa_sparse_gqa_prefill(const dsa_geometry* geom, int32_t n
     return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill: tcap must be a positive multiple of 128");
   return sparse_gqa_prefill("dsa_sparse_gqa_prefill", geom, n_queries, q, q_seq, q_pos, n_seqs, k_cache, v_cache,
                             contiguous_map(tcap), sel, n_sel, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" dsa_status dsa_sparse_gqa_prefill_merged(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                                    const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                                    const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                                                    const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                                    void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_sparse_gqa_prefill_merged: tcap must be a positive multiple of 128");
+  return sparse_gqa_prefill("dsa_sparse_gqa_prefill_merged", geom, n_queries, q, q_seq, q_pos, n_seqs, k_cache,
+                            v_cache, contiguous_map(tcap), sel, n_sel, out, workspace, workspace_bytes, stream,
+                            nullptr, true);
+}
+
+extern "C" dsa_status dsa_sparse_gqa_prefill_merged_paged(const dsa_geometry* geom, int32_t n_queries,
+                                                          const uint16_t* q, const int32_t* q_seq,
+                                                          const int32_t* q_pos, int32_t n_seqs,
+                                                          const dsa_page_table* pages, const uint16_t* k_pool,
+                                                          const uint16_t* v_pool, const int32_t* sel,
+                                                          const int32_t* n_sel, uint16_t* out, void* workspace,
+                                                          size_t workspace_bytes, void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  CacheMap cm;
+  st = paged_map("dsa_sparse_gqa_prefill_merged_paged", pages, &cm);
+  if (st != DSA_OK) return st;
+  return sparse_gqa_prefill("dsa_sparse_gqa_prefill_merged_paged", geom, n_queries, q, q_seq, q_pos, n_seqs, k_pool,
+                            v_pool, cm, sel, n_sel, out, workspace, workspace_bytes, stream, nullptr, true);
 }
 
 extern "C" dsa_status dsa_sparse_gqa_prefill_paged(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,

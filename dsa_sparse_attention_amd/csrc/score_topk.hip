@@ -546,18 +546,6 @@ struct alignas(16) SelectSmem {
   uint32_t teq[KPT * NW];  // same for keys on the boundary
 };
 
-// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts inside
-// each row of 16 lanes, then row broadcasts of lanes 15 and 31).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-  return x;
-}
-
 // Sum over the wave, returned to every lane.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);

@@ -407,6 +407,36 @@ dsa_status dsa_sparse_gqa_prefill_paged(const dsa_geometry* geom, int32_t n_quer
                                         const int32_t* sel, const int32_t* n_sel, uint16_t* out,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Neighbour-merged prefill ([P5], Sparse GQA paragraph: similar selections of
+ * neighbouring tokens are merged to use the GPU better).  Same arguments,
+ * workspace and result as dsa_sparse_gqa_prefill, computed differently:
+ * every 4 consecutive queries of the call (same sequence) walk the union of
+ * their selections once per KV group, each region's K/V read once and
+ * applied to the queries that selected it, so a chunk whose neighbouring
+ * queries select overlapping regions reads and multiplies far less.  Each
+ * query still attends exactly its own selection (here a list is a set:
+ * repeated ids count once).  Queries of different sequences may share a
+ * group of 4 (one pass per sequence).  Pays off when neighbouring
+ * selections overlap; with unrelated selections the per-query call is
+ * faster.
+ */
+dsa_status dsa_sparse_gqa_prefill_merged(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
+                                         const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,
+                                         const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                                         const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* dsa_sparse_gqa_prefill_merged over paged K/V pools; bit-identical to the
+ * contiguous merged call on the same data. */
+dsa_status dsa_sparse_gqa_prefill_merged_paged(const dsa_geometry* geom, int32_t n_queries,
+                                               const uint16_t* q, const int32_t* q_seq,
+                                               const int32_t* q_pos, int32_t n_seqs,
+                                               const dsa_page_table* pages, const uint16_t* k_pool,
+                                               const uint16_t* v_pool, const int32_t* sel,
+                                               const int32_t* n_sel, uint16_t* out, void* workspace,
+                                               size_t workspace_bytes, void* stream);
+
 /* dsa_sparse_gqa_prefill over FP8 K/V caches (maths as in
  * dsa_sparse_gqa_decode_fp8). */
 dsa_status dsa_sparse_gqa_prefill_fp8(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
