@@ -835,7 +835,7 @@ def measure_prefill(args, result):
     log(f"prefill: {n * psteps / psecs:.0f} tok/s, {pms:.3f} ms/step")
 
 
-def union_of_neighbours(sel, nsel, n, topk, width=4):
+def union_of_neighbours(sel, nsel, n, topk, width=2):
     """Mean number of distinct regions per group in the selections of `width` consecutive queries."""
     import numpy as np
     s = sel.view(n, G, topk).cpu().numpy()
@@ -872,7 +872,7 @@ def measure_merged(args, result):
                                   "achieved_TFLOPs": round(tf, 2), "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                   "merge_us": round(st["k_sgqa_merge"][0] * 1e3, 1)}}
         if union is not None:
-            res[key]["mean_union_of_4_neighbours_per_group"] = round(union, 1)
+            res[key]["mean_union_of_2_neighbours_per_group"] = round(union, 1)
         log(f"{key}: {n * steps / secs:.0f} tok/s, attention {att_ms * 1e3:.0f} us")
     result["merged_prefill"] = res
 

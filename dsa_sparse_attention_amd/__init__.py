@@ -347,7 +347,7 @@ def dsa_sparse_gqa_prefill(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap
 
 def dsa_sparse_gqa_prefill_merged(geom, q, q_seq, q_pos, n_seqs, k_cache, v_cache, tcap, sel, n_sel, out,
                                   workspace=None, stream=None):
-    """Neighbour-merged prefill: the result of dsa_sparse_gqa_prefill, 4 consecutive queries sharing each
+    """Neighbour-merged prefill: the result of dsa_sparse_gqa_prefill, 2 consecutive queries sharing each
     region of their selections' union."""
     nq = q_seq.numel()
     for t, nm in ((q, "q"), (out, "out"), (k_cache, "k_cache"), (v_cache, "v_cache")):

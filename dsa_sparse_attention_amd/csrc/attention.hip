@@ -935,9 +935,16 @@ void k_swa_attend(SwaArgs a) {
 // in the lane's softmax region.  Positions no query of the wave uses get
 // their V zeroed; a position one query uses and another masks holds real
 // data and gets weight 0 from the latter.
-template <int NQ>
-__device__ __forceinline__ void core_compute_band(CoreState (&st)[NQ], const bf16x8 (&qb)[NQ][6], ChunkRegs& c,
-                                                  const int (&lo)[NQ], const int (&hi)[NQ], float scale_log2) {
+// after_s() runs once the S tiles are issued (a caller may load c.v there);
+// c.v is first used after the softmax.
+struct NoOp {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <int NQ, class QOf, class AfterS = NoOp>
+__device__ __forceinline__ void core_compute_band(CoreState (&st)[NQ], const QOf& q_of, ChunkRegs& c,
+                                                  const int (&lo)[NQ], const int (&hi)[NQ], float scale_log2,
+                                                  const AfterS& after_s = AfterS()) {
+  constexpr bool kLateV = !__is_same(AfterS, NoOp);  // V arrives in after_s: mask it after the softmax
   int ulo = lo[0], uhi = hi[0];
 #pragma unroll
   for (int j = 1; j < NQ; ++j) {
@@ -945,22 +952,25 @@ __device__ __forceinline__ void core_compute_band(CoreState (&st)[NQ], const bf1
     uhi = hi[j] > uhi ? hi[j] : uhi;
   }
   const bool full = (ulo <= 0 && uhi >= 7);
-  if (__any(!full)) {
-    uint32_t mk[4];
+  auto mask_v = [&]() {
+    if (__any(!full)) {
+      uint32_t mk[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const bool a0 = (2 * w >= ulo && 2 * w <= uhi);
-      const bool a1 = (2 * w + 1 >= ulo && 2 * w + 1 <= uhi);
-      mk[w] = (a0 ? 0x0000FFFFu : 0u) | (a1 ? 0xFFFF0000u : 0u);
-    }
+      for (int w = 0; w < 4; ++w) {
+        const bool a0 = (2 * w >= ulo && 2 * w <= uhi);
+        const bool a1 = (2 * w + 1 >= ulo && 2 * w + 1 <= uhi);
+        mk[w] = (a0 ? 0x0000FFFFu : 0u) | (a1 ? 0xFFFF0000u : 0u);
+      }
 #pragma unroll
-    for (int nt = 0; nt < 12; ++nt) {
-      c.v[nt].x &= mk[0];
-      c.v[nt].y &= mk[1];
-      c.v[nt].z &= mk[2];
-      c.v[nt].w &= mk[3];
+      for (int nt = 0; nt < 12; ++nt) {
+        c.v[nt].x &= mk[0];
+        c.v[nt].y &= mk[1];
+        c.v[nt].z &= mk[2];
+        c.v[nt].w &= mk[3];
+      }
     }
-  }
+  };
+  if constexpr (!kLateV) mask_v();
   // three phases over the NQ queries (S tiles, softmax, P.V) so that one
   // query's MFMAs overlap another's VALU work
   f32x4 s0[NQ], s1[NQ];
@@ -973,9 +983,11 @@ __device__ __forceinline__ void core_compute_band(CoreState (&st)[NQ], const bf1
   for (int q = 0; q < 6; ++q)
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      s0[j] = mfma16x16x32(as_bf16x8(c.k0[q]), qb[j][q], s0[j]);
-      s1[j] = mfma16x16x32(as_bf16x8(c.k1[q]), qb[j][q], s1[j]);
+      const bf16x8 qv = q_of(j, q);
+      s0[j] = mfma16x16x32(as_bf16x8(c.k0[q]), qv, s0[j]);
+      s1[j] = mfma16x16x32(as_bf16x8(c.k1[q]), qv, s1[j]);
     }
+  after_s();
   float sv[NQ][8], m_new[NQ];
   bool grow = false;
 #pragma unroll
@@ -1004,6 +1016,7 @@ __device__ __forceinline__ void core_compute_band(CoreState (&st)[NQ], const bf1
       }
     }
   }
+  if constexpr (kLateV) mask_v();
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const float m_use = st[j].m == -INFINITY ? 0.0f : st[j].m;
@@ -1128,7 +1141,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       lo[j] = in ? (int)((qlo > first ? qlo : first) - first) : 1;
       hi[j] = in ? (int)((pj[j] < first + 7 ? pj[j] : first + 7) - first) : 0;
     }
-    core_compute_band<kBandNQ>(st, qb, cr, lo, hi, a.scale_log2);
+    core_compute_band<kBandNQ>(st, [&](int j, int q) { return qb[j][q]; }, cr, lo, hi, a.scale_log2);
   }
   // copies issued past the last chunk must land before the block's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1143,53 +1156,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // Neighbour-merged prefill ([P5], Sparse GQA paragraph: the selections of
 // neighbouring tokens are merged so that the GPU is used better).  Exact
-// form: a wave takes 4 consecutive queries of one KV group and walks the
+// form: a wave takes 2 consecutive queries of one KV group and walks the
 // union of their selections inside one region range, ascending; each union
-// region's K/V is read once and applied to the 4 queries under their
+// region's K/V is read once and applied to both queries under their
 // membership bits (a query that did not select the region gives it weight
 // 0), so every query gets the attention over its own selection.  A query's
-// list is taken as a set (a repeated id counts once).  When the 4 queries
+// list is taken as a set (a repeated id counts once).  When the 2 queries
 // belong to different sequences, the wave makes one pass per sequence.
 //
 // The union of the range is built in windows of kMrgWin regions: a byte per
 // region collects the membership bits (LDS atomics), a wave-wide scan of the
 // nonzero bytes lists the union in ascending order, then the entries' cache
-// slots are looked up.  The walk prefetches the next 4-region chunk into the
-// wave's own LDS slot with direct-to-LDS copies while the current chunk
-// computes from registers, so no barrier is shared with other waves.
+// slots are looked up.  The queries' Q^T operands sit in LDS, which leaves
+// room for two waves per SIMD (242 VGPRs): chunks load straight into
+// registers, K first and V once the S tiles are issued, and the other wave
+// of the SIMD covers the waits.  No barrier is shared between waves.
 // Partials go to the layout of k_sgqa_prefill and k_sgqa_merge_pre merges.
+// (Four queries per wave, one wave per SIMD, with the next chunk copied into
+// LDS ahead, measured slower: 1.19 ms against 0.93 ms on the correlated 64K
+// chunk.)
 // ---------------------------------------------------------------------------
-constexpr int kMrgQ = 4;        // queries per wave
-constexpr int kMrgWin = 1024;   // regions per union window (64 lanes x 16 bytes)
+constexpr int kMrgQ = 2;       // queries per wave
+constexpr int kMrgWin = 512;   // regions per union window (64 lanes x 8 bytes)
 
 struct MergeWave {
-  uint8_t chunk[kChunkBytes];   // the prefetched chunk: 4 regions, K then V, as in the band ring
+  u32x4 q[kMrgQ][6][64];        // Q^T operand of query j, k-step s, lane
   uint32_t bits[kMrgWin / 4];   // membership byte of each region of the window
   int32_t rid[kMrgWin];         // the window's union, ascending
   int32_t slot[kMrgWin];        // its cache slots
   uint8_t msk[kMrgWin];         // its membership bytes
 };
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_sgqa_prefill_merged(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_sgqa_prefill_merged(
     PrefillArgs a) {
+  constexpr int NQ = kMrgQ;
+  constexpr int kWin = kMrgWin;
+  constexpr int kBytesPerLane = kWin / 64;  // membership bytes a lane scans
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, nn = lane & 15, kb = lane >> 4;
-  const int nqb = (a.nq + 4 * kMrgQ - 1) / (4 * kMrgQ);
+  const int nqb = (a.nq + 4 * NQ - 1) / (4 * NQ);
   const int split = blockIdx.x % kPreSplits;
   const int rest = blockIdx.x / kPreSplits;
   const int g = rest / nqb;
-  const int64_t q0 = ((int64_t)(rest % nqb) * 4 + wave) * kMrgQ;
+  const int64_t q0 = ((int64_t)(rest % nqb) * 4 + wave) * NQ;
   __shared__ __attribute__((aligned(16))) MergeWave lds_all[4];
   MergeWave& L = lds_all[wave];
   if (q0 >= a.nq) return;  // the whole wave; no barrier is shared with the others
   const int64_t tcap = a.cm.R * kRegion;
-  int32_t sq[kMrgQ], cq[kMrgQ];
-  int64_t pq[kMrgQ];
+  int32_t sq[NQ], cq[NQ];
+  int64_t pq[NQ];
   uint32_t todo = 0;
-  bf16x8 qb[kMrgQ][6];
-  CoreState st[kMrgQ];
+  CoreState st[NQ];
 #pragma unroll
-  for (int j = 0; j < kMrgQ; ++j) {
+  for (int j = 0; j < NQ; ++j) {
     const int64_t qi = q0 + j;
     const bool live = qi < a.nq;
     const int64_t qc = live ? qi : q0;
@@ -1200,7 +1219,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int32_t c = live ? a.nsel[qc * kGroups + g] : 0;
     cq[j] = c < 0 ? 0 : (c > a.topk ? a.topk : c);
     todo |= live ? 1u << j : 0u;
-    load_q(a.q, qc, g, qb[j]);
+    bf16x8 t[6];
+    load_q(a.q, qc, g, t);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) L.q[j][q][lane] = *(const u32x4*)&t[q];
     core_init(st[j]);
   }
   const int64_t r0 = (int64_t)split * a.rsplit;
@@ -1210,18 +1232,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int lead = __builtin_ctz(todo);
     int32_t sp = sq[0];
 #pragma unroll
-    for (int j = 1; j < kMrgQ; ++j) sp = lead == j ? sq[j] : sp;
+    for (int j = 1; j < NQ; ++j) sp = lead == j ? sq[j] : sp;
     uint32_t mem = 0;
 #pragma unroll
-    for (int j = 0; j < kMrgQ; ++j) mem |= ((todo >> j) & 1u) && sq[j] == sp ? 1u << j : 0u;
+    for (int j = 0; j < NQ; ++j) mem |= ((todo >> j) & 1u) && sq[j] == sp ? 1u << j : 0u;
     todo &= ~mem;
-    for (int64_t w0 = r0; w0 < r1; w0 += kMrgWin) {
-      const int64_t w1 = w0 + kMrgWin < r1 ? w0 + kMrgWin : r1;
+    for (int64_t w0 = r0; w0 < r1; w0 += kWin) {
+      const int64_t w1 = w0 + kWin < r1 ? w0 + kWin : r1;
       // membership bytes (a wave's LDS operations complete in issue order)
 #pragma unroll
-      for (int i = 0; i < kMrgWin / 4 / 64; ++i) L.bits[64 * i + lane] = 0u;
+      for (int i = 0; i < kWin / 4 / 64; ++i) L.bits[64 * i + lane] = 0u;
 #pragma unroll
-      for (int j = 0; j < kMrgQ; ++j) {
+      for (int j = 0; j < NQ; ++j) {
         if (!((mem >> j) & 1u)) continue;
         const int32_t* lst = a.sel + ((q0 + j) * kGroups + g) * a.topk;
         const int64_t cur = pq[j] / kRegion;
@@ -1233,24 +1255,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           }
         }
       }
-      // the union in ascending order: lane l owns regions w0 + 16l .. +15
-      const u32x4 mb = *(const u32x4*)&L.bits[4 * lane];
-      const uint32_t words[4] = {mb.x, mb.y, mb.z, mb.w};
+      // the union in ascending order: lane l owns regions w0 + l*kBytesPerLane ...
+      uint32_t words[kBytesPerLane / 4];
+#pragma unroll
+      for (int w = 0; w < kBytesPerLane / 4; ++w) words[w] = L.bits[(kBytesPerLane / 4) * lane + w];
       uint32_t cnt = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < kBytesPerLane / 4; ++w)
 #pragma unroll
         for (int b = 0; b < 4; ++b) cnt += ((words[w] >> (8 * b)) & 0xffu) ? 1u : 0u;
       const uint32_t incl = wave_incl_scan(cnt);
       const int nu = __builtin_amdgcn_readlane((int)incl, 63);
       uint32_t at = incl - cnt;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < kBytesPerLane / 4; ++w)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const uint32_t m = (words[w] >> (8 * b)) & 0xffu;
           if (m) {
-            L.rid[at] = (int32_t)(w0 + 16 * lane + 4 * w + b);
+            L.rid[at] = (int32_t)(w0 + kBytesPerLane * lane + 4 * w + b);
             L.msk[at] = (uint8_t)m;
             ++at;
           }
@@ -1260,58 +1283,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int32_t r = L.rid[e];
         L.slot[e] = (int32_t)slot_in(a.cm, a.cm.bt ? page_of(a.cm, sp, r) : 0, sp, g, r);
       }
-      // walk the union 4 regions at a time; the copy of the next chunk runs
-      // while the current one computes
-      auto issue = [&](int e0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = e0 + i < nu ? e0 + i : nu - 1;  // past the end: a re-read, masked
-          const int64_t sl = L.slot[e];
-          const uint8_t* bk = (const uint8_t*)(a.k + sl * kRegionElems);
-          const uint8_t* bv = (const uint8_t*)(a.v + sl * kRegionElems);
-          LdsPtr d = (LdsPtr)(&L.chunk[0] + i * kBandRegion);
-#pragma unroll
-          for (int k = 0; k < 3; ++k) {
-            __builtin_amdgcn_global_load_lds((const void*)(bk + 1024 * k + 16 * lane), d + 1024 * k, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(bv + 1024 * k + 16 * lane), d + kRegionBytes + 1024 * k,
-                                             16, 0, 0);
-          }
-        }
-      };
-      issue(0);
-      for (int e0 = 0; e0 < nu; e0 += 4) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the chunk's copies have landed
-        ChunkRegs cr;
-        const uint8_t* kp = &L.chunk[0] + (nn >> 2) * kBandRegion + ((kb * 4 + (nn & 3)) * 8) * 2;
-#pragma unroll
-        for (int q = 0; q < 6; ++q) {
-          cr.k0[q] = *(const u32x4*)(kp + (q * 16) * 16);
-          cr.k1[q] = *(const u32x4*)(kp + ((6 + q) * 16) * 16);
-        }
-        const uint8_t* vp = &L.chunk[0] + kb * kBandRegion + kRegionBytes;
-#pragma unroll
-        for (int nt = 0; nt < 12; ++nt) cr.v[nt] = *(const u32x4*)(vp + (16 * nt + nn) * 16);
+      auto masks = [&](int e0, int (&lo)[NQ], int (&hi)[NQ]) {
         const int e = e0 + kb;
         const int m = e < nu ? L.msk[e] : 0;
         const int64_t first = (int64_t)(e < nu ? L.rid[e] : 0) * kRegion;
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is free for the next copies
-        if (e0 + 4 < nu) issue(e0 + 4);
-        int lo[kMrgQ], hi[kMrgQ];
 #pragma unroll
-        for (int j = 0; j < kMrgQ; ++j) {
+        for (int j = 0; j < NQ; ++j) {
           const bool in = (m >> j) & 1;
           const int64_t last = pq[j] - first;
           lo[j] = in ? 0 : 1;
           hi[j] = in ? (last >= 7 ? 7 : (int)last) : 0;
         }
-        core_compute_band<kMrgQ>(st, qb, cr, lo, hi, a.scale_log2);
+      };
+      // walk the union 4 regions at a time
+      {
+        auto region_of = [&](int e) -> Region {
+          Region rg;
+          const int64_t sl = e < nu ? L.slot[e] : L.slot[nu - 1];  // past the end: a re-read, masked
+          rg.k = a.k + sl * kRegionElems;
+          rg.v = a.v + sl * kRegionElems;
+          rg.lo = 0;
+          rg.hi = 7;
+          return rg;
+        };
+        // K rows of region (e0 + nn/4) first; the V pack of region (e0 + kb)
+        // once the S tiles are issued (K and V are then not live together,
+        // which keeps two waves per SIMD; the other wave covers the waits)
+        for (int e0 = 0; e0 < nu; e0 += 4) {
+          ChunkRegs cr;
+          const uint16_t* kp = region_of(e0 + (nn >> 2)).k + (kb * 4 + (nn & 3)) * 8;
+#pragma unroll
+          for (int q = 0; q < 6; ++q) {
+            cr.k0[q] = ld16(kp + (q * 16) * 8);
+            cr.k1[q] = ld16(kp + ((6 + q) * 16) * 8);
+          }
+          const uint16_t* vb = region_of(e0 + kb).v;
+          int lo[NQ], hi[NQ];
+          masks(e0, lo, hi);
+          core_compute_band<NQ>(
+              st, [&](int j, int q) { const u32x4 v = L.q[j][q][lane]; return as_bf16x8(v); }, cr, lo, hi,
+              a.scale_log2, [&]() {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nt = 0; nt < 12; ++nt) cr.v[nt] = ld16(vb + (16 * nt + nn) * 8);
+                __builtin_amdgcn_sched_barrier(0);
+              });
+        }
       }
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // partials of this range for the live queries (layout of k_sgqa_prefill)
 #pragma unroll
-  for (int j = 0; j < kMrgQ; ++j) {
+  for (int j = 0; j < NQ; ++j) {
     if (q0 + j >= a.nq) continue;
     const int64_t pr = (((q0 + j) * kGroups + g) * kPreSplits + split) * 16 + nn;
     const float l = core_total_l(st[j]);

@@ -411,15 +411,14 @@ dsa_status dsa_sparse_gqa_prefill_paged(const dsa_geometry* geom, int32_t n_quer
  * Neighbour-merged prefill ([P5], Sparse GQA paragraph: similar selections of
  * neighbouring tokens are merged to use the GPU better).  Same arguments,
  * workspace and result as dsa_sparse_gqa_prefill, computed differently:
- * every 4 consecutive queries of the call (same sequence) walk the union of
- * their selections once per KV group, each region's K/V read once and
- * applied to the queries that selected it, so a chunk whose neighbouring
- * queries select overlapping regions reads and multiplies far less.  Each
- * query still attends exactly its own selection (here a list is a set:
- * repeated ids count once).  Queries of different sequences may share a
- * group of 4 (one pass per sequence).  Pays off when neighbouring
- * selections overlap; with unrelated selections the per-query call is
- * faster.
+ * every 2 consecutive queries of the call walk the union of their
+ * selections once per KV group, each region's K/V read once and applied to
+ * the queries that selected it, so a chunk whose neighbouring queries
+ * select overlapping regions gathers less.  Each query still attends
+ * exactly its own selection (here a list is a set: repeated ids count
+ * once).  Neighbours of different sequences are allowed (one pass per
+ * sequence).  Pays off when neighbouring selections overlap; with
+ * unrelated selections the per-query call is faster.
  */
 dsa_status dsa_sparse_gqa_prefill_merged(const dsa_geometry* geom, int32_t n_queries, const uint16_t* q,
                                          const int32_t* q_seq, const int32_t* q_pos, int32_t n_seqs,

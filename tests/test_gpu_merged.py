@@ -1,7 +1,7 @@
-"""Neighbour-merged prefill (4 consecutive queries walk the union of their selections) through the
+"""Neighbour-merged prefill (2 consecutive queries walk the union of their selections) through the
 C ABI: each query's output meets the oracle's attention over its own selection, on correlated chunks
 (neighbouring selections overlap, the case the merge is for) and on unrelated ones; queries of
-several sequences may share a group of 4; lists are sets (order, repeats and out-of-range ids do not
+several sequences may be neighbours; lists are sets (order, repeats and out-of-range ids do not
 matter); the paged form is bit-identical to the contiguous one."""
 import numpy as np
 import pytest
@@ -92,7 +92,7 @@ def _oracle_check(seed, c, out, step, lists_of=None, what="merged"):
     print(f"{what}: worst max abs {worst[0]:.2e}, rel rms {worst[1]:.2e}")
 
 
-def _union_stats(c, width=4):
+def _union_stats(c, width=2):
     gsel = c["sel"].cpu().numpy().reshape(c["nq"], G, c["topk"])
     gn = c["nsel"].cpu().numpy().reshape(c["nq"], G)
     us = []
@@ -114,13 +114,13 @@ def test_merged_prefill_matches_oracle(seqs, correlated):
     ref = _run(c, False)
     # same maths as the per-query kernel, another summation order
     H.assert_attn(out.reshape(-1, D), ref.reshape(-1, D).astype(np.float64), "merged vs per-query")
-    print(f"mean union of 4 neighbours: {_union_stats(c):.0f} regions per group")
+    print(f"mean union of 2 neighbours: {_union_stats(c):.0f} regions per group")
     _oracle_check(seed, c, out, 97 if c["nq"] > 1000 else 7)
 
 
 def test_merged_prefill_mixed_sequences_and_ragged():
-    """Interleaved queries of 3 sequences (each group of 4 spans several sequences), a count that is
-    not a multiple of 16, and topk 37."""
+    """Interleaved queries of 3 sequences (each pair of neighbours spans two sequences), a count that is
+    not a multiple of 8, and topk 37."""
     seed = 0xA20
     c = _chunk(seed, [(1000, 33), (130, 5), (4096, 21)], order="interleaved", correlated=False, topk=37)
     out = _run(c, True)
