@@ -685,6 +685,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 K/V cache runs of the two headline workloads")
     ap.add_argument("--no-merged", action="store_true",
                     help="skip the neighbour-merged prefill runs (correlated and i.i.d. chunks)")
+    ap.add_argument("--no-frontend", action="store_true", help="skip the indexer front-end runs")
     ap.add_argument("--graph", action="store_true", help="time replays of a HIP graph holding one step")
     ap.add_argument("--separate", action="store_true",
                     help="decode step as three calls (compress, score_topk, sparse_gqa_decode) instead of dsa_decode_step")
@@ -746,6 +747,8 @@ def main():
         measure_fp8(args, result)
     if not args.no_merged and not args.no_prefill:
         measure_merged(args, result)
+    if not args.no_frontend and not args.swa_only:
+        measure_frontend(args, result)
     # ---- the 3:1 sliding-window / DSA stack (decode) and a sliding-window prefill chunk
     if not args.no_swa:
         measure_swa(args, result)
@@ -875,6 +878,72 @@ def measure_merged(args, result):
             res[key]["mean_union_of_2_neighbours_per_group"] = round(union, 1)
         log(f"{key}: {n * steps / secs:.0f} tok/s, attention {att_ms * 1e3:.0f} us")
     result["merged_prefill"] = res
+
+
+FRONTEND = dict(hidden=6144, seed_index=5)  # the pages give no hidden size: 6144 = 32 x 192 stands in
+
+
+def setup_frontend(T):
+    """Indexer front-end of T tokens (hidden states -> index_q, index_k, z) at positions 63,488.."""
+    import numpy as np
+    import torch
+    import dsa_inputs as gi
+    import dsa_sparse_attention_amd as dsa
+    Hd = FRONTEND["hidden"]
+    seed = gi.SEED_BASE + FRONTEND["seed_index"]
+    x, w, gq, gk = gi.host_frontend_inputs(seed, T, Hd, dsa.IDX_PROJ_ROWS)
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16).ravel()).cuda().view(torch.bfloat16)
+    xd, wd = up(x), up(w)
+    gqd, gkd = torch.from_numpy(gq).cuda(), torch.from_numpy(gk).cuda()
+    pos = torch.arange(63488, 63488 + T, dtype=torch.int32, device="cuda")
+    iq = torch.empty(T * HI * P, dtype=torch.bfloat16, device="cuda")
+    ik = torch.empty(T * G * P, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(T * HI, dtype=torch.float32, device="cuda")
+    ws = dsa.workspace(dsa.dsa_indexer_workspace_size(T, Hd))
+    rope = dsa.rope_config()
+    L = dsa.load()
+    p = Calls.p
+    args = (ctypes.byref(rope), T, Hd, p(xd), p(wd), p(gqd), p(gkd), p(pos), p(iq), p(ik), p(z), p(ws), ws.numel())
+
+    def step(st):
+        rc = L.dsa_indexer_project(*args, st)
+        if rc:
+            raise RuntimeError(f"front-end step failed: {rc} {L.dsa_last_error().decode()}")
+
+    return step, (xd, wd, gqd, gkd, pos, iq, ik, z, ws, rope)
+
+
+def measure_frontend(args, result):
+    """The indexer front-end (fused projection + RMSNorm + partial RoPE) for the 2048-token prefill chunk
+    and for one decode step of batch 4: MFMA rate of the projection kernel, and for decode the weight
+    bytes it streams."""
+    import torch
+    import dsa_sparse_attention_amd as dsa
+    Hd = FRONTEND["hidden"]
+    res = {}
+    for key, T in (("prefill_chunk", PREFILL["chunk"]), ("decode_batch4", DECODE["batch"])):
+        step, keep = setup_frontend(T)
+        steps = max(3, args.steps // 3)
+        secs, _, st = timed(step, steps, max(1, args.warmup // 2),
+                            ["k_rope_table", "k_indexer_proj", "k_indexer_finish", "k_indexer_z"], graph=args.graph)
+        st = {k: v for k, v in st.items() if v[1]}
+        del keep
+        torch.cuda.empty_cache()
+        proj_ms = st["k_indexer_proj"][0]
+        flops = 2.0 * T * Hd * (HI + G) * P
+        wbytes = (HI + G) * P * Hd * 2
+        tf = flops / (proj_ms * 1e-3) / 1e12
+        res[key] = {"workload": f"indexer front-end, {T} tokens, hidden {Hd} (stand-in), 16 index_q heads + 4 "
+                                f"index_k groups of 256 + 16 z, RMSNorm + 64-dim llama3 RoPE",
+                    "value": round(T * steps / secs, 1), "unit": "tokens/s", "ms_per_step": round(secs * 1e3 / steps, 4),
+                    "projection": {"kernel": "k_indexer_proj", "avg_launch_us": round(proj_ms * 1e3, 1),
+                                   "algorithmic_flops": flops, "achieved_TFLOPs": round(tf, 2),
+                                   "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   "weight_bytes": wbytes,
+                                   "weight_GBs": round(wbytes / (proj_ms * 1e-3) / 1e9, 1)},
+                    "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in st.items()}}
+        log(f"front-end {key}: projection {proj_ms * 1e3:.1f} us, {tf:.0f} TFLOP/s")
+    result["indexer_frontend"] = res
 
 
 def measure_swa(args, result):

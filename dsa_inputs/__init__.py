@@ -15,6 +15,8 @@ Workload recipe (tensor ids; the seed of workload i is ``SEED_BASE + i``):
   Q=1, K=2, V=3 ~ N(0,1) bf16; index_k=4, index_q=5 ~ N(0,1)/16 bf16;
   z=6 ~ U(0,1) fp32; planted-region mask=7, planted coefficients=9;
   sliding-window layer l (0-based) uses ids + 16*(l+1).
+Indexer front-end: hidden states x (id 12) ~ N(0,1) bf16, projection weights (id 13) ~ N(0,1)/sqrt(H)
+  bf16, RMSNorm gains (id 14) 0.75 + 0.5 U(0,1) fp32 (gamma_q first, then gamma_k).
 Correlated prefill chunk (neighbouring queries select overlapping regions):
   anchors of index_q (id 10, N(0,1)/16) and of z (id 11, U(0,1)) every ``every``
   queries; query i blends anchors a = i // every and a + 1 with t = (i mod every)
@@ -32,6 +34,7 @@ import numpy as np
 SEED_BASE = 0xD5A00000
 TID_Q, TID_K, TID_V, TID_IK, TID_IQ, TID_Z, TID_MASK, TID_COEF = 1, 2, 3, 4, 5, 6, 7, 9
 TID_IQ_ANCHOR, TID_Z_ANCHOR = 10, 11
+TID_X, TID_W, TID_GAMMA = 12, 13, 14
 IK_SCALE = 1.0 / 16.0
 
 LAYOUT_GROUP_MAJOR, LAYOUT_REGION_T, LAYOUT_TOKEN_MAJOR, LAYOUT_KTILED = 0, 1, 2, 3
@@ -230,6 +233,15 @@ def host_correlated_index_queries(seed, nq, heads=16, P=256, every=64, noise=0.1
     iq = c_path * path + np.float32(noise) * own
     z = ((np.float32(1) - t)[:, None] * Z[a] + t[:, None] * Z[a + 1]).astype(np.float32)
     return bf16_rne(iq.astype(np.float32)), z
+
+
+def host_frontend_inputs(seed, T, H, n_rows):
+    """x [T][H] and W [n_rows][H] (bf16 bits), gamma_q and gamma_k [256] (fp32) of the indexer front-end."""
+    x = host_normal_bf16(seed, TID_X, T * H).reshape(T, H)
+    w = host_normal_bf16(seed, TID_W, n_rows * H, 1.0 / float(np.sqrt(H))).reshape(n_rows, H)
+    u = host_uniform_f32(seed, TID_GAMMA, 512)
+    g = (np.float32(0.75) + np.float32(0.5) * u).astype(np.float32)
+    return x, w, g[:256].copy(), g[256:].copy()
 
 
 # ----------------------------------------------------------------------------------------------

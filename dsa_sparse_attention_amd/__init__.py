@@ -35,6 +35,7 @@ ENTRY_POINTS = [
     "dsa_cache_write_fp8", "dsa_sparse_gqa_decode_fp8", "dsa_sparse_gqa_prefill_fp8", "dsa_decode_step_fp8",
     "dsa_cache_write_fp8_paged", "dsa_sparse_gqa_decode_fp8_paged", "dsa_sparse_gqa_prefill_fp8_paged",
     "dsa_decode_step_fp8_paged", "dsa_sparse_gqa_prefill_merged", "dsa_sparse_gqa_prefill_merged_paged",
+    "dsa_rope_config_default", "dsa_indexer_workspace_size", "dsa_indexer_project", "dsa_rope_qk",
 ]
 
 
@@ -49,6 +50,12 @@ class Geometry(ctypes.Structure):
                 ("n_groups", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class RopeConfig(ctypes.Structure):
+    _fields_ = [("rot_dims", ctypes.c_int32), ("theta", ctypes.c_float), ("factor", ctypes.c_float),
+                ("low_freq_factor", ctypes.c_float), ("high_freq_factor", ctypes.c_float),
+                ("original_max_pos", ctypes.c_int32)]
 
 
 class PageTable(ctypes.Structure):
@@ -132,6 +139,12 @@ def load() -> ctypes.CDLL:
     L.dsa_sparse_gqa_prefill_fp8.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     L.dsa_decode_step_fp8.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz,
                                       vp]
+    R = ctypes.POINTER(RopeConfig)
+    L.dsa_rope_config_default.argtypes = [R]
+    L.dsa_indexer_workspace_size.argtypes = [i32, i32]
+    L.dsa_indexer_workspace_size.restype = sz
+    L.dsa_indexer_project.argtypes = [R, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_rope_qk.argtypes = [R, i32, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_gqa_prefill_merged.argtypes = [G, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_gqa_prefill_merged_paged.argtypes = [G, i32, vp, vp, vp, i32, P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_cache_write_fp8_paged.argtypes = [G, i32, vp, vp, vp, vp, P, i32, vp, vp, vp, vp]
@@ -752,6 +765,59 @@ def dsa_decode_step_fp8_paged(geom, q, index_q, z, pages: Pages, ik_pool, k8, v8
                                             _ptr(seq_len), _ptr(summ_pool), _ptr(scale_pool), max_regions, _ptr(sel),
                                             _ptr(n_sel), _ptr(out), _ptr(workspace), workspace.numel(),
                                             _stream(stream)))
+
+
+# ---- indexer front-end and the attention's partial RoPE ---------------------------------------
+IDX_PROJ_ROWS = (IDX_HEADS + GROUPS) * PROXY + IDX_HEADS  # weight rows: index_q heads, index_k groups, z
+
+
+def rope_config(**override) -> RopeConfig:
+    """The library's default rotation settings (pages' llama3 values; theta 10000 and factor 8 as
+    stand-ins), with fields overridden by keyword."""
+    c = RopeConfig()
+    _check(load().dsa_rope_config_default(ctypes.byref(c)))
+    for k, v in override.items():
+        setattr(c, k, v)
+    return c
+
+
+def dsa_indexer_workspace_size(n_tokens, hidden=0) -> int:
+    return int(load().dsa_indexer_workspace_size(n_tokens, hidden))
+
+
+def dsa_indexer_project(rope, x, w, gamma_q, gamma_k, pos, index_q, index_k, z, hidden, workspace=None,
+                        stream=None):
+    n = pos.numel()
+    for t, nm in ((x, "x"), (w, "w"), (index_q, "index_q"), (index_k, "index_k")):
+        _dt(t, torch.bfloat16, nm)
+    for t, nm in ((gamma_q, "gamma_q"), (gamma_k, "gamma_k"), (z, "z")):
+        _dt(t, torch.float32, nm)
+    _dt(pos, torch.int32, "pos")
+    _numel_at_least(x, n * hidden, "x")
+    _numel_at_least(w, IDX_PROJ_ROWS * hidden, "w")
+    _numel_at_least(gamma_q, PROXY, "gamma_q")
+    _numel_at_least(gamma_k, PROXY, "gamma_k")
+    _numel_at_least(index_q, n * IDX_HEADS * PROXY, "index_q")
+    _numel_at_least(index_k, n * GROUPS * PROXY, "index_k")
+    _numel_at_least(z, n * IDX_HEADS, "z")
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_indexer_workspace_size(n, hidden), pos.device)
+    _check(load().dsa_indexer_project(ctypes.byref(rope), n, hidden, _ptr(x), _ptr(w), _ptr(gamma_q),
+                                      _ptr(gamma_k), _ptr(pos), _ptr(index_q), _ptr(index_k), _ptr(z),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dsa_rope_qk(rope, pos, q, k, workspace=None, stream=None):
+    n = pos.numel()
+    _dt(pos, torch.int32, "pos")
+    _dt(q, torch.bfloat16, "q")
+    _dt(k, torch.bfloat16, "k")
+    _numel_at_least(q, n * Q_HEADS * HEAD_DIM, "q")
+    _numel_at_least(k, n * GROUPS * HEAD_DIM, "k")
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_indexer_workspace_size(n), pos.device)
+    _check(load().dsa_rope_qk(ctypes.byref(rope), n, _ptr(pos), _ptr(q), _ptr(k), _ptr(workspace),
+                              workspace.numel(), _stream(stream)))
 
 
 def profile_enable(on: bool = True):

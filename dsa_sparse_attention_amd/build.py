@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "lib", "libdsa_mi355x.so")
-SOURCES = ["api.hip", "compress.hip", "score_topk.hip", "attention.hip"]
+SOURCES = ["api.hip", "compress.hip", "score_topk.hip", "attention.hip", "frontend.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are kept off: the compiler must not form v_pk_* fp32 math.  MFMA results are
 # allocated in ordinary VGPRs where they fit (instead of accumulation registers with copies around

@@ -499,6 +499,69 @@ dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_s
                            uint16_t* k_ring, uint16_t* v_ring, void* stream);
 
 /*
+ * Indexer front-end ([P2] section 索引器打分 + Top-K 选择: the indexer projects
+ * the hidden state into index_q / index_k / index_z, then normalises them and
+ * rotates part of their dimensions; [P1] paragraph after step ④ and [P3]
+ * section 一: llama3-style rope_scaling with low_freq_factor 1.0,
+ * high_freq_factor 32.0, original_max_position_embeddings 1048576, partial
+ * rotary factor 1/3, i.e. 64 of the 192 head dimensions rotate).
+ *
+ * Rotation: pair (i, i + 32) of the first 64 dimensions of a vector turns by
+ * pos * f_i, f_i = llama3(theta^(-2i/64)): frequencies whose wavelength
+ * 2*pi/f is below original_max_pos / high_freq_factor stay, those above
+ * original_max_pos / low_freq_factor are divided by `factor`, and in between
+ * f moves linearly in original_max_pos / wavelength from f/factor to f.
+ * theta and factor are not on the pages: dsa_rope_config_default fills
+ * theta 10000 and factor 8 beside the pages' values.  rot_dims must be 64.
+ */
+typedef struct dsa_rope_config {
+  int32_t rot_dims;
+  float theta;
+  float factor;
+  float low_freq_factor;
+  float high_freq_factor;
+  int32_t original_max_pos;
+} dsa_rope_config;
+
+dsa_status dsa_rope_config_default(dsa_rope_config* rope);
+
+/* Workspace bytes of dsa_indexer_project (hidden size `hidden`) and of
+ * dsa_rope_qk (hidden 0) for n_tokens tokens: a cos/sin table of 32 pairs
+ * per token, and for up to 64 tokens the fp32 partial sums of the split
+ * projection (hidden/256 or hidden/128 splits x n_tokens x 5136). */
+size_t dsa_indexer_workspace_size(int32_t n_tokens, int32_t hidden);
+
+/*
+ * Hidden states -> the indexer's inputs, fused: y = x . W^T (bf16 MFMA, fp32
+ * accumulation); each 256-d index vector is RMS-normalised (eps 1e-6, gain
+ * gamma_q for the 16 query heads, gamma_k for the 4 key groups) and its
+ * first 64 dimensions rotated by the token's position; z is the plain
+ * projection (fp32).
+ *   x        [n_tokens][hidden] bf16, 16-byte aligned; hidden a multiple of 128
+ *   w        [16*256 + 4*256 + 16][hidden] bf16 (rows: index_q heads,
+ *            index_k groups, z heads), 16-byte aligned
+ *   gamma_q, gamma_k  [256] fp32;  pos [n_tokens] int32 (>= 0)
+ *   index_q  [n_tokens][16][256] bf16;  index_k [n_tokens][4][256] bf16
+ *            (the layouts dsa_score_topk and dsa_cache_write read)
+ *   z        [n_tokens][16] fp32
+ *   workspace >= dsa_indexer_workspace_size(n_tokens), 256-byte aligned
+ */
+dsa_status dsa_indexer_project(const dsa_rope_config* rope, int32_t n_tokens, int32_t hidden,
+                               const uint16_t* x, const uint16_t* w, const float* gamma_q,
+                               const float* gamma_k, const int32_t* pos, uint16_t* index_q,
+                               uint16_t* index_k, float* z, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The same rotation applied in place to the attention's projected q
+ * [n_tokens][64][192] and k [n_tokens][4][192] (bf16, token-major): the first
+ * 64 dimensions of every head turn by the token's position (the full-attention
+ * layers' partial RoPE).  Workspace as for dsa_indexer_project.
+ */
+dsa_status dsa_rope_qk(const dsa_rope_config* rope, int32_t n_tokens, const int32_t* pos, uint16_t* q,
+                       uint16_t* k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Instrumentation (not part of the layer's maths).  While enabled, every
  * kernel the library launches outside stream capture is bracketed by two
  * hipEvents recorded on its launch stream.  dsa_profile_enable(on) drops
@@ -507,7 +570,8 @@ dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_s
  * returns the summed interval (ms) and the number of launches.  Kernel
  * names: k_compress, k_cache_write, k_score_decode,
  * k_score_prefill, k_select, k_sgqa_decode, k_sgqa_merge, k_sgqa_prefill,
- * k_swa_stage, k_swa_attend, k_ring_append.  Host-side state only, guarded
+ * k_swa_stage, k_swa_attend, k_ring_append, k_sgqa_prefill_merged, k_rope_table,
+ * k_indexer_proj, k_indexer_finish, k_indexer_z, k_rope_qk.  Host-side state only, guarded
  * by a mutex; at most 8192 launches are recorded between resets.
  */
 dsa_status dsa_profile_enable(int on);

@@ -195,3 +195,27 @@ def test_paged_calls_with_no_work_are_no_ops(lib):
                                                 None, 0, None) == 0
     assert lib.dsa_decode_step_fp8_paged(g, 0, None, None, None, pt, None, None, None, None, None, None, None, 8,
                                          None, None, None, None, 0, None) == 0
+
+
+def test_rope_config_default_and_checks(lib):
+    c = dsa.RopeConfig()
+    assert lib.dsa_rope_config_default(ctypes.byref(c)) == 0
+    assert (c.rot_dims, c.theta, c.factor, c.low_freq_factor, c.high_freq_factor, c.original_max_pos) == \
+        (64, 10000.0, 8.0, 1.0, 32.0, 1048576)
+    vp = ctypes.c_void_p(256)
+    ws = 1 << 20
+    # no work: no-op; bad settings and sizes fail before any launch
+    assert lib.dsa_indexer_project(ctypes.byref(c), 0, 256, None, None, None, None, None, None, None, None, None,
+                                   0, None) == 0
+    assert lib.dsa_rope_qk(ctypes.byref(c), 0, None, None, None, None, 0, None) == 0
+    assert lib.dsa_indexer_project(ctypes.byref(c), 4, 192, vp, vp, vp, vp, vp, vp, vp, vp, vp, ws, None) == 1
+    assert b"multiple of 128" in lib.dsa_last_error()
+    bad = dsa.RopeConfig(c.rot_dims, c.theta, c.factor, c.low_freq_factor, c.high_freq_factor, c.original_max_pos)
+    bad.rot_dims = 32
+    assert lib.dsa_rope_qk(ctypes.byref(bad), 4, vp, vp, vp, vp, ws, None) == 2
+    bad.rot_dims, bad.high_freq_factor = 64, 0.5
+    assert lib.dsa_rope_qk(ctypes.byref(bad), 4, vp, vp, vp, vp, ws, None) == 1
+    assert lib.dsa_rope_qk(None, 4, vp, vp, vp, vp, ws, None) == 1
+    assert lib.dsa_indexer_workspace_size(2048, 6144) >= 2048 * 32 * 8
+    assert lib.dsa_indexer_workspace_size(4, 6144) >= 4 * 32 * 8 + 24 * 4 * 5136 * 4
+    assert lib.dsa_rope_qk(ctypes.byref(c), 4, vp, vp, vp, vp, 16, None) == 3  # workspace too small
