@@ -718,6 +718,19 @@ def main():
                 step(cur_stream())
             torch.cuda.synchronize()
             del keep
+            if not args.no_merged:
+                step, keep = setup_prefill(PREFILL, correlated=True, merged=True)
+                for _ in range(2):
+                    step(cur_stream())
+                torch.cuda.synchronize()
+                del keep
+        if not args.no_frontend and not args.swa_only:
+            for T in (PREFILL["chunk"], DECODE["batch"]):
+                step, keep = setup_frontend(T)
+                for _ in range(2):
+                    step(cur_stream())
+                torch.cuda.synchronize()
+                del keep
         if not args.no_swa:
             for setup, cfg in ((setup_mix, MIX), (setup_swa_prefill, SWA_PREFILL)):
                 step, keep = setup(cfg)

@@ -40,6 +40,17 @@ struct RopeFreqs {
   double f[kRotPairs];
 };
 
+// (cos, sin) of the angle pos * f: the product in double, reduced to
+// [-pi, pi] before sincos.
+__device__ __forceinline__ float2 rope_cs(int32_t pos, double f) {
+  const double a = (double)pos * f;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double r = a - two_pi * rint(a / two_pi);
+  double s, c;
+  sincos(r, &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
 // cos/sin of pair i at the token's position; one block of 64 threads per
 // 2 tokens.
 __global__ __launch_bounds__(64) void k_rope_table(const int32_t* __restrict__ pos, int32_t n, RopeFreqs fr,
@@ -47,12 +58,7 @@ __global__ __launch_bounds__(64) void k_rope_table(const int32_t* __restrict__ p
   const int64_t t = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 5);
   const int i = threadIdx.x & 31;
   if (t >= n) return;
-  const double a = (double)pos[t] * fr.f[i];
-  const double two_pi = 6.283185307179586476925286766559;
-  const double r = a - two_pi * rint(a / two_pi);  // in [-pi, pi]
-  double s, c;
-  sincos(r, &s, &c);
-  cs[t * kRotPairs + i] = make_float2((float)c, (float)s);
+  cs[t * kRotPairs + i] = rope_cs(pos[t], fr.f[i]);
 }
 
 #ifndef DSA_FE_PM
@@ -255,9 +261,9 @@ __global__ __launch_bounds__(64) void k_indexer_proj_splitk(const uint16_t* __re
 // block = (token, output vector 0..19, or 20 = z); thread = column.
 __global__ __launch_bounds__(256) void k_indexer_finish(const float* __restrict__ part, int32_t ks,
                                                         const float* __restrict__ gq, const float* __restrict__ gk,
-                                                        const float2* __restrict__ cs, uint16_t* __restrict__ iq,
-                                                        uint16_t* __restrict__ ik, float* __restrict__ z,
-                                                        int32_t T) {
+                                                        const int32_t* __restrict__ pos, RopeFreqs fr,
+                                                        uint16_t* __restrict__ iq, uint16_t* __restrict__ ik,
+                                                        float* __restrict__ z, int32_t T) {
   const int64_t t = blockIdx.x;
   const int h = blockIdx.y, c = threadIdx.x, lane = c & 63, wave = c >> 6;
   __shared__ float red[4];
@@ -270,6 +276,8 @@ __global__ __launch_bounds__(256) void k_indexer_finish(const float* __restrict_
     }
     return;
   }
+  // the rotation's (cos, sin) for this column's pair, while the partials load
+  const float2 cc = c < kRotDims ? rope_cs(pos[t], fr.f[c & (kRotPairs - 1)]) : make_float2(1.f, 0.f);
   float y = 0.f;
 #pragma unroll 8
   for (int sp = 0; sp < ks; ++sp) y += part[((int64_t)sp * T + t) * kProjN + h * kProxy + c];
@@ -283,7 +291,6 @@ __global__ __launch_bounds__(256) void k_indexer_finish(const float* __restrict_
   if (c < kRotDims) ys[c] = y;
   __syncthreads();
   if (c < kRotDims) {
-    const float2 cc = cs[t * kRotPairs + (c & (kRotPairs - 1))];
     y = c < kRotPairs ? ys[c] * cc.x - ys[c + kRotPairs] * cc.y : ys[c] * cc.x + ys[c - kRotPairs] * cc.y;
   }
   uint16_t* o = h < kIdxHeads ? iq + (t * kIdxHeads + h) * kProxy : ik + (t * kGroups + h - kIdxHeads) * kProxy;
@@ -411,14 +418,7 @@ extern "C" dsa_status dsa_indexer_project(const dsa_rope_config* rope, int32_t n
   if (workspace_bytes < dsa_indexer_workspace_size(n_tokens, hidden))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_indexer_project: workspace too small");
   hipStream_t s = as_stream(stream);
-  float2* cs = (float2*)workspace;
-  {
-    ProfScope prof_("k_rope_table", s);
-    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n_tokens + 1) / 2)), dim3(64), 0, s, pos, n_tokens,
-                       rope_freqs(*rope), cs);
-  }
-  st = check_launch(who);
-  if (st != DSA_OK) return st;
+  const RopeFreqs fr = rope_freqs(*rope);
   if (n_tokens <= kSmallT) {
     const int32_t kper = splitk_kper(hidden), ks = hidden / kper;
     float* part = (float*)((char*)workspace + table_bytes(n_tokens));
@@ -432,10 +432,17 @@ extern "C" dsa_status dsa_indexer_project(const dsa_rope_config* rope, int32_t n
     {
       ProfScope prof_("k_indexer_finish", s);
       hipLaunchKernelGGL(k_indexer_finish, dim3((unsigned)n_tokens, kVecs + 1), dim3(256), 0, s, (const float*)part,
-                         ks, gamma_q, gamma_k, (const float2*)cs, index_q, index_k, z, n_tokens);
+                         ks, gamma_q, gamma_k, pos, fr, index_q, index_k, z, n_tokens);
     }
     return check_launch(who);
   }
+  float2* cs = (float2*)workspace;
+  {
+    ProfScope prof_("k_rope_table", s);
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n_tokens + 1) / 2)), dim3(64), 0, s, pos, n_tokens, fr, cs);
+  }
+  st = check_launch(who);
+  if (st != DSA_OK) return st;
   ProjArgs a;
   a.x = x; a.w = w; a.gq = gamma_q; a.gk = gamma_k; a.cs = cs; a.iq = index_q; a.ik = index_k;
   a.T = n_tokens; a.H = hidden;
