@@ -9,21 +9,16 @@
 // section 一: original_max_position_embeddings 1048576, about 64 of the 192
 // head dimensions rotate.
 //
-// k_indexer_proj: one fused MFMA GEMM + epilogue per (128 tokens, 256-wide
-// output vector).  The 20 vectors are the 16 index_q heads and the 4 index_k
-// groups; a block computes x[128 x H] . W_h^T[H x 256] with 4 waves of 64
-// columns each (8 x 4 tiles of v_mfma_f32_16x16x32_bf16 per wave, 128 fp32
-// accumulators), the x tile staged in LDS (shared by the 4 waves, double
-// buffered, padded rows), the weight fragments read straight from memory
-// (each wave reads its own 64 rows of W).  The epilogue never leaves
-// registers except for the RMS: per-token sums of squares of the 4 waves
-// meet in LDS, then x * rsqrt(mean + eps) * gamma, the rotate-half rotation
-// of dimensions 0..63 (wave 0 holds both halves of every pair in one lane),
-// bf16 rounding and the store.
-// k_indexer_z: the 16 z columns (x . W_z^T, fp32 out), 4 waves splitting H.
-// k_rope_qk: the rotation applied in place to q [T][64][192], k [T][4][192].
-// Angles are pos * freq in double, reduced to [-pi, pi] before sincos, so
-// positions up to 2^31 keep full fp32 accuracy.
+// The projection is one GEMM, y = x . W^T in fp32, W holding the 4096
+// index_q, 1024 index_k and 16 z rows: for many tokens k_indexer_gemm
+// (128 x 128 tiles through LDS, XCD-aware tile order), for up to 64 tokens
+// (decode) k_indexer_proj_splitk (split over the hidden dimension, so the
+// weights stream once over the whole GPU).  k_indexer_finish then sums the
+// partials of each token, RMS-normalises each 256-d vector, applies the
+// gain, rotates dimensions 0..63 (rotate-half) and rounds to bf16; z is
+// the plain sum.  k_rope_qk rotates the attention's q [T][64][192] and
+// k [T][4][192] in place.  Angles are pos * freq in double, reduced to
+// [-pi, pi] before sincos, so positions up to 2^31 keep full fp32 accuracy.
 #include <math.h>
 
 #include "common.hpp"
@@ -59,145 +54,6 @@ __global__ __launch_bounds__(64) void k_rope_table(const int32_t* __restrict__ p
   const int i = threadIdx.x & 31;
   if (t >= n) return;
   cs[t * kRotPairs + i] = rope_cs(pos[t], fr.f[i]);
-}
-
-#ifndef DSA_FE_PM
-#define DSA_FE_PM 128
-#endif
-constexpr int kPM = DSA_FE_PM;  // tokens per block
-constexpr int kPRT = kPM / 16;  // row tiles per wave
-constexpr int kPLR = kPM / 32;  // x-tile rows each thread copies per stage
-constexpr int kPK = 64;        // k per LDS stage
-constexpr int kPPitch = kPK + 8;  // padded row (elements): 144 bytes, conflict-free fragment reads
-
-struct ProjArgs {
-  const uint16_t* x;   // [T][H]
-  const uint16_t* w;   // [kProjN][H]
-  const float* gq;     // [256]
-  const float* gk;     // [256]
-  const float2* cs;    // [T][32] (cos, sin)
-  uint16_t* iq;        // [T][16][256]
-  uint16_t* ik;        // [T][4][256]
-  int32_t T, H;
-};
-
-__global__ __launch_bounds__(256) void k_indexer_proj(ProjArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * kPM;
-  const int h = blockIdx.y;  // output vector 0..19
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kPM * kPPitch];
-  __shared__ float red[4][kPM];
-
-  // x tile loads: thread t copies rows t/8 + 32r, 8 elements at (t%8)*8
-  const int lr = threadIdx.x >> 3, lk = (threadIdx.x & 7) * 8;
-  const uint16_t* xrow[kPLR];
-#pragma unroll
-  for (int r = 0; r < kPLR; ++r) {
-    int64_t t = t0 + lr + 32 * r;
-    t = t < a.T ? t : a.T - 1;  // rows past the end re-read the last token; never stored
-    xrow[r] = a.x + t * a.H + lk;
-  }
-  // weight fragments: column (64*wave + 16*ct + n) of vector h, k = 8*kb .. +7 of each 32-step
-  const uint16_t* wrow[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) wrow[ct] = a.w + ((int64_t)h * kProxy + 64 * wave + 16 * ct + n) * a.H + 8 * kb;
-
-  f32x4 acc[kPRT][4];
-#pragma unroll
-  for (int rt = 0; rt < kPRT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nst = a.H / kPK;
-  u32x4 xr[kPLR];
-#pragma unroll
-  for (int r = 0; r < kPLR; ++r) xr[r] = ld16(xrow[r]);
-#pragma unroll
-  for (int r = 0; r < kPLR; ++r) *(u32x4*)&xs[0][(lr + 32 * r) * kPPitch + lk] = xr[r];
-  // weight fragments run one stage ahead of their use
-  u32x4 wn[2][4];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) wn[ks][ct] = ld16(wrow[ct] + 32 * ks);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    const int64_t k0 = (int64_t)st * kPK;
-    // next stage's x rows and weight fragments while this stage computes
-    // (past the last stage: a re-read of the last one, never used)
-    const int64_t kn = st + 1 < nst ? k0 + kPK : k0;
-#pragma unroll
-    for (int r = 0; r < kPLR; ++r) xr[r] = ld16(xrow[r] + kn);
-    u32x4 wf[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        wf[ks][ct] = wn[ks][ct];
-        wn[ks][ct] = ld16(wrow[ct] + kn + 32 * ks);
-      }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int rt = 0; rt < kPRT; ++rt) {
-        const bf16x8 af = as_bf16x8(*(const u32x4*)&xs[buf][(16 * rt + n) * kPPitch + 32 * ks + 8 * kb]);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = mfma16x16x32(af, as_bf16x8(wf[ks][ct]), acc[rt][ct]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kPLR; ++r) *(u32x4*)&xs[buf ^ 1][(lr + 32 * r) * kPPitch + lk] = xr[r];
-    __syncthreads();
-  }
-
-  // RMS over the vector's 256 columns: lane holds rows 16rt + 4kb + i, columns 64wave + 16ct + n
-#pragma unroll
-  for (int rt = 0; rt < kPRT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float ss = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) ss += acc[rt][ct][i] * acc[rt][ct][i];
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
-      if (n == 0) red[wave][16 * rt + 4 * kb + i] = ss;
-    }
-  __syncthreads();
-  const float* gam = h < kIdxHeads ? a.gq : a.gk;
-  float g[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) g[ct] = gam[64 * wave + 16 * ct + n];
-  uint16_t* out = h < kIdxHeads ? a.iq + (int64_t)h * kProxy : a.ik + (int64_t)(h - kIdxHeads) * kProxy;
-  const int64_t tstride = (h < kIdxHeads ? kIdxHeads : kGroups) * kProxy;
-#pragma unroll
-  for (int rt = 0; rt < kPRT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rt + 4 * kb + i;
-      const int64_t t = t0 + row;
-      const float ms = (red[0][row] + red[1][row] + red[2][row] + red[3][row]) * (1.0f / kProxy);
-      const float inv = 1.0f / sqrtf(ms + kNormEps);
-      float y[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) y[ct] = acc[rt][ct][i] * inv * g[ct];
-      if (wave == 0) {  // columns 0..63: pairs (n, n + 32) and (16 + n, 48 + n)
-        const int64_t tc = t < a.T ? t : a.T - 1;
-        const float2 c0 = a.cs[tc * kRotPairs + n], c1 = a.cs[tc * kRotPairs + 16 + n];
-        const float y0 = y[0] * c0.x - y[2] * c0.y, y2 = y[2] * c0.x + y[0] * c0.y;
-        const float y1 = y[1] * c1.x - y[3] * c1.y, y3 = y[3] * c1.x + y[1] * c1.y;
-        y[0] = y0;
-        y[1] = y1;
-        y[2] = y2;
-        y[3] = y3;
-      }
-      if (t < a.T) {
-        uint16_t* o = out + t * tstride + 64 * wave + n;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) o[16 * ct] = (uint16_t)(pack_bf16x2(y[ct], 0.f) & 0xffffu);
-      }
-    }
 }
 
 // Few tokens (decode): the weights are the cost (5136 x hidden bf16), and
@@ -258,71 +114,155 @@ __global__ __launch_bounds__(64) void k_indexer_proj_splitk(const uint16_t* __re
       }
 }
 
-// block = (token, output vector 0..19, or 20 = z); thread = column.
+// block (t, b) = token t; wave w of it takes vectors 4b + w, 4b + w + 4B,
+// ... (B = gridDim.y: 5 for few tokens, which spreads the split sums over
+// more CUs, 1 for many).  Lane owns columns lane + 64k, k = 0..3: sum of the
+// split partials in split order, RMS by wave reduction, gain, rotation of
+// columns 0..63 (the partner of column c < 32 is lane c + 32 of the same
+// slot), bf16 store; block (t, 0) also sums the z columns.  No barrier.
 __global__ __launch_bounds__(256) void k_indexer_finish(const float* __restrict__ part, int32_t ks,
                                                         const float* __restrict__ gq, const float* __restrict__ gk,
                                                         const int32_t* __restrict__ pos, RopeFreqs fr,
                                                         uint16_t* __restrict__ iq, uint16_t* __restrict__ ik,
                                                         float* __restrict__ z, int32_t T) {
   const int64_t t = blockIdx.x;
-  const int h = blockIdx.y, c = threadIdx.x, lane = c & 63, wave = c >> 6;
-  __shared__ float red[4];
-  __shared__ float ys[kRotDims];
-  if (h == kVecs) {
-    if (c < kIdxHeads) {
-      float acc = 0.f;
-      for (int sp = 0; sp < ks; ++sp) acc += part[((int64_t)sp * T + t) * kProjN + kVecs * kProxy + c];
-      z[t * kIdxHeads + c] = acc;
-    }
-    return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t pstride = (int64_t)T * kProjN;
+  const float* pt = part + t * kProjN;
+  if (blockIdx.y == 0 && wave == 0 && lane < kIdxHeads) {
+    float acc = 0.f;
+    for (int sp = 0; sp < ks; ++sp) acc += pt[sp * pstride + kVecs * kProxy + lane];
+    z[t * kIdxHeads + lane] = acc;
   }
-  // the rotation's (cos, sin) for this column's pair, while the partials load
-  const float2 cc = c < kRotDims ? rope_cs(pos[t], fr.f[c & (kRotPairs - 1)]) : make_float2(1.f, 0.f);
-  float y = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < ks; ++sp) y += part[((int64_t)sp * T + t) * kProjN + h * kProxy + c];
-  float ss = y * y;
+  const float2 cc = rope_cs(pos[t], fr.f[lane & (kRotPairs - 1)]);
+  for (int h = 4 * blockIdx.y + wave; h < kVecs; h += 4 * gridDim.y) {
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int sp = 0; sp < ks; ++sp) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  const float ms = (red[0] + red[1] + red[2] + red[3]) * (1.0f / kProxy);
-  y = y * (1.0f / sqrtf(ms + kNormEps)) * (h < kIdxHeads ? gq : gk)[c];
-  if (c < kRotDims) ys[c] = y;
-  __syncthreads();
-  if (c < kRotDims) {
-    y = c < kRotPairs ? ys[c] * cc.x - ys[c + kRotPairs] * cc.y : ys[c] * cc.x + ys[c - kRotPairs] * cc.y;
+      for (int k = 0; k < 4; ++k) y[k] += pt[sp * pstride + h * kProxy + 64 * k + lane];
+    }
+    float ss = (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kProxy) + kNormEps);
+    const float* g = h < kIdxHeads ? gq : gk;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] *= inv * g[64 * k + lane];
+    const float other = __shfl_xor(y[0], kRotPairs);  // column lane ^ 32 of slot 0
+    y[0] = lane < kRotPairs ? y[0] * cc.x - other * cc.y : y[0] * cc.x + other * cc.y;
+    uint16_t* o = h < kIdxHeads ? iq + (t * kIdxHeads + h) * kProxy : ik + (t * kGroups + h - kIdxHeads) * kProxy;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[64 * k + lane] = (uint16_t)(pack_bf16x2(y[k], 0.f) & 0xffffu);
   }
-  uint16_t* o = h < kIdxHeads ? iq + (t * kIdxHeads + h) * kProxy : ik + (t * kGroups + h - kIdxHeads) * kProxy;
-  o[c] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xffffu);
 }
 
 static int32_t splitk_kper(int32_t hidden) { return hidden % 256 == 0 ? 256 : 128; }
 
-// z = x . W_z^T: block = 16 tokens, wave w takes k in [w*H/4, (w+1)*H/4).
-__global__ __launch_bounds__(256) void k_indexer_z(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                   float* __restrict__ z, int32_t T, int32_t H) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * 16;
-  __shared__ f32x4 part[4][64];
-  int64_t t = t0 + n;
-  t = t < T ? t : T - 1;
-  const uint16_t* xr = x + t * H + 8 * kb;
-  const uint16_t* wr = w + ((int64_t)kVecs * kProxy + n) * H + 8 * kb;
-  const int kq = H / 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = wave * kq; k < (wave + 1) * kq; k += 32)
-    acc = mfma16x16x32(as_bf16x8(ld16(xr + k)), as_bf16x8(ld16(wr + k)), acc);
-  part[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    const f32x4 s = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+// Many tokens: y[T][5136] = x . W^T in fp32 (the finishing kernel then
+// normalises, rotates and converts).  Block = 128 tokens x 128 weight rows,
+// both tiles staged through LDS (double buffered, padded rows) and shared:
+// wave (wm, wn) computes rows 64wm.. x columns 64wn.. as 4 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16, so each 16-byte fragment read from LDS feeds 4
+// MFMAs.  Two blocks fit a CU (72 KB of LDS, < 128 VGPRs).
+constexpr int kGM = 128, kGN = 128, kGK = 64, kGPitch = kGK + 8;
+
+// Tile order: consecutive blocks go to the 8 XCDs in turn, so block b runs
+// on XCD b % 8; XCD x takes the x-th eighth of the tiles, ordered column
+// tile by column tile, so the blocks one XCD runs together share a few
+// weight tiles and every token tile through its own L2.
+__global__ __launch_bounds__(256, 2) void k_indexer_gemm(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w, float* __restrict__ y,
+                                                         int32_t T, int32_t H) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int nrow = (T + kGM - 1) / kGM;
+  const int ntile = nrow * ((kProjN + kGN - 1) / kGN);
+  const int per_xcd = (ntile + 7) / 8;
+  const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (tile >= ntile) return;
+  const int64_t c0 = (int64_t)(tile / nrow) * kGN, t0 = (int64_t)(tile % nrow) * kGM;
+  __shared__ __attribute__((aligned(16))) uint16_t as[2][kGM * kGPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kGN * kGPitch];
+  // tile copies: thread t moves rows t/8 + 32r (r = 0..3) of each tile, 8 elements at (t%8)*8
+  const int lr = threadIdx.x >> 3, lk = (threadIdx.x & 7) * 8;
+  const uint16_t* ar[4];
+  const uint16_t* br[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t tt = t0 + 4 * kb + i;  // row 4kb + i, column n
-      if (tt < T) z[tt * kIdxHeads + n] = s[i];
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int64_t t = t0 + lr + 32 * r, c = c0 + lr + 32 * r;
+    ar[r] = x + (t < T ? t : T - 1) * H + lk;             // rows past the end: re-reads, never stored
+    br[r] = w + (c < kProjN ? c : kProjN - 1) * H + lk;
   }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // two stages of tile copies in flight: the registers of stage st + 2 are
+  // requested while stage st computes from LDS (stage st + 1 already sits in
+  // the other LDS buffer), which covers the memory latency at 2 blocks per CU
+  const int nst = H / kGK;
+  u32x4 ra[2][4], rb[2][4];
+  auto fetch = [&](u32x4 (&a)[4], u32x4 (&b)[4], int stage) {
+    const int64_t k = (int64_t)(stage < nst ? stage : nst - 1) * kGK;  // past the end: a re-read, unused
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = ld16(ar[r] + k);
+      b[r] = ld16(br[r] + k);
+    }
+  };
+  auto stash = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], int buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *(u32x4*)&as[buf][(lr + 32 * r) * kGPitch + lk] = a[r];
+      *(u32x4*)&bs[buf][(lr + 32 * r) * kGPitch + lk] = b[r];
+    }
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = as_bf16x8(*(const u32x4*)&as[buf][(64 * wm + 16 * i + n) * kGPitch + 32 * ks + 8 * kb]);
+        bf[i] = as_bf16x8(*(const u32x4*)&bs[buf][(64 * wn + 16 * i + n) * kGPitch + 32 * ks + 8 * kb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+    }
+  };
+  fetch(ra[0], rb[0], 0);
+  fetch(ra[1], rb[1], 1);
+  stash(ra[0], rb[0], 0);
+  fetch(ra[0], rb[0], 2);
+  __syncthreads();
+  // nst is even (H is a multiple of 128): stages go in pairs with static register sets
+  for (int st = 0; st < nst; st += 2) {
+    compute(0);
+    stash(ra[1], rb[1], 1);  // stage st + 1
+    fetch(ra[1], rb[1], st + 3);
+    __syncthreads();
+    compute(1);
+    stash(ra[0], rb[0], 0);  // stage st + 2
+    fetch(ra[0], rb[0], st + 4);
+    __syncthreads();
+  }
+  // tile (i, j): lane holds rows 4kb + e, column n
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = c0 + 64 * wn + 16 * j + n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t t = t0 + 64 * wm + 16 * i + 4 * kb + e;
+        if (t < T && c < kProjN) y[t * kProjN + c] = acc[i][j][e];
+      }
+    }
 }
 
 // In-place rotation of the first 64 dimensions of every head of q and k:
@@ -376,7 +316,8 @@ static dsa_status check_rope(const char* who, const dsa_rope_config* c) {
 
 static size_t table_bytes(int32_t n) { return ((size_t)n * kRotPairs * sizeof(float2) + 255) / 256 * 256; }
 static size_t splitk_bytes(int32_t n, int32_t hidden) {
-  if (n > kSmallT || hidden <= 0) return 0;
+  if (hidden <= 0) return 0;
+  if (n > kSmallT) return (size_t)n * kProjN * sizeof(float);  // the fp32 projection
   return (size_t)(hidden / splitk_kper(hidden)) * n * kProjN * sizeof(float);
 }
 
@@ -431,33 +372,28 @@ extern "C" dsa_status dsa_indexer_project(const dsa_rope_config* rope, int32_t n
     if (st != DSA_OK) return st;
     {
       ProfScope prof_("k_indexer_finish", s);
-      hipLaunchKernelGGL(k_indexer_finish, dim3((unsigned)n_tokens, kVecs + 1), dim3(256), 0, s, (const float*)part,
-                         ks, gamma_q, gamma_k, pos, fr, index_q, index_k, z, n_tokens);
+      hipLaunchKernelGGL(k_indexer_finish, dim3((unsigned)n_tokens, kVecs / 4), dim3(256), 0, s, (const float*)part, ks,
+                         gamma_q, gamma_k, pos, fr, index_q, index_k, z, n_tokens);
     }
     return check_launch(who);
   }
-  float2* cs = (float2*)workspace;
   {
-    ProfScope prof_("k_rope_table", s);
-    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n_tokens + 1) / 2)), dim3(64), 0, s, pos, n_tokens, fr, cs);
+    float* yv = (float*)((char*)workspace + table_bytes(n_tokens));
+    {
+      ProfScope prof_("k_indexer_proj", s);
+      const int ntile = ((n_tokens + kGM - 1) / kGM) * ((kProjN + kGN - 1) / kGN);
+      hipLaunchKernelGGL(k_indexer_gemm, dim3((unsigned)(8 * ((ntile + 7) / 8))), dim3(256), 0, s, x, w, yv,
+                         n_tokens, hidden);
+    }
+    st = check_launch(who);
+    if (st != DSA_OK) return st;
+    {
+      ProfScope prof_("k_indexer_finish", s);
+      hipLaunchKernelGGL(k_indexer_finish, dim3((unsigned)n_tokens, 1), dim3(256), 0, s, (const float*)yv, 1, gamma_q,
+                         gamma_k, pos, fr, index_q, index_k, z, n_tokens);
+    }
+    return check_launch(who);
   }
-  st = check_launch(who);
-  if (st != DSA_OK) return st;
-  ProjArgs a;
-  a.x = x; a.w = w; a.gq = gamma_q; a.gk = gamma_k; a.cs = cs; a.iq = index_q; a.ik = index_k;
-  a.T = n_tokens; a.H = hidden;
-  {
-    ProfScope prof_("k_indexer_proj", s);
-    hipLaunchKernelGGL(k_indexer_proj, dim3((unsigned)((n_tokens + kPM - 1) / kPM), kVecs), dim3(256), 0, s, a);
-  }
-  st = check_launch(who);
-  if (st != DSA_OK) return st;
-  {
-    ProfScope prof_("k_indexer_z", s);
-    hipLaunchKernelGGL(k_indexer_z, dim3((unsigned)((n_tokens + 15) / 16)), dim3(256), 0, s, x, w, z, n_tokens,
-                       hidden);
-  }
-  return check_launch(who);
 }
 
 extern "C" dsa_status dsa_rope_qk(const dsa_rope_config* rope, int32_t n_tokens, const int32_t* pos, uint16_t* q,

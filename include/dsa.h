@@ -527,12 +527,13 @@ dsa_status dsa_rope_config_default(dsa_rope_config* rope);
 
 /* Workspace bytes of dsa_indexer_project (hidden size `hidden`) and of
  * dsa_rope_qk (hidden 0) for n_tokens tokens: a cos/sin table of 32 pairs
- * per token, and for up to 64 tokens the fp32 partial sums of the split
- * projection (hidden/256 or hidden/128 splits x n_tokens x 5136). */
+ * per token, plus the fp32 projection (n_tokens x 5136; for up to 64 tokens
+ * one such block per split of the hidden dimension, hidden/256 or
+ * hidden/128 splits). */
 size_t dsa_indexer_workspace_size(int32_t n_tokens, int32_t hidden);
 
 /*
- * Hidden states -> the indexer's inputs, fused: y = x . W^T (bf16 MFMA, fp32
+ * Hidden states -> the indexer's inputs: y = x . W^T (bf16 MFMA, fp32
  * accumulation); each 256-d index vector is RMS-normalised (eps 1e-6, gain
  * gamma_q for the 16 query heads, gamma_k for the 4 key groups) and its
  * first 64 dimensions rotated by the token's position; z is the plain
@@ -571,7 +572,7 @@ dsa_status dsa_rope_qk(const dsa_rope_config* rope, int32_t n_tokens, const int3
  * names: k_compress, k_cache_write, k_score_decode,
  * k_score_prefill, k_select, k_sgqa_decode, k_sgqa_merge, k_sgqa_prefill,
  * k_swa_stage, k_swa_attend, k_ring_append, k_sgqa_prefill_merged, k_rope_table,
- * k_indexer_proj, k_indexer_finish, k_indexer_z, k_rope_qk.  Host-side state only, guarded
+ * k_indexer_proj, k_indexer_finish, k_rope_qk.  Host-side state only, guarded
  * by a mutex; at most 8192 launches are recorded between resets.
  */
 dsa_status dsa_profile_enable(int on);

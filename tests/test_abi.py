@@ -216,6 +216,6 @@ def test_rope_config_default_and_checks(lib):
     bad.rot_dims, bad.high_freq_factor = 64, 0.5
     assert lib.dsa_rope_qk(ctypes.byref(bad), 4, vp, vp, vp, vp, ws, None) == 1
     assert lib.dsa_rope_qk(None, 4, vp, vp, vp, vp, ws, None) == 1
-    assert lib.dsa_indexer_workspace_size(2048, 6144) >= 2048 * 32 * 8
+    assert lib.dsa_indexer_workspace_size(2048, 6144) >= 2048 * 32 * 8 + 2048 * 5136 * 4
     assert lib.dsa_indexer_workspace_size(4, 6144) >= 4 * 32 * 8 + 24 * 4 * 5136 * 4
     assert lib.dsa_rope_qk(ctypes.byref(c), 4, vp, vp, vp, vp, 16, None) == 3  # workspace too small

@@ -1,4 +1,4 @@
-"""Indexer front-end (fused projection + RMSNorm + partial RoPE) and the attention's partial RoPE through
+"""Indexer front-end (projection, RMSNorm, partial RoPE) and the attention's partial RoPE through
 the C ABI, against the fp64 oracle of oracle/frontend.py on seeded inputs: ragged token counts around
 the 128-token tile, positions from 0 to 2^20 - 1, and the 2048-token chunk at hidden 6144 (sampled
 tokens).  Tolerances: the index vectors and rotated Q/K are bf16 (one rounding of values near 1: at
