@@ -31,6 +31,8 @@ constexpr int kVecs = kIdxHeads + kGroups;  // 20 normalised 256-d outputs per t
 constexpr int kProjN = kVecs * kProxy + kIdxHeads;  // 5136 weight rows
 constexpr float kNormEps = 1e-6f;
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 struct RopeFreqs {
   double f[kRotPairs];
 };
@@ -162,9 +164,9 @@ static int32_t splitk_kper(int32_t hidden) { return hidden % 256 == 0 ? 256 : 12
 // Many tokens: y[T][5136] = x . W^T in fp32 (the finishing kernel then
 // normalises, rotates and converts).  Block = 128 tokens x 128 weight rows,
 // both tiles staged through LDS (double buffered, padded rows) and shared:
-// wave (wm, wn) computes rows 64wm.. x columns 64wn.. as 4 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16, so each 16-byte fragment read from LDS feeds 4
-// MFMAs.  Two blocks fit a CU (72 KB of LDS, < 128 VGPRs).
+// wave (wm, wn) computes rows 64wm.. x columns 64wn.. as 2 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, so each 16-byte fragment read from LDS feeds 2
+// MFMAs of 32K flops.  Two blocks fit a CU (72 KB of LDS, 186 VGPRs).
 constexpr int kGM = 128, kGN = 128, kGK = 64, kGPitch = kGK + 8;
 
 // Tile order: consecutive blocks go to the 8 XCDs in turn, so block b runs
@@ -195,11 +197,13 @@ __global__ __launch_bounds__(256, 2) void k_indexer_gemm(const uint16_t* __restr
     ar[r] = x + (t < T ? t : T - 1) * H + lk;             // rows past the end: re-reads, never stored
     br[r] = w + (c < kProjN ? c : kProjN - 1) * H + lk;
   }
-  f32x4 acc[4][4];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   // two stages of tile copies in flight: the registers of stage st + 2 are
   // requested while stage st computes from LDS (stage st + 1 already sits in
   // the other LDS buffer), which covers the memory latency at 2 blocks per CU
@@ -221,18 +225,21 @@ __global__ __launch_bounds__(256, 2) void k_indexer_gemm(const uint16_t* __restr
     }
   };
   auto compute = [&](int buf) {
+    // v_mfma_f32_32x32x16_bf16: lane l holds row l % 32, k 8(l / 32) .. +7 of
+    // A (and column l % 32 of B); half the fragment reads per flop of 16x16x32
+    const int r32 = lane & 31, k8 = 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bf[4];
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 af[2], bf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = as_bf16x8(*(const u32x4*)&as[buf][(64 * wm + 16 * i + n) * kGPitch + 32 * ks + 8 * kb]);
-        bf[i] = as_bf16x8(*(const u32x4*)&bs[buf][(64 * wn + 16 * i + n) * kGPitch + 32 * ks + 8 * kb]);
+      for (int i = 0; i < 2; ++i) {
+        af[i] = as_bf16x8(*(const u32x4*)&as[buf][(64 * wm + 32 * i + r32) * kGPitch + 16 * ks + k8]);
+        bf[i] = as_bf16x8(*(const u32x4*)&bs[buf][(64 * wn + 32 * i + r32) * kGPitch + 16 * ks + k8]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   };
   fetch(ra[0], rb[0], 0);
@@ -251,15 +258,15 @@ __global__ __launch_bounds__(256, 2) void k_indexer_gemm(const uint16_t* __restr
     fetch(ra[0], rb[0], st + 4);
     __syncthreads();
   }
-  // tile (i, j): lane holds rows 4kb + e, column n
+  // 32 x 32 tile (i, j): element e of lane l is row 8(e/4) + 4(l/32) + e%4, column l % 32
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t c = c0 + 64 * wn + 16 * j + n;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t c = c0 + 64 * wn + 32 * j + (lane & 31);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t t = t0 + 64 * wm + 16 * i + 4 * kb + e;
+      for (int e = 0; e < 16; ++e) {
+        const int64_t t = t0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (t < T && c < kProjN) y[t * kProjN + c] = acc[i][j][e];
       }
     }
