@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void k_indexer_gemm(const uint16_t* __restr
                                                          const uint16_t* __restrict__ w, float* __restrict__ y,
                                                          int32_t T, int32_t H) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const int lane = threadIdx.x & 63;
   const int wm = wave & 1, wn = wave >> 1;
   const int nrow = (T + kGM - 1) / kGM;
   const int ntile = nrow * ((kProjN + kGN - 1) / kGN);
