@@ -163,3 +163,23 @@ def test_merged_prefill_paged_matches_contiguous():
                                             pools["k"], pools["v"], c["sel"], c["nsel"], out)
     torch.cuda.synchronize()
     assert np.array_equal(o1.view(np.uint32), H.bf16_np(out).reshape(o1.shape).view(np.uint32))
+
+
+def test_merged_prefill_edge_cases():
+    """A chunk at the very start of a sequence (positions 0..11: partial regions 0 and 1), top-1 (only
+    the forced current region), then the same chunk with empty lists for one group of every query and
+    for every group of odd queries (their output is 0, as the oracle defines it)."""
+    seed = 0xA50
+    c = _chunk(seed, [(0, 12)], correlated=False, topk=1)
+    out = _run(c, True)
+    _oracle_check(seed, c, out, 1, what="merged start of sequence")
+    nq = c["nq"]
+    sel = c["sel"].cpu().numpy().reshape(nq, G, 1).copy()
+    nsel = c["nsel"].cpu().numpy().reshape(nq, G).copy()
+    nsel[:, 1] = 0
+    nsel[1::2, :] = 0
+    c["sel"], c["nsel"] = H.i32(sel.ravel()), H.i32(nsel.ravel())
+    out = _run(c, True)
+    assert np.all(out[1::2] == 0.0)
+    assert np.all(out[:, 16:32] == 0.0)
+    _oracle_check(seed, c, out, 1, what="merged empty lists")
