@@ -42,3 +42,27 @@ def test_hadamard_rows_orthonormal():
     d = np.arange(256, dtype=np.uint32)
     H = np.stack([gi.ref_hadamard16(r, d) for r in range(1, 17)]).astype(np.float64)
     assert np.allclose(H @ H.T, np.eye(16))
+
+
+def test_correlated_chunk_recipe(gen_host):
+    """The correlated prefill chunk: noise 1 gives the i.i.d. index_q back bit for bit; with no noise,
+    query 64a is anchor a itself (t = 0) and z runs linearly between anchors; neighbouring queries are
+    far closer than unrelated ones."""
+    import dsa_inputs as gi
+    seed, n = 0xC0, 200
+    iq1, _ = gi.host_correlated_index_queries(seed, n, noise=1.0)
+    own = gi.host_normal_bf16(seed, gi.TID_IQ, n * 16 * 256, gi.IK_SCALE).reshape(n, 16, 256)
+    assert np.array_equal(iq1, own)
+    iq0, z0 = gi.host_correlated_index_queries(seed, n, noise=0.0)
+    anchors = gi.host_normal_bf16(seed, gi.TID_IQ_ANCHOR, (n // 64 + 2) * 16 * 256, gi.IK_SCALE).reshape(-1, 16, 256)
+    za = gi.host_uniform_f32(seed, gi.TID_Z_ANCHOR, (n // 64 + 2) * 16).reshape(-1, 16)
+    for a in range(n // 64 + 1):
+        if 64 * a < n:
+            assert np.array_equal(iq0[64 * a], anchors[a])
+            assert np.array_equal(z0[64 * a], za[a])
+    assert np.allclose(z0[32], 0.5 * (za[0] + za[1]), rtol=1e-6)
+    iq, _ = gi.host_correlated_index_queries(seed, n)
+    f = gi.bf16_to_f32(iq).reshape(n, -1)
+    near = np.mean([np.corrcoef(f[i], f[i + 1])[0, 1] for i in range(0, n - 1, 7)])
+    far = np.mean([np.corrcoef(f[i], f[(i + 97) % n])[0, 1] for i in range(0, n, 7)])
+    assert near > 0.95 and far < 0.6, (near, far)
