@@ -9,7 +9,12 @@ prefix (64K total).  Each figure carries the roofline of its dominant kernel (by
 method needs / the kernel's average hipEvent-timed duration, against the MI355X peak) and the
 CPU oracle's rate on a bounded sample of the same work.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu] [--profile-run]
+Further objects in the same line: the two workloads over paged caches and with FP8 K/V caches, the
+neighbour-merged prefill on a correlated chunk, the indexer front-end, the 3:1 sliding-window/DSA layer
+mix and a sliding-window prefill chunk (each can be skipped with its --no-* flag).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-paged] [--no-fp8] [--no-merged]
+                [--no-frontend] [--no-swa] [--no-cpu] [--graph] [--profile-run]
 Prints one JSON line.
 """
 from __future__ import annotations
