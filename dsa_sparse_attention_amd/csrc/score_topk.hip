@@ -72,11 +72,14 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Current region c of a query (clamped so every index stays in bounds).
+// Current region c of a query (clamped so every index stays in bounds).  Its
+// candidates are regions 0..c-1, so c = max_regions still fits every array
+// sized by max_regions (scores, tile maxima, the scoring grid); a decode query
+// in a partial region c = seq_len/8 is thus covered by max_regions = seq_len/8.
 __device__ __forceinline__ int64_t current_region(int32_t pos, int64_t R, int32_t max_regions) {
   int64_t c = pos < 0 ? 0 : (int64_t)pos / kRegion;
   if (c > R - 1) c = R - 1;
-  if (c > max_regions - 1) c = max_regions - 1;
+  if (c > max_regions) c = max_regions;
   return c;
 }
 

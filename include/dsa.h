@@ -234,7 +234,8 @@ size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_t n_queries
  *   index_q   [n_queries][16][P] bf16;  z [n_queries][16] fp32
  *   q_seq, q_pos [n_queries] int32 device; q_seq in [0, n_seqs)
  *   summ, scale  summaries of n_seqs sequences with capacity tcap (layout above)
- *   max_regions  host bound: p/8 < max_regions for every query (grid, workspace)
+ *   max_regions  host bound: p/8 <= max_regions for every query (grid,
+ *             workspace; the candidates r < p/8 must have r < max_regions)
  *   sel       [n_queries][G][topk] int32, ascending region ids, -1 padded
  *   n_sel     [n_queries][G] int32 = min(topk, c+1)
  *   scores_out NULL or [n_queries][G][max_regions] fp32: score(r) for r < c
@@ -335,7 +336,10 @@ size_t dsa_decode_step_workspace_size(const dsa_geometry* geom, int32_t batch, i
  *             capacity tcap (layouts above); summaries of all complete regions
  *             before the query's region must be present
  *   seq_len   [batch] int32 device, 1 <= seq_len <= tcap, including the token
- *   max_regions host bound: seq_len/8 <= max_regions (grid, workspace)
+ *   max_regions host bound: seq_len/8 <= max_regions (grid, workspace); a
+ *             query in a partial region (seq_len not a multiple of 8) has
+ *             current region seq_len/8 and candidates below it, so this bound
+ *             covers it
  *   sel, n_sel, out as for dsa_score_topk and dsa_sparse_gqa_decode
  *   workspace >= dsa_decode_step_workspace_size() bytes, 256-byte aligned;
  *             the same contents rules as dsa_score_topk's workspace apply

@@ -181,7 +181,11 @@ def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=No
     return res
 
 
-def assert_decode_parity(r, min_identical_frac=0.9):
+def assert_decode_parity(r, min_identical_frac=0.9, report=True):
+    """Every (sequence, group) is checked end to end.  Where the GPU's selection equals the oracle's,
+    its output is compared with the oracle's output; where the two differ inside the band (both
+    correct), with the oracle's attention recomputed on the GPU's own selection.  Selections that
+    differ stay rare (at least min_identical_frac identical); their count is returned and printed."""
     n_same = n_groups = 0
     for b, o in r["oracle"].items():
         L = r["lens"][b]
@@ -191,6 +195,8 @@ def assert_decode_parity(r, min_identical_frac=0.9):
         assert np.array_equal(r["scale"][b][:, :nr].view(np.uint32),
                               o["scales"][:nr].T.copy().view(np.uint32)), f"seq {b}: scales differ"
         c = (L - 1) // 8
+        differ = []
+        gpu_lists = []
         for g in range(G):
             osc = o["scores"][g]
             gsc = r["scores"][b, g, :c].astype(np.float64)
@@ -198,6 +204,7 @@ def assert_decode_parity(r, min_identical_frac=0.9):
                 tol = 2e-5 * max(np.abs(osc).max(), 1e-30)
                 assert np.all(np.abs(gsc - osc) <= tol), f"seq {b} group {g}: scores differ"
             gs = r["sel"][b, g, :r["nsel"][b, g]]
+            gpu_lists.append(gs.copy())
             assert np.all(r["sel"][b, g, r["nsel"][b, g]:] == -1)
             assert r["nsel"][b, g] == o["nsel"][g] == min(r["topk"], c + 1)
             same = check_selection(gs, o["sel"][g, :o["nsel"][g]], osc, c)
@@ -205,7 +212,17 @@ def assert_decode_parity(r, min_identical_frac=0.9):
             if same:
                 n_same += 1
                 assert_attn(r["out"][b, 16 * g:16 * g + 16], o["out"][16 * g:16 * g + 16], f"seq {b} group {g}")
+            else:
+                differ.append(g)
+        if differ:  # the oracle's attention on the GPU's selection
+            ref = O.attend(o["q"], o["K"], o["V"], L - 1, gpu_lists, k=r["topk"])
+            for g in differ:
+                assert_attn(r["out"][b, 16 * g:16 * g + 16], ref[16 * g:16 * g + 16],
+                            f"seq {b} group {g} (on the GPU's selection)")
     assert n_same >= min_identical_frac * n_groups, f"only {n_same}/{n_groups} selections identical"
+    if report:
+        print(f"decode parity: {n_groups} (sequence, group) outputs checked, {n_groups - n_same} of them on the "
+              f"GPU's own selection (differs from the oracle's inside the band)")
     return n_same, n_groups
 
 

@@ -85,6 +85,14 @@ def test_decode_1m_context_batch_of_4():
     H.assert_decode_parity(r)
 
 
+def test_decode_128k_context_batch_of_16():
+    """The 131,072-token batch-16 decode shape (16,384 regions per sequence, 1,024 tiles per problem)
+    in the launch configuration the benchmark times; sequences 0, 7 and 15 are checked against the
+    oracle."""
+    r = H.run_dsa_decode(0xDC, [131072] * 16, topk=512, check_seqs=[0, 7, 15])
+    H.assert_decode_parity(r)
+
+
 def test_decode_layer_mix_shape_batch_8_at_256k():
     """The DSA layer of the 3:1 layer-mix workload as the benchmark times it: batch 8 at 262,144
     tokens (2,048 tiles per problem); sequences 0 and 7 are checked against the oracle."""
@@ -173,6 +181,55 @@ def test_decode_step_matches_the_separate_calls(lens):
     assert torch.equal(s1, s2) and torch.equal(c1.view(torch.int32), c2.view(torch.int32))
 
 
+def test_decode_step_in_a_partial_region_with_tight_max_regions():
+    """Queries in a partial region (seq_len not a multiple of 8) with max_regions = max(seq_len // 8),
+    the documented bound: the current region seq_len // 8 is still selected and attended, and the
+    result equals a call with a generous max_regions bit for bit and the oracle within tolerance."""
+    seed = 0xDF
+    lens = [8195, 1003, 4099, 13]
+    B, tcap = len(lens), H.round128(max(lens))
+    R = tcap // 8
+    tight = max(L // 8 for L in lens)
+    assert tight < R
+    geom = dsa.geometry()
+    ik = H.dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
+    K = H.dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_KTILED)
+    V = H.dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
+    q, iq, z = H.dev_queries(seed, B)
+    lens_np = np.asarray(lens, dtype=np.int32)
+    res = []
+    for mr in (tight, R):
+        summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
+        scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
+        dsa.dsa_compress_regions(geom, ik, tcap, H.i32(np.zeros(B)), H.i32(lens_np // 8), R, summ, scale)
+        sel = torch.empty(B * G * 512, dtype=torch.int32, device="cuda")
+        nsel = torch.empty(B * G, dtype=torch.int32, device="cuda")
+        out = torch.empty(B * HQ * D, dtype=H.BF16, device="cuda")
+        dsa.dsa_decode_step(geom, q, iq, z, ik, K, V, tcap, H.i32(lens_np), summ, scale, mr, sel, nsel, out)
+        res.append((sel, nsel, out))
+    torch.cuda.synchronize()
+    (s1, n1, o1), (s2, n2, o2) = res
+    assert torch.equal(n1, n2) and torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    gsel = s1.cpu().numpy().reshape(B, G, 512)
+    gn = n1.cpu().numpy().reshape(B, G)
+    go = H.bf16_np(o1).reshape(B, HQ, D)
+    hq, hiq, hz = H.host_queries(seed, B)
+    for b in (0, 1):
+        L = lens[b]
+        c = (L - 1) // 8
+        for g in range(G):
+            assert c in gsel[b, g, :gn[b, g]].tolist(), "current region not selected"
+        ikh = gi.host_index_k(seed, tcap, G, P, b, 0, L)
+        Kh = gi.host_tokens_bf16(seed, gi.TID_K, tcap, G, D, b, 0, L)
+        Vh = gi.host_tokens_bf16(seed, gi.TID_V, tcap, G, D, b, 0, L)
+        codes, scales = O.compress_regions(ikh, 0, L // 8)
+        ref = O.attend(hq[b], Kh, Vh, L - 1, [gsel[b, g, :gn[b, g]] for g in range(G)])
+        H.assert_attn(go[b], ref, f"seq {b}")
+        osel, on, _, _ = O.dsa_query(hiq[b], hz[b], codes, scales, hq[b], Kh, Vh, L - 1)
+        assert np.array_equal(on, gn[b])
+
+
 def test_decode_attention_on_oracle_selection():
     """Sparse GQA alone: the oracle's selection is fed to the GPU kernel, every head compared."""
     seed = 0xD7
@@ -257,6 +314,7 @@ def _prefill(seed, seqs, topk=512, check_every=1, zero_z=False):
         osel, on, oout, osc = O.dsa_query(hiq[i], hz[i], codes, scales, hq[i], Kh, Vh, p, k=topk, want_scores=True)
         osels[i], onsel[i] = osel, on
         c = p // 8
+        differ = []
         for g in range(G):
             if c:
                 tol = 2e-5 * max(np.abs(osc[g]).max(), 1e-30)
@@ -268,7 +326,16 @@ def _prefill(seed, seqs, topk=512, check_every=1, zero_z=False):
                 n_same += 1
                 worst.append(H.assert_attn(gout[i, 16 * g:16 * g + 16], oout[16 * g:16 * g + 16],
                                            f"query {i} group {g}"))
+            else:
+                differ.append(g)
+        if differ:  # selections differing inside the band: the oracle's attention on the GPU's selection
+            ref = O.attend(hq[i], Kh, Vh, p, [gsel[i, g, :gnsel[i, g]] for g in range(G)], k=topk)
+            for g in differ:
+                worst.append(H.assert_attn(gout[i, 16 * g:16 * g + 16], ref[16 * g:16 * g + 16],
+                                           f"query {i} group {g} (on the GPU's selection)"))
     assert n_same >= 0.9 * n_tot, (n_same, n_tot)
+    print(f"prefill parity: {n_tot} (query, group) outputs checked, {n_tot - n_same} of them on the GPU's own "
+          f"selection (differs from the oracle's inside the band)")
     # attention alone on the oracle's selection, every head
     out2 = torch.empty(nq * HQ * D, dtype=H.BF16, device="cuda")
     checked = list(range(0, nq, check_every))
@@ -295,6 +362,14 @@ def test_prefill_64k_chunk_sampled():
     # the 64K prefill workload as timed: 2048 queries after a 63,488-token prefix; every 64th query
     # is checked against the oracle
     _prefill(0xE5, [(63488, 2048)], topk=512, check_every=64)
+
+
+def test_prefill_64k_chunk_with_held_back_tail_sampled():
+    """The 64K prefill at its hold-back shape: a 63,485-token prefix (its last region partial, so not
+    yet summarised) and 2,051 new tokens; the chunk completes that region and 256 more, which are
+    summarised in the chunk, and queries in the partial region attend it under the causal mask.
+    Every 64th query is checked against the oracle."""
+    _prefill(0xE7, [(63485, 2051)], topk=512, check_every=64)
 
 
 @pytest.mark.parametrize("seqs", [
@@ -441,6 +516,83 @@ def test_decode_is_deterministic():
     b = H.run_dsa_decode(0xAA, [6000, 3001], topk=512, check_seqs=[])
     for k in ("summ", "scale", "sel", "nsel", "out"):
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+
+
+def _prefill_inputs(seed, p0, n, topk=512):
+    """One sequence: prefix p0 summarised, chunk of n queries scored and selected on the GPU."""
+    tcap = H.round128(p0 + n)
+    R = tcap // 8
+    geom = dsa.geometry(topk=topk)
+    ik = H.dev_cache(seed, gi.TID_IK, 1, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE)
+    K = H.dev_cache(seed, gi.TID_K, 1, tcap, D, tcap, gi.LAYOUT_KTILED)
+    V = H.dev_cache(seed, gi.TID_V, 1, tcap, D, tcap, gi.LAYOUT_REGION_T)
+    summ = torch.zeros(G * R * P, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(G * R, dtype=torch.float32, device="cuda")
+    dsa.dsa_compress_regions(geom, ik, tcap, H.i32([0]), H.i32([(p0 + n) // 8]), R, summ, scale)
+    q, iq, z = H.dev_queries(seed, n)
+    qs, qp = H.i32(np.zeros(n)), H.i32(np.arange(p0, p0 + n))
+    return dict(geom=geom, tcap=tcap, R=R, K=K, V=V, summ=summ, scale=scale, q=q, iq=iq, z=z, qs=qs, qp=qp, n=n,
+                topk=topk)
+
+
+def _prefill_select(a):
+    sel = torch.empty(a["n"] * G * a["topk"], dtype=torch.int32, device="cuda")
+    nsel = torch.empty(a["n"] * G, dtype=torch.int32, device="cuda")
+    dsa.dsa_score_topk(a["geom"], a["iq"], a["z"], a["qs"], a["qp"], 1, a["summ"],
+                       a["scale"], a["tcap"], a["R"], sel, nsel)
+    return sel, nsel
+
+
+def _prefill_attend(a, sel, nsel, ws=None, merged=False):
+    out = torch.empty(a["n"] * HQ * D, dtype=H.BF16, device="cuda")
+    f = dsa.dsa_sparse_gqa_prefill_merged if merged else dsa.dsa_sparse_gqa_prefill
+    f(a["geom"], a["q"], a["qs"], a["qp"], 1, a["K"], a["V"], a["tcap"], sel, nsel, out, workspace=ws)
+    return out
+
+
+def test_prefill_is_deterministic():
+    """Selection and attention of a prefill chunk are bitwise identical from run to run (the 64K
+    prefill shape, every query of the chunk)."""
+    a = _prefill_inputs(0xAC, 63488, 2048)
+    s1, n1 = _prefill_select(a)
+    o1 = _prefill_attend(a, s1, n1)
+    s2, n2 = _prefill_select(a)
+    o2 = _prefill_attend(a, s2, n2)
+    torch.cuda.synchronize()
+    assert torch.equal(n1, n2) and torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_attention_does_not_depend_on_workspace_contents():
+    """The split partials of sparse GQA decode and the region-range partials of prefill (both in the
+    caller's workspace) are fully written before they are read: a workspace filled with NaN bytes
+    gives the same output, bit for bit, as a zeroed one."""
+    # decode: partial last splits (top-37), short and partial-region contexts
+    r = H.run_dsa_decode(0xAD, [3000, 2047, 17, 1], topk=37, check_seqs=[])
+    d = r["dev"]
+    B = r["B"]
+    lens = H.i32(r["lens"])
+    sel, nsel = H.i32(r["sel"].ravel()), H.i32(r["nsel"].ravel())
+    nb = dsa.dsa_sparse_gqa_workspace_size(d["geom"], B)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.empty(B * HQ * D, dtype=H.BF16, device="cuda")
+        dsa.dsa_sparse_gqa_decode(d["geom"], d["q"], d["K"], d["V"], r["tcap"], lens, sel, nsel, out, workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0].float()).any()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    # prefill (per-query and neighbour-merged): a chunk with a partial trailing region
+    a = _prefill_inputs(0xAE, 4003, 300)
+    s, n = _prefill_select(a)
+    nb = dsa.dsa_sparse_gqa_prefill_workspace_size(a["geom"], a["n"])
+    for merged in (False, True):
+        outs = [_prefill_attend(a, s, n, torch.full((nb,), fill, dtype=torch.uint8, device="cuda"), merged)
+                for fill in (0x00, 0xFF)]
+        torch.cuda.synchronize()
+        assert not torch.isnan(outs[0].float()).any()
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), f"merged={merged}"
 
 
 def test_decode_step_replays_from_a_hip_graph():
