@@ -43,6 +43,12 @@ MIX = dict(name="3:1 layer mix, decode: three sliding-window layers (512-token r
            batch=8, context=262144, topk=TOPK, planted=False, seed_index=4, swa_layers=3)
 SWA_PREFILL = dict(name="sliding-window layer, chunked prefill: 2048 new tokens after 63,488 (512-token ring)",
                    prefix=63488, chunk=2048, seed_index=4)
+DECODE_8K = dict(name="DSA decode, batch 1, 8,192-token context, top-512 (32 independent input copies in "
+                      "rotation so the 13.7 MB step is not served from the 256 MB Infinity Cache)",
+                 batch=1, context=8192, topk=TOPK, planted=False, seed_index=0, copies=32)
+DECODE_128K = dict(name="DSA decode, batch 16, 131,072-token context, top-512",
+                   batch=16, context=131072, topk=TOPK, planted=False, seed_index=1)
+QUERY_SETS = 8  # distinct query sets per decode workload, one per step in rotation
 W = 512
 # correlated variant of the prefill chunk: anchors every 64 queries, 10% of each query's own i.i.d.
 # index_q mixed in (adjacent selections then share ~88% of their regions)
@@ -130,58 +136,84 @@ class Calls:
 
 
 def setup_decode(cfg, steps_hint=1):
+    """Decode inputs resident in HBM.  cfg["copies"] independent input sets (caches, summaries and
+    queries of cfg["batch"] sequences each; a step uses copy i mod copies, so a workload smaller than
+    the 256 MB Infinity Cache is not served from it), and cfg["query_sets"] distinct query sets per
+    copy (q, index_q, z; a step uses set i mod query_sets, so neither the selection nor the gathered
+    K/V repeats from one step to the next)."""
     import torch
     import dsa_inputs as gi
     import dsa_sparse_attention_amd as dsa
 
     B, Lc, topk = cfg["batch"], cfg["context"], cfg["topk"]
+    copies, nqs = cfg.get("copies", 1), cfg.get("query_sets", QUERY_SETS)
     tcap, R = Lc, Lc // REG
     seed = gi.SEED_BASE + cfg["seed_index"]
     s = torch.cuda.current_stream().cuda_stream
     geom = dsa.geometry(topk=topk)
     t0 = time.time()
-    ik = torch.empty(B * G * tcap * P, dtype=torch.bfloat16, device="cuda")
-    K = torch.empty(B * G * tcap * D, dtype=torch.bfloat16, device="cuda")
-    V = torch.empty(B * G * tcap * D, dtype=torch.bfloat16, device="cuda")
-    gi.dev_tokens(ik.data_ptr(), s, seed, gi.TID_IK, B, tcap, G, P, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR,
+    NB = B * copies  # sequences of all copies: copy j holds sequences j*B .. j*B+B-1
+    ik = torch.empty(NB * G * tcap * P, dtype=torch.bfloat16, device="cuda")
+    K = torch.empty(NB * G * tcap * D, dtype=torch.bfloat16, device="cuda")
+    V = torch.empty(NB * G * tcap * D, dtype=torch.bfloat16, device="cuda")
+    gi.dev_tokens(ik.data_ptr(), s, seed, gi.TID_IK, NB, tcap, G, P, 0, tcap, tcap, tcap, gi.LAYOUT_GROUP_MAJOR,
                   gi.IK_SCALE, cfg["planted"])
-    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_KTILED)
-    gi.dev_tokens(V.data_ptr(), s, seed, gi.TID_V, B, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_REGION_T)
-    q = torch.empty(B * HQ * D, dtype=torch.bfloat16, device="cuda")
-    iq = torch.empty(B * HI * P, dtype=torch.bfloat16, device="cuda")
-    z = torch.empty(B * HI, dtype=torch.float32, device="cuda")
+    gi.dev_tokens(K.data_ptr(), s, seed, gi.TID_K, NB, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_KTILED)
+    gi.dev_tokens(V.data_ptr(), s, seed, gi.TID_V, NB, tcap, G, D, 0, tcap, tcap, tcap, gi.LAYOUT_REGION_T)
+    # query set u of copy j: queries of sequences j*B.. in the generator's query index space u*NB + j*B + b
+    NQ = NB * nqs
+    q = torch.empty(NQ * HQ * D, dtype=torch.bfloat16, device="cuda")
+    iq = torch.empty(NQ * HI * P, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(NQ * HI, dtype=torch.float32, device="cuda")
     gi.dev_flat(q.data_ptr(), s, seed, gi.TID_Q, q.numel(), 0, 1.0)
     gi.dev_flat(iq.data_ptr(), s, seed, gi.TID_IQ, iq.numel(), 0, gi.IK_SCALE)
     gi.dev_flat(z.data_ptr(), s, seed, gi.TID_Z, z.numel(), 1)
-    summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
-    scale = torch.zeros(B * G * R, dtype=torch.float32, device="cuda")
+    summ = torch.zeros(NB * G * R * P, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(NB * G * R, dtype=torch.float32, device="cuda")
     i32 = lambda v: torch.tensor(v, dtype=torch.int32, device="cuda")
     # untimed: summaries of every region before the one the query token completes
-    dsa.dsa_compress_regions(geom, ik, tcap, i32([0] * B), i32([R - 1] * B), R - 1, summ, scale)
+    dsa.dsa_compress_regions(geom, ik, tcap, i32([0] * NB), i32([R - 1] * NB), R - 1, summ, scale)
     torch.cuda.synchronize()
-    log(f"decode setup: {time.time() - t0:.1f}s")
+    log(f"decode setup ({B} x {Lc}, {copies} copies, {nqs} query sets): {time.time() - t0:.1f}s")
     rb, re_ = i32([R - 1] * B), i32([R] * B)
     qseq, qpos, slen = i32(list(range(B))), i32([Lc - 1] * B), i32([Lc] * B)
-    sel = torch.empty(B * G * topk, dtype=torch.int32, device="cuda")
-    nsel = torch.empty(B * G, dtype=torch.int32, device="cuda")
-    out = torch.empty(B * HQ * D, dtype=torch.bfloat16, device="cuda")
+    sel = torch.empty(NB * G * topk, dtype=torch.int32, device="cuda")
+    nsel = torch.empty(NB * G, dtype=torch.int32, device="cuda")
+    out = torch.empty(NB * HQ * D, dtype=torch.bfloat16, device="cuda")
     ws1 = dsa.workspace(dsa.dsa_score_topk_workspace_size(geom, B, R))
     ws2 = dsa.workspace(dsa.dsa_sparse_gqa_workspace_size(geom, B))
-    L = dsa.load()
-    p = Calls.p
-    gp = ctypes.byref(geom)
-    a_comp = (gp, B, p(ik), tcap, p(rb), p(re_), 1, p(summ), p(scale))
-    a_score = (gp, B, p(iq), p(z), p(qseq), p(qpos), B, p(summ), p(scale), tcap, R, p(sel), p(nsel), None,
-               p(ws1), ws1.numel())
-    a_attn = (gp, B, p(q), p(K), p(V), tcap, p(slen), p(sel), p(nsel), p(out), p(ws2), ws2.numel())
-
     ws3 = dsa.workspace(dsa.dsa_decode_step_workspace_size(geom, B, R))
-    a_fused = (gp, B, p(q), p(iq), p(z), p(ik), p(K), p(V), tcap, p(slen), p(summ), p(scale), R, p(sel), p(nsel),
-               p(out), p(ws3), ws3.numel())
+    L = dsa.load()
+    gp = ctypes.byref(geom)
+
+    def at(t, elems):  # pointer to element offset `elems` of tensor t
+        return ctypes.c_void_p(t.data_ptr() + elems * t.element_size())
+
+    variants = []  # (separate-call argument tuples, fused-call arguments) per (copy, query set)
+    for u in range(nqs):
+        for j in range(copies):
+            b0 = j * B  # first sequence of copy j
+            qi = u * NB + b0  # first query of set u, copy j
+            cq, ciq, cz = at(q, qi * HQ * D), at(iq, qi * HI * P), at(z, qi * HI)
+            cik, cK, cV = at(ik, b0 * G * tcap * P), at(K, b0 * G * tcap * D), at(V, b0 * G * tcap * D)
+            cs, csc = at(summ, b0 * G * R * P), at(scale, b0 * G * R)
+            csel, cns, co = at(sel, b0 * G * topk), at(nsel, b0 * G), at(out, b0 * HQ * D)
+            a_comp = (gp, B, cik, tcap, Calls.p(rb), Calls.p(re_), 1, cs, csc)
+            a_score = (gp, B, ciq, cz, Calls.p(qseq), Calls.p(qpos), B, cs, csc, tcap, R, csel, cns, None,
+                       Calls.p(ws1), ws1.numel())
+            a_attn = (gp, B, cq, cK, cV, tcap, Calls.p(slen), csel, cns, co, Calls.p(ws2), ws2.numel())
+            a_fused = (gp, B, cq, ciq, cz, cik, cK, cV, tcap, Calls.p(slen), cs, csc, R, csel, cns, co,
+                       Calls.p(ws3), ws3.numel())
+            variants.append((a_comp, a_score, a_attn, a_fused))
+    # interleave copies first: consecutive steps use different copies, then different query sets
+    order = [u * copies + j for u in range(nqs) for j in range(copies)]
+    state = {"i": 0}
 
     def step(st):
         # the whole step through one entry point (compression folded into the scoring launch), or
         # the three separate calls
+        a_comp, a_score, a_attn, a_fused = variants[order[state["i"] % len(order)]]
+        state["i"] += 1
         if cfg.get("separate"):
             rc = (L.dsa_compress_regions(*a_comp, st) or L.dsa_score_topk(*a_score, st)
                   or L.dsa_sparse_gqa_decode(*a_attn, st))
@@ -190,8 +222,34 @@ def setup_decode(cfg, steps_hint=1):
         if rc:
             raise RuntimeError(f"decode step failed: {rc} {L.dsa_last_error().decode()}")
 
+    step.variants = len(order)
     keep = (ik, K, V, q, iq, z, summ, scale, rb, re_, qseq, qpos, slen, sel, nsel, out, ws1, ws2, ws3, geom)
     return step, keep
+
+
+def rotate_queries(make_args, q, iq, z, B, fn, what):
+    """A step over QUERY_SETS argument tuples, one per query set u (queries u*B .. u*B+B-1 of q,
+    index_q and z); make_args(q_ptr, iq_ptr, z_ptr) builds one tuple."""
+    def at(t, elems):
+        return ctypes.c_void_p(t.data_ptr() + elems * t.element_size())
+    nqs = q.numel() // (B * HQ * D)
+    variants = [make_args(at(q, u * B * HQ * D), at(iq, u * B * HI * P), at(z, u * B * HI)) for u in range(nqs)]
+    state = {"i": 0}
+
+    def step(st):
+        args = variants[state["i"] % nqs]
+        state["i"] += 1
+        rc = fn(*args, st)
+        if rc:
+            raise RuntimeError(f"{what} failed: {rc} {dsa_error()}")
+
+    step.variants = nqs
+    return step
+
+
+def dsa_error():
+    import dsa_sparse_attention_amd as dsa
+    return dsa.load().dsa_last_error().decode()
 
 
 PAGE = 128  # positions per page of the paged caches
@@ -242,14 +300,11 @@ def paged_decode(cfg, order="interleaved"):
     ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(geom, B, R))
     L = dsa.load()
     p = Calls.p
-    args = (ctypes.byref(geom), B, p(q), p(iq), p(z), ctypes.byref(pages.struct), p(pools["ik"]), p(pools["k"]),
-            p(pools["v"]), p(slen), p(pools["summ"]), p(pools["scale"]), R, p(sel), p(nsel), p(out), p(ws), ws.numel())
-
-    def step(st):
-        rc = L.dsa_decode_step_paged(*args, st)
-        if rc:
-            raise RuntimeError(f"paged decode step failed: {rc} {L.dsa_last_error().decode()}")
-
+    step = rotate_queries(
+        lambda cq, ciq, cz: (ctypes.byref(geom), B, cq, ciq, cz, ctypes.byref(pages.struct), p(pools["ik"]),
+                             p(pools["k"]), p(pools["v"]), p(slen), p(pools["summ"]), p(pools["scale"]), R, p(sel),
+                             p(nsel), p(out), p(ws), ws.numel()),
+        q, iq, z, B, L.dsa_decode_step_paged, "paged decode step")
     return step, (pools, pages, q, iq, z, slen, sel, nsel, out, ws, geom)
 
 
@@ -329,14 +384,10 @@ def fp8_decode(cfg):
     ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(geom, B, R))
     L = dsa.load()
     p = Calls.p
-    args = (ctypes.byref(geom), B, p(q), p(iq), p(z), p(ik), p(k8), p(v8), p(kvs), tcap, p(slen), p(summ), p(scale),
-            R, p(sel), p(nsel), p(out), p(ws), ws.numel())
-
-    def step(st):
-        rc = L.dsa_decode_step_fp8(*args, st)
-        if rc:
-            raise RuntimeError(f"fp8 decode step failed: {rc} {L.dsa_last_error().decode()}")
-
+    step = rotate_queries(
+        lambda cq, ciq, cz: (ctypes.byref(geom), B, cq, ciq, cz, p(ik), p(k8), p(v8), p(kvs), tcap, p(slen),
+                             p(summ), p(scale), R, p(sel), p(nsel), p(out), p(ws), ws.numel()),
+        q, iq, z, B, L.dsa_decode_step_fp8, "fp8 decode step")
     return step, (ik, q, iq, z, summ, scale, slen, sel, nsel, out, k8, v8, kvs, ws, geom)
 
 
@@ -583,23 +634,29 @@ def timed(step, steps, warmup, kernels, graph=True):
     eager = time.perf_counter() - t0
     head = eager
     if graph:
+        # one graph per input variant of the step (rotating inputs), replayed in turn
+        nv = getattr(step, "variants", 1)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step(cur_stream())
+            for _ in range(nv):
+                step(cur_stream())
         torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(cur_stream())
-        for _ in range(2):
+        gs = []
+        for _ in range(nv):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(cur_stream())
+            gs.append(g)
+        for g in gs:
             g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
+        for i in range(steps):
+            gs[i % nv].replay()
         torch.cuda.synchronize()
         head = time.perf_counter() - t0
-        del g
+        del gs
     dsa.profile_enable(True)
     torch.cuda.synchronize()
     for _ in range(steps):
@@ -613,10 +670,29 @@ def timed(step, steps, warmup, kernels, graph=True):
     return head, eager, stats
 
 
+def host_cpu():
+    """The host CPU the oracle runs on: model name (as lscpu reports it, from /proc/cpuinfo) and the
+    number of processors this process may run on (nproc)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "nproc": nproc}
+
+
 def cpu_baseline_decode(cfg, budget_s=15.0):
-    """The oracle on the host cores: one decode query of sequence 0 of the 1M workload (compress the
-    completed region, score all 131,071 candidate regions x 4 groups, top-512, sparse GQA), repeated
-    until about budget_s of CPU time.  The prefix summaries are built untimed, as on the GPU."""
+    """The oracle on the host cores: one decode query of sequence 0 of the workload (compress the
+    completed region, score every candidate region x 4 groups, top-512, sparse GQA), repeated until
+    about budget_s of CPU time.  The prefix summaries are built untimed, as on the GPU."""
     import numpy as np
     import dsa_inputs as gi
     import oracle as O
@@ -644,7 +720,8 @@ def cpu_baseline_decode(cfg, budget_s=15.0):
             break
     return dict(value=n / el, unit="queries/s", cores=O.num_threads(), kind="oracle",
                 sample=f"{n} decode queries of one sequence at {Lc} tokens (compress 1 region, score {R - 1} "
-                       f"regions x 4 groups, top-{topk}, sparse GQA), fp64 C with OpenMP; prefix summaries untimed")
+                       f"regions x 4 groups, top-{topk}, sparse GQA), fp64 C with OpenMP; prefix summaries untimed",
+                **host_cpu())
 
 
 def cpu_baseline_prefill(cfg, n_queries=24):
@@ -673,7 +750,8 @@ def cpu_baseline_prefill(cfg, n_queries=24):
     el = time.perf_counter() - t1
     return dict(value=len(qs) / el, unit="tokens/s", cores=O.num_threads(), kind="oracle",
                 sample=f"{len(qs)} of the {n} chunk queries (evenly spaced) end to end, after compressing the "
-                       f"chunk's {R - P0 // REG} complete regions; fp64 C with OpenMP")
+                       f"chunk's {R - P0 // REG} complete regions; fp64 C with OpenMP",
+                **host_cpu())
 
 
 def main():
@@ -682,6 +760,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the 8K batch-1 and 128K batch-16 decode lines")
     ap.add_argument("--no-swa", action="store_true", help="skip the 3:1 layer mix and sliding-window prefill lines")
     ap.add_argument("--swa-only", action="store_true",
                     help="only the 3:1 layer mix and sliding-window prefill (for per-workload profiles)")
@@ -755,6 +834,8 @@ def main():
         return
 
     result = {} if args.swa_only else measure_decode(args)
+    if not args.swa_only and not args.no_shapes:
+        measure_decode_shapes(args, result)
     # ---- prefill at 64K
     if not args.no_prefill:
         measure_prefill(args, result)
@@ -777,45 +858,69 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measure_decode(args):
+def decode_workload(args, cfg, steps, warmup, traffic_key=None):
+    """Times one decode workload (rotating inputs, see setup_decode).  The roofline is the kernel that
+    moves the most algorithmic bytes: the score stream at long contexts, the K/V gather at short ones."""
     import torch
-    step, keep = setup_decode(DECODE)
-    DECODE["separate"] = args.separate
+    step, keep = setup_decode(cfg)
+    cfg["separate"] = args.separate
     kn = ["k_compress", "k_score_decode", "k_select", "k_sgqa_decode", "k_sgqa_merge"]
-    secs, eager, st = timed(step, args.steps, args.warmup, kn, graph=args.graph)
+    secs, eager, st = timed(step, steps, warmup, kn, graph=args.graph)
     st = {k: v for k, v in st.items() if v[1]}
     del keep
     torch.cuda.empty_cache()
-    B, Lc = DECODE["batch"], DECODE["context"]
-    ms_step = secs * 1e3 / args.steps
-    qps = B * args.steps / secs
-    byt = decode_bytes(B, Lc, DECODE["topk"])
-    score_ms = st["k_score_decode"][0]
+    B, Lc = cfg["batch"], cfg["context"]
+    ms_step = secs * 1e3 / steps
+    byt = decode_bytes(B, Lc, cfg["topk"])
     # (the fused step's compression runs inside the selection launch, not the scoring one)
-    score_bytes = byt["score"]
-    achieved = score_bytes / (score_ms * 1e-3) / 1e9
-    src = source_hash("score_topk.hip")
-    traffic = load_traffic("k_score_decode", "decode_b4_1m", src)
-    result = {
-        "metric": "DSA layer decode queries/s @1M ctx + prefill tok/s @64K, % HBM/MFMA roofline",
-        "value": round(qps, 2), "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "timing": "graph replay" if args.graph else "eager",
-        "eager_ms_per_step": round(eager * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": DECODE["name"], "batch": B, "context_tokens": Lc, "topk": DECODE["topk"],
-                   "regions_per_sequence": Lc // REG,
+    if byt["score"] >= byt["attend"]:
+        kern, kbytes, src = "k_score_decode", byt["score"], source_hash("score_topk.hip")
+    else:
+        kern, kbytes, src = "k_sgqa_decode", byt["attend"], source_hash("attention.hip")
+    kms = st[kern][0]
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    out = {
+        "value": round(B * steps / secs, 2), "unit": "queries/s", "steps": steps,
+        "ms_per_step": round(ms_step, 4), "eager_ms_per_step": round(eager * 1e3 / steps, 4),
+        "config": {"workload": cfg["name"], "batch": B, "context_tokens": Lc, "topk": cfg["topk"],
+                   "regions_per_sequence": Lc // REG, "input_copies": cfg.get("copies", 1),
+                   "query_sets": cfg.get("query_sets", QUERY_SETS),
                    "entry": "separate calls" if args.separate else "dsa_decode_step"},
-        "roofline": {"bound": "hbm", "kernel": "k_score_decode", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": score_bytes,
-                     "avg_launch_us": round(score_ms * 1e3, 2)},
+                     "traffic": load_traffic(kern, traffic_key, src) if traffic_key else None,
+                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": round(kms * 1e3, 2)},
         "step_hbm": {"algorithmic_bytes": byt["total"],
                      "achieved_GBs": round(byt["total"] / (ms_step * 1e-3) / 1e9, 1),
                      "frac": round(byt["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in st.items()},
     }
-    log(f"decode: {qps:.1f} q/s, {ms_step:.3f} ms/step, score kernel {achieved:.0f} GB/s")
+    log(f"decode {B} x {Lc}: {B * steps / secs:.1f} q/s, {ms_step:.4f} ms/step, {kern} {achieved:.0f} GB/s")
+    return out
+
+
+def measure_decode(args):
+    d = decode_workload(args, DECODE, args.steps, args.warmup, traffic_key="decode_b4_1m")
+    result = {
+        "metric": "DSA layer decode queries/s @1M ctx + prefill tok/s @64K, % HBM/MFMA roofline",
+        "value": d["value"], "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": d["ms_per_step"], "timing": "graph replay" if args.graph else "eager",
+        "eager_ms_per_step": d["eager_ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": d["config"], "roofline": d["roofline"], "step_hbm": d["step_hbm"], "kernels_us": d["kernels_us"],
+    }
     return result
+
+
+def measure_decode_shapes(args, result):
+    """The 8K single-query and 128K batch-16 decode workloads, as objects of their own."""
+    for key, cfg, tk in (("decode_8k", DECODE_8K, "decode_b1_8k"), ("decode_128k", DECODE_128K, "decode_b16_128k")):
+        steps = max(args.steps, cfg.get("copies", 1) * 2) if key == "decode_8k" else args.steps
+        d = decode_workload(args, cfg, steps, args.warmup, traffic_key=tk)
+        d["workload"] = d["config"].pop("workload")
+        if not args.no_cpu:
+            d["cpu_baseline"] = cpu_baseline_decode(cfg, budget_s=4.0)
+        result[key] = d
 
 
 def measure_prefill(args, result):

@@ -626,9 +626,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t pg = qi * kGroups + g;
   int32_t cnt = live ? a.nsel[pg] : 0;
   cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
-  // this range's entries of the list, in list order (any order and repeats
-  // are kept as they are; ids outside every range are dropped, as they are
-  // outside [0, p/8] and would be ignored anyway)
+  // this range's entries of the list, in list order (repeats are dropped
+  // below; ids outside every range are dropped here, as they are outside
+  // [0, p/8] and would be ignored anyway)
   const int32_t* lst = a.sel + (live ? pg : 0) * a.topk;
   const int32_t r0 = split * a.rsplit, r1 = r0 + a.rsplit;
   int32_t mine[kMaxTopk / 64];
@@ -658,6 +658,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
   if (!live) return;
+
+  // A list is a set: a repeated id counts once.  A strictly ascending run of
+  // entries (what dsa_score_topk writes) holds no repeats; otherwise every
+  // entry whose id occurs earlier in the run is dropped (rare, caller-made
+  // lists only).
+  {
+    bool unsorted = false;
+    for (int e = lane; e + 1 < n; e += 64) unsorted |= ids[wave][e] >= ids[wave][e + 1];
+    if (__any(unsorted)) {
+      int32_t kid[kMaxTopk / 64], ksl[kMaxTopk / 64];
+      bool keep[kMaxTopk / 64];
+#pragma unroll
+      for (int j = 0; j < kMaxTopk / 64; ++j) {
+        const int e = 64 * j + lane;
+        kid[j] = e < n ? ids[wave][e] : 0;
+        ksl[j] = e < n ? slots[wave][e] : 0;
+        bool first = e < n;
+        for (int e2 = 0; first && e2 < e; ++e2) first = ids[wave][e2] != kid[j];
+        keep[j] = first;
+      }
+      int32_t nk = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxTopk / 64; ++j) {
+        const uint64_t m = __ballot(keep[j]);
+        if (keep[j]) {
+          ids[wave][nk + __popcll(m & lt)] = kid[j];
+          slots[wave][nk + __popcll(m & lt)] = ksl[j];
+        }
+        nk += __popcll(m);
+      }
+      n = nk;
+    }
+  }
 
   bf16x8 qb[6];
   load_q(a.q, qi, g, qb);

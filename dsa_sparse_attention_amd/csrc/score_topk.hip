@@ -44,7 +44,7 @@ constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
 #endif
 constexpr int kHistCopies = DSA_HIST_COPIES;  // decode histogram stripes (by score block index)
 constexpr int kSelCap = 4096;      // LDS candidate capacity of the radix fallback
-constexpr int kCandCap = 1024;     // decode candidates at or above the level-0 digit
+constexpr int kCandCap = 2048;     // decode candidates at or above the level-0 digit
 constexpr int kDirectMax = 8192;   // longest problem selected straight from its scores
 
 struct ScoreArgs {
@@ -1193,15 +1193,20 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   const uint32_t ntl_all = sm.tab[kDecTilesPT * (kDecNT / 64)];
   const uint32_t ntl = min(ntl_all, (uint32_t)kCandCap);
   lds_barrier();
-  // One kept tile per thread (ntl <= kCandCap == kDecNT): its 16 scores in
+  // The kept tiles in rounds of one tile per thread (round rd: kept tiles
+  // rd*kDecNT + tid, so the rounds follow index order): a tile's 16 scores in
   // one 64-byte row, the candidates among them (and those inside digit d)
   // counted, a block scan of the counts in thread order (= index order), and
-  // the candidates written to LDS in index order.
-  static_assert(kCandCap == kDecNT, "one kept tile per thread");
-  uint32_t ncand, nin;
-  {
-    const bool have = (uint32_t)tid < ntl;
-    const int64_t t = have ? sm.tiles[tid] : 0;
+  // the candidates written to LDS in index order after those of earlier
+  // rounds.
+  constexpr int kCandRounds = kCandCap / kDecNT;
+  static_assert(kCandCap == kCandRounds * kDecNT, "whole rounds of one kept tile per thread");
+  uint32_t ncand = 0, nin = 0;
+  for (int rd = 0; rd < kCandRounds; ++rd) {
+    if ((uint32_t)rd * kDecNT >= ntl) break;  // (uniform: ntl is the same for every thread)
+    const uint32_t ti = (uint32_t)rd * kDecNT + tid;
+    const bool have = ti < ntl;
+    const int64_t t = have ? sm.tiles[ti] : 0;
     const u32x4* tp = (const u32x4*)(a.scores + pq * a.ws_stride + t * kTile);
     u32x4 q4[4];
 #pragma unroll
@@ -1222,7 +1227,7 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
       fa |= (ok ? 1u : 0u) << i;
       fb |= (ok && (key[i] >> 20) == d ? 1u : 0u) << i;
     }
-    // both counts in one word: each total is at most 16 * kDecNT < 2^16
+    // both counts in one word: each round's total is at most 16 * kDecNT < 2^16
     const uint32_t packed = ((uint32_t)__popc(fa) << 16) | (uint32_t)__popc(fb);
     const uint32_t incl = wave_incl_scan(packed);
     if (lane == 63) sm.wtot[w] = incl;
@@ -1235,11 +1240,9 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
               (4 * i + 3 < w ? v.w : 0u);
       total += v.x + v.y + v.z + v.w;
     }
-    ncand = total >> 16;
-    nin = total & 0xFFFFu;
     // the thread's keys go through its own LDS column so that the loop over
     // its candidates (about one) can index them
-    uint32_t oa = base >> 16, ob = base & 0xFFFFu;
+    uint32_t oa = ncand + (base >> 16), ob = nin + (base & 0xFFFFu);
     for (uint32_t m = fa; m; m &= m - 1u, ++oa) {
       const int i = __ffs((int)m) - 1;
       const uint32_t k = sm.stage[i][tid];
@@ -1252,6 +1255,9 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
         ++ob;
       }
     }
+    ncand += total >> 16;
+    nin += total & 0xFFFFu;
+    lds_barrier();  // (the next round rewrites sm.wtot)
   }
   // exact check of the digit: ncand keys are >= Tlo and nin of them in digit d
   const uint32_t above = ncand - nin;
@@ -1260,7 +1266,7 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     select_fallback<kDecNT>(a, pq);
     return;
   }
-  lds_barrier();
+  // (the last round's barrier made the candidates visible)
   // 3. wave 0: the need-th largest key T lies in digit d; its next 10 bits,
   // then its last 10, from histograms of the in-digit keys
   const uint32_t M = min(ncand, (uint32_t)kCandCap);
@@ -1276,17 +1282,27 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   }
   __syncthreads();
   const uint32_t T = sm.res[0], need_eq = sm.res[1];
-  // 4. every thread places one candidate: taken entries before it are the
-  // keys above T before it plus min(keys equal to T before it, need_eq)
-  static_assert(kCandCap <= kDecNT, "one candidate per thread");
-  const uint32_t k = tid < M ? sm.ck[tid] : 0u;
-  const bool fg[1] = {tid < M && k > T}, fe[1] = {tid < M && k == T};
-  uint32_t pg[1], pe[1], ng, ne;
-  ordered_positions2<kDecNT, 1>(fg, fe, pg, pe, sm.tab, &ng, &ne);
-  uint32_t pos = need;
-  if (fg[0]) pos = pg[0] + (pe[0] < need_eq ? pe[0] : need_eq);
-  else if (fe[0] && pe[0] < need_eq) pos = pg[0] + pe[0];
-  if (pos < need) sel[pos] = sm.ci[tid];
+  // 4. every thread places candidates tid and tid + kDecNT: taken entries
+  // before one are the keys above T before it plus min(keys equal to T before
+  // it, need_eq)
+  static_assert(kCandCap == 2 * kDecNT, "two candidates per thread");
+  bool fg[2], fe[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t j = (uint32_t)e * kDecNT + tid;
+    const uint32_t k = j < M ? sm.ck[j] : 0u;
+    fg[e] = j < M && k > T;
+    fe[e] = j < M && k == T;
+  }
+  uint32_t pg[2], pe[2], ng, ne;
+  ordered_positions2<kDecNT, 2>(fg, fe, pg, pe, sm.tab, &ng, &ne);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    uint32_t pos = need;
+    if (fg[e]) pos = pg[e] + (pe[e] < need_eq ? pe[e] : need_eq);
+    else if (fe[e] && pe[e] < need_eq) pos = pg[e] + pe[e];
+    if (pos < need) sel[pos] = sm.ci[(uint32_t)e * kDecNT + tid];
+  }
   // the forced current region, the padding and the count (after the last
   // barrier, like the hint's clearing)
   for (int i = (int)need + 1 + tid; i < a.topk; i += kDecNT) sel[i] = -1;
@@ -1793,3 +1809,4 @@ extern "C" dsa_status dsa_decode_step_fp8_paged(const dsa_geometry* geom, int32_
   return decode_step("dsa_decode_step_fp8_paged", geom, batch, q, index_q, z, ik_pool, nullptr, nullptr, cm, seq_len,
                      summ_pool, scale_pool, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
 }
+

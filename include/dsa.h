@@ -389,8 +389,8 @@ size_t dsa_sparse_gqa_prefill_workspace_size(const dsa_geometry* geom, int32_t n
  * sparse_attention_prefill).  Same maths as decode, per query i of sequence
  * q_seq[i] at position q_pos[i] (the current region may be partial; tokens
  * after p are masked).  The chunk's own K/V must already be in the caches.
- * The list entries need not be sorted; each entry counts once (repeats
- * count again), and ids outside [0, p/8] are ignored.
+ * The list entries need not be sorted; a list is a set (a repeated id counts
+ * once), and ids outside [0, p/8] are ignored.
  *   q, out [n_queries][64][D] bf16;  caches of n_seqs sequences, capacity tcap
  *   workspace >= dsa_sparse_gqa_prefill_workspace_size() bytes, 256-byte
  *             aligned: per-(query, group) partial results over 8 ranges of

@@ -84,10 +84,14 @@ def host_queries(seed, nq, q_start=0):
     return q, iq, z
 
 
-def dev_queries(seed, nq):
-    q = dev_flat_bf16(seed, gi.TID_Q, nq * HQ * D)
-    iq = dev_flat_bf16(seed, gi.TID_IQ, nq * HI * P, gi.IK_SCALE)
-    z = dev_flat_uniform(seed, gi.TID_Z, nq * HI)
+def dev_queries(seed, nq, q_start=0):
+    """q, index_q, z of query indices q_start .. q_start+nq-1 (device generator)."""
+    q = torch.empty(nq * HQ * D, dtype=BF16, device="cuda")
+    gi.dev_flat(q.data_ptr(), stream_ptr(), seed, gi.TID_Q, nq * HQ * D, 0, 1.0, start=q_start * HQ * D)
+    iq = torch.empty(nq * HI * P, dtype=BF16, device="cuda")
+    gi.dev_flat(iq.data_ptr(), stream_ptr(), seed, gi.TID_IQ, nq * HI * P, 0, gi.IK_SCALE, start=q_start * HI * P)
+    z = torch.empty(nq * HI, dtype=torch.float32, device="cuda")
+    gi.dev_flat(z.data_ptr(), stream_ptr(), seed, gi.TID_Z, nq * HI, 1, start=q_start * HI)
     return q, iq, z
 
 
@@ -135,9 +139,10 @@ def check_selection(gsel, or_sel, or_scores_g, c):
 # ------------------------------------------------------------------------------------------------
 # DSA decode end to end
 # ------------------------------------------------------------------------------------------------
-def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=None, zero_z=False):
+def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=None, zero_z=False, q_start=0):
     """Runs compress -> score_topk -> sparse GQA decode on the GPU for len(lens) sequences (query b at
-    position lens[b]-1), and the oracle for the sequences in check_seqs (default all)."""
+    position lens[b]-1, generated as query index q_start + b), and the oracle for the sequences in
+    check_seqs (default all)."""
     B = len(lens)
     tcap = tcap or round128(max(lens))
     R = tcap // 8
@@ -145,7 +150,7 @@ def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=No
     ik = dev_cache(seed, gi.TID_IK, B, tcap, P, tcap, gi.LAYOUT_GROUP_MAJOR, gi.IK_SCALE, planted)
     K = dev_cache(seed, gi.TID_K, B, tcap, D, tcap, gi.LAYOUT_KTILED)
     V = dev_cache(seed, gi.TID_V, B, tcap, D, tcap, gi.LAYOUT_REGION_T)
-    q, iq, z = dev_queries(seed, B)
+    q, iq, z = dev_queries(seed, B, q_start)
     if zero_z:  # every score 0: selection falls to the lowest regions (tie rule)
         z.zero_()
     summ = torch.zeros(B * G * R * P, dtype=torch.uint8, device="cuda")
@@ -165,7 +170,7 @@ def run_dsa_decode(seed, lens, topk=512, tcap=None, planted=False, check_seqs=No
                sel=sel.cpu().numpy().reshape(B, G, topk), nsel=nsel.cpu().numpy().reshape(B, G),
                scores=scores.cpu().numpy().reshape(B, G, R), out=bf16_np(out).reshape(B, HQ, D),
                oracle={}, dev=dict(K=K, V=V, q=q, geom=geom, ik=ik, iq=iq, z=z, summ=summ, scale=scale))
-    hq, hiq, hz = host_queries(seed, B)
+    hq, hiq, hz = host_queries(seed, B, q_start)
     if zero_z:
         hz = np.zeros_like(hz)
     for b in (range(B) if check_seqs is None else check_seqs):

@@ -127,9 +127,10 @@ def test_merged_prefill_mixed_sequences_and_ragged():
     _oracle_check(seed, c, out, 1, what="merged mixed")
 
 
-def test_merged_prefill_lists_are_sets():
-    """Unsorted lists with repeats, ids past the query's region and negative ids: the merged call
-    attends each valid region once."""
+@pytest.mark.parametrize("merged", [True, False])
+def test_prefill_lists_are_sets(merged):
+    """Unsorted lists with repeats, ids past the query's region and negative ids: both prefill calls
+    (neighbour-merged and per-query) attend each valid region once."""
     seed = 0xA30
     c = _chunk(seed, [(2000, 40)], correlated=True, topk=64)
     nq, k = c["nq"], 64
@@ -147,8 +148,9 @@ def test_merged_prefill_lists_are_sets():
             nsel[i, g] = len(lst)
             valid[(i, g)] = sorted(set(x for x in lst if 0 <= x <= cur))
     c["sel"], c["nsel"] = H.i32(sel.ravel()), H.i32(nsel.ravel())
-    out = _run(c, True)
-    _oracle_check(seed, c, out, 1, lists_of=lambda i: [valid[(i, g)] for g in range(G)], what="merged sets")
+    out = _run(c, merged)
+    _oracle_check(seed, c, out, 1, lists_of=lambda i: [valid[(i, g)] for g in range(G)],
+                  what="merged sets" if merged else "per-query sets")
 
 
 def test_merged_prefill_paged_matches_contiguous():

@@ -93,6 +93,16 @@ def test_decode_128k_context_batch_of_16():
     H.assert_decode_parity(r)
 
 
+def test_decode_crowded_boundary_digit():
+    """A selection whose boundary bin of the 12-bit score key is crowded: more than 1,024 regions score
+    at or above the bin of the 511th best (1,057 for sequence 1, group 2 of this input: the 1M
+    batch-4 workload, planted bias, with queries 20..23).  The selection still takes its fast path
+    (up to 2,048 candidates) and matches the oracle."""
+    seed = gi.SEED_BASE + 3
+    r = H.run_dsa_decode(seed, [1 << 20] * 4, topk=512, planted=True, check_seqs=[1], q_start=20)
+    H.assert_decode_parity(r)
+
+
 def test_decode_layer_mix_shape_batch_8_at_256k():
     """The DSA layer of the 3:1 layer-mix workload as the benchmark times it: batch 8 at 262,144
     tokens (2,048 tiles per problem); sequences 0 and 7 are checked against the oracle."""
