@@ -36,6 +36,7 @@ ENTRY_POINTS = [
     "dsa_cache_write_fp8_paged", "dsa_sparse_gqa_decode_fp8_paged", "dsa_sparse_gqa_prefill_fp8_paged",
     "dsa_decode_step_fp8_paged", "dsa_sparse_gqa_prefill_merged", "dsa_sparse_gqa_prefill_merged_paged",
     "dsa_rope_config_default", "dsa_indexer_workspace_size", "dsa_indexer_project", "dsa_rope_qk",
+    "dsa_decode_step_noalloc",
 ]
 
 
@@ -123,6 +124,7 @@ def load() -> ctypes.CDLL:
     L.dsa_decode_step_workspace_size.argtypes = [G, i32, i32]
     L.dsa_decode_step_workspace_size.restype = sz
     L.dsa_decode_step.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.dsa_decode_step_noalloc.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp]
     L.swa_attention_workspace_size.argtypes = [G, i32, i32, i32]
     L.swa_attention_workspace_size.restype = sz
     L.swa_attention.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -303,8 +305,8 @@ def dsa_decode_step_workspace_size(geom, batch, max_regions) -> int:
     return int(load().dsa_decode_step_workspace_size(ctypes.byref(geom), batch, max_regions))
 
 
-def dsa_decode_step(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_len, summ, scale, max_regions, sel,
-                    n_sel, out, workspace=None, stream=None):
+def _decode_step_checks(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_len, summ, scale, sel, n_sel,
+                        out):
     batch = seq_len.numel()
     for t, nm in ((q, "q"), (index_q, "index_q"), (index_k, "index_k"), (k_cache, "k_cache"),
                   (v_cache, "v_cache"), (out, "out")):
@@ -326,12 +328,29 @@ def dsa_decode_step(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_le
     _numel_at_least(scale, batch * GROUPS * R, "scale")
     _numel_at_least(sel, batch * GROUPS * geom.topk, "sel")
     _numel_at_least(n_sel, batch * GROUPS, "n_sel")
+    return batch
+
+
+def dsa_decode_step(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_len, summ, scale, max_regions, sel,
+                    n_sel, out, workspace=None, stream=None):
+    batch = _decode_step_checks(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_len, summ, scale, sel,
+                                n_sel, out)
     if workspace is None:
         workspace = globals()["workspace"](dsa_decode_step_workspace_size(geom, batch, max_regions), q.device)
     _check(load().dsa_decode_step(ctypes.byref(geom), batch, _ptr(q), _ptr(index_q), _ptr(z), _ptr(index_k),
                                   _ptr(k_cache), _ptr(v_cache), tcap, _ptr(seq_len), _ptr(summ), _ptr(scale),
                                   max_regions, _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(workspace),
                                   workspace.numel(), _stream(stream)))
+
+
+def dsa_decode_step_noalloc(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_len, summ, scale, max_regions,
+                            sel, n_sel, out, stream=None):
+    """dsa_decode_step with the library's static scratch area as its workspace (nothing allocated)."""
+    batch = _decode_step_checks(geom, q, index_q, z, index_k, k_cache, v_cache, tcap, seq_len, summ, scale, sel,
+                                n_sel, out)
+    _check(load().dsa_decode_step_noalloc(ctypes.byref(geom), batch, _ptr(q), _ptr(index_q), _ptr(z), _ptr(index_k),
+                                          _ptr(k_cache), _ptr(v_cache), tcap, _ptr(seq_len), _ptr(summ), _ptr(scale),
+                                          max_regions, _ptr(sel), _ptr(n_sel), _ptr(out), _stream(stream)))
 
 
 def dsa_sparse_gqa_prefill_workspace_size(geom, n_queries) -> int:

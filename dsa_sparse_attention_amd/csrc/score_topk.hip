@@ -26,6 +26,8 @@
 //    maxima of need tiles that all rank above it), so at most 511 tiles of 16
 //    regions are then ranked exactly.  A radix fallback in global memory
 //    covers problems beyond the register capacity.
+#include <mutex>
+
 #include "compress_dev.hpp"
 
 namespace dsa {
@@ -1810,3 +1812,84 @@ extern "C" dsa_status dsa_decode_step_fp8_paged(const dsa_geometry* geom, int32_
                      summ_pool, scale_pool, max_regions, sel, n_sel, out, workspace, workspace_bytes, stream, &f8);
 }
 
+// ---------------------------------------------------------------------------
+// dsa_decode_step without a caller workspace, for callers that cannot
+// allocate device memory (code under stream capture, serving loops that
+// forbid it).  The workspace is a static device array of fixed size: each
+// GPU the library runs on holds its own copy at its own address, found once
+// per device with hipGetSymbolAddress and kept; the array's name is never
+// used as a device address on the host.  The decode step's workspace holds no
+// state that must start at zero: the digit histogram in it is only a hint
+// (checked against exact counts, cleared by every call), and every partial
+// result is written before it is read.  Calls that overlap on one GPU share
+// the array and race.
+// ---------------------------------------------------------------------------
+namespace dsa {
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on the device that runs `stream` (which must be
+// the current device); nullptr with the message in *err on failure.
+static void* static_scratch(hipStream_t stream, std::string* err) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) {
+    *err = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return nullptr;
+  }
+  hipDevice_t sdev = cur;
+  e = hipStreamGetDevice(stream, &sdev);
+  if (e != hipSuccess) {
+    *err = std::string("hipStreamGetDevice: ") + hipGetErrorString(e);
+    return nullptr;
+  }
+  if ((int)sdev != cur) {
+    *err = "the stream belongs to another device than the current one";
+    return nullptr;
+  }
+  if (cur < 0 || cur >= kMaxScratchDevices) {
+    *err = "device index beyond the supported range";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[cur]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = std::string("hipGetSymbolAddress: ") + hipGetErrorString(e);
+      return nullptr;
+    }
+    g_scratch_ptr[cur] = p;
+  }
+  return g_scratch_ptr[cur];
+}
+}  // namespace dsa
+
+extern "C" dsa_status dsa_decode_step_noalloc(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                              const uint16_t* index_q, const float* z, const uint16_t* index_k,
+                                              const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                                              const int32_t* seq_len, uint8_t* summ, float* scale,
+                                              int32_t max_regions, int32_t* sel, int32_t* n_sel, uint16_t* out,
+                                              void* stream) {
+  dsa_status st = check_geometry(geom);
+  if (st != DSA_OK) return st;
+  if (tcap <= 0 || tcap % kTcapAlign)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step_noalloc: tcap must be a positive multiple of 128");
+  if (batch < 0 || max_regions < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "dsa_decode_step_noalloc: bad sizes");
+  if (batch == 0) return DSA_OK;
+  const size_t need = dsa_decode_step_workspace_size(geom, batch, max_regions);
+  if (need > kStaticScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_decode_step_noalloc: batch and max_regions need " + std::to_string(need) +
+                                         " bytes of scratch; the static area holds " +
+                                         std::to_string(kStaticScratchBytes) + " (use dsa_decode_step)");
+  std::string err;
+  void* ws = static_scratch(as_stream(stream), &err);
+  if (!ws) return fail(DSA_ERR_HIP, "dsa_decode_step_noalloc: " + err);
+  return decode_step("dsa_decode_step_noalloc", geom, batch, q, index_q, z, index_k, k_cache, v_cache,
+                     contiguous_map(tcap), seq_len, summ, scale, max_regions, sel, n_sel, out, ws,
+                     kStaticScratchBytes, stream);
+}

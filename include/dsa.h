@@ -351,6 +351,26 @@ dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16
                            int32_t* sel, int32_t* n_sel, uint16_t* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * dsa_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph / stream capture, serving loops or harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, and results
+ * bit-identical to dsa_decode_step.  Its workspace is a static 64 MiB device
+ * area of the library; each GPU holds its own copy until the process ends.
+ * Shapes whose dsa_decode_step_workspace_size() exceeds 64 MiB (e.g. batch 4
+ * at 1M tokens needs 15.6 MiB, batch 16 at 128K 32.8 MiB) return
+ * DSA_ERR_UNSUPPORTED.  `stream` must belong to the current device; the
+ * first call on a device resolves the area's address there (make it outside
+ * stream capture).  The call allocates and frees nothing.  Every call on one
+ * GPU shares that GPU's area, so calls that overlap on one GPU race: issue
+ * them on one stream or order them.
+ */
+dsa_status dsa_decode_step_noalloc(const dsa_geometry* geom, int32_t batch, const uint16_t* q,
+                                   const uint16_t* index_q, const float* z, const uint16_t* index_k,
+                                   const uint16_t* k_cache, const uint16_t* v_cache, int64_t tcap,
+                                   const int32_t* seq_len, uint8_t* summ, float* scale, int32_t max_regions,
+                                   int32_t* sel, int32_t* n_sel, uint16_t* out, void* stream);
+
 /* dsa_decode_step over paged pools (sequence b = block-table row b): the
  * folded compression reads ik_pool and writes summ_pool/scale_pool; scoring
  * and attention read the pools.  Bit-identical to the contiguous call on the
