@@ -108,6 +108,21 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
+def load_profile_json(kernel, workload_key, tag, src_hash):
+    """A 'tag: {...}' line of profiles/<kernel>__<workload>.md (rocprofv3 counter figures), or None if absent or
+    taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload_key}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path, encoding="utf-8"):
+        if line.startswith(tag + ":"):
+            d = json.loads(line.split(":", 1)[1])
+            if d.get("source_hash") != src_hash:
+                return None
+            return {k: v for k, v in d.items() if k != "source_hash"}
+    return None
+
+
 def load_traffic(kernel, workload_key, src_hash):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/<kernel>__<workload>.md holds
     a line 'traffic_json: {...}'); None if absent or taken on a different kernel source."""
@@ -889,7 +904,9 @@ def decode_workload(args, cfg, steps, warmup, traffic_key=None):
         "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(kern, traffic_key, src) if traffic_key else None,
-                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": round(kms * 1e3, 2)},
+                     "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": round(kms * 1e3, 2),
+                     "counters": (load_profile_json(kern, traffic_key, "mem_json", src)
+                                  or load_profile_json(kern, traffic_key, "mfma_json", src)) if traffic_key else None},
         "step_hbm": {"algorithmic_bytes": byt["total"],
                      "achieved_GBs": round(byt["total"] / (ms_step * 1e-3) / 1e9, 1),
                      "frac": round(byt["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -944,7 +961,9 @@ def measure_prefill(args, result):
         "roofline": {"bound": "mfma", "kernel": "k_sgqa_prefill", "achieved": round(att_tf, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": load_traffic("k_sgqa_prefill", "prefill_64k", source_hash("attention.hip")),
-                     "algorithmic_flops_per_launch": fl["attend"], "avg_launch_us": round(att_ms * 1e3, 1)},
+                     "algorithmic_flops_per_launch": fl["attend"], "avg_launch_us": round(att_ms * 1e3, 1),
+                     "counters": load_profile_json("k_sgqa_prefill", "prefill_64k", "mfma_json",
+                                                   source_hash("attention.hip"))},
         "attention_with_merge": {
             "kernels": ["k_sgqa_prefill", "k_sgqa_merge"],
             "achieved_TFLOPs": round(fl["attend"] / ((att_ms + mg_ms) * 1e-3) / 1e12, 2),
@@ -953,7 +972,9 @@ def measure_prefill(args, result):
             "gather_GBs": round(fl["gather"] / (att_ms * 1e-3) / 1e9, 1)},
         "score_kernel": {"kernel": "k_score_prefill", "achieved_TFLOPs": round(sc_tf, 2),
                          "frac": round(sc_tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl["score"],
-                         "avg_launch_us": round(sc_ms * 1e3, 1)},
+                         "avg_launch_us": round(sc_ms * 1e3, 1),
+                         "counters": load_profile_json("k_score_prefill", "prefill_64k", "mfma_json",
+                                                       source_hash("score_topk.hip"))},
         "step_mfma": {"algorithmic_flops": fl["total"], "achieved_TFLOPs": round(step_tf, 2),
                       "frac": round(step_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in pst.items()},
@@ -1112,7 +1133,9 @@ def measure_swa(args, result):
         "roofline": {"bound": "mfma", "kernel": "k_swa_attend",
                      "achieved": round(fl / (att_ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fl / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "algorithmic_flops_per_launch": fl, "avg_launch_us": round(att_ms * 1e3, 1)},
+                     "algorithmic_flops_per_launch": fl, "avg_launch_us": round(att_ms * 1e3, 1),
+                     "counters": load_profile_json("k_swa_band", "swa_prefill_2048", "mfma_json",
+                                                   source_hash("attention.hip"))},
         "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in sst.items()},
     }
     log(f"swa prefill: {n * ssteps / ssecs:.0f} tok/s, {sms:.3f} ms/step")
