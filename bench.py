@@ -581,7 +581,8 @@ def setup_swa(seed, layer, n_seqs, p0, n_new, geom):
     gp = ctypes.byref(geom)
     a_att = (gp, W, n_seqs, n_new, p(pos0), p(row0), p(q), p(kn), p(vn), p(kr), p(vr), p(out), p(ws), ws.numel())
     a_app = (gp, W, n_seqs, n_new, p(pos0), p(row0), p(kn), p(vn), p(kr), p(vr))
-    return a_att, a_app, (kr, vr, kn, vn, q, out, pos0, row0, ws)
+    a_dec = (gp, W, n_seqs, p(pos0), p(q), p(kn), p(vn), p(kr), p(vr), p(out)) if n_new == 1 else None
+    return a_att, a_app, a_dec, (kr, vr, kn, vn, q, out, pos0, row0, ws)
 
 
 def setup_mix(cfg):
@@ -600,8 +601,9 @@ def setup_mix(cfg):
     layers = [setup_swa(seed, l, B, Lc - 1, 1, geom) for l in range(cfg["swa_layers"])]
 
     def step(st):
-        for a_att, a_app, _ in layers:
-            rc = L.swa_attention(*a_att, st) or L.swa_ring_append(*a_app, st)
+        # each sliding-window layer: attention over its window and the ring append, one launch
+        for _, _, a_dec, _ in layers:
+            rc = L.swa_decode_step(*a_dec, st)
             if rc:
                 raise RuntimeError(f"sliding-window layer failed: {rc} {L.dsa_last_error().decode()}")
         dsa_step(st)
@@ -615,7 +617,7 @@ def setup_swa_prefill(cfg):
 
     seed = gi.SEED_BASE + cfg["seed_index"]
     geom = dsa.geometry()
-    a_att, a_app, tens = setup_swa(seed, 0, 1, cfg["prefix"], cfg["chunk"], geom)
+    a_att, a_app, _, tens = setup_swa(seed, 0, 1, cfg["prefix"], cfg["chunk"], geom)
     L = dsa.load()
 
     def step(st):

@@ -807,6 +807,11 @@ struct SwaArgs {
 __device__ __forceinline__ void seq_rows(const SwaArgs& a, int s, int64_t& p0, int64_t& r0, int64_t& nnew) {
   p0 = a.pos0[s];
   p0 = p0 < 0 ? 0 : p0;
+  if (!a.row0) {  // one new token per sequence, in row s
+    r0 = s;
+    nnew = 1;
+    return;
+  }
   r0 = a.row0[s];
   int64_t r1 = a.row0[s + 1];
   r0 = r0 < 0 ? 0 : (r0 > a.rows ? a.rows : r0);
@@ -873,11 +878,12 @@ __global__ __launch_bounds__(256) void k_swa_stage(SwaArgs a) {
   }
 }
 
-// block = (new token i of sequence s, group g); the window's regions go to
-// the 4 waves in chunks of 4 (wave w: chunks w, w+4, ...), whose partial
-// (max, sum, O) merge through LDS.  DEPTH as for core_run: 2 for few blocks
-// (decode: latency), 0 with two blocks per CU for many (chunked prefill).
-template <int DEPTH, bool DIRECT>
+// Short chunks (fewer than two band tiles per sequence): block = (new token
+// i of sequence s, group g); the window's regions go to the 4 waves in chunks
+// of 4 (wave w: chunks w, w+4, ...), whose partial (max, sum, O) merge through
+// LDS.  The chunk's own positions come from the staged regions.  DEPTH as for
+// core_run: 2 for few blocks (latency), 0 with two blocks per CU for many.
+template <int DEPTH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DEPTH == 0 ? 2 : 1, DEPTH == 0 ? 2 : 1)))
 void k_swa_attend(SwaArgs a) {
   const int64_t i = blockIdx.x;
@@ -898,8 +904,6 @@ void k_swa_attend(SwaArgs a) {
   const uint16_t* rv = a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion;
   const uint16_t* sk = a.st_k + sg * a.nst * kRegion * kHeadDim;
   const uint16_t* sv = a.st_v + sg * a.nst * kHeadDim * kRegion;
-  const uint16_t* knew = a.k_new + (row * kGroups + g) * kHeadDim;
-  const uint16_t* vnew = a.v_new + (row * kGroups + g) * kHeadDim;
 
   bf16x8 qb[6];
   load_q(a.q, row, g, qb);
@@ -916,9 +920,7 @@ void k_swa_attend(SwaArgs a) {
       return rg;
     }
     const int64_t r = rlo + er;
-    if (r < rst || DIRECT) {
-      // DIRECT (one new token per sequence): the current region is the ring's,
-      // with the new token patched in from k_new / v_new at load time
+    if (r < rst) {
       const int64_t pk = r % (W / kRegion);
       rg.k = rk + pk * kRegion * kHeadDim;
       rg.v = rv + pk * kHeadDim * kRegion;
@@ -926,15 +928,13 @@ void k_swa_attend(SwaArgs a) {
       rg.k = sk + (r - rst) * kRegion * kHeadDim;
       rg.v = sv + (r - rst) * kHeadDim * kRegion;
     }
-    rg.kn = knew;
-    rg.vn = vnew;
-    rg.tn = (DIRECT && r == p / kRegion) ? (int)(p % kRegion) : -1;
+    rg.tn = -1;
     const int64_t first = r * kRegion;
     rg.lo = (int)((lo > first ? lo : first) - first);
     rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
     return rg;
   };
-  core_run<DEPTH, DIRECT>(st, qb, mine, region_of, a.scale_log2);
+  core_run<DEPTH>(st, qb, mine, region_of, a.scale_log2);
   // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i), then the merged,
   // normalised output
   const float lt = core_total_l(st);
@@ -959,6 +959,103 @@ void k_swa_attend(SwaArgs a) {
       }
     }
     op[h * kHeadDim + d] = f32_to_bf16(lsum > 0.0f ? acc / lsum : 0.0f);
+  }
+}
+
+// Sliding-window decode, one new token per sequence: block = (sequence s,
+// group g) with kSwdWaves waves; the window's <= 65 regions go to the waves
+// in chunks of 4 (wave w: chunks w, w + kSwdWaves, ...), so all of a window's
+// loads are issued at once instead of chunk after chunk, and the waves'
+// partials merge through LDS.  The current region is the ring's with the new
+// token patched in at load time.  APPEND: the block then writes the new
+// token's K/V into ring slot p mod W; that slot held position p - W, outside
+// this window, and no other block reads this (sequence, group)'s ring.
+constexpr int kSwdWaves = 8;
+
+template <bool APPEND>
+__global__ __launch_bounds__(64 * kSwdWaves) void k_swa_decode(SwaArgs a, uint16_t* k_ring_w, uint16_t* v_ring_w) {
+  const int s = blockIdx.y, g = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  __shared__ float sm_m[kSwdWaves][16], sm_l[kSwdWaves][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[kSwdWaves][16][kORow];
+  int64_t p0, r0, nnew;
+  seq_rows(a, s, p0, r0, nnew);
+  if (nnew <= 0) return;
+  const int64_t p = p0, row = r0;  // the sequence's one new token
+  const int W = a.window;
+  const int64_t lo = p - W + 1 < 0 ? 0 : p - W + 1;
+  const int64_t rlo = lo / kRegion, rhi = p / kRegion;
+  const int64_t sg = (int64_t)s * kGroups + g;
+  const uint16_t* rk = a.k_ring + sg * W * kHeadDim;
+  const uint16_t* rv = a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion;
+  const uint16_t* knew = a.k_new + (row * kGroups + g) * kHeadDim;
+  const uint16_t* vnew = a.v_new + (row * kGroups + g) * kHeadDim;
+  bf16x8 qb[6];
+  load_q(a.q, row, g, qb);
+  CoreState st;
+  core_init(st);
+  const int64_t nreg = rhi - rlo + 1;
+  const int64_t nch = (nreg + 3) / 4;
+  const int64_t mine = wave < nch ? 4 * ((nch - wave + kSwdWaves - 1) / kSwdWaves) : 0;  // this wave's entries
+  auto region_of = [&](int64_t e) -> Region {
+    const int64_t er = 4 * (wave + kSwdWaves * (e >> 2)) + (e & 3);  // window region index of entry e
+    Region rg;
+    if (e >= mine || er >= nreg) {
+      rg.k = rk; rg.v = rv; rg.lo = 1; rg.hi = 0;
+      rg.kn = knew; rg.vn = vnew; rg.tn = -1;
+      return rg;
+    }
+    const int64_t r = rlo + er;
+    const int64_t pk = r % (W / kRegion);
+    rg.k = rk + pk * kRegion * kHeadDim;
+    rg.v = rv + pk * kHeadDim * kRegion;
+    rg.kn = knew;
+    rg.vn = vnew;
+    rg.tn = r == p / kRegion ? (int)(p % kRegion) : -1;
+    const int64_t first = r * kRegion;
+    rg.lo = (int)((lo > first ? lo : first) - first);
+    rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
+    return rg;
+  };
+  core_run<0, true>(st, qb, mine, region_of, a.scale_log2);
+  const float lt = core_total_l(st);
+  if (kb == 0) {
+    sm_m[wave][n] = st.m;
+    sm_l[wave][n] = lt;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) *(f32x4*)&sm_o[wave][n][16 * nt + 4 * kb] = st.o[nt];
+  __syncthreads();
+  uint16_t* op = a.out + (row * kQHeads + kHeadsPerGroup * g) * kHeadDim;
+  for (int e = threadIdx.x; e < 16 * kHeadDim; e += 64 * kSwdWaves) {
+    const int h = e / kHeadDim, d = e - h * kHeadDim;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kSwdWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float acc = 0.0f, lsum = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kSwdWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
+        acc += f * sm_o[w][h][d];
+        lsum += f * sm_l[w][h];
+      }
+    }
+    op[h * kHeadDim + d] = f32_to_bf16(lsum > 0.0f ? acc / lsum : 0.0f);
+  }
+  if constexpr (APPEND) {
+    // (every load of the block completed before the barrier above)
+    const int64_t slot = p % W;
+    const int t = threadIdx.x;
+    if (t < kHeadDim / 8) {  // K: 24 units of 8 channels
+      const int d0 = 8 * t;
+      const u32x4 v = ld16(knew + d0);
+      *(u32x4*)(k_ring_w + (sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, d0)) = v;
+    } else if (t >= 64 && t < 64 + kHeadDim) {  // V: 192 channels
+      const int d = t - 64;
+      v_ring_w[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion] = vnew[d];
+    }
   }
 }
 
@@ -1718,7 +1815,8 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   hipStream_t s = as_stream(stream);
   if (max_new_per_seq == 1) {  // decode: the attention kernel patches the new token in itself
     ProfScope prof_("k_swa_attend", s);
-    hipLaunchKernelGGL((k_swa_attend<2, true>), dim3(1, n_seqs, kGroups), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_swa_decode<false>), dim3(1, n_seqs, kGroups), dim3(64 * kSwdWaves), 0, s, a,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr);
     return check_launch("swa_attention");
   }
   {
@@ -1736,12 +1834,35 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
     } else {
       const dim3 grid(max_new_per_seq, n_seqs, kGroups);
       if ((int64_t)max_new_per_seq * n_seqs * kGroups < 1024)
-        hipLaunchKernelGGL((k_swa_attend<2, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_swa_attend<2>), grid, dim3(256), 0, s, a);
       else
-        hipLaunchKernelGGL((k_swa_attend<0, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_swa_attend<0>), grid, dim3(256), 0, s, a);
     }
   }
   return check_launch("swa_attention");
+}
+
+extern "C" dsa_status swa_decode_step(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
+                                      const int32_t* seq_pos, const uint16_t* q, const uint16_t* k_new,
+                                      const uint16_t* v_new, uint16_t* k_ring, uint16_t* v_ring, uint16_t* out,
+                                      void* stream) {
+  dsa_status st = swa_check(geom, window, n_seqs, 1, "swa_decode_step");
+  if (st != DSA_OK) return st;
+  if (n_seqs == 0) return DSA_OK;
+  if (!seq_pos || !q || !k_new || !v_new || !k_ring || !v_ring || !out)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "swa_decode_step: NULL pointer");
+  SwaArgs a = {};
+  a.pos0 = seq_pos; a.row0 = nullptr; a.q = q; a.k_new = k_new; a.v_new = v_new;
+  a.k_ring = k_ring; a.v_ring = v_ring; a.out = out;
+  a.n_seqs = n_seqs; a.max_new = 1; a.window = window; a.rows = n_seqs;
+  a.scale_log2 = geom->softmax_scale * kLog2e;
+  hipStream_t s = as_stream(stream);
+  {
+    ProfScope prof_("k_swa_attend", s);
+    hipLaunchKernelGGL((k_swa_decode<true>), dim3(1, n_seqs, kGroups), dim3(64 * kSwdWaves), 0, s, a, k_ring,
+                       v_ring);
+  }
+  return check_launch("swa_decode_step");
 }
 
 extern "C" dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_seqs,

@@ -523,6 +523,26 @@ dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_s
                            uint16_t* k_ring, uint16_t* v_ring, void* stream);
 
 /*
+ * One decode step of a sliding-window layer ([P1] section 滑窗注意力只读最近
+ * 512 个 token; [P2] section 512 Token 的环形缓冲区: attention over the last W
+ * positions, the new token written at slot position mod W): sequence s has one
+ * new token at position p = seq_pos[s], in row s of q, k_new and v_new; it
+ * attends to positions max(0, p-W+1)..p, and its K/V are then written into
+ * ring slot p mod W.  The output equals swa_attention with one new token per
+ * sequence (seq_row0 = 0, 1, .., n_seqs) and the rings equal a following
+ * swa_ring_append, in one launch and without a workspace (the slot written
+ * held position p - W, which this step no longer reads).
+ *   window   512
+ *   seq_pos  [n_seqs] int32 device (>= 0)
+ *   q, out   [n_seqs][64][D] bf16;  k_new, v_new [n_seqs][G][D] bf16
+ *   k_ring, v_ring  rings holding positions p-W .. p-1 (those >= 0), layouts as
+ *            for swa_attention; updated in place
+ */
+dsa_status swa_decode_step(const dsa_geometry* geom, int32_t window, int32_t n_seqs, const int32_t* seq_pos,
+                           const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_ring,
+                           uint16_t* v_ring, uint16_t* out, void* stream);
+
+/*
  * Indexer front-end ([P2] section 索引器打分 + Top-K 选择: the indexer projects
  * the hidden state into index_q / index_k / index_z, then normalises them and
  * rotates part of their dimensions; [P1] paragraph after step ④ and [P3]

@@ -475,6 +475,55 @@ def test_swa_batched_decode_with_prefilled_rings():
             assert np.array_equal(kr[s, :, t % H.W, :], Kh[t])
 
 
+def test_swa_decode_step_equals_attention_then_append():
+    """swa_decode_step (attention and ring append in one launch) against swa_attention followed by
+    swa_ring_append on copies of the same rings: the same output bit for bit, the same rings, and the
+    oracle's window attention; positions at the ring's start, a full ring, and region edges."""
+    seed = 0xF9
+    pos = [0, 5, 8, 511, 512, 513, 1023, 4100]
+    S = len(pos)
+    T = max(pos) + 1
+    tq, tk, tv = H.swa_tids(2)
+    geom = dsa.geometry()
+    per = G * H.W * D
+    k_ring = torch.full((S * per,), float("nan"), dtype=H.BF16, device="cuda")
+    v_ring = torch.full((S * per,), float("nan"), dtype=H.BF16, device="cuda")
+    for s, p in enumerate(pos):
+        t0 = max(0, p - H.W)
+        if p > t0:
+            for layout, ring, tid in ((gi.LAYOUT_KTILED, k_ring, tk), (gi.LAYOUT_REGION_T, v_ring, tv)):
+                tmp = torch.empty((s + 1) * per, dtype=H.BF16, device="cuda")
+                gi.dev_tokens(tmp.data_ptr(), H.stream_ptr(), seed, tid, s + 1, T, G, D, t0, p - t0, H.W, H.W,
+                              layout, 1.0)
+                ring[s * per:(s + 1) * per] = tmp[s * per:(s + 1) * per]
+    q = torch.empty(S * HQ * D, dtype=H.BF16, device="cuda")
+    kn = torch.empty(S * G * D, dtype=H.BF16, device="cuda")
+    vn = torch.empty(S * G * D, dtype=H.BF16, device="cuda")
+    for s, p in enumerate(pos):
+        gi.dev_flat(q[s * HQ * D:].data_ptr(), H.stream_ptr(), seed, tq, HQ * D, 0, 1.0, start=(s * T + p) * HQ * D)
+        tmpk = H.dev_cache(seed, tk, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=1)
+        tmpv = H.dev_cache(seed, tv, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=1)
+        kn[s * G * D:(s + 1) * G * D] = tmpk[s * G * D:(s + 1) * G * D]
+        vn[s * G * D:(s + 1) * G * D] = tmpv[s * G * D:(s + 1) * G * D]
+    kr1, vr1 = k_ring.clone(), v_ring.clone()
+    out1 = torch.empty(S * HQ * D, dtype=H.BF16, device="cuda")
+    dsa.swa_attention(geom, H.W, 1, H.i32(pos), H.i32(np.arange(S + 1)), q, kn, vn, kr1, vr1, out1)
+    dsa.swa_ring_append(geom, H.W, 1, H.i32(pos), H.i32(np.arange(S + 1)), kn, vn, kr1, vr1)
+    kr2, vr2 = k_ring.clone(), v_ring.clone()
+    out2 = torch.empty(S * HQ * D, dtype=H.BF16, device="cuda")
+    dsa.swa_decode_step(geom, H.W, H.i32(pos), q, kn, vn, kr2, vr2, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(kr1.view(torch.int16), kr2.view(torch.int16))
+    assert torch.equal(vr1.view(torch.int16), vr2.view(torch.int16))
+    go = H.bf16_np(out2).reshape(S, HQ, D)
+    for s, p in enumerate(pos):
+        Kh = gi.host_tokens_bf16(seed, tk, T, G, D, s, 0, p + 1)
+        Vh = gi.host_tokens_bf16(seed, tv, T, G, D, s, 0, p + 1)
+        hq = gi.host_normal_bf16(seed, tq, HQ * D, 1.0, start=(s * T + p) * HQ * D).reshape(HQ, D)
+        H.assert_attn(go[s], O.swa(hq, Kh, Vh, p, H.W), f"seq {s} at {p}")
+
+
 def test_swa_prefill_chunks_of_several_sequences_in_one_call():
     """Chunks of different lengths for sequences at different positions in one call (the banded
     prefill kernel: tiles of 16 tokens, partial last tiles, short and full rings)."""
