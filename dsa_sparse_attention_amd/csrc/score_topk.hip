@@ -393,6 +393,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
     int32_t cm = (active >> lane & 1ull) ? cqm : 0;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) cm = max(cm, __shfl_xor(cm, o));
+    // uniform: the tile loop's bounds and copy addresses then live in scalars
+    cm = __builtin_amdgcn_readfirstlane(cm);
 
     // A operand: rows = (query, head) pairs of group g; channel permutation
     // pi(s, kb, e) = 64*(s/2) + 16*kb + 8*(s%2) + e.  Rows of queries outside
@@ -418,6 +420,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
       const uint16_t* qp = a.iq + (qr * kIdxHeads + hh) * kProxy + 16 * kb;
 #pragma unroll
       for (int s = 0; s < 8; ++s) A[rs][s] = as_bf16x8(ld16(qp + 64 * (s >> 1) + 8 * (s & 1)));
+    }
+    // The operand and epilogue loads are waited for here, before any copy
+    // is in flight: a first use inside the tile loop would otherwise wait
+    // for every copy issued ahead of it.
+#pragma unroll
+    for (int rs = 0; rs < NRS; ++rs) {
+      asm volatile("" ::"v"(zq[rs]));
+#pragma unroll
+      for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, A[rs][s])));
     }
 
     const int64_t rend = (range0 + kScoreRange < cm) ? range0 + kScoreRange : (int64_t)cm;
@@ -446,6 +457,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
     if (nk > 0)
 #pragma unroll
       for (int k = 0; k < D - 1; ++k) issue(k);
+    // Store offsets: the lane's part (row 4rs+kb of the wave, region t0+n) is
+    // (kb*G*stride + n)*4, the rest ((4rs*G*stride + t0)*4) is uniform and
+    // goes in the scalar offset, so no per-tile offsets stay live in vector
+    // registers.
+    const uint32_t v_ws = ((uint32_t)(kb * kGroups) * (uint32_t)a.ws_stride + (uint32_t)n) * 4u;
+    const uint32_t v_out = OUT ? ((uint32_t)(kb * kGroups) * (uint32_t)a.max_regions + (uint32_t)n) * 4u : 0u;
+    const uint32_t v_tm = TILEMAX ? (uint32_t)(kb * kGroups) * (uint32_t)a.tm_stride * 4u : 0u;
     for (int k = 0; k < nk; ++k) {
       if (k < D - 1) wait_vm<Cfg::W_EARLY>();
       else wait_vm<Cfg::W_FULL>();
@@ -484,12 +502,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
         sv = fmaf(zz[3], fmaxf(acc[3], 0.0f), sv);
         sv *= sc;
         const bool ok = r < cq[rs];  // cq = -1 outside the pass
-        const uint32_t row = (uint32_t)((4 * rs + kb) * kGroups);
-        const uint32_t o_ws = ok ? (row * (uint32_t)a.ws_stride + (uint32_t)r) * 4u : kOutOfView;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), ws_view, o_ws, 0, 0);
+        const uint32_t srow = (uint32_t)(4 * rs * kGroups);
+        const uint32_t s_ws = (srow * (uint32_t)a.ws_stride + (uint32_t)t0) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), ws_view, ok ? v_ws : kOutOfView, s_ws, 0);
         if (OUT) {
-          const uint32_t o_out = ok ? (row * (uint32_t)a.max_regions + (uint32_t)r) * 4u : kOutOfView;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), out_view, o_out, 0, 0);
+          const uint32_t s_out = (srow * (uint32_t)a.max_regions + (uint32_t)t0) * 4u;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), out_view, ok ? v_out : kOutOfView, s_out, 0);
         }
         if (TILEMAX) {  // lanes 16kb..16kb+15 hold one query's tile
           uint32_t key = ok ? score_key(sv) : 0u;
@@ -498,8 +516,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
           key = max(key, (uint32_t)__shfl_xor((int)key, 2));
           key = max(key, (uint32_t)__shfl_xor((int)key, 1));
           const bool tok = n == 0 && t0 < cq[rs];
-          const uint32_t o_tm = tok ? (row * (uint32_t)a.tm_stride + (uint32_t)(t0 / kTile)) * 4u : kOutOfView;
-          __builtin_amdgcn_raw_buffer_store_b32(key, tm_view, o_tm, 0, 0);
+          const uint32_t s_tm = (srow * (uint32_t)a.tm_stride + (uint32_t)(t0 / kTile)) * 4u;
+          __builtin_amdgcn_raw_buffer_store_b32(key, tm_view, tok ? v_tm : kOutOfView, s_tm, 0);
         }
       }
     }
