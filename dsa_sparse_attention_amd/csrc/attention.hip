@@ -962,30 +962,43 @@ void k_swa_attend(SwaArgs a) {
   }
 }
 
-// Sliding-window decode, one new token per sequence: block = (sequence s,
-// group g) with kSwdWaves waves; the window's <= 65 regions go to the waves
-// in chunks of 4 (wave w: chunks w, w + kSwdWaves, ...), so all of a window's
-// loads are issued at once instead of chunk after chunk, and the waves'
-// partials merge through LDS.  The current region is the ring's with the new
-// token patched in at load time.  APPEND: the block then writes the new
-// token's K/V into ring slot p mod W; that slot held position p - W, outside
-// this window, and no other block reads this (sequence, group)'s ring.
-constexpr int kSwdWaves = 8;
+// Sliding-window decode, one new token per sequence, in two launches.  The
+// window's <= 65 regions form <= 17 chunks of 4; part block b of (sequence
+// s, group g) gives chunk kSwpWaves*b + w to its wave w, so a batch of 8
+// spreads its 136 chunks over 160 blocks instead of loading each window
+// through one compute unit.  The waves' partial (max, sum, O) merge through
+// LDS into one unnormalised record per part; k_swa_decode_merge then
+// combines the parts of each (sequence, group) in part order.  The current
+// region is the ring's with the new token patched in at load time.
+constexpr int kSwpWaves = 4;                                             // waves (chunks) per part
+constexpr int kSwpChunks = (kWindow / kRegion + 1 + 3) / 4;              // chunks a window spans
+constexpr int kSwpParts = (kSwpChunks + kSwpWaves - 1) / kSwpWaves;      // part blocks per (sequence, group)
+constexpr int kSwpRec = 2 * kHeadsPerGroup + kHeadsPerGroup * kHeadDim;  // floats per part: m, l, O[16][D]
+static_assert(kHeadsPerGroup == 16 && kHeadDim % 4 == 0, "part records hold 16 heads");
 
-template <bool APPEND>
-__global__ __launch_bounds__(64 * kSwdWaves) void k_swa_decode(SwaArgs a, uint16_t* k_ring_w, uint16_t* v_ring_w) {
-  const int s = blockIdx.y, g = blockIdx.z;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
-  __shared__ float sm_m[kSwdWaves][16], sm_l[kSwdWaves][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[kSwdWaves][16][kORow];
+__device__ __forceinline__ void swa_decode_window(const SwaArgs& a, int s, int64_t& p, int64_t& row,
+                                                  int64_t& rlo, int64_t& nreg) {
   int64_t p0, r0, nnew;
   seq_rows(a, s, p0, r0, nnew);
-  if (nnew <= 0) return;
-  const int64_t p = p0, row = r0;  // the sequence's one new token
+  p = p0;
+  row = r0;
+  const int64_t lo = p - a.window + 1 < 0 ? 0 : p - a.window + 1;
+  rlo = lo / kRegion;
+  nreg = nnew > 0 ? p / kRegion - rlo + 1 : 0;
+}
+
+__global__ __launch_bounds__(64 * kSwpWaves) void k_swa_decode_part(SwaArgs a, float* part) {
+  const int b = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  __shared__ float sm_m[kSwpWaves][16], sm_l[kSwpWaves][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[kSwpWaves][16][kORow];
+  int64_t p, row, rlo, nreg;
+  swa_decode_window(a, s, p, row, rlo, nreg);
+  const int64_t nch = (nreg + 3) / 4;
+  if ((int64_t)b * kSwpWaves >= nch) return;  // (uniform) no chunk for this part: the merge skips it
   const int W = a.window;
   const int64_t lo = p - W + 1 < 0 ? 0 : p - W + 1;
-  const int64_t rlo = lo / kRegion, rhi = p / kRegion;
   const int64_t sg = (int64_t)s * kGroups + g;
   const uint16_t* rk = a.k_ring + sg * W * kHeadDim;
   const uint16_t* rv = a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion;
@@ -995,11 +1008,10 @@ __global__ __launch_bounds__(64 * kSwdWaves) void k_swa_decode(SwaArgs a, uint16
   load_q(a.q, row, g, qb);
   CoreState st;
   core_init(st);
-  const int64_t nreg = rhi - rlo + 1;
-  const int64_t nch = (nreg + 3) / 4;
-  const int64_t mine = wave < nch ? 4 * ((nch - wave + kSwdWaves - 1) / kSwdWaves) : 0;  // this wave's entries
+  const int64_t c = (int64_t)b * kSwpWaves + wave;  // this wave's chunk
+  const int64_t mine = c < nch ? 4 : 0;
   auto region_of = [&](int64_t e) -> Region {
-    const int64_t er = 4 * (wave + kSwdWaves * (e >> 2)) + (e & 3);  // window region index of entry e
+    const int64_t er = 4 * c + e;  // window region index of entry e
     Region rg;
     if (e >= mine || er >= nreg) {
       rg.k = rk; rg.v = rv; rg.lo = 1; rg.hi = 0;
@@ -1027,36 +1039,119 @@ __global__ __launch_bounds__(64 * kSwdWaves) void k_swa_decode(SwaArgs a, uint16
 #pragma unroll
   for (int nt = 0; nt < 12; ++nt) *(f32x4*)&sm_o[wave][n][16 * nt + 4 * kb] = st.o[nt];
   __syncthreads();
-  uint16_t* op = a.out + (row * kQHeads + kHeadsPerGroup * g) * kHeadDim;
-  for (int e = threadIdx.x; e < 16 * kHeadDim; e += 64 * kSwdWaves) {
-    const int h = e / kHeadDim, d = e - h * kHeadDim;
+  // the part's record: m and l of each head, then O[h][d] scaled to the part's max
+  float* rec = part + (sg * kSwpParts + b) * kSwpRec;
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
     float M = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kSwdWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float acc = 0.0f, lsum = 0.0f;
-    if (M != -INFINITY) {
+    for (int w = 1; w < kSwpWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float l = 0.0f;
+    if (M != -INFINITY)
 #pragma unroll
-      for (int w = 0; w < kSwdWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
-        acc += f * sm_o[w][h][d];
-        lsum += f * sm_l[w][h];
-      }
+      for (int w = 0; w < kSwpWaves; ++w) l += __builtin_amdgcn_exp2f(sm_m[w][h] - M) * sm_l[w][h];
+    rec[h] = M;
+    rec[16 + h] = l;
+  }
+  for (int e = threadIdx.x; e < 16 * kHeadDim / 4; e += 64 * kSwpWaves) {
+    const int h = e / (kHeadDim / 4), d = 4 * (e - h * (kHeadDim / 4));
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kSwpWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < kSwpWaves; ++w) acc += __builtin_amdgcn_exp2f(sm_m[w][h] - M) * *(const f32x4*)&sm_o[w][h][d];
+    *(f32x4*)(rec + 32 + h * kHeadDim + d) = acc;
+  }
+}
+
+// block = (sequence s, group g): the parts that hold a chunk, combined in
+// part order, normalised and stored; thread t handles channels 4j..4j+3 of
+// items t, t+256, t+512 (item = head h, channel quad j) and issues all of its
+// record loads before using any.  APPEND: then the new token's K/V go into
+// ring slot p mod W.  That slot held position p - W, outside this window;
+// the part kernel, which read the ring, ran before this launch.
+template <bool APPEND>
+__global__ __launch_bounds__(256) void k_swa_decode_merge(SwaArgs a, const float* part, uint16_t* k_ring_w,
+                                                          uint16_t* v_ring_w) {
+  constexpr int kQuads = kHeadDim / 4, kItems = kHeadsPerGroup * kQuads / 256;
+  static_assert(kHeadsPerGroup * kQuads == 256 * kItems, "items fill the block");
+  const int s = blockIdx.x, g = blockIdx.y;
+  int64_t p, row, rlo, nreg;
+  swa_decode_window(a, s, p, row, rlo, nreg);
+  if (nreg <= 0) return;
+  const int nparts = (int)(((nreg + 3) / 4 + kSwpWaves - 1) / kSwpWaves);
+  const int64_t sg = (int64_t)s * kGroups + g;
+  const float* rec = part + sg * kSwpParts * kSwpRec;
+  const int t = threadIdx.x;
+  const uint16_t* knew = a.k_new + (row * kGroups + g) * kHeadDim;
+  const uint16_t* vnew = a.v_new + (row * kGroups + g) * kHeadDim;
+  u32x4 kv = {0u, 0u, 0u, 0u};
+  uint16_t vv = 0;
+  if constexpr (APPEND) {
+    if (t < kHeadDim / 8) kv = ld16(knew + 8 * t);
+    else if (t >= 64 && t < 64 + kHeadDim) vv = vnew[t - 64];
+  }
+  float m[kItems][kSwpParts], l[kItems][kSwpParts];
+  f32x4 o[kItems][kSwpParts];
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const int e = t + 256 * i, h = e / kQuads, d = 4 * (e - h * kQuads);
+#pragma unroll
+    for (int b = 0; b < kSwpParts; ++b) {
+      const float* rb = rec + (b < nparts ? b : 0) * kSwpRec;  // (parts past nparts: weight 0 below)
+      m[i][b] = rb[h];
+      l[i][b] = rb[16 + h];
+      o[i][b] = *(const f32x4*)(rb + 32 + h * kHeadDim + d);
     }
-    op[h * kHeadDim + d] = f32_to_bf16(lsum > 0.0f ? acc / lsum : 0.0f);
+  }
+  uint16_t* op = a.out + (row * kQHeads + kHeadsPerGroup * g) * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const int e = t + 256 * i, h = e / kQuads, d = 4 * (e - h * kQuads);
+    float M = m[i][0];
+#pragma unroll
+    for (int b = 1; b < kSwpParts; ++b) M = b < nparts ? fmaxf(M, m[i][b]) : M;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.0f;
+    if (M != -INFINITY)
+#pragma unroll
+      for (int b = 0; b < kSwpParts; ++b) {
+        const float f = b < nparts ? __builtin_amdgcn_exp2f(m[i][b] - M) : 0.0f;
+        acc += f * o[i][b];
+        L += f * l[i][b];
+      }
+    uint2 w;
+    w.x = pack_bf16x2(L > 0.0f ? acc[0] / L : 0.0f, L > 0.0f ? acc[1] / L : 0.0f);
+    w.y = pack_bf16x2(L > 0.0f ? acc[2] / L : 0.0f, L > 0.0f ? acc[3] / L : 0.0f);
+    *(uint2*)(op + h * kHeadDim + d) = w;
   }
   if constexpr (APPEND) {
-    // (every load of the block completed before the barrier above)
+    const int W = a.window;
     const int64_t slot = p % W;
-    const int t = threadIdx.x;
-    if (t < kHeadDim / 8) {  // K: 24 units of 8 channels
-      const int d0 = 8 * t;
-      const u32x4 v = ld16(knew + d0);
-      *(u32x4*)(k_ring_w + (sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, d0)) = v;
-    } else if (t >= 64 && t < 64 + kHeadDim) {  // V: 192 channels
-      const int d = t - 64;
-      v_ring_w[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + d) * kRegion + slot % kRegion] = vnew[d];
-    }
+    if (t < kHeadDim / 8)  // K: 24 units of 8 channels
+      *(u32x4*)(k_ring_w + (sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, 8 * t)) = kv;
+    else if (t >= 64 && t < 64 + kHeadDim)  // V: 192 channels
+      v_ring_w[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + (t - 64)) * kRegion + slot % kRegion] = vv;
   }
+}
+
+// Launches the two decode kernels; part records at `part` (swa_decode_part_bytes).
+static void swa_decode_launch(const SwaArgs& a, float* part, uint16_t* k_ring_w, uint16_t* v_ring_w,
+                              hipStream_t s) {
+  ProfScope prof_("k_swa_attend", s);
+  hipLaunchKernelGGL(k_swa_decode_part, dim3(kSwpParts, a.n_seqs, kGroups), dim3(64 * kSwpWaves), 0, s, a, part);
+  if (k_ring_w)
+    hipLaunchKernelGGL((k_swa_decode_merge<true>), dim3(a.n_seqs, kGroups), dim3(256), 0, s, a,
+                       (const float*)part, k_ring_w, v_ring_w);
+  else
+    hipLaunchKernelGGL((k_swa_decode_merge<false>), dim3(a.n_seqs, kGroups), dim3(256), 0, s, a,
+                       (const float*)part, (uint16_t*)nullptr, (uint16_t*)nullptr);
+}
+
+static size_t swa_decode_part_bytes(int32_t n_seqs) {
+  return ((size_t)n_seqs * kGroups * kSwpParts * kSwpRec * sizeof(float) + 255) / 256 * 256;
 }
 
 // S^T tiles, online softmax and O^T += V^T P^T of one chunk for NQ queries
@@ -1775,8 +1870,15 @@ extern "C" size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t
   (void)geom;
   (void)window;
   if (n_seqs <= 0 || max_new_per_seq <= 0) return 256;
+  if (max_new_per_seq == 1) return swa_decode_part_bytes(n_seqs);  // decode: the part records
   const size_t one = (size_t)n_seqs * kGroups * nstage_of(max_new_per_seq) * kRegion * kHeadDim * sizeof(uint16_t);
   return 2 * ((one + 255) / 256 * 256) + 256;
+}
+
+extern "C" size_t swa_decode_step_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs) {
+  (void)geom;
+  (void)window;
+  return n_seqs <= 0 ? 256 : swa_decode_part_bytes(n_seqs);
 }
 
 static dsa_status swa_check(const dsa_geometry* geom, int32_t window, int32_t n_seqs, int32_t max_new,
@@ -1813,10 +1915,8 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   a.st_k = (uint16_t*)workspace;
   a.st_v = (uint16_t*)((char*)workspace + (one + 255) / 256 * 256);
   hipStream_t s = as_stream(stream);
-  if (max_new_per_seq == 1) {  // decode: the attention kernel patches the new token in itself
-    ProfScope prof_("k_swa_attend", s);
-    hipLaunchKernelGGL((k_swa_decode<false>), dim3(1, n_seqs, kGroups), dim3(64 * kSwdWaves), 0, s, a,
-                       (uint16_t*)nullptr, (uint16_t*)nullptr);
+  if (max_new_per_seq == 1) {  // decode: the attention kernels patch the new token in themselves
+    swa_decode_launch(a, (float*)workspace, nullptr, nullptr, s);
     return check_launch("swa_attention");
   }
   {
@@ -1845,23 +1945,22 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
 extern "C" dsa_status swa_decode_step(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
                                       const int32_t* seq_pos, const uint16_t* q, const uint16_t* k_new,
                                       const uint16_t* v_new, uint16_t* k_ring, uint16_t* v_ring, uint16_t* out,
-                                      void* stream) {
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status st = swa_check(geom, window, n_seqs, 1, "swa_decode_step");
   if (st != DSA_OK) return st;
   if (n_seqs == 0) return DSA_OK;
-  if (!seq_pos || !q || !k_new || !v_new || !k_ring || !v_ring || !out)
+  if (!seq_pos || !q || !k_new || !v_new || !k_ring || !v_ring || !out || !workspace)
     return fail(DSA_ERR_INVALID_ARGUMENT, "swa_decode_step: NULL pointer");
+  if ((size_t)workspace & 255)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "swa_decode_step: workspace must be 256-byte aligned");
+  if (workspace_bytes < swa_decode_step_workspace_size(geom, window, n_seqs))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "swa_decode_step: workspace too small");
   SwaArgs a = {};
   a.pos0 = seq_pos; a.row0 = nullptr; a.q = q; a.k_new = k_new; a.v_new = v_new;
   a.k_ring = k_ring; a.v_ring = v_ring; a.out = out;
   a.n_seqs = n_seqs; a.max_new = 1; a.window = window; a.rows = n_seqs;
   a.scale_log2 = geom->softmax_scale * kLog2e;
-  hipStream_t s = as_stream(stream);
-  {
-    ProfScope prof_("k_swa_attend", s);
-    hipLaunchKernelGGL((k_swa_decode<true>), dim3(1, n_seqs, kGroups), dim3(64 * kSwdWaves), 0, s, a, k_ring,
-                       v_ring);
-  }
+  swa_decode_launch(a, (float*)workspace, k_ring, v_ring, as_stream(stream));
   return check_launch("swa_decode_step");
 }
 
