@@ -108,6 +108,14 @@ __device__ __forceinline__ void codes_to_bf16(u32x4 c, bf16x8& lo, bf16x8& hi) {
   hi = bf16x8{p4[0], p4[1], p5[0], p5[1], p6[0], p6[1], p7[0], p7[1]};
 }
 
+// max(x, 0) in one instruction: the median of (x, 0, FLT_MAX), equal to it
+// for every x but +inf.  fmaxf(x, 0) costs two (the compiler first quiets a
+// possible signalling NaN), and so does a median with +inf, which it turns
+// back into fmaxf.  (Not inline asm: the compiler inserts no wait states
+// before an asm block that reads an MFMA result, which can then read the
+// register before the MFMA has written it.)
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f); }
+
 // Exclusive prefix sum over a block of NT threads.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) {
@@ -274,10 +282,10 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
       const int64_t r = w0 + (int64_t)t * kTile + n;
       uint32_t key = 0;
       if (kb == 0 && r < w1) {
-        float sv = zz[0] * fmaxf(acc[0], 0.0f);
-        sv = fmaf(zz[1], fmaxf(acc[1], 0.0f), sv);
-        sv = fmaf(zz[2], fmaxf(acc[2], 0.0f), sv);
-        sv = fmaf(zz[3], fmaxf(acc[3], 0.0f), sv);
+        float sv = zz[0] * relu(acc[0]);
+        sv = fmaf(zz[1], relu(acc[1]), sv);
+        sv = fmaf(zz[2], relu(acc[2]), sv);
+        sv = fmaf(zz[3], relu(acc[3]), sv);
         sv *= bsc[u];
         scores[r] = sv;
         if (scores_out) scores_out[r] = sv;
@@ -496,10 +504,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
         // output rows 4kb..4kb+3 of row-set rs belong to query qw + 4rs + kb
         const f32x4 acc = accs[rs];
         const f32x4 zz = zq[rs];
-        float sv = zz[0] * fmaxf(acc[0], 0.0f);
-        sv = fmaf(zz[1], fmaxf(acc[1], 0.0f), sv);
-        sv = fmaf(zz[2], fmaxf(acc[2], 0.0f), sv);
-        sv = fmaf(zz[3], fmaxf(acc[3], 0.0f), sv);
+        float sv = zz[0] * relu(acc[0]);
+        sv = fmaf(zz[1], relu(acc[1]), sv);
+        sv = fmaf(zz[2], relu(acc[2]), sv);
+        sv = fmaf(zz[3], relu(acc[3]), sv);
         sv *= sc;
         const bool ok = r < cq[rs];  // cq = -1 outside the pass
         const uint32_t srow = (uint32_t)(4 * rs * kGroups);
