@@ -467,8 +467,8 @@ template <bool FP8>
 __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[4][16][kORow];
+  __shared__ float sm_m[2][16], sm_l[2][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[2][16][kORow];
 
   // every load that does not depend on the list is issued at once: the
   // sequence length, the count, this lane's two list entries (clamped index)
@@ -503,32 +503,42 @@ __global__ __launch_bounds__(256) void k_sgqa_decode(DecodeArgs a) {
   } else {
     core_chunk(st, qb, dsa_region(a.k, a.v, slot_a, ra_id, p), dsa_region(a.k, a.v, slot_b, rb_id, p), a.scale_log2);
   }
-  // wave partials -> LDS (O^T lane layout: head n, channels 16nt + 4kb + i)
-  const float lt = core_total_l(st);
-  if (kb == 0) {
-    sm_m[wave][n] = st.m;
-    sm_l[wave][n] = lt;
-  }
-#pragma unroll
-  for (int nt = 0; nt < 12; ++nt) *(f32x4*)&sm_o[wave][n][16 * nt + 4 * kb] = st.o[nt];
-  __syncthreads();
-  float* part = a.part + ((sg * a.nsplit) + split) * 16 * kPartStride;
-  for (int e = threadIdx.x; e < 16 * kHeadDim; e += 256) {
-    const int h = e / kHeadDim, d = e - h * kHeadDim;
-    float M = fmaxf(fmaxf(sm_m[0][h], sm_m[1][h]), fmaxf(sm_m[2][h], sm_m[3][h]));
-    float acc = 0.0f, lsum = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
-        acc += f * sm_o[w][h][d];
-        lsum += f * sm_l[w][h];
-      }
+  // The 4 waves' partials combine in pairs through 25 KB of LDS (waves 2, 3
+  // into 0, 1, then 1 into 0), so that 4 blocks fit per CU; wave 0 writes
+  // the split's (max, sum, unnormalised O).  O^T lane layout: head n,
+  // channels 16nt + 4kb + i.
+  float l = core_total_l(st);
+  auto put = [&](int slot) {
+    if (kb == 0) {
+      sm_m[slot][n] = st.m;
+      sm_l[slot][n] = l;
     }
-    part[h * kPartStride + 4 + d] = acc;
-    if (d == 0) {
-      part[h * kPartStride] = M;
-      part[h * kPartStride + 1] = lsum;
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) *(f32x4*)&sm_o[slot][n][16 * nt + 4 * kb] = st.o[nt];
+  };
+  auto take = [&](int slot) {
+    const float mo = sm_m[slot][n], M = fmaxf(st.m, mo);
+    const float fa = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m - M);
+    const float fb = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mo - M);
+    l = fa * l + fb * sm_l[slot][n];
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) st.o[nt] = fa * st.o[nt] + fb * *(const f32x4*)&sm_o[slot][n][16 * nt + 4 * kb];
+    st.m = M;
+  };
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) take(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+  if (wave == 0) {
+    take(0);
+    float* part = a.part + ((sg * a.nsplit) + split) * 16 * kPartStride + n * kPartStride;
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) *(f32x4*)(part + 4 + 16 * nt + 4 * kb) = st.o[nt];
+    if (kb == 0) {
+      part[0] = st.m;
+      part[1] = l;
     }
   }
 }
