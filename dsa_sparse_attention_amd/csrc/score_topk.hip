@@ -1396,9 +1396,15 @@ static_assert(kHistBins == kPreNT * 16, "each thread owns 16 histogram bins");
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(7))) void k_select_pre(SelectArgs a) {
   constexpr int NW = NT / 64;
+  static_assert(NW == kGroups, "a folded block compresses one query's 4 groups");
   const int64_t pq = blockIdx.x;
   const int qi = (int)(pq / kGroups);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (pq >= (int64_t)a.nq * kGroups) {  // folded compression of a decode step: query pq - nq G, wave w -> group w
+    const int64_t fq = pq - (int64_t)a.nq * kGroups;
+    if (fq < a.nq) folded_compress(a, fq, w);
+    return;
+  }
   __shared__ PreSmem<NT, KPT> sm;
   const int64_t c64 = current_region(query_pos(a.qpos, a.slen, qi), a.cm.R, a.max_regions);
   const uint32_t need = (uint32_t)((c64 < (int64_t)(a.topk - 1)) ? c64 : (int64_t)(a.topk - 1));
@@ -1649,9 +1655,10 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   se.ik = index_k; se.csumm = csumm; se.cscale = cscale; se.n_seqs = n_seqs;
   se.sel = sel; se.nsel = n_sel; se.cm = cm; se.nq = n_queries; se.max_regions = max_regions;
   se.ws_stride = stride; se.tm_stride = sa.tm_stride; se.topk = geom->topk;
-  // the decode step's compression runs as extra blocks of the decode
-  // selection launch, or as its own small launch on the other paths
-  const bool fold_in_select = index_k && w.hist;
+  // the decode step's compression runs as extra blocks of the selection
+  // launch (the decode one, or the short-context one), or as its own small
+  // launch before the tile selection
+  const bool fold_in_select = index_k && (w.hist || !tiled_select(max_regions));
   if (index_k && !fold_in_select) {
     ProfScope prof_("k_compress", s);
     hipLaunchKernelGGL(k_fold_compress, dim3((unsigned)n_queries), dim3(256), 0, s, se);
@@ -1688,8 +1695,10 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   {
     ProfScope prof_("k_select", s);
     const dim3 grid((unsigned)((int64_t)n_queries * kGroups));
-    if (!tiled_select(max_regions))
-      hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>), grid, dim3(kPreNT), 0, s, se);
+    if (!tiled_select(max_regions))  // (+ one block per query for the folded compression)
+      hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>),
+                         dim3((unsigned)((int64_t)n_queries * (kGroups + (fold_in_select ? 1 : 0)))), dim3(kPreNT),
+                         0, s, se);
     else if (w.hist) {
       const int64_t folds = fold_in_select ? ((int64_t)n_queries * kGroups + kDecNT / 64 - 1) / (kDecNT / 64) : 0;
       hipLaunchKernelGGL(k_select_dec, dim3((unsigned)((int64_t)n_queries * kGroups + folds)), dim3(kDecNT), 0, s,
