@@ -368,13 +368,24 @@ template <bool TILEMAX, bool OUT, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAVES, DSA_PRE_WAVES))) void k_score_pre(ScoreArgs a) {
   using Cfg = PreScoreCfg<TILEMAX, OUT>;
   constexpr int NRS = 4, D = Cfg::D;
-  const int g = blockIdx.y;
+  // Block -> (query block, group, region range).  Consecutive blocks go to
+  // the 8 XCDs in turn, so XCD x takes the query blocks x, x + 8, ..., each
+  // as all (group, range) blocks in a row: the ones resident together read
+  // the same few query operands (128 KB per query block and group), which
+  // then come from that XCD's L2, while the summary tiles, copied well ahead
+  // of their use, stream from the Infinity Cache.
+  const int nranges = (a.max_regions + kScoreRange - 1) / kScoreRange;
+  const int per_qblock = nranges * kGroups;
+  const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+  const int qblk = xcd + 8 * (jb / per_qblock);
+  if (qblk * kPreQ >= a.nq) return;  // (uniform) past the last query block
+  const int g = (jb % per_qblock) / nranges;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: buffer views in scalars
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kb = lane >> 4;
-  const int qb = blockIdx.z * kPreQ;   // the block's first query
+  const int qb = qblk * kPreQ;         // the block's first query
   const int qw = qb + 16 * wave;       // the wave's first query
-  const int64_t range0 = (int64_t)blockIdx.x * kScoreRange;
+  const int64_t range0 = (int64_t)((jb % per_qblock) % nranges) * kScoreRange;
   __shared__ __attribute__((aligned(16))) uint8_t ring[D][kPreSlot];
 
   // Query metadata, one round of loads: lane l holds query qb + l (clamped
@@ -1674,7 +1685,8 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   } else {
     ProfScope prof_("k_score_prefill", s);
     const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
-    const dim3 grid(ranges, kGroups, (n_queries + kPreQ - 1) / kPreQ);
+    const int qblocks = (n_queries + kPreQ - 1) / kPreQ;
+    const dim3 grid((unsigned)(8 * ranges * kGroups * ((qblocks + 7) / 8)));  // (see k_score_pre)
     const bool tm = tiled_select(max_regions), out = scores_out != nullptr;
     // (paged and contiguous caches are separate instantiations: the page-id
     // loads stay out of the contiguous kernels)
