@@ -368,6 +368,7 @@ template <bool TILEMAX, bool OUT, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAVES, DSA_PRE_WAVES))) void k_score_pre(ScoreArgs a) {
   using Cfg = PreScoreCfg<TILEMAX, OUT>;
   constexpr int NRS = 4, D = Cfg::D;
+  constexpr bool kPipelined = !TILEMAX && !OUT && !PAGED;
   // Block -> (query block, group, region range).  Consecutive blocks go to
   // the 8 XCDs in turn, so XCD x takes the query blocks x, x + 8, ..., each
   // as all (group, range) blocks in a row: the ones resident together read
@@ -483,13 +484,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
     const uint32_t v_ws = ((uint32_t)(kb * kGroups) * (uint32_t)a.ws_stride + (uint32_t)n) * 4u;
     const uint32_t v_out = OUT ? ((uint32_t)(kb * kGroups) * (uint32_t)a.max_regions + (uint32_t)n) * 4u : 0u;
     const uint32_t v_tm = TILEMAX ? (uint32_t)(kb * kGroups) * (uint32_t)a.tm_stride * 4u : 0u;
+    // Scores of tile k: four row-sets of 4 queries x 4 heads; lane (kb, n)
+    // turns rows 4kb..4kb+3 of row-set rs (query qw + 4rs + kb, the group's
+    // 4 heads) into the score of region t0 + n.  In the plain instance the
+    // epilogue is software-pipelined: tile k's runs in iteration k + 1,
+    // among tile k + 1's MFMAs (one wave can issue independent VALU work
+    // while its MFMAs run), and after the loop for the last tile (3%; the
+    // other instances have no registers left for the previous tile's
+    // accumulators).  Every call issues the same stores (out of the view
+    // when `valid` is false), so the wait counts stay exact.
+    auto epilogue = [&](const f32x4 (&accs)[NRS], float sc, int t0, bool valid) {
+      const int r = t0 + n;
+#pragma unroll
+      for (int rs = 0; rs < NRS; ++rs) {
+        const f32x4 acc = accs[rs];
+        const f32x4 zz = zq[rs];
+        float sv = zz[0] * relu(acc[0]);
+        sv = fmaf(zz[1], relu(acc[1]), sv);
+        sv = fmaf(zz[2], relu(acc[2]), sv);
+        sv = fmaf(zz[3], relu(acc[3]), sv);
+        sv *= sc;
+        const bool ok = valid && r < cq[rs];  // cq = -1 outside the pass
+        const uint32_t srow = (uint32_t)(4 * rs * kGroups);
+        const uint32_t s_ws = (srow * (uint32_t)a.ws_stride + (uint32_t)t0) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), ws_view, ok ? v_ws : kOutOfView, s_ws, 0);
+        if (OUT) {
+          const uint32_t s_out = (srow * (uint32_t)a.max_regions + (uint32_t)t0) * 4u;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), out_view, ok ? v_out : kOutOfView, s_out, 0);
+        }
+        if (TILEMAX) {  // lanes 16kb..16kb+15 hold one query's tile
+          uint32_t key = ok ? score_key(sv) : 0u;
+          key = max(key, (uint32_t)__shfl_xor((int)key, 8));
+          key = max(key, (uint32_t)__shfl_xor((int)key, 4));
+          key = max(key, (uint32_t)__shfl_xor((int)key, 2));
+          key = max(key, (uint32_t)__shfl_xor((int)key, 1));
+          const bool tok = valid && n == 0 && t0 < cq[rs];
+          const uint32_t s_tm = (srow * (uint32_t)a.tm_stride + (uint32_t)(t0 >= 0 ? t0 / kTile : 0)) * 4u;
+          __builtin_amdgcn_raw_buffer_store_b32(key, tm_view, tok ? v_tm : kOutOfView, s_tm, 0);
+        }
+      }
+    };
+    f32x4 pacc[NRS];  // the previous tile's accumulators, scale and first region
+#pragma unroll
+    for (int rs = 0; rs < NRS; ++rs) pacc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float psc = 0.0f;
+    int pt0 = (int)range0;
     for (int k = 0; k < nk; ++k) {
       if (k < D - 1) wait_vm<Cfg::W_EARLY>();
       else wait_vm<Cfg::W_FULL>();
       lds_barrier();  // (a workgroup fence here would drain every copy in flight)
       issue(k + D - 1);
       const int t0 = (int)range0 + k * kTile;  // region indices fit 32 bits (max_regions is int32)
-      const int r = t0 + n;
       const uint8_t* src = &ring[k % D][0];
       const u32x4 c0 = *(const u32x4*)(src + 16 * lane), c1 = *(const u32x4*)(src + 1024 + 16 * lane),
                   c2 = *(const u32x4*)(src + 2048 + 16 * lane), c3 = *(const u32x4*)(src + 3072 + 16 * lane);
@@ -510,36 +555,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_PRE_WAV
           accs[rs] = mfma16x16x32(A[rs][2 * q4 + 1], B1, accs[rs]);
         }
       }
+      if constexpr (kPipelined) {
+        epilogue(pacc, psc, pt0, k > 0);
 #pragma unroll
-      for (int rs = 0; rs < NRS; ++rs) {
-        // output rows 4kb..4kb+3 of row-set rs belong to query qw + 4rs + kb
-        const f32x4 acc = accs[rs];
-        const f32x4 zz = zq[rs];
-        float sv = zz[0] * relu(acc[0]);
-        sv = fmaf(zz[1], relu(acc[1]), sv);
-        sv = fmaf(zz[2], relu(acc[2]), sv);
-        sv = fmaf(zz[3], relu(acc[3]), sv);
-        sv *= sc;
-        const bool ok = r < cq[rs];  // cq = -1 outside the pass
-        const uint32_t srow = (uint32_t)(4 * rs * kGroups);
-        const uint32_t s_ws = (srow * (uint32_t)a.ws_stride + (uint32_t)t0) * 4u;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), ws_view, ok ? v_ws : kOutOfView, s_ws, 0);
-        if (OUT) {
-          const uint32_t s_out = (srow * (uint32_t)a.max_regions + (uint32_t)t0) * 4u;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), out_view, ok ? v_out : kOutOfView, s_out, 0);
-        }
-        if (TILEMAX) {  // lanes 16kb..16kb+15 hold one query's tile
-          uint32_t key = ok ? score_key(sv) : 0u;
-          key = max(key, (uint32_t)__shfl_xor((int)key, 8));
-          key = max(key, (uint32_t)__shfl_xor((int)key, 4));
-          key = max(key, (uint32_t)__shfl_xor((int)key, 2));
-          key = max(key, (uint32_t)__shfl_xor((int)key, 1));
-          const bool tok = n == 0 && t0 < cq[rs];
-          const uint32_t s_tm = (srow * (uint32_t)a.tm_stride + (uint32_t)(t0 / kTile)) * 4u;
-          __builtin_amdgcn_raw_buffer_store_b32(key, tm_view, tok ? v_tm : kOutOfView, s_tm, 0);
-        }
+        for (int rs = 0; rs < NRS; ++rs) pacc[rs] = accs[rs];
+        psc = sc;
+        pt0 = t0;
+      } else {
+        epilogue(accs, sc, t0, true);
       }
     }
+    if (kPipelined && nk > 0) epilogue(pacc, psc, pt0, true);
     // the copies issued past the last tile must land before the ring is reused
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
