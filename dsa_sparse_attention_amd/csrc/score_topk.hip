@@ -188,6 +188,7 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
 #define DSA_SCORE_DEC_DEPTH 4
 #endif
 constexpr int kDecRange = DSA_SCORE_DEC_RANGE;  // regions per decode-score block
+constexpr int kDecRangeShort = 128;               // the same for problems of <= 8192 regions
 constexpr int kDecDepth = DSA_SCORE_DEC_DEPTH;  // tiles in flight per wave
 
 // Decode scoring: one query per block, one (query, group) region range.
@@ -197,7 +198,7 @@ constexpr int kDecDepth = DSA_SCORE_DEC_DEPTH;  // tiles in flight per wave
 // it; the tile's largest key is reduced over those 16 lanes and stored too.
 // When a.hist is set, the level-0 digits of the scores are counted in LDS
 // and added to one stripe of the (query, group) histogram at the end.
-template <bool PAGED>
+template <bool PAGED, int RANGE>
 __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   const int g = blockIdx.y;
   const int qi = blockIdx.z;
@@ -208,8 +209,8 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   if (a.hist)
     for (int i = threadIdx.x; i < kHistBins; i += 256) hist_lds[i] = 0;
 
-  constexpr int kWaveRegions = kDecRange / 4;
-  const int64_t w0 = (int64_t)blockIdx.x * kDecRange + (int64_t)wave * kWaveRegions;
+  constexpr int kWaveRegions = RANGE / 4;
+  const int64_t w0 = (int64_t)blockIdx.x * RANGE + (int64_t)wave * kWaveRegions;
   int32_t seq = query_seq(a.qseq, qi);
   seq = seq < 0 ? 0 : (seq >= a.n_seqs ? a.n_seqs - 1 : seq);
   const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.cm.R, a.max_regions);
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
 
   u32x4 buf[kDecDepth][4];
   float bsc[kDecDepth];
-  static_assert(kDecRange / 4 / kTile <= 64, "a lane per tile of the wave");
+  static_assert(RANGE / 4 / kTile <= 64 && RANGE % (4 * kTile) == 0, "a lane per tile of the wave");
   auto issue = [&](int t, int slot) {
     int64_t tt = (w0 >> 4) + t;  // tile index (uniform)
     tt = tt < ntile_all ? tt : ntile_all - 1;
@@ -1705,9 +1706,17 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   // wave so each summary tile feeds 4 MFMA row-sets.
   if (decode_shaped(n_queries)) {
     ProfScope prof_("k_score_decode", s);
-    const dim3 grid((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries);
-    if (cm.bt) hipLaunchKernelGGL(k_score_dec<true>, grid, dim3(256), 0, s, sa);
-    else hipLaunchKernelGGL(k_score_dec<false>, grid, dim3(256), 0, s, sa);
+    // short contexts: ranges of kDecRangeShort regions, so that even one
+    // query's few thousand regions spread over tens of blocks
+    if (max_regions <= kDirectMax) {
+      const dim3 grid((max_regions + kDecRangeShort - 1) / kDecRangeShort, kGroups, n_queries);
+      if (cm.bt) hipLaunchKernelGGL((k_score_dec<true, kDecRangeShort>), grid, dim3(256), 0, s, sa);
+      else hipLaunchKernelGGL((k_score_dec<false, kDecRangeShort>), grid, dim3(256), 0, s, sa);
+    } else {
+      const dim3 grid((max_regions + kDecRange - 1) / kDecRange, kGroups, n_queries);
+      if (cm.bt) hipLaunchKernelGGL((k_score_dec<true, kDecRange>), grid, dim3(256), 0, s, sa);
+      else hipLaunchKernelGGL((k_score_dec<false, kDecRange>), grid, dim3(256), 0, s, sa);
+    }
   } else {
     ProfScope prof_("k_score_prefill", s);
     const int ranges = (max_regions + kScoreRange - 1) / kScoreRange;
