@@ -1742,10 +1742,13 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   {
     ProfScope prof_("k_select", s);
     const dim3 grid((unsigned)((int64_t)n_queries * kGroups));
-    if (!tiled_select(max_regions))  // (+ one block per query for the folded compression)
-      hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>),
-                         dim3((unsigned)((int64_t)n_queries * (kGroups + (fold_in_select ? 1 : 0)))), dim3(kPreNT),
-                         0, s, se);
+    if (!tiled_select(max_regions)) {  // (+ one block per query for the folded compression)
+      const dim3 g2((unsigned)((int64_t)n_queries * (kGroups + (fold_in_select ? 1 : 0))));
+      if (max_regions <= 4 * kPreNT)  // short problems: 4 score slots per thread instead of 32
+        hipLaunchKernelGGL((k_select_pre<kPreNT, 4>), g2, dim3(kPreNT), 0, s, se);
+      else
+        hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>), g2, dim3(kPreNT), 0, s, se);
+    }
     else if (w.hist) {
       const int64_t folds = fold_in_select ? ((int64_t)n_queries * kGroups + kDecNT / 64 - 1) / (kDecNT / 64) : 0;
       hipLaunchKernelGGL(k_select_dec, dim3((unsigned)((int64_t)n_queries * kGroups + folds)), dim3(kDecNT), 0, s,
