@@ -41,10 +41,6 @@ constexpr int kPreSlot = 4096 + 4 * 256;  // one summary tile in the block's LDS
 #endif
 constexpr int kTile = 16;          // regions per MFMA tile
 constexpr int kHistBins = 4096;    // level-0 digit: key bits 31..20
-#ifndef DSA_HIST_COPIES
-#define DSA_HIST_COPIES 4
-#endif
-constexpr int kHistCopies = DSA_HIST_COPIES;  // decode histogram stripes (by score block index)
 constexpr int kSelCap = 4096;      // LDS candidate capacity of the radix fallback
 constexpr int kCandCap = 2048;     // decode candidates at or above the level-0 digit
 constexpr int kDirectMax = 8192;   // longest problem selected straight from its scores
@@ -60,8 +56,6 @@ struct ScoreArgs {
   float* scores;        // workspace [Nq][G][ws_stride]
   float* scores_out;    // nullable [Nq][G][max_regions]
   uint32_t* tilemax;    // nullable workspace [Nq][G][tm_stride]: largest key of each 16-region tile
-  uint32_t* hist;       // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts, added to
-                        // whatever is there (k_select_dec clears it after reading)
   CacheMap cm;          // where the sequences' summaries live (cm.R regions each)
   int32_t nq, n_seqs, max_regions, ws_stride, tm_stride, topk;
 };
@@ -196,8 +190,6 @@ constexpr int kDecDepth = DSA_SCORE_DEC_DEPTH;  // tiles in flight per wave
 // of summary loads in flight; A holds the query's 4 heads of group g in rows
 // 0..3.  Lanes 0..15 turn MFMA rows 0..3 into the region's score and store
 // it; the tile's largest key is reduced over those 16 lanes and stored too.
-// When a.hist is set, the level-0 digits of the scores are counted in LDS
-// and added to one stripe of the (query, group) histogram at the end.
 template <bool PAGED, int RANGE>
 __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   const int g = blockIdx.y;
@@ -205,9 +197,6 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kb = lane >> 4;
-  __shared__ uint32_t hist_lds[kHistBins];
-  if (a.hist)
-    for (int i = threadIdx.x; i < kHistBins; i += 256) hist_lds[i] = 0;
 
   constexpr int kWaveRegions = RANGE / 4;
   const int64_t w0 = (int64_t)blockIdx.x * RANGE + (int64_t)wave * kWaveRegions;
@@ -291,7 +280,6 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
         scores[r] = sv;
         if (scores_out) scores_out[r] = sv;
         key = score_key(sv);
-        if (a.hist) atomicAdd(&hist_lds[key >> 20], 1u);
       }
       if (tmax) {
         key = max(key, (uint32_t)__shfl_xor((int)key, 8));
@@ -300,16 +288,6 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
         key = max(key, (uint32_t)__shfl_xor((int)key, 1));
         if (lane == 0) tmax[t] = key;
       }
-    }
-  }
-  if (a.hist) {
-    __syncthreads();
-    // striping the flush by block index spreads same-bin atomics of the
-    // problem's blocks over kHistCopies counters
-    uint32_t* gh = a.hist + (pq * kHistCopies + (blockIdx.x % kHistCopies)) * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) {
-      const uint32_t v = hist_lds[i];
-      if (v) atomicAdd(gh + i, v);
     }
   }
 }
@@ -585,7 +563,6 @@ struct SelectArgs {
   float* cscale;
   int32_t n_seqs;
   const uint32_t* tilemax;  // [Nq][G][tm_stride] largest key per 16-region tile, or nullptr
-  uint32_t* hist;           // decode: [Nq][G][kHistCopies][kHistBins] level-0 digit counts (cleared after use)
   const int32_t* qpos;
   int32_t* sel;             // [Nq][G][topk]
   int32_t* nsel;            // [Nq][G]
@@ -1094,13 +1071,17 @@ struct alignas(16) DecSmem {
   uint32_t wtot[kDecNT / 64];
   uint32_t res[4];
   uint32_t tab[kDecTilesPT * (kDecNT / 64) + 1];  // ordered positions of the tiles, then of the final pass
-  union {
+  union alignas(16) {
     int32_t tiles[kCandCap];  // kept tiles (step 2)
     uint32_t hh[1024];        // 10-bit digit histogram of the finishing wave (step 3)
   };
   uint32_t ck[kCandCap];      // candidate keys, index order
   int32_t ci[kCandCap];       // candidate regions
-  uint32_t kin[kCandCap];     // keys in the level-0 digit, any order
+  union alignas(16) {
+    uint32_t hdig[kHistBins];  // level-0 digit counts: tile maxima (step 1), candidates (step 2)
+    uint32_t kin[kCandCap];    // keys in the boundary digit, any order (step 3)
+  };
+  uint32_t n_in;
   uint32_t stage[kTile][kDecNT];  // each thread's 16 tile keys (a column per thread)
 };
 
@@ -1148,16 +1129,20 @@ __device__ __forceinline__ uint32_t wave_digit(const uint32_t* kin, uint32_t n, 
 }
 
 // Decode selection, one block per (query, group), on what k_score_dec left:
-// the scores, each tile's largest key and the level-0 digit histogram.
-//  1. The histogram gives the digit d holding the need-th largest key, the
-//     count above it and the count in it.
-//  2. Tiles whose largest key has a digit >= d hold every region at or above
-//     d; they are compacted in index order, and their regions at or above d
-//     (the candidates, exactly above + in-digit of them) too.
+// the scores and each 16-region tile's largest key.
+//  1. A histogram of the tile maxima's level-0 digits (12 bits) gives the
+//     digit d0 of the need-th largest tile maximum.  The need largest tile
+//     maxima are need different scores, so the need-th largest score is at
+//     least T0 = d0 << 20, the lowest key of that digit: every region to
+//     select lies in a tile whose maximum reaches T0, with a key >= T0.
+//  2. Those tiles are compacted in index order, and their regions with keys
+//     >= T0 (the candidates) too, while the candidates' digits are counted;
+//     the counts give the digit d holding the need-th largest candidate, the
+//     number of candidates above it and in it.
 //  3. One wave finds the need-th largest key from the keys inside digit d
 //     (two 10-bit rounds) and writes the selection in index order.
-// Problems with more candidates than kCandCap or more tiles than the block
-// holds use the radix fallback.
+// Problems with more kept tiles or candidates than kCandCap, or more tiles
+// than the block holds, use the radix fallback.
 __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   const int64_t pq = blockIdx.x;
   const int qi = (int)(pq / kGroups);
@@ -1170,19 +1155,9 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   }
   // Every load that needs only the block index is issued before any of them
   // is waited for: the query's position first (so that waiting for it leaves
-  // the others in flight), then the hint and the tile maxima.
+  // the others in flight), then every tile maximum the block can hold (tiles
+  // past the problem are masked below).
   const int32_t qraw = *(a.qpos ? a.qpos + qi : a.slen + qi);  // (one load, no branch)
-  // The histogram is only a hint for the level-0 digit: it is read here and
-  // cleared for the next call on this workspace at every exit (global stores
-  // issued before a barrier would make the barrier wait for them), and the
-  // digit is checked against exact counts below.  Thread t holds digits
-  // 4095-4t..4092-4t.
-  u32x4 h = {0u, 0u, 0u, 0u};
-  uint32_t* const gh = a.hist + pq * kHistCopies * kHistBins + (kHistBins - 4 - 4 * tid);
-#pragma unroll
-  for (int k = 0; k < kHistCopies; ++k) h += *(const u32x4*)(gh + k * kHistBins);
-  // every tile maximum the block can hold, loaded with the hint (they do not
-  // wait for the query's position; tiles past the problem are masked below)
   const uint32_t* tm = a.tilemax + pq * a.tm_stride;
   uint32_t tk[kDecTilesPT];
 #pragma unroll
@@ -1190,67 +1165,73 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     const int64_t j = (int64_t)e * kDecNT + tid;
     tk[e] = tm[j < a.tm_stride ? j : 0];
   }
-#define DSA_CLEAR_HINT()                                                                  \
-  do {                                                                                    \
-    _Pragma("unroll") for (int k = 0; k < kHistCopies; ++k) *(u32x4*)(gh + k * kHistBins) = \
-        u32x4{0u, 0u, 0u, 0u};                                                            \
-  } while (0)
-  // 1. level-0 digit from the histogram: the hint's wave totals go to LDS
-  // before anything depends on the position, so the loads above stay issued
-  // together (the LDS barrier keeps them before it and does not wait for the
-  // tile maxima)
-  const uint32_t cnt[4] = {h.w, h.z, h.y, h.x};
-  const uint32_t mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-  const uint32_t wi = wave_incl_scan(mine);
-  if (lane == 63) sm.wtot[w] = wi;
+  static_assert(kHistBins == 4 * kDecNT, "thread t owns digits 4095-4t .. 4092-4t");
+  *(u32x4*)&sm.hdig[4 * tid] = u32x4{0u, 0u, 0u, 0u};
+  if (tid == 0) sm.n_in = 0;
+  // The digit holding the need-th largest of the counted keys (digits from
+  // the top, thread t owning digits 4095-4t .. 4092-4t): its value, the count
+  // of keys above it and in it in sm.res[0..2] (res[0] = ~0 when fewer than
+  // need keys were counted).  Ends with a barrier; sm.res[0] must be ~0 on
+  // entry, and sm.wtot is overwritten.
+  auto boundary_digit = [&](uint32_t need_) {
+    const u32x4 h = *(const u32x4*)&sm.hdig[kHistBins - 4 - 4 * tid];
+    const uint32_t cnt[4] = {h.w, h.z, h.y, h.x};
+    const uint32_t mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    const uint32_t wi = wave_incl_scan(mine);
+    if (lane == 63) sm.wtot[w] = wi;
+    lds_barrier();
+    uint32_t run = wi - mine;
+#pragma unroll
+    for (int i = 0; i < kDecNT / 256; ++i) {
+      const u32x4 v = *(const u32x4*)&sm.wtot[4 * i];
+      run += (4 * i < w ? v.x : 0u) + (4 * i + 1 < w ? v.y : 0u) + (4 * i + 2 < w ? v.z : 0u) +
+             (4 * i + 3 < w ? v.w : 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run < need_ && run + cnt[j] >= need_) {
+        sm.res[0] = (uint32_t)(kHistBins - 1 - 4 * tid - j);
+        sm.res[1] = run;
+        sm.res[2] = cnt[j];
+      }
+      run += cnt[j];
+    }
+    lds_barrier();
+  };
   if (tid == 0) sm.res[0] = 0xFFFFFFFFu;
-  lds_barrier();
+  lds_barrier();  // (the histogram cleared)
   const int64_t c = current_region(a.qpos ? qraw : qraw - 1, a.cm.R, a.max_regions);
   const uint32_t need = (uint32_t)((c < (int64_t)(a.topk - 1)) ? c : (int64_t)(a.topk - 1));
   int32_t* sel = a.sel + pq * a.topk;
-  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kDecNT)) {
-    DSA_CLEAR_HINT();
-    return;
-  }
+  if (select_trivial(c, need, sel, a.nsel + pq, a.topk, kDecNT)) return;
   const int64_t ntiles = (c + kTile - 1) / kTile;
   if (ntiles > (int64_t)kDecNT * kDecTilesPT) {
-    DSA_CLEAR_HINT();
     select_fallback<kDecNT>(a, pq);
     return;
   }
 #pragma unroll
-  for (int e = 0; e < kDecTilesPT; ++e)
+  for (int e = 0; e < kDecTilesPT; ++e) {
     if ((int64_t)e * kDecNT + tid >= ntiles) tk[e] = 0u;
-  uint32_t run = wi - mine;
-#pragma unroll
-  for (int i = 0; i < kDecNT / 256; ++i) {
-    const u32x4 v = *(const u32x4*)&sm.wtot[4 * i];
-    run += (4 * i < w ? v.x : 0u) + (4 * i + 1 < w ? v.y : 0u) + (4 * i + 2 < w ? v.z : 0u) +
-           (4 * i + 3 < w ? v.w : 0u);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (run < need && run + cnt[j] >= need) {
-      sm.res[0] = (uint32_t)(kHistBins - 1 - 4 * tid - j);
-      sm.res[1] = run;
-      sm.res[2] = cnt[j];
-    }
-    run += cnt[j];
+    else atomicAdd(&sm.hdig[tk[e] >> 20], 1u);
   }
   lds_barrier();
-  const uint32_t d = sm.res[0], above_h = sm.res[1], inbin_h = sm.res[2];
-  if (d == 0xFFFFFFFFu || above_h + inbin_h > (uint32_t)kCandCap) {
-    DSA_CLEAR_HINT();
+  // 1. the digit of the need-th largest tile maximum
+  boundary_digit(need);
+  const uint32_t d0 = sm.res[0];
+  if (d0 == 0xFFFFFFFFu) {  // (fewer than need tiles hold a score: not on the tile path)
     select_fallback<kDecNT>(a, pq);
     return;
   }
-  const uint32_t Tlo = d << 20;
+  const uint32_t T0 = d0 << 20;
+  // the histogram again, for the candidates' digits (the kept-tile
+  // compaction below passes barriers before any candidate is counted)
+  *(u32x4*)&sm.hdig[4 * tid] = u32x4{0u, 0u, 0u, 0u};
   // 2. kept tiles, then the candidates in them
   {
     bool f[kDecTilesPT];
     uint32_t pos[kDecTilesPT];
 #pragma unroll
-    for (int e = 0; e < kDecTilesPT; ++e) f[e] = tk[e] >= Tlo && (int64_t)e * kDecNT + tid < ntiles;
+    for (int e = 0; e < kDecTilesPT; ++e) f[e] = tk[e] >= T0 && (int64_t)e * kDecNT + tid < ntiles;
     ordered_positions<kDecNT, kDecTilesPT>(f, pos, sm.tab);
 #pragma unroll
     for (int e = 0; e < kDecTilesPT; ++e)
@@ -1259,15 +1240,15 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
   const uint32_t ntl_all = sm.tab[kDecTilesPT * (kDecNT / 64)];
   const uint32_t ntl = min(ntl_all, (uint32_t)kCandCap);
   lds_barrier();
+  if (tid == 0) sm.res[0] = 0xFFFFFFFFu;  // (d0 was read before the barriers above)
   // The kept tiles in rounds of one tile per thread (round rd: kept tiles
   // rd*kDecNT + tid, so the rounds follow index order): a tile's 16 scores in
-  // one 64-byte row, the candidates among them (and those inside digit d)
-  // counted, a block scan of the counts in thread order (= index order), and
-  // the candidates written to LDS in index order after those of earlier
-  // rounds.
+  // one 64-byte row, the candidates among them counted, a block scan of the
+  // counts in thread order (= index order), and the candidates written to
+  // LDS in index order after those of earlier rounds.
   constexpr int kCandRounds = kCandCap / kDecNT;
   static_assert(kCandCap == kCandRounds * kDecNT, "whole rounds of one kept tile per thread");
-  uint32_t ncand = 0, nin = 0;
+  uint32_t ncand = 0;
   for (int rd = 0; rd < kCandRounds; ++rd) {
     if ((uint32_t)rd * kDecNT >= ntl) break;  // (uniform: ntl is the same for every thread)
     const uint32_t ti = (uint32_t)rd * kDecNT + tid;
@@ -1277,7 +1258,7 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     u32x4 q4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) q4[j] = tp[j];
-    uint32_t key[kTile], fa = 0u, fb = 0u;
+    uint32_t key[kTile], fa = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       key[4 * j + 0] = score_key(__uint_as_float(q4[j].x));
@@ -1289,16 +1270,14 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     for (int i = 0; i < kTile; ++i) sm.stage[i][tid] = key[i];
 #pragma unroll
     for (int i = 0; i < kTile; ++i) {
-      const bool ok = have && t * kTile + i < c && key[i] >= Tlo;
+      const bool ok = have && t * kTile + i < c && key[i] >= T0;
       fa |= (ok ? 1u : 0u) << i;
-      fb |= (ok && (key[i] >> 20) == d ? 1u : 0u) << i;
     }
-    // both counts in one word: each round's total is at most 16 * kDecNT < 2^16
-    const uint32_t packed = ((uint32_t)__popc(fa) << 16) | (uint32_t)__popc(fb);
-    const uint32_t incl = wave_incl_scan(packed);
+    const uint32_t cntc = (uint32_t)__popc(fa);
+    const uint32_t incl = wave_incl_scan(cntc);
     if (lane == 63) sm.wtot[w] = incl;
     lds_barrier();
-    uint32_t base = incl - packed, total = 0;
+    uint32_t base = incl - cntc, total = 0;
 #pragma unroll
     for (int i = 0; i < kDecNT / 256; ++i) {
       const u32x4 v = *(const u32x4*)&sm.wtot[4 * i];
@@ -1308,31 +1287,38 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     }
     // the thread's keys go through its own LDS column so that the loop over
     // its candidates (about one) can index them
-    uint32_t oa = ncand + (base >> 16), ob = nin + (base & 0xFFFFu);
+    uint32_t oa = ncand + base;
     for (uint32_t m = fa; m; m &= m - 1u, ++oa) {
       const int i = __ffs((int)m) - 1;
       const uint32_t k = sm.stage[i][tid];
       if (oa < (uint32_t)kCandCap) {
         sm.ck[oa] = k;
         sm.ci[oa] = (int32_t)(t * kTile + i);
-      }
-      if ((fb >> i) & 1u) {
-        if (ob < (uint32_t)kCandCap) sm.kin[ob] = k;
-        ++ob;
+        atomicAdd(&sm.hdig[k >> 20], 1u);
       }
     }
-    ncand += total >> 16;
-    nin += total & 0xFFFFu;
+    ncand += total;
     lds_barrier();  // (the next round rewrites sm.wtot)
   }
-  // exact check of the digit: ncand keys are >= Tlo and nin of them in digit d
-  const uint32_t above = ncand - nin;
-  if (ntl_all > (uint32_t)kCandCap || ncand > (uint32_t)kCandCap || above >= need || ncand < need) {
-    DSA_CLEAR_HINT();
+  if (ntl_all > (uint32_t)kCandCap || ncand > (uint32_t)kCandCap || ncand < need) {
     select_fallback<kDecNT>(a, pq);
     return;
   }
-  // (the last round's barrier made the candidates visible)
+  // the candidates' boundary digit, then the keys inside it gathered for
+  // the finishing wave (two per thread)
+  boundary_digit(need);
+  const uint32_t d = sm.res[0], above = sm.res[1];
+  static_assert(kCandCap == 2 * kDecNT, "two candidates per thread");
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t j = (uint32_t)e * kDecNT + tid;
+    if (j < ncand) {
+      const uint32_t k = sm.ck[j];
+      if ((k >> 20) == d) sm.kin[atomicAdd(&sm.n_in, 1u)] = k;
+    }
+  }
+  lds_barrier();
+  const uint32_t nin = sm.n_in;
   // 3. wave 0: the need-th largest key T lies in digit d; its next 10 bits,
   // then its last 10, from histograms of the in-digit keys
   const uint32_t M = min(ncand, (uint32_t)kCandCap);
@@ -1369,15 +1355,12 @@ __global__ __launch_bounds__(kDecNT) void k_select_dec(SelectArgs a) {
     else if (fe[e] && pe[e] < need_eq) pos = pg[e] + pe[e];
     if (pos < need) sel[pos] = sm.ci[(uint32_t)e * kDecNT + tid];
   }
-  // the forced current region, the padding and the count (after the last
-  // barrier, like the hint's clearing)
+  // the forced current region, the padding and the count
   for (int i = (int)need + 1 + tid; i < a.topk; i += kDecNT) sel[i] = -1;
   if (tid == 0) {
     sel[need] = (int32_t)c;
     a.nsel[pq] = (int32_t)need + 1;
   }
-  DSA_CLEAR_HINT();
-#undef DSA_CLEAR_HINT
 }
 
 
@@ -1623,17 +1606,16 @@ static bool decode_shaped(int32_t n_queries) { return n_queries < 64; }
 static bool tiled_select(int32_t max_regions) { return max_regions > kDirectMax; }
 static int64_t tm_stride_of(int32_t max_regions) { return ((int64_t)max_regions / kTile + 1 + 63) / 64 * 64; }
 
-// Decode-shaped problems long enough for the tile path also get the level-0
-// histogram from the score kernel.
-static bool hist_select(int32_t n_queries, int32_t max_regions) {
+// Decode-shaped problems long enough for the tile path: one selection block
+// of kDecNT threads per (query, group).
+static bool dec_select(int32_t n_queries, int32_t max_regions) {
   return decode_shaped(n_queries) && tiled_select(max_regions);
 }
 
 struct ScoreWs {
-  uint32_t* hist;
   uint32_t* tilemax;
   float* scores;
-  size_t hist_bytes, bytes;
+  size_t bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1643,13 +1625,6 @@ static ScoreWs score_ws_layout(void* base, int32_t nq, int32_t max_regions) {
   char* p = (char*)base;
   const size_t np = (size_t)nq * kGroups;
   size_t off = 0;
-  w.hist = nullptr;
-  w.hist_bytes = 0;
-  if (hist_select(nq, max_regions)) {
-    w.hist = (uint32_t*)(p + off);
-    w.hist_bytes = align256(np * kHistCopies * kHistBins * 4);
-    off += w.hist_bytes;
-  }
   w.tilemax = nullptr;
   if (tiled_select(max_regions)) {
     w.tilemax = (uint32_t*)(p + off);
@@ -1685,18 +1660,18 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
   const int32_t stride = (int32_t)ws_stride_of(max_regions);
   ScoreArgs sa;
   sa.iq = index_q; sa.z = z; sa.qseq = q_seq; sa.qpos = q_pos; sa.slen = seq_len; sa.summ = summ; sa.scale = scale;
-  sa.scores = w.scores; sa.scores_out = scores_out; sa.tilemax = w.tilemax; sa.hist = w.hist;
+  sa.scores = w.scores; sa.scores_out = scores_out; sa.tilemax = w.tilemax;
   sa.cm = cm; sa.nq = n_queries; sa.n_seqs = n_seqs; sa.max_regions = max_regions;
   sa.ws_stride = stride; sa.tm_stride = (int32_t)tm_stride_of(max_regions); sa.topk = geom->topk;
   SelectArgs se;
-  se.scores = w.scores; se.slen = seq_len; se.tilemax = w.tilemax; se.hist = w.hist; se.qpos = q_pos;
+  se.scores = w.scores; se.slen = seq_len; se.tilemax = w.tilemax; se.qpos = q_pos;
   se.ik = index_k; se.csumm = csumm; se.cscale = cscale; se.n_seqs = n_seqs;
   se.sel = sel; se.nsel = n_sel; se.cm = cm; se.nq = n_queries; se.max_regions = max_regions;
   se.ws_stride = stride; se.tm_stride = sa.tm_stride; se.topk = geom->topk;
   // the decode step's compression runs as extra blocks of the selection
   // launch (the decode one, or the short-context one), or as its own small
   // launch before the tile selection
-  const bool fold_in_select = index_k && (w.hist || !tiled_select(max_regions));
+  const bool fold_in_select = index_k && (dec_select(n_queries, max_regions) || !tiled_select(max_regions));
   if (index_k && !fold_in_select) {
     ProfScope prof_("k_compress", s);
     hipLaunchKernelGGL(k_fold_compress, dim3((unsigned)n_queries), dim3(256), 0, s, se);
@@ -1749,7 +1724,7 @@ static dsa_status launch_score_topk(const dsa_geometry* geom, int32_t n_queries,
       else
         hipLaunchKernelGGL((k_select_pre<kPreNT, kDirectMax / kPreNT>), g2, dim3(kPreNT), 0, s, se);
     }
-    else if (w.hist) {
+    else if (dec_select(n_queries, max_regions)) {
       const int64_t folds = fold_in_select ? ((int64_t)n_queries * kGroups + kDecNT / 64 - 1) / (kDecNT / 64) : 0;
       hipLaunchKernelGGL(k_select_dec, dim3((unsigned)((int64_t)n_queries * kGroups + folds)), dim3(kDecNT), 0, s,
                          se);
@@ -1911,9 +1886,8 @@ extern "C" dsa_status dsa_decode_step_fp8_paged(const dsa_geometry* geom, int32_
 // GPU the library runs on holds its own copy at its own address, found once
 // per device with hipGetSymbolAddress and kept; the array's name is never
 // used as a device address on the host.  The decode step's workspace holds no
-// state that must start at zero: the digit histogram in it is only a hint
-// (checked against exact counts, cleared by every call), and every partial
-// result is written before it is read.  Calls that overlap on one GPU share
+// state that must start at zero: every partial result in it is written
+// before it is read.  Calls that overlap on one GPU share
 // the array and race.
 // ---------------------------------------------------------------------------
 namespace dsa {

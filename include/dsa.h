@@ -243,14 +243,10 @@ size_t dsa_score_topk_workspace_size(const dsa_geometry* geom, int32_t n_queries
  *   workspace device buffer of at least dsa_score_topk_workspace_size() bytes
  * Scores are fp32 (bf16 x E4M3 products, fp32 accumulation); on equal fp32
  * scores the lower index wins; a NaN score ranks below every number.
- * The workspace holds the fp32 scores, when max_regions > 8192 the largest
- * score of every 16-region tile, and for decode-shaped calls (n_queries < 64,
- * max_regions > 8192) a digit histogram that guides the selection.  Results
- * never depend on the workspace contents on entry: the histogram is checked
- * against exact counts and the selection falls back to an exact radix pass
- * when it does not fit.  Each call leaves the histogram cleared, so decode
- * calls after the first on one workspace (or the first on a zero-filled one)
- * take the fast path.  Calls sharing a workspace must not overlap.
+ * The workspace holds the fp32 scores and, when max_regions > 8192, the
+ * largest score of every 16-region tile.  Every byte of it is written before
+ * it is read, so results never depend on its contents on entry.  Calls
+ * sharing a workspace must not overlap.
  */
 dsa_status dsa_score_topk(const dsa_geometry* geom, int32_t n_queries, const uint16_t* index_q,
                           const float* z, const int32_t* q_seq, const int32_t* q_pos,
@@ -358,7 +354,7 @@ dsa_status dsa_decode_step(const dsa_geometry* geom, int32_t batch, const uint16
  * bit-identical to dsa_decode_step.  Its workspace is a static 64 MiB device
  * area of the library; each GPU holds its own copy until the process ends.
  * Shapes whose dsa_decode_step_workspace_size() exceeds 64 MiB (e.g. batch 4
- * at 1M tokens needs 15.6 MiB, batch 16 at 128K 32.8 MiB) return
+ * at 1M tokens needs 14.6 MiB, batch 16 at 128K 28.8 MiB) return
  * DSA_ERR_UNSUPPORTED.  `stream` must belong to the current device; the
  * first call on a device resolves the area's address there (make it outside
  * stream capture).  The call allocates and frees nothing.  Every call on one

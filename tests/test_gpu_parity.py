@@ -118,10 +118,9 @@ def test_decode_beyond_tile_capacity_uses_radix_fallback():
 
 
 def test_decode_selection_does_not_depend_on_workspace_contents():
-    """The digit histogram kept in the workspace only guides the decode selection: a workspace full
-    of random bytes gives the same selection (the digit fails its exact check and the radix fallback
-    runs), the call leaves the histogram cleared, and the next call on that workspace, which takes
-    the fast path, agrees too."""
+    """The decode selection reads only what the score kernel of the same call wrote into the
+    workspace (scores and tile maxima): a workspace full of random bytes gives the same selection as
+    a zeroed one, on the first call and on the next call over the same bytes."""
     seed, lens = 0xDA, [131072, 100003, 70001]
     B, tcap = len(lens), H.round128(max(lens))
     R = tcap // 8

@@ -50,7 +50,7 @@ def _same(x, y):
 
 
 def test_noalloc_decode_step_matches_the_workspace_call_twice_in_a_row():
-    # first call: the 1M-token batch-4 shape (16 MiB of scratch, tile selection with the histogram hint)
+    # first call: the 1M-token batch-4 shape (15 MiB of scratch, decode tile selection)
     big = _inputs(0x0A1, [1 << 20] * 4, planted=True)
     ref1 = _run(big, noalloc=False)
     got1 = _run(big, noalloc=True)
