@@ -581,10 +581,8 @@ def setup_swa(seed, layer, n_seqs, p0, n_new, geom):
     gp = ctypes.byref(geom)
     a_att = (gp, W, n_seqs, n_new, p(pos0), p(row0), p(q), p(kn), p(vn), p(kr), p(vr), p(out), p(ws), ws.numel())
     a_app = (gp, W, n_seqs, n_new, p(pos0), p(row0), p(kn), p(vn), p(kr), p(vr))
-    wsd = dsa.workspace(dsa.swa_decode_step_workspace_size(geom, W, n_seqs))
-    a_dec = (gp, W, n_seqs, p(pos0), p(q), p(kn), p(vn), p(kr), p(vr), p(out), p(wsd), wsd.numel()) \
-        if n_new == 1 else None
-    return a_att, a_app, a_dec, (kr, vr, kn, vn, q, out, pos0, row0, ws, wsd)
+    a_dec = (gp, W, n_seqs, p(pos0), p(q), p(kn), p(vn), p(kr), p(vr), p(out)) if n_new == 1 else None
+    return a_att, a_app, a_dec, (kr, vr, kn, vn, q, out, pos0, row0, ws)
 
 
 def setup_mix(cfg):

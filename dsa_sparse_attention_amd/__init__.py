@@ -36,7 +36,7 @@ ENTRY_POINTS = [
     "dsa_cache_write_fp8_paged", "dsa_sparse_gqa_decode_fp8_paged", "dsa_sparse_gqa_prefill_fp8_paged",
     "dsa_decode_step_fp8_paged", "dsa_sparse_gqa_prefill_merged", "dsa_sparse_gqa_prefill_merged_paged",
     "dsa_rope_config_default", "dsa_indexer_workspace_size", "dsa_indexer_project", "dsa_rope_qk",
-    "dsa_decode_step_noalloc", "swa_decode_step", "swa_decode_step_workspace_size",
+    "dsa_decode_step_noalloc", "swa_decode_step",
 ]
 
 
@@ -129,9 +129,7 @@ def load() -> ctypes.CDLL:
     L.swa_attention_workspace_size.restype = sz
     L.swa_attention.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.swa_ring_append.argtypes = [G, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
-    L.swa_decode_step.argtypes = [G, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.swa_decode_step_workspace_size.argtypes = [G, i32, i32]
-    L.swa_decode_step_workspace_size.restype = sz
+    L.swa_decode_step.argtypes = [G, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     P = ctypes.POINTER(PageTable)
     L.dsa_cache_write_paged.argtypes = [G, i32, vp, vp, vp, vp, vp, P, i32, vp, vp, vp, vp]
     L.dsa_compress_regions_paged.argtypes = [G, i32, P, vp, vp, vp, i32, vp, vp, vp]
@@ -211,9 +209,8 @@ def _stream(stream):
 
 
 def workspace(nbytes: int, device=None) -> torch.Tensor:
-    """A zero-filled, 256-byte aligned device buffer (uint8) of at least nbytes.  Zero fill only
-    matters for speed: dsa_score_topk's first decode call on a workspace that is not cleared takes
-    the exact fallback selection."""
+    """A zero-filled, 256-byte aligned device buffer (uint8) of at least nbytes (no entry point
+    depends on the contents of its workspace on entry)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
 
 
@@ -444,11 +441,7 @@ def swa_ring_append(geom, window, max_new_per_seq, seq_pos0, seq_row0, k_new, v_
                                   _stream(stream)))
 
 
-def swa_decode_step_workspace_size(geom, window, n_seqs) -> int:
-    return int(load().swa_decode_step_workspace_size(ctypes.byref(geom), window, n_seqs))
-
-
-def swa_decode_step(geom, window, seq_pos, q, k_new, v_new, k_ring, v_ring, out, workspace=None, stream=None):
+def swa_decode_step(geom, window, seq_pos, q, k_new, v_new, k_ring, v_ring, out, stream=None):
     """Sliding-window decode (one new token per sequence, row s) followed by the ring append."""
     n_seqs = seq_pos.numel()
     _dt(seq_pos, torch.int32, "seq_pos")
@@ -460,11 +453,8 @@ def swa_decode_step(geom, window, seq_pos, q, k_new, v_new, k_ring, v_ring, out,
     _numel_at_least(v_new, n_seqs * GROUPS * HEAD_DIM, "v_new")
     _numel_at_least(q, n_seqs * Q_HEADS * HEAD_DIM, "q")
     _numel_at_least(out, n_seqs * Q_HEADS * HEAD_DIM, "out")
-    if workspace is None:
-        workspace = globals()["workspace"](swa_decode_step_workspace_size(geom, window, n_seqs), q.device)
     _check(load().swa_decode_step(ctypes.byref(geom), window, n_seqs, _ptr(seq_pos), _ptr(q), _ptr(k_new),
-                                  _ptr(v_new), _ptr(k_ring), _ptr(v_ring), _ptr(out), _ptr(workspace),
-                                  workspace.numel(), _stream(stream)))
+                                  _ptr(v_new), _ptr(k_ring), _ptr(v_ring), _ptr(out), _stream(stream)))
 
 
 # ---- paged caches ----------------------------------------------------------------------------

@@ -45,14 +45,19 @@ struct Region {
   int tn;
 };
 
-struct CoreState {
-  f32x4 o[12];
+// A wave's running state: O^T tiles (NT tiles of 16 channels), the lane's
+// reference max and partial denominator.
+template <int NT>
+struct CoreStateN {
+  f32x4 o[NT];
   float m, l;
 };
+using CoreState = CoreStateN<12>;
 
-__device__ __forceinline__ void core_init(CoreState& st) {
+template <int NT>
+__device__ __forceinline__ void core_init(CoreStateN<NT>& st) {
 #pragma unroll
-  for (int i = 0; i < 12; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NT; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.0f;
 }
@@ -68,19 +73,22 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int64_t qrow, int g, b
 // The 4-region chunk as held in registers between its loads and its use:
 // K rows of tile 0 and tile 1 (lane: one token, 48 channels) and the 12
 // V^T operands (lane: one channel, the 8 tokens of region kb), plus the valid
-// position range of the lane's softmax region.
-struct ChunkRegs {
-  u32x4 k0[6], k1[6], v[12];
+// position range of the lane's softmax region.  NT < 12: the V^T operands of
+// NT tiles only (16*NT channels from Region::v / Region::vn on).
+template <int NT>
+struct ChunkRegsN {
+  u32x4 k0[6], k1[6], v[NT];
   int lo, hi;
-  uint32_t vpatch[12];  // patched loads only: the new token's V (channel 16nt + n) and its slot
+  uint32_t vpatch[NT];  // patched loads only: the new token's V (channel 16nt + n) and its slot
   int tn;
 };
+using ChunkRegs = ChunkRegsN<12>;
 
 // Issues the chunk's loads. ra = region of this lane's K rows (entry n/4),
 // rb = region of this lane's softmax weights and V pack (entry kb).  PATCH:
 // Region::tn / kn / vn are honoured.
-template <bool PATCH = false>
-__device__ __forceinline__ void core_load(ChunkRegs& c, const Region& ra, const Region& rb) {
+template <bool PATCH = false, int NT = 12>
+__device__ __forceinline__ void core_load(ChunkRegsN<NT>& c, const Region& ra, const Region& rb) {
   const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
   // region-tiled K: unit ((t*6 + s)*4 + kb)*4 + (n&3) holds token 4t + n%4,
   // channels 48kb + 8s .. +7
@@ -101,10 +109,10 @@ __device__ __forceinline__ void core_load(ChunkRegs& c, const Region& ra, const 
     }
   }
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) c.v[nt] = ld16(rb.v + (16 * nt + n) * 8);
+  for (int nt = 0; nt < NT; ++nt) c.v[nt] = ld16(rb.v + (16 * nt + n) * 8);
   if constexpr (PATCH) {  // the new token's V, put into element tn when the chunk is used
 #pragma unroll
-    for (int nt = 0; nt < 12; ++nt) c.vpatch[nt] = rb.vn[16 * nt + n];
+    for (int nt = 0; nt < NT; ++nt) c.vpatch[nt] = rb.vn[16 * nt + n];
     c.tn = rb.tn;
   }
   c.lo = rb.lo;
@@ -113,10 +121,11 @@ __device__ __forceinline__ void core_load(ChunkRegs& c, const Region& ra, const 
 
 // Puts the new token's V (patched loads) into element tn of the lane's V
 // units; nothing when tn < 0.
-__device__ __forceinline__ void core_apply_patch(ChunkRegs& c) {
+template <int NT>
+__device__ __forceinline__ void core_apply_patch(ChunkRegsN<NT>& c) {
   const int t = c.tn;
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const uint32_t x = c.vpatch[nt];
     const uint32_t keep = (t & 1) ? 0x0000FFFFu : 0xFFFF0000u, put = (t & 1) ? x << 16 : x;
     c.v[nt].x = (t >> 1 == 0) ? (c.v[nt].x & keep) | put : c.v[nt].x;
@@ -127,7 +136,9 @@ __device__ __forceinline__ void core_apply_patch(ChunkRegs& c) {
 }
 
 // S^T tiles, online softmax update, O^T += V^T P^T for one loaded chunk.
-__device__ __forceinline__ void core_compute(CoreState& st, const bf16x8 qb[6], ChunkRegs& c, float scale_log2) {
+template <int NT>
+__device__ __forceinline__ void core_compute(CoreStateN<NT>& st, const bf16x8 qb[6], ChunkRegsN<NT>& c,
+                                             float scale_log2) {
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 6; ++s) {
@@ -153,7 +164,7 @@ __device__ __forceinline__ void core_compute(CoreState& st, const bf16x8 qb[6], 
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 when st.m = -inf
     st.l *= alpha;
 #pragma unroll
-    for (int nt = 0; nt < 12; ++nt) st.o[nt] *= alpha;
+    for (int nt = 0; nt < NT; ++nt) st.o[nt] *= alpha;
     st.m = m_new;
   }
   const float m_use = st.m == -INFINITY ? 0.0f : st.m;  // all masked so far: weights stay 0
@@ -173,7 +184,7 @@ __device__ __forceinline__ void core_compute(CoreState& st, const bf16x8 qb[6], 
       mk[w] = (a0 ? 0x0000FFFFu : 0u) | (a1 ? 0xFFFF0000u : 0u);
     }
 #pragma unroll
-    for (int nt = 0; nt < 12; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       c.v[nt].x &= mk[0];
       c.v[nt].y &= mk[1];
       c.v[nt].z &= mk[2];
@@ -187,7 +198,7 @@ __device__ __forceinline__ void core_compute(CoreState& st, const bf16x8 qb[6], 
   pp.w = pack_bf16x2(p[6], p[7]);
   const bf16x8 pb = as_bf16x8(pp);
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) st.o[nt] = mfma16x16x32(as_bf16x8(c.v[nt]), pb, st.o[nt]);
+  for (int nt = 0; nt < NT; ++nt) st.o[nt] = mfma16x16x32(as_bf16x8(c.v[nt]), pb, st.o[nt]);
 }
 
 // One chunk, loads then compute (no overlap).  The scheduling barrier keeps
@@ -205,15 +216,15 @@ __device__ __forceinline__ void core_chunk(CoreState& st, const bf16x8 qb[6], co
 // registers (for kernels running several waves per SIMD, which overlap each
 // other's loads); DEPTH 1 and 2: one and two chunks' loads in flight while a
 // chunk computes (one wave per SIMD).
-template <int DEPTH, bool PATCH = false, class RegionOf>
-__device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int64_t n, const RegionOf& region_of,
+template <int DEPTH, bool PATCH = false, int NT = 12, class RegionOf>
+__device__ __forceinline__ void core_run(CoreStateN<NT>& st, const bf16x8 qb[6], int64_t n, const RegionOf& region_of,
                                          float scale_log2) {
   const int lane = threadIdx.x & 63, nn = lane & 15, kb = lane >> 4;
   if (n <= 0) return;
   if constexpr (DEPTH == 0) {
     // one chunk in registers per wave; several waves per SIMD overlap the loads
     for (int64_t e0 = 0; e0 < n; e0 += 4) {
-      ChunkRegs c;
+      ChunkRegsN<NT> c;
       core_load<PATCH>(c, region_of(e0 + (nn >> 2)), region_of(e0 + kb));
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (PATCH) core_apply_patch(c);
@@ -226,7 +237,7 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
   // the chunk being used and not the ones in flight behind it.
   if constexpr (DEPTH >= 2) {
   // three chunks in registers: two in flight while one computes
-  ChunkRegs b0, b1, b2;
+  ChunkRegsN<NT> b0, b1, b2;
   core_load<PATCH>(b0, region_of(nn >> 2), region_of(kb));
   core_load<PATCH>(b1, region_of(4 + (nn >> 2)), region_of(4 + kb));
   for (int64_t e0 = 0; e0 < n; e0 += 12) {
@@ -243,7 +254,7 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
     core_compute(st, qb, b2, scale_log2);
   }
   } else {
-  ChunkRegs b0, b1;
+  ChunkRegsN<NT> b0, b1;
   core_load<PATCH>(b0, region_of(nn >> 2), region_of(kb));
   for (int64_t e0 = 0; e0 < n; e0 += 8) {
     core_load<PATCH>(b1, region_of(e0 + 4 + (nn >> 2)), region_of(e0 + 4 + kb));
@@ -258,7 +269,8 @@ __device__ __forceinline__ void core_run(CoreState& st, const bf16x8 qb[6], int6
 }
 
 // Total softmax denominator of the lane's head (sum over the 4 kb lanes).
-__device__ __forceinline__ float core_total_l(const CoreState& st) {
+template <int NT>
+__device__ __forceinline__ float core_total_l(const CoreStateN<NT>& st) {
   return sum_across_rows(st.l);
 }
 
@@ -972,197 +984,196 @@ void k_swa_attend(SwaArgs a) {
   }
 }
 
-// Sliding-window decode, one new token per sequence, in two launches.  The
-// window's <= 65 regions form <= 17 chunks of 4; part block b of (sequence
-// s, group g) gives chunk kSwpWaves*b + w to its wave w, so a batch of 8
-// spreads its 136 chunks over 160 blocks instead of loading each window
-// through one compute unit.  The waves' partial (max, sum, O) merge through
-// LDS into one unnormalised record per part; k_swa_decode_merge then
-// combines the parts of each (sequence, group) in part order.  The current
-// region is the ring's with the new token patched in at load time.
-constexpr int kSwpWaves = 4;                                             // waves (chunks) per part
-constexpr int kSwpChunks = (kWindow / kRegion + 1 + 3) / 4;              // chunks a window spans
-constexpr int kSwpParts = (kSwpChunks + kSwpWaves - 1) / kSwpWaves;      // part blocks per (sequence, group)
-constexpr int kSwpRec = 2 * kHeadsPerGroup + kHeadsPerGroup * kHeadDim;  // floats per part: m, l, O[16][D]
-static_assert(kHeadsPerGroup == 16 && kHeadDim % 4 == 0, "part records hold 16 heads");
+// Sliding-window decode, one new token per sequence, in one launch.  The
+// window of position p (a = p/8, b = p mod 8) is exactly the ring's W/8
+// region slots: slot a mod (W/8) holds the current region's tokens at
+// offsets 0..b (the new token patched in at b when loaded) and, above b,
+// the window's first region's; every other slot holds a whole region of the
+// window.  Before the ring has filled (p < W - 1), slots 0..a hold the
+// window, slot a up to offset b.  So 16 waves take one 4-slot chunk each.
+// A block owns one (sequence, group) and the 16*NT output channels of slice
+// `slice`: every wave scores all 16 heads over the full 192 channels (the
+// same scores in every slice block) and accumulates P.V on its slice only,
+// and the 16 waves' partials combine in LDS.  Blocks go to the 8 XCDs round
+// robin by index, so the 12/NT slice blocks of one (sequence, group) are
+// placed on one XCD and share its L2 for K.
+// APPEND: slice 0 then writes the new token's K/V into the ring at slot p mod
+// W, offset b of region slot a mod (W/8), while other blocks may still read
+// that slot: their K rows of offset b come from the new token instead, and
+// the bytes of offset b in their V loads are replaced by the new token's, so
+// no value read from those bytes is used.
+constexpr int kSwdSlots = kWindow / kRegion;  // ring region slots = window regions
+static_assert(kSwdSlots % 4 == 0, "whole 4-slot chunks");
 
-__device__ __forceinline__ void swa_decode_window(const SwaArgs& a, int s, int64_t& p, int64_t& row,
-                                                  int64_t& rlo, int64_t& nreg) {
-  int64_t p0, r0, nnew;
-  seq_rows(a, s, p0, r0, nnew);
-  p = p0;
-  row = r0;
-  const int64_t lo = p - a.window + 1 < 0 ? 0 : p - a.window + 1;
-  rlo = lo / kRegion;
-  nreg = nnew > 0 ? p / kRegion - rlo + 1 : 0;
+// The chunk of ring slots 4w..4w+3 as wave w of a sliding-window decode
+// block holds it: every load is issued before the position is known (the
+// slots do not depend on it), the new token's K and V included; which token
+// is patched and which are masked is settled once the position arrives.
+template <int NT>
+struct SwdChunk {
+  ChunkRegsN<NT> c;
+  u32x4 kq[6];  // the new token's K, channels 48kb + 8s .. +7
+};
+
+template <int NT>
+__device__ __forceinline__ void swd_load(SwdChunk<NT>& x, const uint16_t* rk, const uint16_t* rv,
+                                         const uint16_t* knew, const uint16_t* vnew, int slot0) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const uint16_t* kp = rk + (int64_t)(slot0 + (n >> 2)) * kRegion * kHeadDim + (kb * 4 + (n & 3)) * 8;
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    x.c.k0[s] = ld16(kp + (s * 16) * 8);
+    x.c.k1[s] = ld16(kp + ((6 + s) * 16) * 8);
+  }
+  const uint16_t* vp = rv + (int64_t)(slot0 + kb) * kHeadDim * kRegion;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) x.c.v[nt] = ld16(vp + (16 * nt + n) * 8);
+#pragma unroll
+  for (int s = 0; s < 6; ++s) x.kq[s] = ld16(knew + 48 * kb + 8 * s);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) x.c.vpatch[nt] = vnew[16 * nt + n];
 }
 
-__global__ __launch_bounds__(64 * kSwpWaves) void k_swa_decode_part(SwaArgs a, float* part) {
-  const int b = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
+// Settles the chunk for position p (current slot cur, offset cb, region ca;
+// full: the ring holds the whole window): the new token replaces offset cb
+// of slot cur in K and V, slots past ca are empty until the ring has filled.
+template <int NT>
+__device__ __forceinline__ void swd_settle(SwdChunk<NT>& x, int slot0, int cur, int cb, int64_t ca, bool full) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  const int jk = slot0 + (n >> 2), jv = slot0 + kb;
+  const bool p0 = jk == cur && cb == (n & 3), p1 = jk == cur && cb == 4 + (n & 3);
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    x.c.k0[s] = p0 ? x.kq[s] : x.c.k0[s];
+    x.c.k1[s] = p1 ? x.kq[s] : x.c.k1[s];
+  }
+  x.c.tn = jv == cur ? cb : -1;
+  x.c.lo = (full || jv <= ca) ? 0 : 1;
+  x.c.hi = (full || jv < ca) ? 7 : (jv == ca ? cb : 0);
+  core_apply_patch(x.c);
+}
+
+template <int NT, int WV, bool APPEND>
+__global__ __launch_bounds__(64 * WV) void k_swa_decode(SwaArgs a, uint16_t* k_ring_w, uint16_t* v_ring_w) {
+  constexpr int kCpw = kSwdSlots / 4 / WV;  // chunks per wave
+  static_assert(kCpw * WV * 4 == kSwdSlots, "the waves cover the ring");
+  constexpr int kSlices = 12 / NT;
+  static_assert(kSlices * NT == 12, "slices of whole 16-channel tiles");
+  constexpr int kCh = 16 * NT;  // output channels per block
+  const int L = blockIdx.x, xcd = L & 7, k = L >> 3;
+  const int slice = k % kSlices;
+  const int64_t sg = (int64_t)(k / kSlices) * 8 + xcd;
+  if (sg >= (int64_t)a.n_seqs * kGroups) return;
+  const int s = (int)(sg / kGroups), g = (int)(sg % kGroups);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
-  __shared__ float sm_m[kSwpWaves][16], sm_l[kSwpWaves][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[kSwpWaves][16][kORow];
-  int64_t p, row, rlo, nreg;
-  swa_decode_window(a, s, p, row, rlo, nreg);
-  const int64_t nch = (nreg + 3) / 4;
-  if ((int64_t)b * kSwpWaves >= nch) return;  // (uniform) no chunk for this part: the merge skips it
+  __shared__ float sm_m[WV][16], sm_l[WV][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[WV][16][kCh + 4];
+  // the position first, then every load that does not depend on it
+  const int32_t praw = a.pos0[s];
+  int64_t row = s;
+  if (a.row0) {  // (swa_attention with one new row per sequence at most)
+    int64_t r0 = a.row0[s], r1 = a.row0[s + 1];
+    r0 = r0 < 0 ? 0 : (r0 > a.rows ? a.rows : r0);
+    r1 = r1 < r0 ? r0 : (r1 > a.rows ? a.rows : r1);
+    if (r1 <= r0) return;
+    row = r0;
+  }
   const int W = a.window;
-  const int64_t lo = p - W + 1 < 0 ? 0 : p - W + 1;
-  const int64_t sg = (int64_t)s * kGroups + g;
+  const int nslot = W / kRegion;
   const uint16_t* rk = a.k_ring + sg * W * kHeadDim;
-  const uint16_t* rv = a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion;
+  const uint16_t* rv = a.v_ring + sg * nslot * kHeadDim * kRegion + kCh * slice * kRegion;
   const uint16_t* knew = a.k_new + (row * kGroups + g) * kHeadDim;
-  const uint16_t* vnew = a.v_new + (row * kGroups + g) * kHeadDim;
+  const uint16_t* vnew = a.v_new + (row * kGroups + g) * kHeadDim + kCh * slice;
   bf16x8 qb[6];
   load_q(a.q, row, g, qb);
-  CoreState st;
+  SwdChunk<NT> x[kCpw];
+#pragma unroll
+  for (int j = 0; j < kCpw; ++j) swd_load(x[j], rk, rv, knew, vnew, 4 * (wave + WV * j));
+  // the append's copy of the new token (slice 0): K units for threads 0..23,
+  // V channels for threads 64..255
+  const int t = threadIdx.x;
+  const uint16_t* kn0 = a.k_new + (row * kGroups + g) * kHeadDim;
+  const uint16_t* vn0 = a.v_new + (row * kGroups + g) * kHeadDim;
+  u32x4 akv = {0u, 0u, 0u, 0u};
+  uint16_t avv = 0;
+  if (APPEND && slice == 0) {
+    if (t < kHeadDim / 8) akv = ld16(kn0 + 8 * t);
+    else if (t >= 64 && t < 64 + kHeadDim) avv = vn0[t - 64];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // (every load issued before any is waited for)
+  const int64_t p = praw < 0 ? 0 : praw;
+  const int64_t ca = p / kRegion;
+  const int cb = (int)(p % kRegion), cur = (int)(ca % nslot);
+  CoreStateN<NT> st;
   core_init(st);
-  const int64_t c = (int64_t)b * kSwpWaves + wave;  // this wave's chunk
-  const int64_t mine = c < nch ? 4 : 0;
-  auto region_of = [&](int64_t e) -> Region {
-    const int64_t er = 4 * c + e;  // window region index of entry e
-    Region rg;
-    if (e >= mine || er >= nreg) {
-      rg.k = rk; rg.v = rv; rg.lo = 1; rg.hi = 0;
-      rg.kn = knew; rg.vn = vnew; rg.tn = -1;
-      return rg;
-    }
-    const int64_t r = rlo + er;
-    const int64_t pk = r % (W / kRegion);
-    rg.k = rk + pk * kRegion * kHeadDim;
-    rg.v = rv + pk * kHeadDim * kRegion;
-    rg.kn = knew;
-    rg.vn = vnew;
-    rg.tn = r == p / kRegion ? (int)(p % kRegion) : -1;
-    const int64_t first = r * kRegion;
-    rg.lo = (int)((lo > first ? lo : first) - first);
-    rg.hi = (int)((p < first + 7 ? p : first + 7) - first);
-    return rg;
-  };
-  core_run<0, true>(st, qb, mine, region_of, a.scale_log2);
+#pragma unroll
+  for (int j = 0; j < kCpw; ++j) {
+    swd_settle(x[j], 4 * (wave + WV * j), cur, cb, ca, p >= W - 1);
+    core_compute(st, qb, x[j].c, a.scale_log2);
+  }
   const float lt = core_total_l(st);
   if (kb == 0) {
     sm_m[wave][n] = st.m;
     sm_l[wave][n] = lt;
   }
 #pragma unroll
-  for (int nt = 0; nt < 12; ++nt) *(f32x4*)&sm_o[wave][n][16 * nt + 4 * kb] = st.o[nt];
+  for (int nt = 0; nt < NT; ++nt) *(f32x4*)&sm_o[wave][n][16 * nt + 4 * kb] = st.o[nt];
   __syncthreads();
-  // the part's record: m and l of each head, then O[h][d] scaled to the part's max
-  float* rec = part + (sg * kSwpParts + b) * kSwpRec;
-  if (threadIdx.x < 16) {
-    const int h = threadIdx.x;
+  // item e: head e / (kCh/4), channels 4q..4q+3 of the slice
+  for (int e = t; e < 16 * kCh / 4; e += 64 * WV) {
+    const int h = e / (kCh / 4), q4 = 4 * (e - h * (kCh / 4));
     float M = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kSwpWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float l = 0.0f;
-    if (M != -INFINITY)
-#pragma unroll
-      for (int w = 0; w < kSwpWaves; ++w) l += __builtin_amdgcn_exp2f(sm_m[w][h] - M) * sm_l[w][h];
-    rec[h] = M;
-    rec[16 + h] = l;
-  }
-  for (int e = threadIdx.x; e < 16 * kHeadDim / 4; e += 64 * kSwpWaves) {
-    const int h = e / (kHeadDim / 4), d = 4 * (e - h * (kHeadDim / 4));
-    float M = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kSwpWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 1; w < WV; ++w) M = fmaxf(M, sm_m[w][h]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float Lsum = 0.0f;
     if (M != -INFINITY)
 #pragma unroll
-      for (int w = 0; w < kSwpWaves; ++w) acc += __builtin_amdgcn_exp2f(sm_m[w][h] - M) * *(const f32x4*)&sm_o[w][h][d];
-    *(f32x4*)(rec + 32 + h * kHeadDim + d) = acc;
+      for (int w = 0; w < WV; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
+        acc += f * *(const f32x4*)&sm_o[w][h][q4];
+        Lsum += f * sm_l[w][h];
+      }
+    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+    uint2 o2;
+    o2.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    o2.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *(uint2*)(a.out + (row * kQHeads + kHeadsPerGroup * g + h) * kHeadDim + kCh * slice + q4) = o2;
   }
-}
-
-// block = (sequence s, group g): the parts that hold a chunk, combined in
-// part order, normalised and stored; thread t handles channels 4j..4j+3 of
-// items t, t+256, t+512 (item = head h, channel quad j) and issues all of its
-// record loads before using any.  APPEND: then the new token's K/V go into
-// ring slot p mod W.  That slot held position p - W, outside this window;
-// the part kernel, which read the ring, ran before this launch.
-template <bool APPEND>
-__global__ __launch_bounds__(256) void k_swa_decode_merge(SwaArgs a, const float* part, uint16_t* k_ring_w,
-                                                          uint16_t* v_ring_w) {
-  constexpr int kQuads = kHeadDim / 4, kItems = kHeadsPerGroup * kQuads / 256;
-  static_assert(kHeadsPerGroup * kQuads == 256 * kItems, "items fill the block");
-  const int s = blockIdx.x, g = blockIdx.y;
-  int64_t p, row, rlo, nreg;
-  swa_decode_window(a, s, p, row, rlo, nreg);
-  if (nreg <= 0) return;
-  const int nparts = (int)(((nreg + 3) / 4 + kSwpWaves - 1) / kSwpWaves);
-  const int64_t sg = (int64_t)s * kGroups + g;
-  const float* rec = part + sg * kSwpParts * kSwpRec;
-  const int t = threadIdx.x;
-  const uint16_t* knew = a.k_new + (row * kGroups + g) * kHeadDim;
-  const uint16_t* vnew = a.v_new + (row * kGroups + g) * kHeadDim;
-  u32x4 kv = {0u, 0u, 0u, 0u};
-  uint16_t vv = 0;
   if constexpr (APPEND) {
-    if (t < kHeadDim / 8) kv = ld16(knew + 8 * t);
-    else if (t >= 64 && t < 64 + kHeadDim) vv = vnew[t - 64];
-  }
-  float m[kItems][kSwpParts], l[kItems][kSwpParts];
-  f32x4 o[kItems][kSwpParts];
-#pragma unroll
-  for (int i = 0; i < kItems; ++i) {
-    const int e = t + 256 * i, h = e / kQuads, d = 4 * (e - h * kQuads);
-#pragma unroll
-    for (int b = 0; b < kSwpParts; ++b) {
-      const float* rb = rec + (b < nparts ? b : 0) * kSwpRec;  // (parts past nparts: weight 0 below)
-      m[i][b] = rb[h];
-      l[i][b] = rb[16 + h];
-      o[i][b] = *(const f32x4*)(rb + 32 + h * kHeadDim + d);
+    if (slice == 0) {
+      const int64_t slot = p % W;
+      if (t < kHeadDim / 8)  // K: 24 units of 8 channels
+        *(u32x4*)(k_ring_w + (sg * nslot + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, 8 * t)) =
+            akv;
+      else if (t >= 64 && t < 64 + kHeadDim)  // V: 192 channels
+        v_ring_w[((sg * nslot + slot / kRegion) * kHeadDim + (t - 64)) * kRegion + slot % kRegion] = avv;
     }
   }
-  uint16_t* op = a.out + (row * kQHeads + kHeadsPerGroup * g) * kHeadDim;
-#pragma unroll
-  for (int i = 0; i < kItems; ++i) {
-    const int e = t + 256 * i, h = e / kQuads, d = 4 * (e - h * kQuads);
-    float M = m[i][0];
-#pragma unroll
-    for (int b = 1; b < kSwpParts; ++b) M = b < nparts ? fmaxf(M, m[i][b]) : M;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.0f;
-    if (M != -INFINITY)
-#pragma unroll
-      for (int b = 0; b < kSwpParts; ++b) {
-        const float f = b < nparts ? __builtin_amdgcn_exp2f(m[i][b] - M) : 0.0f;
-        acc += f * o[i][b];
-        L += f * l[i][b];
-      }
-    uint2 w;
-    w.x = pack_bf16x2(L > 0.0f ? acc[0] / L : 0.0f, L > 0.0f ? acc[1] / L : 0.0f);
-    w.y = pack_bf16x2(L > 0.0f ? acc[2] / L : 0.0f, L > 0.0f ? acc[3] / L : 0.0f);
-    *(uint2*)(op + h * kHeadDim + d) = w;
-  }
-  if constexpr (APPEND) {
-    const int W = a.window;
-    const int64_t slot = p % W;
-    if (t < kHeadDim / 8)  // K: 24 units of 8 channels
-      *(u32x4*)(k_ring_w + (sg * (W / kRegion) + slot / kRegion) * kRegionElems + k_tile_offset(slot % kRegion, 8 * t)) = kv;
-    else if (t >= 64 && t < 64 + kHeadDim)  // V: 192 channels
-      v_ring_w[((sg * (W / kRegion) + slot / kRegion) * kHeadDim + (t - 64)) * kRegion + slot % kRegion] = vv;
-  }
 }
 
-// Launches the two decode kernels; part records at `part` (swa_decode_part_bytes).
-static void swa_decode_launch(const SwaArgs& a, float* part, uint16_t* k_ring_w, uint16_t* v_ring_w,
-                              hipStream_t s) {
+#ifndef DSA_SWD_NT
+#define DSA_SWD_NT 2
+#endif
+#ifndef DSA_SWD_WV
+#define DSA_SWD_WV 8
+#endif
+
+// One launch: (sequence, group) x channel slice blocks, the slices of one
+// (sequence, group) on one XCD (see k_swa_decode).
+static void swa_decode_launch(const SwaArgs& a, uint16_t* k_ring_w, uint16_t* v_ring_w, hipStream_t s) {
   ProfScope prof_("k_swa_attend", s);
-  hipLaunchKernelGGL(k_swa_decode_part, dim3(kSwpParts, a.n_seqs, kGroups), dim3(64 * kSwpWaves), 0, s, a, part);
+  constexpr int NT = DSA_SWD_NT, WV = DSA_SWD_WV;
+  const int64_t nsg = (int64_t)a.n_seqs * kGroups;
+  const dim3 grid((unsigned)((nsg + 7) / 8 * 8 * (12 / NT)));
   if (k_ring_w)
-    hipLaunchKernelGGL((k_swa_decode_merge<true>), dim3(a.n_seqs, kGroups), dim3(256), 0, s, a,
-                       (const float*)part, k_ring_w, v_ring_w);
+    hipLaunchKernelGGL((k_swa_decode<NT, WV, true>), grid, dim3(64 * WV), 0, s, a, k_ring_w, v_ring_w);
   else
-    hipLaunchKernelGGL((k_swa_decode_merge<false>), dim3(a.n_seqs, kGroups), dim3(256), 0, s, a,
-                       (const float*)part, (uint16_t*)nullptr, (uint16_t*)nullptr);
+    hipLaunchKernelGGL((k_swa_decode<NT, WV, false>), grid, dim3(64 * WV), 0, s, a, (uint16_t*)nullptr,
+                       (uint16_t*)nullptr);
 }
 
-static size_t swa_decode_part_bytes(int32_t n_seqs) {
-  return ((size_t)n_seqs * kGroups * kSwpParts * kSwpRec * sizeof(float) + 255) / 256 * 256;
-}
 
 // S^T tiles, online softmax and O^T += V^T P^T of one chunk for NQ queries
 // that share its K/V registers (the band kernel: neighbouring queries of
@@ -1880,15 +1891,9 @@ extern "C" size_t swa_attention_workspace_size(const dsa_geometry* geom, int32_t
   (void)geom;
   (void)window;
   if (n_seqs <= 0 || max_new_per_seq <= 0) return 256;
-  if (max_new_per_seq == 1) return swa_decode_part_bytes(n_seqs);  // decode: the part records
+  if (max_new_per_seq == 1) return 256;  // decode: one launch, no workspace
   const size_t one = (size_t)n_seqs * kGroups * nstage_of(max_new_per_seq) * kRegion * kHeadDim * sizeof(uint16_t);
   return 2 * ((one + 255) / 256 * 256) + 256;
-}
-
-extern "C" size_t swa_decode_step_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs) {
-  (void)geom;
-  (void)window;
-  return n_seqs <= 0 ? 256 : swa_decode_part_bytes(n_seqs);
 }
 
 static dsa_status swa_check(const dsa_geometry* geom, int32_t window, int32_t n_seqs, int32_t max_new,
@@ -1926,7 +1931,7 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   a.st_v = (uint16_t*)((char*)workspace + (one + 255) / 256 * 256);
   hipStream_t s = as_stream(stream);
   if (max_new_per_seq == 1) {  // decode: the attention kernels patch the new token in themselves
-    swa_decode_launch(a, (float*)workspace, nullptr, nullptr, s);
+    swa_decode_launch(a, nullptr, nullptr, s);
     return check_launch("swa_attention");
   }
   {
@@ -1955,22 +1960,18 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
 extern "C" dsa_status swa_decode_step(const dsa_geometry* geom, int32_t window, int32_t n_seqs,
                                       const int32_t* seq_pos, const uint16_t* q, const uint16_t* k_new,
                                       const uint16_t* v_new, uint16_t* k_ring, uint16_t* v_ring, uint16_t* out,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+                                      void* stream) {
   dsa_status st = swa_check(geom, window, n_seqs, 1, "swa_decode_step");
   if (st != DSA_OK) return st;
   if (n_seqs == 0) return DSA_OK;
-  if (!seq_pos || !q || !k_new || !v_new || !k_ring || !v_ring || !out || !workspace)
+  if (!seq_pos || !q || !k_new || !v_new || !k_ring || !v_ring || !out)
     return fail(DSA_ERR_INVALID_ARGUMENT, "swa_decode_step: NULL pointer");
-  if ((size_t)workspace & 255)
-    return fail(DSA_ERR_INVALID_ARGUMENT, "swa_decode_step: workspace must be 256-byte aligned");
-  if (workspace_bytes < swa_decode_step_workspace_size(geom, window, n_seqs))
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "swa_decode_step: workspace too small");
   SwaArgs a = {};
   a.pos0 = seq_pos; a.row0 = nullptr; a.q = q; a.k_new = k_new; a.v_new = v_new;
   a.k_ring = k_ring; a.v_ring = v_ring; a.out = out;
   a.n_seqs = n_seqs; a.max_new = 1; a.window = window; a.rows = n_seqs;
   a.scale_log2 = geom->softmax_scale * kLog2e;
-  swa_decode_launch(a, (float*)workspace, k_ring, v_ring, as_stream(stream));
+  swa_decode_launch(a, k_ring, v_ring, as_stream(stream));
   return check_launch("swa_decode_step");
 }
 

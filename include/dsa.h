@@ -526,27 +526,22 @@ dsa_status swa_ring_append(const dsa_geometry* geom, int32_t window, int32_t n_s
  * attends to positions max(0, p-W+1)..p, and its K/V are then written into
  * ring slot p mod W.  The output equals swa_attention with one new token per
  * sequence (seq_row0 = 0, 1, .., n_seqs) and the rings equal a following
- * swa_ring_append.  Two launches: the window is split over 5 blocks per
- * (sequence, group) whose partial softmax states go to the workspace, then
- * one block per (sequence, group) combines them, writes out and appends the
- * token (the slot written held position p - W, which this step no longer
- * reads).
+ * swa_ring_append.  One launch, no workspace: the window is exactly the
+ * ring's 64 region slots (the slot shared by the window's first and current
+ * regions holds the first region's tokens above offset p mod 8 and the
+ * current region's up to it), each (sequence, group) is served by 6 blocks
+ * owning 32 output channels each, and one of them writes the token into
+ * ring slot p mod W, which held position p - W (no value this step reads).
  *   window   512
  *   seq_pos  [n_seqs] int32 device (>= 0)
  *   q, out   [n_seqs][64][D] bf16;  k_new, v_new [n_seqs][G][D] bf16
  *   k_ring, v_ring  rings holding positions p-W .. p-1 (those >= 0), layouts as
- *            for swa_attention; updated in place
- *   workspace >= swa_decode_step_workspace_size() bytes, 256-byte aligned;
- *            results never depend on its contents on entry.  Calls sharing a
- *            workspace must not overlap.
+ *            for swa_attention; updated in place.  Calls updating one ring
+ *            must not overlap.
  */
 dsa_status swa_decode_step(const dsa_geometry* geom, int32_t window, int32_t n_seqs, const int32_t* seq_pos,
                            const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_ring,
-                           uint16_t* v_ring, uint16_t* out, void* workspace, size_t workspace_bytes,
-                           void* stream);
-
-/* Workspace bytes swa_decode_step needs (about 248 KB per sequence). */
-size_t swa_decode_step_workspace_size(const dsa_geometry* geom, int32_t window, int32_t n_seqs);
+                           uint16_t* v_ring, uint16_t* out, void* stream);
 
 /*
  * Indexer front-end ([P2] section 索引器打分 + Top-K 选择: the indexer projects
