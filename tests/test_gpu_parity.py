@@ -425,6 +425,73 @@ def test_swa_prefill_chunk_at_64k_sampled():
     print(f"swa 64K chunk: worst max abs {worst[0]:.3e}, rel rms {worst[1]:.3e}")
 
 
+def _swa_decode_inputs(seed, pos, layer):
+    """Rings of len(pos) sequences holding positions p-512..p-1 (generator-written, NaN elsewhere),
+    and one new token per sequence at p: q (row s), k_new, v_new."""
+    S = len(pos)
+    T = max(pos) + 1
+    tq, tk, tv = H.swa_tids(layer)
+    per = G * H.W * D
+    k_ring = torch.full((S * per,), float("nan"), dtype=H.BF16, device="cuda")
+    v_ring = torch.full((S * per,), float("nan"), dtype=H.BF16, device="cuda")
+    for s, p in enumerate(pos):
+        t0 = max(0, p - H.W)
+        if p > t0:
+            for layout, ring, tid in ((gi.LAYOUT_KTILED, k_ring, tk), (gi.LAYOUT_REGION_T, v_ring, tv)):
+                tmp = torch.empty((s + 1) * per, dtype=H.BF16, device="cuda")
+                gi.dev_tokens(tmp.data_ptr(), H.stream_ptr(), seed, tid, s + 1, T, G, D, t0, p - t0, H.W, H.W,
+                              layout, 1.0)
+                ring[s * per:(s + 1) * per] = tmp[s * per:(s + 1) * per]
+    q = torch.empty(S * HQ * D, dtype=H.BF16, device="cuda")
+    kn = torch.empty(S * G * D, dtype=H.BF16, device="cuda")
+    vn = torch.empty(S * G * D, dtype=H.BF16, device="cuda")
+    for s, p in enumerate(pos):
+        gi.dev_flat(q[s * HQ * D:].data_ptr(), H.stream_ptr(), seed, tq, HQ * D, 0, 1.0, start=(s * T + p) * HQ * D)
+        tmpk = H.dev_cache(seed, tk, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=1)
+        tmpv = H.dev_cache(seed, tv, s + 1, T, D, 0, gi.LAYOUT_TOKEN_MAJOR, t0=p, nt=1)
+        kn[s * G * D:(s + 1) * G * D] = tmpk[s * G * D:(s + 1) * G * D]
+        vn[s * G * D:(s + 1) * G * D] = tmpv[s * G * D:(s + 1) * G * D]
+    return k_ring, v_ring, q, kn, vn, T, (tq, tk, tv)
+
+
+def _swa_decode_oracle(seed, tids, T, s, p, q_row_start):
+    tq, tk, tv = tids
+    Kh = gi.host_tokens_bf16(seed, tk, T, G, D, s, 0, p + 1)
+    Vh = gi.host_tokens_bf16(seed, tv, T, G, D, s, 0, p + 1)
+    hq = gi.host_normal_bf16(seed, tq, HQ * D, 1.0, start=q_row_start).reshape(HQ, D)
+    return O.swa(hq, Kh, Vh, p, H.W)
+
+
+def test_swa_decode_skips_sequences_without_a_new_row():
+    """swa_attention with one new row per sequence at most (the single-launch decode kernel): a
+    sequence whose row range is empty writes nothing (its output row keeps a sentinel), the others
+    match the oracle; one sequence sits at p mod 8 = 7 with a full ring, one at the ring's first
+    region."""
+    seed = 0xFA
+    pos = [1023, 4096, 6, 2047]
+    S = len(pos)
+    k_ring, v_ring, q, kn, vn, T, tids = _swa_decode_inputs(seed, pos, 1)
+    geom = dsa.geometry()
+    # rows: sequence 1 has none, the others take rows 0, 1, 2 (their inputs moved down by one row
+    # after sequence 1)
+    keep = [0, 2, 3]
+    q2 = torch.zeros_like(q)
+    kn2, vn2 = torch.zeros_like(kn), torch.zeros_like(vn)
+    for r, s in enumerate(keep):
+        q2[r * HQ * D:(r + 1) * HQ * D] = q[s * HQ * D:(s + 1) * HQ * D]
+        kn2[r * G * D:(r + 1) * G * D] = kn[s * G * D:(s + 1) * G * D]
+        vn2[r * G * D:(r + 1) * G * D] = vn[s * G * D:(s + 1) * G * D]
+    row0 = H.i32([0, 1, 1, 2, 3])
+    out = torch.full((S * HQ * D,), 7.0, dtype=H.BF16, device="cuda")
+    dsa.swa_attention(geom, H.W, 1, H.i32(pos), row0, q2, kn2, vn2, k_ring, v_ring, out)
+    torch.cuda.synchronize()
+    go = H.bf16_np(out).reshape(S, HQ, D)
+    for r, s in enumerate(keep):
+        p = pos[s]
+        H.assert_attn(go[r], _swa_decode_oracle(seed, tids, T, s, p, (s * T + p) * HQ * D), f"seq {s} at {p}")
+    assert np.all(go[3] == 7.0), "the row past the last sequence's was written"
+
+
 def test_swa_batched_decode_with_prefilled_rings():
     """Several sequences, one new token each, rings written directly by the generator."""
     seed = 0xF5
