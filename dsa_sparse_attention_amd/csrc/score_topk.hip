@@ -176,7 +176,7 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
 }
 
 #ifndef DSA_SCORE_DEC_RANGE
-#define DSA_SCORE_DEC_RANGE 512
+#define DSA_SCORE_DEC_RANGE 384
 #endif
 #ifndef DSA_SCORE_DEC_DEPTH
 #define DSA_SCORE_DEC_DEPTH 4
