@@ -778,6 +778,51 @@ def test_decode_step_replays_from_a_hip_graph():
         assert torch.equal(other["out"].view(torch.uint8), ref["out"].view(torch.uint8))
 
 
+def test_swa_decode_step_replays_from_a_hip_graph():
+    """The sliding-window decode step (attention and ring append in one launch) captured once and
+    replayed several times, with eager steps on other rings in between: every replay gives the eager
+    output and rings bit for bit (a replay appends the same token to the same slot, which the step
+    itself never reads)."""
+    seed = 0xAC
+    pos = [700, 1023, 40, 512]
+    S = len(pos)
+    k_ring, v_ring, q, kn, vn, T, tids = _swa_decode_inputs(seed, pos, 3)
+    geom = dsa.geometry()
+    p32 = H.i32(pos)
+
+    def make_bufs():
+        return dict(kr=k_ring.clone(), vr=v_ring.clone(), out=torch.empty(S * HQ * D, dtype=H.BF16, device="cuda"))
+
+    def step(b):
+        dsa.swa_decode_step(geom, H.W, p32, q, kn, vn, b["kr"], b["vr"], b["out"])
+
+    ref = make_bufs()
+    step(ref)
+    torch.cuda.synchronize()
+    gb = make_bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(gb)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(gb)
+    for rep in range(3):
+        gb["out"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(gb[k].view(torch.int16), ref[k].view(torch.int16)), (rep, k)
+        other = make_bufs()
+        step(other)
+        torch.cuda.synchronize()
+        assert torch.equal(other["out"].view(torch.int16), ref["out"].view(torch.int16))
+    go = H.bf16_np(ref["out"]).reshape(S, HQ, D)
+    for s_, p in enumerate(pos):
+        H.assert_attn(go[s_], _swa_decode_oracle(seed, tids, T, s_, p, (s_ * T + p) * HQ * D), f"seq {s_} at {p}")
+
+
 def test_cache_write_produces_the_documented_layouts():
     """dsa_cache_write of token-major rows gives the same bytes as the generator's direct fill of the
     group-major index_k, region-tiled K and region-transposed V caches."""
