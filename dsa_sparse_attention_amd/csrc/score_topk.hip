@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
   seq = seq < 0 ? 0 : (seq >= a.n_seqs ? a.n_seqs - 1 : seq);
   const int64_t c = current_region(query_pos(a.qpos, a.slen, qi), a.cm.R, a.max_regions);
   // paged caches: lane l holds the page id of the wave's tile l (clamped when
-  // used); the barrier below waits for it together with the query's loads
+  // used)
   const int64_t ntile_all = a.cm.R / kTile;
   int32_t pgv = 0;
   if constexpr (PAGED) {
@@ -222,19 +222,6 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
     }
   }
   const f32x4 zz = *(const f32x4*)(a.z + (int64_t)qi * kIdxHeads + 4 * g);
-  __syncthreads();
-  // (the page ids are waited for once, here, instead of before every tile's
-  // loads)
-  if constexpr (PAGED) asm volatile("" ::"v"(pgv));
-
-  // this wave's tiles: contiguous quarter of the block's range
-  int64_t w1 = w0 + kWaveRegions;
-  if (w1 > c) w1 = c;
-  const int ntile = w0 < w1 ? (int)((w1 - w0 + kTile - 1) / kTile) : 0;
-  const int64_t pq = (int64_t)qi * kGroups + g;
-  float* scores = a.scores + pq * a.ws_stride;
-  float* scores_out = a.scores_out ? a.scores_out + pq * a.max_regions : nullptr;
-  uint32_t* tmax = a.tilemax ? a.tilemax + pq * a.tm_stride + w0 / kTile : nullptr;
 
   u32x4 buf[kDecDepth][4];
   float bsc[kDecDepth];
@@ -251,9 +238,21 @@ __global__ __launch_bounds__(256) void k_score_dec(ScoreArgs a) {
     buf[slot][3] = ldg16(rp + 3072);
     bsc[slot] = a.scale[ts * kTile + n];
   };
+  // The first tiles are issued before the query operand and the position
+  // are waited for (their slots do not depend on them; tiles past the wave's
+  // last are loaded and never used).  Paged caches wait for the page ids
+  // here, once.
 #pragma unroll
-  for (int t = 0; t < kDecDepth - 1; ++t)
-    if (t < ntile) issue(t, t);
+  for (int t = 0; t < kDecDepth - 1; ++t) issue(t, t);
+
+  // this wave's tiles: contiguous quarter of the block's range
+  int64_t w1 = w0 + kWaveRegions;
+  if (w1 > c) w1 = c;
+  const int ntile = w0 < w1 ? (int)((w1 - w0 + kTile - 1) / kTile) : 0;
+  const int64_t pq = (int64_t)qi * kGroups + g;
+  float* scores = a.scores + pq * a.ws_stride;
+  float* scores_out = a.scores_out ? a.scores_out + pq * a.max_regions : nullptr;
+  uint32_t* tmax = a.tilemax ? a.tilemax + pq * a.tm_stride + w0 / kTile : nullptr;
   for (int t0 = 0; t0 < ntile; t0 += kDecDepth) {
 #pragma unroll
     for (int u = 0; u < kDecDepth; ++u) {
