@@ -19,6 +19,8 @@
 //   O^T[dv][head] += V^T(192x32) . P^T  -> 12 tiles, A = V^T read straight
 //     from the region-transposed V layout (one 16-byte load = the 8 tokens of
 //     a region for one channel), B = the lane's own 8 softmax weights.
+// The core can keep O^T for a slice of the channels only (NT of the 12
+// tiles): the sliding-window decode splits the output channels over blocks.
 // Online softmax in fp32 (exp2 domain), weights rounded to bf16 for the PV
 // product.  Masked positions get weight 0 and their V is zeroed, so stale or
 // uninitialised cache rows can never leak in.

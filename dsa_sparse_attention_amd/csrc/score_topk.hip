@@ -10,21 +10,27 @@
 // same section: regions are tied one-to-one to the 4 GQA groups).
 //
 // Design (gfx950):
-//  * k_score streams the summaries once, coalesced, with the dot products on
-//    the matrix cores: A = the query's 4 group heads (rows; up to 4 queries
-//    per 16-row MFMA tile), B = 16 regions x 32 channels of E4M3 codes turned
-//    into bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1).  The channel
-//    order inside one 256-d dot is permuted so that each lane reads 64
-//    contiguous bytes of one region; A uses the same permutation.  Besides
-//    the scores it stores, per 16-region tile, the largest order-preserving
+//  * Scoring streams the summaries once, coalesced, with the dot products on
+//    the matrix cores: B = 16 regions x 32 channels of E4M3 codes turned into
+//    bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1), A = query heads of
+//    the group.  The channel order inside one 256-d dot is permuted so that
+//    each lane reads 64 contiguous bytes of one region; A uses the same
+//    permutation.  k_score_dec (few queries, long contexts) gives each block
+//    one (query, group) and a run of regions, the 4 heads in MFMA rows 0..3;
+//    k_score_pre (prefill chunks) gives each wave 16 queries as four row-sets
+//    that share every summary tile, which the block streams through an LDS
+//    ring.  Both can store, per 16-region tile, the largest order-preserving
 //    score key of the tile.
-//  * Selection ranks regions by (score desc, region asc) with 32-bit keys and
-//    index order.  Short problems (c <= 8192) keep every key in registers and
-//    find the k-th key by bisection with block-wide ballot counts.  Long
-//    problems first select the need best tiles by their maxima: every region
-//    of the answer lies in them (a region outside them is beaten by the
-//    maxima of need tiles that all rank above it), so at most 511 tiles of 16
-//    regions are then ranked exactly.  A radix fallback in global memory
+//  * Selection ranks regions by (score desc, region asc) with 32-bit keys.
+//    Problems of up to 8192 candidates keep their keys in registers
+//    (k_select_pre): a histogram on a linear score scale finds the bin of
+//    the need-th key, whose few keys are ranked exactly.  Longer problems go
+//    through the tile maxima: the need-th largest tile maximum bounds the
+//    need-th score from below, so only tiles reaching that bound can hold a
+//    selected region.  Decode-shaped problems (k_select_dec) take a digit of
+//    the tile maxima as the bound and finish with a wave-level radix on the
+//    candidates' keys; prefill-shaped ones (k_select_tiles) take the need
+//    best tiles and rank their regions.  A radix fallback in global memory
 //    covers problems beyond the register capacity.
 #include <mutex>
 
