@@ -992,11 +992,12 @@ void k_swa_attend(SwaArgs a) {
 // offsets 0..b (the new token patched in at b when loaded) and, above b,
 // the window's first region's; every other slot holds a whole region of the
 // window.  Before the ring has filled (p < W - 1), slots 0..a hold the
-// window, slot a up to offset b.  So 16 waves take one 4-slot chunk each.
-// A block owns one (sequence, group) and the 16*NT output channels of slice
-// `slice`: every wave scores all 16 heads over the full 192 channels (the
-// same scores in every slice block) and accumulates P.V on its slice only,
-// and the 16 waves' partials combine in LDS.  Blocks go to the 8 XCDs round
+// window, slot a up to offset b.  The 16 chunks of 4 slots go to the block's
+// WV waves (8 waves of two chunks by default, both chunks' loads in flight
+// at once).  A block owns one (sequence, group) and the 16*NT output channels
+// of slice `slice`: every wave scores all 16 heads over the full 192 channels
+// (the same scores in every slice block) and accumulates P.V on its slice
+// only, and the waves' partials combine in LDS.  Blocks go to the 8 XCDs round
 // robin by index, so the 12/NT slice blocks of one (sequence, group) are
 // placed on one XCD and share its L2 for K.
 // APPEND: slice 0 then writes the new token's K/V into the ring at slot p mod
@@ -1007,10 +1008,10 @@ void k_swa_attend(SwaArgs a) {
 constexpr int kSwdSlots = kWindow / kRegion;  // ring region slots = window regions
 static_assert(kSwdSlots % 4 == 0, "whole 4-slot chunks");
 
-// The chunk of ring slots 4w..4w+3 as wave w of a sliding-window decode
-// block holds it: every load is issued before the position is known (the
-// slots do not depend on it), the new token's K and V included; which token
-// is patched and which are masked is settled once the position arrives.
+// A chunk of 4 ring slots as a sliding-window decode wave holds it: every
+// load is issued before the position is known (the slots do not depend on
+// it), the new token's K and V included; which token is patched and which
+// are masked is settled once the position arrives.
 template <int NT>
 struct SwdChunk {
   ChunkRegsN<NT> c;
@@ -1092,16 +1093,15 @@ __global__ __launch_bounds__(64 * WV) void k_swa_decode(SwaArgs a, uint16_t* k_r
   SwdChunk<NT> x[kCpw];
 #pragma unroll
   for (int j = 0; j < kCpw; ++j) swd_load(x[j], rk, rv, knew, vnew, 4 * (wave + WV * j));
-  // the append's copy of the new token (slice 0): K units for threads 0..23,
-  // V channels for threads 64..255
+  // the append's copy of the new token (slice 0, whose vnew is the whole
+  // row): K units for threads 0..23, V channels for threads 64..255
+  static_assert(64 * WV >= 64 + kHeadDim, "a thread per V channel of the append");
   const int t = threadIdx.x;
-  const uint16_t* kn0 = a.k_new + (row * kGroups + g) * kHeadDim;
-  const uint16_t* vn0 = a.v_new + (row * kGroups + g) * kHeadDim;
   u32x4 akv = {0u, 0u, 0u, 0u};
   uint16_t avv = 0;
   if (APPEND && slice == 0) {
-    if (t < kHeadDim / 8) akv = ld16(kn0 + 8 * t);
-    else if (t >= 64 && t < 64 + kHeadDim) avv = vn0[t - 64];
+    if (t < kHeadDim / 8) akv = ld16(knew + 8 * t);
+    else if (t >= 64 && t < 64 + kHeadDim) avv = vnew[t - 64];
   }
   __builtin_amdgcn_sched_barrier(0);  // (every load issued before any is waited for)
   const int64_t p = praw < 0 ? 0 : praw;
