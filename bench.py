@@ -1095,7 +1095,7 @@ def measure_frontend(args, result):
 def measure_swa(args, result):
     import torch
     step, keep = setup_mix(MIX)
-    km = ["k_swa_stage", "k_swa_attend", "k_ring_append", "k_score_decode", "k_select", "k_sgqa_decode",
+    km = ["k_swa_decode", "k_score_decode", "k_select", "k_sgqa_decode",
           "k_sgqa_merge"]
     msteps = max(3, args.steps // 3)
     msecs, meager, mst = timed(step, msteps, max(1, args.warmup // 2), km, graph=args.graph)
@@ -1106,7 +1106,7 @@ def measure_swa(args, result):
     sbytes = swa_decode_bytes(B)
     dbytes = decode_bytes(B, Lc, MIX["topk"])["total"]
     tot = MIX["swa_layers"] * sbytes + dbytes
-    swa_us = sum(mst[k][0] for k in ("k_swa_stage", "k_swa_attend", "k_ring_append")) * 1e3  # per layer
+    swa_us = mst["k_swa_decode"][0] * 1e3  # per layer: attention and ring append in one launch
     result["mix_decode"] = {
         "workload": MIX["name"], "value": round(B * msteps / msecs, 1), "unit": "queries/s (4-layer stack)",
         "steps": msteps, "ms_per_step": round(mms, 4), "eager_ms_per_step": round(meager * 1e3 / msteps, 4),

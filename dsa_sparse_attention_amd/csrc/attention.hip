@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(64 * WV) void k_swa_decode(SwaArgs a, uint16_t* k_r
 // One launch: (sequence, group) x channel slice blocks, the slices of one
 // (sequence, group) on one XCD (see k_swa_decode).
 static void swa_decode_launch(const SwaArgs& a, uint16_t* k_ring_w, uint16_t* v_ring_w, hipStream_t s) {
-  ProfScope prof_("k_swa_attend", s);
+  ProfScope prof_("k_swa_decode", s);
   constexpr int NT = DSA_SWD_NT, WV = DSA_SWD_WV;
   const int64_t nsg = (int64_t)a.n_seqs * kGroups;
   const dim3 grid((unsigned)((nsg + 7) / 8 * 8 * (12 / NT)));

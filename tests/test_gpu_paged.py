@@ -197,7 +197,8 @@ def test_paged_cache_write_and_compress():
         assert np.array_equal(sl[b, :, :L // 8], codes.transpose(1, 0, 2))
 
 
-@pytest.mark.parametrize("lens", [[1 << 20] * 4, [131072, 70001, 9000, 8192, 17, 1]])
+@pytest.mark.parametrize("lens", [[1 << 20] * 4, [131072, 70001, 9000, 8192, 17, 1],
+                                  [8192, 1000, 4096, 17, 8, 1]])
 def test_paged_decode_step_matches_contiguous(lens):
     """dsa_decode_step_paged (folded compression writing into the pools) gives bit for bit what
     dsa_decode_step gives on contiguous caches: selections, outputs and the new summaries."""

@@ -149,11 +149,14 @@ def test_decode_selection_does_not_depend_on_workspace_contents():
         assert np.array_equal(sel, ref_sel)
 
 
-@pytest.mark.parametrize("lens", [[1 << 20] * 4, [131072, 70001, 9000, 8192, 17, 1]])
+@pytest.mark.parametrize("lens", [[1 << 20] * 4, [131072, 70001, 9000, 8192, 17, 1],
+                                  [8192, 1000, 4096, 17, 8, 1]])
 def test_decode_step_matches_the_separate_calls(lens):
-    """dsa_decode_step, whose compression of the completed region runs inside the scoring launch,
+    """dsa_decode_step, whose compression of the completed region runs inside the selection launch,
     gives bit for bit what dsa_compress_regions + dsa_score_topk + dsa_sparse_gqa_decode give,
-    summaries included (only the region a query token completes is written)."""
+    summaries included (only the region a query token completes is written).  The last case (1,024
+    regions of capacity: the short-context scoring and the register selection, which holds the folded
+    compression blocks) has tokens completing regions 8191 // 8, 999 // 8, 4095 // 8 and 7 // 8."""
     seed = 0xDB + len(lens)
     B, tcap = len(lens), H.round128(max(lens))
     R = tcap // 8
