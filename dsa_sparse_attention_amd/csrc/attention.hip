@@ -25,6 +25,7 @@
 // product.  Masked positions get weight 0 and their V is zeroed, so stale or
 // uninitialised cache rows can never leak in.
 #include <math.h>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -1178,8 +1179,8 @@ static void swa_decode_launch(const SwaArgs& a, uint16_t* k_ring_w, uint16_t* v_
 
 
 // S^T tiles, online softmax and O^T += V^T P^T of one chunk for NQ queries
-// that share its K/V registers (the band kernel: neighbouring queries of
-// one group read the same window).  lo[j]/hi[j]: query j's valid positions
+// that share its K/V registers (the neighbour-merged prefill: consecutive
+// queries of one group walk the union of their selections).  lo[j]/hi[j]: query j's valid positions
 // in the lane's softmax region.  Positions no query of the wave uses get
 // their V zeroed; a position one query uses and another masks holds real
 // data and gets weight 0 from the latter.
@@ -1283,32 +1284,126 @@ __device__ __forceinline__ void core_compute_band(CoreState (&st)[NQ], const QOf
   }
 }
 
-// Chunked prefill: block = (16 consecutive new tokens of sequence s, group
-// g), 4 waves of 4 tokens each.  The tokens' windows nearly coincide, so the
-// block streams the union of the windows (≈67 regions) through an LDS ring
-// of 4-region chunks once; each wave loads a chunk's K/V into registers
-// once and applies it to its 4 tokens under their band masks, so a K/V byte
-// read from L2 feeds 16 queries and a byte read from LDS feeds 4.  Each
-// chunk is 24 copies of 1 KB (the DMA form of the loads, global -> LDS):
-// wave w copies region w of it.  Copies run kBandDepth - 1 chunks ahead; a
-// wave's count of outstanding memory operations (the loop issues nothing
-// else) tells when its copies landed, and a barrier makes the whole chunk
-// visible and frees the slot refilled next.
-#ifndef DSA_BAND_NQ
-#define DSA_BAND_NQ 4
-#endif
-constexpr int kBandNQ = DSA_BAND_NQ;              // tokens per wave
-constexpr int kBandQ = 4 * kBandNQ;               // tokens per block
-constexpr int kBandDepth = 4;                     // chunks in the LDS ring
 constexpr int kRegionBytes = kRegionElems * 2;    // K (or V) of one region
 constexpr int kBandRegion = 2 * kRegionBytes + 64;  // a region's K then V in LDS; the 64-byte pad puts
                                                      // the 4 regions' K rows a wave reads together in
                                                      // different banks
 constexpr int kChunkBytes = 4 * kBandRegion;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_swa_band(SwaArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// Chunked prefill: block = (8 consecutive new tokens of sequence s, group
+// g), 4 waves of 2 tokens.  The tokens' windows nearly coincide, so the
+// block streams the union of the windows (about 66 regions) once through an
+// LDS ring of 4-region chunks (direct-to-LDS copies, 24 of 1 KB per chunk:
+// wave w copies region w, two chunks ahead); each wave applies a chunk to
+// its 2 tokens under their band masks, so a K/V byte read from L2 feeds 8
+// queries.  A wave's count of outstanding memory operations (the loop
+// issues nothing else) tells when its copies landed, and a barrier makes
+// the whole chunk visible and frees the slot refilled next.  The ring holds
+// 3 chunks (74.5 KB), so two blocks share a CU and each SIMD runs two waves:
+// one wave's softmax VALU work runs under the other's MFMAs (with one wave
+// per SIMD they run one after another).  The operands are read from LDS as
+// they are used (the K rows of one k-step, the V^T operand of one channel
+// tile), which keeps a wave within the 256 registers two waves per SIMD
+// allow.  V of positions outside the union of the block's windows (in the
+// union's first and last regions only) is zeroed in LDS by the wave that
+// copied the region, so P.V needs no mask: every other position holds a
+// token of some window, and its weight is exactly 0 for the tokens whose
+// band leaves it out.  Chunks inside every window of the block (all but the
+// first and last few) take a form without the band masks.
+constexpr int kBandNQ = 2;               // tokens per wave
+constexpr int kBandQ = 4 * kBandNQ;       // tokens per block
+constexpr int kBandDepth = 3;             // chunks in the LDS ring
+
+// One chunk for NQ tokens (see above).  MASKED: lo/hi give each token's
+// valid offsets in the lane's softmax region kb (lo > hi: none); otherwise
+// every position of the chunk is inside every token's band.
+template <int NQ, bool MASKED>
+__device__ __forceinline__ void band_chunk(CoreState (&st)[NQ], const bf16x8 (&qb)[NQ][6], const uint8_t* ch,
+                                            const int (&lo)[NQ], const int (&hi)[NQ], float scale_log2) {
   const int lane = threadIdx.x & 63, n = lane & 15, kb = lane >> 4;
+  // K rows of region n/4 (tile layout as in memory), V^T of region kb
+  const uint8_t* kp = ch + (n >> 2) * kBandRegion + ((kb * 4 + (n & 3)) * 8) * 2;
+  const uint8_t* vp = ch + kb * kBandRegion + kRegionBytes;
+  f32x4 s0[NQ], s1[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    s0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    const bf16x8 k0 = as_bf16x8(*(const u32x4*)(kp + (q * 16) * 16));
+    const bf16x8 k1 = as_bf16x8(*(const u32x4*)(kp + ((6 + q) * 16) * 16));
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      s0[j] = mfma16x16x32(k0, qb[j][q], s0[j]);
+      s1[j] = mfma16x16x32(k1, qb[j][q], s1[j]);
+    }
+  }
+  // raw scores (masked ones -inf); the scale (> 0) is applied to the row
+  // maximum and folded into the exponent below
+  float sv[NQ][8];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (MASKED) {
+        sv[j][i] = (i >= lo[j] && i <= hi[j]) ? s0[j][i] : -INFINITY;
+        sv[j][4 + i] = (4 + i >= lo[j] && 4 + i <= hi[j]) ? s1[j][i] : -INFINITY;
+      } else {
+        sv[j][i] = s0[j][i];
+        sv[j][4 + i] = s1[j][i];
+      }
+    }
+  float m_new[NQ];
+  bool grow = false;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    float cmax = sv[j][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[j][i]);
+    m_new[j] = fmaxf(st[j].m, max_across_rows(cmax) * scale_log2);
+    grow |= m_new[j] > st[j].m + 8.0f;
+  }
+  // lazy rescaling as in core_compute
+  if (__any(grow)) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      if (__any(m_new[j] > st[j].m + 8.0f)) {
+        const float alpha = __builtin_amdgcn_exp2f(st[j].m - m_new[j]);
+        st[j].l *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 12; ++nt) st[j].o[nt] *= alpha;
+        st[j].m = m_new[j];
+      }
+    }
+  }
+  bf16x8 pb[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const float m_use = st[j].m == -INFINITY ? 0.0f : st[j].m;
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(sv[j][i], scale_log2, -m_use));
+    st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+    u32x4 pp;
+    pp.x = pack_bf16x2(pr[0], pr[1]);
+    pp.y = pack_bf16x2(pr[2], pr[3]);
+    pp.z = pack_bf16x2(pr[4], pr[5]);
+    pp.w = pack_bf16x2(pr[6], pr[7]);
+    pb[j] = as_bf16x8(pp);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 12; ++nt) {
+    const bf16x8 v = as_bf16x8(*(const u32x4*)(vp + (16 * nt + n) * 16));
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) st[j].o[nt] = mfma16x16x32(v, pb[j], st[j].o[nt]);
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_swa_band(SwaArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, kb = lane >> 4;
   const int s = blockIdx.y, g = blockIdx.z;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kBandDepth][kChunkBytes];
   int64_t p0, r0, nnew;
@@ -1320,34 +1415,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t tile = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int64_t i0 = tile * kBandQ;
   if (i0 >= nnew) return;  // the same for the whole block
-  const int W = a.window;
+  constexpr int W = kWindow, kSlots = kWindow / kRegion;
   const int64_t i1 = (i0 + kBandQ < nnew ? i0 + kBandQ : nnew) - 1;
   const int64_t ulo = p0 + i0 - W + 1 < 0 ? 0 : p0 + i0 - W + 1;  // union of the block's windows
-  const int64_t rlo = ulo / kRegion, rhi = (p0 + i1) / kRegion, rst = p0 / kRegion;
+  const int64_t uhi = p0 + i1;
+  const int64_t rlo = ulo / kRegion, rhi = uhi / kRegion, rst = p0 / kRegion;
   const int nch = (int)((rhi - rlo + 1 + 3) / 4);
   const int64_t sg = (int64_t)s * kGroups + g;
-  // wave w copies region w of each chunk (past rhi: a re-read of region rhi, masked)
   const uint8_t* rk = (const uint8_t*)(a.k_ring + sg * W * kHeadDim);
-  const uint8_t* rv = (const uint8_t*)(a.v_ring + sg * (W / kRegion) * kHeadDim * kRegion);
+  const uint8_t* rv = (const uint8_t*)(a.v_ring + sg * kSlots * kHeadDim * kRegion);
   const uint8_t* sk = (const uint8_t*)(a.st_k + sg * a.nst * kRegionElems);
   const uint8_t* sv = (const uint8_t*)(a.st_v + sg * a.nst * kRegionElems);
+  // wave w copies region w of each chunk, K then V (past rhi: a re-read of
+  // region rhi, which no token weighs)
 #define DSA_BAND_ISSUE(c_)                                                                                  \
-  do {                                                                                                      \
-    int64_t r_ = rlo + 4 * (int64_t)(c_) + wave;                                                            \
-    r_ = r_ > rhi ? rhi : r_;                                                                               \
-    const int64_t o_ = r_ < rst ? (r_ % (W / kRegion)) * kRegionBytes : (r_ - rst) * kRegionBytes;          \
-    const uint8_t* bk_ = (r_ < rst ? rk : sk) + o_;                                                         \
-    const uint8_t* bv_ = (r_ < rst ? rv : sv) + o_;                                                         \
+  do {                                                                                                       \
+    int64_t r_ = rlo + 4 * (int64_t)(c_) + wave;                                                             \
+    r_ = r_ > rhi ? rhi : r_;                                                                                \
+    const int64_t o_ = r_ < rst ? (r_ & (kSlots - 1)) * kRegionBytes : (r_ - rst) * kRegionBytes;           \
+    const uint8_t* bk_ = (r_ < rst ? rk : sk) + o_;                                                          \
+    const uint8_t* bv_ = (r_ < rst ? rv : sv) + o_;                                                          \
     LdsPtr d_ = (LdsPtr)(&ring[(c_) % kBandDepth][0] + wave * kBandRegion);                                 \
-    _Pragma("unroll") for (int k_ = 0; k_ < 3; ++k_) {                                                      \
-      __builtin_amdgcn_global_load_lds((const void*)(bk_ + 1024 * k_ + 16 * lane), d_ + 1024 * k_, 16, 0, 0); \
+    _Pragma("unroll") for (int k_ = 0; k_ < 3; ++k_) {                                                       \
+      __builtin_amdgcn_global_load_lds((const void*)(bk_ + 1024 * k_ + 16 * lane), d_ + 1024 * k_, 16, 0, 0);  \
       __builtin_amdgcn_global_load_lds((const void*)(bv_ + 1024 * k_ + 16 * lane), d_ + kRegionBytes + 1024 * k_, \
-                                       16, 0, 0);                                                           \
-    }                                                                                                       \
+                                       16, 0, 0);                                                            \
+    }                                                                                                        \
   } while (0)
   // this wave's tokens (idle ones shadow the last token and store nothing);
-  // Q first: its loads are then older than the copies, and waiting for them
-  // does not wait for the copies
+  // Q first, so that waiting for it does not wait for the copies
   bf16x8 qb[kBandNQ][6];
   CoreState st[kBandNQ];
   int64_t pj[kBandNQ];
@@ -1362,35 +1458,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (nch > 0)
 #pragma unroll
     for (int c = 0; c < kBandDepth - 1; ++c) DSA_BAND_ISSUE(c);
-  for (int c = 0; c < nch; ++c) {
-    // the chunk's 6 copies are older than the 6 * (kBandDepth - 2) issued since
-    static_assert(kBandDepth == 4, "wait count below");
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  // chunk c: wait for its copies, clear V outside the union, then apply it
+  // (MASKED: with each token's band; the chunks inside every window of the
+  // block, from the last token's window start to the first token's
+  // position, need none)
+  auto body = [&](int c, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
+    // the chunk's 6 copies are older than the 6 issued since
+    static_assert(kBandDepth == 3, "wait count below");
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    {  // zero V outside [ulo, uhi] in the region this wave copied
+      int64_t r_ = rlo + 4 * (int64_t)c + wave;
+      r_ = r_ > rhi ? rhi : r_;
+      const int64_t f_ = r_ * kRegion;
+      const int zlo = ulo > f_ ? (int)(ulo - f_) : 0;
+      const int zhi = uhi < f_ + 7 ? (int)(uhi - f_) : 7;
+      if (zlo > 0 || zhi < 7) {  // uniform: the union's first or last region
+        uint32_t mk[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          mk[w] = ((2 * w >= zlo && 2 * w <= zhi) ? 0x0000FFFFu : 0u) |
+                  ((2 * w + 1 >= zlo && 2 * w + 1 <= zhi) ? 0xFFFF0000u : 0u);
+        uint8_t* vrow = &ring[c % kBandDepth][0] + wave * kBandRegion + kRegionBytes;
+#pragma unroll
+        for (int d = 0; d < kHeadDim; d += 64) {
+          u32x4 x = *(u32x4*)(vrow + (d + lane) * 16);
+          x.x &= mk[0];
+          x.y &= mk[1];
+          x.z &= mk[2];
+          x.w &= mk[3];
+          *(u32x4*)(vrow + (d + lane) * 16) = x;
+        }
+      }
+    }
     __syncthreads();
     DSA_BAND_ISSUE(c + kBandDepth - 1);
     const uint8_t* ch = &ring[c % kBandDepth][0];
-    ChunkRegs cr;
-    // K rows of region n/4 (tile layout as in memory), V^T of region kb
-    const uint8_t* kp = ch + (n >> 2) * kBandRegion + ((kb * 4 + (n & 3)) * 8) * 2;
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      cr.k0[q] = *(const u32x4*)(kp + (q * 16) * 16);
-      cr.k1[q] = *(const u32x4*)(kp + ((6 + q) * 16) * 16);
-    }
-    const uint8_t* vp = ch + kb * kBandRegion + kRegionBytes;
-#pragma unroll
-    for (int nt = 0; nt < 12; ++nt) cr.v[nt] = *(const u32x4*)(vp + (16 * nt + n) * 16);
-    const int64_t r = rlo + 4 * c + kb, first = r * kRegion;
     int lo[kBandNQ], hi[kBandNQ];
+    if constexpr (kMasked) {
+      const int64_t r = rlo + 4 * c + kb, first = r * kRegion;
 #pragma unroll
-    for (int j = 0; j < kBandNQ; ++j) {
-      const int64_t qlo = pj[j] - W + 1;
-      const bool in = r <= pj[j] / kRegion && first + 7 >= qlo;
-      lo[j] = in ? (int)((qlo > first ? qlo : first) - first) : 1;
-      hi[j] = in ? (int)((pj[j] < first + 7 ? pj[j] : first + 7) - first) : 0;
+      for (int j = 0; j < kBandNQ; ++j) {
+        const int64_t qlo = pj[j] - W + 1;
+        const bool in = r <= pj[j] / kRegion && first + 7 >= qlo;
+        lo[j] = in ? (int)((qlo > first ? qlo : first) - first) : 1;
+        hi[j] = in ? (int)((pj[j] < first + 7 ? pj[j] : first + 7) - first) : 0;
+      }
     }
-    core_compute_band<kBandNQ>(st, [&](int j, int q) { return qb[j][q]; }, cr, lo, hi, a.scale_log2);
-  }
+    band_chunk<kBandNQ, kMasked>(st, qb, ch, lo, hi, a.scale_log2);
+  };
+  auto interior = [&](int c) {
+    const int64_t cf = (rlo + 4 * (int64_t)c) * kRegion;
+    return cf >= uhi - W + 1 && cf + 4 * kRegion - 1 <= p0 + i0;
+  };
+  // the interior chunks form one run
+  int c = 0;
+  for (; c < nch && !interior(c); ++c) body(c, std::true_type());
+  for (; c < nch && interior(c); ++c) body(c, std::false_type());
+  for (; c < nch; ++c) body(c, std::true_type());
   // copies issued past the last chunk must land before the block's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
@@ -1945,7 +2070,7 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   {
     // few blocks: keep two chunks in flight per wave; many: two blocks per CU instead
     ProfScope prof_("k_swa_attend", s);
-    if (max_new_per_seq >= 2 * kBandQ) {  // chunks: the band kernel shares each window across 16 tokens
+    if (max_new_per_seq >= 2 * kBandQ) {  // chunks: the band kernel shares each window across 8 tokens
       const unsigned tiles = (unsigned)((max_new_per_seq + kBandQ - 1) / kBandQ);
       hipLaunchKernelGGL(k_swa_band, dim3((tiles + 7) / 8 * 8, n_seqs, kGroups), dim3(256), 0, s, a);
     } else {

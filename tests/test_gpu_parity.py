@@ -596,7 +596,7 @@ def test_swa_decode_step_equals_attention_then_append():
 
 def test_swa_prefill_chunks_of_several_sequences_in_one_call():
     """Chunks of different lengths for sequences at different positions in one call (the banded
-    prefill kernel: tiles of 16 tokens, partial last tiles, short and full rings)."""
+    prefill kernel: tiles of 8 tokens, partial last tiles, short and full rings)."""
     seed = 0xF7
     p0s, ns = [0, 300, 1000, 4093], [50, 37, 64, 17]
     S, M = len(p0s), max(ns)
