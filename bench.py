@@ -1120,7 +1120,7 @@ def measure_swa(args, result):
     }
     log(f"mix decode: {B * msteps / msecs:.0f} q/s, {mms:.3f} ms/step")
     step, keep = setup_swa_prefill(SWA_PREFILL)
-    ks = ["k_swa_stage", "k_swa_attend", "k_ring_append"]
+    ks = ["k_swa_stage", "k_swa_band", "k_ring_append"]
     ssteps = max(3, args.steps // 3)
     ssecs, seager, sst = timed(step, ssteps, max(1, args.warmup // 2), ks, graph=args.graph)
     del keep
@@ -1128,11 +1128,11 @@ def measure_swa(args, result):
     n = SWA_PREFILL["chunk"]
     fl = swa_prefill_flops(SWA_PREFILL["prefix"], n)
     sms = ssecs * 1e3 / ssteps
-    att_ms = sst["k_swa_attend"][0]
+    att_ms = sst["k_swa_band"][0]
     result["swa_prefill"] = {
         "workload": SWA_PREFILL["name"], "value": round(n * ssteps / ssecs, 1), "unit": "tokens/s",
         "steps": ssteps, "ms_per_step": round(sms, 4), "eager_ms_per_step": round(seager * 1e3 / ssteps, 4),
-        "roofline": {"bound": "mfma", "kernel": "k_swa_attend",
+        "roofline": {"bound": "mfma", "kernel": "k_swa_band",
                      "achieved": round(fl / (att_ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fl / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                      "algorithmic_flops_per_launch": fl, "avg_launch_us": round(att_ms * 1e3, 1),

@@ -2067,13 +2067,14 @@ extern "C" dsa_status swa_attention(const dsa_geometry* geom, int32_t window, in
   }
   st = check_launch("swa_attention: stage");
   if (st != DSA_OK) return st;
-  {
+  if (max_new_per_seq >= 2 * kBandQ) {  // chunks: the band kernel shares each window across 8 tokens
+    ProfScope prof_("k_swa_band", s);
+    const unsigned tiles = (unsigned)((max_new_per_seq + kBandQ - 1) / kBandQ);
+    hipLaunchKernelGGL(k_swa_band, dim3((tiles + 7) / 8 * 8, n_seqs, kGroups), dim3(256), 0, s, a);
+  } else {
     // few blocks: keep two chunks in flight per wave; many: two blocks per CU instead
     ProfScope prof_("k_swa_attend", s);
-    if (max_new_per_seq >= 2 * kBandQ) {  // chunks: the band kernel shares each window across 8 tokens
-      const unsigned tiles = (unsigned)((max_new_per_seq + kBandQ - 1) / kBandQ);
-      hipLaunchKernelGGL(k_swa_band, dim3((tiles + 7) / 8 * 8, n_seqs, kGroups), dim3(256), 0, s, a);
-    } else {
+    {
       const dim3 grid(max_new_per_seq, n_seqs, kGroups);
       if ((int64_t)max_new_per_seq * n_seqs * kGroups < 1024)
         hipLaunchKernelGGL((k_swa_attend<2>), grid, dim3(256), 0, s, a);

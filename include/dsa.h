@@ -616,7 +616,8 @@ dsa_status dsa_rope_qk(const dsa_rope_config* rope, int32_t n_tokens, const int3
  * returns the summed interval (ms) and the number of launches.  Kernel
  * names: k_compress, k_cache_write, k_score_decode,
  * k_score_prefill, k_select, k_sgqa_decode, k_sgqa_merge, k_sgqa_prefill,
- * k_swa_stage, k_swa_attend, k_swa_decode (swa_decode_step), k_ring_append,
+ * k_swa_stage, k_swa_band (chunks of 16 or more tokens), k_swa_attend (shorter
+ * ones), k_swa_decode (swa_decode_step), k_ring_append,
  * k_sgqa_prefill_merged, k_rope_table,
  * k_indexer_proj, k_indexer_finish, k_rope_qk.  Host-side state only, guarded
  * by a mutex; at most 8192 launches are recorded between resets.
