@@ -808,11 +808,15 @@ def main():
         args.no_prefill, args.no_swa = True, False
     if args.profile_run:
         if not args.swa_only:
-            step, keep = setup_decode(DECODE)
-            for _ in range(3):
-                step(cur_stream())
-            torch.cuda.synchronize()
-            del keep
+            # the 1M batch-4 decode, then (unless --no-shapes) the 8K batch-1 and 128K batch-16 ones:
+            # three steps each, in this order
+            for cfg in (DECODE,) + (() if args.no_shapes else (DECODE_8K, DECODE_128K)):
+                step, keep = setup_decode(cfg)
+                for _ in range(3):
+                    step(cur_stream())
+                torch.cuda.synchronize()
+                del keep
+                torch.cuda.empty_cache()
         if not args.no_prefill:
             step, keep = setup_prefill(PREFILL)
             for _ in range(2):
