@@ -1024,6 +1024,9 @@ def measure_merged(args, result):
                     "attention": {"kernel": kern, "avg_launch_us": round(att_ms * 1e3, 1),
                                   "achieved_TFLOPs": round(tf, 2), "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                   "merge_us": round(st["k_sgqa_merge"][0] * 1e3, 1)}}
+        if key == "correlated_merged":  # rocprofv3 counters of this kernel on this chunk
+            res[key]["attention"]["counters"] = load_profile_json(
+                kern, "prefill_64k_correlated", "mfma_json", source_hash("attention.hip"))
         if union is not None:
             res[key]["mean_union_of_2_neighbours_per_group"] = round(union, 1)
         log(f"{key}: {n * steps / secs:.0f} tok/s, attention {att_ms * 1e3:.0f} us")
@@ -1092,6 +1095,9 @@ def measure_frontend(args, result):
                                    "weight_bytes": wbytes,
                                    "weight_GBs": round(wbytes / (proj_ms * 1e-3) / 1e9, 1)},
                     "kernels_us": {k: round(v[0] * 1e3, 2) for k, v in st.items()}}
+        if key == "prefill_chunk":  # the tiled GEMM's rocprofv3 counters (MFMA busy and executed flops)
+            res[key]["projection"]["counters"] = load_profile_json(
+                "k_indexer_gemm", f"frontend_{T}_h{Hd}", "mfma_json", source_hash("frontend.hip"))
         log(f"front-end {key}: projection {proj_ms * 1e3:.1f} us, {tf:.0f} TFLOP/s")
     result["indexer_frontend"] = res
 
